@@ -1,0 +1,142 @@
+"""Roofline SD on/off toggle and acceptance-aware draft length (pure functions).
+
+Sources:
+* p1 "关键模块" item 2 (system-aware SD toggle): model decode latency with a
+  roofline; speculation pays only when a small active batch leaves decode
+  memory-bound, and costs more than it saves when the batch is large and
+  decode is compute-bound.  p1 "局限": the compute/memory boundary is
+  calibrated per GPU.  p3 section 2 ("Elastic enable", "动态选参"): enable SD
+  only below an active-request threshold, and pick draft depth and verify
+  width per batch size.
+* p1 "关键模块" item 3 (acceptance-aware draft length): raise gamma when recent
+  acceptance is high, lower it when low.
+* p5 section 2.2: an EMA coefficient of 0.3 for the online score and a 1.02
+  margin before switching branches.
+
+Plain reading used here (the pages print no formula):
+
+  alpha_ema <- (1 - beta) * alpha_ema + beta * alpha_step,  beta = 0.3 weighting
+  the new sample, alpha_step = sum(accepted) / sum(trials) over the step's
+  sequences, trials = accepted + 1 after a rejection and gamma after a full
+  acceptance (the maximum-likelihood acceptance of the geometric model).
+
+  E[n](alpha, gamma) = (1 - alpha^(gamma+1)) / (1 - alpha)  (tokens per SD step;
+  gamma + 1 when alpha = 1).
+
+  Forward time T(bytes, flops) = t_fwd + max(bytes / BW, flops / FLOPS).
+  AR step:    bytes = wb*P + B*C*kvb + B*kvb + B*V*4,  flops = 2*P*B + 4*B*C*hq*hd*L
+  draft fwd:  bytes = bq*P + B*C*kvb + B*kvb + B*V*4,  flops = 2*P*B + 4*B*C*hq*hd*L
+  verify fwd: bytes = wb*P + B*C*kvb + B*(g+1)*kvb + B*(g+1)*V*4,
+              flops = 2*P*B*(g+1) + 4*B*(g+1)*C*hq*hd*L
+  SD step:    g * T(draft) + T(verify)
+  (P = streamed linear parameters incl. lm_head, wb = target bytes/param,
+  bq = drafter bytes/param, kvb = KV bytes per token, C = mean committed context.)
+
+  score(0) = B / T(AR);  score(g) = B * E[n](alpha, g) / T_SD(g);
+  g* = argmax over {0} U [g_min, g_max] (ties to the smaller g); keep the
+  current choice unless g*'s score exceeds it by the switch margin.
+  g = 0 means autoregressive, so one rule covers both the toggle and gamma.
+
+Pinned by tests/test_oracle_controller.py: E[n] against direct summation of
+the geometric series and Monte Carlo; the toggle is off above the roofline
+crossover and on below it; g* is non-decreasing in alpha; the margin's
+hysteresis.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+
+@dataclass
+class ModelCost:
+    n_layers: int
+    d_model: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ffn: int
+    vocab: int
+    w_bytes: float        # target bytes per linear parameter (2 bf16, 4 fp32)
+    q_bytes: float        # drafter bytes per linear parameter (0.5 + 3/128 for W4-g128, ~1 for W8)
+    kv_bytes_el: float    # bytes per KV element (2 bf16, 4 fp32)
+
+    @property
+    def p_lin(self) -> float:
+        L, d, hq, hkv, hd, F, V = (self.n_layers, self.d_model, self.n_q_heads, self.n_kv_heads,
+                                   self.head_dim, self.ffn, self.vocab)
+        per_layer = d * (hq + 2 * hkv) * hd + hq * hd * d + 2 * F * d + F * d
+        return float(L * per_layer + V * d)
+
+    @property
+    def kvb(self) -> float:
+        return float(self.n_layers * 2 * self.n_kv_heads * self.head_dim * self.kv_bytes_el)
+
+
+@dataclass
+class Roofline:
+    bw: float = 8.0e12        # bytes/s
+    flops: float = 2.5e15     # flop/s
+    t_fwd: float = 0.0        # fixed seconds per forward (launch overhead)
+
+
+def expected_tokens(alpha: float, gamma: int) -> float:
+    if gamma <= 0:
+        return 1.0
+    if alpha >= 1.0:
+        return float(gamma + 1)
+    return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
+
+
+def fwd_time(r: Roofline, nbytes: float, nflops: float) -> float:
+    return r.t_fwd + max(nbytes / r.bw, nflops / r.flops)
+
+
+def ar_time(m: ModelCost, r: Roofline, B: int, C: float) -> float:
+    P, kvb = m.p_lin, m.kvb
+    by = m.w_bytes * P + B * C * kvb + B * kvb + B * m.vocab * 4.0
+    fl = 2.0 * P * B + 4.0 * B * C * m.n_q_heads * m.head_dim * m.n_layers
+    return fwd_time(r, by, fl)
+
+
+def sd_time(m: ModelCost, r: Roofline, B: int, C: float, g: int) -> float:
+    P, kvb = m.p_lin, m.kvb
+    att = 4.0 * C * m.n_q_heads * m.head_dim * m.n_layers
+    d_by = m.q_bytes * P + B * C * kvb + B * kvb + B * m.vocab * 4.0
+    d_fl = 2.0 * P * B + B * att
+    v_by = m.w_bytes * P + B * C * kvb + B * (g + 1) * kvb + B * (g + 1) * m.vocab * 4.0
+    v_fl = 2.0 * P * B * (g + 1) + B * (g + 1) * att
+    return g * fwd_time(r, d_by, d_fl) + fwd_time(r, v_by, v_fl)
+
+
+def score(m: ModelCost, r: Roofline, B: int, C: float, alpha: float, g: int) -> float:
+    if g == 0:
+        return B / ar_time(m, r, B, C)
+    return B * expected_tokens(alpha, g) / sd_time(m, r, B, C, g)
+
+
+def choose(m: ModelCost, r: Roofline, B: int, C: float, alpha: float, g_min: int, g_max: int,
+           current: int = -1, margin: float = 1.02) -> int:
+    cands = [0] + list(range(g_min, g_max + 1))
+    best, best_s = 0, -1.0
+    for g in cands:
+        s = score(m, r, B, C, alpha, g)
+        if s > best_s:
+            best, best_s = g, s
+    if current in cands and current != best:
+        if best_s <= margin * score(m, r, B, C, alpha, current):
+            return current
+    return best
+
+
+def ema(alpha_ema: float, alpha_step: float, beta: float = 0.3) -> float:
+    return (1.0 - beta) * alpha_ema + beta * alpha_step
+
+
+def alpha_step(accepted, gammas) -> float:
+    """accepted[i] drafts accepted of gammas[i] drafted -> trials-based acceptance rate."""
+    num = 0
+    den = 0
+    for a, g in zip(accepted, gammas):
+        num += a
+        den += (a + 1) if a < g else g
+    return num / den if den > 0 else 0.0
