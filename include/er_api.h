@@ -1,0 +1,276 @@
+/*
+ * er_api.h -- C ABI of the self-speculative rollout step (MI355X / gfx950).
+ *
+ * One rollout step for the active batch: a drafter made by quantizing the
+ * target's own weights (W4 group-128 asymmetric or W8 per-channel symmetric)
+ * proposes gamma tokens per sequence while sharing the target's paged KV
+ * cache; the target verifies all gamma+1 positions in one forward; a lossless
+ * rejection sampler keeps a prefix, resamples the first rejection or adds a
+ * bonus token, and the rejected KV tail is rolled back.  A roofline model of
+ * the live batch turns speculation on or off and picks gamma from an EMA of
+ * the acceptance rate.
+ *
+ * Sources (titles of the pages this follows; sections in quotes):
+ *  - "EfficientRollout: system-aware self-speculative decoding for RL
+ *    rollouts" (ai-feeds summary of arXiv 2606.18967): "关键模块" items 1-3
+ *    (quantized self-drafter sharing the KV cache; roofline SD toggle;
+ *    acceptance-aware draft length), "与现有工作流的接口" (inputs: the policy
+ *    model and its quantized copy; W4A16), "局限" (per-GPU calibration).
+ *  - "Accelerating RL Post-Training Rollouts via System-Integrated
+ *    Speculative Decoding" (abstract): speculation must be lossless.
+ *  - "TLT" reading notes, section 1 (parallel verification discards drafts
+ *    after the first failure) and section 2 (elastic enable, per-batch-size
+ *    parameters).
+ *  - "History Tree Dynamic RL" (cann-recipes-train PR), section 2.2 (draft
+ *    token count default 4; EMA coefficient 0.3; switch margin 1.02) and
+ *    section 4 (speculative-decoding metrics).
+ *
+ * Conventions for every call:
+ *  - Return 0 (ER_OK) or a negative ER_* code.  No C++ exception crosses the
+ *    ABI.  er_last_error() holds a message owned by the context, valid until
+ *    the next call on that context.
+ *  - A context is single-threaded and bound to the HIP stream given at init.
+ *    Every call that launches work is synchronous: it returns after the
+ *    results it reports have been copied to host memory.
+ *  - A failing step changes no sequence state (results are committed on the
+ *    host after the device work succeeded).  ER_ENOMEM from er_kv_alloc or
+ *    from a step's KV reservation is recoverable by freeing sequences.
+ *  - Host pointers are caller-owned and only read/written during the call.
+ *    Device pointers passed to er_rollout_init (weights, arena) are borrowed
+ *    for the life of the context.
+ */
+#ifndef ER_API_H
+#define ER_API_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define ER_OK        0
+#define ER_EINVAL   -1   /* bad argument: null pointer, bad size, unknown sequence id */
+#define ER_ENOMEM   -2   /* device arena or KV block pool exhausted */
+#define ER_EDEVICE  -3   /* a HIP call failed (message in er_last_error) */
+#define ER_ESTATE   -4   /* sequence finished / not prefilled / wrong order of calls */
+
+/* ---- enums ---------------------------------------------------------------- */
+#define ER_F32  0        /* target weights, KV and linear inputs in fp32 */
+#define ER_BF16 1        /* target weights, KV and linear inputs in bf16 */
+
+#define ER_W8_PERCH_SYM  0   /* int8 codes, one fp32 scale per output row */
+#define ER_W4_G128_ASYM  1   /* 4-bit codes, bf16 scale + u8 zero per row and 128 inputs */
+
+#define ER_POLICY_AUTO      0   /* roofline toggle + adaptive gamma */
+#define ER_POLICY_FORCE_SD  1   /* always speculate (gamma adaptive unless pinned) */
+#define ER_POLICY_FORCE_AR  2   /* never speculate */
+
+#define ER_MODE_AR 0
+#define ER_MODE_SD 1
+
+typedef struct er_ctx er_ctx;
+
+/* Decoder shape.  Pre-norm layers: RMSNorm, RoPE (rotate-half), GQA with
+ * n_q_heads % n_kv_heads == 0, SwiGLU FFN; untied lm_head; no biases. */
+typedef struct er_model_desc {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  int32_t dtype;            /* ER_F32 or ER_BF16 */
+  float rms_eps;
+  float rope_theta;
+} er_model_desc;
+
+/* Self-drafter: the target's linears (q/k/v/o, gate/up/down, lm_head)
+ * quantized; embedding and norm gains shared unquantized.  W4 needs every
+ * input dimension K to be a multiple of 128 and a bf16 model. */
+typedef struct er_draft_desc {
+  int32_t quant;            /* ER_W8_PERCH_SYM or ER_W4_G128_ASYM */
+  int32_t group_size;       /* 128 (W4 only) */
+  int32_t quant_lm_head;    /* 1: lm_head quantized too (default); 0: drafter uses the bf16 lm_head */
+} er_draft_desc;
+
+typedef struct er_rollout_desc {
+  uint64_t seed;            /* Philox key */
+  float temperature;        /* 0 = greedy */
+  float top_p;              /* >= 1 disables nucleus filtering */
+  int32_t gamma_init;       /* initial draft length (4) */
+  int32_t gamma_min;        /* adaptive range, 1..gamma_max */
+  int32_t gamma_max;        /* <= 16 */
+  float ema_beta;           /* weight of the newest acceptance sample (0.3) */
+  float switch_margin;      /* a new (mode, gamma) must score this factor better (1.02) */
+  float alpha_init;         /* acceptance prior before the first speculative step */
+  int32_t policy;           /* ER_POLICY_* */
+  int32_t kv_block;         /* tokens per KV block; must be 16 */
+  int32_t max_seqs;         /* sequences alive at once */
+  int32_t max_batch;        /* sequences per step (<= max_seqs); (n_q_heads/n_kv_heads)*(gamma_max+1) <= 64 */
+  int32_t max_ctx;          /* max tokens per sequence (prompt + generated + gamma_max + 1) */
+  int32_t prefill_chunk;    /* max prompt tokens per prefill forward */
+  int64_t kv_pool_blocks;   /* 0: every block the arena can hold after the other buffers */
+  double hbm_bytes_per_s;   /* roofline constants; <= 0: measured at init */
+  double flops_per_s;
+  double t_fwd_s;           /* fixed time per forward (launch overhead); < 0: measured at init */
+} er_rollout_desc;
+
+/* Device pointers to the target's weights, row-major, element type
+ * model.dtype.  Borrowed: they must stay valid and unchanged until
+ * er_update_weights or er_destroy.  Per-layer entries are host arrays of
+ * n_layers device pointers. */
+typedef struct er_weights {
+  const void *embed;        /* [vocab, d_model] */
+  const void *final_norm;   /* [d_model] */
+  const void *lm_head;      /* [vocab, d_model] */
+  const void *const *attn_norm;  /* [d_model] */
+  const void *const *wqkv;       /* [(n_q_heads + 2 n_kv_heads) head_dim, d_model]: q rows, k rows, v rows */
+  const void *const *wo;         /* [d_model, n_q_heads head_dim] */
+  const void *const *mlp_norm;   /* [d_model] */
+  const void *const *wgate_up;   /* [2 ffn, d_model]: gate rows, then up rows */
+  const void *const *wdown;      /* [d_model, ffn] */
+} er_weights;
+
+typedef struct er_step_info {
+  int32_t mode;             /* ER_MODE_SD or ER_MODE_AR */
+  int32_t gamma;            /* draft length used (0 for AR) */
+  int32_t batch;            /* sequences in the step */
+  int32_t accepted;         /* drafts accepted, summed over the batch */
+  int32_t emitted;          /* tokens emitted before stop truncation */
+  int32_t kept;             /* tokens kept after stop truncation */
+  int32_t finished;         /* sequences that reached their stop length in this step */
+  float alpha_step;         /* trials-based acceptance of this step */
+  float alpha_ema;          /* after the update */
+  float ms_draft, ms_verify, ms_sample, ms_total;   /* device time per phase (timed steps only) */
+} er_step_info;
+
+/* Counters named after the speculative-decoding metrics of the History Tree
+ * Dynamic RL page (section 4), plus the controller state. */
+typedef struct er_stats {
+  int64_t predict_times;      /* speculative attempts: SD steps x sequences */
+  int64_t effective_times;    /* attempts that accepted >= 1 draft */
+  int64_t total_right_length; /* accepted drafts, summed */
+  double effective_length;    /* total_right_length / effective_times */
+  double effective_percent;   /* effective_times / predict_times */
+  int64_t sd_steps, ar_steps;
+  int64_t drafted, accepted, emitted, bonus;
+  int64_t tokens_kept;        /* generated tokens after stop truncation (prefill's first tokens included) */
+  double alpha_ema;
+  int32_t gamma;              /* current choice: 0 = AR */
+  int32_t mode;
+  double ms_draft, ms_verify, ms_sample, ms_ar, ms_prefill;   /* accumulated, timed steps only */
+} er_stats;
+
+/* Create a context.  Carves dev_arena (device memory the caller owns, e.g. a
+ * torch uint8 tensor) into the drafter pack, the KV block pool and step
+ * workspaces, then quantizes the target into the drafter (EfficientRollout
+ * "关键模块" item 1).  hip_stream: a hipStream_t, or NULL for the null stream.
+ * Returns ER_ENOMEM if the arena is too small (the message states the bytes
+ * needed), ER_EINVAL for an inconsistent description. */
+int er_rollout_init(const er_model_desc *model, const er_weights *w, const er_draft_desc *draft,
+                    const er_rollout_desc *rollout, void *dev_arena, size_t arena_bytes,
+                    void *hip_stream, er_ctx **out);
+
+/* Bytes of arena er_rollout_init needs for these descriptions (kv_pool_blocks
+ * blocks of KV; 0 counts none).  Pure host computation. */
+int er_arena_bytes(const er_model_desc *model, const er_draft_desc *draft,
+                   const er_rollout_desc *rollout, int64_t kv_pool_blocks, size_t *bytes_out);
+
+/* Re-point the context at (possibly new) target weights and re-quantize the
+ * drafter; call after every policy update so the drafter tracks the policy
+ * (EfficientRollout "关键模块" item 1). */
+int er_update_weights(er_ctx *ctx, const er_weights *w);
+
+/* Register n new sequences.  prompt_lens[i] >= 1 prompt tokens;
+ * max_new[i] >= 1 generated tokens after which sequence i stops (the token
+ * drawn by er_prefill counts); share_group[i] >= 0 makes sequences with equal
+ * groups share their prompt's full KV blocks (their prompts must be equal),
+ * -1 = private; share_group may be NULL.  Writes the new sequence ids, which
+ * are also the Philox sequence words: ids are assigned 0, 1, 2, ... in call
+ * order over the context's life.  ER_ENOMEM if max_seqs would be exceeded or
+ * the prompt blocks do not fit. */
+int er_kv_alloc(er_ctx *ctx, int n, const int32_t *prompt_lens, const int32_t *max_new,
+                const int32_t *share_group, int32_t *seq_ids_out);
+
+/* Run the target over each sequence's prompt (tokens of sequence i are
+ * tokens[offsets[i] .. offsets[i+1])) and draw its first generated token as
+ * an autoregressive sample at position prompt_len.  first_tok_out[n]. */
+int er_prefill(er_ctx *ctx, int n, const int32_t *seq_ids, const int32_t *tokens,
+               const int64_t *offsets, int32_t *first_tok_out);
+
+/* One speculative step for the given active sequences with the current gamma
+ * (pinned by er_set_gamma, else the controller's).  tokens_out[n * (gamma_max+1)]
+ * receives sequence i's emitted tokens at [i*(gamma_max+1), ...), n_emitted_out[i]
+ * of them (after stop truncation).  info_out may be NULL. */
+int er_spec_step(er_ctx *ctx, int n, const int32_t *seq_ids, int32_t *tokens_out,
+                 int32_t *n_emitted_out, er_step_info *info_out);
+
+/* One autoregressive step (target forward at M = n, one sample each). */
+int er_ar_step(er_ctx *ctx, int n, const int32_t *seq_ids, int32_t *tokens_out,
+               er_step_info *info_out);
+
+/* Controller-driven step: the roofline toggle and the gamma rule choose
+ * between er_ar_step and er_spec_step for this batch.  Output layout as
+ * er_spec_step. */
+int er_step(er_ctx *ctx, int n, const int32_t *seq_ids, int32_t *tokens_out,
+            int32_t *n_emitted_out, er_step_info *info_out);
+
+/* Run every given sequence to its stop length with er_step, dropping
+ * finished sequences from the batch as they finish (the shrinking batch).
+ * out_tokens[i * max_new_cap ...] receives the tokens this call generates for
+ * sequence i (the first token, returned by er_prefill, is not repeated),
+ * out_len[i] their count.  Sequences must be prefilled; n <= max_batch;
+ * max_new_cap >= every max_new.  stats_out (nullable) gets er_get_stats. */
+int er_rollout(er_ctx *ctx, int n, const int32_t *seq_ids, int32_t max_new_cap,
+               int32_t *out_tokens, int32_t *out_len, er_stats *stats_out);
+
+/* Pin gamma to 1..gamma_max, or 0 to let the controller adapt it; anything
+ * else is ER_EINVAL. */
+int er_set_gamma(er_ctx *ctx, int gamma);
+
+/* Change the policy (ER_POLICY_*). */
+int er_set_policy(er_ctx *ctx, int policy);
+
+/* Release sequences and their KV blocks (shared blocks when their last user goes). */
+int er_kv_free(er_ctx *ctx, int n, const int32_t *seq_ids);
+
+/* Sequence state: generated count, committed context length, finished flag. */
+int er_seq_info(er_ctx *ctx, int32_t seq_id, int32_t *generated, int32_t *context_len, int32_t *finished);
+
+int er_get_stats(er_ctx *ctx, er_stats *out);
+int er_reset_stats(er_ctx *ctx);
+
+/* Record device time per phase for every `period`-th step and the first
+ * `first_n` steps (0, 0 = never, the default). */
+int er_set_timing(er_ctx *ctx, int period, int first_n);
+
+/* Free KV blocks in the pool. */
+int er_kv_free_blocks(er_ctx *ctx, int64_t *free_blocks, int64_t *total_blocks);
+
+/* ---- diagnostics: the last step's logits and drafts, for checking ------- */
+/* which = 0: drafter logits of batch slot `slot` ([gamma, vocab] fp32);
+ * which = 1: target logits ([gamma+1, vocab] after a speculative step,
+ * [1, vocab] after an autoregressive step or prefill).  rows_out gets the row
+ * count; host_out must hold rows * vocab floats (pass NULL to query rows). */
+int er_debug_logits(er_ctx *ctx, int which, int slot, float *host_out, int32_t *rows_out);
+/* Drafts of the last speculative step, [batch, gamma] int32. */
+int er_debug_drafts(er_ctx *ctx, int32_t *host_out);
+
+/* Pure host functions of the controller (no device work), exposed so that a
+ * caller running its own loop gets the same decisions:
+ * er_controller_choose returns in *gamma_out the argmax over {0 (AR)} U
+ * [gamma_min, gamma_max] of B * E[n](alpha, gamma) / T(B, C, gamma), keeping
+ * `current` unless the best beats it by `margin`. */
+typedef struct er_cost_model {
+  int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+  double w_bytes, q_bytes, kv_bytes_el;
+  double hbm_bytes_per_s, flops_per_s, t_fwd_s;
+} er_cost_model;
+int er_controller_choose(const er_cost_model *m, int batch, double mean_ctx, double alpha,
+                         int gamma_min, int gamma_max, int current, double margin, int *gamma_out);
+double er_expected_tokens(double alpha, int gamma);
+
+const char *er_last_error(const er_ctx *ctx);
+void er_destroy(er_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ER_API_H */

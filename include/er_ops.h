@@ -1,0 +1,96 @@
+/*
+ * er_ops.h -- operation-level C ABI: the individual gfx950 kernels of the
+ * self-speculative step, on caller-provided device buffers.  The rollout
+ * API (er_api.h) composes the same kernels; these entry points let a caller
+ * (and the parity tests) run one operation on inputs of its choice.
+ *
+ * Conventions: every pointer named d_* is device memory the caller owns;
+ * `stream` is a hipStream_t (NULL = null stream).  Calls enqueue work and
+ * return without synchronizing, except where stated.  Return 0 or a negative
+ * ER_* code (er_api.h); a shape the kernel does not support is ER_EINVAL.
+ * Workspace the kernels need (split-K partials) is allocated once per
+ * process on first use and kept.
+ */
+#ifndef ER_OPS_H
+#define ER_OPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats of er_op_linear. */
+#define ER_FMT_F32  0   /* fp32 [N, K] */
+#define ER_FMT_BF16 1   /* bf16 [N, K] */
+#define ER_FMT_W8   2   /* int8 codes [N, K] + fp32 scale [N] */
+#define ER_FMT_W4   3   /* 4-bit codes [N, K/2] in kernel nibble order + bf16 scale [N, K/128] + u8 zero [N, K/128] */
+
+/* Drafter quantization of one weight matrix W [N, K] (EfficientRollout,
+ * "关键模块" item 1; W4A16 in "与现有工作流的接口").
+ * W8: d_codes int8 [N, K], d_scale fp32 [N]: s = max|w|/127 rounded up to
+ *     fp32, q = clamp(rint(w/s), -127, 127); d_zero unused.  w_dtype ER_F32 or ER_BF16.
+ * W4: d_codes uint8 [N, K/2], canonical order (low nibble = even k),
+ *     d_scale bf16 [N, K/128], d_zero u8 [N, K/128]: per 128-group lo =
+ *     min(min w, 0), hi = max(max w, 0), s = (hi-lo)/15 rounded up to bf16,
+ *     z = clamp(rint(-lo/s), 0, 15), q = clamp(rint(w/s) + z, 0, 15).  bf16 W only, K % 128 == 0. */
+int er_op_quantize(int quant, int w_dtype, const void *d_w, int N, int K, void *d_codes, void *d_scale,
+                   void *d_zero, void *stream);
+
+/* Canonical W4 nibble order -> the order er_op_linear's ER_FMT_W4 reads
+ * (within each 32-bit word covering k..k+7: k+2i at bits 4i, k+2i+1 at bits 16+4i). */
+int er_op_w4_kernel_order(const void *d_canon, int N, int K, void *d_out, void *stream);
+
+/* y[m, n] = sum_k x[m, k] W[n, k] for m < M, n < N; y fp32 [M, ldy].
+ * x: [M, ldx] of x_dtype (ER_BF16 or ER_F32).  path: 0 automatic, 1 VALU,
+ * 2 MFMA (bf16 x, K % 128 == 0).  The verify pass runs the target's linears
+ * with this at M = B (gamma + 1); the drafter runs its quantized copies at M = B. */
+int er_op_linear(int x_dtype, const void *d_x, int ldx, int M, int fmt, const void *d_w, const void *d_scale,
+                 const void *d_zero, int N, int K, float *d_y, int ldy, int path, void *stream);
+
+/* Paged GQA attention (TLT reading notes, section 1: the target scores all
+ * drafted positions in one pass).  q: [Mq, hq, hd] of act_dtype; out same
+ * shape.  KV pool of blocks of 16 positions, element (block, layer, k|v,
+ * kv_head, t, e) at ((((block*L + layer)*2 + kv)*hkv + head)*16 + t)*hd + e.
+ * Item i: q rows q_row0[i] .. + q_count[i]-1 at positions q_pos0[i] .. of the
+ * sequence whose block table row is bt_row[i] (block_table [rows, bt_stride]);
+ * a query at position t sees keys 0..t.  (n_q_heads/n_kv_heads)*max_q_count <= 64,
+ * hd in {64, 128}. */
+int er_op_attention(int act_dtype, const void *d_q, void *d_out, const void *d_kv_pool, int n_layers, int layer,
+                    int hq, int hkv, int hd, const int32_t *d_block_table, int bt_stride, const int32_t *d_bt_row,
+                    const int32_t *d_q_row0, const int32_t *d_q_pos0, const int32_t *d_q_count, int n_items,
+                    int max_q_count, int max_ctx, void *stream);
+
+/* Per-row sampling statistics of fp32 logits rows [rows, ld] (max, argmax,
+ * softmax mass in fp64, top-p threshold).  d_stats: er_op_stats_bytes() each. */
+size_t er_op_stats_bytes(void);
+int er_op_row_stats(const float *d_logits, int rows, int V, long ld, float temperature, float top_p, void *d_stats,
+                    void *stream);
+
+/* One draw per row from pi(row; T, top_p): the smallest index whose running
+ * sum in vocabulary order reaches u * total, u = Philox4x32-10 uniform of
+ * (seed; seq_id[r], pos[r], draft_idx, purpose).  d_out[r * out_stride]. */
+int er_op_sample_rows(const float *d_logits, const void *d_stats, int rows, int V, long ld, float temperature,
+                      uint64_t seed, const int32_t *d_seq_id, const int32_t *d_pos, int draft_idx, int purpose,
+                      int32_t *d_out, int out_stride, void *stream);
+
+/* Speculative decision for B sequences (standard speculative sampling, the
+ * lossless rule): target rows [B*(gamma+1), V] b-major, drafter rows
+ * [gamma*B, V] draft-index-major, with their stats; d_tokens [B, gamma+1]
+ * holds (pending, d_1..d_gamma); accept d_j iff u*q_j(d_j) <= p_j(d_j), else
+ * resample normalize(max(0, p_j - q_j)) and stop; bonus from p_{gamma+1}
+ * after a full acceptance.  d_out_tok [B, gamma+1], d_n_acc [B]. */
+int er_op_spec_decide(const float *d_p_logits, const void *d_p_stats, const float *d_q_logits, const void *d_q_stats,
+                      const int32_t *d_tokens, int B, int gamma, int V, float temperature, uint64_t seed,
+                      const int32_t *d_seq_id, const int32_t *d_pos0, int32_t *d_out_tok, int32_t *d_n_acc,
+                      void *stream);
+
+/* u[i] = Philox4x32-10 uniform of counter d_ctr[4i..4i+3] under key seed:
+ * ((out0 >> 8) + 1) * 2^-24, as fp64. */
+int er_op_philox_uniform(uint64_t seed, const uint32_t *d_ctr, int n, double *d_u, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ER_OPS_H */

@@ -1,0 +1,163 @@
+"""ctypes binding of libsdrl.so (include/er_api.h, include/er_ops.h).
+
+Argument marshalling only: every step of the rollout runs in the library's
+gfx950 kernels.  Loading fails loudly when the library has not been built or
+cannot be opened; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdrl.so")
+
+ER_OK, ER_EINVAL, ER_ENOMEM, ER_EDEVICE, ER_ESTATE = 0, -1, -2, -3, -4
+ER_F32, ER_BF16 = 0, 1
+ER_W8_PERCH_SYM, ER_W4_G128_ASYM = 0, 1
+ER_POLICY_AUTO, ER_POLICY_FORCE_SD, ER_POLICY_FORCE_AR = 0, 1, 2
+ER_MODE_AR, ER_MODE_SD = 0, 1
+ER_FMT_F32, ER_FMT_BF16, ER_FMT_W8, ER_FMT_W4 = 0, 1, 2, 3
+PURPOSE_DRAFT, PURPOSE_ACCEPT, PURPOSE_RESIDUAL, PURPOSE_AR = 0, 1, 2, 3
+
+_NAMES = {ER_EINVAL: "ER_EINVAL", ER_ENOMEM: "ER_ENOMEM", ER_EDEVICE: "ER_EDEVICE", ER_ESTATE: "ER_ESTATE"}
+
+
+class ModelDesc(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32), ("vocab", C.c_int32),
+                ("dtype", C.c_int32), ("rms_eps", C.c_float), ("rope_theta", C.c_float)]
+
+
+class DraftDesc(C.Structure):
+    _fields_ = [("quant", C.c_int32), ("group_size", C.c_int32), ("quant_lm_head", C.c_int32)]
+
+
+class RolloutDesc(C.Structure):
+    _fields_ = [("seed", C.c_uint64), ("temperature", C.c_float), ("top_p", C.c_float),
+                ("gamma_init", C.c_int32), ("gamma_min", C.c_int32), ("gamma_max", C.c_int32),
+                ("ema_beta", C.c_float), ("switch_margin", C.c_float), ("alpha_init", C.c_float),
+                ("policy", C.c_int32), ("kv_block", C.c_int32), ("max_seqs", C.c_int32), ("max_batch", C.c_int32),
+                ("max_ctx", C.c_int32), ("prefill_chunk", C.c_int32), ("kv_pool_blocks", C.c_int64),
+                ("hbm_bytes_per_s", C.c_double), ("flops_per_s", C.c_double), ("t_fwd_s", C.c_double)]
+
+
+class Weights(C.Structure):
+    _fields_ = [("embed", C.c_void_p), ("final_norm", C.c_void_p), ("lm_head", C.c_void_p),
+                ("attn_norm", C.POINTER(C.c_void_p)), ("wqkv", C.POINTER(C.c_void_p)),
+                ("wo", C.POINTER(C.c_void_p)), ("mlp_norm", C.POINTER(C.c_void_p)),
+                ("wgate_up", C.POINTER(C.c_void_p)), ("wdown", C.POINTER(C.c_void_p))]
+
+
+class StepInfo(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("gamma", C.c_int32), ("batch", C.c_int32), ("accepted", C.c_int32),
+                ("emitted", C.c_int32), ("kept", C.c_int32), ("finished", C.c_int32),
+                ("alpha_step", C.c_float), ("alpha_ema", C.c_float), ("ms_draft", C.c_float),
+                ("ms_verify", C.c_float), ("ms_sample", C.c_float), ("ms_total", C.c_float)]
+
+
+class Stats(C.Structure):
+    _fields_ = [("predict_times", C.c_int64), ("effective_times", C.c_int64), ("total_right_length", C.c_int64),
+                ("effective_length", C.c_double), ("effective_percent", C.c_double),
+                ("sd_steps", C.c_int64), ("ar_steps", C.c_int64), ("drafted", C.c_int64), ("accepted", C.c_int64),
+                ("emitted", C.c_int64), ("bonus", C.c_int64), ("tokens_kept", C.c_int64),
+                ("alpha_ema", C.c_double), ("gamma", C.c_int32), ("mode", C.c_int32),
+                ("ms_draft", C.c_double), ("ms_verify", C.c_double), ("ms_sample", C.c_double),
+                ("ms_ar", C.c_double), ("ms_prefill", C.c_double)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class CostModel(C.Structure):
+    _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32), ("vocab", C.c_int32),
+                ("w_bytes", C.c_double), ("q_bytes", C.c_double), ("kv_bytes_el", C.c_double),
+                ("hbm_bytes_per_s", C.c_double), ("flops_per_s", C.c_double), ("t_fwd_s", C.c_double)]
+
+
+P = C.c_void_p
+I32P = C.POINTER(C.c_int32)
+I64P = C.POINTER(C.c_int64)
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    # er_api.h
+    "er_rollout_init": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(Weights), C.POINTER(DraftDesc),
+                                  C.POINTER(RolloutDesc), P, C.c_size_t, P, C.POINTER(P)]),
+    "er_arena_bytes": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(DraftDesc), C.POINTER(RolloutDesc), C.c_int64,
+                                 C.POINTER(C.c_size_t)]),
+    "er_update_weights": (C.c_int, [P, C.POINTER(Weights)]),
+    "er_kv_alloc": (C.c_int, [P, C.c_int, I32P, I32P, I32P, I32P]),
+    "er_prefill": (C.c_int, [P, C.c_int, I32P, I32P, I64P, I32P]),
+    "er_spec_step": (C.c_int, [P, C.c_int, I32P, I32P, I32P, C.POINTER(StepInfo)]),
+    "er_ar_step": (C.c_int, [P, C.c_int, I32P, I32P, C.POINTER(StepInfo)]),
+    "er_step": (C.c_int, [P, C.c_int, I32P, I32P, I32P, C.POINTER(StepInfo)]),
+    "er_rollout": (C.c_int, [P, C.c_int, I32P, C.c_int32, I32P, I32P, C.POINTER(Stats)]),
+    "er_set_gamma": (C.c_int, [P, C.c_int]),
+    "er_set_policy": (C.c_int, [P, C.c_int]),
+    "er_kv_free": (C.c_int, [P, C.c_int, I32P]),
+    "er_seq_info": (C.c_int, [P, C.c_int32, I32P, I32P, I32P]),
+    "er_get_stats": (C.c_int, [P, C.POINTER(Stats)]),
+    "er_reset_stats": (C.c_int, [P]),
+    "er_set_timing": (C.c_int, [P, C.c_int, C.c_int]),
+    "er_kv_free_blocks": (C.c_int, [P, I64P, I64P]),
+    "er_debug_logits": (C.c_int, [P, C.c_int, C.c_int, C.POINTER(C.c_float), I32P]),
+    "er_debug_drafts": (C.c_int, [P, I32P]),
+    "er_controller_choose": (C.c_int, [C.POINTER(CostModel), C.c_int, C.c_double, C.c_double, C.c_int, C.c_int,
+                                       C.c_int, C.c_double, C.POINTER(C.c_int)]),
+    "er_expected_tokens": (C.c_double, [C.c_double, C.c_int]),
+    "er_last_error": (C.c_char_p, [P]),
+    "er_destroy": (None, [P]),
+    # er_ops.h
+    "er_op_quantize": (C.c_int, [C.c_int, C.c_int, P, C.c_int, C.c_int, P, P, P, P]),
+    "er_op_w4_kernel_order": (C.c_int, [P, C.c_int, C.c_int, P, P]),
+    "er_op_linear": (C.c_int, [C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P, C.c_int, C.c_int, P, C.c_int,
+                               C.c_int, P]),
+    "er_op_attention": (C.c_int, [C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int, P, P,
+                                  P, P, C.c_int, C.c_int, C.c_int, P]),
+    "er_op_stats_bytes": (C.c_size_t, []),
+    "er_op_row_stats": (C.c_int, [P, C.c_int, C.c_int, C.c_long, C.c_float, C.c_float, P, P]),
+    "er_op_sample_rows": (C.c_int, [P, P, C.c_int, C.c_int, C.c_long, C.c_float, C.c_uint64, P, P, C.c_int, C.c_int,
+                                    P, C.c_int, P]),
+    "er_op_spec_decide": (C.c_int, [P, P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_uint64, P, P, P, P, P]),
+    "er_op_philox_uniform": (C.c_int, [C.c_uint64, P, C.c_int, P, P]),
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return LIB_PATH
+
+
+def load() -> C.CDLL:
+    """Open libsdrl.so and declare every exported signature; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run speculative_decoding_rl_amd/build.py (or __graft_entry__.build())")
+    lib = C.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class ErError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+def check(code: int, ctx=None, what: str = ""):
+    if code == ER_OK:
+        return
+    msg = what
+    if ctx:
+        m = load().er_last_error(ctx)
+        msg = f"{what}: {m.decode() if m else ''}"
+    raise ErError(code, msg)

@@ -1,0 +1,1502 @@
+// C ABI of the self-speculative rollout step: context, arena, drafter build,
+// paged KV bookkeeping, the step drivers (speculative / autoregressive /
+// controller-chosen), prefill, the full shrinking-batch rollout loop,
+// statistics and diagnostics.  See include/er_api.h for the contract.
+//
+// The step follows the EfficientRollout page ("关键模块" items 1-3): the
+// drafter is the target with quantized linears and shares the target's KV
+// cache; the target verifies gamma+1 positions in one forward; a lossless
+// rejection sampler (standard speculative sampling, the "lossless primitive"
+// of the System-Integrated Speculative Decoding abstract) decides; the KV
+// tail past the accepted prefix is released (TLT notes, section 1); a
+// roofline toggle and an EMA of the acceptance rate pick AR vs SD and gamma.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/er_api.h"
+#include "controller.h"
+#include "kernels.h"
+#include "kvpool.h"
+
+using namespace er;
+
+namespace {
+
+struct Lin4 {
+  LinearW qkv, o, gu, down;
+};
+
+struct Seq {
+  bool alive = false, prefilled = false, finished = false;
+  int32_t prompt_len = 0, max_new = 0, generated = 0;
+  int32_t n = 0;        // position of the pending token == committed KV entries
+  int32_t pending = 0;
+  int32_t group = -1;
+  bool leader = true;   // computes the shared prompt for its group
+  int32_t leader_id = -1;
+  BlockTable bt;
+};
+
+struct Meta {
+  char* h = nullptr;
+  char* d = nullptr;
+  size_t used = 0, cap = 0;
+  bool ok = true;
+  void reset() { used = 0; ok = true; }
+  template <class T>
+  T* push(size_t n, size_t* off) {
+    const size_t a = (used + 255) & ~(size_t)255;
+    if (a + n * sizeof(T) > cap) { ok = false; *off = 0; return nullptr; }
+    *off = a;
+    used = a + n * sizeof(T);
+    return (T*)(h + a);
+  }
+  template <class T>
+  T* dev(size_t off) const { return (T*)(d + off); }
+};
+
+}  // namespace
+
+struct er_ctx {
+  er_model_desc md{};
+  er_draft_desc dd{};
+  er_rollout_desc rd{};
+  bool bf16 = true;
+  int act_bytes = 2;
+  hipStream_t st = nullptr;
+
+  // weights
+  const void* embed = nullptr;
+  const void* final_norm = nullptr;
+  std::vector<const void*> attn_norm, mlp_norm;
+  std::vector<Lin4> tgt, drf;
+  LinearW lm_t{}, lm_d{};
+
+  // arena
+  char* arena = nullptr;
+  size_t arena_bytes = 0, arena_used = 0;
+
+  // device buffers
+  float2* cs = nullptr;
+  float* h = nullptr;
+  void* xbuf = nullptr;
+  float* qkv = nullptr;
+  void* qb = nullptr;
+  float* gu = nullptr;
+  float* logits_p = nullptr;
+  float* logits_q = nullptr;
+  RowStats* stats_p = nullptr;
+  RowStats* stats_q = nullptr;
+  int32_t* out_d = nullptr;     // [rows] tokens + [max_batch] accepted counts
+  int32_t* out_h = nullptr;     // pinned
+  LinearWs lws{};
+  float* attn_ws = nullptr;
+  size_t attn_ws_floats = 0;
+  uint8_t* w4_tmp = nullptr;
+  size_t w4_tmp_bytes = 0;
+  uint32_t* sink = nullptr;
+  void* kv_pool = nullptr;
+  size_t block_bytes = 0;
+  Meta meta;
+
+  int max_rows = 0;       // rows of the activation buffers
+  int logit_rows = 0;     // rows of logits_p
+  int lin_path = 0;
+
+  BlockPool pool;
+  std::vector<Seq> seqs;
+  int32_t alive = 0;
+
+  // controller
+  CostModel cost{};
+  double alpha_ema = 0.8;
+  int gamma_pinned = 0;
+  int choice = -1;        // last controller choice (0 = AR), -1 none yet
+  int policy = ER_POLICY_AUTO;
+
+  er_stats stats{};
+  std::string err;
+
+  // diagnostics
+  int last_mode = -1, last_gamma = 0, last_B = 0;
+  size_t last_tok_off = 0;  // verify tokens [B, gamma+1] of the last speculative step, in the metadata region
+  std::vector<int32_t> last_prefill_row;
+
+  // timing
+  int timing_period = 0, timing_first = 0;
+  long step_count = 0;
+  hipEvent_t ev[6] = {};
+  bool have_ev = false;
+};
+
+namespace {
+
+int fail(er_ctx* c, int code, const char* fmt, ...) {
+  if (c) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    c->err = buf;
+  }
+  return code;
+}
+
+#define HIPC(c, x)                                                                      \
+  do {                                                                                  \
+    hipError_t e_ = (x);                                                                \
+    if (e_ != hipSuccess) return fail((c), ER_EDEVICE, "%s: %s", #x, hipGetErrorString(e_)); \
+  } while (0)
+
+#define KC(c, x)                                                                        \
+  do {                                                                                  \
+    int r_ = (x);                                                                       \
+    if (r_ != 0) {                                                                      \
+      hipError_t e_ = hipGetLastError();                                                \
+      return fail((c), r_ == -2 ? ER_ENOMEM : (r_ == -1 ? ER_EINVAL : ER_EDEVICE),      \
+                  "%s failed (%d): %s", #x, r_, hipGetErrorString(e_));                 \
+    }                                                                                   \
+  } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Layout of everything but the KV pool, shared by er_arena_bytes and init.
+struct Layout {
+  size_t drafter = 0, cs = 0, h = 0, xbuf = 0, qkv = 0, qb = 0, gu = 0, lp = 0, lq = 0, sp = 0, sq = 0;
+  size_t out = 0, partial = 0, counters = 0, attn = 0, w4tmp = 0, sink = 0, meta = 0;
+  size_t block_bytes = 0;
+  int max_rows = 0, logit_rows = 0;
+  size_t total_fixed() const {
+    return drafter + cs + h + xbuf + qkv + qb + gu + lp + lq + sp + sq + out + partial + counters + attn + w4tmp +
+           sink + meta;
+  }
+};
+
+size_t quant_bytes(const er_draft_desc& dd, long N, long K) {
+  if (dd.quant == ER_W8_PERCH_SYM) return align256((size_t)N * K) + align256((size_t)N * 4);
+  const long G = K / 128;
+  return align256((size_t)N * K / 2) + align256((size_t)N * G * 2) + align256((size_t)N * G);
+}
+
+int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollout_desc& r, Layout* L,
+                std::string* why) {
+  const long d = m.d_model, hq = m.n_q_heads, hkv = m.n_kv_heads, hd = m.head_dim, F = m.ffn, V = m.vocab;
+  const int ab = m.dtype == ER_BF16 ? 2 : 4;
+  const int G1 = r.gamma_max + 1;
+  L->max_rows = std::max(r.max_batch * G1, r.prefill_chunk);
+  L->logit_rows = std::max(r.max_batch * G1, r.max_batch);
+  const long qkvN = (hq + 2 * hkv) * hd;
+  size_t dr = 0;
+  for (int l = 0; l < m.n_layers; ++l) {
+    dr += quant_bytes(dd, qkvN, d) + quant_bytes(dd, d, hq * hd) + quant_bytes(dd, 2 * F, d) + quant_bytes(dd, d, F);
+  }
+  if (dd.quant_lm_head) dr += quant_bytes(dd, V, d);
+  L->drafter = dr;
+  L->cs = align256((size_t)r.max_ctx * (hd / 2) * sizeof(float2));
+  const long R = L->max_rows;
+  L->h = align256((size_t)R * d * 4);
+  L->xbuf = align256((size_t)R * std::max(std::max(d, hq * hd), F) * ab);
+  L->qkv = align256((size_t)R * qkvN * 4);
+  L->qb = align256((size_t)R * hq * hd * ab);
+  L->gu = align256((size_t)R * 2 * F * 4);
+  L->lp = align256((size_t)L->logit_rows * V * 4);
+  L->lq = align256((size_t)r.max_batch * r.gamma_max * V * 4);
+  L->sp = align256((size_t)L->logit_rows * sizeof(RowStats));
+  L->sq = align256((size_t)r.max_batch * r.gamma_max * sizeof(RowStats));
+  L->out = align256((size_t)(L->max_rows + r.max_batch) * 4);
+  L->partial = align256((size_t)16 << 20) * 4;  // 16M floats
+  L->counters = align256((size_t)65536 * 4);
+  L->attn = align256((size_t)8 << 20) * 4;      // 8M floats
+  size_t w4 = 0;
+  if (dd.quant == ER_W4_G128_ASYM) {
+    w4 = std::max({(size_t)qkvN * d / 2, (size_t)d * hq * hd / 2, (size_t)2 * F * d / 2, (size_t)d * F / 2});
+    if (dd.quant_lm_head) w4 = std::max(w4, (size_t)V * d / 2);
+  }
+  L->w4tmp = align256(w4);
+  L->sink = 256;
+  L->meta = align256((size_t)64 << 20);
+  L->block_bytes = (size_t)m.n_layers * 2 * hkv * KV_BLOCK * hd * ab;
+  (void)why;
+  return 0;
+}
+
+int validate(const er_model_desc* m, const er_draft_desc* dd, const er_rollout_desc* r, std::string* why) {
+  auto bad = [&](const char* s) { *why = s; return ER_EINVAL; };
+  if (!m || !dd || !r) return bad("null description");
+  if (m->n_layers <= 0 || m->d_model <= 0 || m->n_q_heads <= 0 || m->n_kv_heads <= 0 || m->ffn <= 0 || m->vocab <= 0)
+    return bad("model sizes must be positive");
+  if (m->n_q_heads % m->n_kv_heads) return bad("n_q_heads must be a multiple of n_kv_heads");
+  if (m->head_dim != 64 && m->head_dim != 128) return bad("head_dim must be 64 or 128");
+  if (m->dtype != ER_F32 && m->dtype != ER_BF16) return bad("dtype must be ER_F32 or ER_BF16");
+  if (m->d_model % 8 || m->ffn % 8) return bad("d_model and ffn must be multiples of 8");
+  if (dd->quant != ER_W8_PERCH_SYM && dd->quant != ER_W4_G128_ASYM) return bad("unknown drafter format");
+  if (dd->quant == ER_W4_G128_ASYM) {
+    if (m->dtype != ER_BF16) return bad("W4 drafter needs a bf16 model");
+    if (dd->group_size != 128) return bad("W4 group_size must be 128");
+    if (m->d_model % 128 || m->ffn % 128 || (m->n_q_heads * m->head_dim) % 128)
+      return bad("W4 needs every input dimension to be a multiple of 128");
+  }
+  if (r->kv_block != KV_BLOCK) return bad("kv_block must be 16");
+  if (r->gamma_max < 1 || r->gamma_max > 16) return bad("gamma_max must be in 1..16");
+  if (r->gamma_min < 1 || r->gamma_min > r->gamma_max) return bad("gamma_min must be in 1..gamma_max");
+  if (r->gamma_init < 1 || r->gamma_init > r->gamma_max) return bad("gamma_init must be in 1..gamma_max");
+  if (r->max_seqs <= 0 || r->max_batch <= 0 || r->max_batch > r->max_seqs) return bad("bad max_seqs / max_batch");
+  if (r->max_ctx <= 0 || r->prefill_chunk <= 0) return bad("bad max_ctx / prefill_chunk");
+  if (!(r->temperature >= 0.f)) return bad("temperature must be >= 0");
+  if (!(r->top_p > 0.f)) return bad("top_p must be > 0");
+  if (r->policy < ER_POLICY_AUTO || r->policy > ER_POLICY_FORCE_AR) return bad("unknown policy");
+  const int grp = m->n_q_heads / m->n_kv_heads;
+  if (grp * (r->gamma_max + 1) > 64) return bad("(n_q_heads/n_kv_heads) * (gamma_max+1) must be <= 64");
+  return ER_OK;
+}
+
+// ---- forward ---------------------------------------------------------------
+struct Fwd {
+  bool draft = false;
+  int M = 0;
+  const int32_t* tokens = nullptr;
+  int tok_stride = 1;
+  const int32_t* pos = nullptr;
+  const int64_t* slot = nullptr;
+  const int32_t* bt = nullptr;
+  int bt_stride = 0;
+  const int32_t *it_bt = nullptr, *it_row0 = nullptr, *it_pos0 = nullptr, *it_cnt = nullptr;
+  int n_items = 0, max_q = 0, max_ctx = 0;
+  const int32_t* logit_rows = nullptr;  // rows whose logits are computed (with n_logit > 0)
+  int n_logit = -1;                      // -1: every row; 0: none (prefill chunk with no last token)
+  float* logits = nullptr;
+  long ldl = 0;
+};
+
+int lin(er_ctx* c, const void* x, int M, const LinearW& W, void* y, int ldy, int epi) {
+  const int ldx = W.K;
+  KC(c, launch_linear(x, c->bf16, ldx, M, W, y, ldy, epi, c->lws, c->lin_path, c->st));
+  return ER_OK;
+}
+
+int forward(er_ctx* c, const Fwd& f) {
+  const er_model_desc& m = c->md;
+  const int d = m.d_model, hq = m.n_q_heads, hkv = m.n_kv_heads, hd = m.head_dim, F = m.ffn;
+  const std::vector<Lin4>& W = f.draft ? c->drf : c->tgt;
+  KC(c, launch_embed(f.tokens, f.tok_stride, f.M, c->embed, c->bf16, d, c->h, c->st));
+  AttnArgs a{};
+  a.q = c->qb;
+  a.out = c->xbuf;
+  a.kv_pool = c->kv_pool;
+  a.block_table = f.bt;
+  a.bt_stride = f.bt_stride;
+  a.item_bt_row = f.it_bt;
+  a.item_q_row0 = f.it_row0;
+  a.item_q_pos0 = f.it_pos0;
+  a.item_q_count = f.it_cnt;
+  a.n_items = f.n_items;
+  a.max_q_count = f.max_q;
+  a.max_ctx = f.max_ctx;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.hd = hd;
+  a.n_layers = m.n_layers;
+  a.bf16 = c->bf16;
+  a.ws = c->attn_ws;
+  a.ws_floats = c->attn_ws_floats;
+  for (int l = 0; l < m.n_layers; ++l) {
+    KC(c, launch_rmsnorm(c->h, f.M, d, c->attn_norm[l], c->bf16, m.rms_eps, c->xbuf, nullptr, c->st));
+    int r = lin(c, c->xbuf, f.M, W[l].qkv, c->qkv, (hq + 2 * hkv) * hd, EPI_F32);
+    if (r) return r;
+    KC(c, launch_rope_kv(c->qkv, f.M, hq, hkv, hd, f.pos, f.slot, c->cs, c->qb, c->kv_pool, l, m.n_layers, c->bf16,
+                         c->st));
+    a.layer = l;
+    KC(c, launch_attention(a, c->st));
+    r = lin(c, c->xbuf, f.M, W[l].o, c->h, d, EPI_RESID);
+    if (r) return r;
+    KC(c, launch_rmsnorm(c->h, f.M, d, c->mlp_norm[l], c->bf16, m.rms_eps, c->xbuf, nullptr, c->st));
+    r = lin(c, c->xbuf, f.M, W[l].gu, c->gu, 2 * F, EPI_F32);
+    if (r) return r;
+    KC(c, launch_swiglu(c->gu, f.M, F, c->xbuf, c->bf16, c->st));
+    r = lin(c, c->xbuf, f.M, W[l].down, c->h, d, EPI_RESID);
+    if (r) return r;
+  }
+  const int nl = f.n_logit < 0 ? f.M : f.n_logit;
+  if (nl == 0) return ER_OK;
+  KC(c, launch_rmsnorm(c->h, nl, d, c->final_norm, c->bf16, m.rms_eps, c->xbuf, f.logit_rows, c->st));
+  const LinearW& lm = f.draft ? c->lm_d : c->lm_t;
+  return lin(c, c->xbuf, nl, lm, f.logits, (int)f.ldl, EPI_F32);
+}
+
+// ---- drafter build (A0) -----------------------------------------------------
+int quantize_into(er_ctx* c, const void* W, long N, long K, LinearW* out, char** cursor) {
+  out->N = (int)N;
+  out->K = (int)K;
+  if (c->dd.quant == ER_W8_PERCH_SYM) {
+    out->fmt = FMT_W8;
+    int8_t* q = (int8_t*)*cursor;
+    *cursor += align256((size_t)N * K);
+    float* s = (float*)*cursor;
+    *cursor += align256((size_t)N * 4);
+    KC(c, launch_quantize_w8(W, c->bf16, (int)N, (int)K, q, s, c->st));
+    out->w = q;
+    out->scale = s;
+    out->zero = nullptr;
+  } else {
+    out->fmt = FMT_W4;
+    const long G = K / 128;
+    uint8_t* p = (uint8_t*)*cursor;
+    *cursor += align256((size_t)N * K / 2);
+    uint16_t* s = (uint16_t*)*cursor;
+    *cursor += align256((size_t)N * G * 2);
+    uint8_t* z = (uint8_t*)*cursor;
+    *cursor += align256((size_t)N * G);
+    KC(c, launch_quantize_w4(W, (int)N, (int)K, c->w4_tmp, s, z, c->st));
+    KC(c, launch_w4_to_kernel_order(c->w4_tmp, (int)N, (int)K, p, c->st));
+    out->w = p;
+    out->scale = s;
+    out->zero = z;
+  }
+  return ER_OK;
+}
+
+int set_weights(er_ctx* c, const er_weights* w) {
+  const er_model_desc& m = c->md;
+  if (!w || !w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wqkv || !w->wo || !w->mlp_norm ||
+      !w->wgate_up || !w->wdown)
+    return fail(c, ER_EINVAL, "null weight pointer");
+  const long d = m.d_model, hq = m.n_q_heads, hkv = m.n_kv_heads, hd = m.head_dim, F = m.ffn, V = m.vocab;
+  const int tf = c->bf16 ? FMT_BF16 : FMT_F32;
+  c->embed = w->embed;
+  c->final_norm = w->final_norm;
+  c->attn_norm.assign(w->attn_norm, w->attn_norm + m.n_layers);
+  c->mlp_norm.assign(w->mlp_norm, w->mlp_norm + m.n_layers);
+  c->tgt.resize(m.n_layers);
+  c->drf.resize(m.n_layers);
+  for (int l = 0; l < m.n_layers; ++l) {
+    if (!w->attn_norm[l] || !w->wqkv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->wgate_up[l] || !w->wdown[l])
+      return fail(c, ER_EINVAL, "null weight pointer in layer %d", l);
+    c->tgt[l].qkv = LinearW{tf, w->wqkv[l], nullptr, nullptr, (int)((hq + 2 * hkv) * hd), (int)d};
+    c->tgt[l].o = LinearW{tf, w->wo[l], nullptr, nullptr, (int)d, (int)(hq * hd)};
+    c->tgt[l].gu = LinearW{tf, w->wgate_up[l], nullptr, nullptr, (int)(2 * F), (int)d};
+    c->tgt[l].down = LinearW{tf, w->wdown[l], nullptr, nullptr, (int)d, (int)F};
+  }
+  c->lm_t = LinearW{tf, w->lm_head, nullptr, nullptr, (int)V, (int)d};
+  char* cur = c->arena;  // the drafter pack sits at the start of the arena
+  for (int l = 0; l < m.n_layers; ++l) {
+    int r;
+    if ((r = quantize_into(c, c->tgt[l].qkv.w, c->tgt[l].qkv.N, d, &c->drf[l].qkv, &cur))) return r;
+    if ((r = quantize_into(c, c->tgt[l].o.w, d, hq * hd, &c->drf[l].o, &cur))) return r;
+    if ((r = quantize_into(c, c->tgt[l].gu.w, 2 * F, d, &c->drf[l].gu, &cur))) return r;
+    if ((r = quantize_into(c, c->tgt[l].down.w, d, F, &c->drf[l].down, &cur))) return r;
+  }
+  if (c->dd.quant_lm_head) {
+    int r;
+    if ((r = quantize_into(c, w->lm_head, V, d, &c->lm_d, &cur))) return r;
+  } else {
+    c->lm_d = c->lm_t;
+  }
+  HIPC(c, hipStreamSynchronize(c->st));
+  return ER_OK;
+}
+
+// ---- sequences --------------------------------------------------------------
+int check_batch(er_ctx* c, int n, const int32_t* ids, bool need_prefilled) {
+  if (n <= 0 || !ids) return fail(c, ER_EINVAL, "empty batch");
+  if (n > c->rd.max_batch) return fail(c, ER_EINVAL, "batch %d exceeds max_batch %d", n, c->rd.max_batch);
+  for (int i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= (int32_t)c->seqs.size() || !c->seqs[id].alive)
+      return fail(c, ER_EINVAL, "unknown sequence id %d", id);
+    const Seq& s = c->seqs[id];
+    if (need_prefilled && !s.prefilled) return fail(c, ER_ESTATE, "sequence %d not prefilled", id);
+    if (need_prefilled && s.finished) return fail(c, ER_ESTATE, "sequence %d already finished", id);
+    for (int j = 0; j < i; ++j)
+      if (ids[j] == id) return fail(c, ER_EINVAL, "sequence %d listed twice", id);
+  }
+  return ER_OK;
+}
+
+bool timed_step(er_ctx* c) {
+  if (!c->have_ev) return false;
+  if (c->step_count < c->timing_first) return true;
+  return c->timing_period > 0 && (c->step_count % c->timing_period) == 0;
+}
+
+float ev_ms(er_ctx* c, int a, int b) {
+  float ms = 0.f;
+  if (hipEventElapsedTime(&ms, c->ev[a], c->ev[b]) != hipSuccess) return 0.f;
+  return ms;
+}
+
+// Build the block table of a batch into the metadata region.
+int32_t* put_block_table(er_ctx* c, int n, const int32_t* ids, int* stride, size_t* off) {
+  size_t mx = 1;
+  for (int i = 0; i < n; ++i) mx = std::max(mx, c->seqs[ids[i]].bt.blocks.size());
+  *stride = (int)mx;
+  int32_t* bt = c->meta.push<int32_t>((size_t)n * mx, off);
+  if (!bt) return nullptr;
+  for (int i = 0; i < n; ++i) {
+    const auto& b = c->seqs[ids[i]].bt.blocks;
+    for (size_t j = 0; j < mx; ++j) bt[(size_t)i * mx + j] = j < b.size() ? b[j] : 0;
+  }
+  return bt;
+}
+
+int64_t slot_of(const Seq& s, int32_t pos) {
+  return (int64_t)s.bt.blocks[(size_t)(pos / KV_BLOCK)] * KV_BLOCK + (pos % KV_BLOCK);
+}
+
+void finish_seq(er_ctx* c, Seq& s) {
+  s.finished = true;
+  s.bt.release(c->pool);
+}
+
+int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_stride, int32_t* n_emitted,
+          er_step_info* info) {
+  const bool timed = timed_step(c);
+  std::vector<size_t> had(n);
+  for (int i = 0; i < n; ++i) {
+    Seq& s = c->seqs[ids[i]];
+    had[i] = s.bt.blocks.size();
+    if (!s.bt.reserve(c->pool, (int64_t)s.n + 1)) {
+      for (int j = 0; j < i; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)had[j] * KV_BLOCK);
+      return fail(c, ER_ENOMEM, "KV pool exhausted (%lld free blocks)", (long long)c->pool.free_count());
+    }
+  }
+  auto rollback = [&]() {
+    for (int j = 0; j < n; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)c->seqs[ids[j]].n);
+  };
+  Meta& M = c->meta;
+  M.reset();
+  size_t o_ids, o_tok, o_pos, o_spos, o_slot, o_bt, o_ib, o_ir, o_ip, o_ic;
+  int32_t* h_ids = M.push<int32_t>(n, &o_ids);
+  int32_t* h_tok = M.push<int32_t>(n, &o_tok);
+  int32_t* h_pos = M.push<int32_t>(n, &o_pos);
+  int32_t* h_spos = M.push<int32_t>(n, &o_spos);
+  int64_t* h_slot = M.push<int64_t>(n, &o_slot);
+  int stride = 0;
+  int32_t* h_bt = put_block_table(c, n, ids, &stride, &o_bt);
+  int32_t* h_ib = M.push<int32_t>(n, &o_ib);
+  int32_t* h_ir = M.push<int32_t>(n, &o_ir);
+  int32_t* h_ip = M.push<int32_t>(n, &o_ip);
+  int32_t* h_ic = M.push<int32_t>(n, &o_ic);
+  if (!M.ok || !h_bt) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
+  int max_ctx = 1;
+  for (int i = 0; i < n; ++i) {
+    const Seq& s = c->seqs[ids[i]];
+    h_ids[i] = ids[i];
+    h_tok[i] = s.pending;
+    h_pos[i] = s.n;
+    h_spos[i] = s.n + 1;
+    h_slot[i] = slot_of(s, s.n);
+    h_ib[i] = i;
+    h_ir[i] = i;
+    h_ip[i] = s.n;
+    h_ic[i] = 1;
+    max_ctx = std::max(max_ctx, s.n + 1);
+  }
+  auto run = [&]() -> int {
+    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
+    Fwd f;
+    f.draft = false;
+    f.M = n;
+    f.tokens = M.dev<int32_t>(o_tok);
+    f.pos = M.dev<int32_t>(o_pos);
+    f.slot = M.dev<int64_t>(o_slot);
+    f.bt = M.dev<int32_t>(o_bt);
+    f.bt_stride = stride;
+    f.it_bt = M.dev<int32_t>(o_ib);
+    f.it_row0 = M.dev<int32_t>(o_ir);
+    f.it_pos0 = M.dev<int32_t>(o_ip);
+    f.it_cnt = M.dev<int32_t>(o_ic);
+    f.n_items = n;
+    f.max_q = 1;
+    f.max_ctx = max_ctx;
+    f.logits = c->logits_p;
+    f.ldl = c->md.vocab;
+    int r = forward(c, f);
+    if (r) return r;
+    if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
+    KC(c, launch_row_stats(c->logits_p, n, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
+    KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.seed,
+                             M.dev<int32_t>(o_ids), M.dev<int32_t>(o_spos), 0, PURPOSE_AR, c->out_d, 1, nullptr,
+                             c->st));
+    if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
+    HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)n * 4, hipMemcpyDeviceToHost, c->st));
+    HIPC(c, hipStreamSynchronize(c->st));
+    return ER_OK;
+  };
+  const int r = run();
+  if (r) { rollback(); return r; }
+  // commit
+  int kept_tot = 0, fin = 0;
+  for (int i = 0; i < n; ++i) {
+    Seq& s = c->seqs[ids[i]];
+    const int32_t t = c->out_h[i];
+    s.n += 1;
+    s.pending = t;
+    s.generated += 1;
+    tokens_out[(size_t)i * out_stride] = t;
+    if (n_emitted) n_emitted[i] = 1;
+    ++kept_tot;
+    if (s.generated >= s.max_new) { finish_seq(c, s); ++fin; }
+  }
+  c->stats.ar_steps += 1;
+  c->stats.emitted += n;
+  c->stats.tokens_kept += kept_tot;
+  float ms_f = 0.f, ms_s = 0.f;
+  if (timed) {
+    ms_f = ev_ms(c, 0, 1);
+    ms_s = ev_ms(c, 1, 2);
+    c->stats.ms_ar += ms_f + ms_s;
+  }
+  c->last_mode = ER_MODE_AR;
+  c->last_gamma = 0;
+  c->last_B = n;
+  if (info) {
+    *info = er_step_info{};
+    info->mode = ER_MODE_AR;
+    info->gamma = 0;
+    info->batch = n;
+    info->emitted = n;
+    info->kept = kept_tot;
+    info->finished = fin;
+    info->alpha_ema = (float)c->alpha_ema;
+    info->ms_verify = ms_f;
+    info->ms_sample = ms_s;
+    info->ms_total = ms_f + ms_s;
+  }
+  ++c->step_count;
+  return ER_OK;
+}
+
+int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, int out_stride, int32_t* n_emitted,
+            er_step_info* info) {
+  const bool timed = timed_step(c);
+  const int G1 = g + 1;
+  const int V = c->md.vocab;
+  std::vector<size_t> had(n);
+  for (int i = 0; i < n; ++i) {
+    Seq& s = c->seqs[ids[i]];
+    had[i] = s.bt.blocks.size();
+    if (!s.bt.reserve(c->pool, (int64_t)s.n + G1)) {
+      for (int j = 0; j < i; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)had[j] * KV_BLOCK);
+      return fail(c, ER_ENOMEM, "KV pool exhausted (%lld free blocks)", (long long)c->pool.free_count());
+    }
+  }
+  auto rollback = [&]() {
+    for (int j = 0; j < n; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)c->seqs[ids[j]].n);
+  };
+  Meta& M = c->meta;
+  M.reset();
+  size_t o_ids, o_pos0, o_tok, o_bt;
+  int32_t* h_ids = M.push<int32_t>(n, &o_ids);
+  int32_t* h_pos0 = M.push<int32_t>(n, &o_pos0);
+  int32_t* h_tok = M.push<int32_t>((size_t)n * G1, &o_tok);
+  int stride = 0;
+  int32_t* h_bt = put_block_table(c, n, ids, &stride, &o_bt);
+  // per draft step j (1..g): positions, slots, items (bt row, q row0, pos0, count), sample positions
+  std::vector<size_t> o_dp(g), o_ds(g), o_dsp(g);
+  size_t o_ib, o_ir, o_ic, o_vp, o_vs, o_vir, o_vic;
+  std::vector<int32_t*> h_dp(g), h_dsp(g);
+  std::vector<int64_t*> h_ds(g);
+  for (int j = 0; j < g; ++j) {
+    h_dp[j] = M.push<int32_t>(n, &o_dp[j]);
+    h_ds[j] = M.push<int64_t>(n, &o_ds[j]);
+    h_dsp[j] = M.push<int32_t>(n, &o_dsp[j]);
+  }
+  int32_t* h_ib = M.push<int32_t>(n, &o_ib);   // item b -> block-table row b (draft and verify)
+  int32_t* h_ir = M.push<int32_t>(n, &o_ir);   // draft: q row b
+  int32_t* h_ic = M.push<int32_t>(n, &o_ic);   // draft: 1 query
+  int32_t* h_vp = M.push<int32_t>((size_t)n * G1, &o_vp);
+  int64_t* h_vs = M.push<int64_t>((size_t)n * G1, &o_vs);
+  int32_t* h_vir = M.push<int32_t>(n, &o_vir);  // verify: q row b*G1
+  int32_t* h_vic = M.push<int32_t>(n, &o_vic);  // verify: G1 queries
+  if (!M.ok || !h_bt) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
+  int max_ctx = 1;
+  for (int b = 0; b < n; ++b) {
+    const Seq& s = c->seqs[ids[b]];
+    h_ids[b] = ids[b];
+    h_pos0[b] = s.n;
+    h_tok[(size_t)b * G1] = s.pending;
+    for (int i = 1; i < G1; ++i) h_tok[(size_t)b * G1 + i] = 0;
+    for (int j = 0; j < g; ++j) {
+      h_dp[j][b] = s.n + j;
+      h_ds[j][b] = slot_of(s, s.n + j);
+      h_dsp[j][b] = s.n + j + 1;
+    }
+    h_ib[b] = b;
+    h_ir[b] = b;
+    h_ic[b] = 1;
+    for (int i = 0; i < G1; ++i) {
+      h_vp[(size_t)b * G1 + i] = s.n + i;
+      h_vs[(size_t)b * G1 + i] = slot_of(s, s.n + i);
+    }
+    h_vir[b] = b * G1;
+    h_vic[b] = G1;
+    max_ctx = std::max(max_ctx, s.n + G1);
+  }
+  auto run = [&]() -> int {
+    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
+    int32_t* d_tok = M.dev<int32_t>(o_tok);
+    for (int j = 0; j < g; ++j) {
+      Fwd f;
+      f.draft = true;
+      f.M = n;
+      f.tokens = d_tok + j;
+      f.tok_stride = G1;
+      f.pos = M.dev<int32_t>(o_dp[j]);
+      f.slot = M.dev<int64_t>(o_ds[j]);
+      f.bt = M.dev<int32_t>(o_bt);
+      f.bt_stride = stride;
+      f.it_bt = M.dev<int32_t>(o_ib);
+      f.it_row0 = M.dev<int32_t>(o_ir);
+      f.it_pos0 = M.dev<int32_t>(o_dp[j]);
+      f.it_cnt = M.dev<int32_t>(o_ic);
+      f.n_items = n;
+      f.max_q = 1;
+      f.max_ctx = max_ctx;
+      f.logits = c->logits_q + (size_t)j * n * V;
+      f.ldl = V;
+      int r = forward(c, f);
+      if (r) return r;
+      KC(c, launch_row_stats(f.logits, n, V, V, c->rd.temperature, c->rd.top_p, c->stats_q + (size_t)j * n, c->st));
+      KC(c, launch_sample_rows(f.logits, c->stats_q + (size_t)j * n, n, V, V, c->rd.temperature, c->rd.seed,
+                               M.dev<int32_t>(o_ids), M.dev<int32_t>(o_dsp[j]), j + 1, PURPOSE_DRAFT, d_tok + j + 1,
+                               G1, nullptr, c->st));
+    }
+    if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
+    Fwd f;
+    f.draft = false;
+    f.M = n * G1;
+    f.tokens = d_tok;
+    f.tok_stride = 1;
+    f.pos = M.dev<int32_t>(o_vp);
+    f.slot = M.dev<int64_t>(o_vs);
+    f.bt = M.dev<int32_t>(o_bt);
+    f.bt_stride = stride;
+    f.it_bt = M.dev<int32_t>(o_ib);
+    f.it_row0 = M.dev<int32_t>(o_vir);
+    f.it_pos0 = M.dev<int32_t>(o_pos0);
+    f.it_cnt = M.dev<int32_t>(o_vic);
+    f.n_items = n;
+    f.max_q = G1;
+    f.max_ctx = max_ctx;
+    f.logits = c->logits_p;
+    f.ldl = V;
+    int r = forward(c, f);
+    if (r) return r;
+    if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
+    KC(c, launch_row_stats(c->logits_p, n * G1, V, V, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
+    KC(c, launch_spec_decide(c->logits_p, c->stats_p, c->logits_q, c->stats_q, d_tok, n, g, V, c->rd.temperature,
+                             c->rd.seed, M.dev<int32_t>(o_ids), M.dev<int32_t>(o_pos0), c->out_d, c->out_d + n * G1,
+                             c->st));
+    if (timed) HIPC(c, hipEventRecord(c->ev[3], c->st));
+    HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)(n * G1 + n) * 4, hipMemcpyDeviceToHost, c->st));
+    HIPC(c, hipStreamSynchronize(c->st));
+    return ER_OK;
+  };
+  const int r = run();
+  if (r) { rollback(); return r; }
+  c->last_tok_off = o_tok;
+  // commit
+  AlphaAcc acc;
+  int acc_tot = 0, emit_tot = 0, kept_tot = 0, fin = 0;
+  const int32_t* out_tok = c->out_h;
+  const int32_t* nacc = c->out_h + n * G1;
+  for (int b = 0; b < n; ++b) {
+    Seq& s = c->seqs[ids[b]];
+    const int a = nacc[b];
+    const int em = a + 1;
+    const int room = s.max_new - s.generated;
+    const int kept = std::min(em, room);
+    for (int i = 0; i < kept; ++i) tokens_out[(size_t)b * out_stride + i] = out_tok[(size_t)b * G1 + i];
+    if (n_emitted) n_emitted[b] = kept;
+    s.generated += kept;
+    s.n += a + 1;
+    s.pending = out_tok[(size_t)b * G1 + a];
+    s.bt.truncate(c->pool, (int64_t)s.n);
+    acc.add(a, g);
+    acc_tot += a;
+    emit_tot += em;
+    kept_tot += kept;
+    c->stats.predict_times += 1;
+    if (a > 0) c->stats.effective_times += 1;
+    c->stats.total_right_length += a;
+    if (a == g) c->stats.bonus += 1;
+    if (s.generated >= s.max_new) { finish_seq(c, s); ++fin; }
+  }
+  const double a_step = acc.value();
+  c->alpha_ema = ema(c->alpha_ema, a_step, c->rd.ema_beta);
+  c->stats.sd_steps += 1;
+  c->stats.drafted += (int64_t)n * g;
+  c->stats.accepted += acc_tot;
+  c->stats.emitted += emit_tot;
+  c->stats.tokens_kept += kept_tot;
+  float md = 0.f, mv = 0.f, ms = 0.f;
+  if (timed) {
+    md = ev_ms(c, 0, 1);
+    mv = ev_ms(c, 1, 2);
+    ms = ev_ms(c, 2, 3);
+    c->stats.ms_draft += md;
+    c->stats.ms_verify += mv;
+    c->stats.ms_sample += ms;
+  }
+  c->last_mode = ER_MODE_SD;
+  c->last_gamma = g;
+  c->last_B = n;
+  if (info) {
+    *info = er_step_info{};
+    info->mode = ER_MODE_SD;
+    info->gamma = g;
+    info->batch = n;
+    info->accepted = acc_tot;
+    info->emitted = emit_tot;
+    info->kept = kept_tot;
+    info->finished = fin;
+    info->alpha_step = (float)a_step;
+    info->alpha_ema = (float)c->alpha_ema;
+    info->ms_draft = md;
+    info->ms_verify = mv;
+    info->ms_sample = ms;
+    info->ms_total = md + mv + ms;
+  }
+  ++c->step_count;
+  return ER_OK;
+}
+
+// Controller choice for this batch (0 = AR).
+int plan(er_ctx* c, int n, const int32_t* ids) {
+  if (c->policy == ER_POLICY_FORCE_AR) return 0;
+  double C = 0;
+  for (int i = 0; i < n; ++i) C += c->seqs[ids[i]].n;
+  C /= n;
+  const int lo = c->gamma_pinned ? c->gamma_pinned : c->rd.gamma_min;
+  const int hi = c->gamma_pinned ? c->gamma_pinned : c->rd.gamma_max;
+  const bool allow_ar = c->policy == ER_POLICY_AUTO;
+  const int cur = c->choice;
+  const int g = choose(c->cost, n, C, c->alpha_ema, lo, hi, allow_ar, cur, c->rd.switch_margin);
+  c->choice = g;
+  return g;
+}
+
+int current_gamma(er_ctx* c) {
+  if (c->gamma_pinned) return c->gamma_pinned;
+  if (c->choice > 0) return c->choice;
+  return c->rd.gamma_init;
+}
+
+// Roofline constants: streaming-read bandwidth over part of the KV pool, and
+// the per-forward overhead fitted from a target and a drafter forward at M = 1
+// (EfficientRollout "局限": the compute/memory boundary is calibrated per GPU).
+int calibrate(er_ctx* c) {
+  const er_model_desc& m = c->md;
+  c->cost.n_layers = m.n_layers;
+  c->cost.d_model = m.d_model;
+  c->cost.n_q_heads = m.n_q_heads;
+  c->cost.n_kv_heads = m.n_kv_heads;
+  c->cost.head_dim = m.head_dim;
+  c->cost.ffn = m.ffn;
+  c->cost.vocab = m.vocab;
+  c->cost.w_bytes = c->bf16 ? 2.0 : 4.0;
+  c->cost.q_bytes = c->dd.quant == ER_W8_PERCH_SYM ? 1.0 : 0.5 + 3.0 / 128.0;
+  c->cost.kv_bytes_el = c->bf16 ? 2.0 : 4.0;
+  c->cost.bw = c->rd.hbm_bytes_per_s > 0 ? c->rd.hbm_bytes_per_s : 0.0;
+  c->cost.flops = c->rd.flops_per_s > 0 ? c->rd.flops_per_s : 2.5e15;
+  c->cost.t_fwd = c->rd.t_fwd_s >= 0 ? c->rd.t_fwd_s : 0.0;
+  if (c->cost.bw <= 0) {
+    const size_t bytes = std::min((size_t)1 << 30, (size_t)c->pool.total() * c->block_bytes) & ~(size_t)4095;
+    if (bytes < ((size_t)64 << 20)) {
+      c->cost.bw = 8.0e12;
+    } else {
+      hipEvent_t a, b;
+      HIPC(c, hipEventCreate(&a));
+      HIPC(c, hipEventCreate(&b));
+      KC(c, launch_stream_read(c->kv_pool, bytes, c->sink, c->st));
+      HIPC(c, hipEventRecord(a, c->st));
+      for (int i = 0; i < 4; ++i) KC(c, launch_stream_read(c->kv_pool, bytes, c->sink, c->st));
+      HIPC(c, hipEventRecord(b, c->st));
+      HIPC(c, hipEventSynchronize(b));
+      float ms = 0.f;
+      HIPC(c, hipEventElapsedTime(&ms, a, b));
+      (void)hipEventDestroy(a);
+      (void)hipEventDestroy(b);
+      c->cost.bw = ms > 0 ? 4.0 * bytes / (ms * 1e-3) : 8.0e12;
+    }
+  }
+  if (c->rd.t_fwd_s < 0 && c->pool.free_count() >= 1) {
+    // one scratch block: run both forwards at position 0 of a throwaway sequence
+    BlockTable bt;
+    if (!bt.reserve(c->pool, 1)) return ER_OK;
+    Meta& M = c->meta;
+    M.reset();
+    size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ic;
+    int32_t* t = M.push<int32_t>(1, &o_tok);
+    int32_t* p = M.push<int32_t>(1, &o_pos);
+    int64_t* s = M.push<int64_t>(1, &o_slot);
+    int32_t* btp = M.push<int32_t>(1, &o_bt);
+    int32_t* ib = M.push<int32_t>(1, &o_ib);
+    int32_t* ir = M.push<int32_t>(1, &o_ir);
+    int32_t* ic = M.push<int32_t>(1, &o_ic);
+    *t = 0; *p = 0; *s = (int64_t)bt.blocks[0] * KV_BLOCK; *btp = bt.blocks[0]; *ib = 0; *ir = 0; *ic = 1;
+    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    Fwd f;
+    f.M = 1;
+    f.tokens = M.dev<int32_t>(o_tok);
+    f.pos = M.dev<int32_t>(o_pos);
+    f.slot = M.dev<int64_t>(o_slot);
+    f.bt = M.dev<int32_t>(o_bt);
+    f.bt_stride = 1;
+    f.it_bt = M.dev<int32_t>(o_ib);
+    f.it_row0 = M.dev<int32_t>(o_ir);
+    f.it_pos0 = M.dev<int32_t>(o_pos);
+    f.it_cnt = M.dev<int32_t>(o_ic);
+    f.n_items = 1;
+    f.max_q = 1;
+    f.max_ctx = 1;
+    f.logits = c->logits_p;
+    f.ldl = m.vocab;
+    float times[2] = {0, 0};
+    hipEvent_t a, b;
+    HIPC(c, hipEventCreate(&a));
+    HIPC(c, hipEventCreate(&b));
+    for (int which = 0; which < 2; ++which) {
+      f.draft = which == 1;
+      int r = forward(c, f);  // warm
+      if (r) { bt.release(c->pool); return r; }
+      HIPC(c, hipEventRecord(a, c->st));
+      for (int i = 0; i < 3; ++i) {
+        r = forward(c, f);
+        if (r) { bt.release(c->pool); return r; }
+      }
+      HIPC(c, hipEventRecord(b, c->st));
+      HIPC(c, hipEventSynchronize(b));
+      float ms = 0.f;
+      HIPC(c, hipEventElapsedTime(&ms, a, b));
+      times[which] = ms / 3.0f * 1e-3f;
+    }
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    bt.release(c->pool);
+    const double P = c->cost.p_lin();
+    const double tt = times[0] - c->cost.w_bytes * P / c->cost.bw;
+    const double td = times[1] - c->cost.q_bytes * P / c->cost.bw;
+    c->cost.t_fwd = std::max(0.0, 0.5 * (tt + td));
+  }
+  return ER_OK;
+}
+
+}  // namespace
+
+// =============================================================================
+// C ABI
+// =============================================================================
+extern "C" {
+
+int er_arena_bytes(const er_model_desc* model, const er_draft_desc* draft, const er_rollout_desc* rollout,
+                   int64_t kv_pool_blocks, size_t* bytes_out) {
+  try {
+    std::string why;
+    if (!bytes_out) return ER_EINVAL;
+    int r = validate(model, draft, rollout, &why);
+    if (r) return r;
+    Layout L;
+    make_layout(*model, *draft, *rollout, &L, &why);
+    *bytes_out = L.total_fixed() + (size_t)std::max<int64_t>(0, kv_pool_blocks) * L.block_bytes + 4096;
+    return ER_OK;
+  } catch (...) {
+    return ER_EINVAL;
+  }
+}
+
+int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_draft_desc* draft,
+                    const er_rollout_desc* rollout, void* dev_arena, size_t arena_bytes, void* hip_stream,
+                    er_ctx** out) {
+  if (!out) return ER_EINVAL;
+  *out = nullptr;
+  er_ctx* c = nullptr;
+  try {
+    c = new er_ctx();
+    std::string why;
+    int r = validate(model, draft, rollout, &why);
+    if (r) { c->err = why; *out = c; return r; }
+    if (!dev_arena) { *out = c; return fail(c, ER_EINVAL, "null arena"); }
+    c->md = *model;
+    c->dd = *draft;
+    c->rd = *rollout;
+    c->bf16 = model->dtype == ER_BF16;
+    c->act_bytes = c->bf16 ? 2 : 4;
+    c->st = (hipStream_t)hip_stream;
+    c->arena = (char*)dev_arena;
+    c->arena_bytes = arena_bytes;
+    c->policy = rollout->policy;
+    c->alpha_ema = rollout->alpha_init > 0 ? rollout->alpha_init : 0.8;
+    Layout L;
+    make_layout(*model, *draft, *rollout, &L, &why);
+    const size_t fixed = L.total_fixed() + 4096;
+    if (fixed > arena_bytes) {
+      *out = c;
+      return fail(c, ER_ENOMEM, "arena of %zu bytes is smaller than the %zu fixed bytes needed", arena_bytes, fixed);
+    }
+    // carve
+    char* cur = c->arena + L.drafter;  // drafter pack first (filled by set_weights)
+    auto take = [&](size_t n) { char* p = cur; cur += n; return p; };
+    c->cs = (float2*)take(L.cs);
+    c->h = (float*)take(L.h);
+    c->xbuf = take(L.xbuf);
+    c->qkv = (float*)take(L.qkv);
+    c->qb = take(L.qb);
+    c->gu = (float*)take(L.gu);
+    c->logits_p = (float*)take(L.lp);
+    c->logits_q = (float*)take(L.lq);
+    c->stats_p = (RowStats*)take(L.sp);
+    c->stats_q = (RowStats*)take(L.sq);
+    c->out_d = (int32_t*)take(L.out);
+    c->lws.partial = (float*)take(L.partial);
+    c->lws.partial_floats = L.partial / 4;
+    c->lws.counters = (int*)take(L.counters);
+    c->lws.n_counters = (int)(L.counters / 4);
+    c->attn_ws = (float*)take(L.attn);
+    c->attn_ws_floats = L.attn / 4;
+    c->w4_tmp = (uint8_t*)take(L.w4tmp);
+    c->w4_tmp_bytes = L.w4tmp;
+    c->sink = (uint32_t*)take(L.sink);
+    c->meta.d = take(L.meta);
+    c->meta.cap = L.meta;
+    c->max_rows = L.max_rows;
+    c->logit_rows = L.logit_rows;
+    c->block_bytes = L.block_bytes;
+    // KV pool: the rest of the arena (block aligned to 256 bytes)
+    char* kv0 = (char*)(((uintptr_t)cur + 255) & ~(uintptr_t)255);
+    const size_t left = (size_t)(c->arena + arena_bytes - kv0);
+    int64_t nblk = (int64_t)(left / L.block_bytes);
+    if (rollout->kv_pool_blocks > 0) {
+      if (rollout->kv_pool_blocks > nblk) {
+        *out = c;
+        return fail(c, ER_ENOMEM, "arena holds %lld KV blocks, %lld requested", (long long)nblk,
+                    (long long)rollout->kv_pool_blocks);
+      }
+      nblk = rollout->kv_pool_blocks;
+    }
+    if (nblk < 1) { *out = c; return fail(c, ER_ENOMEM, "no room for KV blocks"); }
+    c->kv_pool = kv0;
+    c->pool.init(nblk);
+    c->seqs.clear();
+    // host buffers
+    if (hipHostMalloc((void**)&c->meta.h, L.meta) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "hipHostMalloc"); }
+    if (hipHostMalloc((void**)&c->out_h, L.out) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "hipHostMalloc"); }
+    for (auto& e : c->ev) {
+      if (hipEventCreate(&e) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "hipEventCreate"); }
+    }
+    c->have_ev = true;
+    // counters start at zero
+    if (hipMemsetAsync(c->lws.counters, 0, L.counters, c->st) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "memset"); }
+    // RoPE table: cos/sin of pos * theta^(-2i/hd), fp64 on the host
+    {
+      const int half = model->head_dim / 2;
+      std::vector<float2> tab((size_t)rollout->max_ctx * half);
+      for (int p = 0; p < rollout->max_ctx; ++p)
+        for (int i = 0; i < half; ++i) {
+          const double inv = std::pow((double)model->rope_theta, -2.0 * i / model->head_dim);
+          const double ang = (double)p * inv;
+          tab[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        }
+      if (hipMemcpy(c->cs, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+        *out = c;
+        return fail(c, ER_EDEVICE, "upload RoPE table");
+      }
+    }
+    r = set_weights(c, w);
+    if (r) { *out = c; return r; }
+    r = calibrate(c);
+    if (r) { *out = c; return r; }
+    c->stats.alpha_ema = c->alpha_ema;
+    c->stats.gamma = rollout->gamma_init;
+    *out = c;
+    return ER_OK;
+  } catch (...) {
+    if (c) { *out = c; c->err = "internal error"; }
+    return ER_EINVAL;
+  }
+}
+
+int er_update_weights(er_ctx* c, const er_weights* w) {
+  if (!c) return ER_EINVAL;
+  try {
+    return set_weights(c, w);
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_kv_alloc(er_ctx* c, int n, const int32_t* prompt_lens, const int32_t* max_new, const int32_t* share_group,
+                int32_t* seq_ids_out) {
+  if (!c) return ER_EINVAL;
+  try {
+    if (n <= 0 || !prompt_lens || !max_new || !seq_ids_out) return fail(c, ER_EINVAL, "bad arguments");
+    if (c->alive + n > c->rd.max_seqs) return fail(c, ER_ENOMEM, "max_seqs %d exceeded", c->rd.max_seqs);
+    for (int i = 0; i < n; ++i) {
+      if (prompt_lens[i] < 1 || max_new[i] < 1) return fail(c, ER_EINVAL, "prompt_lens and max_new must be >= 1");
+      if ((int64_t)prompt_lens[i] + max_new[i] + c->rd.gamma_max + 1 > c->rd.max_ctx)
+        return fail(c, ER_EINVAL, "sequence of %d + %d tokens exceeds max_ctx %d", prompt_lens[i], max_new[i],
+                    c->rd.max_ctx);
+    }
+    // groups: the first member of a group in this call leads
+    const size_t base = c->seqs.size();
+    std::vector<Seq> add((size_t)n);
+    std::vector<int32_t> leader_of(n, -1);
+    for (int i = 0; i < n; ++i) {
+      Seq& s = add[(size_t)i];
+      s.alive = true;
+      s.prompt_len = prompt_lens[i];
+      s.max_new = max_new[i];
+      s.group = share_group ? share_group[i] : -1;
+      s.leader = true;
+      s.leader_id = (int32_t)(base + i);
+      if (s.group >= 0) {
+        for (int j = 0; j < i; ++j)
+          if (add[(size_t)j].group == s.group && add[(size_t)j].leader) {
+            if (prompt_lens[j] != prompt_lens[i]) return fail(c, ER_EINVAL, "group %d has unequal prompt lengths", s.group);
+            s.leader = false;
+            s.leader_id = (int32_t)(base + j);
+            leader_of[i] = j;
+            break;
+          }
+      }
+    }
+    // blocks: leaders/private reserve their prompt; members share full blocks
+    int i_ok = 0;
+    bool oom = false;
+    for (int i = 0; i < n && !oom; ++i) {
+      Seq& s = add[(size_t)i];
+      if (s.leader) {
+        if (!s.bt.reserve(c->pool, s.prompt_len)) oom = true;
+      } else {
+        const Seq& L = add[(size_t)leader_of[i]];
+        const int full = s.prompt_len / KV_BLOCK;
+        for (int b = 0; b < full; ++b) {
+          s.bt.blocks.push_back(L.bt.blocks[(size_t)b]);
+          c->pool.incref(L.bt.blocks[(size_t)b]);
+        }
+        if (!s.bt.reserve(c->pool, s.prompt_len)) oom = true;
+      }
+      if (!oom) i_ok = i + 1;
+    }
+    if (oom) {
+      for (int i = 0; i <= std::min(i_ok, n - 1); ++i) add[(size_t)i].bt.release(c->pool);
+      return fail(c, ER_ENOMEM, "KV pool exhausted while allocating prompts");
+    }
+    for (int i = 0; i < n; ++i) {
+      c->seqs.push_back(std::move(add[(size_t)i]));
+      seq_ids_out[i] = (int32_t)(base + i);
+    }
+    c->alive += n;
+    return ER_OK;
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, const int64_t* offsets,
+               int32_t* first_tok_out) {
+  if (!c) return ER_EINVAL;
+  try {
+    if (n <= 0 || !ids || !tokens || !offsets || !first_tok_out) return fail(c, ER_EINVAL, "bad arguments");
+    if (n > c->logit_rows) return fail(c, ER_EINVAL, "at most %d sequences per prefill call", c->logit_rows);
+    for (int i = 0; i < n; ++i) {
+      const int32_t id = ids[i];
+      if (id < 0 || id >= (int32_t)c->seqs.size() || !c->seqs[id].alive) return fail(c, ER_EINVAL, "unknown sequence %d", id);
+      const Seq& s = c->seqs[id];
+      if (s.prefilled) return fail(c, ER_ESTATE, "sequence %d already prefilled", id);
+      if (offsets[i + 1] - offsets[i] != s.prompt_len)
+        return fail(c, ER_EINVAL, "sequence %d: %lld tokens given, prompt_len %d", id,
+                    (long long)(offsets[i + 1] - offsets[i]), s.prompt_len);
+      for (int64_t k = offsets[i]; k < offsets[i + 1]; ++k)
+        if (tokens[k] < 0 || tokens[k] >= c->md.vocab) return fail(c, ER_EINVAL, "token out of range");
+      for (int j = 0; j < i; ++j)
+        if (ids[j] == id) return fail(c, ER_EINVAL, "sequence %d listed twice", id);
+      if (!s.leader) {
+        bool found = false;
+        for (int j = 0; j < n; ++j) found |= ids[j] == s.leader_id;
+        if (!found && !c->seqs[s.leader_id].prefilled)
+          return fail(c, ER_ESTATE, "sequence %d shares the prompt of %d, which is not prefilled", id, s.leader_id);
+      }
+    }
+    const int grp = c->md.n_q_heads / c->md.n_kv_heads;
+    const int qmax = std::max(1, 64 / grp);
+    const int V = c->md.vocab;
+    // computing sequences: leaders and private ones in this call
+    std::vector<int> comp;
+    for (int i = 0; i < n; ++i)
+      if (c->seqs[ids[i]].leader) comp.push_back(i);
+    // logits row of each computing sequence once its last token is processed
+    std::vector<int32_t> row_of_call(n, -1);
+    int next_row = 0;
+    size_t ci = 0;
+    int64_t done_in_seq = 0;
+    while (ci < comp.size()) {
+      // pack one chunk
+      struct Seg { int call_i; int32_t p0; int32_t cnt; };
+      std::vector<Seg> segs;
+      int rows = 0;
+      while (ci < comp.size() && rows < c->rd.prefill_chunk) {
+        const int i = comp[ci];
+        const Seq& s = c->seqs[ids[i]];
+        const int32_t take = (int32_t)std::min<int64_t>(s.prompt_len - done_in_seq, c->rd.prefill_chunk - rows);
+        segs.push_back(Seg{i, (int32_t)done_in_seq, take});
+        rows += take;
+        done_in_seq += take;
+        if (done_in_seq == s.prompt_len) { ++ci; done_in_seq = 0; }
+      }
+      Meta& M = c->meta;
+      M.reset();
+      std::vector<int32_t> cids;
+      for (auto& sg : segs) cids.push_back(ids[sg.call_i]);
+      size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ip, o_ic, o_lr;
+      int32_t* h_tok = M.push<int32_t>(rows, &o_tok);
+      int32_t* h_pos = M.push<int32_t>(rows, &o_pos);
+      int64_t* h_slot = M.push<int64_t>(rows, &o_slot);
+      int stride = 0;
+      int32_t* h_bt = put_block_table(c, (int)cids.size(), cids.data(), &stride, &o_bt);
+      int n_items = 0;
+      for (auto& sg : segs) n_items += (sg.cnt + qmax - 1) / qmax;
+      int32_t* h_ib = M.push<int32_t>(n_items, &o_ib);
+      int32_t* h_ir = M.push<int32_t>(n_items, &o_ir);
+      int32_t* h_ip = M.push<int32_t>(n_items, &o_ip);
+      int32_t* h_ic = M.push<int32_t>(n_items, &o_ic);
+      int32_t* h_lr = M.push<int32_t>(segs.size(), &o_lr);
+      if (!M.ok || !h_bt) return fail(c, ER_ENOMEM, "metadata region too small for a prefill chunk");
+      int row = 0, it = 0, nl = 0, max_ctx = 1;
+      std::vector<int> finishing;
+      for (size_t k = 0; k < segs.size(); ++k) {
+        const Seg& sg = segs[k];
+        const Seq& s = c->seqs[ids[sg.call_i]];
+        const int32_t* tk = tokens + offsets[sg.call_i];
+        for (int32_t q = 0; q < sg.cnt; ++q) {
+          const int32_t p = sg.p0 + q;
+          h_tok[row + q] = tk[p];
+          h_pos[row + q] = p;
+          h_slot[row + q] = slot_of(s, p);
+        }
+        for (int32_t q = 0; q < sg.cnt; q += qmax) {
+          h_ib[it] = (int32_t)k;
+          h_ir[it] = row + q;
+          h_ip[it] = sg.p0 + q;
+          h_ic[it] = std::min(qmax, sg.cnt - q);
+          ++it;
+        }
+        max_ctx = std::max(max_ctx, sg.p0 + sg.cnt);
+        if (sg.p0 + sg.cnt == s.prompt_len) {
+          h_lr[nl++] = row + sg.cnt - 1;
+          finishing.push_back(sg.call_i);
+        }
+        row += sg.cnt;
+      }
+      HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+      Fwd f;
+      f.M = rows;
+      f.tokens = M.dev<int32_t>(o_tok);
+      f.pos = M.dev<int32_t>(o_pos);
+      f.slot = M.dev<int64_t>(o_slot);
+      f.bt = M.dev<int32_t>(o_bt);
+      f.bt_stride = stride;
+      f.it_bt = M.dev<int32_t>(o_ib);
+      f.it_row0 = M.dev<int32_t>(o_ir);
+      f.it_pos0 = M.dev<int32_t>(o_ip);
+      f.it_cnt = M.dev<int32_t>(o_ic);
+      f.n_items = n_items;
+      f.max_q = qmax;
+      f.max_ctx = max_ctx;
+      f.logit_rows = M.dev<int32_t>(o_lr);
+      f.n_logit = nl;
+      f.logits = c->logits_p + (size_t)next_row * V;
+      f.ldl = V;
+      {
+        int r = forward(c, f);  // nl == 0: the layers still run (they write the KV)
+        if (r) return r;
+      }
+      for (size_t k = 0; k < finishing.size(); ++k) row_of_call[finishing[k]] = next_row + (int)k;
+      next_row += nl;
+    }
+    // shared members: copy the leader's partial tail block, reuse its logits row
+    for (int i = 0; i < n; ++i) {
+      Seq& s = c->seqs[ids[i]];
+      if (s.leader) continue;
+      int li = -1;
+      for (int j = 0; j < n; ++j)
+        if (ids[j] == s.leader_id) li = j;
+      if (li < 0) return fail(c, ER_ESTATE, "leader of sequence %d must be prefilled in the same call", ids[i]);
+      row_of_call[i] = row_of_call[li];
+      if (s.prompt_len % KV_BLOCK) {
+        const Seq& L = c->seqs[s.leader_id];
+        const size_t b = (size_t)(s.prompt_len / KV_BLOCK);
+        HIPC(c, hipMemcpyAsync((char*)c->kv_pool + (size_t)s.bt.blocks[b] * c->block_bytes,
+                               (char*)c->kv_pool + (size_t)L.bt.blocks[b] * c->block_bytes, c->block_bytes,
+                               hipMemcpyDeviceToDevice, c->st));
+      }
+    }
+    // first tokens: AR draws at position prompt_len
+    Meta& M = c->meta;
+    M.reset();
+    size_t o_ids, o_pos, o_map;
+    int32_t* h_ids = M.push<int32_t>(n, &o_ids);
+    int32_t* h_pos = M.push<int32_t>(n, &o_pos);
+    int32_t* h_map = M.push<int32_t>(n, &o_map);
+    for (int i = 0; i < n; ++i) {
+      h_ids[i] = ids[i];
+      h_pos[i] = c->seqs[ids[i]].prompt_len;
+      h_map[i] = row_of_call[i];
+    }
+    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    KC(c, launch_row_stats(c->logits_p, next_row, V, V, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
+    KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, V, V, c->rd.temperature, c->rd.seed, M.dev<int32_t>(o_ids),
+                             M.dev<int32_t>(o_pos), 0, PURPOSE_AR, c->out_d, 1, M.dev<int32_t>(o_map), c->st));
+    HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)n * 4, hipMemcpyDeviceToHost, c->st));
+    HIPC(c, hipStreamSynchronize(c->st));
+    c->last_prefill_row.assign(row_of_call.begin(), row_of_call.end());
+    c->last_mode = 2;
+    c->last_B = n;
+    for (int i = 0; i < n; ++i) {
+      Seq& s = c->seqs[ids[i]];
+      s.prefilled = true;
+      s.n = s.prompt_len;
+      s.pending = c->out_h[i];
+      s.generated = 1;
+      first_tok_out[i] = c->out_h[i];
+      c->stats.tokens_kept += 1;
+      if (s.generated >= s.max_new) finish_seq(c, s);
+    }
+    return ER_OK;
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_spec_step(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int32_t* n_emitted_out,
+                 er_step_info* info) {
+  if (!c) return ER_EINVAL;
+  try {
+    int r = check_batch(c, n, ids, true);
+    if (r) return r;
+    if (!tokens_out || !n_emitted_out) return fail(c, ER_EINVAL, "null output");
+    return do_spec(c, n, ids, current_gamma(c), tokens_out, c->rd.gamma_max + 1, n_emitted_out, info);
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_ar_step(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, er_step_info* info) {
+  if (!c) return ER_EINVAL;
+  try {
+    int r = check_batch(c, n, ids, true);
+    if (r) return r;
+    if (!tokens_out) return fail(c, ER_EINVAL, "null output");
+    return do_ar(c, n, ids, tokens_out, 1, nullptr, info);
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_step(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int32_t* n_emitted_out, er_step_info* info) {
+  if (!c) return ER_EINVAL;
+  try {
+    int r = check_batch(c, n, ids, true);
+    if (r) return r;
+    if (!tokens_out || !n_emitted_out) return fail(c, ER_EINVAL, "null output");
+    const int g = plan(c, n, ids);
+    const int stride = c->rd.gamma_max + 1;
+    if (g == 0) return do_ar(c, n, ids, tokens_out, stride, n_emitted_out, info);
+    return do_spec(c, n, ids, g, tokens_out, stride, n_emitted_out, info);
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_rollout(er_ctx* c, int n, const int32_t* ids, int32_t cap, int32_t* out_tokens, int32_t* out_len,
+               er_stats* stats_out) {
+  if (!c) return ER_EINVAL;
+  try {
+    if (n <= 0 || !ids || !out_tokens || !out_len || cap <= 0) return fail(c, ER_EINVAL, "bad arguments");
+    if (n > c->rd.max_batch) return fail(c, ER_EINVAL, "batch %d exceeds max_batch %d", n, c->rd.max_batch);
+    for (int i = 0; i < n; ++i) {
+      const int32_t id = ids[i];
+      if (id < 0 || id >= (int32_t)c->seqs.size() || !c->seqs[id].alive) return fail(c, ER_EINVAL, "unknown sequence %d", id);
+      const Seq& s = c->seqs[id];
+      if (!s.prefilled) return fail(c, ER_ESTATE, "sequence %d not prefilled", id);
+      if (s.max_new > cap) return fail(c, ER_EINVAL, "max_new of %d exceeds cap", id);
+      out_len[i] = 0;
+    }
+    // the prefill token (and any generated since) is not retrievable here;
+    // the loop records what it generates after the current state.
+    std::vector<int32_t> act, slot;
+    for (int i = 0; i < n; ++i)
+      if (!c->seqs[ids[i]].finished) { act.push_back(ids[i]); slot.push_back(i); }
+    const int stride = c->rd.gamma_max + 1;
+    std::vector<int32_t> tok((size_t)n * stride), ne(n);
+    while (!act.empty()) {
+      const int B = (int)act.size();
+      int r = er_step(c, B, act.data(), tok.data(), ne.data(), nullptr);
+      if (r) return r;
+      std::vector<int32_t> act2, slot2;
+      for (int b = 0; b < B; ++b) {
+        const int i = slot[b];
+        for (int k = 0; k < ne[b]; ++k) out_tokens[(size_t)i * cap + out_len[i] + k] = tok[(size_t)b * stride + k];
+        out_len[i] += ne[b];
+        if (!c->seqs[act[b]].finished) { act2.push_back(act[b]); slot2.push_back(i); }
+      }
+      act.swap(act2);
+      slot.swap(slot2);
+    }
+    if (stats_out) return er_get_stats(c, stats_out);
+    return ER_OK;
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_set_gamma(er_ctx* c, int gamma) {
+  if (!c) return ER_EINVAL;
+  if (gamma < 0 || gamma > c->rd.gamma_max) return fail(c, ER_EINVAL, "gamma %d outside 0..%d", gamma, c->rd.gamma_max);
+  c->gamma_pinned = gamma;
+  if (gamma > 0 && c->choice > 0) c->choice = gamma;
+  return ER_OK;
+}
+
+int er_set_policy(er_ctx* c, int policy) {
+  if (!c) return ER_EINVAL;
+  if (policy < ER_POLICY_AUTO || policy > ER_POLICY_FORCE_AR) return fail(c, ER_EINVAL, "unknown policy %d", policy);
+  c->policy = policy;
+  c->choice = -1;
+  return ER_OK;
+}
+
+int er_kv_free(er_ctx* c, int n, const int32_t* ids) {
+  if (!c) return ER_EINVAL;
+  if (n < 0 || (n > 0 && !ids)) return fail(c, ER_EINVAL, "bad arguments");
+  for (int i = 0; i < n; ++i) {
+    const int32_t id = ids[i];
+    if (id < 0 || id >= (int32_t)c->seqs.size() || !c->seqs[id].alive) return fail(c, ER_EINVAL, "unknown sequence %d", id);
+  }
+  for (int i = 0; i < n; ++i) {
+    Seq& s = c->seqs[ids[i]];
+    s.bt.release(c->pool);
+    s.alive = false;
+    --c->alive;
+  }
+  return ER_OK;
+}
+
+int er_seq_info(er_ctx* c, int32_t id, int32_t* generated, int32_t* context_len, int32_t* finished) {
+  if (!c) return ER_EINVAL;
+  if (id < 0 || id >= (int32_t)c->seqs.size() || !c->seqs[id].alive) return fail(c, ER_EINVAL, "unknown sequence %d", id);
+  const Seq& s = c->seqs[id];
+  if (generated) *generated = s.generated;
+  if (context_len) *context_len = s.n;
+  if (finished) *finished = s.finished ? 1 : 0;
+  return ER_OK;
+}
+
+int er_get_stats(er_ctx* c, er_stats* out) {
+  if (!c || !out) return ER_EINVAL;
+  er_stats s = c->stats;
+  s.effective_length = s.effective_times ? (double)s.total_right_length / (double)s.effective_times : 0.0;
+  s.effective_percent = s.predict_times ? (double)s.effective_times / (double)s.predict_times : 0.0;
+  s.alpha_ema = c->alpha_ema;
+  s.gamma = c->choice < 0 ? current_gamma(c) : c->choice;
+  s.mode = c->choice == 0 ? ER_MODE_AR : ER_MODE_SD;
+  *out = s;
+  return ER_OK;
+}
+
+int er_reset_stats(er_ctx* c) {
+  if (!c) return ER_EINVAL;
+  c->stats = er_stats{};
+  return ER_OK;
+}
+
+int er_set_timing(er_ctx* c, int period, int first_n) {
+  if (!c || period < 0 || first_n < 0) return ER_EINVAL;
+  c->timing_period = period;
+  c->timing_first = first_n;
+  c->step_count = 0;
+  return ER_OK;
+}
+
+int er_kv_free_blocks(er_ctx* c, int64_t* free_blocks, int64_t* total_blocks) {
+  if (!c) return ER_EINVAL;
+  if (free_blocks) *free_blocks = c->pool.free_count();
+  if (total_blocks) *total_blocks = c->pool.total();
+  return ER_OK;
+}
+
+int er_debug_logits(er_ctx* c, int which, int slot, float* host_out, int32_t* rows_out) {
+  if (!c) return ER_EINVAL;
+  const int V = c->md.vocab;
+  if (slot < 0 || slot >= c->last_B) return fail(c, ER_EINVAL, "slot %d outside the last batch", slot);
+  std::vector<const float*> rows;
+  if (which == 0) {
+    if (c->last_mode != ER_MODE_SD) return fail(c, ER_ESTATE, "last step was not speculative");
+    for (int j = 0; j < c->last_gamma; ++j) rows.push_back(c->logits_q + ((size_t)j * c->last_B + slot) * V);
+  } else if (which == 1) {
+    if (c->last_mode == ER_MODE_SD) {
+      for (int i = 0; i <= c->last_gamma; ++i) rows.push_back(c->logits_p + ((size_t)slot * (c->last_gamma + 1) + i) * V);
+    } else if (c->last_mode == ER_MODE_AR) {
+      rows.push_back(c->logits_p + (size_t)slot * V);
+    } else if (c->last_mode == 2) {
+      rows.push_back(c->logits_p + (size_t)c->last_prefill_row[(size_t)slot] * V);
+    } else {
+      return fail(c, ER_ESTATE, "no step yet");
+    }
+  } else {
+    return fail(c, ER_EINVAL, "which must be 0 or 1");
+  }
+  if (rows_out) *rows_out = (int32_t)rows.size();
+  if (!host_out) return ER_OK;
+  for (size_t i = 0; i < rows.size(); ++i)
+    HIPC(c, hipMemcpy(host_out + i * V, rows[i], (size_t)V * 4, hipMemcpyDeviceToHost));
+  return ER_OK;
+}
+
+int er_debug_drafts(er_ctx* c, int32_t* host_out) {
+  if (!c || !host_out) return ER_EINVAL;
+  if (c->last_mode != ER_MODE_SD) return fail(c, ER_ESTATE, "last step was not speculative");
+  const int G1 = c->last_gamma + 1;
+  std::vector<int32_t> tok((size_t)c->last_B * G1);
+  HIPC(c, hipMemcpy(tok.data(), c->meta.d + c->last_tok_off, tok.size() * 4, hipMemcpyDeviceToHost));
+  for (int b = 0; b < c->last_B; ++b)
+    for (int j = 0; j < c->last_gamma; ++j) host_out[(size_t)b * c->last_gamma + j] = tok[(size_t)b * G1 + 1 + j];
+  return ER_OK;
+}
+
+int er_controller_choose(const er_cost_model* m, int batch, double mean_ctx, double alpha, int gamma_min,
+                         int gamma_max, int current, double margin, int* gamma_out) {
+  if (!m || !gamma_out || batch <= 0 || gamma_min < 1 || gamma_max < gamma_min) return ER_EINVAL;
+  CostModel cm{m->n_layers, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, m->ffn, m->vocab,
+               m->w_bytes, m->q_bytes, m->kv_bytes_el, m->hbm_bytes_per_s, m->flops_per_s, m->t_fwd_s};
+  *gamma_out = choose(cm, batch, mean_ctx, alpha, gamma_min, gamma_max, true, current, margin);
+  return ER_OK;
+}
+
+double er_expected_tokens(double alpha, int gamma) { return expected_tokens(alpha, gamma); }
+
+const char* er_last_error(const er_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+void er_destroy(er_ctx* c) {
+  if (!c) return;
+  if (c->st) (void)hipStreamSynchronize(c->st);
+  else (void)hipDeviceSynchronize();
+  if (c->meta.h) (void)hipHostFree(c->meta.h);
+  if (c->out_h) (void)hipHostFree(c->out_h);
+  if (c->have_ev)
+    for (auto& e : c->ev) (void)hipEventDestroy(e);
+  delete c;
+}
+
+}  // extern "C"

@@ -1,0 +1,296 @@
+"""Kernel-level parity: each gfx950 kernel (through the er_op_* C ABI) against the oracle.
+
+Inputs are seeded and synthetic; expected values come only from oracle/.
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from oracle import philox as OP  # noqa: E402
+from oracle import quant as OQ  # noqa: E402
+from oracle import sampling as OS  # noqa: E402
+from oracle import spec as OSP  # noqa: E402
+from oracle.numerics import round_bf16  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from speculative_decoding_rl_amd import ops as _ops
+    from speculative_decoding_rl_amd import _lib
+    _lib.load()
+    return _ops
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+# ---------------------------------------------------------------------------
+def test_philox_bit_exact(ops):
+    rng = np.random.Generator(np.random.PCG64(0))
+    n = 4096
+    ctr = rng.integers(0, 2**32, size=(n, 4), dtype=np.uint64).astype(np.uint32)
+    ctr[:4] = [[0, 0, 0, 0], [2**32 - 1] * 4, [1, 2, 3, 4], [7, 0, 9, 1]]
+    for seed in (0, 1, 0xDEADBEEF12345678, 2**64 - 1):
+        u = torch.zeros(n, dtype=torch.float64, device="cuda")
+        ops.philox_uniform(seed, dev(ctr.view(np.int32)), u)
+        torch.cuda.synchronize()
+        want = OP.uniform(seed, ctr[:, 0].astype(np.uint64), ctr[:, 1].astype(np.uint64),
+                          ctr[:, 2].astype(np.uint64), ctr[:, 3].astype(np.uint64))
+        assert np.array_equal(u.cpu().numpy(), want)
+
+
+# ---------------------------------------------------------------------------
+def _bf16_weights(N, K, seed, std=0.02):
+    g = torch.Generator().manual_seed(seed)
+    w = (torch.randn(N, K, generator=g) * std).to(torch.bfloat16)
+    return w
+
+
+@pytest.mark.parametrize("N,K", [(37, 128), (64, 3584), (300, 384)])
+def test_quantize_w4_bit_exact(ops, N, K):
+    w = _bf16_weights(N, K, N + K)
+    w[0] = 0.0                      # all-zero row
+    w[1, :128] = 0.0                # all-zero group
+    w[2, 5] = 0.5                   # outlier
+    w[3, :] = w[3, :].abs()         # all-positive row (lo = 0)
+    G = K // 128
+    codes = torch.zeros(N, K // 2, dtype=torch.uint8, device="cuda")
+    scale = torch.zeros(N, G, dtype=torch.bfloat16, device="cuda")
+    zero = torch.zeros(N, G, dtype=torch.uint8, device="cuda")
+    ops.quantize("w4", w.cuda(), codes, scale, zero)
+    torch.cuda.synchronize()
+    c, s, z = OQ.quantize_w4(w.float().numpy().astype(np.float64))
+    assert np.array_equal(codes.cpu().numpy(), OQ.pack_w4(c))
+    assert np.array_equal(scale.float().cpu().numpy().astype(np.float64), s)
+    assert np.array_equal(zero.cpu().numpy(), z)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_w8_bit_exact(ops, dtype):
+    N, K = 129, 688
+    g = torch.Generator().manual_seed(7)
+    w = torch.randn(N, K, generator=g) * 0.02
+    w[0] = 0
+    w = w.to(torch.bfloat16) if dtype == "bf16" else w
+    codes = torch.zeros(N, K, dtype=torch.int8, device="cuda")
+    scale = torch.zeros(N, dtype=torch.float32, device="cuda")
+    ops.quantize("w8", w.cuda(), codes, scale)
+    torch.cuda.synchronize()
+    q, s = OQ.quantize_w8(w.float().numpy().astype(np.float64))
+    assert np.array_equal(codes.cpu().numpy(), q)
+    assert np.array_equal(scale.cpu().numpy().astype(np.float64), s)
+
+
+# ---------------------------------------------------------------------------
+def _linear_case(ops, fmt, M, N, K, path, seed=0):
+    from speculative_decoding_rl_amd import _lib
+    g = torch.Generator().manual_seed(seed)
+    act_bf16 = fmt != "f32"
+    x = torch.randn(M, K, generator=g)
+    x = x.to(torch.bfloat16) if act_bf16 else x
+    xd = x.float().numpy().astype(np.float64)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    if fmt in ("f32", "bf16"):
+        w = torch.randn(N, K, generator=g) * 0.02
+        w = w.to(torch.bfloat16) if fmt == "bf16" else w
+        wd = w.float().numpy().astype(np.float64)
+        ops.linear(x.cuda(), _lib.ER_FMT_BF16 if fmt == "bf16" else _lib.ER_FMT_F32, w.cuda(), N, K, y, path=path)
+    elif fmt == "w8":
+        w = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16)
+        codes = torch.zeros(N, K, dtype=torch.int8, device="cuda")
+        scale = torch.zeros(N, dtype=torch.float32, device="cuda")
+        ops.quantize("w8", w.cuda(), codes, scale)
+        q, s = OQ.quantize_w8(w.float().numpy().astype(np.float64))
+        wd = OQ.dequantize_w8(q, s)
+        ops.linear(x.cuda(), _lib.ER_FMT_W8, codes, N, K, y, scale=scale, path=path)
+    else:
+        w = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16)
+        canon = torch.zeros(N, K // 2, dtype=torch.uint8, device="cuda")
+        kord = torch.zeros_like(canon)
+        scale = torch.zeros(N, K // 128, dtype=torch.bfloat16, device="cuda")
+        zero = torch.zeros(N, K // 128, dtype=torch.uint8, device="cuda")
+        ops.quantize("w4", w.cuda(), canon, scale, zero)
+        ops.w4_kernel_order(canon, N, K, kord)
+        c, s, z = OQ.quantize_w4(w.float().numpy().astype(np.float64))
+        wd = OQ.dequantize_w4(c, s, z)
+        ops.linear(x.cuda(), _lib.ER_FMT_W4, kord, N, K, y, scale=scale, zero=zero, path=path)
+    torch.cuda.synchronize()
+    ref = xd @ wd.T
+    got = y.cpu().numpy().astype(np.float64)
+    # fp32 accumulation over K terms: error bounded by a small multiple of eps * sum|x||w|
+    bound = np.abs(xd) @ np.abs(wd).T
+    err = np.abs(got - ref)
+    assert np.all(np.isfinite(got))
+    return float(np.max(err / (bound + 1e-30)))
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "w8", "w4"])
+@pytest.mark.parametrize("M", [1, 5, 16, 33, 70])
+@pytest.mark.parametrize("path", [1, 2])
+def test_linear_bf16_paths(ops, fmt, M, path):
+    # N ragged (not a multiple of the 64/128 tiles), K spans several chunks and split-K
+    r = _linear_case(ops, fmt, M, 200, 1152, path, seed=M)
+    assert r < 4e-6, r
+
+
+@pytest.mark.parametrize("fmt", ["f32", "w8"])
+def test_linear_fp32_activations(ops, fmt):
+    r = _linear_case(ops, fmt, 7, 300, 688, 0, seed=3)
+    assert r < 4e-6, r
+
+
+def test_linear_wide_and_deep(ops):
+    # lm_head-like width (wide tiles) and ffn-like depth (many split-K chunks)
+    assert _linear_case(ops, "w4", 3, 8192, 256, 2, seed=1) < 4e-6
+    assert _linear_case(ops, "bf16", 9, 96, 18944, 2, seed=2) < 4e-6
+
+
+# ---------------------------------------------------------------------------
+def _attn_case(ops, bf16, hq, hkv, hd, items, L=2, layer=1, seed=0):
+    """items: list of (ctx_len_before, q_count) per sequence."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    max_pos = max(c + q for c, q in items)
+    nblk_seq = [(c + q + 15) // 16 for c, q in items]
+    total_blocks = sum(nblk_seq) + 3
+    perm = rng.permutation(total_blocks)
+    bt = np.zeros((len(items), max(nblk_seq)), dtype=np.int32)
+    k = 0
+    for i, nb in enumerate(nblk_seq):
+        bt[i, :nb] = perm[k:k + nb]
+        k += nb
+    pool = rng.standard_normal((total_blocks, L, 2, hkv, 16, hd))
+    Mq = sum(q for _, q in items)
+    qv = rng.standard_normal((Mq, hq, hd))
+    if bf16:
+        pool = round_bf16(pool).reshape(pool.shape)
+        qv = round_bf16(qv).reshape(qv.shape)
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    pool_t = dev(pool.astype(np.float32)).to(tdt)
+    q_t = dev(qv.astype(np.float32)).to(tdt)
+    out = torch.zeros(Mq, hq * hd, dtype=tdt, device="cuda")
+    row0, pos0, cnt = [], [], []
+    r = 0
+    for c, q in items:
+        row0.append(r)
+        pos0.append(c)
+        cnt.append(q)
+        r += q
+    i32 = lambda a: dev(np.asarray(a, dtype=np.int32))
+    ops.attention(q_t, out, pool_t, L, layer, hq, hkv, hd, i32(bt), i32(np.arange(len(items))), i32(row0), i32(pos0),
+                  i32(cnt), max(cnt), max_pos)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(Mq, hq, hd)
+    grp = hq // hkv
+    ref = np.zeros_like(got, dtype=np.float64)
+    for i, (c, q) in enumerate(items):
+        for qi in range(q):
+            p = c + qi
+            keys = np.arange(p + 1)
+            blocks = bt[i][keys // 16]
+            for h in range(hq):
+                g = h // grp
+                K = pool[blocks, layer, 0, g, keys % 16]
+                Vv = pool[blocks, layer, 1, g, keys % 16]
+                s = K @ qv[row0[i] + qi, h] / np.sqrt(hd)
+                w = np.exp(s - s.max())
+                w /= w.sum()
+                ref[row0[i] + qi, h] = w @ Vv
+    return np.max(np.abs(got - ref))
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_attention_decode_and_verify(ops, bf16):
+    items = [(0, 1), (15, 1), (16, 5), (37, 9), (300, 2), (1000, 1)]
+    err = _attn_case(ops, bf16, hq=28, hkv=4, hd=128, items=items)
+    assert err < (2e-2 if bf16 else 1e-5), err
+
+
+def test_attention_head_dim_64_and_long_split(ops):
+    assert _attn_case(ops, False, hq=4, hkv=2, hd=64, items=[(3000, 4), (5, 3)], seed=2) < 1e-5
+    assert _attn_case(ops, True, hq=40, hkv=8, hd=128, items=[(4100, 1)], seed=3) < 2e-2
+
+
+# ---------------------------------------------------------------------------
+def _stats(ops, logits_t, T, top_p):
+    n = logits_t.shape[0]
+    st = torch.zeros(n * ops.stats_bytes(), dtype=torch.uint8, device="cuda")
+    ops.row_stats(logits_t, T, top_p, st)
+    return st
+
+
+@pytest.mark.parametrize("T,top_p", [(1.0, 1.0), (0.7, 0.9), (1.0, 0.95), (0.0, 1.0)])
+def test_sample_rows_match_oracle(ops, T, top_p):
+    from speculative_decoding_rl_amd import _lib
+    rng = np.random.Generator(np.random.PCG64(11))
+    R, V = 64, 5000
+    z = (rng.standard_normal((R, V)) * 1.5).astype(np.float32)
+    z[0, 10] = z[0, 20] = z[0].max() + 1.0       # tie at the argmax
+    z[1, ::2] = 0.25                              # many equal logits
+    zt = dev(z)
+    st = _stats(ops, zt, T, top_p)
+    seq = np.arange(R, dtype=np.int32) * 3 + 1
+    pos = np.arange(R, dtype=np.int32) + 100
+    out = torch.zeros(R, dtype=torch.int32, device="cuda")
+    ops.sample_rows(zt, st, T, 42, dev(seq), dev(pos), 2, _lib.PURPOSE_DRAFT, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    sp = OSP.SamplingParams(seed=42, temperature=T, top_p=top_p)
+    flagged = 0
+    for r in range(R):
+        w = OS.pi(z[r].astype(np.float64), T, top_p)
+        u = OP.u1(42, int(seq[r]), int(pos[r]), 2, OP.PURPOSE_DRAFT)
+        want = OS.sample(w, u)
+        if got[r] != want:
+            assert OS.cdf_margin(w, u, want) < 1e-12, (r, got[r], want)
+            flagged += 1
+        assert w[got[r]] > 0
+    assert flagged <= 1
+
+
+@pytest.mark.parametrize("T,top_p,gamma", [(1.0, 1.0, 4), (0.8, 0.9, 3), (0.0, 1.0, 4), (1.0, 1.0, 1)])
+def test_spec_decide_matches_oracle(ops, T, top_p, gamma):
+    rng = np.random.Generator(np.random.PCG64(5 + gamma))
+    B, V = 48, 3000
+    G1 = gamma + 1
+    base = rng.standard_normal((B, G1, V)) * 1.2
+    p = base.astype(np.float32)
+    # drafter logits: target plus noise of varying size -> a spread of acceptance
+    noise = rng.standard_normal((gamma, B, V)) * np.linspace(0.05, 2.0, B)[None, :, None]
+    q = (np.transpose(base[:, :gamma], (1, 0, 2)) + noise).astype(np.float32)
+    toks = np.zeros((B, G1), dtype=np.int32)
+    seq = (np.arange(B) * 7 + 3).astype(np.int32)
+    pos0 = (np.arange(B) * 11 + 50).astype(np.int32)
+    # drafts drawn from q with the oracle (any valid draft works: the decision is what is tested)
+    for b in range(B):
+        toks[b, 0] = rng.integers(0, V)
+        for j in range(1, gamma + 1):
+            toks[b, j] = OSP.draft_sample(q[j - 1, b].astype(np.float64), int(seq[b]), int(pos0[b]) + j, j,
+                                          OSP.SamplingParams(seed=9, temperature=T, top_p=top_p))
+    pt = dev(p.reshape(B * G1, V))
+    qt = dev(q.reshape(gamma * B, V))
+    ps = _stats(ops, pt, T, top_p)
+    qs = _stats(ops, qt, T, top_p)
+    out = torch.zeros(B * G1, dtype=torch.int32, device="cuda")
+    nacc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    ops.spec_decide(pt, ps, qt, qs, dev(toks), B, gamma, T, 9, dev(seq), dev(pos0), out, nacc)
+    torch.cuda.synchronize()
+    got_tok = out.cpu().numpy().reshape(B, G1)
+    got_a = nacc.cpu().numpy()
+    sp = OSP.SamplingParams(seed=9, temperature=T, top_p=top_p)
+    accepted_any = 0
+    for b in range(B):
+        a, em = OSP.spec_decide(p[b].astype(np.float64), q[:, b].astype(np.float64), toks[b, 1:], int(seq[b]),
+                                int(pos0[b]), sp)
+        assert got_a[b] == a, b
+        assert list(got_tok[b, :a + 1]) == em, b
+        accepted_any += a
+    assert 0 < accepted_any < B * gamma or T == 0.0
