@@ -1,0 +1,335 @@
+"""Rollout throughput of the self-speculative step vs plain autoregressive decoding.
+
+Workload (defaults): Qwen2.5-7B-shaped decoder in bf16, random init N(0, 0.02),
+W4 group-128 asymmetric self-drafter, 256 prompts of 512 uniform tokens,
+per-sequence stop lengths lognormal(median 2048, sigma 0.75) capped at 16384,
+so the active batch shrinks from 256 to 1; temperature 1, top-p 1, gamma
+adaptive in 1..8 (roofline toggle + EMA of the acceptance rate).
+
+A step is one pass of the whole hot path over the live batch: the controller
+picks AR or SD (and gamma), then draft -> verify -> rejection sample -> KV
+commit/rollback -> batch shrink.  With --steps 0 (default) the rollout runs to
+completion and `steps` reports how many steps that took; --steps K times the
+first K steps.  The same workload is then run with speculation forced off (the
+AR baseline).  Prefill is timed separately and excluded from `value`.
+
+Prints one JSON line (rank 0, N = 1 only: this build runs on one GPU).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "rollout tokens/s SD vs AR, batch 256→1; verify/draft HBM GB/s as % of peak"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=0, help="0 = run the rollout to completion")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="qwen2.5-7b")
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--prompt-len", type=int, default=512)
+    ap.add_argument("--median", type=float, default=2048)
+    ap.add_argument("--cap", type=int, default=16384)
+    ap.add_argument("--gamma-max", type=int, default=8)
+    ap.add_argument("--temperature", type=float, default=1.0)
+    ap.add_argument("--top-p", type=float, default=1.0)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--mode", choices=["both", "sd", "ar", "force-sd"], default="both")
+    ap.add_argument("--gamma", type=int, default=0, help="pin gamma (0 = adaptive)")
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (testing only)")
+    ap.add_argument("--kv-blocks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--progress", type=float, default=20.0, help="seconds between progress lines")
+    return ap.parse_args()
+
+
+def make_engine(args, shape, wts, policy):
+    from speculative_decoding_rl_amd import Engine
+
+    max_ctx = args.prompt_len + args.cap + args.gamma_max + 16
+    max_ctx = (max_ctx + 15) // 16 * 16
+    if args.kv_blocks:
+        kv_blocks = args.kv_blocks
+    else:
+        # peak live KV of the shrinking batch is far below batch * max_ctx; size the pool
+        # for the expected peak with margin (the lognormal tail is long, the batch is not)
+        exp_len = args.prompt_len + args.median * math.exp(0.75 ** 2 / 2)
+        kv_blocks = int(args.batch * (exp_len / 16 + 2) * 1.6) + 2 * (max_ctx // 16)
+    return Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
+                  gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=policy, max_seqs=args.batch + 64,
+                  max_batch=args.batch, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
+
+
+def run_rollout(eng, args, prompts, stops, label):
+    """Prefill, then steps until done (or K steps). Returns per-step records and totals."""
+    import torch
+
+    n = len(prompts)
+    ids = eng.kv_alloc([args.prompt_len] * n, stops)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    first = eng.prefill(ids, list(prompts))
+    torch.cuda.synchronize()
+    t_prefill = time.perf_counter() - t0
+    log(f"[{label}] prefill {n}x{args.prompt_len} tokens: {t_prefill:.2f} s")
+    gen = {int(i): 1 for i in ids}                 # the prefill token counts toward the stop length
+    stop = {int(i): int(s) for i, s in zip(ids, stops)}
+    active = [int(i) for i in ids if gen[int(i)] < stop[int(i)]]
+    recs = []
+    eng.reset_stats()
+    if not args.no_kernel_profile:
+        eng.reset_kernel_profile()
+        eng.set_kernel_profile(True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    t_last = t_start
+    k = 0
+    while active and (args.steps == 0 or k < args.steps):
+        B = len(active)
+        ts = time.perf_counter()
+        tok, ne, info = eng.step(active)
+        te = time.perf_counter()
+        recs.append((B, int(info.mode), int(info.gamma), int(ne.sum()), te - ts, int(info.accepted)))
+        for b, a in enumerate(active):
+            gen[a] += int(ne[b])
+        active = [a for a in active if gen[a] < stop[a]]
+        k += 1
+        if te - t_last > args.progress:
+            done = sum(r[3] for r in recs)
+            log(f"[{label}] step {k}: active {len(active)}, tokens {done}, "
+                f"{done / (te - t_start):.0f} tok/s, mode {'SD' if info.mode else 'AR'} gamma {info.gamma}")
+            t_last = te
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    kprof = eng.kernel_profile() if not args.no_kernel_profile else []
+    if not args.no_kernel_profile:
+        eng.set_kernel_profile(False)
+    stats = eng.stats()
+    left = [a for a in ids if gen[int(a)] < stop[int(a)]]
+    eng.kv_free(ids)
+    tokens = sum(r[3] for r in recs)
+    log(f"[{label}] {k} steps, {tokens} tokens in {t_total:.2f} s -> {tokens / t_total:.1f} tok/s")
+    return dict(recs=recs, t=t_total, tokens=tokens, steps=k, prefill_s=t_prefill, kprof=kprof, stats=stats,
+                unfinished=len(left))
+
+
+def bins(recs):
+    edges = [256, 128, 64, 32, 16, 8, 4, 2, 1]
+    out = []
+    for hi, lo in zip(edges[:-1] + [1], edges[1:] + [0]):
+        sel = [r for r in recs if lo < r[0] <= hi]
+        if not sel:
+            continue
+        tok = sum(r[3] for r in sel)
+        t = sum(r[4] for r in sel)
+        sd = sum(1 for r in sel if r[1] == 1)
+        out.append(dict(batch=f"{lo + 1}-{hi}", steps=len(sel), tokens=tok, seconds=round(t, 4),
+                        tok_per_s=round(tok / t, 1) if t > 0 else None, sd_steps=sd))
+    return out
+
+
+def roofline_from(kprof):
+    lin = [k for k in kprof if "k_linear" in k["name"]]
+    if not lin:
+        return None, None
+    top = max(lin, key=lambda k: k["ms"])
+    gbs = top["bytes"] / (top["ms"] * 1e-3) / 1e9
+    rf = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    detail = {"kernel": top["name"], "launches": top["launches"], "avg_us": round(top["ms"] * 1e3 / top["launches"], 2),
+              "avg_bytes": round(top["bytes"] / top["launches"])}
+    return rf, detail
+
+
+def kernel_table(kprof):
+    rows = []
+    for k in sorted(kprof, key=lambda k: -k["ms"]):
+        gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9 if k["ms"] > 0 else 0.0
+        rows.append(dict(name=k["name"], launches=k["launches"], ms=round(k["ms"], 2),
+                         avg_us=round(k["ms"] * 1e3 / max(1, k["launches"]), 2), gbs=round(gbs, 1),
+                         frac_hbm=round(gbs / HBM_PEAK_GBS, 3)))
+    return rows
+
+
+def cpu_baseline(shape_name, args):
+    """The oracle (fp64 NumPy) on the host: SD and AR decode steps of the same model shape.
+
+    Sample: a 2-layer, full-width slice of the model (vocab, widths, heads as
+    the workload) at batch 1 with a 512-token context; gamma = 4.  Per-step
+    time is scaled to the full depth by the ratio of streamed linear
+    parameters (the oracle is bound by reading its fp64 weights).
+    """
+    import torch
+
+    import synth
+    from oracle import spec as OSP
+    from oracle.controller import ModelCost
+    from oracle.model import KVStore, config_from, forward, weights_from
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    full = synth.shape(shape_name)
+    sl = synth.shape(shape_name, n_layers=2)
+    t0 = time.perf_counter()
+    wts = synth.weights(sl, seed=args.seed)
+    cfg = config_from(sl)
+    W = weights_from(cfg, {k: v.float().numpy() for k, v in wts.items()})
+    del wts
+    D = OSP.build_drafter(W, sl.quant)
+    setup = time.perf_counter() - t0
+    sp = OSP.SamplingParams(seed=args.seed, temperature=args.temperature, top_p=args.top_p)
+    ctx = 512
+    prompt = list(synth.prompts(1, ctx, sl.vocab, seed=args.seed)[0])
+    st = OSP.prefill(cfg, W, 0, prompt, 10**6, ctx + 64, sp)
+    gamma = 4
+    t1 = time.perf_counter()
+    n_sd, tok_sd = 0, 0
+    while time.perf_counter() - t1 < 12.0 and n_sd < 6:
+        rec = OSP.spec_step(cfg, W, D, st, gamma, sp)
+        tok_sd += len(rec.emitted)
+        n_sd += 1
+    t_sd = (time.perf_counter() - t1) / n_sd
+    t2 = time.perf_counter()
+    n_ar = 0
+    while time.perf_counter() - t2 < 6.0 and n_ar < 12:
+        OSP.ar_step(cfg, W, st, sp)
+        n_ar += 1
+    t_ar = (time.perf_counter() - t2) / n_ar
+    mc = lambda s: ModelCost(s.n_layers, s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab, 2, 0.52, 2)
+    scale = mc(full).p_lin / mc(sl).p_lin
+    sd_tps = (tok_sd / n_sd) / (t_sd * scale)
+    ar_tps = 1.0 / (t_ar * scale)
+    return {"value": round(sd_tps, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle (fp64 numpy) on {threads} BLAS threads: {n_sd} SD steps (gamma {gamma}, "
+                       f"{tok_sd / n_sd:.2f} tokens/step) and {n_ar} AR steps at batch 1, context {ctx}, on a "
+                       f"2-layer full-width slice of {shape_name}; per-step time scaled to {full.n_layers} layers "
+                       f"by streamed parameters (x{scale:.2f}, extrapolated); setup {setup:.0f} s untimed"),
+            "ar_value": round(ar_tps, 4), "measured_s": round(t_sd * n_sd + t_ar * n_ar, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
+                                   "described in DESIGN.md but not built)"}))
+        sys.exit(2)
+    import torch
+
+    import synth
+    from speculative_decoding_rl_amd import _lib
+
+    torch.cuda.set_device(0)
+    over = {"n_layers": args.layers} if args.layers else {}
+    shape = synth.shape(args.config, **over)
+    t0 = time.perf_counter()
+    wts = synth.weights(shape, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    log(f"weights {sum(v.numel() for v in wts.values()) / 1e9:.2f} B params on device in {time.perf_counter() - t0:.1f} s")
+    prompts = synth.prompts(args.batch, args.prompt_len, shape.vocab, seed=args.seed)
+    stops = synth.stop_lengths(args.batch, args.median, args.cap, seed=args.seed)
+    log(f"stop lengths: sum {int(stops.sum())}, max {int(stops.max())}, median {int(np.median(stops))}")
+
+    t0 = time.perf_counter()
+    eng = make_engine(args, shape, wts, _lib.ER_POLICY_AUTO)
+    torch.cuda.synchronize()
+    log(f"engine init (drafter quantization + calibration) {time.perf_counter() - t0:.1f} s")
+    if args.gamma:
+        eng.set_gamma(args.gamma)
+
+    # warm-up: a few steps of each mode on a small side batch (untimed)
+    if args.warmup > 0:
+        nw = min(8, args.batch)
+        wp = synth.prompts(nw, 64, shape.vocab, seed=args.seed + 1)
+        for pol in (_lib.ER_POLICY_FORCE_SD, _lib.ER_POLICY_FORCE_AR):
+            eng.set_policy(pol)
+            wid = eng.kv_alloc([64] * nw, [args.warmup + 2] * nw)
+            eng.prefill(wid, list(wp))
+            for _ in range(args.warmup):
+                act = [int(a) for a in wid if not eng.seq_info(int(a))[2]]
+                if act:
+                    eng.step(act)
+            eng.kv_free(wid)
+        torch.cuda.synchronize()
+
+    res = {}
+    modes = {"both": ["sd", "ar"], "sd": ["sd"], "ar": ["ar"], "force-sd": ["force-sd"]}[args.mode]
+    for m in modes:
+        eng.set_policy({"sd": _lib.ER_POLICY_AUTO, "ar": _lib.ER_POLICY_FORCE_AR,
+                        "force-sd": _lib.ER_POLICY_FORCE_SD}[m])
+        res[m] = run_rollout(eng, args, prompts, stops, m)
+
+    main_run = res.get("sd") or res.get("force-sd") or res["ar"]
+    value = main_run["tokens"] / main_run["t"]
+    rf, rf_detail = roofline_from(main_run["kprof"])
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": main_run["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(main_run["t"] * 1e3 / max(1, main_run["steps"]), 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (random-init weights N(0,0.02), uniform prompts, lognormal stop lengths)",
+        "config": {"workload": (f"{args.config}-shaped decoder{'' if not args.layers else f' ({args.layers} layers)'}"
+                                f", {shape.quant.upper()} self-drafter, {args.batch} prompts x {args.prompt_len} "
+                                f"tokens, stop lengths lognormal(median {int(args.median)}, sigma 0.75) cap "
+                                f"{args.cap}, T={args.temperature}, top-p={args.top_p}, gamma "
+                                f"{'adaptive 1..%d' % args.gamma_max if not args.gamma else args.gamma}, "
+                                f"{'full rollout 256->1' if args.steps == 0 else f'first {args.steps} steps'}"),
+                   "mode": "SD-auto (roofline toggle)" if "sd" in res else modes[0],
+                   "global_batch": args.batch, "seq_len": args.prompt_len, "parallelism": "none (1 GPU)"},
+        "roofline": rf,
+    }
+    if "ar" in res and main_run is not res["ar"]:
+        ar_v = res["ar"]["tokens"] / res["ar"]["t"]
+        out["ar_value"] = round(ar_v, 2)
+        out["sd_over_ar"] = round(value / ar_v, 4)
+    st = main_run["stats"]
+    out["acceptance"] = {"alpha_ema_end": round(st["alpha_ema"], 4),
+                         "accepted_per_draft": round(st["accepted"] / st["drafted"], 4) if st["drafted"] else None,
+                         "mean_emitted_per_sd_seq_step": round(st["emitted"] / max(1, st["predict_times"]), 4)
+                         if st["predict_times"] else None,
+                         "sd_steps": st["sd_steps"], "ar_steps": st["ar_steps"],
+                         "effective_length": round(st["effective_length"], 4),
+                         "effective_percent": round(st["effective_percent"], 4)}
+    out["prefill_s"] = round(main_run["prefill_s"], 3)
+    out["by_batch"] = {m: bins(r["recs"]) for m, r in res.items()}
+    out["kernels_top"] = kernel_table(main_run["kprof"])[:8]
+    if rf_detail:
+        out["roofline_kernel"] = rf_detail
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(args.config, args)
+        except Exception as e:  # reported, not fatal
+            out["cpu_baseline"] = {"error": repr(e)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -241,8 +241,34 @@ int er_reset_stats(er_ctx *ctx);
  * `first_n` steps (0, 0 = never, the default). */
 int er_set_timing(er_ctx *ctx, int period, int first_n);
 
+/* bf16 models run a fused forward by default: RMSNorm formed on the input
+ * load of the following projection, RoPE and the KV append in the QKV
+ * projection's epilogue, SwiGLU in the gate/up projection's epilogue, the
+ * residual add in the output projections' epilogues.  on = 0 selects the
+ * unfused sequence of kernels (same arithmetic, separate passes); fp32 models
+ * always run unfused.  Takes effect at the next forward. */
+int er_set_fused(er_ctx *ctx, int on);
+
 /* Free KV blocks in the pool. */
 int er_kv_free_blocks(er_ctx *ctx, int64_t *free_blocks, int64_t *total_blocks);
+
+/* ---- per-kernel timing ---------------------------------------------------
+ * When on, every linear-layer and attention launch of the steps is bracketed
+ * with HIP events on the context's stream; totals are kept per kernel name
+ * (the name the profiler shows, e.g. "er::k_linear_mfma<3, 16, 2>") with the
+ * algorithmic bytes (weights incl. scales/zeros + activations in + results
+ * out; attention: K/V of every key read + q + out) and flops of each launch. */
+typedef struct er_kernel_stat {
+  char name[64];
+  int64_t launches;
+  double ms;        /* summed device time */
+  double bytes;     /* summed algorithmic bytes */
+  double flops;     /* summed algorithmic flops */
+} er_kernel_stat;
+int er_set_kernel_profile(er_ctx *ctx, int on);
+/* Copies min(max, count) entries; *n_out = count. */
+int er_get_kernel_profile(er_ctx *ctx, er_kernel_stat *out, int max, int *n_out);
+int er_reset_kernel_profile(er_ctx *ctx);
 
 /* ---- diagnostics: the last step's logits and drafts, for checking ------- */
 /* which = 0: drafter logits of batch slot `slot` ([gamma, vocab] fp32);

@@ -44,15 +44,56 @@ int er_op_w4_kernel_order(const void *d_canon, int N, int K, void *d_out, void *
 
 /* y[m, n] = sum_k x[m, k] W[n, k] for m < M, n < N; y fp32 [M, ldy].
  * x: [M, ldx] of x_dtype (ER_BF16 or ER_F32).  path: 0 automatic, 1 VALU,
- * 2 MFMA (bf16 x, K % 128 == 0).  The verify pass runs the target's linears
+ * 2 MFMA (bf16 x, K % 128 == 0), 3 tiled GEMM (bf16 W), or a skinny MFMA
+ * variant 1000 + 100*NR + 10*KS + MT/16 (16*NR rows per wave, K split over KS
+ * of the 8 waves, m-tile MT in {16, 32}; ER_EINVAL if M > MT).  The verify pass runs the target's linears
  * with this at M = B (gamma + 1); the drafter runs its quantized copies at M = B. */
 int er_op_linear(int x_dtype, const void *d_x, int ldx, int M, int fmt, const void *d_w, const void *d_scale,
                  const void *d_zero, int N, int K, float *d_y, int ldy, int path, void *stream);
 
+/* Fused linear with bf16 activations (MFMA paths; the bf16 model's forward
+ * runs its projections through this).  Input: xnorm = 0 reads x' = d_x as
+ * bf16 [M, ldx]; xnorm = 1 forms x'[m] = bf16(h[r] * rstd(r) * g) on load, h =
+ * d_x fp32 [rows, ldx], r = d_xrow ? d_xrow[m] : m, rstd(r) = 1/sqrt(S[r]/K +
+ * eps) with S[r] = d_ssq_in[r] * 2^-24 (fixed-point sum of squares of h's row)
+ * and g = d_gnorm bf16 [K] (RMSNorm, EfficientRollout's Qwen2.5 family;
+ * standard pre-norm decoder).  acc = x' W^T (fmt as er_op_linear).
+ * Epilogue epi:
+ *   ER_EPI_F32    d_y fp32 [M, ldy] = acc
+ *   ER_EPI_RESID  d_y fp32 [M, ldy] += acc; if d_ssq_acc, d_ssq_acc[m] +=
+ *                 the updated row's sum of squares in 2^-24 fixed point
+ *                 (each work-group adds its rounded partial)
+ *   ER_EPI_SWIGLU W = [gate (F rows); up (F rows)], d_y bf16 [M, ldy]:
+ *                 y[m, f] = silu(acc[m, f]) * acc[m, F + f]
+ *   ER_EPI_QKV    W = [q; k; v] heads of hd rows; rotate-half RoPE on q and k
+ *                 at position pos[m] (cos/sin table [max_pos, hd/2] of
+ *                 (cos, sin) fp32 pairs); q -> d_q_out bf16 [M, hq, hd]; k, v ->
+ *                 the paged KV pool (er_op_attention's layout) at slot[m].
+ * If d_ssq_zero, rows [0, M) of it are set to 0 (it may not alias d_ssq_in or
+ * d_ssq_acc).  path as er_op_linear (0, 2, 3 or a skinny variant). */
+#define ER_EPI_F32    0
+#define ER_EPI_RESID  2
+#define ER_EPI_SWIGLU 3
+#define ER_EPI_QKV    4
+typedef struct {
+  int hq, hkv, hd;
+  const int32_t *d_pos;       /* [M] */
+  const int64_t *d_slot;      /* [M] block * 16 + offset */
+  const float *d_cos_sin;     /* [max_pos, hd/2, 2] */
+  void *d_q_out;              /* bf16 [M, hq, hd] */
+  void *d_kv_pool;            /* bf16 pool */
+  int layer, n_layers;
+} er_qkv_args;
+int er_op_linear_fused(int epi, const void *d_x, int ldx, int M, int xnorm, const int32_t *d_xrow,
+                       const uint64_t *d_ssq_in, const void *d_gnorm, float eps, int fmt, const void *d_w,
+                       const void *d_scale, const void *d_zero, int N, int K, void *d_y, int ldy,
+                       uint64_t *d_ssq_acc, uint64_t *d_ssq_zero, const er_qkv_args *qkv, int path, void *stream);
+
 /* Paged GQA attention (TLT reading notes, section 1: the target scores all
  * drafted positions in one pass).  q: [Mq, hq, hd] of act_dtype; out same
- * shape.  KV pool of blocks of 16 positions, element (block, layer, k|v,
- * kv_head, t, e) at ((((block*L + layer)*2 + kv)*hkv + head)*16 + t)*hd + e.
+ * shape.  KV pool of blocks of 16 positions: block b, layer l, kv head h holds
+ * K as [16][hd] starting at ((((b*L + l)*2 + 0)*hkv + h)*16)*hd and V
+ * transposed, [hd][16], starting at ((((b*L + l)*2 + 1)*hkv + h)*16)*hd.
  * Item i: q rows q_row0[i] .. + q_count[i]-1 at positions q_pos0[i] .. of the
  * sequence whose block table row is bt_row[i] (block_table [rows, bt_stride]);
  * a query at position t sees keys 0..t.  (n_q_heads/n_kv_heads)*max_q_count <= 64,
@@ -62,9 +103,10 @@ int er_op_attention(int act_dtype, const void *d_q, void *d_out, const void *d_k
                     const int32_t *d_q_row0, const int32_t *d_q_pos0, const int32_t *d_q_count, int n_items,
                     int max_q_count, int max_ctx, void *stream);
 
-/* Per-row sampling statistics of fp32 logits rows [rows, ld] (max, argmax,
- * softmax mass in fp64, top-p threshold).  d_stats: er_op_stats_bytes() each. */
-size_t er_op_stats_bytes(void);
+/* Per-row sampling statistics of fp32 logits rows [rows, ld]: per vocabulary
+ * chunk of 2048 tokens the max, its first index and the softmax mass relative
+ * to it (fp64), plus the top-p threshold.  d_stats: er_op_stats_bytes(V) per row. */
+size_t er_op_stats_bytes(int V);
 int er_op_row_stats(const float *d_logits, int rows, int V, long ld, float temperature, float top_p, void *d_stats,
                     void *stream);
 
@@ -72,8 +114,8 @@ int er_op_row_stats(const float *d_logits, int rows, int V, long ld, float tempe
  * sum in vocabulary order reaches u * total, u = Philox4x32-10 uniform of
  * (seed; seq_id[r], pos[r], draft_idx, purpose).  d_out[r * out_stride]. */
 int er_op_sample_rows(const float *d_logits, const void *d_stats, int rows, int V, long ld, float temperature,
-                      uint64_t seed, const int32_t *d_seq_id, const int32_t *d_pos, int draft_idx, int purpose,
-                      int32_t *d_out, int out_stride, void *stream);
+                      float top_p, uint64_t seed, const int32_t *d_seq_id, const int32_t *d_pos, int draft_idx,
+                      int purpose, int32_t *d_out, int out_stride, void *stream);
 
 /* Speculative decision for B sequences (standard speculative sampling, the
  * lossless rule): target rows [B*(gamma+1), V] b-major, drafter rows
@@ -82,7 +124,7 @@ int er_op_sample_rows(const float *d_logits, const void *d_stats, int rows, int 
  * resample normalize(max(0, p_j - q_j)) and stop; bonus from p_{gamma+1}
  * after a full acceptance.  d_out_tok [B, gamma+1], d_n_acc [B]. */
 int er_op_spec_decide(const float *d_p_logits, const void *d_p_stats, const float *d_q_logits, const void *d_q_stats,
-                      const int32_t *d_tokens, int B, int gamma, int V, float temperature, uint64_t seed,
+                      const int32_t *d_tokens, int B, int gamma, int V, float temperature, float top_p, uint64_t seed,
                       const int32_t *d_seq_id, const int32_t *d_pos0, int32_t *d_out_tok, int32_t *d_n_acc,
                       void *stream);
 

@@ -69,6 +69,11 @@ class Stats(C.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class KernelStat(C.Structure):
+    _fields_ = [("name", C.c_char * 64), ("launches", C.c_int64), ("ms", C.c_double), ("bytes", C.c_double),
+                ("flops", C.c_double)]
+
+
 class CostModel(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32), ("vocab", C.c_int32),
@@ -81,6 +86,14 @@ I32P = C.POINTER(C.c_int32)
 I64P = C.POINTER(C.c_int64)
 
 # name -> (restype, argtypes)
+class QkvArgs(C.Structure):
+    _fields_ = [("hq", C.c_int), ("hkv", C.c_int), ("hd", C.c_int), ("d_pos", C.c_void_p), ("d_slot", C.c_void_p),
+                ("d_cos_sin", C.c_void_p), ("d_q_out", C.c_void_p), ("d_kv_pool", C.c_void_p), ("layer", C.c_int),
+                ("n_layers", C.c_int)]
+
+
+EPI_F32, EPI_RESID, EPI_SWIGLU, EPI_QKV = 0, 2, 3, 4
+
 SIGNATURES = {
     # er_api.h
     "er_rollout_init": (C.c_int, [C.POINTER(ModelDesc), C.POINTER(Weights), C.POINTER(DraftDesc),
@@ -101,7 +114,11 @@ SIGNATURES = {
     "er_get_stats": (C.c_int, [P, C.POINTER(Stats)]),
     "er_reset_stats": (C.c_int, [P]),
     "er_set_timing": (C.c_int, [P, C.c_int, C.c_int]),
+    "er_set_fused": (C.c_int, [P, C.c_int]),
     "er_kv_free_blocks": (C.c_int, [P, I64P, I64P]),
+    "er_set_kernel_profile": (C.c_int, [P, C.c_int]),
+    "er_get_kernel_profile": (C.c_int, [P, C.POINTER(KernelStat), C.c_int, C.POINTER(C.c_int)]),
+    "er_reset_kernel_profile": (C.c_int, [P]),
     "er_debug_logits": (C.c_int, [P, C.c_int, C.c_int, C.POINTER(C.c_float), I32P]),
     "er_debug_drafts": (C.c_int, [P, I32P]),
     "er_controller_choose": (C.c_int, [C.POINTER(CostModel), C.c_int, C.c_double, C.c_double, C.c_int, C.c_int,
@@ -114,13 +131,16 @@ SIGNATURES = {
     "er_op_w4_kernel_order": (C.c_int, [P, C.c_int, C.c_int, P, P]),
     "er_op_linear": (C.c_int, [C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P, C.c_int, C.c_int, P, C.c_int,
                                C.c_int, P]),
+    "er_op_linear_fused": (C.c_int, [C.c_int, P, C.c_int, C.c_int, C.c_int, P, P, P, C.c_float, C.c_int, P, P, P,
+                                     C.c_int, C.c_int, P, C.c_int, P, P, C.POINTER(QkvArgs), C.c_int, P]),
     "er_op_attention": (C.c_int, [C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int, P, P,
                                   P, P, C.c_int, C.c_int, C.c_int, P]),
-    "er_op_stats_bytes": (C.c_size_t, []),
+    "er_op_stats_bytes": (C.c_size_t, [C.c_int]),
     "er_op_row_stats": (C.c_int, [P, C.c_int, C.c_int, C.c_long, C.c_float, C.c_float, P, P]),
-    "er_op_sample_rows": (C.c_int, [P, P, C.c_int, C.c_int, C.c_long, C.c_float, C.c_uint64, P, P, C.c_int, C.c_int,
-                                    P, C.c_int, P]),
-    "er_op_spec_decide": (C.c_int, [P, P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_uint64, P, P, P, P, P]),
+    "er_op_sample_rows": (C.c_int, [P, P, C.c_int, C.c_int, C.c_long, C.c_float, C.c_float, C.c_uint64, P, P, C.c_int,
+                                    C.c_int, P, C.c_int, P]),
+    "er_op_spec_decide": (C.c_int, [P, P, P, P, P, C.c_int, C.c_int, C.c_int, C.c_float, C.c_float, C.c_uint64, P, P,
+                                    P, P, P]),
     "er_op_philox_uniform": (C.c_int, [C.c_uint64, P, C.c_int, P, P]),
 }
 

@@ -18,6 +18,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -93,8 +94,14 @@ struct er_ctx {
   float* gu = nullptr;
   float* logits_p = nullptr;
   float* logits_q = nullptr;
-  RowStats* stats_p = nullptr;
-  RowStats* stats_q = nullptr;
+  void* stats_p = nullptr;     // sampler statistics, stats_row_bytes(nch) per logits row
+  void* stats_q = nullptr;
+  double* resid = nullptr;     // residual chunk masses [max_batch, nch]
+  // fixed-point row sums of squares of h (ping-pong between the residual
+  // producers and the normalizing consumers of the fused bf16 forward)
+  unsigned long long* ssq[2] = {nullptr, nullptr};
+  bool fuse = false;
+  int nch = 1;
   int32_t* out_d = nullptr;     // [rows] tokens + [max_batch] accepted counts
   int32_t* out_h = nullptr;     // pinned
   LinearWs lws{};
@@ -129,6 +136,15 @@ struct er_ctx {
   int last_mode = -1, last_gamma = 0, last_B = 0;
   size_t last_tok_off = 0;  // verify tokens [B, gamma+1] of the last speculative step, in the metadata region
   std::vector<int32_t> last_prefill_row;
+
+  // per-kernel timing (events around each linear / attention launch)
+  bool kprof = false;
+  std::vector<hipEvent_t> kev;
+  size_t kev_used = 0;
+  struct KRec { std::string name; double bytes, flops; int e0, e1; };
+  std::vector<KRec> krec;
+  struct KStat { long n = 0; double ms = 0, bytes = 0, flops = 0; };
+  std::map<std::string, KStat> kstat;
 
   // timing
   int timing_period = 0, timing_first = 0;
@@ -169,15 +185,52 @@ int fail(er_ctx* c, int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int kp_begin(er_ctx* c) {
+  if (!c->kprof || c->kev_used + 2 > c->kev.size()) return -1;
+  const int i = (int)c->kev_used;
+  c->kev_used += 2;
+  if (hipEventRecord(c->kev[(size_t)i], c->st) != hipSuccess) return -1;
+  return i;
+}
+void kp_end(er_ctx* c, int i, const char* name, double bytes, double flops) {
+  if (i < 0) return;
+  if (hipEventRecord(c->kev[(size_t)i + 1], c->st) != hipSuccess) return;
+  c->krec.push_back(er_ctx::KRec{name, bytes, flops, i, i + 1});
+}
+// After the stream is synchronized: fold the recorded launches into the totals.
+void kp_flush(er_ctx* c) {
+  for (const auto& r : c->krec) {
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, c->kev[(size_t)r.e0], c->kev[(size_t)r.e1]) != hipSuccess) continue;
+    auto& k = c->kstat[r.name];
+    k.n += 1;
+    k.ms += ms;
+    k.bytes += r.bytes;
+    k.flops += r.flops;
+  }
+  c->krec.clear();
+  c->kev_used = 0;
+}
+
+double weight_bytes(const LinearW& W) {
+  const double nk = (double)W.N * W.K;
+  switch (W.fmt) {
+    case FMT_F32: return 4 * nk;
+    case FMT_BF16: return 2 * nk;
+    case FMT_W8: return nk + 4.0 * W.N;
+    default: return nk / 2 + 3.0 * W.N * (W.K / 128);
+  }
+}
+
 // Layout of everything but the KV pool, shared by er_arena_bytes and init.
 struct Layout {
   size_t drafter = 0, cs = 0, h = 0, xbuf = 0, qkv = 0, qb = 0, gu = 0, lp = 0, lq = 0, sp = 0, sq = 0;
-  size_t out = 0, partial = 0, counters = 0, attn = 0, w4tmp = 0, sink = 0, meta = 0;
+  size_t out = 0, partial = 0, counters = 0, attn = 0, w4tmp = 0, sink = 0, meta = 0, resid = 0, ssq = 0;
   size_t block_bytes = 0;
   int max_rows = 0, logit_rows = 0;
   size_t total_fixed() const {
     return drafter + cs + h + xbuf + qkv + qb + gu + lp + lq + sp + sq + out + partial + counters + attn + w4tmp +
-           sink + meta;
+           sink + meta + resid + ssq;
   }
 };
 
@@ -210,8 +263,11 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
   L->gu = align256((size_t)R * 2 * F * 4);
   L->lp = align256((size_t)L->logit_rows * V * 4);
   L->lq = align256((size_t)r.max_batch * r.gamma_max * V * 4);
-  L->sp = align256((size_t)L->logit_rows * sizeof(RowStats));
-  L->sq = align256((size_t)r.max_batch * r.gamma_max * sizeof(RowStats));
+  const long srb = stats_row_bytes(sampler_chunks((int)V));
+  L->sp = align256((size_t)L->logit_rows * srb);
+  L->sq = align256((size_t)r.max_batch * r.gamma_max * srb);
+  L->resid = align256((size_t)r.max_batch * sampler_chunks((int)V) * 8);
+  L->ssq = 2 * align256((size_t)R * 8);
   L->out = align256((size_t)(L->max_rows + r.max_batch) * 4);
   L->partial = align256((size_t)16 << 20) * 4;  // 16M floats
   L->counters = align256((size_t)65536 * 4);
@@ -271,6 +327,7 @@ struct Fwd {
   int bt_stride = 0;
   const int32_t *it_bt = nullptr, *it_row0 = nullptr, *it_pos0 = nullptr, *it_cnt = nullptr;
   int n_items = 0, max_q = 0, max_ctx = 0;
+  double kv_keys = 0;                    // sum over items of keys read (for per-kernel byte counts)
   const int32_t* logit_rows = nullptr;  // rows whose logits are computed (with n_logit > 0)
   int n_logit = -1;                      // -1: every row; 0: none (prefill chunk with no last token)
   float* logits = nullptr;
@@ -279,7 +336,72 @@ struct Fwd {
 
 int lin(er_ctx* c, const void* x, int M, const LinearW& W, void* y, int ldy, int epi) {
   const int ldx = W.K;
-  KC(c, launch_linear(x, c->bf16, ldx, M, W, y, ldy, epi, c->lws, c->lin_path, c->st));
+  LinearInfo li{};
+  const int e = kp_begin(c);
+  KC(c, launch_linear(x, c->bf16, ldx, M, W, y, ldy, epi, c->lws, c->lin_path, c->st, &li));
+  if (e >= 0) {
+    // algorithmic bytes: weights (with scales/zeros) + activations in + result out (read+write for +=)
+    const double by = weight_bytes(W) + (double)M * W.K * c->act_bytes + (double)M * W.N * (epi == EPI_RESID ? 8 : 4);
+    kp_end(c, e, li.name, by, 2.0 * M * (double)W.N * W.K);
+  }
+  return ER_OK;
+}
+
+// Fused linear (bf16 models): x' = RMSNorm(h) on load when `xn` (sums of
+// squares from ssq_in), epilogue `epi`; residual epilogues accumulate the new
+// sums of squares into ssq_acc and clear ssq_zero.
+struct FLin {
+  const void* x = nullptr;
+  int ldx = 0;
+  const void* gnorm = nullptr;
+  const int32_t* xrow = nullptr;
+  const unsigned long long* ssq_in = nullptr;
+  unsigned long long* ssq_acc = nullptr;
+  unsigned long long* ssq_zero = nullptr;
+};
+
+int flin(er_ctx* c, const Fwd& f, const FLin& fl, int M, const LinearW& W, void* y, int ldy, int epi, int layer) {
+  const er_model_desc& m = c->md;
+  LinArgs a{};
+  a.x = fl.x;
+  a.ldx = fl.ldx;
+  a.M = M;
+  a.xnorm = fl.gnorm != nullptr;
+  a.xrow = fl.xrow;
+  a.ssq_in = fl.ssq_in;
+  a.gnorm = fl.gnorm;
+  a.eps = m.rms_eps;
+  a.W = W;
+  a.epi = epi;
+  a.y = y;
+  a.ldy = ldy;
+  a.act_bf16 = 1;
+  a.ssq_acc = fl.ssq_acc;
+  a.ssq_zero = fl.ssq_zero;
+  a.hq = m.n_q_heads;
+  a.hkv = m.n_kv_heads;
+  a.hd = m.head_dim;
+  a.pos = f.pos;
+  a.slot = f.slot;
+  a.cs = c->cs;
+  a.qout = c->qb;
+  a.kv_pool = c->kv_pool;
+  a.layer = layer;
+  a.n_layers = m.n_layers;
+  a.F = m.ffn;
+  LinearInfo li{};
+  const int e = kp_begin(c);
+  KC(c, launch_linear_fused(a, c->lws, c->lin_path, c->st, &li));
+  if (e >= 0) {
+    // algorithmic bytes: weights (with scales/zeros) + x' in (fp32 h when normalized on load) + outputs
+    double out_b;
+    if (epi == EPI_RESID) out_b = (double)M * W.N * 8;
+    else if (epi == EPI_SWIGLU) out_b = (double)M * (W.N / 2) * 2;
+    else if (epi == EPI_QKV) out_b = (double)M * W.N * 2;
+    else out_b = (double)M * W.N * 4;
+    const double by = weight_bytes(W) + (double)M * W.K * (a.xnorm ? 4 : 2) + out_b;
+    kp_end(c, e, li.name, by, 2.0 * M * (double)W.N * W.K);
+  }
   return ER_OK;
 }
 
@@ -287,7 +409,10 @@ int forward(er_ctx* c, const Fwd& f) {
   const er_model_desc& m = c->md;
   const int d = m.d_model, hq = m.n_q_heads, hkv = m.n_kv_heads, hd = m.head_dim, F = m.ffn;
   const std::vector<Lin4>& W = f.draft ? c->drf : c->tgt;
-  KC(c, launch_embed(f.tokens, f.tok_stride, f.M, c->embed, c->bf16, d, c->h, c->st));
+  unsigned long long* S0 = c->ssq[0];
+  unsigned long long* S1 = c->ssq[1];
+  KC(c, launch_embed(f.tokens, f.tok_stride, f.M, c->embed, c->bf16, d, c->h, c->fuse ? S0 : nullptr,
+                     c->fuse ? S1 : nullptr, c->st));
   AttnArgs a{};
   a.q = c->qb;
   a.out = c->xbuf;
@@ -309,13 +434,57 @@ int forward(er_ctx* c, const Fwd& f) {
   a.ws = c->attn_ws;
   a.ws_floats = c->attn_ws_floats;
   for (int l = 0; l < m.n_layers; ++l) {
-    KC(c, launch_rmsnorm(c->h, f.M, d, c->attn_norm[l], c->bf16, m.rms_eps, c->xbuf, nullptr, c->st));
-    int r = lin(c, c->xbuf, f.M, W[l].qkv, c->qkv, (hq + 2 * hkv) * hd, EPI_F32);
+    int r;
+    if (c->fuse) {
+      // h (sums of squares in S0) -> norm -> qkv with RoPE and the KV append
+      FLin q;
+      q.x = c->h;
+      q.ldx = d;
+      q.gnorm = c->attn_norm[l];
+      q.ssq_in = S0;
+      r = flin(c, f, q, f.M, W[l].qkv, nullptr, 0, EPI_QKV, l);
+    } else {
+      KC(c, launch_rmsnorm(c->h, f.M, d, c->attn_norm[l], c->bf16, m.rms_eps, c->xbuf, nullptr, c->st));
+      r = lin(c, c->xbuf, f.M, W[l].qkv, c->qkv, (hq + 2 * hkv) * hd, EPI_F32);
+      if (r) return r;
+      KC(c, launch_rope_kv(c->qkv, f.M, hq, hkv, hd, f.pos, f.slot, c->cs, c->qb, c->kv_pool, l, m.n_layers, c->bf16,
+                           c->st));
+    }
     if (r) return r;
-    KC(c, launch_rope_kv(c->qkv, f.M, hq, hkv, hd, f.pos, f.slot, c->cs, c->qb, c->kv_pool, l, m.n_layers, c->bf16,
-                         c->st));
     a.layer = l;
-    KC(c, launch_attention(a, c->st));
+    {
+      const int e = kp_begin(c);
+      KC(c, launch_attention(a, c->st));
+      if (e >= 0) {
+        const double kvb = 2.0 * hkv * hd * c->act_bytes;  // K and V of one position, one layer
+        const double by = f.kv_keys * kvb + 2.0 * f.M * hq * hd * c->act_bytes;
+        kp_end(c, e, c->bf16 ? "er::k_attn<true>" : "er::k_attn<false>", by, 4.0 * (f.kv_keys / std::max(1, f.n_items)) * f.M * hq * hd);
+      }
+    }
+    if (c->fuse) {
+      FLin o;  // h += attn W_o^T; new sums of squares -> S1; S0 (read above) cleared
+      o.x = c->xbuf;
+      o.ldx = hq * hd;
+      o.ssq_acc = S1;
+      o.ssq_zero = S0;
+      r = flin(c, f, o, f.M, W[l].o, c->h, d, EPI_RESID, l);
+      if (r) return r;
+      FLin g;  // norm(h) -> gate/up -> SwiGLU
+      g.x = c->h;
+      g.ldx = d;
+      g.gnorm = c->mlp_norm[l];
+      g.ssq_in = S1;
+      r = flin(c, f, g, f.M, W[l].gu, c->xbuf, F, EPI_SWIGLU, l);
+      if (r) return r;
+      FLin dn;  // h += act W_down^T; sums of squares -> S0; S1 cleared
+      dn.x = c->xbuf;
+      dn.ldx = F;
+      dn.ssq_acc = S0;
+      dn.ssq_zero = S1;
+      r = flin(c, f, dn, f.M, W[l].down, c->h, d, EPI_RESID, l);
+      if (r) return r;
+      continue;
+    }
     r = lin(c, c->xbuf, f.M, W[l].o, c->h, d, EPI_RESID);
     if (r) return r;
     KC(c, launch_rmsnorm(c->h, f.M, d, c->mlp_norm[l], c->bf16, m.rms_eps, c->xbuf, nullptr, c->st));
@@ -327,8 +496,17 @@ int forward(er_ctx* c, const Fwd& f) {
   }
   const int nl = f.n_logit < 0 ? f.M : f.n_logit;
   if (nl == 0) return ER_OK;
-  KC(c, launch_rmsnorm(c->h, nl, d, c->final_norm, c->bf16, m.rms_eps, c->xbuf, f.logit_rows, c->st));
   const LinearW& lm = f.draft ? c->lm_d : c->lm_t;
+  if (c->fuse) {
+    FLin h;
+    h.x = c->h;
+    h.ldx = d;
+    h.gnorm = c->final_norm;
+    h.xrow = f.logit_rows;
+    h.ssq_in = S0;
+    return flin(c, f, h, nl, lm, f.logits, (int)f.ldl, EPI_F32, 0);
+  }
+  KC(c, launch_rmsnorm(c->h, nl, d, c->final_norm, c->bf16, m.rms_eps, c->xbuf, f.logit_rows, c->st));
   return lin(c, c->xbuf, nl, lm, f.logits, (int)f.ldl, EPI_F32);
 }
 
@@ -487,8 +665,10 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
   int32_t* h_ic = M.push<int32_t>(n, &o_ic);
   if (!M.ok || !h_bt) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   int max_ctx = 1;
+  double kv_keys = 0;
   for (int i = 0; i < n; ++i) {
     const Seq& s = c->seqs[ids[i]];
+    kv_keys += s.n + 1;
     h_ids[i] = ids[i];
     h_tok[i] = s.pending;
     h_pos[i] = s.n;
@@ -518,21 +698,23 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.n_items = n;
     f.max_q = 1;
     f.max_ctx = max_ctx;
+    f.kv_keys = kv_keys;
     f.logits = c->logits_p;
     f.ldl = c->md.vocab;
     int r = forward(c, f);
     if (r) return r;
     if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
     KC(c, launch_row_stats(c->logits_p, n, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
-    KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.seed,
-                             M.dev<int32_t>(o_ids), M.dev<int32_t>(o_spos), 0, PURPOSE_AR, c->out_d, 1, nullptr,
-                             c->st));
+    KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.top_p,
+                             c->rd.seed, M.dev<int32_t>(o_ids), M.dev<int32_t>(o_spos), 0, PURPOSE_AR, c->out_d, 1,
+                             nullptr, c->st));
     if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
     HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)n * 4, hipMemcpyDeviceToHost, c->st));
     HIPC(c, hipStreamSynchronize(c->st));
     return ER_OK;
   };
   const int r = run();
+  kp_flush(c);
   if (r) { rollback(); return r; }
   // commit
   int kept_tot = 0, fin = 0;
@@ -620,8 +802,10 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   int32_t* h_vic = M.push<int32_t>(n, &o_vic);  // verify: G1 queries
   if (!M.ok || !h_bt) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   int max_ctx = 1;
+  double kv_sum = 0;
   for (int b = 0; b < n; ++b) {
     const Seq& s = c->seqs[ids[b]];
+    kv_sum += s.n;
     h_ids[b] = ids[b];
     h_pos0[b] = s.n;
     h_tok[(size_t)b * G1] = s.pending;
@@ -663,12 +847,14 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.n_items = n;
       f.max_q = 1;
       f.max_ctx = max_ctx;
+      f.kv_keys = kv_sum + (double)n * (j + 1);
       f.logits = c->logits_q + (size_t)j * n * V;
       f.ldl = V;
       int r = forward(c, f);
       if (r) return r;
-      KC(c, launch_row_stats(f.logits, n, V, V, c->rd.temperature, c->rd.top_p, c->stats_q + (size_t)j * n, c->st));
-      KC(c, launch_sample_rows(f.logits, c->stats_q + (size_t)j * n, n, V, V, c->rd.temperature, c->rd.seed,
+      void* sq = (char*)c->stats_q + (size_t)j * n * stats_row_bytes(c->nch);
+      KC(c, launch_row_stats(f.logits, n, V, V, c->rd.temperature, c->rd.top_p, sq, c->st));
+      KC(c, launch_sample_rows(f.logits, sq, n, V, V, c->rd.temperature, c->rd.top_p, c->rd.seed,
                                M.dev<int32_t>(o_ids), M.dev<int32_t>(o_dsp[j]), j + 1, PURPOSE_DRAFT, d_tok + j + 1,
                                G1, nullptr, c->st));
     }
@@ -689,6 +875,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.n_items = n;
     f.max_q = G1;
     f.max_ctx = max_ctx;
+    f.kv_keys = kv_sum + (double)n * G1;
     f.logits = c->logits_p;
     f.ldl = V;
     int r = forward(c, f);
@@ -696,14 +883,15 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
     KC(c, launch_row_stats(c->logits_p, n * G1, V, V, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
     KC(c, launch_spec_decide(c->logits_p, c->stats_p, c->logits_q, c->stats_q, d_tok, n, g, V, c->rd.temperature,
-                             c->rd.seed, M.dev<int32_t>(o_ids), M.dev<int32_t>(o_pos0), c->out_d, c->out_d + n * G1,
-                             c->st));
+                             c->rd.top_p, c->rd.seed, M.dev<int32_t>(o_ids), M.dev<int32_t>(o_pos0), c->out_d,
+                             c->out_d + n * G1, c->resid, c->st));
     if (timed) HIPC(c, hipEventRecord(c->ev[3], c->st));
     HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)(n * G1 + n) * 4, hipMemcpyDeviceToHost, c->st));
     HIPC(c, hipStreamSynchronize(c->st));
     return ER_OK;
   };
   const int r = run();
+  kp_flush(c);
   if (r) { rollback(); return r; }
   c->last_tok_off = o_tok;
   // commit
@@ -956,8 +1144,13 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->gu = (float*)take(L.gu);
     c->logits_p = (float*)take(L.lp);
     c->logits_q = (float*)take(L.lq);
-    c->stats_p = (RowStats*)take(L.sp);
-    c->stats_q = (RowStats*)take(L.sq);
+    c->stats_p = take(L.sp);
+    c->stats_q = take(L.sq);
+    c->resid = (double*)take(L.resid);
+    c->ssq[0] = (unsigned long long*)take(L.ssq / 2);
+    c->ssq[1] = (unsigned long long*)take(L.ssq / 2);
+    c->fuse = c->bf16;
+    c->nch = sampler_chunks(model->vocab);
     c->out_d = (int32_t*)take(L.out);
     c->lws.partial = (float*)take(L.partial);
     c->lws.partial_floats = L.partial / 4;
@@ -998,6 +1191,7 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->have_ev = true;
     // counters start at zero
     if (hipMemsetAsync(c->lws.counters, 0, L.counters, c->st) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "memset"); }
+    if (hipMemsetAsync(c->ssq[0], 0, L.ssq, c->st) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "memset"); }
     // RoPE table: cos/sin of pos * theta^(-2i/hd), fp64 on the host
     {
       const int half = model->head_dim / 2;
@@ -1256,8 +1450,9 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
     }
     HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
     KC(c, launch_row_stats(c->logits_p, next_row, V, V, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
-    KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, V, V, c->rd.temperature, c->rd.seed, M.dev<int32_t>(o_ids),
-                             M.dev<int32_t>(o_pos), 0, PURPOSE_AR, c->out_d, 1, M.dev<int32_t>(o_map), c->st));
+    KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, V, V, c->rd.temperature, c->rd.top_p, c->rd.seed,
+                             M.dev<int32_t>(o_ids), M.dev<int32_t>(o_pos), 0, PURPOSE_AR, c->out_d, 1,
+                             M.dev<int32_t>(o_map), c->st));
     HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)n * 4, hipMemcpyDeviceToHost, c->st));
     HIPC(c, hipStreamSynchronize(c->st));
     c->last_prefill_row.assign(row_of_call.begin(), row_of_call.end());
@@ -1429,6 +1624,12 @@ int er_set_timing(er_ctx* c, int period, int first_n) {
   return ER_OK;
 }
 
+int er_set_fused(er_ctx* c, int on) {
+  if (!c) return ER_EINVAL;
+  c->fuse = c->bf16 && on != 0;
+  return ER_OK;
+}
+
 int er_kv_free_blocks(er_ctx* c, int64_t* free_blocks, int64_t* total_blocks) {
   if (!c) return ER_EINVAL;
   if (free_blocks) *free_blocks = c->pool.free_count();
@@ -1475,6 +1676,44 @@ int er_debug_drafts(er_ctx* c, int32_t* host_out) {
   return ER_OK;
 }
 
+int er_set_kernel_profile(er_ctx* c, int on) {
+  if (!c) return ER_EINVAL;
+  if (on && c->kev.empty()) {
+    c->kev.resize(16384);
+    for (auto& e : c->kev)
+      if (hipEventCreate(&e) != hipSuccess) return fail(c, ER_EDEVICE, "hipEventCreate");
+  }
+  c->kprof = on != 0;
+  c->krec.clear();
+  c->kev_used = 0;
+  return ER_OK;
+}
+
+int er_get_kernel_profile(er_ctx* c, er_kernel_stat* out, int max, int* n_out) {
+  if (!c || !n_out || max < 0 || (max > 0 && !out)) return ER_EINVAL;
+  int i = 0;
+  for (const auto& kv : c->kstat) {
+    if (i < max) {
+      er_kernel_stat& o = out[i];
+      memset(&o, 0, sizeof o);
+      snprintf(o.name, sizeof o.name, "%s", kv.first.c_str());
+      o.launches = kv.second.n;
+      o.ms = kv.second.ms;
+      o.bytes = kv.second.bytes;
+      o.flops = kv.second.flops;
+    }
+    ++i;
+  }
+  *n_out = i;
+  return ER_OK;
+}
+
+int er_reset_kernel_profile(er_ctx* c) {
+  if (!c) return ER_EINVAL;
+  c->kstat.clear();
+  return ER_OK;
+}
+
 int er_controller_choose(const er_cost_model* m, int batch, double mean_ctx, double alpha, int gamma_min,
                          int gamma_max, int current, double margin, int* gamma_out) {
   if (!m || !gamma_out || batch <= 0 || gamma_min < 1 || gamma_max < gamma_min) return ER_EINVAL;
@@ -1496,6 +1735,7 @@ void er_destroy(er_ctx* c) {
   if (c->out_h) (void)hipHostFree(c->out_h);
   if (c->have_ev)
     for (auto& e : c->ev) (void)hipEventDestroy(e);
+  for (auto& e : c->kev) (void)hipEventDestroy(e);
   delete c;
 }
 

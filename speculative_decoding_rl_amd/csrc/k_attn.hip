@@ -8,12 +8,22 @@
 // its own provisional entries for draft positions (EfficientRollout "关键模块"
 // item 1: the drafter shares the target's KV cache).
 //
-// One work-group = (item, kv head, KV split).  All grp = hq/hkv query heads of
-// the KV head and all query positions of the item are handled together, so a
-// K/V block is read from HBM once per (item, kv head) and reused from LDS by
-// every query row.  Softmax is the online (running max / running sum) form;
-// long contexts are split over work-groups and merged by k_attn_combine in a
-// fixed order (deterministic).
+// KV block layout (16 positions): K as [16][hd], V transposed as [hd][16], so
+// that both MFMA operands load as contiguous 16/8-byte pieces.
+//
+// bf16 path (k_attn_mfma): one work-group = (item, kv head, KV split); the
+// grp = hq/hkv query heads of the KV head times the item's query positions
+// form up to 64 "rows", 16 per wave.  Scores are computed transposed,
+// S^T[token][row] = K . Q^T with v_mfma_f32_16x16x32_bf16, which leaves each
+// lane holding 4 consecutive tokens of one row: exactly the A operand of the
+// P.V product (v_mfma_f32_16x16x16_bf16 with V^T as B).  Softmax is the online
+// (running max / running sum) form in fp32; the P operand is rounded to bf16.
+// When the rows fill fewer than 4 waves, the spare waves take interleaved KV
+// blocks and the partial results merge in LDS; long contexts also split over
+// work-groups and merge in k_attn_combine.  All merges run in a fixed order.
+//
+// fp32 path (k_attn_valu): a plain per-row online softmax, one wavefront per
+// row, for the fp32 model (small shapes only).
 
 #include <algorithm>
 
@@ -22,117 +32,245 @@
 
 namespace er {
 
-constexpr int ATT_MAXQ = 64 * 128;  // floats of the query tile in LDS (rows * hd)
+typedef short __attribute__((ext_vector_type(4))) bf16x4s_t;
 
-template <bool BF>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a, int nsplit, int bps) {
-  const int item = blockIdx.x;
-  const int g = blockIdx.y;
-  const int sp = blockIdx.z;
+ER_DEV long kv_block_base(long phys, int layer, int L, int kv, int hkv, int head, int hd) {
+  return ((((phys * L + layer) * 2 + kv) * hkv + head) * 16) * (long)hd;
+}
+
+// Split partial record of one row: [hd] unnormalised output, then running max, then running sum.
+ER_DEV float* partial_row(const AttnArgs& a, int item, int g, int sp, int nsplit, int r) {
+  const int grp = a.hq / a.hkv;
+  return a.ws + ((((long)item * a.hkv + g) * nsplit + sp) * (long)(grp * a.max_q_count) + r) * (a.hd + 2);
+}
+
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int bps) {
+  constexpr int NC = HD / 16;   // 16-column output tiles
+  constexpr int NQ = HD / 32;   // 32-wide k slices of the score MFMA
+  const int item = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hd = a.hd, grp = a.hq / a.hkv;
+  const int l16 = lane & 15, kb = lane >> 4;
+  const int grp = a.hq / a.hkv;
   const int qc = a.item_q_count[item];
   const int pos0 = a.item_q_pos0[item];
   const int qrow0 = a.item_q_row0[item];
   const int R = grp * qc;
-  const int nkeys = pos0 + qc;                 // keys 0..pos0+qc-1
-  const int nblk = (nkeys + 15) >> 4;
+  const int rgroups = (R + 15) >> 4;
+  const int rgn = rgroups == 1 ? 1 : (rgroups == 2 ? 2 : 4);
+  const int s_in = 4 / rgn;                  // waves sharing one row group
+  const int rgi = wave / s_in, sin = wave % s_in;
+  const int nblk = (pos0 + qc + 15) >> 4;
   const int b0 = sp * bps;
   const int b1 = min(nblk, b0 + bps);
-  const float scale = 1.0f / sqrtf((float)hd);
+  const float scale = 1.0f / sqrtf((float)HD);
 
-  __shared__ float qs[ATT_MAXQ];
-  __shared__ float ks[16 * 128];
-  __shared__ float vs[16 * 128];
+  __shared__ float o_sh[4][16 * HD];
+  __shared__ float ml_sh[4][2][16];
 
-  typedef typename Act<BF>::T T;
-  const T* q = (const T*)a.q;
-  for (int idx = tid; idx < R * hd; idx += 256) {
-    const int r = idx / hd, e = idx - r * hd;
-    const int qi = r / grp, hh = g * grp + (r - qi * grp);
-    qs[idx] = Act<BF>::ld(q, ((long)(qrow0 + qi) * a.hq + hh) * hd + e) * scale;
+  // this lane's query row (as the MFMA column n = l16)
+  const int r_q = rgi * 16 + l16;
+  const bool q_ok = rgi < rgroups && r_q < R;
+  const int qi_q = q_ok ? r_q / grp : 0;
+  const int hh_q = g * grp + (q_ok ? r_q % grp : 0);
+  const int qpos_q = pos0 + qi_q;
+
+  // Q^T fragments (B operand): k = 8*kb .. +8 of slice i
+  bf16x8_t qf[NQ];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + ((long)(qrow0 + qi_q) * a.hq + hh_q) * HD;
+#pragma unroll
+    for (int i = 0; i < NQ; ++i) {
+      const uint4 v = q_ok ? *(const uint4*)(qp + 32 * i + 8 * kb) : uint4{0u, 0u, 0u, 0u};
+      qf[i] = __builtin_bit_cast(bf16x8_t, v);
+    }
   }
 
-  // per-row running state, rows r = wave + 4 * j
-  constexpr int RMAX = 16;
-  float mrun[RMAX], lrun[RMAX], acc0[RMAX], acc1[RMAX];
+  f32x4_t o[NC];
 #pragma unroll
-  for (int j = 0; j < RMAX; ++j) { mrun[j] = -INFINITY; lrun[j] = 0.f; acc0[j] = 0.f; acc1[j] = 0.f; }
+  for (int c = 0; c < NC; ++c) o[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
 
-  const int t = lane & 15, sl = lane >> 4;
-  const int slw = hd >> 2;  // elements per slice
-  const T* pool = (const T*)a.kv_pool;
-  const int* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
+  const uint16_t* pool = (const uint16_t*)a.kv_pool;
+  const int32_t* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
 
-  for (int blk = b0; blk < b1; ++blk) {
-    __syncthreads();
-    const long phys = bt[blk];
-    const long kb = ((((phys * a.n_layers + a.layer) * 2 + 0) * a.hkv + g) * 16) * hd;
-    const long vb = ((((phys * a.n_layers + a.layer) * 2 + 1) * a.hkv + g) * 16) * hd;
-    for (int idx = tid; idx < 16 * hd; idx += 256) {
-      ks[idx] = Act<BF>::ld(pool, kb + idx);
-      vs[idx] = Act<BF>::ld(pool, vb + idx);
-    }
-    __syncthreads();
-    const int kpos = blk * 16 + t;
+  if (rgi < rgroups) {
+    for (int blk = b0 + sin; blk < b1; blk += s_in) {
+      const long phys = bt[blk];
+      const uint16_t* kp = pool + kv_block_base(phys, a.layer, a.n_layers, 0, a.hkv, g, HD);
+      const uint16_t* vp = pool + kv_block_base(phys, a.layer, a.n_layers, 1, a.hkv, g, HD);
+      // S^T = K . Q^T: A = K rows (token l16), k = 8*kb + 32*i
+      f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < RMAX; ++j) {
-      const int r = wave + 4 * j;
-      if (r >= R) break;
-      const int qi = r / grp;
-      const int qpos = pos0 + qi;
-      float s = 0.f;
-      const float* qr = qs + r * hd + sl * slw;
-      const float* kr = ks + t * hd + sl * slw;
-      for (int e = 0; e < slw; ++e) s = fmaf(qr[e], kr[e], s);
-      s += __shfl_xor(s, 16, 64);
-      s += __shfl_xor(s, 32, 64);
-      if (kpos > qpos) s = -INFINITY;
-      float mb = s;
-      mb = fmaxf(mb, __shfl_xor(mb, 1, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 2, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 4, 64));
-      mb = fmaxf(mb, __shfl_xor(mb, 8, 64));
-      const float mnew = fmaxf(mrun[j], mb);
-      if (mnew == -INFINITY) continue;  // whole block masked for this row (and nothing before)
-      const float corr = expf(mrun[j] - mnew);
-      const float p = (s == -INFINITY) ? 0.f : expf(s - mnew);
-      float ps = p;
-      ps += __shfl_xor(ps, 1, 64);
-      ps += __shfl_xor(ps, 2, 64);
-      ps += __shfl_xor(ps, 4, 64);
-      ps += __shfl_xor(ps, 8, 64);
-      lrun[j] = lrun[j] * corr + ps;
-      float a0 = acc0[j] * corr, a1 = acc1[j] * corr;
-      for (int tt = 0; tt < 16; ++tt) {
-        const float pt = __shfl(p, tt, 64);
-        a0 = fmaf(pt, vs[tt * hd + lane], a0);
-        if (hd > 64) a1 = fmaf(pt, vs[tt * hd + 64 + lane], a1);
+      for (int i = 0; i < NQ; ++i) {
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const uint4*)(kp + l16 * HD + 32 * i + 8 * kb));
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i], s, 0, 0, 0);
       }
-      acc0[j] = a0;
-      acc1[j] = a1;
-      mrun[j] = mnew;
+      // lane holds tokens 4*kb + r of row l16
+      float mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kpos = blk * 16 + 4 * kb + r;
+        float v = s[r] * scale;
+        if (!q_ok || kpos > qpos_q) v = -INFINITY;
+        s[r] = v;
+        mx = fmaxf(mx, v);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      // P enters the P.V product as two bf16 terms, p = hi + lo (hi = bf16(p),
+      // lo = bf16(p - hi)): V is exact in bf16, so the product keeps ~16
+      // mantissa bits of p instead of 8 at the cost of a second small MFMA.
+      float corr, psum = 0.f;
+      uint32_t pk[2], pl[2];
+      if (m_new == -INFINITY) {
+        corr = 1.f;
+        pk[0] = pk[1] = pl[0] = pl[1] = 0u;
+      } else {
+        corr = expf(m_run - m_new);
+        float p[4];
+        uint32_t hb[4], lb[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = (s[r] == -INFINITY) ? 0.f : expf(s[r] - m_new);
+          psum += p[r];
+          hb[r] = f2bf(p[r]);
+          lb[r] = f2bf(p[r] - bf2f((uint16_t)hb[r]));
+        }
+        pk[0] = hb[0] | (hb[1] << 16);
+        pk[1] = hb[2] | (hb[3] << 16);
+        pl[0] = lb[0] | (lb[1] << 16);
+        pl[1] = lb[2] | (lb[3] << 16);
+      }
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run = l_run * corr + psum;
+      m_run = m_new;
+      // rescale O rows (rows 4*kb + r live in lanes l16 == 4*kb + r of the score layout)
+      float cr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * kb + r, 64);
+      const bf16x4s_t pa = __builtin_bit_cast(bf16x4s_t, *(const uint2*)pk);
+      const bf16x4s_t pb = __builtin_bit_cast(bf16x4s_t, *(const uint2*)pl);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[c][r] *= cr[r];
+        // B = V^T: n = column 16c + l16, k = tokens 4*kb .. +4
+        const bf16x4s_t vf = __builtin_bit_cast(bf16x4s_t, *(const uint2*)(vp + (16 * c + l16) * 16 + 4 * kb));
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[c], 0, 0, 0);
+        o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vf, o[c], 0, 0, 0);
+      }
     }
   }
 
-  // write out
-  T* out = (T*)a.out;
+  // merge the s_in waves of each row group (fixed order), then normalise or emit partials
+  if (s_in > 1) {
 #pragma unroll
-  for (int j = 0; j < RMAX; ++j) {
-    const int r = wave + 4 * j;
-    if (r >= R) break;
-    const int qi = r / grp, hh = g * grp + (r - qi * grp);
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o_sh[wave][(4 * kb + r) * HD + 16 * c + l16] = o[c][r];
+    if (kb == 0) { ml_sh[wave][0][l16] = m_run; ml_sh[wave][1][l16] = l_run; }
+    __syncthreads();
+    if (sin != 0) return;
+    float M = -INFINITY;
+    for (int w = wave; w < wave + s_in; ++w) M = fmaxf(M, ml_sh[w][0][l16]);
+    float lsum = 0.f;
+    float wgt[4];
+    for (int w = 0; w < s_in; ++w) {
+      const float mw = ml_sh[wave + w][0][l16];
+      const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
+      lsum += f * ml_sh[wave + w][1][l16];
+      if (w < 4) wgt[w] = f;
+    }
+    // o rows are in the row layout (4*kb + r); fetch each row's weights from lane 4*kb + r
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v = 0.f;
+        for (int w = 0; w < s_in; ++w) {
+          const float f = __shfl(wgt[w], 4 * kb + r, 64);
+          v += f * o_sh[wave + w][(4 * kb + r) * HD + 16 * c + l16];
+        }
+        o[c][r] = v;
+      }
+    m_run = M;
+    l_run = lsum;
+  }
+  if (rgi >= rgroups) return;
+
+  float rl[4], rm[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    rl[r] = __shfl(l_run, 4 * kb + r, 64);
+    rm[r] = __shfl(m_run, 4 * kb + r, 64);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rr = rgi * 16 + 4 * kb + r;
+    if (rr >= R) continue;
+    const int qi = rr / grp, hh = g * grp + rr % grp;
     if (nsplit == 1) {
-      const float inv = lrun[j] > 0.f ? 1.0f / lrun[j] : 0.f;
-      const long o = ((long)(qrow0 + qi) * a.hq + hh) * hd;
-      if (lane < hd) Act<BF>::st(out, o + lane, acc0[j] * inv);
-      if (hd > 64) Act<BF>::st(out, o + 64 + lane, acc1[j] * inv);
+      const float inv = rl[r] > 0.f ? 1.0f / rl[r] : 0.f;
+      uint16_t* out = (uint16_t*)a.out + ((long)(qrow0 + qi) * a.hq + hh) * HD;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) out[16 * c + l16] = (uint16_t)f2bf(o[c][r] * inv);
     } else {
-      // partial: [item][g][sp][r][hd + 2]
-      float* pp = a.ws + ((((long)item * a.hkv + g) * nsplit + sp) * (long)(grp * a.max_q_count) + r) * (hd + 2);
-      if (lane < hd) pp[lane] = acc0[j];
-      if (hd > 64) pp[64 + lane] = acc1[j];
-      if (lane == 0) { pp[hd] = mrun[j]; pp[hd + 1] = lrun[j]; }
+      float* pp = partial_row(a, item, g, sp, nsplit, rr);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) pp[16 * c + l16] = o[c][r];
+      if (l16 == 0) { pp[HD] = rm[r]; pp[HD + 1] = rl[r]; }
+    }
+  }
+}
+
+// fp32 (small models): one wavefront per row, keys streamed from the pool.
+__global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int nsplit, int bps) {
+  const int item = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int hd = a.hd, grp = a.hq / a.hkv;
+  const int qc = a.item_q_count[item], pos0 = a.item_q_pos0[item], qrow0 = a.item_q_row0[item];
+  const int R = grp * qc;
+  const int nkeys = pos0 + qc;
+  const int k0 = sp * bps * 16;
+  const int k1 = min(nkeys, k0 + bps * 16);
+  const float scale = 1.0f / sqrtf((float)hd);
+  const float* pool = (const float*)a.kv_pool;
+  const int32_t* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
+  for (int r = wave; r < R; r += 4) {
+    const int qi = r / grp, hh = g * grp + r % grp;
+    const int qpos = pos0 + qi;
+    const float* q = (const float*)a.q + ((long)(qrow0 + qi) * a.hq + hh) * hd;
+    const float q0 = lane < hd ? q[lane] : 0.f;
+    const float q1 = lane + 64 < hd ? q[lane + 64] : 0.f;
+    float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
+    const int kend = min(k1, qpos + 1);
+    for (int k = k0; k < kend; ++k) {
+      const long phys = bt[k >> 4];
+      const int t = k & 15;
+      const float* kr = pool + kv_block_base(phys, a.layer, a.n_layers, 0, a.hkv, g, hd) + t * hd;
+      const float* vb = pool + kv_block_base(phys, a.layer, a.n_layers, 1, a.hkv, g, hd);
+      float s = (lane < hd ? q0 * kr[lane] : 0.f) + (lane + 64 < hd ? q1 * kr[lane + 64] : 0.f);
+      s = wave_sum(s) * scale;
+      const float mn = fmaxf(m, s);
+      const float c = expf(m - mn), p = expf(s - mn);
+      l = l * c + p;
+      if (lane < hd) o0 = o0 * c + p * vb[lane * 16 + t];
+      if (lane + 64 < hd) o1 = o1 * c + p * vb[(lane + 64) * 16 + t];
+      m = mn;
+    }
+    if (nsplit == 1) {
+      float* out = (float*)a.out + ((long)(qrow0 + qi) * a.hq + hh) * hd;
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      if (lane < hd) out[lane] = o0 * inv;
+      if (lane + 64 < hd) out[lane + 64] = o1 * inv;
+    } else {
+      float* pp = partial_row(a, item, g, sp, nsplit, r);
+      if (lane < hd) pp[lane] = o0;
+      if (lane + 64 < hd) pp[lane + 64] = o1;
+      if (lane == 0) { pp[hd] = m; pp[hd + 1] = l; }
     }
   }
 }
@@ -144,7 +282,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int nsplit) {
   const int qc = a.item_q_count[item];
   if (r >= grp * qc) return;
   const long stride_sp = (long)(grp * a.max_q_count) * (hd + 2);
-  const float* base = a.ws + ((((long)item * a.hkv + g) * nsplit) * (long)(grp * a.max_q_count) + r) * (hd + 2);
+  const float* base = partial_row(a, item, g, 0, nsplit, r);
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * stride_sp + hd]);
   const int e = threadIdx.x;
@@ -169,9 +307,10 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
   if (a.n_items <= 0) return 0;
   const int grp = a.hq / a.hkv;
   if ((a.hd != 64 && a.hd != 128) || a.hq % a.hkv != 0) return -1;
-  if (grp * a.max_q_count > 64 || grp * a.max_q_count * a.hd > ATT_MAXQ) return -1;
+  if (grp * a.max_q_count > 64) return -1;
   const int maxblk = (a.max_ctx + 15) / 16;
-  long base = (long)a.n_items * a.hkv;
+  const long base = (long)a.n_items * a.hkv;
+  // split the keys over work-groups until ~512 groups are in flight (>= 4 blocks each)
   int nsplit = (int)std::max(1L, std::min((long)(maxblk + 3) / 4, (512 + base - 1) / base));
   const int bps = (maxblk + nsplit - 1) / nsplit;
   nsplit = (maxblk + bps - 1) / bps;
@@ -180,8 +319,12 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
     if (need > a.ws_floats) return -2;
   }
   dim3 grid(a.n_items, a.hkv, nsplit);
-  if (a.bf16) hipLaunchKernelGGL(k_attn<true>, grid, dim3(256), 0, st, a, nsplit, bps);
-  else hipLaunchKernelGGL(k_attn<false>, grid, dim3(256), 0, st, a, nsplit, bps);
+  if (a.bf16) {
+    if (a.hd == 128) hipLaunchKernelGGL(k_attn_mfma<128>, grid, dim3(256), 0, st, a, nsplit, bps);
+    else hipLaunchKernelGGL(k_attn_mfma<64>, grid, dim3(256), 0, st, a, nsplit, bps);
+  } else {
+    hipLaunchKernelGGL(k_attn_valu, grid, dim3(256), 0, st, a, nsplit, bps);
+  }
   if (hipGetLastError() != hipSuccess) return -3;
   if (nsplit > 1) {
     dim3 g2(a.n_items, a.hkv, grp * a.max_q_count);

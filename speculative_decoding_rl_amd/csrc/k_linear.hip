@@ -8,14 +8,17 @@
 //    straight into registers and fed to v_mfma_f32_16x16x32_bf16.  Quantized
 //    codes are turned into bf16 with exponent-field tricks (no per-element
 //    int->float conversion for W4), and the zero points are folded out per
-//    128-wide K chunk with row sums of x.  Split-K across work-groups with a
-//    deterministic last-arriving-group reduction keeps >= ~4 groups per CU for
-//    the narrow projections; the block index is remapped so that the m-tiles
-//    sharing a weight tile land on the same XCD (and its L2).
+//    128-wide K chunk with row sums of x.  Narrow projections split K across
+//    the 8 waves of a work-group and reduce in LDS (deterministic, and no
+//    device-scope fence: on gfx950 one costs an L2 write-back per group);
+//    the block index is remapped so that the m-tiles sharing a weight tile
+//    land on the same XCD (and its L2).
 //
 // The drafter kernels are the dequant-fused GEMV/skinny-GEMM of the
 // EfficientRollout page ("关键模块" item 1: W4/W8 drafter from the target's own
 // weights); the verify kernels are the target's linears at M = B * (gamma+1).
+
+#include <cstdio>
 
 #include "common.h"
 #include "kernels.h"
@@ -84,13 +87,13 @@ __global__ __launch_bounds__(256) void k_linear_valu(const void* __restrict__ xv
 }
 
 // ----------------------------------------------------------------------------
-// MFMA skinny GEMM.
+// MFMA linears (bf16 activations) with fused prologue / epilogue.
 // ----------------------------------------------------------------------------
 template <int FMT> struct WRegs { static constexpr int n = (FMT == FMT_BF16) ? 4 : (FMT == FMT_W8 ? 2 : 1); };
 
-// LDS column (in bf16 elements within the 128-wide chunk) of the 8 k-slots that
-// lane group kb feeds to MFMA number i; the same mapping decides which weight
-// bytes a lane loads, so A and B agree on every k.
+// LDS/register column (in bf16 elements within the 128-wide chunk) of the 8
+// k-slots that lane group kb feeds to MFMA number i; the same mapping decides
+// which weight bytes a lane loads, so A and B agree on every k.
 template <int FMT>
 ER_DEV int kcol(int i, int kb) {
   if constexpr (FMT == FMT_BF16) return 32 * i + 8 * kb;
@@ -123,42 +126,143 @@ ER_DEV bf16x8_t w4_to_bf16(uint32_t w) {
   return __builtin_bit_cast(bf16x8_t, *(const uint4*)r);
 }
 
-template <int FMT, int MT, int NR>
-__global__ __launch_bounds__(256) void k_linear_mfma(
-    const uint16_t* __restrict__ x, int ldx, int M, const void* __restrict__ wv,
-    const void* __restrict__ sv, const void* __restrict__ zv, int N, int K, void* __restrict__ yv,
-    int ldy, int epi, int act_bf16, int mtiles, int nsplit, int cps, float* __restrict__ partial,
-    int* __restrict__ counters) {
-  constexpr int MI = MT / 16;
-  constexpr int NT = 64 * NR;
-  constexpr int LDSR = 136;  // 128 + 8 bf16 of padding per row
-  constexpr int WR = WRegs<FMT>::n;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT * LDSR];
-  __shared__ float xsum[2][MT];
-  __shared__ int s_last;
+// Physical weight row of logical row 16*s + l16.  Paired epilogues need the
+// two operands of each pair in lanes l16 and l16 ^ 8 of one 16-row subtile:
+// SwiGLU pairs gate row f with up row F + f; RoPE pairs rows i and i + hd/2
+// of a head.  Other epilogues use the identity.
+ER_DEV int phys_row(const LinArgs& a, int s, int l16) {
+  if (a.epi == EPI_SWIGLU) {
+    const int f = s * 8 + (l16 & 7);
+    return (l16 & 8) ? a.F + f : f;
+  }
+  if (a.epi == EPI_QKV) {
+    const int per_head = a.hd >> 4;  // subtiles per head
+    const int h = s / per_head, pb = (s - h * per_head) * 8;
+    return h * a.hd + pb + (l16 & 7) + ((l16 & 8) ? (a.hd >> 1) : 0);
+  }
+  return 16 * s + l16;
+}
 
-  // XCD-aware logical index: consecutive logical ids run on one XCD.
+ER_DEV float rstd_of(const LinArgs& a, long hrow) {
+  const double ss = (double)a.ssq_in[hrow] / SSQ_SCALE;
+  return 1.0f / sqrtf((float)ss / (float)a.W.K + a.eps);
+}
+
+// 8 consecutive x' values (bf16) of row m at column k0.
+ER_DEV uint4 load_x8(const LinArgs& a, long hrow, float rs, long k0) {
+  if (!a.xnorm) return *(const uint4*)((const uint16_t*)a.x + hrow * a.ldx + k0);
+  const float* hp = (const float*)a.x + hrow * a.ldx + k0;
+  const float4 h0 = *(const float4*)hp, h1 = *(const float4*)(hp + 4);
+  const uint4 g = *(const uint4*)((const uint16_t*)a.gnorm + k0);
+  uint4 o;
+  o.x = f2bf(h0.x * rs * bf_lo(g.x)) | (f2bf(h0.y * rs * bf_hi(g.x)) << 16);
+  o.y = f2bf(h0.z * rs * bf_lo(g.y)) | (f2bf(h0.w * rs * bf_hi(g.y)) << 16);
+  o.z = f2bf(h1.x * rs * bf_lo(g.z)) | (f2bf(h1.y * rs * bf_hi(g.z)) << 16);
+  o.w = f2bf(h1.z * rs * bf_lo(g.w)) | (f2bf(h1.w * rs * bf_hi(g.w)) << 16);
+  return o;
+}
+
+// Epilogue for the value v of (row m, physical column n); partner = the value
+// of lane l16 ^ 8 (the other half of a SwiGLU / RoPE pair).  `write` is false
+// for lanes whose m or n is out of range (they still provide partners).
+ER_DEV void epilogue(const LinArgs& a, int m, int n, float v, float partner, bool write, int l16) {
+  if (!write) return;
+  if (a.epi == EPI_SWIGLU) {
+    if (l16 & 8) return;  // gate lane writes silu(g) * u
+    const float r = v / (1.0f + expf(-v)) * partner;
+    ((uint16_t*)a.y)[(long)m * a.ldy + n] = (uint16_t)f2bf(r);
+    return;
+  }
+  if (a.epi == EPI_QKV) {
+    const int hd = a.hd, half = hd >> 1;
+    const int head = n / hd, i = n - head * hd;
+    const long sl = a.slot[m];
+    if (head < a.hq + a.hkv) {
+      const int ip = i & (half - 1);
+      const float2 c = a.cs[(long)a.pos[m] * half + ip];
+      const float r = (i < half) ? v * c.x - partner * c.y : v * c.x + partner * c.y;
+      if (head < a.hq) {
+        ((uint16_t*)a.qout)[((long)m * a.hq + head) * hd + i] = (uint16_t)f2bf(r);
+      } else {
+        const long blk = sl >> 4;
+        const long o = ((((blk * a.n_layers + a.layer) * 2 + 0) * a.hkv + (head - a.hq)) * 16 + (sl & 15)) * hd + i;
+        ((uint16_t*)a.kv_pool)[o] = (uint16_t)f2bf(r);
+      }
+    } else {
+      const long blk = sl >> 4;
+      const int g = head - a.hq - a.hkv;
+      const long o = ((((blk * a.n_layers + a.layer) * 2 + 1) * a.hkv + g) * 16) * (long)hd + (long)i * 16 + (sl & 15);
+      ((uint16_t*)a.kv_pool)[o] = (uint16_t)f2bf(v);
+    }
+    return;
+  }
+  const long o = (long)m * a.ldy + n;
+  if (a.epi == EPI_RESID) ((float*)a.y)[o] += v;
+  else if (a.epi == EPI_ACT && a.act_bf16) ((uint16_t*)a.y)[o] = (uint16_t)f2bf(v);
+  else ((float*)a.y)[o] = v;
+}
+
+// Sum of squares of the updated residual rows: `sq` is this lane's
+// contribution to row m; the 16 lanes of each lane group (lane / 16) are
+// summed and the group's lane `lead` adds the total (callers whose row spans
+// several groups reduce across them first and pass one leader).
+ER_DEV void ssq_add(const LinArgs& a, int m, float sq, bool lead, bool mok) {
+  sq += __shfl_xor(sq, 1, 64);
+  sq += __shfl_xor(sq, 2, 64);
+  sq += __shfl_xor(sq, 4, 64);
+  sq += __shfl_xor(sq, 8, 64);
+  if (lead && mok) atomicAdd(a.ssq_acc + m, (unsigned long long)rint((double)sq * SSQ_SCALE));
+}
+
+// ----------------------------------------------------------------------------
+// Skinny MFMA linear (M <= 32).  One work-group = 8 waves over
+// R = 16 * NR * (8 / KS) output rows and one m-tile of MT rows of x.  Wave w
+// owns the 16*NR rows starting at 16 * NR * (w / KS) and the K chunks
+// c = w % KS, w % KS + KS, ... (128 inputs per chunk); the KS partial tiles
+// of a row group are summed in LDS in a fixed order, so the result is
+// deterministic and no device-scope fence is needed (on gfx950 one costs an
+// L2 write-back per work-group).  Weights and x fragments are loaded straight
+// into registers (x is L1/L2 resident at these M; rows >= M are not loaded);
+// each x fragment feeds NR weight subtiles, and the next chunk is in flight
+// while the current one is multiplied.  The block index is remapped so that
+// the m-tiles sharing a weight tile land on the same XCD (and its L2).
+// ----------------------------------------------------------------------------
+template <int FMT, int MT, int NR, int KS>
+__global__ __launch_bounds__(512) void k_linear_mfma(LinArgs a, int mtiles) {
+  constexpr int MI = MT / 16;
+  constexpr int RG = 8 / KS;
+  constexpr int R = 16 * NR * RG;
+  constexpr int WR = WRegs<FMT>::n;
+  __shared__ f32x4_t red[(KS > 1) ? 8 * MI * NR * 64 : 1];
+
   const int b = blockIdx.x, nwg = gridDim.x;
   const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
   const int L = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
   const int mt = L % mtiles;
-  const int t2 = L / mtiles;
-  const int sp = t2 % nsplit;
-  const int nt = t2 / nsplit;
+  const int nt = L / mtiles;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave / KS, ks = wave % KS;
   const int kb = lane >> 4, l16 = lane & 15;
   const int m0 = mt * MT;
+  const int M = a.M, N = a.W.N, K = a.W.K;
   const int nchunks = K >> 7;
-  const int c0 = sp * cps;
-  const int c1 = min(nchunks, c0 + cps);
   const long G = K >> 7;
+  const void* __restrict__ wv = a.W.w;
+  const void* __restrict__ sv = a.W.scale;
+  const void* __restrict__ zv = a.W.zero;
 
-  int nrow[NR];
+  if (b == 0 && a.ssq_zero)
+    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+
+  int n_lane[NR];
+  long nrow[NR];
 #pragma unroll
   for (int ni = 0; ni < NR; ++ni) {
-    const int n = nt * NT + wave * 16 * NR + ni * 16 + l16;
-    nrow[ni] = n < N ? n : N - 1;  // clamp loads; results past N are dropped
+    const int s = (nt * RG + rg) * NR + ni;  // logical 16-row subtile
+    const bool in = 16 * s + l16 < N;
+    n_lane[ni] = in ? phys_row(a, s, l16) : N;
+    nrow[ni] = in ? n_lane[ni] : N - 1;      // clamp loads; results past N are dropped
   }
 
   f32x4_t acc[MI][NR];
@@ -167,56 +271,50 @@ __global__ __launch_bounds__(256) void k_linear_mfma(
 #pragma unroll
     for (int ni = 0; ni < NR; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 wreg[2][NR][WR];
-  float wsc[2][NR], wz[2][NR];
-  uint4 xreg[MI];
+  long xrow[MI];
+  bool xok[MI];
+  float xrs[MI];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi) {
+    const int m = m0 + mi * 16 + l16;
+    xok[mi] = m < M;
+    xrow[mi] = xok[mi] ? (a.xrow ? a.xrow[m] : m) : 0;
+    xrs[mi] = (a.xnorm && xok[mi]) ? rstd_of(a, xrow[mi]) : 1.f;
+  }
 
-  auto load_w = [&](int c, int buf) {
+  uint4 wreg[2][NR][WR];
+  uint4 xreg[2][MI][4];
+  float wsc[2][NR], wz[2][NR];
+
+  auto load = [&](int c, int buf) {
 #pragma unroll
     for (int ni = 0; ni < NR; ++ni) {
-      const long n = nrow[ni];
       if constexpr (FMT == FMT_BF16) {
-        const uint16_t* p = (const uint16_t*)wv + n * K + (long)c * 128;
+        const uint16_t* p = (const uint16_t*)wv + nrow[ni] * K + (long)c * 128;
 #pragma unroll
         for (int i = 0; i < 4; ++i) wreg[buf][ni][i] = *(const uint4*)(p + kcol<FMT>(i, kb));
       } else if constexpr (FMT == FMT_W8) {
-        const int8_t* p = (const int8_t*)wv + n * K + (long)c * 128;
+        const int8_t* p = (const int8_t*)wv + nrow[ni] * K + (long)c * 128;
 #pragma unroll
         for (int h = 0; h < 2; ++h) wreg[buf][ni][h] = *(const uint4*)(p + 64 * h + 16 * kb);
       } else {
-        const uint8_t* p = (const uint8_t*)wv + (n * K + (long)c * 128) / 2;
+        const uint8_t* p = (const uint8_t*)wv + (nrow[ni] * K + (long)c * 128) / 2;
         wreg[buf][ni][0] = *(const uint4*)(p + 16 * kb);
-        wsc[buf][ni] = bf2f(((const uint16_t*)sv)[n * G + c]);
-        wz[buf][ni] = 128.0f + (float)((const uint8_t*)zv)[n * G + c];
+        wsc[buf][ni] = bf2f(((const uint16_t*)sv)[nrow[ni] * G + c]);
+        wz[buf][ni] = 128.0f + (float)((const uint8_t*)zv)[nrow[ni] * G + c];
+      }
+    }
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint4 v = uint4{0u, 0u, 0u, 0u};
+        if (xok[mi]) v = load_x8(a, xrow[mi], xrs[mi], (long)c * 128 + kcol<FMT>(i, kb));
+        xreg[buf][mi][i] = v;
       }
     }
   };
-  auto load_x = [&](int c) {
-#pragma unroll
-    for (int p = 0; p < MI; ++p) {
-      const int row = p * 16 + (tid >> 4);
-      const int m = m0 + row;
-      if (m < M) xreg[p] = *(const uint4*)(x + (long)m * ldx + (long)c * 128 + (tid & 15) * 8);
-      else xreg[p] = uint4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < MI; ++p) {
-      const int row = p * 16 + (tid >> 4);
-      *(uint4*)(&xs[buf][row * LDSR + (tid & 15) * 8]) = xreg[p];
-      if constexpr (FMT != FMT_BF16) {
-        const uint4 v = xreg[p];
-        float sm = bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) +
-                   bf_lo(v.w) + bf_hi(v.w);
-        sm += __shfl_xor(sm, 1, 64);
-        sm += __shfl_xor(sm, 2, 64);
-        sm += __shfl_xor(sm, 4, 64);
-        sm += __shfl_xor(sm, 8, 64);
-        if ((tid & 15) == 0) xsum[buf][row] = sm;
-      }
-    }
-  };
+
   auto compute = [&](int buf) {
     f32x4_t accg[MI][NR];
     if constexpr (FMT != FMT_BF16) {
@@ -243,22 +341,32 @@ __global__ __launch_bounds__(256) void k_linear_mfma(
       }
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        const bf16x8_t a = *(const bf16x8_t*)(&xs[buf][(mi * 16 + l16) * LDSR + kcol<FMT>(i, kb)]);
+        const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xreg[buf][mi][i]);
 #pragma unroll
         for (int ni = 0; ni < NR; ++ni) {
           if constexpr (FMT == FMT_BF16)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[ni], acc[mi][ni], 0, 0, 0);
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw[ni], acc[mi][ni], 0, 0, 0);
           else
-            accg[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bw[ni], accg[mi][ni], 0, 0, 0);
+            accg[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw[ni], accg[mi][ni], 0, 0, 0);
         }
       }
     }
     if constexpr (FMT != FMT_BF16) {
+      // zero-point / offset correction needs the chunk's row sums of x':
+      // this lane holds 32 of row l16's 128 values; 4 lanes (kb) hold the rest.
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
+        float sm = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = xreg[buf][mi][i];
+          sm += bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) + bf_lo(v.w) + bf_hi(v.w);
+        }
+        sm += __shfl_xor(sm, 16, 64);
+        sm += __shfl_xor(sm, 32, 64);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float xsm = xsum[buf][mi * 16 + 4 * kb + r];
+          const float xsm = __shfl(sm, 4 * kb + r, 64);  // row 4*kb + r of this m-subtile
 #pragma unroll
           for (int ni = 0; ni < NR; ++ni) {
             if constexpr (FMT == FMT_W8)
@@ -271,26 +379,17 @@ __global__ __launch_bounds__(256) void k_linear_mfma(
     }
   };
 
-  if (c0 < c1) {
-    load_w(c0, 0);
-    load_x(c0);
-    store_x(0);
-    __syncthreads();
+  if (ks < nchunks) {
+    load(ks, 0);
     int buf = 0;
-    for (int c = c0; c < c1; ++c) {
-      const bool nxt = c + 1 < c1;
-      if (nxt) {
-        if (buf == 0) load_w(c + 1, 1); else load_w(c + 1, 0);
-        load_x(c + 1);
-      }
+    for (int c = ks; c < nchunks; c += KS) {
+      const bool nxt = c + KS < nchunks;
+      if (nxt) { if (buf == 0) load(c + KS, 1); else load(c + KS, 0); }
       if (buf == 0) compute(0); else compute(1);
-      if (nxt) { if (buf == 0) store_x(1); else store_x(0); }
-      __syncthreads();
       buf ^= 1;
     }
   }
 
-  // W8: per-row scale.
   if constexpr (FMT == FMT_W8) {
 #pragma unroll
     for (int ni = 0; ni < NR; ++ni) {
@@ -302,132 +401,378 @@ __global__ __launch_bounds__(256) void k_linear_mfma(
     }
   }
 
-  if (nsplit > 1) {
-    const long tile = (long)mt + (long)mtiles * nt;
-    float* pp = partial + (tile * nsplit + sp) * (long)(MT * NT);
+  if constexpr (KS > 1) {
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NR; ++ni)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pp[(((wave * MI + mi) * NR + ni) * 4 + r) * 64 + lane] = acc[mi][ni][r];
-    __threadfence();
+      for (int ni = 0; ni < NR; ++ni) red[((wave * MI + mi) * NR + ni) * 64 + lane] = acc[mi][ni];
     __syncthreads();
-    if (tid == 0) {
-      const int prev = atomicAdd(&counters[tile], 1);
-      s_last = (prev == nsplit - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-    const float* p0 = partial + tile * nsplit * (long)(MT * NT);
+    if (ks != 0) return;
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < NR; ++ni)
+      for (int ni = 0; ni < NR; ++ni) {
+        f32x4_t v = red[((wave * MI + mi) * NR + ni) * 64 + lane];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const long o = (((wave * MI + mi) * NR + ni) * 4 + r) * 64 + lane;
-          float v = 0.f;
-          for (int q = 0; q < nsplit; ++q) v += __builtin_nontemporal_load(p0 + (long)q * (MT * NT) + o);
-          acc[mi][ni][r] = v;
+        for (int s = 1; s < KS; ++s) {
+          const f32x4_t o = red[(((wave + s) * MI + mi) * NR + ni) * 64 + lane];
+          v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
         }
-    if (tid == 0) counters[tile] = 0;
-  }
-
-#pragma unroll
-  for (int ni = 0; ni < NR; ++ni) {
-    const int n = nt * NT + wave * 16 * NR + ni * 16 + l16;
-    if (n >= N) continue;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + mi * 16 + 4 * kb + r;
-        if (m >= M) continue;
-        const long o = (long)m * ldy + n;
-        const float v = acc[mi][ni][r];
-        if (epi == EPI_RESID) ((float*)yv)[o] += v;
-        else if (epi == EPI_ACT && act_bf16) ((uint16_t*)yv)[o] = (uint16_t)f2bf(v);
-        else ((float*)yv)[o] = v;
+        acc[mi][ni] = v;
       }
   }
+
+  const bool want_ssq = a.epi == EPI_RESID && a.ssq_acc;
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = m0 + mi * 16 + 4 * kb + r;
+      const bool mok = m < M;
+      float sq = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni) {
+        const float v = acc[mi][ni][r];
+        const float partner = __shfl_xor(v, 8, 64);
+        const bool ok = mok && n_lane[ni] < N;
+        epilogue(a, m, n_lane[ni], v, partner, ok, l16);
+        if (want_ssq && ok) {
+          const float hn = ((const float*)a.y)[(long)m * a.ldy + n_lane[ni]];
+          sq = fmaf(hn, hn, sq);
+        }
+      }
+      if (want_ssq) ssq_add(a, m, sq, l16 == 0, mok);
+    }
 }
 
 // ----------------------------------------------------------------------------
-template <int FMT, int MT, int NR>
-static int run_mfma(const void* x, int ldx, int M, const LinearW& W, void* y, int ldy, int epi, bool act_bf16,
-                    const LinearWs& ws, hipStream_t st) {
-  constexpr int NT = 64 * NR;
-  const int mtiles = (M + MT - 1) / MT;
-  const int ntiles = (W.N + NT - 1) / NT;
-  const int nchunks = W.K / 128;
+// Tiled bf16 GEMM for M > 32 (verify at moderate batch, AR at large batch,
+// prefill): 128x128 output tile per work-group (4 waves, 64x64 each, 16x16x32
+// MFMA), both operands staged through double-buffered LDS in 64-wide K steps,
+// next step's global loads in flight during the current MFMAs.  Narrow
+// outputs split K over work-groups; partial tiles then go to a workspace and
+// k_splitk_reduce sums them in a fixed order and applies the epilogue.
+// ----------------------------------------------------------------------------
+constexpr int GB_M = 128, GB_N = 128, GB_K = 64, GB_LD = GB_K + 8;
+
+__global__ __launch_bounds__(256) void k_gemm_bf16(LinArgs a, float* __restrict__ part, int nsplit,
+                                                   int ksteps_per_split, int mtiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][GB_M * GB_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GB_N * GB_LD];
+  __shared__ float rs_sh[GB_M];
+  const int b = blockIdx.x, nwg = gridDim.x;
+  const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
+  const int L = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+  const int mt = L % mtiles;
+  const int t2 = L / mtiles;
+  const int sp = t2 % nsplit;
+  const int nt = t2 / nsplit;
+  const int M = a.M, N = a.W.N, K = a.W.K;
+  const int m0 = mt * GB_M, n0 = nt * GB_N;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kb = lane >> 4, l16 = lane & 15;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int nsteps = K / GB_K;
+  const int s0 = sp * ksteps_per_split;
+  const int s1 = min(nsteps, s0 + ksteps_per_split);
+  const uint16_t* __restrict__ W = (const uint16_t*)a.W.w;
+
+  if (b == 0 && a.ssq_zero && nsplit == 1)
+    for (int m = tid; m < M; m += 256) a.ssq_zero[m] = 0ull;
+  if (tid < GB_M) {
+    const int m = m0 + tid;
+    rs_sh[tid] = (a.xnorm && m < M) ? rstd_of(a, a.xrow ? a.xrow[m] : m) : 1.f;
+  }
+  __syncthreads();
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // weight tile rows: 16-row subtiles s = n0/16 + row/16 in the epilogue's row order
+  long wrow[4];
+  bool wok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (tid + 256 * i) >> 3;
+    const int s = (n0 >> 4) + (row >> 4);
+    wok[i] = n0 + row < N;
+    wrow[i] = wok[i] ? phys_row(a, s, row & 15) : 0;
+  }
+  uint4 ra[4], rb[4];
+  auto gload = [&](int st) {
+    const long k0 = (long)st * GB_K;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx >> 3, c8 = (idx & 7) * 8;
+      const int m = m0 + row;
+      ra[i] = uint4{0u, 0u, 0u, 0u};
+      if (m < M) ra[i] = load_x8(a, a.xrow ? a.xrow[m] : m, rs_sh[row], k0 + c8);
+      rb[i] = wok[i] ? *(const uint4*)(W + wrow[i] * K + k0 + c8) : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i;
+      const int row = idx >> 3, c8 = (idx & 7) * 8;
+      *(uint4*)(&As[buf][row * GB_LD + c8]) = ra[i];
+      *(uint4*)(&Bs[buf][row * GB_LD + c8]) = rb[i];
+    }
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        af[i] = *(const bf16x8_t*)(&As[buf][(64 * wm + 16 * i + l16) * GB_LD + 32 * ks + 8 * kb]);
+        bfr[i] = *(const bf16x8_t*)(&Bs[buf][(64 * wn + 16 * i + l16) * GB_LD + 32 * ks + 8 * kb]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (s0 < s1) {
+    gload(s0);
+    sstore(0);
+    __syncthreads();
+    int buf = 0;
+    for (int st = s0; st < s1; ++st) {
+      const bool nxt = st + 1 < s1;
+      if (nxt) gload(st + 1);
+      mma(buf);
+      if (nxt) sstore(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+  }
+
+  // Stage the 128x128 tile through LDS (reusing the operand buffers) so the
+  // epilogue walks it row-wise: coalesced stores, pair partners at column ^ 8,
+  // one sum-of-squares partial per (row, 64 columns).
+  // acc[i][j][r] is row 64 wm + 16 i + 4 kb + r, column 64 wn + 16 j + l16.
+  float* Cs = reinterpret_cast<float*>(&As[0][0]);
+  constexpr int CLD = GB_N + 4;
+  static_assert(sizeof(As) + sizeof(Bs) >= sizeof(float) * GB_M * CLD, "C tile does not fit");
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Cs[(64 * wm + 16 * i + 4 * kb + r) * CLD + 64 * wn + 16 * j + l16] = acc[i][j][r];
+  __syncthreads();
+  const bool want_ssq = a.epi == EPI_RESID && a.ssq_acc && nsplit == 1;
+  for (int e = tid; e < GB_M * GB_N; e += 256) {
+    const int row = e >> 7, col = e & 127;  // a wave covers 64 columns of one row
+    const int m = m0 + row, nl = n0 + col;
+    const bool mok = m < M, nok = nl < N;
+    const int n = nok ? phys_row(a, nl >> 4, nl & 15) : N;
+    const float v = Cs[row * CLD + col];
+    float sq = 0.f;
+    if (nsplit > 1) {
+      if (mok && nok) part[((long)sp * M + m) * N + n] = v;
+    } else {
+      epilogue(a, m, n, v, Cs[row * CLD + (col ^ 8)], mok && nok, nl & 15);
+      if (want_ssq && mok && nok) {
+        const float hn = ((const float*)a.y)[(long)m * a.ldy + n];
+        sq = hn * hn;
+      }
+    }
+    if (want_ssq) {  // wave-uniform: all 64 lanes share the row
+      sq += __shfl_xor(sq, 16, 64);
+      sq += __shfl_xor(sq, 32, 64);
+      ssq_add(a, m, sq, lane == 0, mok);
+    }
+  }
+}
+
+// Split-K reduction: one wave per (row, 64 logical columns); the partials are
+// summed in split order, then the same epilogue as the unsplit kernel.
+__global__ __launch_bounds__(256) void k_splitk_reduce(LinArgs a, const float* __restrict__ part, int nsplit) {
+  const int M = a.M, N = a.W.N;
+  const int lane = threadIdx.x & 63;
+  const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const long ngroups = (N + 63) / 64;
+  if (blockIdx.x == 0 && a.ssq_zero)
+    for (int m = threadIdx.x; m < M; m += 256) a.ssq_zero[m] = 0ull;
+  if (wid >= (long)M * ngroups) return;
+  const int m = (int)(wid / ngroups);
+  const int nl = (int)(wid - (long)m * ngroups) * 64 + lane;
+  const bool nok = nl < N;
+  const int l16 = lane & 15;
+  const int n = nok ? phys_row(a, nl >> 4, l16) : 0;
+  float v = 0.f;
+  if (nok)
+    for (int s = 0; s < nsplit; ++s) v += part[((long)s * M + m) * N + n];
+  const float partner = __shfl_xor(v, 8, 64);
+  epilogue(a, m, n, v, partner, nok, l16);
+  if (a.epi == EPI_RESID && a.ssq_acc) {
+    float sq = 0.f;
+    if (nok) {
+      const float hn = ((const float*)a.y)[(long)m * a.ldy + n];
+      sq = hn * hn;
+    }
+    sq += __shfl_xor(sq, 16, 64);
+    sq += __shfl_xor(sq, 32, 64);
+    ssq_add(a, m, sq, lane == 0, true);
+  }
+}
+
+static int run_gemm(const LinArgs& a, const LinearWs& ws, hipStream_t st, LinearInfo* info) {
+  const int M = a.M;
+  const int mtiles = (M + GB_M - 1) / GB_M;
+  const int ntiles = (a.W.N + GB_N - 1) / GB_N;
+  const int nsteps = a.W.K / GB_K;
   const long base = (long)mtiles * ntiles;
   int nsplit = 1;
-  while (base * nsplit < 1024 && nchunks / (nsplit * 2) >= 2) nsplit *= 2;
-  const int cps = (nchunks + nsplit - 1) / nsplit;
-  nsplit = (nchunks + cps - 1) / cps;
-  if (nsplit > 1) {
-    if ((size_t)base * nsplit * MT * NT > ws.partial_floats || base > ws.n_counters) nsplit = 1;
+  while (base * nsplit < 256 && nsteps / (nsplit * 2) >= 4 &&
+         (size_t)(nsplit * 2) * M * a.W.N <= ws.partial_floats)
+    nsplit *= 2;
+  const int kps = (nsteps + nsplit - 1) / nsplit;
+  nsplit = (nsteps + kps - 1) / kps;
+  if (info) {
+    snprintf(info->name, sizeof info->name, "er::k_gemm_bf16");
+    info->nsplit = nsplit;
   }
-  const int cps2 = nsplit == 1 ? nchunks : cps;
-  const long nwg = base * nsplit;
+  hipLaunchKernelGGL(k_gemm_bf16, dim3((unsigned)(base * nsplit)), dim3(256), 0, st, a, ws.partial, nsplit, kps,
+                     mtiles);
+  if (hipGetLastError() != hipSuccess) return -3;
+  if (nsplit > 1) {
+    const long waves = (long)M * ((a.W.N + 63) / 64);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, ws.partial, nsplit);
+    if (hipGetLastError() != hipSuccess) return -3;
+  }
+  return 0;
+}
+
+// ----------------------------------------------------------------------------
+template <int FMT, int MT, int NR, int KS>
+static int run_mfma(const LinArgs& a, hipStream_t st, LinearInfo* info) {
+  constexpr int R = 16 * NR * (8 / KS);
+  const int mtiles = (a.M + MT - 1) / MT;
+  const long ntiles = (a.W.N + R - 1) / R;
+  const long nwg = ntiles * mtiles;
   if (nwg > 0x7FFFFFFF) return -1;
-  hipLaunchKernelGGL((k_linear_mfma<FMT, MT, NR>), dim3((unsigned)nwg), dim3(256), 0, st, (const uint16_t*)x, ldx,
-                     M, W.w, W.scale, W.zero, W.N, W.K, y, ldy, epi, (int)act_bf16, mtiles, nsplit, cps2, ws.partial,
-                     ws.counters);
+  if (info) {
+    snprintf(info->name, sizeof info->name, "er::k_linear_mfma<%d, %d, %d, %d>", FMT, MT, NR, KS);
+    info->nsplit = KS;
+  }
+  hipLaunchKernelGGL((k_linear_mfma<FMT, MT, NR, KS>), dim3((unsigned)nwg), dim3(512), 0, st, a, mtiles);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
+// Explicit variant (tuning / tests): code = 1000 + 100*NR + 10*KS + MT/16.
 template <int FMT>
-static int dispatch_mfma(const void* x, int ldx, int M, const LinearW& W, void* y, int ldy, int epi, bool act_bf16,
-                         const LinearWs& ws, hipStream_t st) {
-  const bool wide = (W.N + 127) / 128 >= 512;
-  if (M <= 16) return wide ? run_mfma<FMT, 16, 2>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st)
-                           : run_mfma<FMT, 16, 1>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st);
-  if (M <= 32) return wide ? run_mfma<FMT, 32, 2>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st)
-                           : run_mfma<FMT, 32, 1>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st);
-  return wide ? run_mfma<FMT, 64, 2>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st)
-              : run_mfma<FMT, 64, 1>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st);
+static int run_variant(int code, const LinArgs& a, hipStream_t st, LinearInfo* info) {
+  const int nr = (code / 100) % 10, ks = (code / 10) % 10, mt = 16 * (code % 10);
+  if (a.M > mt) return -1;
+#define ER_V(NR_, KS_, MT_) \
+  if (nr == NR_ && ks == KS_ && mt == MT_) return run_mfma<FMT, MT_, NR_, KS_>(a, st, info);
+#define ER_VK(NR_, MT_) ER_V(NR_, 1, MT_) ER_V(NR_, 2, MT_) ER_V(NR_, 4, MT_) ER_V(NR_, 8, MT_)
+  ER_VK(1, 16) ER_VK(2, 16) ER_VK(4, 16) ER_VK(1, 32) ER_VK(2, 32)
+#undef ER_VK
+#undef ER_V
+  return -1;
+}
+
+// Automatic choice, from a sweep of the 7B-shaped projections on MI355X:
+// splitting K over all 8 waves wins at M <= 16 for every width; two 16-row
+// subtiles per wave pay off for wide outputs (and for the quantized formats,
+// whose x fragments are relatively expensive); M in 17..32 uses 32-row
+// m-tiles; larger M goes to the tiled GEMM (bf16) .
+template <int FMT>
+static int dispatch_mfma(const LinArgs& a, hipStream_t st, LinearInfo* info) {
+  const bool wide = a.W.N >= 16384;
+  if (a.M <= 16) {
+    if (wide || (FMT != FMT_BF16 && a.W.N >= 4096)) return run_mfma<FMT, 16, 2, 8>(a, st, info);
+    return run_mfma<FMT, 16, 1, 8>(a, st, info);
+  }
+  if (wide) return run_mfma<FMT, 32, 2, 4>(a, st, info);
+  return run_mfma<FMT, 32, 1, 8>(a, st, info);
+}
+
+int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info) {
+  if (a.M <= 0 || a.W.N <= 0) return 0;
+  if (a.W.K % 128 != 0 || (!a.xnorm && a.ldx % 8 != 0) || (a.xnorm && a.ldx % 4 != 0)) return -1;
+  if ((a.epi == EPI_SWIGLU && a.W.N != 2 * a.F) ||
+      (a.epi == EPI_QKV && (a.W.N != (a.hq + 2 * a.hkv) * a.hd || a.hd % 16 != 0)))
+    return -1;
+  if (a.epi == EPI_SWIGLU && a.F % 8 != 0) return -1;
+  const bool gemm_ok = a.W.fmt == FMT_BF16 && a.W.K % GB_K == 0 && ws.partial != nullptr;
+  if (path == 3 || (path == 0 && a.M > 32 && gemm_ok)) {
+    if (!gemm_ok) return -1;
+    return run_gemm(a, ws, st, info);
+  }
+  if (path >= 1000) {
+    switch (a.W.fmt) {
+      case FMT_BF16: return run_variant<FMT_BF16>(path, a, st, info);
+      case FMT_W8: return run_variant<FMT_W8>(path, a, st, info);
+      case FMT_W4: return run_variant<FMT_W4>(path, a, st, info);
+    }
+    return -1;
+  }
+  // skinny path; larger M is processed in 32-row m-tiles
+  switch (a.W.fmt) {
+    case FMT_BF16: return dispatch_mfma<FMT_BF16>(a, st, info);
+    case FMT_W8: return dispatch_mfma<FMT_W8>(a, st, info);
+    case FMT_W4: return dispatch_mfma<FMT_W4>(a, st, info);
+  }
+  return -1;
 }
 
 template <int FMT, bool XBF>
-static int run_valu(const void* x, int ldx, int M, const LinearW& W, void* y, int ldy, int epi, hipStream_t st) {
+static int run_valu(const void* x, int ldx, int M, const LinearW& W, void* y, int ldy, int epi, hipStream_t st,
+                    LinearInfo* info) {
   dim3 grid((W.N + 3) / 4, (M + 3) / 4);
+  if (info) {
+    snprintf(info->name, sizeof info->name, "er::k_linear_valu<%d, %s>", FMT, XBF ? "true" : "false");
+    info->nsplit = 1;
+  }
   hipLaunchKernelGGL((k_linear_valu<FMT, XBF>), grid, dim3(256), 0, st, x, ldx, M, W.w, W.scale, W.zero, W.N, W.K,
                      y, ldy, epi);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
 int launch_linear(const void* x, bool act_bf16, int ldx, int M, const LinearW& W, void* y, int ldy, int epi,
-                  const LinearWs& ws, int path, hipStream_t st) {
+                  const LinearWs& ws, int path, hipStream_t st, LinearInfo* info) {
   if (M <= 0 || W.N <= 0) return 0;
   if (W.K % 4 != 0) return -1;
   if (W.fmt == FMT_W4 && W.K % 128 != 0) return -1;
+  if (epi != EPI_F32 && epi != EPI_ACT && epi != EPI_RESID) return -1;
   const bool mfma_ok = act_bf16 && W.fmt != FMT_F32 && W.K % 128 == 0 && ldx % 8 == 0;
-  const bool use_mfma = mfma_ok && path != 1;
-  if (path == 2 && !mfma_ok) return -1;
-  if (use_mfma) {
-    switch (W.fmt) {
-      case FMT_BF16: return dispatch_mfma<FMT_BF16>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st);
-      case FMT_W8: return dispatch_mfma<FMT_W8>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st);
-      case FMT_W4: return dispatch_mfma<FMT_W4>(x, ldx, M, W, y, ldy, epi, act_bf16, ws, st);
-    }
-    return -1;
+  if ((path >= 2) && !mfma_ok) return -1;
+  if (mfma_ok && path != 1) {
+    LinArgs a{};
+    a.x = x;
+    a.ldx = ldx;
+    a.M = M;
+    a.W = W;
+    a.epi = epi;
+    a.y = y;
+    a.ldy = ldy;
+    a.act_bf16 = act_bf16;
+    return launch_linear_fused(a, ws, path, st, info);
   }
   if (act_bf16) {
     switch (W.fmt) {
-      case FMT_F32: return run_valu<FMT_F32, true>(x, ldx, M, W, y, ldy, epi, st);
-      case FMT_BF16: return run_valu<FMT_BF16, true>(x, ldx, M, W, y, ldy, epi, st);
-      case FMT_W8: return run_valu<FMT_W8, true>(x, ldx, M, W, y, ldy, epi, st);
-      case FMT_W4: return run_valu<FMT_W4, true>(x, ldx, M, W, y, ldy, epi, st);
+      case FMT_F32: return run_valu<FMT_F32, true>(x, ldx, M, W, y, ldy, epi, st, info);
+      case FMT_BF16: return run_valu<FMT_BF16, true>(x, ldx, M, W, y, ldy, epi, st, info);
+      case FMT_W8: return run_valu<FMT_W8, true>(x, ldx, M, W, y, ldy, epi, st, info);
+      case FMT_W4: return run_valu<FMT_W4, true>(x, ldx, M, W, y, ldy, epi, st, info);
     }
   } else {
     switch (W.fmt) {
-      case FMT_F32: return run_valu<FMT_F32, false>(x, ldx, M, W, y, ldy, epi, st);
-      case FMT_BF16: return run_valu<FMT_BF16, false>(x, ldx, M, W, y, ldy, epi, st);
-      case FMT_W8: return run_valu<FMT_W8, false>(x, ldx, M, W, y, ldy, epi, st);
-      case FMT_W4: return run_valu<FMT_W4, false>(x, ldx, M, W, y, ldy, epi, st);
+      case FMT_F32: return run_valu<FMT_F32, false>(x, ldx, M, W, y, ldy, epi, st, info);
+      case FMT_BF16: return run_valu<FMT_BF16, false>(x, ldx, M, W, y, ldy, epi, st, info);
+      case FMT_W8: return run_valu<FMT_W8, false>(x, ldx, M, W, y, ldy, epi, st, info);
+      case FMT_W4: return run_valu<FMT_W4, false>(x, ldx, M, W, y, ldy, epi, st, info);
     }
   }
   return -1;

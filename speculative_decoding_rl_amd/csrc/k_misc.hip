@@ -21,22 +21,39 @@
 namespace er {
 
 __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ tok, int stride, const void* __restrict__ E,
-                                               int bf16, int d, float* __restrict__ h) {
+                                               int bf16, int d, float* __restrict__ h, unsigned long long* __restrict__ ssq,
+                                               unsigned long long* __restrict__ ssq_zero) {
   const int m = blockIdx.x;
   const long t = tok[(long)m * stride];
+  float s = 0.f;
   if (bf16) {
     const uint16_t* e = (const uint16_t*)E + t * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) h[(long)m * d + i] = bf2f(e[i]);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      const float v = bf2f(e[i]);
+      h[(long)m * d + i] = v;
+      s = fmaf(v, v, s);
+    }
   } else {
     const float* e = (const float*)E + t * d;
-    for (int i = threadIdx.x; i < d; i += blockDim.x) h[(long)m * d + i] = e[i];
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      const float v = e[i];
+      h[(long)m * d + i] = v;
+      s = fmaf(v, v, s);
+    }
   }
+  if (ssq_zero && threadIdx.x == 0) ssq_zero[m] = 0ull;
+  if (!ssq) return;
+  s = wave_sum(s);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) ssq[m] = (unsigned long long)rint((double)(red[0] + red[1] + red[2] + red[3]) * SSQ_SCALE);
 }
 
 int launch_embed(const int32_t* tokens, int tok_stride, int M, const void* embed, bool bf16, int d, float* h,
-                 hipStream_t st) {
+                 unsigned long long* ssq, unsigned long long* ssq_zero, hipStream_t st) {
   if (M <= 0) return 0;
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, tokens, tok_stride, embed, (int)bf16, d, h);
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, tokens, tok_stride, embed, (int)bf16, d, h, ssq, ssq_zero);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -72,12 +89,12 @@ int launch_rmsnorm(const float* h, int M, int d, const void* g, bool bf16, float
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// KV pool element (block, layer, kv, head, t, e) lives at
-// ((((block * L + layer) * 2 + kv) * hkv + head) * 16 + t) * hd + e.
-ER_DEV long kv_index(long slot, int layer, int L, int kv, int hkv, int head, int hd) {
+// KV pool: block b (16 positions), layer l, head h holds K as [16][hd] at
+// ((((b * L + l) * 2 + 0) * hkv + h) * 16) * hd and V transposed as [hd][16]
+// at ((((b * L + l) * 2 + 1) * hkv + h) * 16) * hd.
+ER_DEV long kv_base(long slot, int layer, int L, int kv, int hkv, int head, int hd) {
   const long block = slot >> 4;
-  const long t = slot & 15;
-  return ((((block * L + layer) * 2 + kv) * hkv + head) * 16 + t) * hd;
+  return ((((block * L + layer) * 2 + kv) * hkv + head) * 16) * (long)hd;
 }
 
 __global__ __launch_bounds__(256) void k_rope_kv(const float* __restrict__ qkv, int hq, int hkv, int hd,
@@ -108,7 +125,7 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float* __restrict__ qkv, 
         ((float*)qout)[o + i + half] = r2;
       }
     } else {
-      const long o = kv_index(sl, layer, L, 0, hkv, head - hq, hd);
+      const long o = kv_base(sl, layer, L, 0, hkv, head - hq, hd) + (sl & 15) * hd;
       if (bf16) {
         ((uint16_t*)pool)[o + i] = (uint16_t)f2bf(r1);
         ((uint16_t*)pool)[o + i + half] = (uint16_t)f2bf(r2);
@@ -121,7 +138,7 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float* __restrict__ qkv, 
   for (int idx = threadIdx.x; idx < hkv * hd; idx += blockDim.x) {
     const int g = idx / hd, e = idx - g * hd;
     const float v = row[(hq + hkv) * hd + idx];
-    const long o = kv_index(sl, layer, L, 1, hkv, g, hd) + e;
+    const long o = kv_base(sl, layer, L, 1, hkv, g, hd) + (long)e * 16 + (sl & 15);
     if (bf16) ((uint16_t*)pool)[o] = (uint16_t)f2bf(v);
     else ((float*)pool)[o] = v;
   }

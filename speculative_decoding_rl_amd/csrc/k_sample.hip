@@ -1,5 +1,5 @@
 // Fused sampler of the speculative step: softmax / temperature / top-p
-// statistics per logits row, categorical draws by inverse CDF in vocabulary
+// statistics of logits rows, categorical draws by inverse CDF in vocabulary
 // order, and the speculative decision (accept with probability
 // min(1, p/q), resample the first rejection from normalize(max(0, p - q)),
 // bonus draw from p_{gamma+1} after a full acceptance).
@@ -10,365 +10,464 @@
 // rejected draft follows the TLT reading notes, section 1.  The accept /
 // residual / bonus rule is standard speculative sampling.
 //
-// All probability arithmetic is fp64 (exp of (z - zmax)/T formed from the
-// fp32 logits in fp64), prefix sums are wavefront scans in a fixed order, and
-// every draw takes its uniform from Philox4x32-10 keyed by (seed) with counter
-// (sequence, position, draft index, purpose), so a step is a deterministic
-// function of its logits.
+// Layout of the work: the vocabulary is cut into chunks of 2048 tokens, each
+// owned by one wavefront that walks it in 32 tiles of 64.  Per (row, chunk) a
+// single pass keeps the chunk max m_c, its first argmax and
+// s_c = sum exp((z - m_c)/T) over the chunk (fp64, tiles summed in order).  A
+// row's softmax mass is S = sum_c s_c exp((m_c - M)/T).  A draw with uniform u
+// picks the first chunk whose running mass reaches u*S, then rescans that
+// chunk with the same additions in the same order (so the crossing is always
+// inside it) and finds the lane by an inclusive shuffle scan.  Everything is
+// deterministic; uniforms come from Philox4x32-10 keyed by the seed with
+// counter (sequence, position, draft index, purpose).
+//
+// Top-p (< 1): the nucleus threshold is found per row by a radix select over
+// the order-preserving key of the logit (ties in index order), then the chunk
+// masses are recomputed over the kept tokens only.
 
 #include "common.h"
 #include "kernels.h"
 
 namespace er {
 
-constexpr int SB = 256;  // threads per sampler block (4 waves)
+constexpr int SCH = 2048;   // tokens per chunk
+constexpr int SB = 256;
 
-// Un-normalised weight of token i in row r: exp((z - zmax)/T) if kept by
-// top-p, else 0; greedy (T == 0) rows are one-hot at the argmax.
-ER_DEV double tok_weight(const float* __restrict__ z, int i, const RowStats& s, float T) {
-  if (T == 0.0f) return i == s.argmax ? 1.0 : 0.0;
-  const float zi = z[i];
-  const uint32_t k = float_key(zi);
-  if (k < s.thr_key || (k == s.thr_key && i > s.thr_idx)) return 0.0;
-  return exp(((double)zi - (double)s.zmax) / (double)T);
+ER_DEV bool kept(const RowStats& t, float z, int i) {
+  const uint32_t k = float_key(z);
+  return !(k < t.thr_key || (k == t.thr_key && i > t.thr_idx));
 }
 
-// Block-wide fixed-order sum of one double per thread.
-ER_DEV double block_sum_d(double v, double* red) {
-  v = wave_sum_d(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
+ER_DEV const RowStats& row_thr(const void* stats, long r, int nch) {
+  return *(const RowStats*)((const char*)stats + r * stats_row_bytes(nch));
+}
+ER_DEV RowStats& row_thr_w(void* stats, long r, int nch) {
+  return *(RowStats*)((char*)stats + r * stats_row_bytes(nch));
+}
+ER_DEV const ChunkStat* row_chunks(const void* stats, long r, int nch) {
+  return (const ChunkStat*)((const char*)stats + r * stats_row_bytes(nch) + sizeof(RowStats));
+}
+ER_DEV ChunkStat* row_chunks_w(void* stats, long r, int nch) {
+  return (ChunkStat*)((char*)stats + r * stats_row_bytes(nch) + sizeof(RowStats));
 }
 
-__global__ __launch_bounds__(SB) void k_row_stats(const float* __restrict__ logits, int V, long ld, float T,
-                                                  float top_p, RowStats* __restrict__ stats) {
+// Row combination: global max (first chunk attaining it gives the lowest-index argmax).
+struct RowView {
+  float M;
+  int arg;
+  double S;
+};
+ER_DEV RowView row_view(const ChunkStat* ch, int nch, float T) {
+  RowView v{-INFINITY, 0, 0.0};
+  for (int c = 0; c < nch; ++c)
+    if (ch[c].m > v.M) { v.M = ch[c].m; v.arg = ch[c].arg; }
+  if (T == 0.0f) { v.S = 1.0; return v; }
+  for (int c = 0; c < nch; ++c)
+    if (ch[c].s > 0.0) v.S += ch[c].s * exp(((double)ch[c].m - (double)v.M) / (double)T);
+  return v;
+}
+
+// Weight of token i relative to reference m: exp((z - m)/T) if kept, else 0.
+ER_DEV double w_rel(float z, int i, double m, float T, const RowStats& t, bool topp) {
+  if (topp && !kept(t, z, i)) return 0.0;
+  return exp(((double)z - m) / (double)T);
+}
+
+// ---------------------------------------------------------------------------
+// Per-chunk statistics: one wave per (row, chunk).
+// ---------------------------------------------------------------------------
+template <bool KEPT>
+__global__ __launch_bounds__(SB) void k_chunk_stats(const float* __restrict__ logits, int V, long ld, float T,
+                                                    void* __restrict__ stats, int nch) {
+  const int r = blockIdx.x;
+  const int c = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (c >= nch) return;
+  const float* z = logits + (long)r * ld;
+  const int base = c * SCH;
+  float m = -INFINITY;
+  int arg = 0x7FFFFFFF;
+  for (int t = 0; t < SCH / 64; ++t) {
+    const int i = base + t * 64 + lane;
+    if (i < V) {
+      const float v = z[i];
+      if (v > m) { m = v; arg = i; }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float om = __shfl_xor(m, o, 64);
+    const int oa = __shfl_xor(arg, o, 64);
+    if (om > m || (om == m && oa < arg)) { m = om; arg = oa; }
+  }
+  double s = 0.0;
+  if (T != 0.0f) {
+    RowStats thr{0u, 0x7FFFFFFF};
+    if (KEPT) thr = row_thr(stats, r, nch);
+    for (int t = 0; t < SCH / 64; ++t) {
+      const int i = base + t * 64 + lane;
+      const double w = (i < V) ? w_rel(z[i], i, (double)m, T, thr, KEPT) : 0.0;
+      s += wave_sum_d(w);
+    }
+  }
+  if (lane == 0) {
+    ChunkStat& o = row_chunks_w(stats, r, nch)[c];
+    o.m = m;
+    o.arg = arg;
+    o.s = s;
+  }
+}
+
+// Nucleus threshold (top_p < 1), one work-group per row: the kept set is the
+// shortest probability-descending prefix (equal probabilities by index)
+// whose mass reaches top_p * S.
+__global__ __launch_bounds__(SB) void k_topp(const float* __restrict__ logits, int V, long ld, float T, float top_p,
+                                             void* __restrict__ stats, int nch) {
   const int r = blockIdx.x;
   const float* z = logits + (long)r * ld;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  __shared__ double red[4];
-  __shared__ float redm[4];
-  __shared__ int redi[4];
+  const int tid = threadIdx.x;
   __shared__ double hist[256];
   __shared__ uint32_t s_prefix;
   __shared__ double s_above;
   __shared__ int s_cnt[SB];
-
-  // argmax (lowest index among equal maxima)
-  float bm = -INFINITY;
-  int bi = 0x7FFFFFFF;
-  for (int i = tid; i < V; i += SB) {
-    const float v = z[i];
-    if (v > bm) { bm = v; bi = i; }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float om = __shfl_xor(bm, o, 64);
-    const int oi = __shfl_xor(bi, o, 64);
-    if (om > bm || (om == bm && oi < bi)) { bm = om; bi = oi; }
-  }
-  if (lane == 0) { redm[wave] = bm; redi[wave] = bi; }
-  __syncthreads();
-  float zmax = redm[0];
-  int amax = redi[0];
-  for (int w = 1; w < 4; ++w)
-    if (redm[w] > zmax || (redm[w] == zmax && redi[w] < amax)) { zmax = redm[w]; amax = redi[w]; }
-
-  RowStats s;
-  s.zmax = zmax;
-  s.argmax = amax;
-  if (T == 0.0f) {
-    s.total = 1.0;
-    s.kept = 1.0;
-    s.thr_key = 0;
-    s.thr_idx = 0x7FFFFFFF;
-    if (tid == 0) stats[r] = s;
-    return;
-  }
-  double tot = 0.0;
-  for (int i = tid; i < V; i += SB) tot += exp(((double)z[i] - (double)zmax) / (double)T);
-  tot = block_sum_d(tot, red);
-  s.total = tot;
-  s.kept = tot;
-  s.thr_key = 0;
-  s.thr_idx = 0x7FFFFFFF;
-  if (top_p < 1.0f) {
-    // Nucleus threshold: the kept set is the longest-probability prefix (ties
-    // by index) whose mass first reaches top_p * total.  Radix select over
-    // the order-preserving key of the logit, 8 bits per pass, masses in fp64.
-    const double target = (double)top_p * tot;
-    uint32_t prefix = 0, mask = 0;
-    double above = 0.0;
-    for (int d = 3; d >= 0; --d) {
-      for (int b = tid; b < 256; b += SB) hist[b] = 0.0;
-      __syncthreads();
-      for (int i = tid; i < V; i += SB) {
-        const uint32_t k = float_key(z[i]);
-        if ((k & mask) == prefix) {
-          const double w = exp(((double)z[i] - (double)zmax) / (double)T);
-          atomicAdd(&hist[(k >> (8 * d)) & 255u], w);
-        }
-      }
-      __syncthreads();
-      if (tid == 0) {
-        // highest bin whose cumulative mass reaches the target; if rounding
-        // leaves none, the lowest non-empty bin (so the bin always holds tokens)
-        double cum = above, cum_last = above;
-        int chosen = -1, last_nz = -1;
-        for (int b = 255; b >= 0; --b) {
-          if (hist[b] > 0.0) {
-            if (cum + hist[b] >= target) { chosen = b; break; }
-            last_nz = b;
-            cum_last = cum;
-          }
-          cum += hist[b];
-        }
-        if (chosen < 0) { chosen = last_nz; cum = cum_last; }
-        s_prefix = prefix | ((uint32_t)chosen << (8 * d));
-        s_above = cum;
-      }
-      __syncthreads();
-      prefix = s_prefix;
-      above = s_above;
-      mask |= 255u << (8 * d);
-    }
-    // Tokens with key == prefix all carry the same weight; keep the first c in
-    // index order, c the smallest count that reaches the target.
-    int tie_i = -1;
-    for (int i = tid; i < V && tie_i < 0; i += SB)
-      if (float_key(z[i]) == prefix) tie_i = i;
-    // weight of a tied token
-    __shared__ int s_anyi;
-    if (tid == 0) s_anyi = 0x7FFFFFFF;
+  __shared__ int s_any;
+  const RowView rv = row_view(row_chunks(stats, r, nch), nch, T);
+  const double M = rv.M;
+  const double target = (double)top_p * rv.S;
+  uint32_t prefix = 0, mask = 0;
+  double above = 0.0;
+  for (int d = 3; d >= 0; --d) {
+    for (int b = tid; b < 256; b += SB) hist[b] = 0.0;
     __syncthreads();
-    if (tie_i >= 0) atomicMin(&s_anyi, tie_i);
-    __syncthreads();
-    if (s_anyi == 0x7FFFFFFF) {  // cannot happen (the chosen bin always holds mass); keep everything
-      if (tid == 0) { s.thr_key = 0; s.thr_idx = 0x7FFFFFFF; s.kept = tot; stats[r] = s; }
-      return;
+    for (int i = tid; i < V; i += SB) {
+      const uint32_t k = float_key(z[i]);
+      if ((k & mask) == prefix) atomicAdd(&hist[(k >> (8 * d)) & 255u], exp(((double)z[i] - M) / (double)T));
     }
-    const double wt = exp(((double)z[s_anyi] - (double)zmax) / (double)T);
-    double need = (target - above) / wt;
-    int c = (int)ceil(need);
-    if (c < 1) c = 1;
-    // c-th smallest tied index: contiguous chunks keep index order
-    const int chunk = (V + SB - 1) / SB;
-    const int lo = tid * chunk, hi = min(V, lo + chunk);
-    int cnt = 0;
-    for (int i = lo; i < hi; ++i) cnt += (float_key(z[i]) == prefix);
-    s_cnt[tid] = cnt;
     __syncthreads();
     if (tid == 0) {
-      int run = 0;
-      for (int t = 0; t < SB; ++t) { const int v = s_cnt[t]; s_cnt[t] = run; run += v; }
-      if (c > run) c = run;
-      s_anyi = c;  // reuse as the target count
-    }
-    __syncthreads();
-    c = s_anyi;
-    int idx = -1;
-    {
-      int run = s_cnt[tid];
-      if (run < c) {
-        for (int i = lo; i < hi; ++i) {
-          if (float_key(z[i]) == prefix) {
-            ++run;
-            if (run == c) { idx = i; break; }
-          }
+      // highest bin whose cumulative mass reaches the target; if rounding
+      // leaves none, the lowest non-empty bin (so the bin always holds tokens)
+      double cum = above, cum_last = above;
+      int chosen = -1, last_nz = -1;
+      for (int b = 255; b >= 0; --b) {
+        if (hist[b] > 0.0) {
+          if (cum + hist[b] >= target) { chosen = b; break; }
+          last_nz = b;
+          cum_last = cum;
         }
+        cum += hist[b];
       }
+      if (chosen < 0) { chosen = last_nz < 0 ? 0 : last_nz; cum = cum_last; }
+      s_prefix = prefix | ((uint32_t)chosen << (8 * d));
+      s_above = cum;
     }
     __syncthreads();
-    if (idx >= 0) s_anyi = idx;
-    __syncthreads();
-    s.thr_key = prefix;
-    s.thr_idx = s_anyi;
-    s.kept = above + (double)c * wt;
+    prefix = s_prefix;
+    above = s_above;
+    mask |= 255u << (8 * d);
   }
-  if (tid == 0) stats[r] = s;
+  // tokens with key == prefix share one weight; keep the first c in index order
+  if (tid == 0) s_any = 0x7FFFFFFF;
+  __syncthreads();
+  for (int i = tid; i < V; i += SB)
+    if (float_key(z[i]) == prefix) { atomicMin(&s_any, i); break; }
+  __syncthreads();
+  if (s_any == 0x7FFFFFFF) {  // cannot happen (the chosen bin holds mass); keep everything
+    if (tid == 0) row_thr_w(stats, r, nch) = RowStats{0u, 0x7FFFFFFF};
+    return;
+  }
+  const double wt = exp(((double)z[s_any] - M) / (double)T);
+  int c = (int)ceil((target - above) / wt);
+  if (c < 1) c = 1;
+  const int chunk = (V + SB - 1) / SB;
+  const int lo = tid * chunk, hi = min(V, lo + chunk);
+  int cnt = 0;
+  for (int i = lo; i < hi; ++i) cnt += (float_key(z[i]) == prefix);
+  s_cnt[tid] = cnt;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int t = 0; t < SB; ++t) { const int v = s_cnt[t]; s_cnt[t] = run; run += v; }
+    if (c > run) c = run;
+    s_any = c;
+  }
+  __syncthreads();
+  c = s_any;
+  int idx = -1;
+  {
+    int run = s_cnt[tid];
+    if (run < c)
+      for (int i = lo; i < hi; ++i)
+        if (float_key(z[i]) == prefix && ++run == c) { idx = i; break; }
+  }
+  __syncthreads();
+  if (idx >= 0) s_any = idx;
+  __syncthreads();
+  if (tid == 0) row_thr_w(stats, r, nch) = RowStats{prefix, s_any};
 }
 
-int launch_row_stats(const float* logits, int rows, int V, long ld, float T, float top_p, RowStats* stats,
+__global__ void k_stats_init(void* __restrict__ stats, int rows, int nch) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < rows) row_thr_w(stats, r, nch) = RowStats{0u, 0x7FFFFFFF};
+}
+
+int launch_row_stats(const float* logits, int rows, int V, long ld, float T, float top_p, void* stats,
                      hipStream_t st) {
   if (rows <= 0) return 0;
-  hipLaunchKernelGGL(k_row_stats, dim3(rows), dim3(SB), 0, st, logits, V, ld, T, top_p, stats);
+  const int nch = sampler_chunks(V);
+  hipLaunchKernelGGL(k_stats_init, dim3((rows + 255) / 256), dim3(256), 0, st, stats, rows, nch);
+  hipLaunchKernelGGL(k_chunk_stats<false>, dim3(rows, (nch + 3) / 4), dim3(SB), 0, st, logits, V, ld, T, stats, nch);
+  if (T != 0.0f && top_p < 1.0f) {
+    hipLaunchKernelGGL(k_topp, dim3(rows), dim3(SB), 0, st, logits, V, ld, T, top_p, stats, nch);
+    hipLaunchKernelGGL(k_chunk_stats<true>, dim3(rows, (nch + 3) / 4), dim3(SB), 0, st, logits, V, ld, T, stats, nch);
+  }
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// Inverse-CDF draw over a weight function in vocabulary order: the smallest i
-// with sum_{k<=i} w_k >= u * sum_k w_k.  Wave w scans the contiguous range
-// [w*span, (w+1)*span) in 64-wide tiles; the first pass forms the wave totals,
-// the wave holding the crossing rescans with the same additions in the same
-// order and finds the lane by an inclusive shuffle scan.
-template <class WF>
-ER_DEV int draw_inverse_cdf(const WF& wf, int V, double u, double* red, int* s_out) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int span = ((V + 4 * 64 - 1) / (4 * 64)) * 64;
-  const int lo = wave * span, hi = min(V, lo + span);
-  double run = 0.0;
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const double w = (i < hi) ? wf(i) : 0.0;
-    run += wave_sum_d(w);
-  }
-  __syncthreads();
-  if (lane == 0) red[wave] = run;
-  if (tid == 0) *s_out = -1;
-  __syncthreads();
-  const double tot = red[0] + red[1] + red[2] + red[3];
-  const double target = u * tot;
-  // wave holding the crossing; if rounding leaves none, the last wave with mass
+// ---------------------------------------------------------------------------
+// Inverse-CDF draw by one wavefront: first chunk whose running mass reaches
+// target, then the same tile sums in the same order inside that chunk.
+// WF(i, mref) gives token i's weight relative to mref; chunk c's sum was
+// formed relative to ref(c) and enters the row total scaled by f(c).
+// ---------------------------------------------------------------------------
+template <class WF, class CS>
+ER_DEV int wave_draw(const WF& wf, const CS& cs, int nch, int V, double u, double total) {
+  const int lane = threadIdx.x & 63;
+  const double target = u * total;
   double pre = 0.0, pre_last = 0.0;
-  int cw = -1, last_w = 0;
-  for (int w = 0; w < 4; ++w) {
-    if (red[w] > 0.0) {
-      if (pre + red[w] >= target) { cw = w; break; }
-      last_w = w;
+  int cc = -1, last_c = -1;
+  for (int c = 0; c < nch; ++c) {
+    const double sc = cs.sum(c);
+    if (sc > 0.0) {
+      if (pre + sc * cs.f(c) >= target) { cc = c; break; }
+      last_c = c;
       pre_last = pre;
     }
-    pre += red[w];
+    pre += sc * cs.f(c);
   }
-  if (cw < 0) { cw = last_w; pre = pre_last; }
-  if (wave == cw) {
-    double r = pre;
-    int found = -1;
-    int last_nz = -1;
-    for (int base = lo; base < hi && found < 0; base += 64) {
-      const int i = base + lane;
-      const double w = (i < hi) ? wf(i) : 0.0;
-      const double ts = wave_sum_d(w);
-      if (w > 0.0) last_nz = i;
-      if (r + ts >= target) {
-        double sc = w;  // inclusive scan
+  if (cc < 0) { cc = last_c; pre = pre_last; }
+  if (cc < 0) return 0;
+  const double f = cs.f(cc);
+  const double ref = cs.ref(cc);
+  const int base = cc * SCH;
+  double r = 0.0;
+  int found = -1, last_nz = -1;
+  for (int t = 0; t < SCH / 64 && found == -1; ++t) {
+    const int i = base + t * 64 + lane;
+    const double w = (i < V) ? wf(i, ref) : 0.0;
+    const double ts = wave_sum_d(w);
+    if (w > 0.0) last_nz = i;
+    if (pre + (r + ts) * f >= target) {
+      double sc = w;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const double t = __shfl_up(sc, o, 64);
-          if (lane >= o) sc += t;
-        }
-        const bool hit = (r + sc >= target) && (w > 0.0);
-        const unsigned long long m = __ballot(hit);
-        if (m) found = base + __ffsll(m) - 1;
+      for (int o = 1; o < 64; o <<= 1) {
+        const double v = __shfl_up(sc, o, 64);
+        if (lane >= o) sc += v;
       }
-      r += ts;
+      const bool hit = (pre + (r + sc) * f >= target) && (w > 0.0);
+      const unsigned long long msk = __ballot(hit);
+      found = msk ? base + t * 64 + __ffsll(msk) - 1 : -2;  // -2: rounding left no lane; fall back below
     }
-    // reduce last non-zero over the wave (fallback when rounding leaves no hit)
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) last_nz = max(last_nz, __shfl_xor(last_nz, o, 64));
-    if (lane == 0) *s_out = found >= 0 ? found : last_nz;
+    r += ts;
   }
-  __syncthreads();
-  int res = *s_out;
-  if (res < 0) res = 0;
-  return res;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) last_nz = max(last_nz, __shfl_xor(last_nz, o, 64));
+  return found >= 0 ? found : (last_nz >= 0 ? last_nz : base);
 }
 
-struct RowWeight {
-  const float* z;
-  RowStats s;
+struct ChunkView {
+  const ChunkStat* ch;
+  float M;
   float T;
-  ER_DEV double operator()(int i) const { return tok_weight(z, i, s, T); }
+  ER_DEV double sum(int c) const { return ch[c].s; }
+  ER_DEV double f(int c) const { return exp(((double)ch[c].m - (double)M) / (double)T); }
+  ER_DEV double ref(int c) const { return (double)ch[c].m; }
 };
 
-__global__ __launch_bounds__(SB) void k_sample_rows(const float* __restrict__ logits, const RowStats* __restrict__ stats,
-                                                    int V, long ld, float T, uint64_t seed,
-                                                    const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
-                                                    int didx, int purpose, int32_t* __restrict__ out, int out_stride,
-                                                    const int32_t* __restrict__ row_map) {
+struct RowW {
+  const float* z;
+  RowStats thr;
+  float T;
+  bool topp;
+  ER_DEV double operator()(int i, double ref) const { return w_rel(z[i], i, ref, T, thr, topp); }
+};
+
+__global__ __launch_bounds__(64) void k_sample_rows(const float* __restrict__ logits, const void* __restrict__ stats,
+                                                   int V, long ld, float T, float top_p, uint64_t seed,
+                                                   const int32_t* __restrict__ seq_id, const int32_t* __restrict__ pos,
+                                                   int didx, int purpose, int32_t* __restrict__ out, int out_stride,
+                                                   const int32_t* __restrict__ row_map, int nch) {
   const int r = blockIdx.x;
   const long lr = row_map ? row_map[r] : r;
-  __shared__ double red[4];
-  __shared__ int s_out;
-  RowWeight wf{logits + lr * ld, stats[lr], T};
+  const ChunkStat* ch = row_chunks(stats, lr, nch);
+  const RowView rv = row_view(ch, nch, T);
+  int t;
   if (T == 0.0f) {
-    if (threadIdx.x == 0) out[(long)r * out_stride] = wf.s.argmax;
-    return;
+    t = rv.arg;
+  } else {
+    const double u = philox_uniform(seed, (uint32_t)seq_id[r], (uint32_t)pos[r], (uint32_t)didx, (uint32_t)purpose);
+    RowW wf{logits + lr * ld, row_thr(stats, lr, nch), T, top_p < 1.0f};
+    t = wave_draw(wf, ChunkView{ch, rv.M, T}, nch, V, u, rv.S);
   }
-  const double u = philox_uniform(seed, (uint32_t)seq_id[r], (uint32_t)pos[r], (uint32_t)didx, (uint32_t)purpose);
-  const int t = draw_inverse_cdf(wf, V, u, red, &s_out);
   if (threadIdx.x == 0) out[(long)r * out_stride] = t;
 }
 
-int launch_sample_rows(const float* logits, const RowStats* stats, int rows, int V, long ld, float T, uint64_t seed,
-                       const int32_t* seq_id, const int32_t* pos, int didx, int purpose, int32_t* out, int out_stride,
-                       const int32_t* row_map, hipStream_t st) {
+int launch_sample_rows(const float* logits, const void* stats, int rows, int V, long ld, float T, float top_p,
+                       uint64_t seed, const int32_t* seq_id, const int32_t* pos, int didx, int purpose, int32_t* out,
+                       int out_stride, const int32_t* row_map, hipStream_t st) {
   if (rows <= 0) return 0;
-  hipLaunchKernelGGL(k_sample_rows, dim3(rows), dim3(SB), 0, st, logits, stats, V, ld, T, seed, seq_id, pos, didx,
-                     purpose, out, out_stride, row_map);
+  hipLaunchKernelGGL(k_sample_rows, dim3(rows), dim3(64), 0, st, logits, stats, V, ld, T, top_p, seed, seq_id, pos,
+                     didx, purpose, out, out_stride, row_map, sampler_chunks(V));
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-struct ResidualWeight {
+// ---------------------------------------------------------------------------
+// Speculative decision.
+//  1. k_decide_accept (one wave per sequence): accept tests in order; records
+//     the accepted count and writes the accepted drafts.
+//  2. k_resid_chunks (one wave per (sequence, chunk)): mass of
+//     max(0, p_j - q_j) per chunk at the first rejected position j (skipped
+//     after a full acceptance).
+//  3. k_decide_draw (one wave per sequence): the residual or bonus draw.
+// ---------------------------------------------------------------------------
+ER_DEV double prob(const float* z, int i, const RowStats& thr, float T, bool topp, const RowView& rv) {
+  if (T == 0.0f) return i == rv.arg ? 1.0 : 0.0;
+  return w_rel(z[i], i, (double)rv.M, T, thr, topp) / rv.S;
+}
+
+__global__ __launch_bounds__(64) void k_decide_accept(const float* __restrict__ p_logits, const void* __restrict__ p_stats,
+                                                     const float* __restrict__ q_logits, const void* __restrict__ q_stats,
+                                                     const int32_t* __restrict__ tokens, int B, int gamma, int V,
+                                                     float T, int topp, uint64_t seed,
+                                                     const int32_t* __restrict__ seq_id,
+                                                     const int32_t* __restrict__ pos0, int32_t* __restrict__ out_tok,
+                                                     int32_t* __restrict__ n_acc, int nch) {
+  const int b = blockIdx.x;
+  const int G1 = gamma + 1;
+  const uint32_t sid = (uint32_t)seq_id[b];
+  const uint32_t n = (uint32_t)pos0[b];
+  const int32_t* drafts = tokens + (long)b * G1 + 1;
+  int a = gamma;
+  for (int j = 1; j <= gamma; ++j) {
+    const long pr = (long)b * G1 + (j - 1);
+    const long qr = (long)(j - 1) * B + b;
+    const RowView pv = row_view(row_chunks(p_stats, pr, nch), nch, T);
+    const RowView qv = row_view(row_chunks(q_stats, qr, nch), nch, T);
+    const int d = drafts[j - 1];
+    const double pd = prob(p_logits + pr * V, d, row_thr(p_stats, pr, nch), T, topp, pv);
+    const double qd = prob(q_logits + qr * V, d, row_thr(q_stats, qr, nch), T, topp, qv);
+    const double u = philox_uniform(seed, sid, n + j, (uint32_t)j, PURPOSE_ACCEPT);
+    if (!(u * qd <= pd)) { a = j - 1; break; }
+  }
+  if (threadIdx.x == 0) {
+    for (int i = 0; i < a; ++i) out_tok[(long)b * G1 + i] = drafts[i];
+    n_acc[b] = a;
+  }
+}
+
+struct ResidW {
   const float* zp;
   const float* zq;
-  RowStats sp, sq;
+  RowStats tp, tq;
+  RowView pv, qv;
   float T;
-  ER_DEV double operator()(int i) const {
-    const double p = tok_weight(zp, i, sp, T) / sp.kept;
-    const double q = tok_weight(zq, i, sq, T) / sq.kept;
+  bool topp;
+  ER_DEV double operator()(int i, double) const {
+    double p, q;
+    if (T == 0.0f) {
+      p = i == pv.arg ? 1.0 : 0.0;
+      q = i == qv.arg ? 1.0 : 0.0;
+    } else {
+      p = w_rel(zp[i], i, (double)pv.M, T, tp, topp) / pv.S;
+      q = w_rel(zq[i], i, (double)qv.M, T, tq, topp) / qv.S;
+    }
     return p > q ? p - q : 0.0;
   }
 };
 
-__global__ __launch_bounds__(SB) void k_spec_decide(const float* __restrict__ p_logits, const RowStats* __restrict__ p_stats,
-                                                    const float* __restrict__ q_logits, const RowStats* __restrict__ q_stats,
-                                                    const int32_t* __restrict__ tokens, int gamma, int V, float T,
-                                                    uint64_t seed, const int32_t* __restrict__ seq_id,
-                                                    const int32_t* __restrict__ pos0, int32_t* __restrict__ out_tok,
-                                                    int32_t* __restrict__ n_acc) {
+__global__ __launch_bounds__(SB) void k_resid_chunks(const float* __restrict__ p_logits, const void* __restrict__ p_stats,
+                                                     const float* __restrict__ q_logits, const void* __restrict__ q_stats,
+                                                     const int32_t* __restrict__ n_acc, int B, int gamma, int V, float T,
+                                                     int topp, double* __restrict__ resid, int nch) {
   const int b = blockIdx.x;
+  const int c = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (c >= nch) return;
+  const int a = n_acc[b];
+  if (a >= gamma) return;  // full acceptance: the bonus draw uses p_{gamma+1}'s own chunks
+  const int j = a + 1;
   const int G1 = gamma + 1;
-  __shared__ double red[4];
-  __shared__ int s_out;
-  const uint32_t sid = (uint32_t)seq_id[b];
-  const uint32_t n = (uint32_t)pos0[b];
-  const int32_t* drafts = tokens + (long)b * G1 + 1;
-  for (int j = 1; j <= gamma; ++j) {
-    const long prow = (long)b * G1 + (j - 1);
-    const long qrow = (long)(j - 1) * gridDim.x + b;  // drafter rows are [gamma][B]
-    const float* zp = p_logits + prow * V;
-    const float* zq = q_logits + qrow * V;
-    const RowStats sp = p_stats[prow], sq = q_stats[qrow];
-    const int d = drafts[j - 1];
-    const double pd = tok_weight(zp, d, sp, T) / sp.kept;
-    const double qd = tok_weight(zq, d, sq, T) / sq.kept;
-    const double u = philox_uniform(seed, sid, n + j, (uint32_t)j, PURPOSE_ACCEPT);
-    if (!(u * qd <= pd)) {
-      const double u2 = philox_uniform(seed, sid, n + j, (uint32_t)j, PURPOSE_RESIDUAL);
-      ResidualWeight rw{zp, zq, sp, sq, T};
-      // zero residual mass (p == q on every token) falls back to p
-      double part = 0.0;
-      for (int i = threadIdx.x; i < V; i += SB) part += rw(i);
-      __shared__ double red2[4];
-      const double rs = block_sum_d(part, red2);
-      int t;
-      if (rs > 0.0) t = draw_inverse_cdf(rw, V, u2, red, &s_out);
-      else t = draw_inverse_cdf(RowWeight{zp, sp, T}, V, u2, red, &s_out);
-      if (threadIdx.x == 0) {
-        for (int i = 0; i < j - 1; ++i) out_tok[(long)b * G1 + i] = drafts[i];
-        out_tok[(long)b * G1 + j - 1] = t;
-        n_acc[b] = j - 1;
-      }
-      return;
-    }
+  const long pr = (long)b * G1 + (j - 1);
+  const long qr = (long)(j - 1) * B + b;
+  ResidW rw{p_logits + pr * V, q_logits + qr * V, row_thr(p_stats, pr, nch), row_thr(q_stats, qr, nch),
+            row_view(row_chunks(p_stats, pr, nch), nch, T), row_view(row_chunks(q_stats, qr, nch), nch, T), T,
+            topp != 0};
+  double s = 0.0;
+  const int base = c * SCH;
+  for (int t = 0; t < SCH / 64; ++t) {
+    const int i = base + t * 64 + lane;
+    s += wave_sum_d(i < V ? rw(i, 0.0) : 0.0);
   }
-  const long prow = (long)b * G1 + gamma;
-  const double u = philox_uniform(seed, sid, n + gamma + 1, (uint32_t)(gamma + 1), PURPOSE_RESIDUAL);
-  const int t = draw_inverse_cdf(RowWeight{p_logits + prow * V, p_stats[prow], T}, V, u, red, &s_out);
-  if (threadIdx.x == 0) {
-    for (int i = 0; i < gamma; ++i) out_tok[(long)b * G1 + i] = drafts[i];
-    out_tok[(long)b * G1 + gamma] = t;
-    n_acc[b] = gamma;
-  }
+  if (lane == 0) resid[(long)b * nch + c] = s;
 }
 
-int launch_spec_decide(const float* p_logits, const RowStats* p_stats, const float* q_logits, const RowStats* q_stats,
-                       const int32_t* tokens, int B, int gamma, int V, float T, uint64_t seed, const int32_t* seq_id,
-                       const int32_t* pos0, int32_t* out_tok, int32_t* n_acc, hipStream_t st) {
+struct ResidChunks {
+  const double* s;
+  ER_DEV double sum(int c) const { return s[c]; }
+  ER_DEV double f(int) const { return 1.0; }
+  ER_DEV double ref(int) const { return 0.0; }
+};
+
+__global__ __launch_bounds__(64) void k_decide_draw(const float* __restrict__ p_logits, const void* __restrict__ p_stats,
+                                                   const float* __restrict__ q_logits, const void* __restrict__ q_stats,
+                                                   const int32_t* __restrict__ n_acc, int B, int gamma, int V, float T,
+                                                   int topp, uint64_t seed, const int32_t* __restrict__ seq_id,
+                                                   const int32_t* __restrict__ pos0, const double* __restrict__ resid,
+                                                   int32_t* __restrict__ out_tok, int nch) {
+  const int b = blockIdx.x;
+  const int G1 = gamma + 1;
+  const uint32_t sid = (uint32_t)seq_id[b];
+  const uint32_t n = (uint32_t)pos0[b];
+  const int a = n_acc[b];
+  const int j = a + 1;  // position index of the draw (gamma+1 = bonus)
+  const double u = philox_uniform(seed, sid, n + j, (uint32_t)j, PURPOSE_RESIDUAL);
+  const long pr = (long)b * G1 + (j - 1);
+  const ChunkStat* pc = row_chunks(p_stats, pr, nch);
+  const RowView pv = row_view(pc, nch, T);
+  const RowW pw{p_logits + pr * V, row_thr(p_stats, pr, nch), T, topp != 0};
+  int t;
+  if (a < gamma) {
+    const long qr = (long)(j - 1) * B + b;
+    const double* rs = resid + (long)b * nch;
+    double tot = 0.0;
+    for (int c = 0; c < nch; ++c) tot += rs[c];
+    if (tot > 0.0) {
+      ResidW rw{p_logits + pr * V, q_logits + qr * V, row_thr(p_stats, pr, nch), row_thr(q_stats, qr, nch), pv,
+                row_view(row_chunks(q_stats, qr, nch), nch, T), T, topp != 0};
+      t = wave_draw(rw, ResidChunks{rs}, nch, V, u, tot);
+    } else {  // residual without mass: fall back to p
+      t = T == 0.0f ? pv.arg : wave_draw(pw, ChunkView{pc, pv.M, T}, nch, V, u, pv.S);
+    }
+  } else {
+    t = T == 0.0f ? pv.arg : wave_draw(pw, ChunkView{pc, pv.M, T}, nch, V, u, pv.S);
+  }
+  if (threadIdx.x == 0) out_tok[(long)b * G1 + a] = t;
+}
+
+int launch_spec_decide(const float* p_logits, const void* p_stats, const float* q_logits, const void* q_stats,
+                       const int32_t* tokens, int B, int gamma, int V, float T, float top_p, uint64_t seed,
+                       const int32_t* seq_id, const int32_t* pos0, int32_t* out_tok, int32_t* n_acc, double* resid,
+                       hipStream_t st) {
   if (B <= 0) return 0;
-  hipLaunchKernelGGL(k_spec_decide, dim3(B), dim3(SB), 0, st, p_logits, p_stats, q_logits, q_stats, tokens, gamma, V,
-                     T, seed, seq_id, pos0, out_tok, n_acc);
+  const int nch = sampler_chunks(V);
+  const int topp = (T != 0.0f && top_p < 1.0f) ? 1 : 0;
+  hipLaunchKernelGGL(k_decide_accept, dim3(B), dim3(64), 0, st, p_logits, p_stats, q_logits, q_stats, tokens, B,
+                     gamma, V, T, topp, seed, seq_id, pos0, out_tok, n_acc, nch);
+  if (gamma > 0)
+    hipLaunchKernelGGL(k_resid_chunks, dim3(B, (nch + 3) / 4), dim3(SB), 0, st, p_logits, p_stats, q_logits, q_stats,
+                       n_acc, B, gamma, V, T, topp, resid, nch);
+  hipLaunchKernelGGL(k_decide_draw, dim3(B), dim3(64), 0, st, p_logits, p_stats, q_logits, q_stats, n_acc, B, gamma, V,
+                     T, topp, seed, seq_id, pos0, resid, out_tok, nch);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

@@ -23,9 +23,45 @@ struct LinearW {
 
 // Epilogues of the linear kernels.
 enum Epi {
-  EPI_F32 = 0,    // y (fp32) [m*ldy + n] = acc
-  EPI_ACT = 1,    // y (bf16 if act_bf16 else fp32) = acc
-  EPI_RESID = 2,  // y (fp32 residual stream) += acc
+  EPI_F32 = 0,     // y (fp32) [m*ldy + n] = acc
+  EPI_ACT = 1,     // y (bf16 if act_bf16 else fp32) = acc
+  EPI_RESID = 2,   // y (fp32 residual stream) += acc; optional per-row sum-of-squares partials
+  EPI_SWIGLU = 3,  // W = [gate; up] (2F rows): y (act) [m*ldy + f] = silu(gate_f) * up_f
+  EPI_QKV = 4,     // W = [q; k; v]: rotate-half RoPE on q, k; q -> qout, k, v -> paged KV pool
+};
+
+// Fused linear: y = epilogue(x' W^T) where x' is x (act type) or, with
+// xnorm, RMSNorm(h) * g formed on load from the fp32 residual stream h.
+// Row sums of squares of h travel between kernels as 64-bit fixed point
+// (units of 2^-24) so that the accumulation is exact and order-free:
+// residual epilogues add into ssq_acc, and the next residual producer clears
+// the buffer the previous consumer read (ssq_zero).
+constexpr double SSQ_SCALE = 16777216.0;  // 2^24
+struct LinArgs {
+  const void* x;            // act [M, ldx], or fp32 h [*, ldx] when xnorm
+  int ldx, M;
+  int xnorm;
+  const int32_t* xrow;      // xnorm: row m of x' is row xrow[m] of h (nullable = identity)
+  const unsigned long long* ssq_in;  // xnorm: [rows of h] fixed-point sums of squares
+  const void* gnorm;        // xnorm: gain [K], model dtype
+  float eps;
+  LinearW W;
+  int epi;
+  void* y;
+  int ldy;
+  int act_bf16;
+  unsigned long long* ssq_acc;   // EPI_RESID: add the updated rows' sums of squares (nullable)
+  unsigned long long* ssq_zero;  // cleared for rows [0, M) by work-group 0 (nullable)
+  // EPI_QKV
+  int hq, hkv, hd;
+  const int32_t* pos;       // [M]
+  const int64_t* slot;      // [M] KV slot (block * 16 + offset)
+  const float2* cs;         // cos/sin [max_pos][hd/2]
+  void* qout;               // [M, hq, hd] act
+  void* kv_pool;
+  int layer, n_layers;
+  // EPI_SWIGLU
+  int F;
 };
 
 struct LinearWs {
@@ -35,13 +71,25 @@ struct LinearWs {
   int n_counters;
 };
 
-// Path choice: 0 = automatic, 1 = force VALU, 2 = force MFMA (when legal).
+// What a launch_linear call ran (for per-kernel timing): kernel name as the
+// profiler demangles it, split count.
+struct LinearInfo {
+  char name[64];
+  int nsplit;
+};
+
+// Path choice: 0 = automatic, 1 = VALU, 2 = MFMA (when legal), 3 = tiled GEMM (bf16),
+// 1000 + 100*NR + 10*KS + MT/16 = that skinny MFMA variant.
 int launch_linear(const void* x, bool act_bf16, int ldx, int M, const LinearW& W, void* y, int ldy,
-                  int epi, const LinearWs& ws, int path, hipStream_t st);
+                  int epi, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info = nullptr);
+// bf16 activations only (MFMA paths).
+int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info = nullptr);
 
 // Small fused ops.
+// h[m] = embed[token]; optional ssq[m] = fixed-point sum h^2 (plain store),
+// ssq_zero[m] = 0.
 int launch_embed(const int32_t* tokens, int tok_stride, int M, const void* embed, bool bf16, int d,
-                 float* h, hipStream_t st);
+                 float* h, unsigned long long* ssq, unsigned long long* ssq_zero, hipStream_t st);
 int launch_rmsnorm(const float* h, int M, int d, const void* g, bool bf16, float eps, void* x,
                    const int32_t* row_index, hipStream_t st);
 // q/k/v from the fused projection qkv [M, (hq+2hkv)hd] (fp32): rotate q, k
@@ -85,30 +133,37 @@ int launch_w4_to_kernel_order(const uint8_t* canon, int N, int K, uint8_t* out, 
 // Philox counter word 3: which draw of a position this is.
 enum Purpose { PURPOSE_DRAFT = 0, PURPOSE_ACCEPT = 1, PURPOSE_RESIDUAL = 2, PURPOSE_AR = 3 };
 
-// Sampler.
-struct RowStats {            // per logits row
-  float zmax;
-  int32_t argmax;
-  double total;              // sum exp((z - zmax)/T) over all tokens
-  double kept;               // mass kept by top-p (== total when top_p >= 1)
-  uint32_t thr_key;          // tokens with key > thr_key are kept ...
-  int32_t thr_idx;           // ... and those with key == thr_key and index <= thr_idx
+// Sampler.  Statistics of a logits row live in one record of
+// stats_row_bytes(nch) bytes: the top-p threshold, then one ChunkStat per
+// vocabulary chunk of 2048 tokens.
+struct RowStats {            // tokens with key > thr_key are kept, and those with key == thr_key and index <= thr_idx
+  uint32_t thr_key;
+  int32_t thr_idx;
+  uint32_t pad[2];
 };
-int launch_row_stats(const float* logits, int rows, int V, long ld, float T, float top_p,
-                     RowStats* stats, hipStream_t st);
+struct ChunkStat {           // per vocabulary chunk: max logit, its first index, sum exp((z - m)/T) of kept tokens
+  float m;
+  int32_t arg;
+  double s;
+};
+__host__ __device__ inline int sampler_chunks(int V) { return (V + 2047) / 2048; }
+__host__ __device__ inline long stats_row_bytes(int nch) { return (long)sizeof(RowStats) + (long)nch * sizeof(ChunkStat); }
+
+int launch_row_stats(const float* logits, int rows, int V, long ld, float T, float top_p, void* stats,
+                     hipStream_t st);
 // Draw one token per row r from pi(logits row row_map[r] (or r)) with
 // u(seed, seq_id[r], pos[r], didx, purpose); writes out[r * out_stride].
-int launch_sample_rows(const float* logits, const RowStats* stats, int rows, int V, long ld,
-                       float T, uint64_t seed, const int32_t* seq_id, const int32_t* pos,
-                       int didx, int purpose, int32_t* out, int out_stride, const int32_t* row_map,
-                       hipStream_t st);
+int launch_sample_rows(const float* logits, const void* stats, int rows, int V, long ld, float T, float top_p,
+                       uint64_t seed, const int32_t* seq_id, const int32_t* pos, int didx, int purpose,
+                       int32_t* out, int out_stride, const int32_t* row_map, hipStream_t st);
 // Speculative decision for each sequence b of a batch: target rows
 // [B*(g+1)] (b-major), drafter rows [g*B] (draft-index-major), drafts =
 // tokens[b*(g+1) + 1 .. g]; writes out_tok[b*(g+1) ...], n_acc[b].
-int launch_spec_decide(const float* p_logits, const RowStats* p_stats, const float* q_logits,
-                       const RowStats* q_stats, const int32_t* tokens, int B, int gamma, int V,
-                       float T, uint64_t seed, const int32_t* seq_id, const int32_t* pos0,
-                       int32_t* out_tok, int32_t* n_acc, hipStream_t st);
+// resid: workspace of B * sampler_chunks(V) doubles.
+int launch_spec_decide(const float* p_logits, const void* p_stats, const float* q_logits, const void* q_stats,
+                       const int32_t* tokens, int B, int gamma, int V, float T, float top_p, uint64_t seed,
+                       const int32_t* seq_id, const int32_t* pos0, int32_t* out_tok, int32_t* n_acc,
+                       double* resid, hipStream_t st);
 
 int launch_philox_uniform(uint64_t seed, const uint32_t* ctr4, int n, double* u, hipStream_t st);
 

@@ -16,6 +16,7 @@ struct OpWs {
   float* partial = nullptr;
   int* counters = nullptr;
   float* attn = nullptr;
+  double* resid = nullptr;
   int device = -1;
 };
 OpWs g_ws;
@@ -24,6 +25,7 @@ std::mutex g_mu;
 constexpr size_t kPartialFloats = (size_t)16 << 20;
 constexpr int kCounters = 65536;
 constexpr size_t kAttnFloats = (size_t)8 << 20;
+constexpr size_t kResidDoubles = (size_t)1 << 20;
 
 int ensure_ws() {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -34,6 +36,7 @@ int ensure_ws() {
   if (hipMalloc(&g_ws.counters, kCounters * 4) != hipSuccess) return ER_ENOMEM;
   if (hipMemset(g_ws.counters, 0, kCounters * 4) != hipSuccess) return ER_EDEVICE;
   if (hipMalloc(&g_ws.attn, kAttnFloats * 4) != hipSuccess) return ER_ENOMEM;
+  if (hipMalloc(&g_ws.resid, kResidDoubles * 8) != hipSuccess) return ER_ENOMEM;
   g_ws.device = dev;
   return ER_OK;
 }
@@ -67,7 +70,7 @@ int er_op_linear(int x_dtype, const void* d_x, int ldx, int M, int fmt, const vo
                  const void* d_zero, int N, int K, float* d_y, int ldy, int path, void* stream) {
   if (!d_x || !d_w || !d_y || M < 0 || N <= 0 || K <= 0 || ldx < K || ldy < N) return ER_EINVAL;
   if (x_dtype != ER_F32 && x_dtype != ER_BF16) return ER_EINVAL;
-  if (fmt < ER_FMT_F32 || fmt > ER_FMT_W4 || path < 0 || path > 2) return ER_EINVAL;
+  if (fmt < ER_FMT_F32 || fmt > ER_FMT_W4 || path < 0 || (path > 3 && path < 1000)) return ER_EINVAL;
   if ((fmt == ER_FMT_W8 || fmt == ER_FMT_W4) && !d_scale) return ER_EINVAL;
   if (fmt == ER_FMT_W4 && !d_zero) return ER_EINVAL;
   int r = ensure_ws();
@@ -75,6 +78,59 @@ int er_op_linear(int x_dtype, const void* d_x, int ldx, int M, int fmt, const vo
   LinearW W{fmt, d_w, d_scale, d_zero, N, K};
   LinearWs ws{g_ws.partial, kPartialFloats, g_ws.counters, kCounters};
   return code(launch_linear(d_x, x_dtype == ER_BF16, ldx, M, W, d_y, ldy, EPI_F32, ws, path, (hipStream_t)stream));
+}
+
+int er_op_linear_fused(int epi, const void* d_x, int ldx, int M, int xnorm, const int32_t* d_xrow,
+                       const uint64_t* d_ssq_in, const void* d_gnorm, float eps, int fmt, const void* d_w,
+                       const void* d_scale, const void* d_zero, int N, int K, void* d_y, int ldy,
+                       uint64_t* d_ssq_acc, uint64_t* d_ssq_zero, const er_qkv_args* qkv, int path, void* stream) {
+  if (!d_x || !d_w || M < 0 || N <= 0 || K <= 0 || ldx < K) return ER_EINVAL;
+  if (fmt < ER_FMT_BF16 || fmt > ER_FMT_W4 || path < 0 || path == 1 || (path > 3 && path < 1000)) return ER_EINVAL;
+  if ((fmt == ER_FMT_W8 || fmt == ER_FMT_W4) && !d_scale) return ER_EINVAL;
+  if (fmt == ER_FMT_W4 && !d_zero) return ER_EINVAL;
+  if (xnorm && (!d_ssq_in || !d_gnorm)) return ER_EINVAL;
+  if (epi != ER_EPI_F32 && epi != ER_EPI_RESID && epi != ER_EPI_SWIGLU && epi != ER_EPI_QKV) return ER_EINVAL;
+  if (epi == ER_EPI_QKV) {
+    if (!qkv || !qkv->d_pos || !qkv->d_slot || !qkv->d_cos_sin || !qkv->d_q_out || !qkv->d_kv_pool) return ER_EINVAL;
+    if (qkv->hq <= 0 || qkv->hkv <= 0 || qkv->n_layers <= 0 || qkv->layer < 0 || qkv->layer >= qkv->n_layers)
+      return ER_EINVAL;
+  } else if (!d_y || ldy < (epi == ER_EPI_SWIGLU ? N / 2 : N)) {
+    return ER_EINVAL;
+  }
+  if (d_ssq_zero && (d_ssq_zero == d_ssq_in || d_ssq_zero == d_ssq_acc)) return ER_EINVAL;
+  int r = ensure_ws();
+  if (r) return r;
+  LinArgs a{};
+  a.x = d_x;
+  a.ldx = ldx;
+  a.M = M;
+  a.xnorm = xnorm != 0;
+  a.xrow = d_xrow;
+  a.ssq_in = (const unsigned long long*)d_ssq_in;
+  a.gnorm = d_gnorm;
+  a.eps = eps;
+  a.W = LinearW{fmt, d_w, d_scale, d_zero, N, K};
+  a.epi = epi;
+  a.y = d_y;
+  a.ldy = ldy;
+  a.act_bf16 = 1;
+  a.ssq_acc = (unsigned long long*)d_ssq_acc;
+  a.ssq_zero = (unsigned long long*)d_ssq_zero;
+  if (epi == ER_EPI_QKV) {
+    a.hq = qkv->hq;
+    a.hkv = qkv->hkv;
+    a.hd = qkv->hd;
+    a.pos = qkv->d_pos;
+    a.slot = qkv->d_slot;
+    a.cs = (const float2*)qkv->d_cos_sin;
+    a.qout = qkv->d_q_out;
+    a.kv_pool = qkv->d_kv_pool;
+    a.layer = qkv->layer;
+    a.n_layers = qkv->n_layers;
+  }
+  if (epi == ER_EPI_SWIGLU) a.F = N / 2;
+  LinearWs ws{g_ws.partial, kPartialFloats, g_ws.counters, kCounters};
+  return code(launch_linear_fused(a, ws, path, (hipStream_t)stream));
 }
 
 int er_op_attention(int act_dtype, const void* d_q, void* d_out, const void* d_kv_pool, int n_layers, int layer,
@@ -112,34 +168,36 @@ int er_op_attention(int act_dtype, const void* d_q, void* d_out, const void* d_k
   return code(launch_attention(a, (hipStream_t)stream));
 }
 
-size_t er_op_stats_bytes(void) { return sizeof(RowStats); }
+size_t er_op_stats_bytes(int V) { return V > 0 ? (size_t)stats_row_bytes(sampler_chunks(V)) : 0; }
 
 int er_op_row_stats(const float* d_logits, int rows, int V, long ld, float temperature, float top_p, void* d_stats,
                     void* stream) {
   if (!d_logits || !d_stats || rows < 0 || V <= 0 || ld < V || !(temperature >= 0.f) || !(top_p > 0.f))
     return ER_EINVAL;
-  return code(launch_row_stats(d_logits, rows, V, ld, temperature, top_p, (RowStats*)d_stats, (hipStream_t)stream));
+  return code(launch_row_stats(d_logits, rows, V, ld, temperature, top_p, d_stats, (hipStream_t)stream));
 }
 
 int er_op_sample_rows(const float* d_logits, const void* d_stats, int rows, int V, long ld, float temperature,
-                      uint64_t seed, const int32_t* d_seq_id, const int32_t* d_pos, int draft_idx, int purpose,
-                      int32_t* d_out, int out_stride, void* stream) {
+                      float top_p, uint64_t seed, const int32_t* d_seq_id, const int32_t* d_pos, int draft_idx,
+                      int purpose, int32_t* d_out, int out_stride, void* stream) {
   if (!d_logits || !d_stats || !d_seq_id || !d_pos || !d_out || rows < 0 || V <= 0 || ld < V || out_stride < 1)
     return ER_EINVAL;
-  return code(launch_sample_rows(d_logits, (const RowStats*)d_stats, rows, V, ld, temperature, seed, d_seq_id, d_pos,
-                                 draft_idx, purpose, d_out, out_stride, nullptr, (hipStream_t)stream));
+  return code(launch_sample_rows(d_logits, d_stats, rows, V, ld, temperature, top_p, seed, d_seq_id, d_pos, draft_idx,
+                                 purpose, d_out, out_stride, nullptr, (hipStream_t)stream));
 }
 
 int er_op_spec_decide(const float* d_p_logits, const void* d_p_stats, const float* d_q_logits, const void* d_q_stats,
-                      const int32_t* d_tokens, int B, int gamma, int V, float temperature, uint64_t seed,
+                      const int32_t* d_tokens, int B, int gamma, int V, float temperature, float top_p, uint64_t seed,
                       const int32_t* d_seq_id, const int32_t* d_pos0, int32_t* d_out_tok, int32_t* d_n_acc,
                       void* stream) {
   if (!d_p_logits || !d_p_stats || !d_tokens || !d_seq_id || !d_pos0 || !d_out_tok || !d_n_acc) return ER_EINVAL;
   if (gamma > 0 && (!d_q_logits || !d_q_stats)) return ER_EINVAL;
   if (B < 0 || gamma < 0 || V <= 0) return ER_EINVAL;
-  return code(launch_spec_decide(d_p_logits, (const RowStats*)d_p_stats, d_q_logits, (const RowStats*)d_q_stats,
-                                 d_tokens, B, gamma, V, temperature, seed, d_seq_id, d_pos0, d_out_tok, d_n_acc,
-                                 (hipStream_t)stream));
+  if ((size_t)B * sampler_chunks(V) > kResidDoubles) return ER_EINVAL;
+  int r = ensure_ws();
+  if (r) return r;
+  return code(launch_spec_decide(d_p_logits, d_p_stats, d_q_logits, d_q_stats, d_tokens, B, gamma, V, temperature,
+                                 top_p, seed, d_seq_id, d_pos0, d_out_tok, d_n_acc, g_ws.resid, (hipStream_t)stream));
 }
 
 int er_op_philox_uniform(uint64_t seed, const uint32_t* d_ctr, int n, double* d_u, void* stream) {

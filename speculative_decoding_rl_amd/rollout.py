@@ -180,6 +180,9 @@ class Engine:
     def reset_stats(self):
         check(self.lib.er_reset_stats(self.ctx), self.ctx, "er_reset_stats")
 
+    def set_fused(self, on: bool):
+        check(self.lib.er_set_fused(self.ctx, int(bool(on))), self.ctx, "er_set_fused")
+
     def set_timing(self, period: int, first_n: int = 0):
         check(self.lib.er_set_timing(self.ctx, period, first_n), self.ctx, "er_set_timing")
 
@@ -187,6 +190,20 @@ class Engine:
         f, t = C.c_int64(), C.c_int64()
         check(self.lib.er_kv_free_blocks(self.ctx, C.byref(f), C.byref(t)), self.ctx, "er_kv_free_blocks")
         return f.value, t.value
+
+    def set_kernel_profile(self, on: bool):
+        check(self.lib.er_set_kernel_profile(self.ctx, 1 if on else 0), self.ctx, "er_set_kernel_profile")
+
+    def reset_kernel_profile(self):
+        check(self.lib.er_reset_kernel_profile(self.ctx), self.ctx, "er_reset_kernel_profile")
+
+    def kernel_profile(self) -> list:
+        n = C.c_int()
+        check(self.lib.er_get_kernel_profile(self.ctx, None, 0, C.byref(n)), self.ctx, "er_get_kernel_profile")
+        arr = (_lib.KernelStat * max(1, n.value))()
+        check(self.lib.er_get_kernel_profile(self.ctx, arr, n.value, C.byref(n)), self.ctx, "er_get_kernel_profile")
+        return [dict(name=a.name.decode(), launches=a.launches, ms=a.ms, bytes=a.bytes, flops=a.flops)
+                for a in arr[:n.value]]
 
     def debug_logits(self, which: int, slot: int) -> np.ndarray:
         rows = C.c_int32()

@@ -43,6 +43,9 @@ class Shape:
 
 SHAPES = {
     "tiny": Shape("tiny", 2, 256, 4, 2, 64, 688, 1024, "f32", 1e-6, 1e4, "w8"),
+    # small bf16 decoder with the 7B family's head layout (hd 128, GQA) and a
+    # vocabulary that is not a multiple of the sampler's 2048-token chunks
+    "mini-bf16": Shape("mini-bf16", 2, 512, 4, 2, 128, 1536, 8000, "bf16", 1e-6, 1e6, "w4"),
     "qwen2.5-7b": Shape("qwen2.5-7b", 28, 3584, 28, 4, 128, 18944, 152064, "bf16", 1e-6, 1e6, "w4"),
     "qwen2.5-14b": Shape("qwen2.5-14b", 48, 5120, 40, 8, 128, 13824, 152064, "bf16", 1e-6, 1e6, "w4"),
     "qwen2.5-32b": Shape("qwen2.5-32b", 64, 5120, 40, 8, 128, 27648, 152064, "bf16", 1e-6, 1e6, "w4"),

@@ -19,7 +19,7 @@ import numpy as np
 from oracle import philox as OP
 from oracle import sampling as OS
 from oracle import spec as OSP
-from oracle.model import forward
+from oracle.model import KVStore, forward
 
 
 def rel_err(got, ref):
@@ -85,3 +85,64 @@ class Tally:
             self.max_abs_q = max(self.max_abs_q, abs_err(gq, oq))
         self.max_rel_p = max(self.max_rel_p, rel_err(gp, op))
         self.max_abs_p = max(self.max_abs_p, abs_err(gp, op))
+
+
+def run_lockstep(eng, cfg, W, D, prompts, new, gamma, sp: OSP.SamplingParams, max_steps=None):
+    """Prefill `prompts` on the engine and run spec steps at fixed gamma until
+    every sequence has `new` tokens (or `max_steps`), checking each step
+    against the oracle.  Returns (generated tokens per sequence, Tally)."""
+    n_seq = len(prompts)
+    eng.set_gamma(gamma)
+    ids = eng.kv_alloc([len(p) for p in prompts], [new] * n_seq)
+    first = eng.prefill(ids, [list(p) for p in prompts])
+    tally = Tally()
+    states = []
+    for i in range(n_seq):
+        kv = KVStore(cfg, len(prompts[i]) + new + gamma + 4)
+        z = forward(cfg, W, list(prompts[i]), list(range(len(prompts[i]))), kv)
+        gz = eng.debug_logits(1, i)
+        tally.logits(None, None, gz[0], z[-1])
+        # sampler on the GPU's logits reproduces the GPU's token exactly
+        assert OSP.ar_sample(gz[0].astype(np.float64), int(ids[i]), len(prompts[i]), sp) == first[i]
+        st = OSP.SeqState(seq_id=int(ids[i]), pending=int(first[i]), n=len(prompts[i]), kv=kv, stop_len=new,
+                          generated=[int(first[i])])
+        states.append(st)
+    gen = [[int(first[i])] for i in range(n_seq)]
+    active = list(range(n_seq))
+    while active and (max_steps is None or tally.steps < max_steps):
+        b_ids = [int(ids[i]) for i in active]
+        tok, ne, info = eng.spec_step(b_ids)
+        drafts = eng.debug_drafts(len(active), gamma)
+        tally.steps += 1
+        nxt = []
+        for slot, i in enumerate(active):
+            st = states[i]
+            gq = eng.debug_logits(0, slot)
+            gp = eng.debug_logits(1, slot)
+            oq, op = teacher_forced(cfg, W, D, st, drafts[slot])
+            tally.logits(gq, oq, gp, op)
+            # drafts: the oracle sampler on the GPU's drafter logits gives the GPU's drafts
+            for j in range(gamma):
+                assert OSP.draft_sample(gq[j].astype(np.float64), st.seq_id, st.n + j + 1, j + 1, sp) == drafts[slot][j]
+            # decision on the GPU's logits: exact
+            a_g, em_g = OSP.spec_decide(gp.astype(np.float64), gq.astype(np.float64), drafts[slot], st.seq_id, st.n, sp)
+            kept = int(ne[slot])
+            assert em_g[:kept] == list(tok[slot, :kept]), (tally.steps, slot)
+            # decision on the oracle's logits: equal unless flagged
+            a_o, em_o = OSP.spec_decide(op, oq, drafts[slot], st.seq_id, st.n, sp)
+            if (a_o, em_o) != (a_g, em_g):
+                if decision_flags(op, oq, drafts[slot], st.seq_id, st.n, sp, min(a_o, a_g)) or \
+                        decision_flags(gp.astype(np.float64), gq.astype(np.float64), drafts[slot], st.seq_id, st.n,
+                                       sp, min(a_o, a_g)) or a_o == a_g:
+                    tally.flagged += 1
+                    if tally.first_flag_step is None:
+                        tally.first_flag_step = tally.steps
+                else:
+                    tally.unflagged_mismatch += 1
+            OSP.commit(st, em_g, a_g)
+            gen[i].extend(int(t) for t in tok[slot, :kept])
+            if len(st.generated) < new:
+                nxt.append(i)
+        active = nxt
+    eng.kv_free(ids)
+    return gen, tally

@@ -14,9 +14,9 @@ torch = pytest.importorskip("torch")
 
 import synth  # noqa: E402
 from oracle import spec as OSP  # noqa: E402
-from oracle.model import KVStore, config_from, forward, weights_from  # noqa: E402
+from oracle.model import config_from, forward, weights_from  # noqa: E402
 
-from lockstep import Tally, decision_flags, teacher_forced  # noqa: E402
+from lockstep import run_lockstep  # noqa: E402
 
 
 def _engine(shape, wts, quant, **kw):
@@ -49,59 +49,9 @@ def _lockstep_rollout(tiny, T, top_p, gamma, n_seq=4, plen=32, new=64, seed=0):
     shape, wts, cfg, W, D = tiny
     prompts = synth.prompts(n_seq, plen, shape.vocab, seed=seed)
     eng = _engine(shape, wts, "w8", seed=seed, temperature=T, top_p=top_p, gamma_max=8)
-    eng.set_gamma(gamma)
-    ids = eng.kv_alloc([plen] * n_seq, [new] * n_seq)
-    first = eng.prefill(ids, list(prompts))
     sp = OSP.SamplingParams(seed=seed, temperature=T, top_p=top_p)
-    tally = Tally()
-    states = []
-    for i in range(n_seq):
-        kv = KVStore(cfg, plen + new + gamma + 4)
-        z = forward(cfg, W, list(prompts[i]), list(range(plen)), kv)
-        gz = eng.debug_logits(1, i)
-        tally.logits(None, None, gz[0], z[-1])
-        # sampler on the GPU's logits reproduces the GPU's token exactly
-        assert OSP.ar_sample(gz[0].astype(np.float64), int(ids[i]), plen, sp) == first[i]
-        st = OSP.SeqState(seq_id=int(ids[i]), pending=int(first[i]), n=plen, kv=kv, stop_len=new,
-                          generated=[int(first[i])])
-        states.append(st)
-    gen = [[int(first[i])] for i in range(n_seq)]
-    active = list(range(n_seq))
-    while active:
-        b_ids = [int(ids[i]) for i in active]
-        tok, ne, info = eng.spec_step(b_ids)
-        drafts = eng.debug_drafts(len(active), gamma)
-        tally.steps += 1
-        nxt = []
-        for slot, i in enumerate(active):
-            st = states[i]
-            gq = eng.debug_logits(0, slot)
-            gp = eng.debug_logits(1, slot)
-            oq, op = teacher_forced(cfg, W, D, st, drafts[slot])
-            tally.logits(gq, oq, gp, op)
-            # drafts: the oracle sampler on the GPU's drafter logits gives the GPU's drafts
-            for j in range(gamma):
-                assert OSP.draft_sample(gq[j].astype(np.float64), st.seq_id, st.n + j + 1, j + 1, sp) == drafts[slot][j]
-            # decision on the GPU's logits: exact
-            a_g, em_g = OSP.spec_decide(gp.astype(np.float64), gq.astype(np.float64), drafts[slot], st.seq_id, st.n, sp)
-            kept = int(ne[slot])
-            assert em_g[:kept] == list(tok[slot, :kept]), (tally.steps, slot)
-            # decision on the oracle's logits: equal unless flagged
-            a_o, em_o = OSP.spec_decide(op, oq, drafts[slot], st.seq_id, st.n, sp)
-            if (a_o, em_o) != (a_g, em_g):
-                if decision_flags(op, oq, drafts[slot], st.seq_id, st.n, sp, min(a_o, a_g)) or \
-                        decision_flags(gp.astype(np.float64), gq.astype(np.float64), drafts[slot], st.seq_id, st.n,
-                                       sp, min(a_o, a_g)) or a_o == a_g:
-                    tally.flagged += 1
-                    if tally.first_flag_step is None:
-                        tally.first_flag_step = tally.steps
-                else:
-                    tally.unflagged_mismatch += 1
-            OSP.commit(st, em_g, a_g)
-            gen[i].extend(int(t) for t in tok[slot, :kept])
-            if len(st.generated) < new:
-                nxt.append(i)
-        active = nxt
+    gen, tally = run_lockstep(eng, cfg, W, D, prompts, new, gamma, sp)
+    eng.close()
     return gen, tally, prompts
 
 

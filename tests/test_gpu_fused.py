@@ -1,0 +1,213 @@
+"""Parity of the fused linear (er_op_linear_fused) against the oracle's pieces.
+
+Each case builds x' the way the oracle's decoder does (RMSNorm of the fp32
+residual rows, stored as bf16), multiplies by the weights in fp64 and applies
+the oracle's epilogue (residual add, SwiGLU, rotate-half RoPE with the KV
+append).  Tolerances follow from the arithmetic: the kernel accumulates in
+fp32 (error a small multiple of 2^-24 * sum|x'||w| = "bound"), x' may land one
+bf16 ulp away where the norm's rounding differs (2^-8 relative per element, so
+at most 2^-8 * bound on a dot product), and bf16 outputs carry one more
+rounding (2^-8 relative).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+from oracle import quant as OQ  # noqa: E402
+from oracle.model import rmsnorm, rope, rope_cos_sin, silu  # noqa: E402
+from oracle.numerics import round_bf16  # noqa: E402
+
+SSQ = float(2 ** 24)
+BF = 2.0 ** -8
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from speculative_decoding_rl_amd import ops as _ops
+    from speculative_decoding_rl_amd import _lib
+    _lib.load()
+    return _ops
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def _weights(fmt, N, K, g, ops):
+    """Device weight operands and the oracle's (dequantized) fp64 matrix."""
+    from speculative_decoding_rl_amd import _lib
+    w = (torch.randn(N, K, generator=g) * 0.02).to(torch.bfloat16)
+    if fmt == "bf16":
+        return (_lib.ER_FMT_BF16, w.cuda(), None, None), w.float().numpy().astype(np.float64)
+    if fmt == "w8":
+        codes = torch.zeros(N, K, dtype=torch.int8, device="cuda")
+        scale = torch.zeros(N, dtype=torch.float32, device="cuda")
+        ops.quantize("w8", w.cuda(), codes, scale)
+        q, s = OQ.quantize_w8(w.float().numpy().astype(np.float64))
+        return (_lib.ER_FMT_W8, codes, scale, None), OQ.dequantize_w8(q, s)
+    canon = torch.zeros(N, K // 2, dtype=torch.uint8, device="cuda")
+    kord = torch.zeros_like(canon)
+    scale = torch.zeros(N, K // 128, dtype=torch.bfloat16, device="cuda")
+    zero = torch.zeros(N, K // 128, dtype=torch.uint8, device="cuda")
+    ops.quantize("w4", w.cuda(), canon, scale, zero)
+    ops.w4_kernel_order(canon, N, K, kord)
+    c, s, z = OQ.quantize_w4(w.float().numpy().astype(np.float64))
+    return (_lib.ER_FMT_W4, kord, scale, zero), OQ.dequantize_w4(c, s, z)
+
+
+def _norm_input(M, K, g, rows=None):
+    """fp32 residual rows h, gain g, row map, fixed-point sums of squares, and x' (oracle)."""
+    R = rows or M
+    h = (torch.randn(R, K, generator=g) * 0.7).numpy().astype(np.float32)
+    gain = (1.0 + 0.1 * torch.randn(K, generator=g)).to(torch.bfloat16)
+    xrow = np.arange(M, dtype=np.int32) if rows is None else \
+        torch.randperm(R, generator=g)[:M].numpy().astype(np.int32)
+    hd = h.astype(np.float64)
+    ssq = np.rint(np.sum(hd * hd, axis=1) * SSQ).astype(np.uint64)
+    xs = round_bf16(rmsnorm(hd[xrow], gain.float().numpy().astype(np.float64), 1e-6))
+    return h, gain, xrow, ssq, xs
+
+
+def _bound(xs, wd):
+    return np.abs(xs) @ np.abs(wd).T
+
+
+CASES = [  # (fmt, M, path): skinny M-tiles, the tiled GEMM and its split-K reduction
+    ("bf16", 1, 0), ("bf16", 13, 0), ("bf16", 29, 0), ("bf16", 45, 0), ("bf16", 20, 3),
+    ("w4", 1, 0), ("w4", 20, 0), ("w4", 45, 0), ("w8", 7, 0), ("w8", 33, 0),
+]
+
+
+@pytest.mark.parametrize("fmt,M,path", CASES)
+def test_fused_norm_plain(ops, fmt, M, path):
+    """x' = RMSNorm(h[xrow]) * g on load; y = x' W^T (the lm-head form, rows gathered)."""
+    from speculative_decoding_rl_amd import _lib
+    g = torch.Generator().manual_seed(100 + M)
+    N, K = 1000, 640
+    h, gain, xrow, ssq, xs = _norm_input(M, K, g, rows=M + 9)
+    (f, w, sc, zr), wd = _weights(fmt, N, K, g, ops)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ops.linear_fused(_lib.EPI_F32, dev(h), M, f, w, N, K, y, sc, zr, xnorm=True, xrow=dev(xrow),
+                     ssq_in=dev(ssq.view(np.int64)), gnorm=gain.cuda(), path=path)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    ref = xs @ wd.T
+    bound = _bound(xs, wd)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= BF * bound + 1e-6), np.max(np.abs(got - ref) / bound)
+
+
+@pytest.mark.parametrize("fmt,M,path", CASES)
+def test_fused_residual_and_sums_of_squares(ops, fmt, M, path):
+    """h += x W^T (x bf16); the updated rows' sums of squares are added in 2^-24 fixed point; ssq_zero cleared."""
+    from speculative_decoding_rl_amd import _lib
+    g = torch.Generator().manual_seed(200 + M)
+    N, K = 896, 1536
+    x = torch.randn(M, K, generator=g).to(torch.bfloat16)
+    xd = x.float().numpy().astype(np.float64)
+    (f, w, sc, zr), wd = _weights(fmt, N, K, g, ops)
+    h0 = (torch.randn(M, N, generator=g)).numpy().astype(np.float32)
+    y = dev(h0)
+    acc0 = np.arange(M, dtype=np.uint64) * 12345 + 7
+    acc = dev(acc0.view(np.int64))
+    zero = dev(np.full(M + 5, 99, dtype=np.int64))
+    ops.linear_fused(_lib.EPI_RESID, x.cuda(), M, f, w, N, K, y, sc, zr, ssq_acc=acc, ssq_zero=zero, path=path)
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    ref = h0.astype(np.float64) + xd @ wd.T
+    bound = _bound(xd, wd)
+    # same accumulation bound as er_op_linear's parity test (4e-6 of sum|x||w|) plus the add's rounding
+    assert np.all(np.abs(got - ref) <= 8e-6 * bound + 2.0 ** -23 * np.abs(ref) + 1e-6), np.max(np.abs(got - ref) / bound)
+    # sums of squares of the rows as stored, each work-group's partial rounded to 2^-24
+    s_got = (acc.cpu().numpy().view(np.uint64) - acc0).astype(np.float64) / SSQ
+    s_ref = np.sum(got * got, axis=1)
+    assert np.all(np.abs(s_got - s_ref) <= 1e-6 * s_ref + N * 2.0 ** -24), np.max(np.abs(s_got - s_ref) / s_ref)
+    z = zero.cpu().numpy()
+    assert np.all(z[:M] == 0) and np.all(z[M:] == 99)
+
+
+@pytest.mark.parametrize("fmt,M,path", CASES)
+def test_fused_norm_swiglu(ops, fmt, M, path):
+    """W = [gate; up]: y = bf16(silu(x' Wg^T) * (x' Wu^T))."""
+    from speculative_decoding_rl_amd import _lib
+    g = torch.Generator().manual_seed(300 + M)
+    F, K = 328, 512  # F % 8 == 0, not a multiple of the 16-row subtile pairs' 64-row tiles
+    h, gain, xrow, ssq, xs = _norm_input(M, K, g)
+    (f, w, sc, zr), wd = _weights(fmt, 2 * F, K, g, ops)
+    y = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ops.linear_fused(_lib.EPI_SWIGLU, dev(h), M, f, w, 2 * F, K, y, sc, zr, xnorm=True,
+                     ssq_in=dev(ssq.view(np.int64)), gnorm=gain.cuda(), path=path)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    gu = xs @ wd.T
+    bound = _bound(xs, wd) * BF
+    ga, up = gu[:, :F], gu[:, F:]
+    ref = silu(ga) * up
+    tol = BF * np.abs(ref) + 1.1 * np.abs(up) * bound[:, :F] + np.abs(silu(ga)) * bound[:, F:] + 1e-6
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= tol), np.max(np.abs(got - ref) / tol)
+
+
+@pytest.mark.parametrize("fmt,M,path", CASES)
+def test_fused_norm_qkv_rope_kv_append(ops, fmt, M, path):
+    """W = [q; k; v]: RoPE on q, k at pos[m]; q -> q_out, k and v -> the paged pool at slot[m]."""
+    from speculative_decoding_rl_amd import _lib
+    g = torch.Generator().manual_seed(400 + M)
+    hq, hkv, hd, K = 4, 2, 128, 512
+    N = (hq + 2 * hkv) * hd
+    L, layer, nblk = 3, 1, 8
+    h, gain, xrow, ssq, xs = _norm_input(M, K, g)
+    (f, w, sc, zr), wd = _weights(fmt, N, K, g, ops)
+    pos = torch.randint(0, 500, (M,), generator=g).numpy().astype(np.int32)
+    slot = torch.randperm(nblk * 16, generator=g)[:M].numpy().astype(np.int64)
+    max_pos = 512
+    cos, sin = rope_cos_sin(np.arange(max_pos), hd, 1e6)
+    cs = np.stack([cos, sin], axis=-1).astype(np.float32)
+    pool_elems = nblk * L * 2 * hkv * 16 * hd
+    sentinel = np.float32(-3.0)
+    pool = torch.full((pool_elems,), float(sentinel), dtype=torch.bfloat16, device="cuda")
+    qout = torch.full((M, hq, hd), float("nan"), dtype=torch.bfloat16, device="cuda")
+    qkv = dict(hq=hq, hkv=hkv, hd=hd, pos=dev(pos), slot=dev(slot), cos_sin=dev(cs), q_out=qout, kv_pool=pool,
+               layer=layer, n_layers=L)
+    ops.linear_fused(_lib.EPI_QKV, dev(h), M, f, w, N, K, None, sc, zr, xnorm=True, ssq_in=dev(ssq.view(np.int64)),
+                     gnorm=gain.cuda(), qkv=qkv, path=path)
+    torch.cuda.synchronize()
+    raw = xs @ wd.T
+    bound = _bound(xs, wd) * BF
+    q = raw[:, :hq * hd].reshape(M, hq, hd)
+    k = raw[:, hq * hd:(hq + hkv) * hd].reshape(M, hkv, hd)
+    v = raw[:, (hq + hkv) * hd:].reshape(M, hkv, hd)
+    # error of a rotated pair is at most the sum of both inputs' errors (|cos|, |sin| <= 1)
+    def pair_bound(b):
+        b = b.reshape(M, -1, hd)
+        s = b[..., :hd // 2] + b[..., hd // 2:]
+        return np.concatenate([s, s], axis=-1)
+    qb = pair_bound(bound[:, :hq * hd])
+    kb = pair_bound(bound[:, hq * hd:(hq + hkv) * hd])
+    vb = bound[:, (hq + hkv) * hd:].reshape(M, hkv, hd)
+    q_ref = rope(q, pos, 1e6)
+    k_ref = rope(k, pos, 1e6)
+    q_got = qout.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(q_got - q_ref) <= BF * np.abs(q_ref) + qb + 1e-5)
+    P = pool.float().cpu().numpy().astype(np.float64).reshape(nblk, L, 2, hkv, 16, hd)
+    touched = np.zeros(P.shape, dtype=bool)
+    for m in range(M):
+        b, o = divmod(int(slot[m]), 16)
+        k_got = P[b, layer, 0, :, o, :]
+        assert np.all(np.abs(k_got - k_ref[m]) <= BF * np.abs(k_ref[m]) + kb[m] + 1e-5)
+        touched[b, layer, 0, :, o, :] = True
+        # V is stored transposed within the block: [hd][16]
+        vt = P[b, layer, 1].reshape(hkv, hd, 16)[:, :, o]
+        assert np.all(np.abs(vt - v[m]) <= BF * np.abs(v[m]) + vb[m] + 1e-5)
+        tv = touched[b, layer, 1].reshape(hkv, hd, 16)
+        tv[:, :, o] = True
+        touched[b, layer, 1] = tv.reshape(hkv, 16, hd)
+    assert np.all(P[~touched] == sentinel)

@@ -149,9 +149,16 @@ def test_linear_fp32_activations(ops, fmt):
 
 
 def test_linear_wide_and_deep(ops):
-    # lm_head-like width (wide tiles) and ffn-like depth (many split-K chunks)
+    # lm_head-like width (wide tiles) and ffn-like depth (many K chunks split over waves)
     assert _linear_case(ops, "w4", 3, 8192, 256, 2, seed=1) < 4e-6
+    assert _linear_case(ops, "w4", 16, 130, 18944, 2, seed=4) < 4e-6
     assert _linear_case(ops, "bf16", 9, 96, 18944, 2, seed=2) < 4e-6
+
+
+@pytest.mark.parametrize("M,N,K", [(40, 96, 18944), (300, 200, 1152), (1000, 300, 512), (129, 4608, 384)])
+def test_linear_tiled_gemm(ops, M, N, K):
+    # M > 32 takes the LDS-tiled GEMM (split-K with a fixed-order reduction when tiles are few)
+    assert _linear_case(ops, "bf16", M, N, K, 0, seed=M) < 4e-6
 
 
 # ---------------------------------------------------------------------------
@@ -167,14 +174,16 @@ def _attn_case(ops, bf16, hq, hkv, hd, items, L=2, layer=1, seed=0):
     for i, nb in enumerate(nblk_seq):
         bt[i, :nb] = perm[k:k + nb]
         k += nb
-    pool = rng.standard_normal((total_blocks, L, 2, hkv, 16, hd))
+    pool = rng.standard_normal((total_blocks, L, 2, hkv, 16, hd))   # logical [.., position, element]
     Mq = sum(q for _, q in items)
     qv = rng.standard_normal((Mq, hq, hd))
     if bf16:
         pool = round_bf16(pool).reshape(pool.shape)
         qv = round_bf16(qv).reshape(qv.shape)
     tdt = torch.bfloat16 if bf16 else torch.float32
-    pool_t = dev(pool.astype(np.float32)).to(tdt)
+    stored = pool.copy()
+    stored[:, :, 1] = np.swapaxes(pool[:, :, 1], -1, -2).reshape(pool[:, :, 1].shape)  # V stored as [hd][16]
+    pool_t = dev(stored.astype(np.float32)).to(tdt)
     q_t = dev(qv.astype(np.float32)).to(tdt)
     out = torch.zeros(Mq, hq * hd, dtype=tdt, device="cuda")
     row0, pos0, cnt = [], [], []
@@ -221,8 +230,8 @@ def test_attention_head_dim_64_and_long_split(ops):
 
 # ---------------------------------------------------------------------------
 def _stats(ops, logits_t, T, top_p):
-    n = logits_t.shape[0]
-    st = torch.zeros(n * ops.stats_bytes(), dtype=torch.uint8, device="cuda")
+    n, V = logits_t.shape
+    st = torch.zeros(n * ops.stats_bytes(V), dtype=torch.uint8, device="cuda")
     ops.row_stats(logits_t, T, top_p, st)
     return st
 
@@ -231,7 +240,7 @@ def _stats(ops, logits_t, T, top_p):
 def test_sample_rows_match_oracle(ops, T, top_p):
     from speculative_decoding_rl_amd import _lib
     rng = np.random.Generator(np.random.PCG64(11))
-    R, V = 64, 5000
+    R, V = 64, 9000
     z = (rng.standard_normal((R, V)) * 1.5).astype(np.float32)
     z[0, 10] = z[0, 20] = z[0].max() + 1.0       # tie at the argmax
     z[1, ::2] = 0.25                              # many equal logits
@@ -240,7 +249,7 @@ def test_sample_rows_match_oracle(ops, T, top_p):
     seq = np.arange(R, dtype=np.int32) * 3 + 1
     pos = np.arange(R, dtype=np.int32) + 100
     out = torch.zeros(R, dtype=torch.int32, device="cuda")
-    ops.sample_rows(zt, st, T, 42, dev(seq), dev(pos), 2, _lib.PURPOSE_DRAFT, out)
+    ops.sample_rows(zt, st, T, 42, dev(seq), dev(pos), 2, _lib.PURPOSE_DRAFT, out, top_p=top_p)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     sp = OSP.SamplingParams(seed=42, temperature=T, top_p=top_p)
@@ -281,7 +290,7 @@ def test_spec_decide_matches_oracle(ops, T, top_p, gamma):
     qs = _stats(ops, qt, T, top_p)
     out = torch.zeros(B * G1, dtype=torch.int32, device="cuda")
     nacc = torch.zeros(B, dtype=torch.int32, device="cuda")
-    ops.spec_decide(pt, ps, qt, qs, dev(toks), B, gamma, T, 9, dev(seq), dev(pos0), out, nacc)
+    ops.spec_decide(pt, ps, qt, qs, dev(toks), B, gamma, T, 9, dev(seq), dev(pos0), out, nacc, top_p=top_p)
     torch.cuda.synchronize()
     got_tok = out.cpu().numpy().reshape(B, G1)
     got_a = nacc.cpu().numpy()
