@@ -43,11 +43,20 @@ int er_op_quantize(int quant, int w_dtype, const void *d_w, int N, int K, void *
 int er_op_w4_kernel_order(const void *d_canon, int N, int K, void *d_out, void *stream);
 
 /* y[m, n] = sum_k x[m, k] W[n, k] for m < M, n < N; y fp32 [M, ldy].
- * x: [M, ldx] of x_dtype (ER_BF16 or ER_F32).  path: 0 automatic, 1 VALU,
- * 2 MFMA (bf16 x, K % 128 == 0), 3 tiled GEMM (bf16 W), or a skinny MFMA
- * variant 1000 + 100*NR + 10*KS + MT/16 (16*NR rows per wave, K split over KS
- * of the 8 waves, m-tile MT in {16, 32}; ER_EINVAL if M > MT).  The verify pass runs the target's linears
- * with this at M = B (gamma + 1); the drafter runs its quantized copies at M = B. */
+ * x: [M, ldx] of x_dtype (ER_BF16 or ER_F32).  The verify pass runs the
+ * target's linears at M = B (gamma + 1); the drafter runs its quantized copies
+ * at M = B.  path (ER_EINVAL where a kernel does not take the shape):
+ *   0      automatic (what the rollout uses)
+ *   1      VALU (fp32 activations or weights)
+ *   2      register-fed skinny MFMA kernel, 32-row m-tiles (bf16 x, K % 128 == 0)
+ *   3      LDS-tiled 128x128 GEMM (bf16 W)
+ *   1000 + 100*NR + 10*KS + MT/16   that register-fed variant (16*NR rows per
+ *          wave, K split over KS of the 8 waves, m-tile MT in {16, 32})
+ *   2000 + 100*NR + 10*KS + D       streaming kernel, M <= 16: x staged in LDS,
+ *          weights through a D-deep register ring
+ *   30000 + 1000*NR + 100*KS + 10*D + i   weight-streaming GEMM, M <= 16 * {2,4,8,16}[i]
+ *   40000 + 100*i + 10*D + w        deep-pipelined GEMM, BM = {_,64,128,256}[i],
+ *          register ring depth D, split-K until 256*w work-groups */
 int er_op_linear(int x_dtype, const void *d_x, int ldx, int M, int fmt, const void *d_w, const void *d_scale,
                  const void *d_zero, int N, int K, float *d_y, int ldy, int path, void *stream);
 

@@ -225,12 +225,12 @@ double weight_bytes(const LinearW& W) {
 // Layout of everything but the KV pool, shared by er_arena_bytes and init.
 struct Layout {
   size_t drafter = 0, cs = 0, h = 0, xbuf = 0, qkv = 0, qb = 0, gu = 0, lp = 0, lq = 0, sp = 0, sq = 0;
-  size_t out = 0, partial = 0, counters = 0, attn = 0, w4tmp = 0, sink = 0, meta = 0, resid = 0, ssq = 0;
+  size_t out = 0, partial = 0, counters = 0, attn = 0, w4tmp = 0, sink = 0, meta = 0, resid = 0, ssq = 0, xn = 0;
   size_t block_bytes = 0;
   int max_rows = 0, logit_rows = 0;
   size_t total_fixed() const {
     return drafter + cs + h + xbuf + qkv + qb + gu + lp + lq + sp + sq + out + partial + counters + attn + w4tmp +
-           sink + meta + resid + ssq;
+           sink + meta + resid + ssq + xn;
   }
 };
 
@@ -268,6 +268,7 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
   L->sq = align256((size_t)r.max_batch * r.gamma_max * srb);
   L->resid = align256((size_t)r.max_batch * sampler_chunks((int)V) * 8);
   L->ssq = 2 * align256((size_t)R * 8);
+  L->xn = align256((size_t)R * d * 2);
   L->out = align256((size_t)(L->max_rows + r.max_batch) * 4);
   L->partial = align256((size_t)16 << 20) * 4;  // 16M floats
   L->counters = align256((size_t)65536 * 4);
@@ -1156,6 +1157,8 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->lws.partial_floats = L.partial / 4;
     c->lws.counters = (int*)take(L.counters);
     c->lws.n_counters = (int)(L.counters / 4);
+    c->lws.xn = (uint16_t*)take(L.xn);
+    c->lws.xn_elems = L.xn / 2;
     c->attn_ws = (float*)take(L.attn);
     c->attn_ws_floats = L.attn / 4;
     c->w4_tmp = (uint8_t*)take(L.w4tmp);

@@ -95,15 +95,33 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   const int32_t* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
 
   if (rgi < rgroups) {
-    for (int blk = b0 + sin; blk < b1; blk += s_in) {
+    // K and V fragments of the next block are loaded while the current one
+    // is scored (register double buffer)
+    uint4 kn[NQ];
+    uint2 vn[NC];
+    auto fetch = [&](int blk) {
       const long phys = bt[blk];
       const uint16_t* kp = pool + kv_block_base(phys, a.layer, a.n_layers, 0, a.hkv, g, HD);
       const uint16_t* vp = pool + kv_block_base(phys, a.layer, a.n_layers, 1, a.hkv, g, HD);
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) kn[i] = *(const uint4*)(kp + l16 * HD + 32 * i + 8 * kb);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vn[c] = *(const uint2*)(vp + (16 * c + l16) * 16 + 4 * kb);
+    };
+    if (b0 + sin < b1) fetch(b0 + sin);
+    for (int blk = b0 + sin; blk < b1; blk += s_in) {
+      uint4 kc[NQ];
+      uint2 vc[NC];
+#pragma unroll
+      for (int i = 0; i < NQ; ++i) kc[i] = kn[i];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) vc[c] = vn[c];
+      if (blk + s_in < b1) fetch(blk + s_in);
       // S^T = K . Q^T: A = K rows (token l16), k = 8*kb + 32*i
       f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NQ; ++i) {
-        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, *(const uint4*)(kp + l16 * HD + 32 * i + 8 * kb));
+        const bf16x8_t kf = __builtin_bit_cast(bf16x8_t, kc[i]);
         s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[i], s, 0, 0, 0);
       }
       // lane holds tokens 4*kb + r of row l16
@@ -158,7 +176,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[c][r] *= cr[r];
         // B = V^T: n = column 16c + l16, k = tokens 4*kb .. +4
-        const bf16x4s_t vf = __builtin_bit_cast(bf16x4s_t, *(const uint2*)(vp + (16 * c + l16) * 16 + 4 * kb));
+        const bf16x4s_t vf = __builtin_bit_cast(bf16x4s_t, vc[c]);
         o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[c], 0, 0, 0);
         o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vf, o[c], 0, 0, 0);
       }
@@ -310,8 +328,18 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
   if (grp * a.max_q_count > 64) return -1;
   const int maxblk = (a.max_ctx + 15) / 16;
   const long base = (long)a.n_items * a.hkv;
-  // split the keys over work-groups until ~512 groups are in flight (>= 4 blocks each)
-  int nsplit = (int)std::max(1L, std::min((long)(maxblk + 3) / 4, (512 + base - 1) / base));
+  // Waves of a work-group that share its KV range (the rest hold other query
+  // rows): 4 when the rows fit one 16-row group, 2 for two, else 1.
+  const int rows = grp * a.max_q_count;
+  const int rgroups = (rows + 15) / 16;
+  const int s_in = rgroups == 1 ? 4 : (rgroups == 2 ? 2 : 1);
+  // Split the keys over work-groups until each wave walks at most 4 blocks
+  // (each block is a dependent load of scattered pages), but no further than
+  // ~512 groups in flight.
+  const int per_wg = 4 * s_in;
+  int nsplit = 1;
+  if (maxblk > per_wg)
+    nsplit = (int)std::max(1L, std::min((long)(maxblk + per_wg - 1) / per_wg, (512 + base - 1) / base));
   const int bps = (maxblk + nsplit - 1) / nsplit;
   nsplit = (maxblk + bps - 1) / bps;
   if (nsplit > 1) {

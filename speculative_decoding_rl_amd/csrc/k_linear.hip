@@ -18,6 +18,7 @@
 // EfficientRollout page ("关键模块" item 1: W4/W8 drafter from the target's own
 // weights); the verify kernels are the target's linears at M = B * (gamma+1).
 
+#include <algorithm>
 #include <cstdio>
 
 #include "common.h"
@@ -200,6 +201,12 @@ ER_DEV void epilogue(const LinArgs& a, int m, int n, float v, float partner, boo
   if (a.epi == EPI_RESID) ((float*)a.y)[o] += v;
   else if (a.epi == EPI_ACT && a.act_bf16) ((uint16_t*)a.y)[o] = (uint16_t)f2bf(v);
   else ((float*)a.y)[o] = v;
+}
+
+// Out-of-line epilogue for kernels with large accumulator tiles: keeps the
+// fully unrolled store loop small enough that the tile stays in registers.
+__device__ __noinline__ void epilogue_call(const LinArgs& a, int m, int n, float v, float partner, bool write, int l16) {
+  epilogue(a, m, n, v, partner, write, l16);
 }
 
 // Sum of squares of the updated residual rows: `sq` is this lane's
@@ -454,11 +461,13 @@ __global__ __launch_bounds__(512) void k_linear_mfma(LinArgs a, int mtiles) {
 // k_splitk_reduce sums them in a fixed order and applies the epilogue.
 // ----------------------------------------------------------------------------
 constexpr int GB_M = 128, GB_N = 128, GB_K = 64, GB_LD = GB_K + 8;
+constexpr size_t kSkinnyLdsMax = (size_t)160 << 10;
 
 __global__ __launch_bounds__(256) void k_gemm_bf16(LinArgs a, float* __restrict__ part, int nsplit,
                                                    int ksteps_per_split, int mtiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][GB_M * GB_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][GB_N * GB_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * GB_M * GB_LD + 2 * GB_N * GB_LD];
+  uint16_t (*As)[GB_M * GB_LD] = reinterpret_cast<uint16_t (*)[GB_M * GB_LD]>(smem);
+  uint16_t (*Bs)[GB_N * GB_LD] = reinterpret_cast<uint16_t (*)[GB_N * GB_LD]>(smem + 2 * GB_M * GB_LD);
   __shared__ float rs_sh[GB_M];
   const int b = blockIdx.x, nwg = gridDim.x;
   const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
@@ -558,9 +567,9 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(LinArgs a, float* __restrict_
   // epilogue walks it row-wise: coalesced stores, pair partners at column ^ 8,
   // one sum-of-squares partial per (row, 64 columns).
   // acc[i][j][r] is row 64 wm + 16 i + 4 kb + r, column 64 wn + 16 j + l16.
-  float* Cs = reinterpret_cast<float*>(&As[0][0]);
+  float* Cs = reinterpret_cast<float*>(smem);
   constexpr int CLD = GB_N + 4;
-  static_assert(sizeof(As) + sizeof(Bs) >= sizeof(float) * GB_M * CLD, "C tile does not fit");
+  static_assert(sizeof(smem) >= sizeof(float) * GB_M * CLD, "C tile does not fit");
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -653,6 +662,776 @@ static int run_gemm(const LinArgs& a, const LinearWs& ws, hipStream_t st, Linear
 }
 
 // ----------------------------------------------------------------------------
+// Streaming skinny linear for M <= 16 (decode, drafting, small verify).
+// x' (M rows x K, bf16, formed from the fp32 residual when normalizing) is
+// staged once per work-group in LDS; each wave then streams its weight rows
+// from HBM through a register ring DEPTH stages deep.  LDS reads are counted
+// apart from vector-memory loads, so reading x' never waits on weights still
+// in flight, and a normalizing prologue does not serialize the weight stream.
+// A stage is 128 k of one 16-row subtile per lane group: bf16 4 x 16 B per
+// lane, W8 2 x 16 B, W4 1 x 16 B (one quantization group).  For the quantized
+// formats the per-group row sums of x' (zero-point terms) are computed once in
+// the prologue.  Waves split K (KS) within the work-group and reduce in LDS in
+// a fixed order; the first DEPTH-1 weight stages are issued before the x'
+// fill so that the two overlap.
+// ----------------------------------------------------------------------------
+template <int FMT> struct StageW { static constexpr int NW = (FMT == FMT_BF16) ? 4 : (FMT == FMT_W8 ? 2 : 1); };
+
+// LDS of k_skinny: x' [M][K+8] bf16; quantized formats add per-chunk row sums
+// of x' [K/128][16] and the work-group's scale/zero pairs [R][K/128] (float2);
+// then the KS reduction area.
+struct SkinnyLds {
+  size_t xsum, sz, red, total;
+};
+static inline SkinnyLds skinny_lds(int fmt, int M, int K, int NR, int KS) {
+  SkinnyLds L;
+  const size_t nch = (size_t)K / 128;
+  const size_t R = (size_t)16 * NR * (8 / KS);
+  size_t b = (size_t)M * ((size_t)K + 8) * 2;
+  b = (b + 15) & ~(size_t)15;
+  L.xsum = b;
+  if (fmt != FMT_BF16) b += nch * 16 * 4;
+  L.sz = b;
+  if (fmt == FMT_W4) b += R * nch * 8;
+  // the KS reduction runs after every wave is done with x' and reuses its space
+  L.red = 0;
+  const size_t red = KS > 1 ? (size_t)8 * NR * 64 * 16 : 0;
+  L.total = std::max(b, red);
+  return L;
+}
+
+template <int FMT, int NR, int KS, int DEPTH>
+__global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+  constexpr int RG = 8 / KS;
+  constexpr int R = 16 * NR * RG;
+  constexpr int NW = StageW<FMT>::NW;
+  const int M = a.M, N = a.W.N, K = a.W.K;
+  const int ldsx = K + 8;
+  const int nchunks = K >> 7;
+  char* lds = reinterpret_cast<char*>(xs);
+  float* xsum = reinterpret_cast<float*>(lds + L.xsum);   // [nchunks][16] row sums of x' per chunk
+  float2* szl = reinterpret_cast<float2*>(lds + L.sz);    // [R][nchunks] (scale, 128 + zero), W4
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + L.red);
+
+  const int b = blockIdx.x, nwg = gridDim.x;
+  const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
+  const int nt = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave / KS, ks = wave % KS;
+  const int kb = lane >> 4, l16 = lane & 15;
+  const long G = K >> 7;
+  const void* __restrict__ wv = a.W.w;
+  const void* __restrict__ sv = a.W.scale;
+  const void* __restrict__ zv = a.W.zero;
+
+  if (b == 0 && a.ssq_zero)
+    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+
+  int n_lane[NR];
+  long nrow[NR];
+#pragma unroll
+  for (int ni = 0; ni < NR; ++ni) {
+    const int s = (nt * RG + rg) * NR + ni;
+    const bool in = 16 * s + l16 < N;
+    n_lane[ni] = in ? phys_row(a, s, l16) : N;
+    nrow[ni] = in ? n_lane[ni] : N - 1;
+  }
+
+  // this wave's stages: chunks ks, ks + KS, ...
+  const int n_it = (nchunks - ks + KS - 1) / KS;
+  uint4 wreg[DEPTH][NR][NW];
+
+  auto issue = [&](int it, int slot) {
+    const long c = ks + (long)KS * it;
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) {
+      if constexpr (FMT == FMT_BF16) {
+        const uint16_t* p = (const uint16_t*)wv + nrow[ni] * K + c * 128 + 8 * kb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wreg[slot][ni][i] = *(const uint4*)(p + 32 * i);
+      } else if constexpr (FMT == FMT_W8) {
+        const int8_t* p = (const int8_t*)wv + nrow[ni] * K + c * 128 + 16 * kb;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) wreg[slot][ni][h] = *(const uint4*)(p + 64 * h);
+      } else {
+        const uint8_t* p = (const uint8_t*)wv + (nrow[ni] * K + c * 128) / 2 + 16 * kb;
+        wreg[slot][ni][0] = *(const uint4*)p;
+      }
+    }
+  };
+
+  f32x4_t acc[NR];
+#pragma unroll
+  for (int ni = 0; ni < NR; ++ni) acc[ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int it, int slot) {
+    const int c = ks + KS * it;
+    const bool xrow_ok = l16 < M;
+    bf16x8_t xa[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 v = uint4{0u, 0u, 0u, 0u};
+      if (xrow_ok) v = *(const uint4*)(xs + l16 * ldsx + c * 128 + kcol<FMT>(i, kb));
+      xa[i] = __builtin_bit_cast(bf16x8_t, v);
+    }
+    f32x4_t accg[NR];
+    if constexpr (FMT != FMT_BF16) {
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni) accg[ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni) {
+        bf16x8_t bw;
+        if constexpr (FMT == FMT_BF16) {
+          bw = __builtin_bit_cast(bf16x8_t, wreg[slot][ni][i]);
+          acc[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], bw, acc[ni], 0, 0, 0);
+        } else {
+          if constexpr (FMT == FMT_W8) {
+            const uint4 v = wreg[slot][ni][i >> 1];
+            bw = (i & 1) ? w8_to_bf16(v.z, v.w) : w8_to_bf16(v.x, v.y);
+          } else {
+            const uint4 v = wreg[slot][ni][0];
+            const uint32_t word = (i == 0) ? v.x : (i == 1) ? v.y : (i == 2) ? v.z : v.w;
+            bw = w4_to_bf16(word);
+          }
+          accg[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[i], bw, accg[ni], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (FMT != FMT_BF16) {
+      const float4 xs4 = *reinterpret_cast<const float4*>(xsum + c * 16 + 4 * kb);  // rows 4kb .. 4kb+3
+      const float xsm[4] = {xs4.x, xs4.y, xs4.z, xs4.w};
+      float2 sz[NR];
+      if constexpr (FMT == FMT_W4) {
+#pragma unroll
+        for (int ni = 0; ni < NR; ++ni) sz[ni] = szl[(rg * NR + ni) * 16 * nchunks + l16 * nchunks + c];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int ni = 0; ni < NR; ++ni) {
+          if constexpr (FMT == FMT_W8)
+            acc[ni][r] += accg[ni][r] - 128.0f * xsm[r];
+          else
+            acc[ni][r] = fmaf(sz[ni].x, fmaf(-sz[ni].y, xsm[r], accg[ni][r]), acc[ni][r]);
+        }
+      }
+    }
+  };
+
+  // weights for the first stages go out before the x' fill
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d)
+    if (d < n_it) issue(d, d);
+
+  {
+    const int K8 = K >> 3;
+    for (int e = tid; e < M * K8; e += 512) {
+      const int m = e / K8, k8 = e - m * K8;
+      const long hrow = a.xrow ? a.xrow[m] : m;
+      uint4 v;
+      if (a.xnorm) v = load_x8(a, hrow, rstd_of(a, hrow), (long)k8 * 8);
+      else v = *(const uint4*)((const uint16_t*)a.x + hrow * a.ldx + (long)k8 * 8);
+      *(uint4*)(xs + m * ldsx + k8 * 8) = v;
+    }
+    if constexpr (FMT == FMT_W4) {
+      // this work-group's rows: logical subtile (nt*RG + rg')*NR + ni, lane row l16
+      const int rows = 16 * NR * RG;
+      for (int e = tid; e < rows * nchunks; e += 512) {
+        const int rr = e / nchunks, c = e - rr * nchunks;
+        const int s2 = nt * RG * NR + (rr >> 4);
+        const int l = rr & 15;
+        const long n = (16 * s2 + l < N) ? phys_row(a, s2, l) : N - 1;
+        szl[e] = make_float2(bf2f(((const uint16_t*)sv)[n * G + c]), 128.0f + (float)((const uint8_t*)zv)[n * G + c]);
+      }
+    }
+    if constexpr (FMT != FMT_BF16) {
+      __syncthreads();
+      for (int e = tid; e < 16 * nchunks; e += 512) {
+        const int c = e >> 4, m = e & 15;
+        float sm = 0.f;
+        if (m < M) {
+          const uint4* p = (const uint4*)(xs + m * ldsx + c * 128);
+#pragma unroll 4
+          for (int j = 0; j < 16; ++j) {
+            const uint4 v = p[j];
+            sm += bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) + bf_lo(v.w) + bf_hi(v.w);
+          }
+        }
+        xsum[e] = sm;
+      }
+    }
+    __syncthreads();
+  }
+
+  for (int i0 = 0; i0 < n_it; i0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int it = i0 + d;
+      if (it + DEPTH - 1 < n_it) issue(it + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+      if (it < n_it) compute(it, d);
+    }
+  }
+
+  if constexpr (FMT == FMT_W8) {
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) {
+      const float sc = ((const float*)sv)[nrow[ni]];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[ni][r] *= sc;
+    }
+  }
+
+  if constexpr (KS > 1) {
+    __syncthreads();  // the reduction area overlays x'
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) red[(wave * NR + ni) * 64 + lane] = acc[ni];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) {
+      f32x4_t v = red[(wave * NR + ni) * 64 + lane];
+#pragma unroll
+      for (int s2 = 1; s2 < KS; ++s2) {
+        const f32x4_t o = red[((wave + s2) * NR + ni) * 64 + lane];
+        v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
+      }
+      acc[ni] = v;
+    }
+  }
+
+  const bool want_ssq = a.epi == EPI_RESID && a.ssq_acc;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * kb + r;
+    const bool mok = m < M;
+    float sq = 0.f;
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) {
+      const float v = acc[ni][r];
+      const float partner = __shfl_xor(v, 8, 64);
+      const bool ok = mok && n_lane[ni] < N;
+      epilogue(a, m, n_lane[ni], v, partner, ok, l16);
+      if (want_ssq && ok) {
+        const float hn = ((const float*)a.y)[(long)m * a.ldy + n_lane[ni]];
+        sq = fmaf(hn, hn, sq);
+      }
+    }
+    if (want_ssq) ssq_add(a, m, sq, l16 == 0, mok);
+  }
+}
+
+template <int FMT, int NR, int KS, int DEPTH>
+static int run_skinny(const LinArgs& a, hipStream_t st, LinearInfo* info) {
+  constexpr int R = 16 * NR * (8 / KS);
+  const SkinnyLds L = skinny_lds(FMT, a.M, a.W.K, NR, KS);
+  const size_t lds = L.total;
+  if (a.M > 16 || lds > kSkinnyLdsMax) return -1;
+  const long nwg = (a.W.N + R - 1) / R;
+  if (info) {
+    snprintf(info->name, sizeof info->name, "er::k_skinny<%d, %d, %d, %d>", FMT, NR, KS, DEPTH);
+    info->nsplit = KS;
+  }
+  hipLaunchKernelGGL((k_skinny<FMT, NR, KS, DEPTH>), dim3((unsigned)nwg), dim3(512), lds, st, a, L);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
+// Explicit streaming variant: code = 2000 + 100*NR + 10*KS + DEPTH.
+template <int FMT>
+static int run_skinny_variant(int code, const LinArgs& a, hipStream_t st, LinearInfo* info) {
+  const int nr = (code / 100) % 10, ks = (code / 10) % 10, dp = code % 10;
+#define ER_S(NR_, KS_, D_) \
+  if (nr == NR_ && ks == KS_ && dp == D_) return run_skinny<FMT, NR_, KS_, D_>(a, st, info);
+#define ER_SK(NR_, D_) ER_S(NR_, 2, D_) ER_S(NR_, 4, D_) ER_S(NR_, 8, D_)
+  ER_SK(1, 2) ER_SK(1, 3) ER_SK(1, 4) ER_SK(2, 2) ER_SK(2, 3) ER_SK(2, 4)
+  if constexpr (FMT != FMT_BF16) { ER_SK(4, 2) ER_SK(4, 3) ER_SK(4, 4) ER_SK(1, 6) ER_SK(2, 6) ER_SK(1, 8) }
+#undef ER_SK
+#undef ER_S
+  return -1;
+}
+
+// ----------------------------------------------------------------------------
+// Weight-streaming GEMM for 16 < M <= 256 (bf16 weights): large-batch decode
+// and verify, where the layer is still bound by reading W once.  Each wave
+// streams its own 16*NR weight rows through a register ring (DEPTH stages of
+// 128 k); the M x (KS*128) window of x for the current step is staged in LDS
+// and shared by every wave (double-buffered, one barrier per step).  The next
+// window's loads are issued ahead of the weights so that writing it to LDS
+// never waits on weight loads still in flight.  KS waves split each step's K
+// range and reduce in LDS; nsplit > 1 splits K over work-groups, with the
+// partial tiles summed in a fixed order by k_splitk_reduce.
+// ----------------------------------------------------------------------------
+template <int MI, int NR, int KS, int DEPTH>
+__global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ part, int nsplit, int cps) {
+  constexpr int RG = 8 / KS;
+  constexpr int MT = 16 * MI;
+  constexpr int WK = KS * 128;           // k per step
+  constexpr int LDX = WK + 8;            // LDS row stride (bf16)
+  constexpr int XV = MT * WK / 8 / 512;  // uint4 of the x window per thread
+  static_assert(MT * WK % (8 * 512) == 0, "x window must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t xw[2][MT * LDX];
+
+  const int b = blockIdx.x, nwg = gridDim.x;
+  const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
+  const int L = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+  const int sp = L % nsplit, nt = L / nsplit;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rg = wave / KS, ks = wave % KS;
+  const int kb = lane >> 4, l16 = lane & 15;
+  const int M = a.M, N = a.W.N, K = a.W.K;
+  const int nchunks = K >> 7;
+  const int c0 = sp * cps, c1 = min(nchunks, c0 + cps);
+  const int T = (c1 - c0 + KS - 1) / KS;  // steps
+  const uint16_t* __restrict__ W = (const uint16_t*)a.W.w;
+  const uint16_t* __restrict__ X = (const uint16_t*)a.x;
+
+  if (b == 0 && a.ssq_zero && nsplit == 1)
+    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+
+  int n_lane[NR];
+  long nrow[NR];
+#pragma unroll
+  for (int ni = 0; ni < NR; ++ni) {
+    const int s = (nt * RG + rg) * NR + ni;
+    const bool in = 16 * s + l16 < N;
+    n_lane[ni] = in ? phys_row(a, s, l16) : N;
+    nrow[ni] = in ? n_lane[ni] : N - 1;
+  }
+
+  uint4 wreg[DEPTH][NR][4];
+  uint4 xr[XV];
+  auto issue_w = [&](int t, int slot) {
+    const long c = c0 + (long)t * KS + ks;
+    if (c >= c1) return;
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) {
+      const uint16_t* p = W + nrow[ni] * K + c * 128 + 8 * kb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wreg[slot][ni][i] = *(const uint4*)(p + 32 * i);
+    }
+  };
+  auto load_x = [&](int t) {
+    const long k0 = (long)(c0 + t * KS) * 128;
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int e = tid + 512 * v;
+      const int m = e / (WK / 8), k8 = e - m * (WK / 8);
+      uint4 val = uint4{0u, 0u, 0u, 0u};
+      if (m < M && k0 + k8 * 8 < (long)c1 * 128) val = *(const uint4*)(X + (long)m * a.ldx + k0 + k8 * 8);
+      xr[v] = val;
+    }
+  };
+  auto store_x = [&](int buf) {
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int e = tid + 512 * v;
+      const int m = e / (WK / 8), k8 = e - m * (WK / 8);
+      *(uint4*)(&xw[buf][m * LDX + k8 * 8]) = xr[v];
+    }
+  };
+
+  f32x4_t acc[MI][NR];
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int t, int slot, int buf) {
+    const int c = c0 + t * KS + ks;
+    if (c >= c1) return;
+    const uint16_t* xb = &xw[buf][ks * 128 + 8 * kb];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi) {
+        const bf16x8_t xa = *(const bf16x8_t*)(xb + (mi * 16 + l16) * LDX + 32 * i);
+#pragma unroll
+        for (int ni = 0; ni < NR; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8_t, wreg[slot][ni][i]),
+                                                                acc[mi][ni], 0, 0, 0);
+      }
+    }
+  };
+
+  // prologue: x window 0 first, then the first weight stages
+  load_x(0);
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d)
+    if (d < T) issue_w(d, d);
+  store_x(0);
+  __syncthreads();
+
+  for (int t0 = 0; t0 < T; t0 += 2 * DEPTH) {
+#pragma unroll
+    for (int d = 0; d < 2 * DEPTH; ++d) {
+      const int t = t0 + d;
+      if (t < T) {
+        if (t + 1 < T) load_x(t + 1);
+        if (t + DEPTH - 1 < T) issue_w(t + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+        compute(t, d % DEPTH, d & 1);
+        if (t + 1 < T) store_x((d + 1) & 1);
+        __syncthreads();
+      }
+    }
+  }
+
+  // reduce the KS partial tiles (fixed order) through the x window's LDS
+  if constexpr (KS > 1) {
+    f32x4_t* red = reinterpret_cast<f32x4_t*>(&xw[0][0]);
+    static_assert(sizeof(xw) >= sizeof(f32x4_t) * 8 * MI * NR * 64, "reduction area does not fit");
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni) red[((wave * MI + mi) * NR + ni) * 64 + lane] = acc[mi][ni];
+    __syncthreads();
+    if (ks != 0) return;
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni) {
+        f32x4_t v = red[((wave * MI + mi) * NR + ni) * 64 + lane];
+#pragma unroll
+        for (int s2 = 1; s2 < KS; ++s2) {
+          const f32x4_t o = red[(((wave + s2) * MI + mi) * NR + ni) * 64 + lane];
+          v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
+        }
+        acc[mi][ni] = v;
+      }
+  }
+
+  const bool want_ssq = a.epi == EPI_RESID && a.ssq_acc && nsplit == 1;
+  if constexpr (MI * NR > 8) {
+    // Large tiles: stage the (MT x R) result through LDS and walk it row-wise,
+    // so that the fully unrolled register loop stays small.
+    static_assert(KS == 1 && 16 * NR * RG == 128, "LDS epilogue expects 128-column tiles");
+    constexpr int R = 128, CLD = R + 4;
+    static_assert(sizeof(xw) >= sizeof(float) * MT * CLD, "result tile does not fit");
+    float* Cs = reinterpret_cast<float*>(&xw[0][0]);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Cs[(mi * 16 + 4 * kb + r) * CLD + (rg * NR + ni) * 16 + l16] = acc[mi][ni][r];
+    __syncthreads();
+    for (int e = tid; e < MT * R; e += 512) {
+      const int row = e >> 7, col = e & 127;  // a wave covers 64 columns of one row
+      const int m = row;
+      const int sidx = (nt * RG) * NR + (col >> 4);
+      const bool mok = m < M, nok = 16 * sidx + (col & 15) < N;
+      const int n = nok ? phys_row(a, sidx, col & 15) : N;
+      const float v = Cs[row * CLD + col];
+      float sq = 0.f;
+      if (nsplit > 1) {
+        if (mok && nok) part[((long)sp * M + m) * N + n] = v;
+      } else {
+        epilogue(a, m, n, v, Cs[row * CLD + (col ^ 8)], mok && nok, col & 15);
+        if (want_ssq && mok && nok) {
+          const float hn = ((const float*)a.y)[(long)m * a.ldy + n];
+          sq = hn * hn;
+        }
+      }
+      if (want_ssq) {
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        ssq_add(a, m, sq, lane == 0, mok);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mi * 16 + 4 * kb + r;
+      const bool mok = m < M;
+      float sq = 0.f;
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni) {
+        const float v = acc[mi][ni][r];
+        const bool ok = mok && n_lane[ni] < N;
+        if (nsplit > 1) {
+          if (ok) part[((long)sp * M + m) * N + n_lane[ni]] = v;
+          continue;
+        }
+        const float partner = __shfl_xor(v, 8, 64);
+        epilogue(a, m, n_lane[ni], v, partner, ok, l16);
+        if (want_ssq && ok) {
+          const float hn = ((const float*)a.y)[(long)m * a.ldy + n_lane[ni]];
+          sq = fmaf(hn, hn, sq);
+        }
+      }
+      if (want_ssq) ssq_add(a, m, sq, l16 == 0, mok);
+    }
+}
+
+template <int MI, int NR, int KS, int DEPTH>
+static int run_wgemm(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStream_t st, LinearInfo* info) {
+  constexpr int R = 16 * NR * (8 / KS);
+  if (a.M > 16 * MI || a.W.fmt != FMT_BF16 || a.xnorm) return -1;
+  const int nchunks = a.W.K / 128;
+  const long ntiles = (a.W.N + R - 1) / R;
+  int nsplit = 1;
+  // split K over work-groups while the grid is short of want_wgs and every
+  // split keeps at least 4 steps
+  while (ntiles * nsplit * 2 <= want_wgs && nchunks / (nsplit * 2 * KS) >= 4 &&
+         (size_t)(nsplit * 2) * a.M * a.W.N <= ws.partial_floats && ws.partial)
+    nsplit *= 2;
+  const int cps = (nchunks + nsplit - 1) / nsplit;
+  nsplit = (nchunks + cps - 1) / cps;
+  if (info) {
+    snprintf(info->name, sizeof info->name, "er::k_wgemm<%d, %d, %d, %d>", MI, NR, KS, DEPTH);
+    info->nsplit = nsplit;
+  }
+  hipLaunchKernelGGL((k_wgemm<MI, NR, KS, DEPTH>), dim3((unsigned)(ntiles * nsplit)), dim3(512), 0, st, a, ws.partial,
+                     nsplit, cps);
+  if (hipGetLastError() != hipSuccess) return -3;
+  if (nsplit > 1) {
+    const long waves = (long)a.M * ((a.W.N + 63) / 64);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, ws.partial, nsplit);
+    if (hipGetLastError() != hipSuccess) return -3;
+  }
+  return 0;
+}
+
+// Explicit weight-streaming variant: code = 3000 + 100*MI(1 digit: 2,4,8; 0 = 16) + 10*KS + 10000*NR... kept
+// simple: code = 30000 + 1000*NR + 100*KS + 10*DEPTH + MI index (0: MI 2, 1: 4, 2: 8, 3: 16);
+// want_wgs comes from the caller.
+static int run_wgemm_variant(int code, const LinArgs& a, const LinearWs& ws, hipStream_t st, LinearInfo* info) {
+  const int nr = (code / 1000) % 10, ks = (code / 100) % 10, dp = (code / 10) % 10, mix = code % 10;
+  const int want = 512;
+#define ER_W(MI_, NR_, KS_, D_, IX_) \
+  if (mix == IX_ && nr == NR_ && ks == KS_ && dp == D_) return run_wgemm<MI_, NR_, KS_, D_>(a, ws, want, st, info);
+  ER_W(2, 1, 4, 2, 0) ER_W(2, 1, 4, 3, 0) ER_W(2, 2, 4, 2, 0) ER_W(2, 1, 2, 3, 0)
+  ER_W(4, 1, 2, 2, 1) ER_W(4, 1, 2, 3, 1) ER_W(4, 2, 2, 2, 1) ER_W(4, 1, 1, 3, 1)
+  ER_W(8, 1, 1, 2, 2) ER_W(8, 1, 1, 3, 2)
+  ER_W(16, 1, 1, 2, 3) ER_W(16, 1, 1, 3, 3)
+#undef ER_W
+  return -1;
+}
+
+// ----------------------------------------------------------------------------
+// Deep-pipelined tiled GEMM for bf16 weights, M > 16: BM x 128 output tile
+// per work-group of 8 waves (WM x WN waves, each (BM/WM) x (128/WN)), K steps
+// of 64.  Both operands go global -> register ring (DEPTH steps ahead) ->
+// LDS (double buffer) -> MFMA.  x and W of a step are issued together, so the
+// wait before a step's LDS store never covers loads of later steps: DEPTH - 2
+// steps of latency stay hidden.  Split-K partials go through
+// k_splitk_reduce, as for k_gemm_bf16.
+// ----------------------------------------------------------------------------
+template <int BM, int WM, int DEPTH>
+__global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ part, int nsplit, int sps, int mtiles) {
+  constexpr int BN = 128, BK = 64, LDA = BK + 8;
+  constexpr int WN = 8 / WM;
+  constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
+  constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 fragments per wave
+  constexpr int XV = BM * BK / 8 / 512;       // uint4 of x per thread per step
+  constexpr int WV = BN * BK / 8 / 512;       // uint4 of W per thread per step (2)
+  static_assert(XV >= 1 && WV == 2, "tile does not split over 512 threads");
+  // one LDS array, carved explicitly: the epilogue overlays its C tile on the
+  // operand buffers, which needs their order and adjacency to be fixed
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BM * LDA + 2 * BN * LDA];
+  uint16_t (*As)[BM * LDA] = reinterpret_cast<uint16_t (*)[BM * LDA]>(smem);
+  uint16_t (*Bs)[BN * LDA] = reinterpret_cast<uint16_t (*)[BN * LDA]>(smem + 2 * BM * LDA);
+
+  const int b = blockIdx.x, nwg = gridDim.x;
+  const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
+  const int L = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
+  const int mt = L % mtiles;
+  const int t2 = L / mtiles;
+  const int sp = t2 % nsplit;
+  const int nt = t2 / nsplit;
+  const int M = a.M, N = a.W.N, K = a.W.K;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kb = lane >> 4, l16 = lane & 15;
+  const int wm = wave / WN, wn = wave % WN;
+  const int nsteps = K / BK;
+  const int s0 = sp * sps;
+  const int s1 = min(nsteps, s0 + sps);
+  const int T = s1 - s0;
+  const uint16_t* __restrict__ W = (const uint16_t*)a.W.w;
+  const uint16_t* __restrict__ X = (const uint16_t*)a.x;
+
+  if (b == 0 && a.ssq_zero && nsplit == 1)
+    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+
+  // per-thread load slots: row = e / 8, 16-byte column c8 = e % 8
+  long wsrc[WV];
+  bool wok[WV];
+#pragma unroll
+  for (int v = 0; v < WV; ++v) {
+    const int e = tid + 512 * v, row = e >> 3;
+    wok[v] = n0 + row < N;
+    wsrc[v] = wok[v] ? (long)phys_row(a, (n0 >> 4) + (row >> 4), row & 15) * K + (e & 7) * 8 : 0;
+  }
+  long xsrc[XV];
+  bool xok[XV];
+#pragma unroll
+  for (int v = 0; v < XV; ++v) {
+    const int e = tid + 512 * v, row = e >> 3;
+    const int m = m0 + row;
+    xok[v] = m < M;
+    xsrc[v] = xok[v] ? (long)(a.xrow ? a.xrow[m] : m) * a.ldx + (e & 7) * 8 : 0;
+  }
+
+  uint4 wr[DEPTH][WV], xr[DEPTH][XV];
+  auto issue = [&](int t, int slot) {
+    const long k0 = (long)(s0 + t) * BK;
+#pragma unroll
+    for (int v = 0; v < XV; ++v) xr[slot][v] = xok[v] ? *(const uint4*)(X + xsrc[v] + k0) : uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int v = 0; v < WV; ++v) wr[slot][v] = wok[v] ? *(const uint4*)(W + wsrc[v] + k0) : uint4{0u, 0u, 0u, 0u};
+  };
+  auto stash = [&](int slot, int buf) {
+#pragma unroll
+    for (int v = 0; v < XV; ++v) {
+      const int e = tid + 512 * v;
+      *(uint4*)(&As[buf][(e >> 3) * LDA + (e & 7) * 8]) = xr[slot][v];
+    }
+#pragma unroll
+    for (int v = 0; v < WV; ++v) {
+      const int e = tid + 512 * v;
+      *(uint4*)(&Bs[buf][(e >> 3) * LDA + (e & 7) * 8]) = wr[slot][v];
+    }
+  };
+
+  f32x4_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t af[FM], bfr[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = *(const bf16x8_t*)(&As[buf][(TM * wm + 16 * i + l16) * LDA + 32 * kk + 8 * kb]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = *(const bf16x8_t*)(&Bs[buf][(TN * wn + 16 * j + l16) * LDA + 32 * kk + 8 * kb]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  if (T > 0) {
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+      if (d < T) issue(d, d);
+    stash(0, 0);
+    __syncthreads();
+    for (int t0 = 0; t0 < T; t0 += 2 * DEPTH) {
+#pragma unroll
+      for (int d = 0; d < 2 * DEPTH; ++d) {
+        const int t = t0 + d;
+        if (t < T) {
+          if (t + DEPTH - 1 < T) issue(t + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+          mma(d & 1);
+          if (t + 1 < T) stash((d + 1) % DEPTH, (d + 1) & 1);
+          __syncthreads();
+        }
+      }
+    }
+  }
+
+  // epilogue through LDS (overlaying the operand buffers): row-wise walk,
+  // pair partners at column ^ 8, one sum-of-squares partial per (row, 64 cols)
+  constexpr int CLD = BN + 4;
+  // rows per pass so that the C tile fits in the operand buffers
+  constexpr int NPASS = (sizeof(float) * BM * CLD + sizeof(smem) - 1) / sizeof(smem);
+  constexpr int RP = BM / NPASS;
+  static_assert(BM % NPASS == 0 && RP % TM == 0, "epilogue passes must hold whole wave tiles");
+  static_assert(sizeof(float) * RP * CLD <= sizeof(smem), "C tile pass does not fit");
+  float* Cs = reinterpret_cast<float*>(smem);
+  const bool want_ssq = a.epi == EPI_RESID && a.ssq_acc && nsplit == 1;
+#pragma unroll
+  for (int pass = 0; pass < NPASS; ++pass) {
+    if (pass > 0) __syncthreads();
+    if ((TM * wm) / RP == pass) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Cs[(TM * wm - pass * RP + 16 * i + 4 * kb + r) * CLD + TN * wn + 16 * j + l16] = acc[i][j][r];
+    }
+    __syncthreads();
+    for (int e = tid; e < RP * BN; e += 512) {
+      const int row = e >> 7, col = e & 127;
+      const int m = m0 + pass * RP + row, nl = n0 + col;
+      const bool mok = m < M, nok = nl < N;
+      const int n = nok ? phys_row(a, nl >> 4, nl & 15) : N;
+      const float v = Cs[row * CLD + col];
+      float sq = 0.f;
+      if (nsplit > 1) {
+        if (mok && nok) part[((long)sp * M + m) * N + n] = v;
+      } else {
+        epilogue(a, m, n, v, Cs[row * CLD + (col ^ 8)], mok && nok, nl & 15);
+        if (want_ssq && mok && nok) {
+          const float hn = ((const float*)a.y)[(long)m * a.ldy + n];
+          sq = hn * hn;
+        }
+      }
+      if (want_ssq) {
+        sq += __shfl_xor(sq, 16, 64);
+        sq += __shfl_xor(sq, 32, 64);
+        ssq_add(a, m, sq, lane == 0, mok);
+      }
+    }
+  }
+}
+
+template <int BM, int WM, int DEPTH>
+static int run_gemm2(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStream_t st, LinearInfo* info) {
+  if (a.W.fmt != FMT_BF16 || a.xnorm || a.W.K % 64) return -1;
+  const int mtiles = (a.M + BM - 1) / BM;
+  const long ntiles = (a.W.N + 127) / 128;
+  const int nsteps = a.W.K / 64;
+  const long base = (long)mtiles * ntiles;
+  int nsplit = 1;
+  while (base * nsplit * 2 <= want_wgs && nsteps / (nsplit * 2) >= 8 &&
+         (size_t)(nsplit * 2) * a.M * a.W.N <= ws.partial_floats && ws.partial)
+    nsplit *= 2;
+  const int sps = (nsteps + nsplit - 1) / nsplit;
+  nsplit = (nsteps + sps - 1) / sps;
+  if (info) {
+    snprintf(info->name, sizeof info->name, "er::k_gemm2<%d, %d, %d>", BM, WM, DEPTH);
+    info->nsplit = nsplit;
+  }
+  hipLaunchKernelGGL((k_gemm2<BM, WM, DEPTH>), dim3((unsigned)(base * nsplit)), dim3(512), 0, st, a, ws.partial,
+                     nsplit, sps, mtiles);
+  if (hipGetLastError() != hipSuccess) return -3;
+  if (nsplit > 1) {
+    const long waves = (long)a.M * ((a.W.N + 63) / 64);
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a, ws.partial, nsplit);
+    if (hipGetLastError() != hipSuccess) return -3;
+  }
+  return 0;
+}
+
+// Explicit deep-pipelined GEMM variant: code = 40000 + 1000*ix(BM: 0=32,1=64,2=128,3=256) + 10*want/64 ... kept as
+// code = 40000 + 100*ix + 10*DEPTH + (want_wgs / 256)
+static int run_gemm2_variant(int code, const LinArgs& a, const LinearWs& ws, hipStream_t st, LinearInfo* info) {
+  const int ix = (code / 100) % 10, dp = (code / 10) % 10, want = 256 * (code % 10);
+#define ER_G(BM_, WM_, IX_, D_) \
+  if (ix == IX_ && dp == D_) return run_gemm2<BM_, WM_, D_>(a, ws, want, st, info);
+  ER_G(64, 1, 1, 4) ER_G(64, 1, 1, 6) ER_G(128, 2, 2, 3) ER_G(128, 2, 2, 4)
+  ER_G(128, 2, 2, 6) ER_G(256, 4, 3, 3) ER_G(256, 4, 3, 4)
+#undef ER_G
+  return -1;
+}
+
+// ----------------------------------------------------------------------------
 template <int FMT, int MT, int NR, int KS>
 static int run_mfma(const LinArgs& a, hipStream_t st, LinearInfo* info) {
   constexpr int R = 16 * NR * (8 / KS);
@@ -698,6 +1477,101 @@ static int dispatch_mfma(const LinArgs& a, hipStream_t st, LinearInfo* info) {
   return run_mfma<FMT, 32, 1, 8>(a, st, info);
 }
 
+// Automatic choice among the streaming variants, from a sweep of the Qwen2.5-7B
+// projections on MI355X with weights rotating through more than the 256 MB
+// last-level cache (M = 1 and 4): K split over all 8 waves for narrow and
+// wide outputs, over 4 waves with 2-deep rings in between; W4 wants deeper
+// rings (its stages are 16 bytes per lane).
+template <int FMT>
+static int dispatch_skinny(const LinArgs& a, hipStream_t st, LinearInfo* info) {
+  const int N = a.W.N, K = a.W.K;
+  if constexpr (FMT == FMT_BF16) {
+    if (N >= 16384) return a.M <= 2 ? run_skinny<FMT, 1, 8, 3>(a, st, info) : run_skinny<FMT, 1, 8, 2>(a, st, info);
+    if (N >= 4096) return run_skinny<FMT, 1, 4, 2>(a, st, info);
+    return run_skinny<FMT, 1, 8, 2>(a, st, info);
+  } else {
+    if (K >= 8192) return run_skinny<FMT, 1, 8, 6>(a, st, info);
+    if (N >= 8192) return a.M <= 2 ? run_skinny<FMT, 1, 2, 4>(a, st, info) : run_skinny<FMT, 1, 2, 3>(a, st, info);
+    return run_skinny<FMT, 1, 8, 3>(a, st, info);
+  }
+}
+
+// Automatic kernel choice (bf16 weights by M; the quantized drafter formats
+// use the streaming kernel while x' fits in LDS).  Sizes from sweeps of the
+// Qwen2.5-7B projections on MI355X with weights rotating through more than the
+// 256 MB last-level cache.
+enum Plan { P_STREAM, P_SKINNY_OLD, P_WGEMM, P_GEMM2, P_GEMM };
+
+static Plan plan_of(const LinArgs& a) {
+  const int M = a.M, N = a.W.N, K = a.W.K;
+  const size_t lds = skinny_lds(a.W.fmt, M, K, 1, 8).total;
+  const bool stream_fits = M <= 16 && lds <= kSkinnyLdsMax;
+  if (a.W.fmt != FMT_BF16) {
+    if (!stream_fits) return P_SKINNY_OLD;
+    if (M <= 8 || N >= 65536 || (N >= 16384 && M <= 12)) return P_STREAM;
+    return P_SKINNY_OLD;
+  }
+  if (M <= 8) return stream_fits ? P_STREAM : P_SKINNY_OLD;
+  if (M <= 16) return (stream_fits && N >= 4096) ? P_STREAM : P_SKINNY_OLD;
+  if (K % 64) return P_SKINNY_OLD;
+  if (M <= 32) return N < 4096 ? P_SKINNY_OLD : P_WGEMM;
+  if (M <= 64) return (N >= 16384 || K >= 8192) ? P_GEMM2 : P_WGEMM;
+  if (M <= 256) return P_GEMM2;
+  return P_GEMM;
+}
+
+template <int FMT>
+static int run_stream_auto(const LinArgs& a, hipStream_t st, LinearInfo* info) {
+  const int N = a.W.N, K = a.W.K, M = a.M;
+  if constexpr (FMT == FMT_BF16) {
+    if (M > 8) {
+      if (N >= 65536) return run_skinny<FMT, 2, 2, 3>(a, st, info);
+      if (N >= 16384) return run_skinny<FMT, 1, 2, 2>(a, st, info);
+      return run_skinny<FMT, 1, 4, 2>(a, st, info);
+    }
+    return dispatch_skinny<FMT>(a, st, info);
+  } else {
+    if (M > 8) {
+      if (N >= 65536) return run_skinny<FMT, 2, 2, 3>(a, st, info);
+      return run_skinny<FMT, 4, 2, 3>(a, st, info);
+    }
+    (void)N; (void)K;
+    return dispatch_skinny<FMT>(a, st, info);
+  }
+}
+
+static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st, LinearInfo* info) {
+  const int M = a.M, N = a.W.N, K = a.W.K;
+  switch (p) {
+    case P_STREAM:
+      switch (a.W.fmt) {
+        case FMT_BF16: return run_stream_auto<FMT_BF16>(a, st, info);
+        case FMT_W8: return run_stream_auto<FMT_W8>(a, st, info);
+        case FMT_W4: return run_stream_auto<FMT_W4>(a, st, info);
+      }
+      return -1;
+    case P_WGEMM:
+      if (M <= 32) return (N >= 16384 || K >= 8192) ? run_wgemm<2, 1, 2, 3>(a, ws, 512, st, info)
+                                                   : run_wgemm<2, 1, 4, 3>(a, ws, 512, st, info);
+      return run_wgemm<4, 1, 1, 3>(a, ws, 512, st, info);
+    case P_GEMM2:
+      if (M <= 64) return run_gemm2<64, 1, 4>(a, ws, 512, st, info);
+      if (M <= 128) return N < 4096 ? run_gemm2<64, 1, 6>(a, ws, 512, st, info)
+                                    : run_gemm2<128, 2, 3>(a, ws, 512, st, info);
+      return K >= 8192 ? run_gemm2<256, 4, 3>(a, ws, 512, st, info) : run_gemm2<256, 4, 4>(a, ws, 512, st, info);
+    case P_GEMM:
+      return run_gemm(a, ws, st, info);
+    case P_SKINNY_OLD:
+      switch (a.W.fmt) {
+        case FMT_BF16: return dispatch_mfma<FMT_BF16>(a, st, info);
+        case FMT_W8: return dispatch_mfma<FMT_W8>(a, st, info);
+        case FMT_W4: return dispatch_mfma<FMT_W4>(a, st, info);
+      }
+      return -1;
+  }
+  return -1;
+}
+
 int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info) {
   if (a.M <= 0 || a.W.N <= 0) return 0;
   if (a.W.K % 128 != 0 || (!a.xnorm && a.ldx % 8 != 0) || (a.xnorm && a.ldx % 4 != 0)) return -1;
@@ -706,9 +1580,19 @@ int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStrea
     return -1;
   if (a.epi == EPI_SWIGLU && a.F % 8 != 0) return -1;
   const bool gemm_ok = a.W.fmt == FMT_BF16 && a.W.K % GB_K == 0 && ws.partial != nullptr;
-  if (path == 3 || (path == 0 && a.M > 32 && gemm_ok)) {
+  if (path == 3) {
     if (!gemm_ok) return -1;
     return run_gemm(a, ws, st, info);
+  }
+  if (path >= 40000) return run_gemm2_variant(path, a, ws, st, info);
+  if (path >= 30000) return run_wgemm_variant(path, a, ws, st, info);
+  if (path >= 2000) {
+    switch (a.W.fmt) {
+      case FMT_BF16: return run_skinny_variant<FMT_BF16>(path, a, st, info);
+      case FMT_W8: return run_skinny_variant<FMT_W8>(path, a, st, info);
+      case FMT_W4: return run_skinny_variant<FMT_W4>(path, a, st, info);
+    }
+    return -1;
   }
   if (path >= 1000) {
     switch (a.W.fmt) {
@@ -718,13 +1602,33 @@ int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStrea
     }
     return -1;
   }
-  // skinny path; larger M is processed in 32-row m-tiles
-  switch (a.W.fmt) {
-    case FMT_BF16: return dispatch_mfma<FMT_BF16>(a, st, info);
-    case FMT_W8: return dispatch_mfma<FMT_W8>(a, st, info);
-    case FMT_W4: return dispatch_mfma<FMT_W4>(a, st, info);
+  if (path == 2) {  // the register-fed skinny kernel, any M (32-row m-tiles)
+    switch (a.W.fmt) {
+      case FMT_BF16: return dispatch_mfma<FMT_BF16>(a, st, info);
+      case FMT_W8: return dispatch_mfma<FMT_W8>(a, st, info);
+      case FMT_W4: return dispatch_mfma<FMT_W4>(a, st, info);
+    }
+    return -1;
   }
-  return -1;
+  Plan p = plan_of(a);
+  if ((p == P_GEMM || p == P_GEMM2 || p == P_WGEMM) && !gemm_ok) p = P_SKINNY_OLD;
+  if (a.xnorm && p != P_STREAM) {
+    // these kernels read bf16 x: form x' = RMSNorm(h) * g once, in the workspace
+    if (ws.xn && (size_t)a.M * a.W.K <= ws.xn_elems) {
+      int r = launch_rmsnorm((const float*)a.x, a.M, a.W.K, a.gnorm, true, a.eps, ws.xn, a.xrow, st);
+      if (r) return r;
+      LinArgs b = a;
+      b.x = ws.xn;
+      b.ldx = a.W.K;
+      b.xnorm = 0;
+      b.xrow = nullptr;
+      b.ssq_in = nullptr;
+      return run_auto(b, ws, p, st, info);
+    }
+    if (p != P_SKINNY_OLD) p = (p == P_GEMM) ? P_GEMM : P_SKINNY_OLD;  // these two normalize on load themselves
+    if (p == P_GEMM) return run_gemm(a, ws, st, info);
+  }
+  return run_auto(a, ws, p, st, info);
 }
 
 template <int FMT, bool XBF>

@@ -69,6 +69,8 @@ struct LinearWs {
   size_t partial_floats;
   int* counters;      // zero-initialised tile counters
   int n_counters;
+  uint16_t* xn;       // bf16 x' for kernels that do not normalize on load (nullable)
+  size_t xn_elems;
 };
 
 // What a launch_linear call ran (for per-kernel timing): kernel name as the

@@ -17,6 +17,7 @@ struct OpWs {
   int* counters = nullptr;
   float* attn = nullptr;
   double* resid = nullptr;
+  uint16_t* xn = nullptr;
   int device = -1;
 };
 OpWs g_ws;
@@ -26,6 +27,7 @@ constexpr size_t kPartialFloats = (size_t)16 << 20;
 constexpr int kCounters = 65536;
 constexpr size_t kAttnFloats = (size_t)8 << 20;
 constexpr size_t kResidDoubles = (size_t)1 << 20;
+constexpr size_t kXnElems = (size_t)8 << 20;
 
 int ensure_ws() {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -37,6 +39,7 @@ int ensure_ws() {
   if (hipMemset(g_ws.counters, 0, kCounters * 4) != hipSuccess) return ER_EDEVICE;
   if (hipMalloc(&g_ws.attn, kAttnFloats * 4) != hipSuccess) return ER_ENOMEM;
   if (hipMalloc(&g_ws.resid, kResidDoubles * 8) != hipSuccess) return ER_ENOMEM;
+  if (hipMalloc(&g_ws.xn, kXnElems * 2) != hipSuccess) return ER_ENOMEM;
   g_ws.device = dev;
   return ER_OK;
 }
@@ -76,7 +79,7 @@ int er_op_linear(int x_dtype, const void* d_x, int ldx, int M, int fmt, const vo
   int r = ensure_ws();
   if (r) return r;
   LinearW W{fmt, d_w, d_scale, d_zero, N, K};
-  LinearWs ws{g_ws.partial, kPartialFloats, g_ws.counters, kCounters};
+  LinearWs ws{g_ws.partial, kPartialFloats, g_ws.counters, kCounters, g_ws.xn, kXnElems};
   return code(launch_linear(d_x, x_dtype == ER_BF16, ldx, M, W, d_y, ldy, EPI_F32, ws, path, (hipStream_t)stream));
 }
 
@@ -129,7 +132,7 @@ int er_op_linear_fused(int epi, const void* d_x, int ldx, int M, int xnorm, cons
     a.n_layers = qkv->n_layers;
   }
   if (epi == ER_EPI_SWIGLU) a.F = N / 2;
-  LinearWs ws{g_ws.partial, kPartialFloats, g_ws.counters, kCounters};
+  LinearWs ws{g_ws.partial, kPartialFloats, g_ws.counters, kCounters, g_ws.xn, kXnElems};
   return code(launch_linear_fused(a, ws, path, (hipStream_t)stream));
 }
 

@@ -80,8 +80,10 @@ def _bound(xs, wd):
     return np.abs(xs) @ np.abs(wd).T
 
 
-CASES = [  # (fmt, M, path): skinny M-tiles, the tiled GEMM and its split-K reduction
-    ("bf16", 1, 0), ("bf16", 13, 0), ("bf16", 29, 0), ("bf16", 45, 0), ("bf16", 20, 3),
+CASES = [  # (fmt, M, path): streaming and register-fed skinny kernels, the weight-streaming and
+    # deep-pipelined GEMMs (64/128/256-row tiles), the tiled GEMM and the split-K reductions
+    ("bf16", 1, 0), ("bf16", 13, 0), ("bf16", 29, 0), ("bf16", 45, 0), ("bf16", 20, 3), ("bf16", 100, 0),
+    ("bf16", 200, 0), ("bf16", 16, 2),
     ("w4", 1, 0), ("w4", 20, 0), ("w4", 45, 0), ("w8", 7, 0), ("w8", 33, 0),
 ]
 
@@ -163,11 +165,13 @@ def test_fused_norm_qkv_rope_kv_append(ops, fmt, M, path):
     g = torch.Generator().manual_seed(400 + M)
     hq, hkv, hd, K = 4, 2, 128, 512
     N = (hq + 2 * hkv) * hd
-    L, layer, nblk = 3, 1, 8
+    # enough 16-slot blocks that every row gets its own slot (plus spare blocks that must stay untouched)
+    L, layer, nblk = 3, 1, (M + 15) // 16 + 2
     h, gain, xrow, ssq, xs = _norm_input(M, K, g)
     (f, w, sc, zr), wd = _weights(fmt, N, K, g, ops)
     pos = torch.randint(0, 500, (M,), generator=g).numpy().astype(np.int32)
     slot = torch.randperm(nblk * 16, generator=g)[:M].numpy().astype(np.int64)
+    assert slot.shape == (M,) and pos.shape == (M,)
     max_pos = 512
     cos, sin = rope_cos_sin(np.arange(max_pos), hd, 1e6)
     cs = np.stack([cos, sin], axis=-1).astype(np.float32)

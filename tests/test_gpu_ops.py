@@ -142,6 +142,18 @@ def test_linear_bf16_paths(ops, fmt, M, path):
     assert r < 4e-6, r
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "w8", "w4"])
+@pytest.mark.parametrize("M", [1, 5, 16])
+@pytest.mark.parametrize("code", [2182, 2142, 2223, 2124, 2186, 2244])
+def test_linear_streaming_variants(ops, fmt, M, code):
+    # x' staged in LDS, weights through a register ring: K split 2/4/8 ways,
+    # 1/2/4 subtiles per wave, ring depth 2..6; N ragged, K = 11 chunks
+    if code in (2244, 2186) and fmt == "bf16":
+        pytest.skip("4 subtiles per wave and rings deeper than 4 are built for the quantized formats only")
+    r = _linear_case(ops, fmt, M, 200, 1408, code, seed=M + code)
+    assert r < 4e-6, r
+
+
 @pytest.mark.parametrize("fmt", ["f32", "w8"])
 def test_linear_fp32_activations(ops, fmt):
     r = _linear_case(ops, fmt, 7, 300, 688, 0, seed=3)
@@ -153,6 +165,16 @@ def test_linear_wide_and_deep(ops):
     assert _linear_case(ops, "w4", 3, 8192, 256, 2, seed=1) < 4e-6
     assert _linear_case(ops, "w4", 16, 130, 18944, 2, seed=4) < 4e-6
     assert _linear_case(ops, "bf16", 9, 96, 18944, 2, seed=2) < 4e-6
+
+
+@pytest.mark.parametrize("code,M", [
+    (31420, 17), (31230, 32), (31131, 50), (31221, 64), (31122, 100), (31123, 256), (31133, 130),   # weight-streaming
+    (40141, 33), (40161, 64), (40231, 100), (40262, 128), (40332, 200), (40342, 256), (40241, 250),  # deep-pipelined
+])
+def test_linear_gemm_variants(ops, code, M):
+    # N ragged against the 128-row tiles; K = 26 chunks (split-K over groups where the grid is short)
+    r = _linear_case(ops, "bf16", M, 456, 3328, code, seed=code % 97 + M)
+    assert r < 4e-6, r
 
 
 @pytest.mark.parametrize("M,N,K", [(40, 96, 18944), (300, 200, 1152), (1000, 300, 512), (129, 4608, 384)])
