@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU): the library loads and exports every
+function include/*.h declares, the Python binding declares each one, the
+host-only entry points (controller, arena sizing, argument validation) behave
+as specified, and the paged KV pool keeps its invariants under a sanitizer.
+"""
+import ctypes as C
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from oracle import controller as OC
+from speculative_decoding_rl_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in ("er_api.h", "er_ops.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(er_[a-z_0-9]+)\s*\(", text))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.lib_path()):
+        pytest.skip("libsdrl.so not built")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert len(declared) > 30
+    missing = [n for n in sorted(declared) if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a signature for each
+    assert not (declared - set(_lib.SIGNATURES)), sorted(declared - set(_lib.SIGNATURES))
+
+
+def _cost(shape_q=0.5 + 3 / 128):
+    # Qwen2.5-7B-shaped constants
+    return dict(n_layers=28, d_model=3584, n_q_heads=28, n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064,
+                w_bytes=2.0, q_bytes=shape_q, kv_bytes_el=2.0, hbm_bytes_per_s=6.4e12, flops_per_s=2.5e15,
+                t_fwd_s=4.0e-4)
+
+
+@pytest.mark.parametrize("B,C,alpha,cur", [(1, 600, 0.55, -1), (1, 600, 0.9, -1), (4, 2000, 0.8, 0),
+                                           (16, 2000, 0.8, 3), (64, 3000, 0.8, -1), (256, 1000, 0.95, 2),
+                                           (2, 8000, 0.6, 4), (8, 8000, 0.8, 0)])
+def test_controller_choice_matches_oracle(lib, B, C, alpha, cur):
+    from speculative_decoding_rl_amd.rollout import controller_choose
+    c = _cost()
+    m = OC.ModelCost(c["n_layers"], c["d_model"], c["n_q_heads"], c["n_kv_heads"], c["head_dim"], c["ffn"],
+                     c["vocab"], c["w_bytes"], c["q_bytes"], c["kv_bytes_el"])
+    r = OC.Roofline(c["hbm_bytes_per_s"], c["flops_per_s"], c["t_fwd_s"])
+    want = OC.choose(m, r, B, C, alpha, 1, 8, current=cur, margin=1.02)
+    assert controller_choose(c, B, C, alpha, 1, 8, current=cur, margin=1.02) == want
+
+
+def test_expected_tokens_matches_oracle(lib):
+    for a in (0.0, 0.3, 0.57, 0.8, 0.99, 1.0):
+        for g in (0, 1, 2, 4, 8):
+            assert abs(lib.er_expected_tokens(a, g) - OC.expected_tokens(a, g)) < 1e-12
+
+
+def _descs(**over):
+    md = _lib.ModelDesc(2, 512, 4, 2, 128, 1536, 8000, _lib.ER_BF16, 1e-6, 1e6)
+    dd = _lib.DraftDesc(_lib.ER_W4_G128_ASYM, 128, 1)
+    rd = dict(seed=0, temperature=1.0, top_p=1.0, gamma_init=4, gamma_min=1, gamma_max=8, ema_beta=0.3,
+              switch_margin=1.02, alpha_init=0.8, policy=_lib.ER_POLICY_AUTO, kv_block=16, max_seqs=16,
+              max_batch=16, max_ctx=512, prefill_chunk=512, kv_pool_blocks=64, hbm_bytes_per_s=0.0,
+              flops_per_s=0.0, t_fwd_s=-1.0)
+    rd.update(over)
+    return md, dd, _lib.RolloutDesc(*rd.values())
+
+
+def test_arena_bytes_grows_with_kv_blocks_and_validates(lib):
+    md, dd, rd = _descs()
+    a, b = C.c_size_t(0), C.c_size_t(0)
+    assert lib.er_arena_bytes(C.byref(md), C.byref(dd), C.byref(rd), 64, C.byref(a)) == 0
+    assert lib.er_arena_bytes(C.byref(md), C.byref(dd), C.byref(rd), 128, C.byref(b)) == 0
+    block = 2 * 2 * 2 * 16 * 128 * 2  # layers * (K,V) * kv heads * 16 positions * hd * bf16
+    assert b.value - a.value == 64 * block
+    for bad in (dict(gamma_max=0), dict(gamma_min=9), dict(kv_block=32), dict(top_p=0.0), dict(max_batch=17),
+                dict(temperature=-1.0), dict(policy=7)):
+        md, dd, rd = _descs(**bad)
+        assert lib.er_arena_bytes(C.byref(md), C.byref(dd), C.byref(rd), 64, C.byref(a)) == _lib.ER_EINVAL, bad
+    md, dd, rd = _descs()
+    md.head_dim = 96
+    assert lib.er_arena_bytes(C.byref(md), C.byref(dd), C.byref(rd), 64, C.byref(a)) == _lib.ER_EINVAL
+
+
+def test_op_entry_points_reject_bad_arguments_without_a_gpu(lib):
+    # argument checks run before any device call
+    assert lib.er_op_linear(_lib.ER_BF16, None, 8, 1, _lib.ER_FMT_BF16, None, None, None, 8, 8, None, 8, 0,
+                            None) == _lib.ER_EINVAL
+    assert lib.er_op_row_stats(None, 1, 8, 8, 1.0, 1.0, None, None) == _lib.ER_EINVAL
+    assert lib.er_op_stats_bytes(0) == 0 and lib.er_op_stats_bytes(152064) > 0
+
+
+def test_kvpool_invariants_under_sanitizers(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no g++")
+    exe = tmp_path / "kvpool_test"
+    src = os.path.join(ROOT, "tests", "host", "kvpool_test.cpp")
+    r = subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover",
+                        src, "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and "kvpool ok" in r.stdout, r.stdout + r.stderr
