@@ -59,6 +59,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
     ap.add_argument("--progress", type=float, default=20.0, help="seconds between progress lines")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only copy this many bytes device-to-device 10 times and exit (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -147,8 +149,11 @@ def bins(recs):
     return out
 
 
+LINEAR_KERNELS = ("k_skinny", "k_linear_mfma", "k_linear_valu", "k_wgemm", "k_gemm2", "k_gemm_bf16")
+
+
 def roofline_from(kprof):
-    lin = [k for k in kprof if "k_linear" in k["name"]]
+    lin = [k for k in kprof if any(n in k["name"] for n in LINEAR_KERNELS)]
     if not lin:
         return None, None
     top = max(lin, key=lambda k: k["ms"])
@@ -241,6 +246,14 @@ def main():
     from speculative_decoding_rl_amd import _lib
 
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": 10}))
+        return
     over = {"n_layers": args.layers} if args.layers else {}
     shape = synth.shape(args.config, **over)
     t0 = time.perf_counter()

@@ -64,6 +64,33 @@ struct Meta {
   T* dev(size_t off) const { return (T*)(d + off); }
 };
 
+// Attention work units of the n items whose queries start at pos0[i] and
+// number cnt[i], pushed into the metadata region as [n + 1] exclusive prefix
+// sums of units per item followed by [n] blocks per unit of each item.  The
+// unit length aims at ~1024 work-groups over all KV heads (enough to fill the
+// GPU, so that a long sequence no longer sets the kernel time alone) but
+// never goes below 8 blocks; an item's units split its blocks evenly, and an
+// item that fits in one unit is not split (no combine for it).
+size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, int* n_units) {
+  size_t off = 0;
+  int32_t* us = M.push<int32_t>((size_t)2 * n + 1, &off);
+  if (!us) return 0;
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
+  const int64_t target = std::max<int64_t>(8, (total * hkv + 1023) / 1024);
+  int32_t acc = 0;
+  for (int i = 0; i < n; ++i) {
+    us[i] = acc;
+    const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
+    const int64_t nu = std::max<int64_t>(1, (nblk + target - 1) / target);
+    us[n + 1 + i] = (int32_t)((nblk + nu - 1) / nu);
+    acc += (int32_t)nu;
+  }
+  us[n] = acc;
+  *n_units = acc;
+  return off;
+}
+
 }  // namespace
 
 struct er_ctx {
@@ -272,7 +299,13 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
   L->out = align256((size_t)(L->max_rows + r.max_batch) * 4);
   L->partial = align256((size_t)16 << 20) * 4;  // 16M floats
   L->counters = align256((size_t)65536 * 4);
-  L->attn = align256((size_t)8 << 20) * 4;      // 8M floats
+  {
+    // attention partials: one record of (hd + 2) floats per (work unit, kv head, query row); the worst case
+    // is every sequence of the largest batch at max_ctx with gamma_max + 1 query rows
+    const size_t units = (size_t)r.max_batch * ((r.max_ctx + 16 * 8 - 1) / (16 * 8));  // units are >= 8 blocks
+    const size_t recs = units * hkv * (size_t)(hq / hkv) * G1;
+    L->attn = align256(std::max((size_t)8 << 20, recs * (size_t)(hd + 2)) * 4);
+  }
   size_t w4 = 0;
   if (dd.quant == ER_W4_G128_ASYM) {
     w4 = std::max({(size_t)qkvN * d / 2, (size_t)d * hq * hd / 2, (size_t)2 * F * d / 2, (size_t)d * F / 2});
@@ -328,6 +361,8 @@ struct Fwd {
   int bt_stride = 0;
   const int32_t *it_bt = nullptr, *it_row0 = nullptr, *it_pos0 = nullptr, *it_cnt = nullptr;
   int n_items = 0, max_q = 0, max_ctx = 0;
+  const int32_t* unit_start = nullptr;   // attention work units (see push_units); null = uniform splits
+  int n_units = 0;
   double kv_keys = 0;                    // sum over items of keys read (for per-kernel byte counts)
   const int32_t* logit_rows = nullptr;  // rows whose logits are computed (with n_logit > 0)
   int n_logit = -1;                      // -1: every row; 0: none (prefill chunk with no last token)
@@ -427,6 +462,11 @@ int forward(er_ctx* c, const Fwd& f) {
   a.n_items = f.n_items;
   a.max_q_count = f.max_q;
   a.max_ctx = f.max_ctx;
+  a.unit_start = f.unit_start;
+  a.n_units = f.n_units;
+  if (a.unit_start &&
+      (size_t)a.n_units * hkv * (size_t)(hq / hkv) * f.max_q * (size_t)(hd + 2) > c->attn_ws_floats)
+    a.unit_start = nullptr;  // more units than the partials area holds: uniform splits instead
   a.hq = hq;
   a.hkv = hkv;
   a.hd = hd;
@@ -681,6 +721,9 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     h_ic[i] = 1;
     max_ctx = std::max(max_ctx, s.n + 1);
   }
+  int n_units = 0;
+  const size_t o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units);
+  if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
     if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
@@ -699,6 +742,8 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.n_items = n;
     f.max_q = 1;
     f.max_ctx = max_ctx;
+    f.unit_start = M.dev<int32_t>(o_us);
+    f.n_units = n_units;
     f.kv_keys = kv_keys;
     f.logits = c->logits_p;
     f.ldl = c->md.vocab;
@@ -827,6 +872,12 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     h_vic[b] = G1;
     max_ctx = std::max(max_ctx, s.n + G1);
   }
+  std::vector<size_t> o_dus(g);
+  std::vector<int> n_dus(g);
+  for (int j = 0; j < g; ++j) o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, &n_dus[j]);
+  int n_vus = 0;
+  const size_t o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, &n_vus);
+  if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
     if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
@@ -848,6 +899,8 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.n_items = n;
       f.max_q = 1;
       f.max_ctx = max_ctx;
+      f.unit_start = M.dev<int32_t>(o_dus[j]);
+      f.n_units = n_dus[j];
       f.kv_keys = kv_sum + (double)n * (j + 1);
       f.logits = c->logits_q + (size_t)j * n * V;
       f.ldl = V;
@@ -876,6 +929,8 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.n_items = n;
     f.max_q = G1;
     f.max_ctx = max_ctx;
+    f.unit_start = M.dev<int32_t>(o_vus);
+    f.n_units = n_vus;
     f.kv_keys = kv_sum + (double)n * G1;
     f.logits = c->logits_p;
     f.ldl = V;
@@ -1396,6 +1451,9 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
         }
         row += sg.cnt;
       }
+      int n_units = 0;
+      const size_t o_us = push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units);
+      if (!M.ok) return fail(c, ER_ENOMEM, "metadata region too small for a prefill chunk");
       HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
       Fwd f;
       f.M = rows;
@@ -1411,6 +1469,8 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       f.n_items = n_items;
       f.max_q = qmax;
       f.max_ctx = max_ctx;
+      f.unit_start = M.dev<int32_t>(o_us);
+      f.n_units = n_units;
       f.logit_rows = M.dev<int32_t>(o_lr);
       f.n_logit = nl;
       f.logits = c->logits_p + (size_t)next_row * V;

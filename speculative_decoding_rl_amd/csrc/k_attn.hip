@@ -38,17 +38,50 @@ ER_DEV long kv_block_base(long phys, int layer, int L, int kv, int hkv, int head
   return ((((phys * L + layer) * 2 + kv) * hkv + head) * 16) * (long)hd;
 }
 
-// Split partial record of one row: [hd] unnormalised output, then running max, then running sum.
-ER_DEV float* partial_row(const AttnArgs& a, int item, int g, int sp, int nsplit, int r) {
+// Split partial record of one row of work unit u: [hd] unnormalised output,
+// then running max, then running sum.
+ER_DEV float* partial_row(const AttnArgs& a, long u, int g, int r) {
   const int grp = a.hq / a.hkv;
-  return a.ws + ((((long)item * a.hkv + g) * nsplit + sp) * (long)(grp * a.max_q_count) + r) * (a.hd + 2);
+  return a.ws + (((long)u * a.hkv + g) * (long)(grp * a.max_q_count) + r) * (a.hd + 2);
+}
+
+// Work unit u: its item, its index among the item's units, how many units the
+// item has, and its first block.  With a unit table, item i owns units
+// unit_start[i] .. of unit_start[n_items + 1 + i] blocks each; otherwise every item
+// has nsplit units of bps blocks (unit = item * nsplit + split).
+struct Unit {
+  int item, sp, nu, b0, bps;
+};
+ER_DEV Unit unit_of(const AttnArgs& a, int u, int nsplit, int bps) {
+  Unit w;
+  if (a.unit_start) {
+    int lo = 0, hi = a.n_items;  // largest i with unit_start[i] <= u
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (a.unit_start[mid] <= u) lo = mid; else hi = mid;
+    }
+    w.item = lo;
+    w.sp = u - a.unit_start[lo];
+    w.nu = a.unit_start[lo + 1] - a.unit_start[lo];
+    w.bps = a.unit_start[a.n_items + 1 + lo];
+  } else {
+    w.item = u / nsplit;
+    w.sp = u - w.item * nsplit;
+    w.nu = nsplit;
+    w.bps = bps;
+  }
+  w.b0 = w.sp * w.bps;
+  return w;
 }
 
 template <int HD>
 __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int bps) {
   constexpr int NC = HD / 16;   // 16-column output tiles
   constexpr int NQ = HD / 32;   // 32-wide k slices of the score MFMA
-  const int item = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int u = blockIdx.x, g = blockIdx.y;
+  if (a.unit_start && u >= a.n_units) return;
+  const Unit w = unit_of(a, u, nsplit, bps);
+  const int item = w.item;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, kb = lane >> 4;
   const int grp = a.hq / a.hkv;
@@ -61,8 +94,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   const int s_in = 4 / rgn;                  // waves sharing one row group
   const int rgi = wave / s_in, sin = wave % s_in;
   const int nblk = (pos0 + qc + 15) >> 4;
-  const int b0 = sp * bps;
-  const int b1 = min(nblk, b0 + bps);
+  const int b0 = w.b0;
+  const int b1 = min(nblk, b0 + w.bps);
   const float scale = 1.0f / sqrtf((float)HD);
 
   __shared__ float o_sh[4][16 * HD];
@@ -230,13 +263,13 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
     const int rr = rgi * 16 + 4 * kb + r;
     if (rr >= R) continue;
     const int qi = rr / grp, hh = g * grp + rr % grp;
-    if (nsplit == 1) {
+    if (w.nu == 1) {
       const float inv = rl[r] > 0.f ? 1.0f / rl[r] : 0.f;
       uint16_t* out = (uint16_t*)a.out + ((long)(qrow0 + qi) * a.hq + hh) * HD;
 #pragma unroll
       for (int c = 0; c < NC; ++c) out[16 * c + l16] = (uint16_t)f2bf(o[c][r] * inv);
     } else {
-      float* pp = partial_row(a, item, g, sp, nsplit, rr);
+      float* pp = partial_row(a, u, g, rr);
 #pragma unroll
       for (int c = 0; c < NC; ++c) pp[16 * c + l16] = o[c][r];
       if (l16 == 0) { pp[HD] = rm[r]; pp[HD + 1] = rl[r]; }
@@ -246,14 +279,17 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
 
 // fp32 (small models): one wavefront per row, keys streamed from the pool.
 __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int nsplit, int bps) {
-  const int item = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int u = blockIdx.x, g = blockIdx.y;
+  if (a.unit_start && u >= a.n_units) return;
+  const Unit w = unit_of(a, u, nsplit, bps);
+  const int item = w.item;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int hd = a.hd, grp = a.hq / a.hkv;
   const int qc = a.item_q_count[item], pos0 = a.item_q_pos0[item], qrow0 = a.item_q_row0[item];
   const int R = grp * qc;
   const int nkeys = pos0 + qc;
-  const int k0 = sp * bps * 16;
-  const int k1 = min(nkeys, k0 + bps * 16);
+  const int k0 = w.b0 * 16;
+  const int k1 = min(nkeys, k0 + w.bps * 16);
   const float scale = 1.0f / sqrtf((float)hd);
   const float* pool = (const float*)a.kv_pool;
   const int32_t* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
@@ -279,13 +315,13 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int nsplit, int b
       if (lane + 64 < hd) o1 = o1 * c + p * vb[(lane + 64) * 16 + t];
       m = mn;
     }
-    if (nsplit == 1) {
+    if (w.nu == 1) {
       float* out = (float*)a.out + ((long)(qrow0 + qi) * a.hq + hh) * hd;
       const float inv = l > 0.f ? 1.0f / l : 0.f;
       if (lane < hd) out[lane] = o0 * inv;
       if (lane + 64 < hd) out[lane + 64] = o1 * inv;
     } else {
-      float* pp = partial_row(a, item, g, sp, nsplit, r);
+      float* pp = partial_row(a, u, g, r);
       if (lane < hd) pp[lane] = o0;
       if (lane + 64 < hd) pp[lane + 64] = o1;
       if (lane == 0) { pp[hd] = m; pp[hd + 1] = l; }
@@ -299,8 +335,11 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int nsplit) {
   const int grp = a.hq / a.hkv, hd = a.hd;
   const int qc = a.item_q_count[item];
   if (r >= grp * qc) return;
-  const long stride_sp = (long)(grp * a.max_q_count) * (hd + 2);
-  const float* base = partial_row(a, item, g, 0, nsplit, r);
+  const int u0 = a.unit_start ? a.unit_start[item] : item * nsplit;
+  if (a.unit_start) nsplit = a.unit_start[item + 1] - u0;
+  if (nsplit == 1) return;  // written directly by its only unit
+  const long stride_sp = (long)a.hkv * (grp * a.max_q_count) * (hd + 2);
+  const float* base = partial_row(a, u0, g, r);
   float M = -INFINITY;
   for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * stride_sp + hd]);
   const int e = threadIdx.x;
@@ -342,11 +381,14 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
     nsplit = (int)std::max(1L, std::min((long)(maxblk + per_wg - 1) / per_wg, (512 + base - 1) / base));
   const int bps = (maxblk + nsplit - 1) / nsplit;
   nsplit = (maxblk + bps - 1) / bps;
-  if (nsplit > 1) {
-    const size_t need = (size_t)a.n_items * a.hkv * nsplit * grp * a.max_q_count * (a.hd + 2);
+  const long units = a.unit_start ? (long)a.n_units : (long)a.n_items * nsplit;
+  const bool combine = a.unit_start ? a.n_units > a.n_items : nsplit > 1;
+  if (combine) {
+    const size_t need = (size_t)units * a.hkv * grp * a.max_q_count * (a.hd + 2);
     if (need > a.ws_floats) return -2;
   }
-  dim3 grid(a.n_items, a.hkv, nsplit);
+  if (units <= 0) return 0;
+  dim3 grid((unsigned)units, a.hkv, 1);
   if (a.bf16) {
     if (a.hd == 128) hipLaunchKernelGGL(k_attn_mfma<128>, grid, dim3(256), 0, st, a, nsplit, bps);
     else hipLaunchKernelGGL(k_attn_mfma<64>, grid, dim3(256), 0, st, a, nsplit, bps);
@@ -354,7 +396,7 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_attn_valu, grid, dim3(256), 0, st, a, nsplit, bps);
   }
   if (hipGetLastError() != hipSuccess) return -3;
-  if (nsplit > 1) {
+  if (combine) {
     dim3 g2(a.n_items, a.hkv, grp * a.max_q_count);
     if (a.bf16) hipLaunchKernelGGL(k_attn_combine<true>, g2, dim3(128), 0, st, a, nsplit);
     else hipLaunchKernelGGL(k_attn_combine<false>, g2, dim3(128), 0, st, a, nsplit);

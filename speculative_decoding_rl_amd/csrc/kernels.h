@@ -123,6 +123,12 @@ struct AttnArgs {
   bool bf16;
   float* ws;                 // split partials
   size_t ws_floats;
+  // Work units (optional): item i owns units unit_start[i] .. unit_start[i+1]-1
+  // (exclusive prefix sum, n_items + 1 entries, n_units in total), each of
+  // unit_start[n_items + 1 + i] blocks (the last one shorter).  Null: every
+  // item gets the same split count.
+  const int32_t* unit_start;
+  int n_units;
 };
 int launch_attention(const AttnArgs& a, hipStream_t st);
 
