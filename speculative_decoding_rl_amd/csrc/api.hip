@@ -70,24 +70,28 @@ struct Meta {
 // unit length aims at ~1024 work-groups over all KV heads (enough to fill the
 // GPU, so that a long sequence no longer sets the kernel time alone) but
 // never goes below 8 blocks; an item's units split its blocks evenly, and an
-// item that fits in one unit is not split (no combine for it).
-size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, int* n_units) {
+// item that fits in one unit is not split (no combine for it).  Then the
+// list of the items that were split ([n] entries, n_split used).
+size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, int* n_units, int* n_split) {
   size_t off = 0;
-  int32_t* us = M.push<int32_t>((size_t)2 * n + 1, &off);
+  int32_t* us = M.push<int32_t>((size_t)3 * n + 1, &off);
   if (!us) return 0;
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  const int64_t target = std::max<int64_t>(8, (total * hkv + 1023) / 1024);
+  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 1023) / 1024));
   int32_t acc = 0;
+  int ns = 0;
   for (int i = 0; i < n; ++i) {
     us[i] = acc;
     const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
     const int64_t nu = std::max<int64_t>(1, (nblk + target - 1) / target);
     us[n + 1 + i] = (int32_t)((nblk + nu - 1) / nu);
+    if (nu > 1) us[2 * n + 1 + ns++] = i;
     acc += (int32_t)nu;
   }
   us[n] = acc;
   *n_units = acc;
+  *n_split = ns;
   return off;
 }
 
@@ -362,7 +366,7 @@ struct Fwd {
   const int32_t *it_bt = nullptr, *it_row0 = nullptr, *it_pos0 = nullptr, *it_cnt = nullptr;
   int n_items = 0, max_q = 0, max_ctx = 0;
   const int32_t* unit_start = nullptr;   // attention work units (see push_units); null = uniform splits
-  int n_units = 0;
+  int n_units = 0, n_split = 0;
   double kv_keys = 0;                    // sum over items of keys read (for per-kernel byte counts)
   const int32_t* logit_rows = nullptr;  // rows whose logits are computed (with n_logit > 0)
   int n_logit = -1;                      // -1: every row; 0: none (prefill chunk with no last token)
@@ -464,6 +468,8 @@ int forward(er_ctx* c, const Fwd& f) {
   a.max_ctx = f.max_ctx;
   a.unit_start = f.unit_start;
   a.n_units = f.n_units;
+  a.split_items = f.unit_start ? f.unit_start + 2 * f.n_items + 1 : nullptr;
+  a.n_split = f.n_split;
   if (a.unit_start &&
       (size_t)a.n_units * hkv * (size_t)(hq / hkv) * f.max_q * (size_t)(hd + 2) > c->attn_ws_floats)
     a.unit_start = nullptr;  // more units than the partials area holds: uniform splits instead
@@ -494,12 +500,24 @@ int forward(er_ctx* c, const Fwd& f) {
     if (r) return r;
     a.layer = l;
     {
-      const int e = kp_begin(c);
-      KC(c, launch_attention(a, c->st));
+      // scoring kernel and (when keys were split) the combine, timed apart
+      int e = kp_begin(c);
+      int combined = 0;
+      KC(c, launch_attention(a, c->st, 1, &combined));
       if (e >= 0) {
         const double kvb = 2.0 * hkv * hd * c->act_bytes;  // K and V of one position, one layer
         const double by = f.kv_keys * kvb + 2.0 * f.M * hq * hd * c->act_bytes;
-        kp_end(c, e, c->bf16 ? "er::k_attn<true>" : "er::k_attn<false>", by, 4.0 * (f.kv_keys / std::max(1, f.n_items)) * f.M * hq * hd);
+        const char* nm = !c->bf16 ? "er::k_attn_valu" : (hd == 128 ? "er::k_attn_mfma<128>" : "er::k_attn_mfma<64>");
+        kp_end(c, e, nm, by, 4.0 * f.kv_keys * f.max_q * (double)hq * hd);
+      }
+      if (combined) {
+        e = kp_begin(c);
+        KC(c, launch_attention(a, c->st, 2));
+        if (e >= 0) {
+          const double units = a.unit_start ? (double)a.n_units : (double)f.n_items;
+          const double by = units * hkv * (double)(hq / hkv) * f.max_q * (hd + 2) * 4.0 + 2.0 * f.M * hq * hd * c->act_bytes;
+          kp_end(c, e, c->bf16 ? "er::k_attn_combine<true>" : "er::k_attn_combine<false>", by, 0.0);
+        }
       }
     }
     if (c->fuse) {
@@ -722,7 +740,8 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     max_ctx = std::max(max_ctx, s.n + 1);
   }
   int n_units = 0;
-  const size_t o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units);
+  int n_split = 0;
+  const size_t o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
@@ -744,6 +763,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.max_ctx = max_ctx;
     f.unit_start = M.dev<int32_t>(o_us);
     f.n_units = n_units;
+    f.n_split = n_split;
     f.kv_keys = kv_keys;
     f.logits = c->logits_p;
     f.ldl = c->md.vocab;
@@ -874,9 +894,11 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   }
   std::vector<size_t> o_dus(g);
   std::vector<int> n_dus(g);
-  for (int j = 0; j < g; ++j) o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, &n_dus[j]);
+  std::vector<int> s_dus(g);
+  for (int j = 0; j < g; ++j) o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, &n_dus[j], &s_dus[j]);
   int n_vus = 0;
-  const size_t o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, &n_vus);
+  int s_vus = 0;
+  const size_t o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, &n_vus, &s_vus);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
@@ -901,6 +923,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.max_ctx = max_ctx;
       f.unit_start = M.dev<int32_t>(o_dus[j]);
       f.n_units = n_dus[j];
+      f.n_split = s_dus[j];
       f.kv_keys = kv_sum + (double)n * (j + 1);
       f.logits = c->logits_q + (size_t)j * n * V;
       f.ldl = V;
@@ -931,6 +954,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.max_ctx = max_ctx;
     f.unit_start = M.dev<int32_t>(o_vus);
     f.n_units = n_vus;
+    f.n_split = s_vus;
     f.kv_keys = kv_sum + (double)n * G1;
     f.logits = c->logits_p;
     f.ldl = V;
@@ -1452,7 +1476,8 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
         row += sg.cnt;
       }
       int n_units = 0;
-      const size_t o_us = push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units);
+      int n_split = 0;
+      const size_t o_us = push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split);
       if (!M.ok) return fail(c, ER_ENOMEM, "metadata region too small for a prefill chunk");
       HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
       Fwd f;
@@ -1471,6 +1496,7 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       f.max_ctx = max_ctx;
       f.unit_start = M.dev<int32_t>(o_us);
       f.n_units = n_units;
+      f.n_split = n_split;
       f.logit_rows = M.dev<int32_t>(o_lr);
       f.n_logit = nl;
       f.logits = c->logits_p + (size_t)next_row * V;

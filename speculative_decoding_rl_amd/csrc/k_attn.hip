@@ -128,12 +128,20 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   const int32_t* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
 
   if (rgi < rgroups) {
+    // This wave's blocks are b0 + sin + s_in * t.  Their physical ids are read
+    // 64 at a time into one register per lane and broadcast with readlane, so
+    // that loading a block's K and V never waits on its block-table entry.
+    int bt_win = 0;
+    auto refill = [&](int t) {
+      const int blk = b0 + sin + s_in * (t + lane);
+      bt_win = blk < b1 ? bt[blk] : 0;
+    };
     // K and V fragments of the next block are loaded while the current one
     // is scored (register double buffer)
     uint4 kn[NQ];
     uint2 vn[NC];
-    auto fetch = [&](int blk) {
-      const long phys = bt[blk];
+    auto fetch = [&](int t) {
+      const long phys = __builtin_amdgcn_readlane(bt_win, t & 63);
       const uint16_t* kp = pool + kv_block_base(phys, a.layer, a.n_layers, 0, a.hkv, g, HD);
       const uint16_t* vp = pool + kv_block_base(phys, a.layer, a.n_layers, 1, a.hkv, g, HD);
 #pragma unroll
@@ -141,15 +149,20 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
 #pragma unroll
       for (int c = 0; c < NC; ++c) vn[c] = *(const uint2*)(vp + (16 * c + l16) * 16 + 4 * kb);
     };
-    if (b0 + sin < b1) fetch(b0 + sin);
-    for (int blk = b0 + sin; blk < b1; blk += s_in) {
+    refill(0);
+    if (b0 + sin < b1) fetch(0);
+    int t = 0;
+    for (int blk = b0 + sin; blk < b1; blk += s_in, ++t) {
       uint4 kc[NQ];
       uint2 vc[NC];
 #pragma unroll
       for (int i = 0; i < NQ; ++i) kc[i] = kn[i];
 #pragma unroll
       for (int c = 0; c < NC; ++c) vc[c] = vn[c];
-      if (blk + s_in < b1) fetch(blk + s_in);
+      if (blk + s_in < b1) {
+        if (((t + 1) & 63) == 0) refill(t + 1);
+        fetch(t + 1);
+      }
       // S^T = K . Q^T: A = K rows (token l16), k = 8*kb + 32*i
       f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -331,7 +344,8 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int nsplit, int b
 
 template <bool BF>
 __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int nsplit) {
-  const int item = blockIdx.x, g = blockIdx.y, r = blockIdx.z;
+  const int item = a.unit_start ? a.split_items[blockIdx.x] : blockIdx.x;
+  const int g = blockIdx.y, r = blockIdx.z;
   const int grp = a.hq / a.hkv, hd = a.hd;
   const int qc = a.item_q_count[item];
   if (r >= grp * qc) return;
@@ -360,7 +374,7 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int nsplit) {
   Act<BF>::st((T*)a.out, o, den > 0.f ? num / den : 0.f);
 }
 
-int launch_attention(const AttnArgs& a, hipStream_t st) {
+int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined) {
   if (a.n_items <= 0) return 0;
   const int grp = a.hq / a.hkv;
   if ((a.hd != 64 && a.hd != 128) || a.hq % a.hkv != 0) return -1;
@@ -382,13 +396,15 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
   const int bps = (maxblk + nsplit - 1) / nsplit;
   nsplit = (maxblk + bps - 1) / bps;
   const long units = a.unit_start ? (long)a.n_units : (long)a.n_items * nsplit;
-  const bool combine = a.unit_start ? a.n_units > a.n_items : nsplit > 1;
+  const bool combine = a.unit_start ? a.n_split > 0 : nsplit > 1;
   if (combine) {
     const size_t need = (size_t)units * a.hkv * grp * a.max_q_count * (a.hd + 2);
     if (need > a.ws_floats) return -2;
   }
+  if (combined) *combined = combine ? 1 : 0;
   if (units <= 0) return 0;
   dim3 grid((unsigned)units, a.hkv, 1);
+  if (phase != 2) {
   if (a.bf16) {
     if (a.hd == 128) hipLaunchKernelGGL(k_attn_mfma<128>, grid, dim3(256), 0, st, a, nsplit, bps);
     else hipLaunchKernelGGL(k_attn_mfma<64>, grid, dim3(256), 0, st, a, nsplit, bps);
@@ -396,8 +412,9 @@ int launch_attention(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(k_attn_valu, grid, dim3(256), 0, st, a, nsplit, bps);
   }
   if (hipGetLastError() != hipSuccess) return -3;
-  if (combine) {
-    dim3 g2(a.n_items, a.hkv, grp * a.max_q_count);
+  }
+  if (combine && phase != 1) {
+    dim3 g2(a.unit_start ? a.n_split : a.n_items, a.hkv, grp * a.max_q_count);
     if (a.bf16) hipLaunchKernelGGL(k_attn_combine<true>, g2, dim3(128), 0, st, a, nsplit);
     else hipLaunchKernelGGL(k_attn_combine<false>, g2, dim3(128), 0, st, a, nsplit);
     if (hipGetLastError() != hipSuccess) return -3;

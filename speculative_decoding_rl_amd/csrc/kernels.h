@@ -129,8 +129,14 @@ struct AttnArgs {
   // item gets the same split count.
   const int32_t* unit_start;
   int n_units;
+  // Items that have more than one unit (they alone need the combine); with a
+  // unit table, null means none.
+  const int32_t* split_items;
+  int n_split;
 };
-int launch_attention(const AttnArgs& a, hipStream_t st);
+// phase 0: scores + combine; 1: the scoring kernel only; 2: the combine only
+// (same arguments).  *combined (nullable) tells whether a combine is needed.
+int launch_attention(const AttnArgs& a, hipStream_t st, int phase = 0, int* combined = nullptr);
 
 // Quantizers (drafter build) and layout conversion.
 int launch_quantize_w8(const void* W, bool bf16, int N, int K, int8_t* q, float* scale, hipStream_t st);
