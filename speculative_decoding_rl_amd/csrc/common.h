@@ -83,3 +83,13 @@ ER_DEV uint32_t float_key(float f) {
   if ((u << 1) == 0) u = 0;  // -0 and +0 are the same logit
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Work-group barrier for LDS hand-offs only: waits for this wave's LDS
+// operations (lgkmcnt(0); vmcnt and expcnt left at their maxima) and then
+// meets the other waves.  Unlike __syncthreads() it carries no memory fence,
+// so global loads issued ahead (software pipelines) stay in flight.
+ER_DEV void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+}
+

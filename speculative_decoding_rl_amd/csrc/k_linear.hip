@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(LinArgs a, float* __restrict_
       if (nxt) gload(st + 1);
       mma(buf);
       if (nxt) sstore(buf ^ 1);
-      __syncthreads();
+      lds_barrier();
       buf ^= 1;
     }
   }
@@ -744,7 +744,7 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
   uint4 wreg[DEPTH][NR][NW];
 
   auto issue = [&](int it, int slot) {
-    const long c = ks + (long)KS * it;
+    const long c = min(ks + (long)KS * it, (long)nchunks - 1);
 #pragma unroll
     for (int ni = 0; ni < NR; ++ni) {
       if constexpr (FMT == FMT_BF16) {
@@ -766,16 +766,15 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
 #pragma unroll
   for (int ni = 0; ni < NR; ++ni) acc[ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // lanes of rows >= M read row M-1 instead (their outputs are never stored):
+  // no predicated LDS reads in the loop
+  const int xr_row = l16 < M ? l16 : M - 1;
   auto compute = [&](int it, int slot) {
     const int c = ks + KS * it;
-    const bool xrow_ok = l16 < M;
     bf16x8_t xa[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 v = uint4{0u, 0u, 0u, 0u};
-      if (xrow_ok) v = *(const uint4*)(xs + l16 * ldsx + c * 128 + kcol<FMT>(i, kb));
-      xa[i] = __builtin_bit_cast(bf16x8_t, v);
-    }
+    for (int i = 0; i < 4; ++i)
+      xa[i] = __builtin_bit_cast(bf16x8_t, *(const uint4*)(xs + xr_row * ldsx + c * 128 + kcol<FMT>(i, kb)));
     f32x4_t accg[NR];
     if constexpr (FMT != FMT_BF16) {
 #pragma unroll
@@ -823,10 +822,13 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
     }
   };
 
-  // weights for the first stages go out before the x' fill
+  // Weights for the first stages go out before the x' fill.  Every loop
+  // iteration issues exactly one stage (clamped to the last one: re-reads hit
+  // the cache), so the compiler can keep DEPTH - 1 stages in flight instead
+  // of draining the load counter at each use.
+  const int last_it = n_it > 0 ? n_it - 1 : 0;
 #pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d)
-    if (d < n_it) issue(d, d);
+  for (int d = 0; d < DEPTH - 1; ++d) issue(min(d, last_it), d);
 
   {
     const int K8 = K >> 3;
@@ -872,7 +874,7 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int it = i0 + d;
-      if (it + DEPTH - 1 < n_it) issue(it + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+      issue(min(it + DEPTH - 1, last_it), (d + DEPTH - 1) % DEPTH);
       if (it < n_it) compute(it, d);
     }
   }
@@ -1074,7 +1076,7 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
         if (t + DEPTH - 1 < T) issue_w(t + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
         compute(t, d % DEPTH, d & 1);
         if (t + 1 < T) store_x((d + 1) & 1);
-        __syncthreads();
+        lds_barrier();
       }
     }
   }
@@ -1337,7 +1339,7 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
           if (t + DEPTH - 1 < T) issue(t + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
           mma(d & 1);
           if (t + 1 < T) stash((d + 1) % DEPTH, (d + 1) & 1);
-          __syncthreads();
+          lds_barrier();
         }
       }
     }
@@ -1479,20 +1481,21 @@ static int dispatch_mfma(const LinArgs& a, hipStream_t st, LinearInfo* info) {
 
 // Automatic choice among the streaming variants, from a sweep of the Qwen2.5-7B
 // projections on MI355X with weights rotating through more than the 256 MB
-// last-level cache (M = 1 and 4): K split over all 8 waves for narrow and
-// wide outputs, over 4 waves with 2-deep rings in between; W4 wants deeper
-// rings (its stages are 16 bytes per lane).
+// last-level cache (M = 1 and 4): 2-deep rings for bf16 (its 16-byte stages
+// already keep enough bytes in flight), K split over all 8 waves for narrow
+// outputs and over 2 or 4 for wide ones; the W4 drafter wants 3-4 deep rings
+// on its long-K and wide layers.
 template <int FMT>
 static int dispatch_skinny(const LinArgs& a, hipStream_t st, LinearInfo* info) {
   const int N = a.W.N, K = a.W.K;
   if constexpr (FMT == FMT_BF16) {
-    if (N >= 16384) return a.M <= 2 ? run_skinny<FMT, 1, 8, 3>(a, st, info) : run_skinny<FMT, 1, 8, 2>(a, st, info);
+    if (N >= 16384) return a.M <= 2 ? run_skinny<FMT, 1, 4, 2>(a, st, info) : run_skinny<FMT, 1, 2, 2>(a, st, info);
     if (N >= 4096) return run_skinny<FMT, 1, 4, 2>(a, st, info);
     return run_skinny<FMT, 1, 8, 2>(a, st, info);
   } else {
-    if (K >= 8192) return run_skinny<FMT, 1, 8, 6>(a, st, info);
-    if (N >= 8192) return a.M <= 2 ? run_skinny<FMT, 1, 2, 4>(a, st, info) : run_skinny<FMT, 1, 2, 3>(a, st, info);
-    return run_skinny<FMT, 1, 8, 3>(a, st, info);
+    if (K >= 8192) return run_skinny<FMT, 1, 8, 4>(a, st, info);
+    if (N >= 8192) return run_skinny<FMT, 1, 2, 3>(a, st, info);
+    return run_skinny<FMT, 1, 8, 2>(a, st, info);
   }
 }
 
