@@ -72,7 +72,8 @@ struct Meta {
 // never goes below 8 blocks; an item's units split its blocks evenly, and an
 // item that fits in one unit is not split (no combine for it).  Then the
 // list of the items that were split ([n] entries, n_split used).
-size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, int* n_units, int* n_split) {
+size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, int* n_units, int* n_split,
+                  int* max_units) {
   size_t off = 0;
   int32_t* us = M.push<int32_t>((size_t)3 * n + 1, &off);
   if (!us) return 0;
@@ -80,7 +81,7 @@ size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* c
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
   const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 1023) / 1024));
   int32_t acc = 0;
-  int ns = 0;
+  int ns = 0, mu = 0;
   for (int i = 0; i < n; ++i) {
     us[i] = acc;
     const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
@@ -88,10 +89,12 @@ size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* c
     us[n + 1 + i] = (int32_t)((nblk + nu - 1) / nu);
     if (nu > 1) us[2 * n + 1 + ns++] = i;
     acc += (int32_t)nu;
+    mu = std::max(mu, (int)nu);
   }
   us[n] = acc;
   *n_units = acc;
   *n_split = ns;
+  *max_units = mu;
   return off;
 }
 
@@ -366,7 +369,7 @@ struct Fwd {
   const int32_t *it_bt = nullptr, *it_row0 = nullptr, *it_pos0 = nullptr, *it_cnt = nullptr;
   int n_items = 0, max_q = 0, max_ctx = 0;
   const int32_t* unit_start = nullptr;   // attention work units (see push_units); null = uniform splits
-  int n_units = 0, n_split = 0;
+  int n_units = 0, n_split = 0, max_units = 0;
   double kv_keys = 0;                    // sum over items of keys read (for per-kernel byte counts)
   const int32_t* logit_rows = nullptr;  // rows whose logits are computed (with n_logit > 0)
   int n_logit = -1;                      // -1: every row; 0: none (prefill chunk with no last token)
@@ -470,6 +473,7 @@ int forward(er_ctx* c, const Fwd& f) {
   a.n_units = f.n_units;
   a.split_items = f.unit_start ? f.unit_start + 2 * f.n_items + 1 : nullptr;
   a.n_split = f.n_split;
+  a.max_units = f.max_units;
   if (a.unit_start &&
       (size_t)a.n_units * hkv * (size_t)(hq / hkv) * f.max_q * (size_t)(hd + 2) > c->attn_ws_floats)
     a.unit_start = nullptr;  // more units than the partials area holds: uniform splits instead
@@ -741,7 +745,8 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
   }
   int n_units = 0;
   int n_split = 0;
-  const size_t o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split);
+  int max_units = 0;
+  const size_t o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split, &max_units);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
@@ -764,6 +769,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.unit_start = M.dev<int32_t>(o_us);
     f.n_units = n_units;
     f.n_split = n_split;
+    f.max_units = max_units;
     f.kv_keys = kv_keys;
     f.logits = c->logits_p;
     f.ldl = c->md.vocab;
@@ -895,10 +901,13 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   std::vector<size_t> o_dus(g);
   std::vector<int> n_dus(g);
   std::vector<int> s_dus(g);
-  for (int j = 0; j < g; ++j) o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, &n_dus[j], &s_dus[j]);
+  std::vector<int> m_dus(g);
+  for (int j = 0; j < g; ++j)
+    o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, &n_dus[j], &s_dus[j], &m_dus[j]);
   int n_vus = 0;
   int s_vus = 0;
-  const size_t o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, &n_vus, &s_vus);
+  int m_vus = 0;
+  const size_t o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, &n_vus, &s_vus, &m_vus);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
@@ -924,6 +933,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.unit_start = M.dev<int32_t>(o_dus[j]);
       f.n_units = n_dus[j];
       f.n_split = s_dus[j];
+      f.max_units = m_dus[j];
       f.kv_keys = kv_sum + (double)n * (j + 1);
       f.logits = c->logits_q + (size_t)j * n * V;
       f.ldl = V;
@@ -955,6 +965,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.unit_start = M.dev<int32_t>(o_vus);
     f.n_units = n_vus;
     f.n_split = s_vus;
+    f.max_units = m_vus;
     f.kv_keys = kv_sum + (double)n * G1;
     f.logits = c->logits_p;
     f.ldl = V;
@@ -1477,7 +1488,8 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       }
       int n_units = 0;
       int n_split = 0;
-      const size_t o_us = push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split);
+      int max_units = 0;
+      const size_t o_us = push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split, &max_units);
       if (!M.ok) return fail(c, ER_ENOMEM, "metadata region too small for a prefill chunk");
       HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
       Fwd f;
@@ -1497,6 +1509,7 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       f.unit_start = M.dev<int32_t>(o_us);
       f.n_units = n_units;
       f.n_split = n_split;
+      f.max_units = max_units;
       f.logit_rows = M.dev<int32_t>(o_lr);
       f.n_logit = nl;
       f.logits = c->logits_p + (size_t)next_row * V;

@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   const int b1 = min(nblk, b0 + w.bps);
   const float scale = 1.0f / sqrtf((float)HD);
 
-  __shared__ float o_sh[4][16 * HD];
+  constexpr int OS = HD + 4;   // padded row stride of the merge area (rows 4 apart hit other banks)
+  __shared__ float o_sh[4][16 * OS];
   __shared__ float ml_sh[4][2][16];
 
   // this lane's query row (as the MFMA column n = l16)
@@ -229,48 +230,58 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
     }
   }
 
-  // merge the s_in waves of each row group (fixed order), then normalise or emit partials
+  // Merge the s_in waves of each row group in LDS (sources in a fixed
+  // order).  Each of them then finishes the column tiles c with
+  // c % s_in == sin, so the merge costs every wave only its share.
+  float rl[4], rm[4];
   if (s_in > 1) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o_sh[wave][(4 * kb + r) * HD + 16 * c + l16] = o[c][r];
+      for (int r = 0; r < 4; ++r) o_sh[wave][(4 * kb + r) * OS + 16 * c + l16] = o[c][r];
     if (kb == 0) { ml_sh[wave][0][l16] = m_run; ml_sh[wave][1][l16] = l_run; }
     __syncthreads();
-    if (sin != 0) return;
-    float M = -INFINITY;
-    for (int w = wave; w < wave + s_in; ++w) M = fmaxf(M, ml_sh[w][0][l16]);
-    float lsum = 0.f;
-    float wgt[4];
-    for (int w = 0; w < s_in; ++w) {
-      const float mw = ml_sh[wave + w][0][l16];
-      const float f = (mw == -INFINITY) ? 0.f : expf(mw - M);
-      lsum += f * ml_sh[wave + w][1][l16];
-      if (w < 4) wgt[w] = f;
-    }
-    // o rows are in the row layout (4*kb + r); fetch each row's weights from lane 4*kb + r
+    const int w0 = rgi * s_in;
+    float f[4][4];
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * kb + r;
+      float mr[4], M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        mr[w] = w < s_in ? ml_sh[w0 + w][0][row] : -INFINITY;
+        M = fmaxf(M, mr[w]);
+      }
+      float L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f[r][w] = (mr[w] == -INFINITY) ? 0.f : expf(mr[w] - M);
+        if (w < s_in) L = fmaf(f[r][w], ml_sh[w0 + w][1][row], L);
+      }
+      rm[r] = M;
+      rl[r] = L;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      if (c % s_in != sin) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = 0.f;
-        for (int w = 0; w < s_in; ++w) {
-          const float f = __shfl(wgt[w], 4 * kb + r, 64);
-          v += f * o_sh[wave + w][(4 * kb + r) * HD + 16 * c + l16];
-        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          if (w < s_in) v = fmaf(f[r][w], o_sh[w0 + w][(4 * kb + r) * OS + 16 * c + l16], v);
         o[c][r] = v;
       }
-    m_run = M;
-    l_run = lsum;
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      rl[r] = __shfl(l_run, 4 * kb + r, 64);
+      rm[r] = __shfl(m_run, 4 * kb + r, 64);
+    }
   }
   if (rgi >= rgroups) return;
 
-  float rl[4], rm[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    rl[r] = __shfl(l_run, 4 * kb + r, 64);
-    rm[r] = __shfl(m_run, 4 * kb + r, 64);
-  }
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int rr = rgi * 16 + 4 * kb + r;
@@ -280,12 +291,14 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
       const float inv = rl[r] > 0.f ? 1.0f / rl[r] : 0.f;
       uint16_t* out = (uint16_t*)a.out + ((long)(qrow0 + qi) * a.hq + hh) * HD;
 #pragma unroll
-      for (int c = 0; c < NC; ++c) out[16 * c + l16] = (uint16_t)f2bf(o[c][r] * inv);
+      for (int c = 0; c < NC; ++c)
+        if (c % s_in == sin) out[16 * c + l16] = (uint16_t)f2bf(o[c][r] * inv);
     } else {
       float* pp = partial_row(a, u, g, rr);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) pp[16 * c + l16] = o[c][r];
-      if (l16 == 0) { pp[HD] = rm[r]; pp[HD + 1] = rl[r]; }
+      for (int c = 0; c < NC; ++c)
+        if (c % s_in == sin) pp[16 * c + l16] = o[c][r];
+      if (sin == 0 && l16 == 0) { pp[HD] = rm[r]; pp[HD + 1] = rl[r]; }
     }
   }
 }
@@ -342,32 +355,63 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int nsplit, int b
   }
 }
 
+// Combine of an item's units for one (KV head, row): the units' maxima and
+// weights exp(m_s - M) first (weights kept in LDS), then blockDim / hd thread
+// groups each sum a strided subset of the units for one output element per
+// thread, and the groups add in a fixed order.
+constexpr int kCombineMaxUnits = 4096;
 template <bool BF>
-__global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a, int nsplit) {
+__global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
+  __shared__ float w_sh[kCombineMaxUnits];
+  __shared__ float red[2][16];
+  __shared__ float acc_sh[1024];
   const int item = a.unit_start ? a.split_items[blockIdx.x] : blockIdx.x;
   const int g = blockIdx.y, r = blockIdx.z;
   const int grp = a.hq / a.hkv, hd = a.hd;
   const int qc = a.item_q_count[item];
   if (r >= grp * qc) return;
   const int u0 = a.unit_start ? a.unit_start[item] : item * nsplit;
-  if (a.unit_start) nsplit = a.unit_start[item + 1] - u0;
-  if (nsplit == 1) return;  // written directly by its only unit
+  const int nu = a.unit_start ? a.unit_start[item + 1] - u0 : nsplit;
+  if (nu == 1) return;  // written directly by its only unit
   const long stride_sp = (long)a.hkv * (grp * a.max_q_count) * (hd + 2);
   const float* base = partial_row(a, u0, g, r);
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < nu; s += nt) mx = fmaxf(mx, base[s * stride_sp + hd]);
+  mx = wave_max(mx);
+  if (lane == 0) red[0][wave] = mx;
+  __syncthreads();
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[s * stride_sp + hd]);
-  const int e = threadIdx.x;
-  if (e >= hd) return;
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = base[s * stride_sp + hd];
-      if (ms == -INFINITY) continue;
-      const float w = expf(ms - M);
-      num = fmaf(w, base[s * stride_sp + e], num);
-      den = fmaf(w, base[s * stride_sp + hd + 1], den);
-    }
+  for (int w = 0; w < nw; ++w) M = fmaxf(M, red[0][w]);
+  float dl = 0.f;
+  for (int s = tid; s < nu; s += nt) {
+    const float ms = base[s * stride_sp + hd];
+    const float wt = (ms == -INFINITY) ? 0.f : expf(ms - M);
+    w_sh[s] = wt;
+    dl = fmaf(wt, base[s * stride_sp + hd + 1], dl);
   }
+  dl = wave_sum(dl);
+  if (lane == 0) red[1][wave] = dl;
+  __syncthreads();
+  float den = 0.f;
+  for (int w = 0; w < nw; ++w) den += red[1][w];
+
+  const int ng = nt / hd, gi = tid / hd, e = tid - gi * hd;
+  float num = 0.f;
+  int s = gi;
+  for (; s + 7 * ng < nu; s += 8 * ng) {
+    float p[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[j] = base[(s + j * ng) * stride_sp + e];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) num = fmaf(w_sh[s + j * ng], p[j], num);
+  }
+  for (; s < nu; s += ng) num = fmaf(w_sh[s], base[s * stride_sp + e], num);
+  acc_sh[tid] = num;
+  __syncthreads();
+  if (gi != 0) return;
+  for (int k = 1; k < ng; ++k) num += acc_sh[k * hd + e];
   const int qi = r / grp, hh = g * grp + (r - qi * grp);
   const long o = ((long)(a.item_q_row0[item] + qi) * a.hq + hh) * hd + e;
   typedef typename Act<BF>::T T;
@@ -397,6 +441,7 @@ int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined
   nsplit = (maxblk + bps - 1) / bps;
   const long units = a.unit_start ? (long)a.n_units : (long)a.n_items * nsplit;
   const bool combine = a.unit_start ? a.n_split > 0 : nsplit > 1;
+  if (combine && (a.unit_start ? (maxblk + 7) / 8 : nsplit) > kCombineMaxUnits) return -1;
   if (combine) {
     const size_t need = (size_t)units * a.hkv * grp * a.max_q_count * (a.hd + 2);
     if (need > a.ws_floats) return -2;
@@ -414,9 +459,13 @@ int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined
   if (hipGetLastError() != hipSuccess) return -3;
   }
   if (combine && phase != 1) {
+    // threads: hd per group, about one group per 8 units of the largest item
+    const int mu = a.unit_start ? (a.max_units > 0 ? a.max_units : (maxblk + 7) / 8) : nsplit;
+    int ngr = 1;
+    while (ngr < 1024 / a.hd && ngr * 8 < mu) ngr *= 2;
     dim3 g2(a.unit_start ? a.n_split : a.n_items, a.hkv, grp * a.max_q_count);
-    if (a.bf16) hipLaunchKernelGGL(k_attn_combine<true>, g2, dim3(128), 0, st, a, nsplit);
-    else hipLaunchKernelGGL(k_attn_combine<false>, g2, dim3(128), 0, st, a, nsplit);
+    if (a.bf16) hipLaunchKernelGGL(k_attn_combine<true>, g2, dim3(ngr * a.hd), 0, st, a, nsplit);
+    else hipLaunchKernelGGL(k_attn_combine<false>, g2, dim3(ngr * a.hd), 0, st, a, nsplit);
     if (hipGetLastError() != hipSuccess) return -3;
   }
   return 0;

@@ -129,6 +129,7 @@ struct AttnArgs {
   // item gets the same split count.
   const int32_t* unit_start;
   int n_units;
+  int max_units;             // most units of one item (0: unknown, bounded from max_ctx)
   // Items that have more than one unit (they alone need the combine); with a
   // unit table, null means none.
   const int32_t* split_items;
