@@ -353,6 +353,9 @@ def main():
                          "sd_steps": st["sd_steps"], "ar_steps": st["ar_steps"],
                          "effective_length": round(st["effective_length"], 4),
                          "effective_percent": round(st["effective_percent"], 4)}
+    cm = eng.cost_model()
+    out["controller"] = {"hbm_gbs": round(cm["hbm_bytes_per_s"] / 1e9, 1), "tflops": round(cm["flops_per_s"] / 1e12, 1),
+                         "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3)}
     out["prefill_s"] = round(main_run["prefill_s"], 3)
     out["by_batch"] = {m: bins(r["recs"]) for m, r in res.items()}
     out["kernels_top"] = kernel_table(main_run["kprof"])[:8]

@@ -63,7 +63,9 @@ extern "C" {
 #define ER_W8_PERCH_SYM  0   /* int8 codes, one fp32 scale per output row */
 #define ER_W4_G128_ASYM  1   /* 4-bit codes, bf16 scale + u8 zero per row and 128 inputs */
 
-#define ER_POLICY_AUTO      0   /* roofline toggle + adaptive gamma */
+#define ER_POLICY_AUTO      0   /* roofline toggle + adaptive gamma; while it stays
+                                   autoregressive where alpha_init would make speculation
+                                   pay, every 32nd step speculates to refresh the EMA */
 #define ER_POLICY_FORCE_SD  1   /* always speculate (gamma adaptive unless pinned) */
 #define ER_POLICY_FORCE_AR  2   /* never speculate */
 
@@ -108,7 +110,8 @@ typedef struct er_rollout_desc {
   int32_t prefill_chunk;    /* max prompt tokens per prefill forward */
   int64_t kv_pool_blocks;   /* 0: every block the arena can hold after the other buffers */
   double hbm_bytes_per_s;   /* roofline constants; <= 0: measured at init */
-  double flops_per_s;
+  double flops_per_s;       /* <= 0: the rate a target forward over 512 rows reaches, measured at
+                               init (2.5e15 if that forward stays bound by the weight stream) */
   double t_fwd_s;           /* fixed time per forward (launch overhead); < 0: measured at init */
 } er_rollout_desc;
 
@@ -235,6 +238,8 @@ int er_kv_free(er_ctx *ctx, int n, const int32_t *seq_ids);
 int er_seq_info(er_ctx *ctx, int32_t seq_id, int32_t *generated, int32_t *context_len, int32_t *finished);
 
 int er_get_stats(er_ctx *ctx, er_stats *out);
+/* Clear the counters and restart the controller: acceptance EMA back to
+ * alpha_init, no current choice. */
 int er_reset_stats(er_ctx *ctx);
 
 /* Record device time per phase for every `period`-th step and the first
@@ -292,6 +297,9 @@ typedef struct er_cost_model {
 int er_controller_choose(const er_cost_model *m, int batch, double mean_ctx, double alpha,
                          int gamma_min, int gamma_max, int current, double margin, int *gamma_out);
 double er_expected_tokens(double alpha, int gamma);
+/* The cost model a context's controller uses (roofline constants as given or
+ * as calibrated at init). */
+int er_get_cost_model(const er_ctx *ctx, er_cost_model *out);
 
 const char *er_last_error(const er_ctx *ctx);
 void er_destroy(er_ctx *ctx);

@@ -124,6 +124,7 @@ SIGNATURES = {
     "er_controller_choose": (C.c_int, [C.POINTER(CostModel), C.c_int, C.c_double, C.c_double, C.c_int, C.c_int,
                                        C.c_int, C.c_double, C.POINTER(C.c_int)]),
     "er_expected_tokens": (C.c_double, [C.c_double, C.c_int]),
+    "er_get_cost_model": (C.c_int, [P, C.POINTER(CostModel)]),
     "er_last_error": (C.c_char_p, [P]),
     "er_destroy": (None, [P]),
     # er_ops.h

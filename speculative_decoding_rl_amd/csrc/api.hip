@@ -159,8 +159,10 @@ struct er_ctx {
   // controller
   CostModel cost{};
   double alpha_ema = 0.8;
+  double alpha_init = 0.8;
   int gamma_pinned = 0;
   int choice = -1;        // last controller choice (0 = AR), -1 none yet
+  int ar_streak = 0;      // consecutive autoregressive steps chosen by the controller
   int policy = ER_POLICY_AUTO;
 
   er_stats stats{};
@@ -1051,6 +1053,8 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   return ER_OK;
 }
 
+constexpr int kAlphaProbe = 32;
+
 // Controller choice for this batch (0 = AR).
 int plan(er_ctx* c, int n, const int32_t* ids) {
   if (c->policy == ER_POLICY_FORCE_AR) return 0;
@@ -1063,7 +1067,18 @@ int plan(er_ctx* c, int n, const int32_t* ids) {
   const int cur = c->choice;
   const int g = choose(c->cost, n, C, c->alpha_ema, lo, hi, allow_ar, cur, c->rd.switch_margin);
   c->choice = g;
-  return g;
+  if (g > 0 || !allow_ar) {
+    c->ar_streak = 0;
+    return g;
+  }
+  // The acceptance estimate only moves on speculative steps.  While the
+  // controller stays autoregressive in a regime where the initial estimate
+  // would make speculation pay, one speculative step every kAlphaProbe steps
+  // refreshes it (the choice itself stays AR).
+  if (++c->ar_streak < kAlphaProbe) return 0;
+  c->ar_streak = 0;
+  if (choose(c->cost, n, C, c->alpha_init, lo, hi, true, -1, 1.0) == 0) return 0;
+  return choose(c->cost, n, C, c->alpha_ema, lo, hi, false, -1, 1.0);
 }
 
 int current_gamma(er_ctx* c) {
@@ -1088,7 +1103,7 @@ int calibrate(er_ctx* c) {
   c->cost.q_bytes = c->dd.quant == ER_W8_PERCH_SYM ? 1.0 : 0.5 + 3.0 / 128.0;
   c->cost.kv_bytes_el = c->bf16 ? 2.0 : 4.0;
   c->cost.bw = c->rd.hbm_bytes_per_s > 0 ? c->rd.hbm_bytes_per_s : 0.0;
-  c->cost.flops = c->rd.flops_per_s > 0 ? c->rd.flops_per_s : 2.5e15;
+  c->cost.flops = c->rd.flops_per_s > 0 ? c->rd.flops_per_s : 2.5e15;  // replaced by the measurement below
   c->cost.t_fwd = c->rd.t_fwd_s >= 0 ? c->rd.t_fwd_s : 0.0;
   if (c->cost.bw <= 0) {
     const size_t bytes = std::min((size_t)1 << 30, (size_t)c->pool.total() * c->block_bytes) & ~(size_t)4095;
@@ -1169,6 +1184,91 @@ int calibrate(er_ctx* c) {
     const double td = times[1] - c->cost.q_bytes * P / c->cost.bw;
     c->cost.t_fwd = std::max(0.0, 0.5 * (tt + td));
   }
+  if (c->rd.flops_per_s <= 0) {
+    // Dense-contraction rate the kernels reach: a target forward over Mc
+    // prompt-like rows of one throwaway sequence (positions 0..Mc-1), logits
+    // for every row, timed beyond the fixed time and the weight stream.
+    const int grp = (int)(m.n_q_heads / m.n_kv_heads);
+    const int qmax = std::max(1, 64 / grp);
+    const int Mc = std::min(512, std::min(c->max_rows, c->logit_rows));
+    BlockTable bt;
+    if (Mc >= 64 && c->pool.free_count() >= (Mc + KV_BLOCK - 1) / KV_BLOCK &&
+        bt.reserve(c->pool, Mc)) {
+      const int nb = (int)bt.blocks.size();
+      const int n_items = (Mc + qmax - 1) / qmax;
+      Meta& M = c->meta;
+      M.reset();
+      size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ip, o_ic;
+      int32_t* t = M.push<int32_t>(Mc, &o_tok);
+      int32_t* p = M.push<int32_t>(Mc, &o_pos);
+      int64_t* sl = M.push<int64_t>(Mc, &o_slot);
+      int32_t* btp = M.push<int32_t>(nb, &o_bt);
+      int32_t* ib = M.push<int32_t>(n_items, &o_ib);
+      int32_t* ir = M.push<int32_t>(n_items, &o_ir);
+      int32_t* ip = M.push<int32_t>(n_items, &o_ip);
+      int32_t* ic = M.push<int32_t>(n_items, &o_ic);
+      if (M.ok) {
+        for (int i = 0; i < Mc; ++i) {
+          t[i] = i % m.vocab;
+          p[i] = i;
+          sl[i] = (int64_t)bt.blocks[i / KV_BLOCK] * KV_BLOCK + i % KV_BLOCK;
+        }
+        for (int b = 0; b < nb; ++b) btp[b] = bt.blocks[b];
+        for (int k = 0; k < n_items; ++k) {
+          ib[k] = 0;
+          ir[k] = k * qmax;
+          ip[k] = k * qmax;
+          ic[k] = std::min(qmax, Mc - k * qmax);
+        }
+        int n_units = 0, n_split = 0, max_units = 0;
+        const size_t o_us = push_units(M, n_items, (int)m.n_kv_heads, ip, ic, &n_units, &n_split, &max_units);
+        if (M.ok) {
+          HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+          Fwd f;
+          f.M = Mc;
+          f.tokens = M.dev<int32_t>(o_tok);
+          f.pos = M.dev<int32_t>(o_pos);
+          f.slot = M.dev<int64_t>(o_slot);
+          f.bt = M.dev<int32_t>(o_bt);
+          f.bt_stride = nb;
+          f.it_bt = M.dev<int32_t>(o_ib);
+          f.it_row0 = M.dev<int32_t>(o_ir);
+          f.it_pos0 = M.dev<int32_t>(o_ip);
+          f.it_cnt = M.dev<int32_t>(o_ic);
+          f.n_items = n_items;
+          f.max_q = qmax;
+          f.max_ctx = Mc;
+          f.unit_start = M.dev<int32_t>(o_us);
+          f.n_units = n_units;
+          f.n_split = n_split;
+          f.max_units = max_units;
+          f.logits = c->logits_p;
+          f.ldl = m.vocab;
+          hipEvent_t a, b;
+          HIPC(c, hipEventCreate(&a));
+          HIPC(c, hipEventCreate(&b));
+          int r = forward(c, f);  // warm
+          if (!r) {
+            HIPC(c, hipEventRecord(a, c->st));
+            for (int i = 0; i < 2 && !r; ++i) r = forward(c, f);
+            HIPC(c, hipEventRecord(b, c->st));
+            HIPC(c, hipEventSynchronize(b));
+          }
+          float ms = 0.f;
+          if (!r) HIPC(c, hipEventElapsedTime(&ms, a, b));
+          (void)hipEventDestroy(a);
+          (void)hipEventDestroy(b);
+          if (r) { bt.release(c->pool); return r; }
+          const double T = ms / 2.0 * 1e-3;
+          const double P = c->cost.p_lin();
+          const double busy = T - c->cost.t_fwd;
+          // above the weight stream: compute-bound at Mc rows, take the rate
+          if (busy > c->cost.w_bytes * P / c->cost.bw) c->cost.flops = 2.0 * P * Mc / busy;
+        }
+      }
+      bt.release(c->pool);
+    }
+  }
   return ER_OK;
 }
 
@@ -1217,6 +1317,7 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->arena_bytes = arena_bytes;
     c->policy = rollout->policy;
     c->alpha_ema = rollout->alpha_init > 0 ? rollout->alpha_init : 0.8;
+    c->alpha_init = c->alpha_ema;
     Layout L;
     make_layout(*model, *draft, *rollout, &L, &why);
     const size_t fixed = L.total_fixed() + 4096;
@@ -1715,6 +1816,9 @@ int er_get_stats(er_ctx* c, er_stats* out) {
 int er_reset_stats(er_ctx* c) {
   if (!c) return ER_EINVAL;
   c->stats = er_stats{};
+  c->alpha_ema = c->alpha_init;
+  c->choice = -1;
+  c->ar_streak = 0;
   return ER_OK;
 }
 
@@ -1826,6 +1930,14 @@ int er_controller_choose(const er_cost_model* m, int batch, double mean_ctx, dou
 }
 
 double er_expected_tokens(double alpha, int gamma) { return expected_tokens(alpha, gamma); }
+
+int er_get_cost_model(const er_ctx* c, er_cost_model* out) {
+  if (!c || !out) return ER_EINVAL;
+  const CostModel& m = c->cost;
+  *out = er_cost_model{m.n_layers, m.d_model, m.n_q_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab,
+                       m.w_bytes, m.q_bytes, m.kv_bytes_el, m.bw, m.flops, m.t_fwd};
+  return ER_OK;
+}
 
 const char* er_last_error(const er_ctx* c) { return c ? c->err.c_str() : "null context"; }
 

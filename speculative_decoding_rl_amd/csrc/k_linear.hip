@@ -1269,7 +1269,9 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
   for (int v = 0; v < WV; ++v) {
     const int e = tid + 512 * v, row = e >> 3;
     wok[v] = n0 + row < N;
-    wsrc[v] = wok[v] ? (long)phys_row(a, (n0 >> 4) + (row >> 4), row & 15) * K + (e & 7) * 8 : 0;
+    // rows past the end load row N-1 (always in bounds) and are zeroed when stashed
+    const int nr = wok[v] ? n0 + row : N - 1;
+    wsrc[v] = (long)phys_row(a, nr >> 4, nr & 15) * K + (e & 7) * 8;
   }
   long xsrc[XV];
   bool xok[XV];
@@ -1278,27 +1280,39 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
     const int e = tid + 512 * v, row = e >> 3;
     const int m = m0 + row;
     xok[v] = m < M;
-    xsrc[v] = xok[v] ? (long)(a.xrow ? a.xrow[m] : m) * a.ldx + (e & 7) * 8 : 0;
+    const int mr = xok[v] ? m : M - 1;
+    xsrc[v] = (long)(a.xrow ? a.xrow[mr] : mr) * a.ldx + (e & 7) * 8;
   }
 
   uint4 wr[DEPTH][WV], xr[DEPTH][XV];
+  // Loads are unpredicated (clamped rows, a clamped step index): exec-masked
+  // loads inside the ring make the compiler drain the whole load counter at
+  // every use instead of waiting for the oldest stage only.
   auto issue = [&](int t, int slot) {
     const long k0 = (long)(s0 + t) * BK;
 #pragma unroll
-    for (int v = 0; v < XV; ++v) xr[slot][v] = xok[v] ? *(const uint4*)(X + xsrc[v] + k0) : uint4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < XV; ++v) xr[slot][v] = *(const uint4*)(X + xsrc[v] + k0);
 #pragma unroll
-    for (int v = 0; v < WV; ++v) wr[slot][v] = wok[v] ? *(const uint4*)(W + wsrc[v] + k0) : uint4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < WV; ++v) wr[slot][v] = *(const uint4*)(W + wsrc[v] + k0);
   };
+  // out-of-range rows are cleared with a mask (a select here would become a
+  // select of addresses and push the ring into scratch memory)
+  uint32_t xmask[XV], wmask[WV];
+#pragma unroll
+  for (int v = 0; v < XV; ++v) xmask[v] = xok[v] ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int v = 0; v < WV; ++v) wmask[v] = wok[v] ? 0xFFFFFFFFu : 0u;
+  auto and4 = [](uint4 q, uint32_t m) { return uint4{q.x & m, q.y & m, q.z & m, q.w & m}; };
   auto stash = [&](int slot, int buf) {
 #pragma unroll
     for (int v = 0; v < XV; ++v) {
       const int e = tid + 512 * v;
-      *(uint4*)(&As[buf][(e >> 3) * LDA + (e & 7) * 8]) = xr[slot][v];
+      *(uint4*)(&As[buf][(e >> 3) * LDA + (e & 7) * 8]) = and4(xr[slot][v], xmask[v]);
     }
 #pragma unroll
     for (int v = 0; v < WV; ++v) {
       const int e = tid + 512 * v;
-      *(uint4*)(&Bs[buf][(e >> 3) * LDA + (e & 7) * 8]) = wr[slot][v];
+      *(uint4*)(&Bs[buf][(e >> 3) * LDA + (e & 7) * 8]) = and4(wr[slot][v], wmask[v]);
     }
   };
 
@@ -1326,21 +1340,35 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
   };
 
   if (T > 0) {
+    const int tl = T - 1;
 #pragma unroll
     for (int d = 0; d < DEPTH - 1; ++d)
       if (d < T) issue(d, d);
     stash(0, 0);
     __syncthreads();
-    for (int t0 = 0; t0 < T; t0 += 2 * DEPTH) {
+    // Whole groups of 2 * DEPTH steps run without any condition, so that the
+    // load counter is the same on every path and each stash waits for its
+    // own stage only.  Re-issues of the last stage and the stash after the
+    // last step touch data nobody reads.
+    int t0 = 0;
+    for (; t0 + 2 * DEPTH <= T; t0 += 2 * DEPTH) {
 #pragma unroll
       for (int d = 0; d < 2 * DEPTH; ++d) {
-        const int t = t0 + d;
-        if (t < T) {
-          if (t + DEPTH - 1 < T) issue(t + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
-          mma(d & 1);
-          if (t + 1 < T) stash((d + 1) % DEPTH, (d + 1) & 1);
-          lds_barrier();
-        }
+        issue(min(t0 + d + DEPTH - 1, tl), (d + DEPTH - 1) % DEPTH);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the math
+        mma(d & 1);
+        stash((d + 1) % DEPTH, (d + 1) & 1);
+        lds_barrier();
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < 2 * DEPTH; ++d) {
+      const int t = t0 + d;
+      if (t < T) {
+        if (t + DEPTH - 1 < T) issue(t + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+        mma(d & 1);
+        if (t + 1 < T) stash((d + 1) % DEPTH, (d + 1) & 1);
+        lds_barrier();
       }
     }
   }
@@ -1500,9 +1528,13 @@ static int dispatch_skinny(const LinArgs& a, hipStream_t st, LinearInfo* info) {
 }
 
 // Automatic kernel choice (bf16 weights by M; the quantized drafter formats
-// use the streaming kernel while x' fits in LDS).  Sizes from sweeps of the
+// use the streaming kernel while x' fits in LDS).  From sweeps of the
 // Qwen2.5-7B projections on MI355X with weights rotating through more than the
-// 256 MB last-level cache.
+// 256 MB last-level cache: the streaming kernel up to M = 8 (and for the
+// narrower layers up to 16), the deep-pipelined GEMM for long K and for the
+// vocabulary projection from M = 9 and for everything from M = 33, the
+// weight-streaming GEMM for the wide layers in between, and the register-fed
+// kernel for the square attention output projection up to M = 32.
 enum Plan { P_STREAM, P_SKINNY_OLD, P_WGEMM, P_GEMM2, P_GEMM };
 
 static Plan plan_of(const LinArgs& a) {
@@ -1514,11 +1546,15 @@ static Plan plan_of(const LinArgs& a) {
     if (M <= 8 || N >= 65536 || (N >= 16384 && M <= 12)) return P_STREAM;
     return P_SKINNY_OLD;
   }
-  if (M <= 8) return stream_fits ? P_STREAM : P_SKINNY_OLD;
-  if (M <= 16) return (stream_fits && N >= 4096) ? P_STREAM : P_SKINNY_OLD;
+  if (M <= 8 && stream_fits) return P_STREAM;
   if (K % 64) return P_SKINNY_OLD;
-  if (M <= 32) return N < 4096 ? P_SKINNY_OLD : P_WGEMM;
-  if (M <= 64) return (N >= 16384 || K >= 8192) ? P_GEMM2 : P_WGEMM;
+  if (M <= 8) return P_GEMM2;  // long K (x' does not fit in LDS)
+  if (M <= 32) {
+    if (N < 4096) return K >= 8192 ? P_GEMM2 : P_SKINNY_OLD;
+    if (N >= 65536) return P_GEMM2;
+    if (M <= 16 && N < 16384 && stream_fits) return P_STREAM;
+    return P_WGEMM;
+  }
   if (M <= 256) return P_GEMM2;
   return P_GEMM;
 }
@@ -1554,14 +1590,16 @@ static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st
       }
       return -1;
     case P_WGEMM:
-      if (M <= 32) return (N >= 16384 || K >= 8192) ? run_wgemm<2, 1, 2, 3>(a, ws, 512, st, info)
-                                                   : run_wgemm<2, 1, 4, 3>(a, ws, 512, st, info);
+      if (M <= 32) return run_wgemm<2, 1, 4, 3>(a, ws, 512, st, info);
       return run_wgemm<4, 1, 1, 3>(a, ws, 512, st, info);
     case P_GEMM2:
-      if (M <= 64) return run_gemm2<64, 1, 4>(a, ws, 512, st, info);
-      if (M <= 128) return N < 4096 ? run_gemm2<64, 1, 6>(a, ws, 512, st, info)
-                                    : run_gemm2<128, 2, 3>(a, ws, 512, st, info);
-      return K >= 8192 ? run_gemm2<256, 4, 3>(a, ws, 512, st, info) : run_gemm2<256, 4, 4>(a, ws, 512, st, info);
+      if (M <= 64) return run_gemm2<64, 1, 4>(a, ws, 256, st, info);
+      if (M <= 128) {
+        if (K < 8192 && (N < 4096 || (N >= 16384 && N < 65536))) return run_gemm2<64, 1, 6>(a, ws, 512, st, info);
+        return run_gemm2<128, 2, 3>(a, ws, 512, st, info);
+      }
+      if (K >= 8192 || N >= 65536) return run_gemm2<256, 4, 3>(a, ws, 512, st, info);
+      return run_gemm2<128, 2, 4>(a, ws, 512, st, info);
     case P_GEMM:
       return run_gemm(a, ws, st, info);
     case P_SKINNY_OLD:

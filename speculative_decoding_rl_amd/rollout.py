@@ -180,6 +180,11 @@ class Engine:
     def reset_stats(self):
         check(self.lib.er_reset_stats(self.ctx), self.ctx, "er_reset_stats")
 
+    def cost_model(self) -> dict:
+        m = _lib.CostModel()
+        check(self.lib.er_get_cost_model(self.ctx, C.byref(m)), self.ctx, "er_get_cost_model")
+        return {f: getattr(m, f) for f, _ in m._fields_}
+
     def set_fused(self, on: bool):
         check(self.lib.er_set_fused(self.ctx, int(bool(on))), self.ctx, "er_set_fused")
 
