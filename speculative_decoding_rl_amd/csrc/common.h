@@ -93,3 +93,6 @@ ER_DEV void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Index of this wave in its work-group, known to the compiler to be
+// wave-uniform (so that branches and addresses derived from it stay scalar).
+ER_DEV int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

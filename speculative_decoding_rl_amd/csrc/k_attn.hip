@@ -82,7 +82,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   if (a.unit_start && u >= a.n_units) return;
   const Unit w = unit_of(a, u, nsplit, bps);
   const int item = w.item;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index through readfirstlane, so that everything derived from it
+  // (this wave's block list, its block-id loads) is known to be wave-uniform
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kb = lane >> 4;
   const int grp = a.hq / a.hkv;
   const int qc = a.item_q_count[item];
@@ -129,41 +131,30 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   const int32_t* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
 
   if (rgi < rgroups) {
-    // This wave's blocks are b0 + sin + s_in * t.  Their physical ids are read
-    // 64 at a time into one register per lane and broadcast with readlane, so
-    // that loading a block's K and V never waits on its block-table entry.
-    int bt_win = 0;
-    auto refill = [&](int t) {
-      const int blk = b0 + sin + s_in * (t + lane);
-      bt_win = blk < b1 ? bt[blk] : 0;
-    };
-    // K and V fragments of the next block are loaded while the current one
-    // is scored (register double buffer)
-    uint4 kn[NQ];
-    uint2 vn[NC];
-    auto fetch = [&](int t) {
-      const long phys = __builtin_amdgcn_readlane(bt_win, t & 63);
+    // This wave's blocks are first + s_in * t, t < nb.  Their K and V
+    // fragments go through a ring of D register stages (loads of blocks t+1
+    // and t+2 are in flight while block t is scored); the block ids come from
+    // scalar loads one iteration ahead.  Every load is unconditional (indices
+    // clamped to the last block): conditional loads would make the compiler
+    // drain the whole load counter at each use.
+    constexpr int D = 3;
+    const int first = b0 + sin;
+    const int nb = first < b1 ? (b1 - first + s_in - 1) / s_in : 0;
+    const int tl = nb > 0 ? nb - 1 : 0;
+    uint4 kq[D][NQ];
+    uint2 vq[D][NC];
+    auto bid = [&](int t) -> long { return (long)bt[first + s_in * min(t, tl)]; };
+    auto fetch = [&](int slot, long phys) {
       const uint16_t* kp = pool + kv_block_base(phys, a.layer, a.n_layers, 0, a.hkv, g, HD);
       const uint16_t* vp = pool + kv_block_base(phys, a.layer, a.n_layers, 1, a.hkv, g, HD);
 #pragma unroll
-      for (int i = 0; i < NQ; ++i) kn[i] = *(const uint4*)(kp + l16 * HD + 32 * i + 8 * kb);
+      for (int i = 0; i < NQ; ++i) kq[slot][i] = *(const uint4*)(kp + l16 * HD + 32 * i + 8 * kb);
 #pragma unroll
-      for (int c = 0; c < NC; ++c) vn[c] = *(const uint2*)(vp + (16 * c + l16) * 16 + 4 * kb);
+      for (int c = 0; c < NC; ++c) vq[slot][c] = *(const uint2*)(vp + (16 * c + l16) * 16 + 4 * kb);
     };
-    refill(0);
-    if (b0 + sin < b1) fetch(0);
-    int t = 0;
-    for (int blk = b0 + sin; blk < b1; blk += s_in, ++t) {
-      uint4 kc[NQ];
-      uint2 vc[NC];
-#pragma unroll
-      for (int i = 0; i < NQ; ++i) kc[i] = kn[i];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) vc[c] = vn[c];
-      if (blk + s_in < b1) {
-        if (((t + 1) & 63) == 0) refill(t + 1);
-        fetch(t + 1);
-      }
+    auto process = [&](int slot, int blk) {
+      const uint4* kc = kq[slot];
+      const uint2* vc = vq[slot];
       // S^T = K . Q^T: A = K rows (token l16), k = 8*kb + 32*i
       f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -226,6 +217,20 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
         const bf16x4s_t vf = __builtin_bit_cast(bf16x4s_t, vc[c]);
         o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[c], 0, 0, 0);
         o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb, vf, o[c], 0, 0, 0);
+      }
+    };
+    if (nb > 0) {
+      fetch(0, bid(0));
+      fetch(1, bid(1));
+      long idn = bid(2);
+      for (int t0 = 0; t0 < nb; t0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          const int t = t0 + d;
+          fetch((d + 2) % D, idn);  // block t + 2 (re-loads of the last block past the end)
+          idn = bid(t + 3);
+          if (t < nb) process(d, first + s_in * t);
+        }
       }
     }
   }

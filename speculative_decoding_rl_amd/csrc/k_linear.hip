@@ -121,9 +121,16 @@ ER_DEV bf16x8_t w8_to_bf16(uint32_t a, uint32_t b) {
 // One kernel-order W4 word (8 codes) -> bf16 of (q + 128), exact: the code
 // lands in the mantissa of 128.0.
 ER_DEV bf16x8_t w4_to_bf16(uint32_t w) {
+  // (w >> 4j) & 0x000F000F | 0x43004300.  The two constants come from
+  // opaque moves (mask in an SGPR, magic in a VGPR) so that the compiler
+  // selects one v_and_or_b32 per word instead of an and + an or with literal
+  // operands; the arithmetic itself stays plain code.
+  uint32_t mask, magic;
+  asm("s_mov_b32 %0, 0x000F000F" : "=s"(mask));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(magic));
   uint32_t r[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = ((w >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+  for (int j = 0; j < 4; ++j) r[j] = ((w >> (4 * j)) & mask) | magic;
   return __builtin_bit_cast(bf16x8_t, *(const uint4*)r);
 }
 
@@ -248,7 +255,7 @@ __global__ __launch_bounds__(512) void k_linear_mfma(LinArgs a, int mtiles) {
   const int mt = L % mtiles;
   const int nt = L / mtiles;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rg = wave / KS, ks = wave % KS;
   const int kb = lane >> 4, l16 = lane & 15;
   const int m0 = mt * MT;
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(LinArgs a, float* __restrict_
   const int nt = t2 / nsplit;
   const int M = a.M, N = a.W.N, K = a.W.K;
   const int m0 = mt * GB_M, n0 = nt * GB_N;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int kb = lane >> 4, l16 = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
   const int nsteps = K / GB_K;
@@ -718,7 +725,7 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
   const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
   const int nt = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rg = wave / KS, ks = wave % KS;
   const int kb = lane >> 4, l16 = lane & 15;
   const long G = K >> 7;
@@ -831,24 +838,50 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
   for (int d = 0; d < DEPTH - 1; ++d) issue(min(d, last_it), d);
 
   {
-    const int K8 = K >> 3;
-    for (int e = tid; e < M * K8; e += 512) {
-      const int m = e / K8, k8 = e - m * K8;
-      const long hrow = a.xrow ? a.xrow[m] : m;
-      uint4 v;
-      if (a.xnorm) v = load_x8(a, hrow, rstd_of(a, hrow), (long)k8 * 8);
-      else v = *(const uint4*)((const uint16_t*)a.x + hrow * a.ldx + (long)k8 * 8);
-      *(uint4*)(xs + m * ldsx + k8 * 8) = v;
+    // x' fill: four 16-byte pieces per thread in flight at once
+    const int K8 = K >> 3, tot = M * K8;
+    for (int e0 = 0; e0 < tot; e0 += 4 * 512) {
+      uint4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = min(e0 + tid + 512 * j, tot - 1);
+        const int m = e / K8, k8 = e - m * K8;
+        const long hrow = a.xrow ? a.xrow[m] : m;
+        if (a.xnorm) v[j] = load_x8(a, hrow, rstd_of(a, hrow), (long)k8 * 8);
+        else v[j] = *(const uint4*)((const uint16_t*)a.x + hrow * a.ldx + (long)k8 * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + tid + 512 * j;
+        if (e < tot) {
+          const int m = e / K8, k8 = e - m * K8;
+          *(uint4*)(xs + m * ldsx + k8 * 8) = v[j];
+        }
+      }
     }
     if constexpr (FMT == FMT_W4) {
-      // this work-group's rows: logical subtile (nt*RG + rg')*NR + ni, lane row l16
+      // this work-group's rows: logical subtile (nt*RG + rg')*NR + ni, lane row
+      // l16; eight entries per thread in flight at once (a plain loop would
+      // wait out one load latency per entry)
       const int rows = 16 * NR * RG;
-      for (int e = tid; e < rows * nchunks; e += 512) {
-        const int rr = e / nchunks, c = e - rr * nchunks;
-        const int s2 = nt * RG * NR + (rr >> 4);
-        const int l = rr & 15;
-        const long n = (16 * s2 + l < N) ? phys_row(a, s2, l) : N - 1;
-        szl[e] = make_float2(bf2f(((const uint16_t*)sv)[n * G + c]), 128.0f + (float)((const uint8_t*)zv)[n * G + c]);
+      const int total = rows * nchunks;
+      for (int e0 = 0; e0 < total; e0 += 8 * 512) {
+        uint32_t sc[8], zc[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = min(e0 + tid + 512 * j, total - 1);
+          const int rr = e / nchunks, c = e - rr * nchunks;
+          const int s2 = nt * RG * NR + (rr >> 4);
+          const int l = rr & 15;
+          const long n = (16 * s2 + l < N) ? phys_row(a, s2, l) : N - 1;
+          sc[j] = ((const uint16_t*)sv)[n * G + c];
+          zc[j] = ((const uint8_t*)zv)[n * G + c];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int e = e0 + tid + 512 * j;
+          if (e < total) szl[e] = make_float2(bf2f((uint16_t)sc[j]), 128.0f + (float)zc[j]);
+        }
       }
     }
     if constexpr (FMT != FMT_BF16) {
@@ -981,7 +1014,7 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
   const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
   const int L = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
   const int sp = L % nsplit, nt = L / nsplit;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rg = wave / KS, ks = wave % KS;
   const int kb = lane >> 4, l16 = lane & 15;
   const int M = a.M, N = a.W.N, K = a.W.K;
@@ -1249,7 +1282,7 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
   const int nt = t2 / nsplit;
   const int M = a.M, N = a.W.N, K = a.W.K;
   const int m0 = mt * BM, n0 = nt * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int kb = lane >> 4, l16 = lane & 15;
   const int wm = wave / WN, wn = wave % WN;
   const int nsteps = K / BK;
