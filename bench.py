@@ -358,7 +358,7 @@ def main():
                          "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3)}
     out["prefill_s"] = round(main_run["prefill_s"], 3)
     out["by_batch"] = {m: bins(r["recs"]) for m, r in res.items()}
-    out["kernels_top"] = kernel_table(main_run["kprof"])[:8]
+    out["kernels_top"] = kernel_table(main_run["kprof"])
     if rf_detail:
         out["roofline_kernel"] = rf_detail
     if not args.no_cpu_baseline:

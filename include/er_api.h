@@ -65,7 +65,8 @@ extern "C" {
 
 #define ER_POLICY_AUTO      0   /* roofline toggle + adaptive gamma; while it stays
                                    autoregressive where alpha_init would make speculation
-                                   pay, every 32nd step speculates to refresh the EMA */
+                                   pay, a speculative probe step refreshes the EMA (after
+                                   32 steps, the gap doubling to at most 1024) */
 #define ER_POLICY_FORCE_SD  1   /* always speculate (gamma adaptive unless pinned) */
 #define ER_POLICY_FORCE_AR  2   /* never speculate */
 

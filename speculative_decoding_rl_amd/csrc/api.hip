@@ -163,6 +163,7 @@ struct er_ctx {
   int gamma_pinned = 0;
   int choice = -1;        // last controller choice (0 = AR), -1 none yet
   int ar_streak = 0;      // consecutive autoregressive steps chosen by the controller
+  int probe_every = 0;    // autoregressive steps between acceptance probes (0: kAlphaProbe)
   int policy = ER_POLICY_AUTO;
 
   er_stats stats{};
@@ -1054,6 +1055,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
 }
 
 constexpr int kAlphaProbe = 32;
+constexpr int kAlphaProbeMax = 1024;
 
 // Controller choice for this batch (0 = AR).
 int plan(er_ctx* c, int n, const int32_t* ids) {
@@ -1069,15 +1071,20 @@ int plan(er_ctx* c, int n, const int32_t* ids) {
   c->choice = g;
   if (g > 0 || !allow_ar) {
     c->ar_streak = 0;
+    if (g > 0) c->probe_every = kAlphaProbe;
     return g;
   }
   // The acceptance estimate only moves on speculative steps.  While the
   // controller stays autoregressive in a regime where the initial estimate
-  // would make speculation pay, one speculative step every kAlphaProbe steps
-  // refreshes it (the choice itself stays AR).
-  if (++c->ar_streak < kAlphaProbe) return 0;
+  // would make speculation pay, a speculative probe step refreshes it (the
+  // choice itself stays AR).  Probes start kAlphaProbe steps apart and the
+  // gap doubles (up to kAlphaProbeMax) each time the controller stays
+  // autoregressive after one, so a steady low acceptance costs few probes.
+  if (c->probe_every <= 0) c->probe_every = kAlphaProbe;
+  if (++c->ar_streak < c->probe_every) return 0;
   c->ar_streak = 0;
   if (choose(c->cost, n, C, c->alpha_init, lo, hi, true, -1, 1.0) == 0) return 0;
+  c->probe_every = std::min(2 * c->probe_every, kAlphaProbeMax);
   return choose(c->cost, n, C, c->alpha_ema, lo, hi, false, -1, 1.0);
 }
 
@@ -1819,6 +1826,7 @@ int er_reset_stats(er_ctx* c) {
   c->alpha_ema = c->alpha_init;
   c->choice = -1;
   c->ar_streak = 0;
+  c->probe_every = kAlphaProbe;
   return ER_OK;
 }
 
