@@ -1258,7 +1258,7 @@ static int run_wgemm_variant(int code, const LinArgs& a, const LinearWs& ws, hip
 // steps of latency stay hidden.  Split-K partials go through
 // k_splitk_reduce, as for k_gemm_bf16.
 // ----------------------------------------------------------------------------
-template <int BM, int WM, int DEPTH, bool XN>
+template <int BM, int WM, int DEPTH>
 __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ part, int nsplit, int sps, int mtiles) {
   constexpr int BN = 128, BK = 64, LDA = BK + 8;
   constexpr int WN = 8 / WM;
@@ -1306,56 +1306,27 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
     const int nr = wok[v] ? n0 + row : N - 1;
     wsrc[v] = (long)phys_row(a, nr >> 4, nr & 15) * K + (e & 7) * 8;
   }
-  // x' rows of this thread's load slots (XN: RMSNorm(h) * g formed here from
-  // the fp32 residual stream, with the row's 1/rms computed once)
   long xsrc[XV];
   bool xok[XV];
-  float xrs[XV];
 #pragma unroll
   for (int v = 0; v < XV; ++v) {
     const int e = tid + 512 * v, row = e >> 3;
     const int m = m0 + row;
     xok[v] = m < M;
     const int mr = xok[v] ? m : M - 1;
-    const long hrow = a.xrow ? a.xrow[mr] : mr;
-    xsrc[v] = hrow * a.ldx + (e & 7) * 8;
-    xrs[v] = XN ? rstd_of(a, hrow) : 1.f;
+    xsrc[v] = (long)(a.xrow ? a.xrow[mr] : mr) * a.ldx + (e & 7) * 8;
   }
-  constexpr int XP = XN ? 3 : 1;  // 16-byte pieces per x slot: bf16 x, or fp32 h (2) + gain
 
-  uint4 wr[DEPTH][WV], xr[DEPTH][XV][XP];
+  uint4 wr[DEPTH][WV], xr[DEPTH][XV];
   // Loads are unpredicated (clamped rows, a clamped step index): exec-masked
   // loads inside the ring make the compiler drain the whole load counter at
   // every use instead of waiting for the oldest stage only.
   auto issue = [&](int t, int slot) {
     const long k0 = (long)(s0 + t) * BK;
 #pragma unroll
-    for (int v = 0; v < XV; ++v) {
-      if constexpr (XN) {
-        const float* hp = (const float*)a.x + xsrc[v] + k0;
-        xr[slot][v][0] = *(const uint4*)hp;
-        xr[slot][v][1] = *(const uint4*)(hp + 4);
-        xr[slot][v][2] = *(const uint4*)((const uint16_t*)a.gnorm + k0 + ((tid + 512 * v) & 7) * 8);
-      } else {
-        xr[slot][v][0] = *(const uint4*)(X + xsrc[v] + k0);
-      }
-    }
+    for (int v = 0; v < XV; ++v) xr[slot][v] = *(const uint4*)(X + xsrc[v] + k0);
 #pragma unroll
     for (int v = 0; v < WV; ++v) wr[slot][v] = *(const uint4*)(W + wsrc[v] + k0);
-  };
-  auto xval = [&](int slot, int v) -> uint4 {
-    if constexpr (XN) {
-      const float rs = xrs[v];
-      const uint4 h0 = xr[slot][v][0], h1 = xr[slot][v][1], g = xr[slot][v][2];
-      uint4 o;
-      o.x = f2bf(__uint_as_float(h0.x) * rs * bf_lo(g.x)) | (f2bf(__uint_as_float(h0.y) * rs * bf_hi(g.x)) << 16);
-      o.y = f2bf(__uint_as_float(h0.z) * rs * bf_lo(g.y)) | (f2bf(__uint_as_float(h0.w) * rs * bf_hi(g.y)) << 16);
-      o.z = f2bf(__uint_as_float(h1.x) * rs * bf_lo(g.z)) | (f2bf(__uint_as_float(h1.y) * rs * bf_hi(g.z)) << 16);
-      o.w = f2bf(__uint_as_float(h1.z) * rs * bf_lo(g.w)) | (f2bf(__uint_as_float(h1.w) * rs * bf_hi(g.w)) << 16);
-      return o;
-    } else {
-      return xr[slot][v][0];
-    }
   };
   // out-of-range rows are cleared with a mask (a select here would become a
   // select of addresses and push the ring into scratch memory)
@@ -1369,7 +1340,7 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
 #pragma unroll
     for (int v = 0; v < XV; ++v) {
       const int e = tid + 512 * v;
-      *(uint4*)(&As[buf][(e >> 3) * LDA + (e & 7) * 8]) = and4(xval(slot, v), xmask[v]);
+      *(uint4*)(&As[buf][(e >> 3) * LDA + (e & 7) * 8]) = and4(xr[slot][v], xmask[v]);
     }
 #pragma unroll
     for (int v = 0; v < WV; ++v) {
@@ -1485,7 +1456,7 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
 
 template <int BM, int WM, int DEPTH>
 static int run_gemm2(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStream_t st, LinearInfo* info) {
-  if (a.W.fmt != FMT_BF16 || a.W.K % 64 || (a.xnorm && (a.ldx % 4 || BM == 256))) return -1;
+  if (a.W.fmt != FMT_BF16 || a.xnorm || a.W.K % 64) return -1;
   const int mtiles = (a.M + BM - 1) / BM;
   const long ntiles = (a.W.N + 127) / 128;
   const int nsteps = a.W.K / 64;
@@ -1497,17 +1468,11 @@ static int run_gemm2(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStre
   const int sps = (nsteps + nsplit - 1) / nsplit;
   nsplit = (nsteps + sps - 1) / sps;
   if (info) {
-    snprintf(info->name, sizeof info->name, "er::k_gemm2<%d, %d, %d, %s>", BM, WM, DEPTH, a.xnorm ? "true" : "false");
+    snprintf(info->name, sizeof info->name, "er::k_gemm2<%d, %d, %d>", BM, WM, DEPTH);
     info->nsplit = nsplit;
   }
-  if constexpr (BM < 256) {  // (the 256-row tile has no registers left for the fp32 ring)
-    if (a.xnorm)
-      hipLaunchKernelGGL((k_gemm2<BM, WM, DEPTH, true>), dim3((unsigned)(base * nsplit)), dim3(512), 0, st, a,
-                         ws.partial, nsplit, sps, mtiles);
-  }
-  if (!a.xnorm)
-    hipLaunchKernelGGL((k_gemm2<BM, WM, DEPTH, false>), dim3((unsigned)(base * nsplit)), dim3(512), 0, st, a,
-                       ws.partial, nsplit, sps, mtiles);
+  hipLaunchKernelGGL((k_gemm2<BM, WM, DEPTH>), dim3((unsigned)(base * nsplit)), dim3(512), 0, st, a, ws.partial,
+                     nsplit, sps, mtiles);
   if (hipGetLastError() != hipSuccess) return -3;
   if (nsplit > 1) {
     const long waves = (long)a.M * ((a.W.N + 63) / 64);
@@ -1666,7 +1631,7 @@ static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st
         if (K < 8192 && (N < 4096 || (N >= 16384 && N < 65536))) return run_gemm2<64, 1, 6>(a, ws, 512, st, info);
         return run_gemm2<128, 2, 3>(a, ws, 512, st, info);
       }
-      if ((K >= 8192 || N >= 65536) && !a.xnorm) return run_gemm2<256, 4, 3>(a, ws, 512, st, info);
+      if (K >= 8192 || N >= 65536) return run_gemm2<256, 4, 3>(a, ws, 512, st, info);
       return run_gemm2<128, 2, 4>(a, ws, 512, st, info);
     case P_GEMM:
       return run_gemm(a, ws, st, info);
@@ -1721,7 +1686,7 @@ int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStrea
   }
   Plan p = plan_of(a);
   if ((p == P_GEMM || p == P_GEMM2 || p == P_WGEMM) && !gemm_ok) p = P_SKINNY_OLD;
-  if (a.xnorm && p != P_STREAM && p != P_GEMM2) {
+  if (a.xnorm && p != P_STREAM) {
     // these kernels read bf16 x: form x' = RMSNorm(h) * g once, in the workspace
     if (ws.xn && (size_t)a.M * a.W.K <= ws.xn_elems) {
       int r = launch_rmsnorm((const float*)a.x, a.M, a.W.K, a.gnorm, true, a.eps, ws.xn, a.xrow, st);
