@@ -55,8 +55,9 @@ int er_op_w4_kernel_order(const void *d_canon, int N, int K, void *d_out, void *
  *   2000 + 100*NR + 10*KS + D       streaming kernel, M <= 16: x staged in LDS,
  *          weights through a D-deep register ring
  *   30000 + 1000*NR + 100*KS + 10*D + i   weight-streaming GEMM, M <= 16 * {2,4,8,16}[i]
- *   40000 + 100*i + 10*D + w        deep-pipelined GEMM, BM = {_,64,128,256}[i],
- *          register ring depth D, split-K until 256*w work-groups */
+ *   40000 + 100*i + 10*D + w        deep-pipelined GEMM, BM = {_,64,128,256}[i] with 64-wide
+ *          k steps (i = 1..3) or BM = 128 with 32-wide k steps (i = 5), register
+ *          ring depth D, split-K until 256*w work-groups */
 int er_op_linear(int x_dtype, const void *d_x, int ldx, int M, int fmt, const void *d_w, const void *d_scale,
                  const void *d_zero, int N, int K, float *d_y, int ldy, int path, void *stream);
 

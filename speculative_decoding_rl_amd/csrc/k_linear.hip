@@ -1258,15 +1258,17 @@ static int run_wgemm_variant(int code, const LinArgs& a, const LinearWs& ws, hip
 // steps of latency stay hidden.  Split-K partials go through
 // k_splitk_reduce, as for k_gemm_bf16.
 // ----------------------------------------------------------------------------
-template <int BM, int WM, int DEPTH>
+template <int BM, int WM, int DEPTH, int BK>
 __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ part, int nsplit, int sps, int mtiles) {
-  constexpr int BN = 128, BK = 64, LDA = BK + 8;
+  constexpr int BN = 128, LDA = BK + 8;
+  constexpr int KK = BK / 32;                 // 32-wide k slices per step
   constexpr int WN = 8 / WM;
   constexpr int TM = BM / WM, TN = BN / WN;   // wave tile
   constexpr int FM = TM / 16, FN = TN / 16;   // 16x16 fragments per wave
   constexpr int XV = BM * BK / 8 / 512;       // uint4 of x per thread per step
-  constexpr int WV = BN * BK / 8 / 512;       // uint4 of W per thread per step (2)
-  static_assert(XV >= 1 && WV == 2, "tile does not split over 512 threads");
+  constexpr int WV = BN * BK / 8 / 512;       // uint4 of W per thread per step
+  constexpr int CPR = BK / 8;                 // 16-byte pieces per tile row
+  static_assert(XV >= 1 && WV >= 1 && BK % 32 == 0, "tile does not split over 512 threads");
   // one LDS array, carved explicitly: the epilogue overlays its C tile on the
   // operand buffers, which needs their order and adjacency to be fixed
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BM * LDA + 2 * BN * LDA];
@@ -1300,21 +1302,21 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
   bool wok[WV];
 #pragma unroll
   for (int v = 0; v < WV; ++v) {
-    const int e = tid + 512 * v, row = e >> 3;
+    const int e = tid + 512 * v, row = e / CPR;
     wok[v] = n0 + row < N;
     // rows past the end load row N-1 (always in bounds) and are zeroed when stashed
     const int nr = wok[v] ? n0 + row : N - 1;
-    wsrc[v] = (long)phys_row(a, nr >> 4, nr & 15) * K + (e & 7) * 8;
+    wsrc[v] = (long)phys_row(a, nr >> 4, nr & 15) * K + (e % CPR) * 8;
   }
   long xsrc[XV];
   bool xok[XV];
 #pragma unroll
   for (int v = 0; v < XV; ++v) {
-    const int e = tid + 512 * v, row = e >> 3;
+    const int e = tid + 512 * v, row = e / CPR;
     const int m = m0 + row;
     xok[v] = m < M;
     const int mr = xok[v] ? m : M - 1;
-    xsrc[v] = (long)(a.xrow ? a.xrow[mr] : mr) * a.ldx + (e & 7) * 8;
+    xsrc[v] = (long)(a.xrow ? a.xrow[mr] : mr) * a.ldx + (e % CPR) * 8;
   }
 
   uint4 wr[DEPTH][WV], xr[DEPTH][XV];
@@ -1340,12 +1342,12 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
 #pragma unroll
     for (int v = 0; v < XV; ++v) {
       const int e = tid + 512 * v;
-      *(uint4*)(&As[buf][(e >> 3) * LDA + (e & 7) * 8]) = and4(xr[slot][v], xmask[v]);
+      *(uint4*)(&As[buf][(e / CPR) * LDA + (e % CPR) * 8]) = and4(xr[slot][v], xmask[v]);
     }
 #pragma unroll
     for (int v = 0; v < WV; ++v) {
       const int e = tid + 512 * v;
-      *(uint4*)(&Bs[buf][(e >> 3) * LDA + (e & 7) * 8]) = and4(wr[slot][v], wmask[v]);
+      *(uint4*)(&Bs[buf][(e / CPR) * LDA + (e % CPR) * 8]) = and4(wr[slot][v], wmask[v]);
     }
   };
 
@@ -1357,7 +1359,7 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
 
   auto mma = [&](int buf) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       bf16x8_t af[FM], bfr[FN];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -1410,7 +1412,8 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
   // pair partners at column ^ 8, one sum-of-squares partial per (row, 64 cols)
   constexpr int CLD = BN + 4;
   // rows per pass so that the C tile fits in the operand buffers
-  constexpr int NPASS = (sizeof(float) * BM * CLD + sizeof(smem) - 1) / sizeof(smem);
+  constexpr int NPASS0 = (sizeof(float) * BM * CLD + sizeof(smem) - 1) / sizeof(smem);
+  constexpr int NPASS = NPASS0 <= 1 ? 1 : NPASS0 <= 2 ? 2 : NPASS0 <= 4 ? 4 : 8;  // a power of two divides BM
   constexpr int RP = BM / NPASS;
   static_assert(BM % NPASS == 0 && RP % TM == 0, "epilogue passes must hold whole wave tiles");
   static_assert(sizeof(float) * RP * CLD <= sizeof(smem), "C tile pass does not fit");
@@ -1454,24 +1457,24 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
   }
 }
 
-template <int BM, int WM, int DEPTH>
+template <int BM, int WM, int DEPTH, int BK = 64>
 static int run_gemm2(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStream_t st, LinearInfo* info) {
-  if (a.W.fmt != FMT_BF16 || a.xnorm || a.W.K % 64) return -1;
+  if (a.W.fmt != FMT_BF16 || a.xnorm || a.W.K % BK) return -1;
   const int mtiles = (a.M + BM - 1) / BM;
   const long ntiles = (a.W.N + 127) / 128;
-  const int nsteps = a.W.K / 64;
+  const int nsteps = a.W.K / BK;
   const long base = (long)mtiles * ntiles;
   int nsplit = 1;
-  while (base * nsplit * 2 <= want_wgs && nsteps / (nsplit * 2) >= 8 &&
+  while (base * nsplit * 2 <= want_wgs && nsteps / (nsplit * 2) >= 512 / BK &&
          (size_t)(nsplit * 2) * a.M * a.W.N <= ws.partial_floats && ws.partial)
     nsplit *= 2;
   const int sps = (nsteps + nsplit - 1) / nsplit;
   nsplit = (nsteps + sps - 1) / sps;
   if (info) {
-    snprintf(info->name, sizeof info->name, "er::k_gemm2<%d, %d, %d>", BM, WM, DEPTH);
+    snprintf(info->name, sizeof info->name, "er::k_gemm2<%d, %d, %d, %d>", BM, WM, DEPTH, BK);
     info->nsplit = nsplit;
   }
-  hipLaunchKernelGGL((k_gemm2<BM, WM, DEPTH>), dim3((unsigned)(base * nsplit)), dim3(512), 0, st, a, ws.partial,
+  hipLaunchKernelGGL((k_gemm2<BM, WM, DEPTH, BK>), dim3((unsigned)(base * nsplit)), dim3(512), 0, st, a, ws.partial,
                      nsplit, sps, mtiles);
   if (hipGetLastError() != hipSuccess) return -3;
   if (nsplit > 1) {
@@ -1482,8 +1485,9 @@ static int run_gemm2(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStre
   return 0;
 }
 
-// Explicit deep-pipelined GEMM variant: code = 40000 + 1000*ix(BM: 0=32,1=64,2=128,3=256) + 10*want/64 ... kept as
-// code = 40000 + 100*ix + 10*DEPTH + (want_wgs / 256)
+// Explicit deep-pipelined GEMM variant: code = 40000 + 100*ix + 10*DEPTH +
+// want_wgs/256, ix = 1, 2, 3: BM = 64, 128, 256 with 64-wide k steps; ix = 5:
+// BM = 128 with 32-wide k steps (deeper rings at the same register cost)
 static int run_gemm2_variant(int code, const LinArgs& a, const LinearWs& ws, hipStream_t st, LinearInfo* info) {
   const int ix = (code / 100) % 10, dp = (code / 10) % 10, want = 256 * (code % 10);
 #define ER_G(BM_, WM_, IX_, D_) \
@@ -1491,6 +1495,10 @@ static int run_gemm2_variant(int code, const LinArgs& a, const LinearWs& ws, hip
   ER_G(64, 1, 1, 4) ER_G(64, 1, 1, 6) ER_G(128, 2, 2, 3) ER_G(128, 2, 2, 4)
   ER_G(128, 2, 2, 6) ER_G(256, 4, 3, 3) ER_G(256, 4, 3, 4)
 #undef ER_G
+#define ER_G32(BM_, WM_, IX_, D_) \
+  if (ix == IX_ && dp == D_) return run_gemm2<BM_, WM_, D_, 32>(a, ws, want, st, info);
+  ER_G32(128, 2, 5, 6) ER_G32(128, 2, 5, 8)
+#undef ER_G32
   return -1;
 }
 
@@ -1626,13 +1634,17 @@ static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st
       if (M <= 32) return run_wgemm<2, 1, 4, 3>(a, ws, 512, st, info);
       return run_wgemm<4, 1, 1, 3>(a, ws, 512, st, info);
     case P_GEMM2:
+      // split K until about one wave of work-groups (256): more splits cost
+      // more in the reduction than they gain in parallelism
       if (M <= 64) return run_gemm2<64, 1, 4>(a, ws, 256, st, info);
       if (M <= 128) {
-        if (K < 8192 && (N < 4096 || (N >= 16384 && N < 65536))) return run_gemm2<64, 1, 6>(a, ws, 512, st, info);
-        return run_gemm2<128, 2, 3>(a, ws, 512, st, info);
+        if (K < 8192 && (N < 4096 || (N >= 16384 && N < 65536))) return run_gemm2<64, 1, 6>(a, ws, 256, st, info);
+        return run_gemm2<128, 2, 3>(a, ws, 256, st, info);
       }
-      if (K >= 8192 || N >= 65536) return run_gemm2<256, 4, 3>(a, ws, 512, st, info);
-      return run_gemm2<128, 2, 4>(a, ws, 512, st, info);
+      if (K >= 8192) return run_gemm2<256, 4, 3>(a, ws, 256, st, info);
+      if (N >= 65536) return run_gemm2<256, 4, 3>(a, ws, 512, st, info);
+      if (N >= 16384) return run_gemm2<128, 2, 6, 32>(a, ws, 256, st, info);
+      return run_gemm2<128, 2, 4>(a, ws, 256, st, info);
     case P_GEMM:
       return run_gemm(a, ws, st, info);
     case P_SKINNY_OLD:

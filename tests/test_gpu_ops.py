@@ -170,6 +170,7 @@ def test_linear_wide_and_deep(ops):
 @pytest.mark.parametrize("code,M", [
     (31420, 17), (31230, 32), (31131, 50), (31221, 64), (31122, 100), (31123, 256), (31133, 130),   # weight-streaming
     (40141, 33), (40161, 64), (40231, 100), (40262, 128), (40332, 200), (40342, 256), (40241, 250),  # deep-pipelined
+    (40561, 150), (40581, 256), (40562, 97),  # deep-pipelined, 32-wide k steps
 ])
 def test_linear_gemm_variants(ops, code, M):
     # N ragged against the 128-row tiles; K = 26 chunks (split-K over groups where the grid is short)
