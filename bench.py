@@ -153,6 +153,34 @@ def bins(recs):
 LINEAR_KERNELS = ("k_skinny", "k_linear_mfma", "k_linear_valu", "k_wgemm", "k_gemm2", "k_gemm_bf16")
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from a committed counter summary under profiles/, or None.
+
+    A summary names its kernel, the source file that defines it and that file's sha256 when the counters
+    were taken; a summary whose source has changed since is ignored (the counters describe other code).
+    """
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        fields = {}
+        for line in open(path):
+            k, sep, v = line.partition(":")
+            if sep and k.strip() in ("kernel", "source", "source_sha256", "traffic_bytes_per_launch"):
+                fields[k.strip()] = v.strip()
+        if fields.get("kernel") != kernel or "source" not in fields:
+            continue
+        src = os.path.join(ROOT, fields["source"])
+        if not os.path.exists(src):
+            continue
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("source_sha256"):
+            continue
+        try:
+            return float(fields["traffic_bytes_per_launch"])
+        except (KeyError, ValueError):
+            continue
+    return None
+
+
 def roofline_from(kprof):
     """Roofline object of the dominant kernel (largest total time over the timed region).
 
@@ -172,8 +200,9 @@ def roofline_from(kprof):
               "frac": round(tfs / MFMA_PEAK_TFS, 4), "traffic": None}
     else:
         gbs = top["bytes"] / sec / 1e9
+        tr = measured_traffic(top["name"])
         rf = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}
+              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": round(tr) if tr is not None else None}
     detail = {"kernel": top["name"], "launches": top["launches"], "avg_us": round(top["ms"] * 1e3 / top["launches"], 2),
               "avg_bytes": round(top["bytes"] / top["launches"]), "avg_flops": round(top["flops"] / top["launches"]),
               "share_of_profiled_time": round(top["ms"] / sum(k["ms"] for k in kprof), 4)}

@@ -1,0 +1,49 @@
+"""Host-side pieces of bench.py: the roofline object and the measured-traffic lookup."""
+import hashlib
+import importlib.util
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _tree(tmp_path, src_text, sha):
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "k.hip").write_text(src_text)
+    (tmp_path / "profiles" / "k_traffic.md").write_text(
+        "notes\n\nkernel: er::k<1>\nsource: k.hip\nsource_sha256: %s\ntraffic_bytes_per_launch: 1234\n" % sha)
+
+
+def test_traffic_reported_while_source_unchanged(tmp_path, monkeypatch):
+    b = _bench()
+    text = "kernel source\n"
+    _tree(tmp_path, text, hashlib.sha256(text.encode()).hexdigest())
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    assert b.measured_traffic("er::k<1>") == 1234.0
+    assert b.measured_traffic("er::other") is None
+
+
+def test_traffic_dropped_once_source_changes(tmp_path, monkeypatch):
+    b = _bench()
+    _tree(tmp_path, "edited source\n", hashlib.sha256(b"the source the counters saw\n").hexdigest())
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    assert b.measured_traffic("er::k<1>") is None
+
+
+def test_roofline_object_fields(monkeypatch):
+    b = _bench()
+    monkeypatch.setattr(b, "measured_traffic", lambda name: 2.0e6)
+    kprof = [dict(name="er::a", launches=10, ms=1.0, bytes=4.0e9, flops=1.0e9),
+             dict(name="er::k_gemm2<64, 1, 4, 64>", launches=5, ms=0.5, bytes=1.0e9, flops=1.0e9)]
+    rf, detail = b.roofline_from(kprof)
+    # dominant kernel: 4 GB in 1 ms -> 4000 GB/s against 8000 GB/s, HBM-bound
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s"
+    assert abs(rf["achieved"] - 4000.0) < 1e-6 and abs(rf["frac"] - 0.5) < 1e-9
+    assert rf["traffic"] == 2000000
+    assert detail["kernel"] == "er::a" and detail["top_linear"]["kernel"].startswith("er::k_gemm2")
