@@ -67,11 +67,14 @@ struct Meta {
 // Attention work units of the n items whose queries start at pos0[i] and
 // number cnt[i], pushed into the metadata region as [n + 1] exclusive prefix
 // sums of units per item followed by [n] blocks per unit of each item.  The
-// unit length aims at ~1024 work-groups over all KV heads (enough to fill the
-// GPU, so that a long sequence no longer sets the kernel time alone) but
-// never goes below 8 blocks; an item's units split its blocks evenly, and an
-// item that fits in one unit is not split (no combine for it).  Then the
-// list of the items that were split ([n] entries, n_split used).
+// unit length aims at ~256 work-groups over all KV heads (one per compute
+// unit: fewer, longer units keep each wave's block ring full, and a long
+// sequence no longer sets the kernel time alone; from a sweep of 128 / 256 /
+// 512 / 1024 / 2048 on MI355X at batch 1..128 and 4k/8k context) but never
+// goes below 8 blocks; an item's units split its blocks evenly, and an item
+// that fits in one unit is not split (no combine for it).  Then the list of
+// the items that were split ([n] entries, n_split used), and the most units
+// of one item.
 size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, int* n_units, int* n_split,
                   int* max_units) {
   size_t off = 0;
@@ -79,7 +82,7 @@ size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* c
   if (!us) return 0;
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 1023) / 1024));
+  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 255) / 256));
   int32_t acc = 0;
   int ns = 0, mu = 0;
   for (int i = 0; i < n; ++i) {
