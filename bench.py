@@ -44,7 +44,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0, help="0 = run the rollout to completion")
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", default="qwen2.5-7b")
+    ap.add_argument("--config", default="", help="model shape (default qwen2.5-7b; qwen2.5-14b with --crossover)")
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--prompt-len", type=int, default=512)
     ap.add_argument("--median", type=float, default=2048)
@@ -60,6 +60,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
     ap.add_argument("--progress", type=float, default=20.0, help="seconds between progress lines")
+    ap.add_argument("--crossover", action="store_true",
+                    help="fixed-batch SD/AR sweep instead of the rollout: every sequence at --context keys, "
+                         "batches --batches, gamma in --gammas and AR (default config qwen2.5-14b)")
+    ap.add_argument("--batches", default="1,2,4,8,16,32,64,128")
+    ap.add_argument("--gammas", default="2,4,6,8")
+    ap.add_argument("--context", type=int, default=8192)
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only copy this many bytes device-to-device 10 times and exit (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -108,10 +114,11 @@ def run_rollout(eng, args, prompts, stops, label):
     k = 0
     while active and (args.steps == 0 or k < args.steps):
         B = len(active)
+        cbar = args.prompt_len + sum(gen[a] for a in active) / B - 1   # committed keys before this step
         ts = time.perf_counter()
         tok, ne, info = eng.step(active)
         te = time.perf_counter()
-        recs.append((B, int(info.mode), int(info.gamma), int(ne.sum()), te - ts, int(info.accepted)))
+        recs.append((B, int(info.mode), int(info.gamma), int(ne.sum()), te - ts, int(info.accepted), cbar))
         for b, a in enumerate(active):
             gen[a] += int(ne[b])
         active = [a for a in active if gen[a] < stop[a]]
@@ -135,7 +142,37 @@ def run_rollout(eng, args, prompts, stops, label):
                 unfinished=len(left))
 
 
-def bins(recs):
+class Roofline:
+    """Per-step roofline time of the method's algorithmic work (bytes at 8 TB/s, flops at 2.5 PFLOP/s).
+
+    AR step: bytes 2*P_lin + B*C*kvb + B*kvb + 4*B*V, flops 2*P_lin*B + 4*B*C*hq*hd*L.  SD step: gamma
+    drafter forwards (b_q*P_lin + B*C*kvb + B*kvb + 4*B*V bytes each) plus one verify forward over B*(gamma+1)
+    rows.  C = committed keys per sequence; each forward is priced at max(bytes/BW, flops/FLOPS).
+    """
+
+    def __init__(self, shape):
+        d, hq, hkv, hd, F, L, V = (shape.d_model, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.ffn,
+                                   shape.n_layers, shape.vocab)
+        self.P = L * (d * (hq + 2 * hkv) * hd + hq * hd * d + 3 * F * d) + V * d
+        el = 2 if shape.dtype == "bf16" else 4
+        self.wb = el
+        self.qb = 0.5 + 3.0 / 128 if shape.quant == "w4" else 1.0
+        self.kvb = L * 2 * hkv * hd * el
+        self.att = 4.0 * hq * hd * L
+        self.V = V
+
+    def fwd(self, wbytes, rows, B, C):
+        by = wbytes * self.P + B * C * self.kvb + rows * self.kvb + 4.0 * rows * self.V
+        fl = 2.0 * self.P * rows + rows * C * self.att
+        return max(by / (HBM_PEAK_GBS * 1e9), fl / (MFMA_PEAK_TFS * 1e12))
+
+    def step(self, mode, gamma, B, C):
+        if mode == 0:
+            return self.fwd(self.wb, B, B, C)
+        return gamma * self.fwd(self.qb, B, B, C) + self.fwd(self.wb, B * (gamma + 1), B, C)
+
+
+def bins(recs, roof=None):
     edges = [256, 128, 64, 32, 16, 8, 4, 2, 1]
     out = []
     for hi, lo in zip(edges[:-1] + [1], edges[1:] + [0]):
@@ -145,8 +182,12 @@ def bins(recs):
         tok = sum(r[3] for r in sel)
         t = sum(r[4] for r in sel)
         sd = sum(1 for r in sel if r[1] == 1)
-        out.append(dict(batch=f"{lo + 1}-{hi}", steps=len(sel), tokens=tok, seconds=round(t, 4),
-                        tok_per_s=round(tok / t, 1) if t > 0 else None, sd_steps=sd))
+        row = dict(batch=f"{lo + 1}-{hi}", steps=len(sel), tokens=tok, seconds=round(t, 4),
+                   tok_per_s=round(tok / t, 1) if t > 0 else None, sd_steps=sd)
+        if roof is not None and t > 0:
+            # the same steps at the roofline: how much of the HBM / MFMA bound the step time reaches
+            row["roofline_frac"] = round(sum(roof.step(r[1], r[2], r[0], r[6]) for r in sel) / t, 4)
+        out.append(row)
     return out
 
 
@@ -285,6 +326,98 @@ def cpu_baseline(shape_name, args):
             "ar_value": round(ar_tps, 4), "measured_s": round(t_sd * n_sd + t_ar * n_ar, 2)}
 
 
+def crossover(args, shape, wts):
+    """Fixed-batch SD vs AR at a fixed context: every sequence holds `context` keys; for each batch B
+    (largest first, so the pool holds the largest batch before any growth) run AR and SD at each pinned
+    gamma for a few steps and time them.  Reports tokens/s, tokens per step, the SD/AR ratio, the batch
+    where SD stops paying (measured), and the same ratio predicted by the roofline with the measured mean
+    tokens per step."""
+    import torch
+
+    import synth
+    from speculative_decoding_rl_amd import Engine, _lib
+
+    batches = sorted({int(b) for b in args.batches.split(",")}, reverse=True)
+    gammas = [int(g) for g in args.gammas.split(",")]
+    warm = 1
+
+    def timed_steps(B):  # more steps where few sequences average the acceptance
+        return 12 if B <= 4 else 6 if B <= 16 else 3
+
+    def growth(i):  # keys sequence i gains over the sweep (it runs in every batch larger than i)
+        return sum((warm + timed_steps(b)) * (max(gammas) + 1) * (len(gammas) + 1) for b in batches if b > i)
+
+    C = args.context
+    max_ctx = (C + growth(0) + 32 + 15) // 16 * 16
+    Bmax = batches[0]
+    kv_blocks = sum((C + growth(i) + 32) // 16 + 2 for i in range(Bmax))
+    eng = Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
+                 gamma_init=4, gamma_min=1, gamma_max=max(gammas), policy=_lib.ER_POLICY_FORCE_AR, max_seqs=Bmax,
+                 max_batch=Bmax, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
+    prompts = synth.prompts(Bmax, C, shape.vocab, seed=args.seed)
+    ids = [int(i) for i in eng.kv_alloc([C] * Bmax, [max_ctx - C - 16] * Bmax)]
+    t0 = time.perf_counter()
+    eng.prefill(ids, list(prompts))
+    torch.cuda.synchronize()
+    log(f"[crossover] prefill {Bmax} x {C} tokens in {time.perf_counter() - t0:.1f} s")
+    roof = Roofline(shape)
+    rows = []
+    for bi, B in enumerate(batches):
+        act = ids[:B]
+        res = {}
+        for g in [0] + gammas:
+            if g == 0:
+                eng.set_policy(_lib.ER_POLICY_FORCE_AR)
+            else:
+                eng.set_policy(_lib.ER_POLICY_FORCE_SD)
+                eng.set_gamma(g)
+            for _ in range(warm):
+                eng.step(act)
+            torch.cuda.synchronize()
+            timed = timed_steps(B)
+            ts = time.perf_counter()
+            tok = 0
+            for _ in range(timed):
+                _, ne, _ = eng.step(act)
+                tok += int(ne.sum())
+            torch.cuda.synchronize()
+            dt = (time.perf_counter() - ts) / timed
+            cbar = C + sum(eng.seq_info(a)[1] - C for a in act) / B
+            en = tok / timed / B
+            t_roof = roof.step(0 if g == 0 else 1, g, B, cbar)
+            res[g] = dict(ms_per_step=dt * 1e3, tok_per_step=en, tok_s=tok / timed / dt, roof_tok_s=B * en / t_roof)
+            log(f"[crossover] B={B:4d} gamma={g} {dt * 1e3:8.2f} ms/step {en:.2f} tokens/seq/step "
+                f"{res[g]['tok_s']:9.1f} tok/s (roofline {res[g]['roof_tok_s']:9.1f})")
+        for g in gammas:
+            rows.append(dict(batch=B, gamma=g, sd_tok_s=round(res[g]["tok_s"], 1), ar_tok_s=round(res[0]["tok_s"], 1),
+                             sd_over_ar=round(res[g]["tok_s"] / res[0]["tok_s"], 4),
+                             tokens_per_seq_step=round(res[g]["tok_per_step"], 3),
+                             sd_ms_per_step=round(res[g]["ms_per_step"], 3), ar_ms_per_step=round(res[0]["ms_per_step"], 3),
+                             roofline_sd_over_ar=round(res[g]["roof_tok_s"] / res[0]["roof_tok_s"], 4),
+                             roofline_frac_sd=round(res[g]["tok_s"] / res[g]["roof_tok_s"], 4),
+                             roofline_frac_ar=round(res[0]["tok_s"] / res[0]["roof_tok_s"], 4)))
+        nxt = batches[bi + 1] if bi + 1 < len(batches) else 0
+        if nxt < B:
+            eng.kv_free(ids[nxt:B])
+
+    def bstar(key):
+        out = {}
+        for g in gammas:
+            won = [r["batch"] for r in rows if r["gamma"] == g and r[key] > 1.0]
+            out[str(g)] = max(won) if won else 0
+        return out
+
+    st = eng.stats()
+    return {"metric": "fixed-batch SD vs AR tokens/s at fixed context (crossover sweep)", "unit": "tokens/s",
+            "config": {"workload": f"{shape.name}-shaped decoder, {shape.quant.upper()} self-drafter, every sequence "
+                                   f"at {C} keys, T={args.temperature}, top-p={args.top_p}",
+                       "batches": batches, "gammas": gammas, "steps_timed": {b: timed_steps(b) for b in batches}},
+            "data": "synthetic (random-init weights N(0,0.02), uniform prompts)",
+            "alpha_ema_end": round(st["alpha_ema"], 4),
+            "crossover_batch_measured": bstar("sd_over_ar"), "crossover_batch_roofline": bstar("roofline_sd_over_ar"),
+            "rows": rows}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -306,11 +439,16 @@ def main():
         print(json.dumps({"copy_probe_bytes": args.copy_probe, "copies": 10}))
         return
     over = {"n_layers": args.layers} if args.layers else {}
+    if not args.config:
+        args.config = "qwen2.5-14b" if args.crossover else "qwen2.5-7b"
     shape = synth.shape(args.config, **over)
     t0 = time.perf_counter()
     wts = synth.weights(shape, seed=args.seed, device="cuda")
     torch.cuda.synchronize()
     log(f"weights {sum(v.numel() for v in wts.values()) / 1e9:.2f} B params on device in {time.perf_counter() - t0:.1f} s")
+    if args.crossover:
+        print(json.dumps(crossover(args, shape, wts)), flush=True)
+        return
     prompts = synth.prompts(args.batch, args.prompt_len, shape.vocab, seed=args.seed)
     stops = synth.stop_lengths(args.batch, args.median, args.cap, seed=args.seed)
     log(f"stop lengths: sum {int(stops.sum())}, max {int(stops.max())}, median {int(np.median(stops))}")
@@ -386,7 +524,10 @@ def main():
     out["controller"] = {"hbm_gbs": round(cm["hbm_bytes_per_s"] / 1e9, 1), "tflops": round(cm["flops_per_s"] / 1e12, 1),
                          "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3)}
     out["prefill_s"] = round(main_run["prefill_s"], 3)
-    out["by_batch"] = {m: bins(r["recs"]) for m, r in res.items()}
+    roof = Roofline(shape)
+    out["by_batch"] = {m: bins(r["recs"], roof) for m, r in res.items()}
+    out["roofline_frac_rollout"] = {m: round(sum(roof.step(x[1], x[2], x[0], x[6]) for x in r["recs"]) / r["t"], 4)
+                                    for m, r in res.items()}
     out["kernels_top"] = kernel_table(main_run["kprof"])
     if rf_detail:
         out["roofline_kernel"] = rf_detail
