@@ -610,34 +610,61 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(LinArgs a, float* __restrict_
 }
 
 // Split-K reduction: one wave per (row, 64 logical columns); the partials are
-// summed in split order, then the same epilogue as the unsplit kernel.
+// summed in split order, then the same epilogue as the unsplit kernel.  The
+// four waves of a work-group cover consecutive column groups, mostly of one
+// row, so a residual epilogue's sum of squares is added once per (work-group,
+// row) after an LDS pre-sum instead of once per wave (fewer same-address
+// atomics).
 __global__ __launch_bounds__(256) void k_splitk_reduce(LinArgs a, const float* __restrict__ part, int nsplit) {
+  __shared__ float ssq_sh[4];
+  __shared__ int row_sh[4];
   const int M = a.M, N = a.W.N;
-  const int lane = threadIdx.x & 63;
-  const long wid = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const long wid = (long)blockIdx.x * 4 + wave;
   const long ngroups = (N + 63) / 64;
   if (blockIdx.x == 0 && a.ssq_zero)
     for (int m = threadIdx.x; m < M; m += 256) a.ssq_zero[m] = 0ull;
-  if (wid >= (long)M * ngroups) return;
-  const int m = (int)(wid / ngroups);
-  const int nl = (int)(wid - (long)m * ngroups) * 64 + lane;
-  const bool nok = nl < N;
-  const int l16 = lane & 15;
-  const int n = nok ? phys_row(a, nl >> 4, l16) : 0;
-  float v = 0.f;
-  if (nok)
-    for (int s = 0; s < nsplit; ++s) v += part[((long)s * M + m) * N + n];
-  const float partner = __shfl_xor(v, 8, 64);
-  epilogue(a, m, n, v, partner, nok, l16);
-  if (a.epi == EPI_RESID && a.ssq_acc) {
-    float sq = 0.f;
-    if (nok) {
+  const bool want_ssq = a.epi == EPI_RESID && a.ssq_acc;
+  const bool live = wid < (long)M * ngroups;
+  if (!live && !want_ssq) return;
+  float sq = 0.f;
+  int m = -1;
+  if (live) {
+    m = (int)(wid / ngroups);
+    const int nl = (int)(wid - (long)m * ngroups) * 64 + lane;
+    const bool nok = nl < N;
+    const int l16 = lane & 15;
+    const int n = nok ? phys_row(a, nl >> 4, l16) : 0;
+    float v = 0.f;
+    if (nok)
+      for (int s = 0; s < nsplit; ++s) v += part[((long)s * M + m) * N + n];
+    const float partner = __shfl_xor(v, 8, 64);
+    epilogue(a, m, n, v, partner, nok, l16);
+    if (want_ssq && nok) {
       const float hn = ((const float*)a.y)[(long)m * a.ldy + n];
       sq = hn * hn;
     }
-    sq += __shfl_xor(sq, 16, 64);
-    sq += __shfl_xor(sq, 32, 64);
-    ssq_add(a, m, sq, lane == 0, true);
+  }
+  if (!want_ssq) return;
+  sq = wave_sum(sq);
+  if (lane == 0) {
+    ssq_sh[wave] = sq;
+    row_sh[wave] = m;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int cur = -1;
+    float acc = 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const int r = row_sh[w];
+      if (r != cur) {
+        if (cur >= 0) atomicAdd(a.ssq_acc + cur, (unsigned long long)rint((double)acc * SSQ_SCALE));
+        cur = r;
+        acc = 0.f;
+      }
+      acc += ssq_sh[w];
+    }
+    if (cur >= 0) atomicAdd(a.ssq_acc + cur, (unsigned long long)rint((double)acc * SSQ_SCALE));
   }
 }
 
