@@ -64,6 +64,10 @@ struct Meta {
   T* dev(size_t off) const { return (T*)(d + off); }
 };
 
+// Slots of the fixed-point sums of squares (see LinArgs): the residual
+// producers of one row spread their atomic adds over this many cache lines.
+constexpr int kSsqSlots = 16;
+
 // Attention work units of the n items whose queries start at pos0[i] and
 // number cnt[i], pushed into the metadata region as [n + 1] exclusive prefix
 // sums of units per item followed by [n] blocks per unit of each item.  The
@@ -307,7 +311,7 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
   L->sp = align256((size_t)L->logit_rows * srb);
   L->sq = align256((size_t)r.max_batch * r.gamma_max * srb);
   L->resid = align256((size_t)r.max_batch * sampler_chunks((int)V) * 8);
-  L->ssq = 2 * align256((size_t)R * 8);
+  L->ssq = 2 * align256((size_t)kSsqSlots * R * 8);
   L->xn = align256((size_t)R * d * 2);
   L->out = align256((size_t)(L->max_rows + r.max_batch) * 4);
   L->partial = align256((size_t)16 << 20) * 4;  // 16M floats
@@ -427,6 +431,8 @@ int flin(er_ctx* c, const Fwd& f, const FLin& fl, int M, const LinearW& W, void*
   a.act_bf16 = 1;
   a.ssq_acc = fl.ssq_acc;
   a.ssq_zero = fl.ssq_zero;
+  a.ssq_slots = kSsqSlots;
+  a.ssq_stride = c->max_rows;
   a.hq = m.n_q_heads;
   a.hkv = m.n_kv_heads;
   a.hd = m.head_dim;
@@ -461,7 +467,7 @@ int forward(er_ctx* c, const Fwd& f) {
   unsigned long long* S0 = c->ssq[0];
   unsigned long long* S1 = c->ssq[1];
   KC(c, launch_embed(f.tokens, f.tok_stride, f.M, c->embed, c->bf16, d, c->h, c->fuse ? S0 : nullptr,
-                     c->fuse ? S1 : nullptr, c->st));
+                     c->fuse ? S1 : nullptr, c->st, kSsqSlots, c->max_rows));
   AttnArgs a{};
   a.q = c->qb;
   a.out = c->xbuf;

@@ -151,8 +151,21 @@ ER_DEV int phys_row(const LinArgs& a, int s, int l16) {
   return 16 * s + l16;
 }
 
+ER_DEV int ssq_nslots(const LinArgs& a) { return a.ssq_slots > 1 ? a.ssq_slots : 1; }
+
+constexpr int kMaxSsqSlots = 16;
+
 ER_DEV float rstd_of(const LinArgs& a, long hrow) {
-  const double ss = (double)a.ssq_in[hrow] / SSQ_SCALE;
+  // all slots' loads in flight at once (a rolled loop would wait out one
+  // load latency per slot)
+  const int ns = ssq_nslots(a);
+  unsigned long long v[kMaxSsqSlots];
+#pragma unroll
+  for (int i = 0; i < kMaxSsqSlots; ++i) v[i] = i < ns ? a.ssq_in[(long)i * a.ssq_stride + hrow] : 0ull;
+  unsigned long long t = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSsqSlots; ++i) t += v[i];
+  const double ss = (double)t / SSQ_SCALE;
   return 1.0f / sqrtf((float)ss / (float)a.W.K + a.eps);
 }
 
@@ -220,12 +233,23 @@ __device__ __noinline__ void epilogue_call(const LinArgs& a, int m, int n, float
 // contribution to row m; the 16 lanes of each lane group (lane / 16) are
 // summed and the group's lane `lead` adds the total (callers whose row spans
 // several groups reduce across them first and pass one leader).
+// This work-group's slot of row m's running sum of squares.
+ER_DEV unsigned long long* ssq_slot(const LinArgs& a, int m) {
+  return a.ssq_acc + (long)(blockIdx.x % ssq_nslots(a)) * a.ssq_stride + m;
+}
+
+// Clear rows [0, M) of ssq_zero in every slot.
+ER_DEV void ssq_clear(const LinArgs& a, int tid, int nt) {
+  const int M = a.M, tot = ssq_nslots(a) * M;
+  for (int e = tid; e < tot; e += nt) a.ssq_zero[(long)(e / M) * a.ssq_stride + e % M] = 0ull;
+}
+
 ER_DEV void ssq_add(const LinArgs& a, int m, float sq, bool lead, bool mok) {
   sq += __shfl_xor(sq, 1, 64);
   sq += __shfl_xor(sq, 2, 64);
   sq += __shfl_xor(sq, 4, 64);
   sq += __shfl_xor(sq, 8, 64);
-  if (lead && mok) atomicAdd(a.ssq_acc + m, (unsigned long long)rint((double)sq * SSQ_SCALE));
+  if (lead && mok) atomicAdd(ssq_slot(a, m), (unsigned long long)rint((double)sq * SSQ_SCALE));
 }
 
 // ----------------------------------------------------------------------------
@@ -267,7 +291,7 @@ __global__ __launch_bounds__(512) void k_linear_mfma(LinArgs a, int mtiles) {
   const void* __restrict__ zv = a.W.zero;
 
   if (b == 0 && a.ssq_zero)
-    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+    ssq_clear(a, tid, 512);
 
   int n_lane[NR];
   long nrow[NR];
@@ -494,7 +518,7 @@ __global__ __launch_bounds__(256) void k_gemm_bf16(LinArgs a, float* __restrict_
   const uint16_t* __restrict__ W = (const uint16_t*)a.W.w;
 
   if (b == 0 && a.ssq_zero && nsplit == 1)
-    for (int m = tid; m < M; m += 256) a.ssq_zero[m] = 0ull;
+    ssq_clear(a, tid, 256);
   if (tid < GB_M) {
     const int m = m0 + tid;
     rs_sh[tid] = (a.xnorm && m < M) ? rstd_of(a, a.xrow ? a.xrow[m] : m) : 1.f;
@@ -623,7 +647,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(LinArgs a, const float* _
   const long wid = (long)blockIdx.x * 4 + wave;
   const long ngroups = (N + 63) / 64;
   if (blockIdx.x == 0 && a.ssq_zero)
-    for (int m = threadIdx.x; m < M; m += 256) a.ssq_zero[m] = 0ull;
+    ssq_clear(a, threadIdx.x, 256);
   const bool want_ssq = a.epi == EPI_RESID && a.ssq_acc;
   const bool live = wid < (long)M * ngroups;
   if (!live && !want_ssq) return;
@@ -658,13 +682,13 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(LinArgs a, const float* _
     for (int w = 0; w < 4; ++w) {
       const int r = row_sh[w];
       if (r != cur) {
-        if (cur >= 0) atomicAdd(a.ssq_acc + cur, (unsigned long long)rint((double)acc * SSQ_SCALE));
+        if (cur >= 0) atomicAdd(ssq_slot(a, cur), (unsigned long long)rint((double)acc * SSQ_SCALE));
         cur = r;
         acc = 0.f;
       }
       acc += ssq_sh[w];
     }
-    if (cur >= 0) atomicAdd(a.ssq_acc + cur, (unsigned long long)rint((double)acc * SSQ_SCALE));
+    if (cur >= 0) atomicAdd(ssq_slot(a, cur), (unsigned long long)rint((double)acc * SSQ_SCALE));
   }
 }
 
@@ -761,7 +785,7 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
   const void* __restrict__ zv = a.W.zero;
 
   if (b == 0 && a.ssq_zero)
-    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+    ssq_clear(a, tid, 512);
 
   int n_lane[NR];
   long nrow[NR];
@@ -865,24 +889,54 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
   for (int d = 0; d < DEPTH - 1; ++d) issue(min(d, last_it), d);
 
   {
-    // x' fill: four 16-byte pieces per thread in flight at once
+    // x' fill: four 16-byte pieces per thread in flight at once.  With the
+    // norm on load, the rows' 1/rms come from one slot load per (row, slot)
+    // lane summed over 16 lanes into LDS, issued together with the first
+    // pieces' loads; the pieces are normalized after the barrier.
+    __shared__ float rs_sh[16];
+    if (a.xnorm && tid < 16 * M) {
+      const int m = tid >> 4, sl = tid & 15;
+      const long hrow = a.xrow ? a.xrow[m] : m;
+      unsigned long long t = sl < ssq_nslots(a) ? a.ssq_in[(long)sl * a.ssq_stride + hrow] : 0ull;
+      t += __shfl_xor(t, 1, 64);
+      t += __shfl_xor(t, 2, 64);
+      t += __shfl_xor(t, 4, 64);
+      t += __shfl_xor(t, 8, 64);
+      if (sl == 0) rs_sh[m] = 1.0f / sqrtf((float)((double)t / SSQ_SCALE) / (float)K + a.eps);
+    }
     const int K8 = K >> 3, tot = M * K8;
     for (int e0 = 0; e0 < tot; e0 += 4 * 512) {
-      uint4 v[4];
+      uint4 v[4], h1[4], g[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = min(e0 + tid + 512 * j, tot - 1);
         const int m = e / K8, k8 = e - m * K8;
         const long hrow = a.xrow ? a.xrow[m] : m;
-        if (a.xnorm) v[j] = load_x8(a, hrow, rstd_of(a, hrow), (long)k8 * 8);
-        else v[j] = *(const uint4*)((const uint16_t*)a.x + hrow * a.ldx + (long)k8 * 8);
+        if (a.xnorm) {
+          const float* hp = (const float*)a.x + hrow * a.ldx + (long)k8 * 8;
+          v[j] = *(const uint4*)hp;
+          h1[j] = *(const uint4*)(hp + 4);
+          g[j] = *(const uint4*)((const uint16_t*)a.gnorm + (long)k8 * 8);
+        } else {
+          v[j] = *(const uint4*)((const uint16_t*)a.x + hrow * a.ldx + (long)k8 * 8);
+        }
       }
+      if (a.xnorm && e0 == 0) __syncthreads();  // rs_sh
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = e0 + tid + 512 * j;
         if (e < tot) {
           const int m = e / K8, k8 = e - m * K8;
-          *(uint4*)(xs + m * ldsx + k8 * 8) = v[j];
+          uint4 o = v[j];
+          if (a.xnorm) {
+            const float rs = rs_sh[m];
+            const uint4 h0 = v[j], hh = h1[j], gg = g[j];
+            o.x = f2bf(__uint_as_float(h0.x) * rs * bf_lo(gg.x)) | (f2bf(__uint_as_float(h0.y) * rs * bf_hi(gg.x)) << 16);
+            o.y = f2bf(__uint_as_float(h0.z) * rs * bf_lo(gg.y)) | (f2bf(__uint_as_float(h0.w) * rs * bf_hi(gg.y)) << 16);
+            o.z = f2bf(__uint_as_float(hh.x) * rs * bf_lo(gg.z)) | (f2bf(__uint_as_float(hh.y) * rs * bf_hi(gg.z)) << 16);
+            o.w = f2bf(__uint_as_float(hh.z) * rs * bf_lo(gg.w)) | (f2bf(__uint_as_float(hh.w) * rs * bf_hi(gg.w)) << 16);
+          }
+          *(uint4*)(xs + m * ldsx + k8 * 8) = o;
         }
       }
     }
@@ -1052,7 +1106,7 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
   const uint16_t* __restrict__ X = (const uint16_t*)a.x;
 
   if (b == 0 && a.ssq_zero && nsplit == 1)
-    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+    ssq_clear(a, tid, 512);
 
   int n_lane[NR];
   long nrow[NR];
@@ -1322,7 +1376,7 @@ __global__ __launch_bounds__(512) void k_gemm2(LinArgs a, float* __restrict__ pa
   const uint16_t* __restrict__ X = (const uint16_t*)a.x;
 
   if (b == 0 && a.ssq_zero && nsplit == 1)
-    for (int m = tid; m < M; m += 512) a.ssq_zero[m] = 0ull;
+    ssq_clear(a, tid, 512);
 
   // per-thread load slots: row = e / 8, 16-byte column c8 = e % 8
   long wsrc[WV];
@@ -1687,6 +1741,7 @@ static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st
 
 int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info) {
   if (a.M <= 0 || a.W.N <= 0) return 0;
+  if (a.ssq_slots > kMaxSsqSlots || (a.ssq_slots > 1 && a.ssq_stride < a.M)) return -1;
   if (a.W.K % 128 != 0 || (!a.xnorm && a.ldx % 8 != 0) || (a.xnorm && a.ldx % 4 != 0)) return -1;
   if ((a.epi == EPI_SWIGLU && a.W.N != 2 * a.F) ||
       (a.epi == EPI_QKV && (a.W.N != (a.hq + 2 * a.hkv) * a.hd || a.hd % 16 != 0)))

@@ -22,7 +22,7 @@ namespace er {
 
 __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ tok, int stride, const void* __restrict__ E,
                                                int bf16, int d, float* __restrict__ h, unsigned long long* __restrict__ ssq,
-                                               unsigned long long* __restrict__ ssq_zero) {
+                                               unsigned long long* __restrict__ ssq_zero, int slots, long sstride) {
   const int m = blockIdx.x;
   const long t = tok[(long)m * stride];
   float s = 0.f;
@@ -41,8 +41,10 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ tok, 
       s = fmaf(v, v, s);
     }
   }
-  if (ssq_zero && threadIdx.x == 0) ssq_zero[m] = 0ull;
+  // every slot of the row: the sum in slot 0, the other slots cleared
+  if (ssq_zero && (int)threadIdx.x < slots) ssq_zero[(long)threadIdx.x * sstride + m] = 0ull;
   if (!ssq) return;
+  if (threadIdx.x > 0 && (int)threadIdx.x < slots) ssq[(long)threadIdx.x * sstride + m] = 0ull;
   s = wave_sum(s);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
@@ -51,9 +53,13 @@ __global__ __launch_bounds__(256) void k_embed(const int32_t* __restrict__ tok, 
 }
 
 int launch_embed(const int32_t* tokens, int tok_stride, int M, const void* embed, bool bf16, int d, float* h,
-                 unsigned long long* ssq, unsigned long long* ssq_zero, hipStream_t st) {
+                 unsigned long long* ssq, unsigned long long* ssq_zero, hipStream_t st, int ssq_slots,
+                 long ssq_stride) {
   if (M <= 0) return 0;
-  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, tokens, tok_stride, embed, (int)bf16, d, h, ssq, ssq_zero);
+  if (ssq_slots < 1) ssq_slots = 1;
+  if (ssq_slots > 256) return -1;
+  hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, tokens, tok_stride, embed, (int)bf16, d, h, ssq, ssq_zero,
+                     ssq_slots, ssq_stride);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

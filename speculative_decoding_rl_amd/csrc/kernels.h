@@ -52,6 +52,12 @@ struct LinArgs {
   int act_bf16;
   unsigned long long* ssq_acc;   // EPI_RESID: add the updated rows' sums of squares (nullable)
   unsigned long long* ssq_zero;  // cleared for rows [0, M) by work-group 0 (nullable)
+  // The three sum-of-squares buffers may be split into ssq_slots slots (slot s
+  // of row r at s * ssq_stride + r; a row's value is the sum over its slots):
+  // producers add into slot blockIdx.x % ssq_slots, so that the work-groups
+  // of one row do not all update one cache line.  ssq_slots <= 1: one slot.
+  int ssq_slots;
+  long ssq_stride;
   // EPI_QKV
   int hq, hkv, hd;
   const int32_t* pos;       // [M]
@@ -88,10 +94,11 @@ int launch_linear(const void* x, bool act_bf16, int ldx, int M, const LinearW& W
 int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info = nullptr);
 
 // Small fused ops.
-// h[m] = embed[token]; optional ssq[m] = fixed-point sum h^2 (plain store),
-// ssq_zero[m] = 0.
+// h[m] = embed[token]; optional ssq[m] = fixed-point sum h^2 (plain store,
+// other slots 0), ssq_zero[m] = 0 in every slot.
 int launch_embed(const int32_t* tokens, int tok_stride, int M, const void* embed, bool bf16, int d,
-                 float* h, unsigned long long* ssq, unsigned long long* ssq_zero, hipStream_t st);
+                 float* h, unsigned long long* ssq, unsigned long long* ssq_zero, hipStream_t st,
+                 int ssq_slots = 1, long ssq_stride = 0);
 int launch_rmsnorm(const float* h, int M, int d, const void* g, bool bf16, float eps, void* x,
                    const int32_t* row_index, hipStream_t st);
 // q/k/v from the fused projection qkv [M, (hq+2hkv)hd] (fp32): rotate q, k
