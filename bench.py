@@ -197,23 +197,33 @@ LINEAR_KERNELS = ("k_skinny", "k_linear_mfma", "k_linear_valu", "k_wgemm", "k_ge
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from a committed counter summary under profiles/, or None.
 
-    A summary names its kernel, the source file that defines it and that file's sha256 when the counters
-    were taken; a summary whose source has changed since is ignored (the counters describe other code).
+    A summary names its kernel and the source files its traffic depends on, each with its sha256 when the
+    counters were taken; a summary any of whose sources has changed since is ignored (the counters
+    describe other code).
     """
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
-        fields = {}
+        fields, sources = {}, []
         for line in open(path):
             k, sep, v = line.partition(":")
-            if sep and k.strip() in ("kernel", "source", "source_sha256", "traffic_bytes_per_launch"):
-                fields[k.strip()] = v.strip()
-        if fields.get("kernel") != kernel or "source" not in fields:
+            k, v = k.strip(), v.strip()
+            if not sep:
+                continue
+            if k == "source":
+                sources.append([v, None])
+            elif k == "source_sha256" and sources:
+                sources[-1][1] = v
+            elif k in ("kernel", "traffic_bytes_per_launch"):
+                fields[k] = v
+        if fields.get("kernel") != kernel or not sources:
             continue
-        src = os.path.join(ROOT, fields["source"])
-        if not os.path.exists(src):
-            continue
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != fields.get("source_sha256"):
+        ok = True
+        for rel, sha in sources:
+            src = os.path.join(ROOT, rel)
+            if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+                ok = False
+        if not ok:
             continue
         try:
             return float(fields["traffic_bytes_per_launch"])

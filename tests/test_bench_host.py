@@ -47,3 +47,19 @@ def test_roofline_object_fields(monkeypatch):
     assert abs(rf["achieved"] - 4000.0) < 1e-6 and abs(rf["frac"] - 0.5) < 1e-9
     assert rf["traffic"] == 2000000
     assert detail["kernel"] == "er::a" and detail["top_linear"]["kernel"].startswith("er::k_gemm2")
+
+
+def test_traffic_needs_every_source_unchanged(tmp_path, monkeypatch):
+    b = _bench()
+    (tmp_path / "profiles").mkdir()
+    (tmp_path / "a.hip").write_text("kernel\n")
+    (tmp_path / "b.hip").write_text("host, edited\n")
+    sha_a = hashlib.sha256(b"kernel\n").hexdigest()
+    sha_b_old = hashlib.sha256(b"host\n").hexdigest()
+    rec = "kernel: er::k<1>\nsource: a.hip\nsource_sha256: %s\nsource: b.hip\nsource_sha256: %s\n" \
+          "traffic_bytes_per_launch: 99\n"
+    (tmp_path / "profiles" / "k_traffic.md").write_text(rec % (sha_a, sha_b_old))
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    assert b.measured_traffic("er::k<1>") is None
+    (tmp_path / "b.hip").write_text("host\n")
+    assert b.measured_traffic("er::k<1>") == 99.0
