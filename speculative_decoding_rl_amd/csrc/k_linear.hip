@@ -1739,6 +1739,41 @@ static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st
   return -1;
 }
 
+// x' = bf16(RMSNorm(h[xrow[m]]) * g) materialized for the kernels that read
+// bf16 x, with the row's 1/rms from the producers' fixed-point sums of
+// squares (no second pass over h).  Work-group (m, c) covers 2048 columns of
+// row m, 8 per thread; the h loads are issued before the barrier that
+// publishes 1/rms.
+__global__ __launch_bounds__(256) void k_xnorm(LinArgs a, uint16_t* __restrict__ xn) {
+  __shared__ float rs_sh;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int K = a.W.K;
+  const long hrow = a.xrow ? a.xrow[m] : m;
+  const int k0 = (blockIdx.y * 256 + tid) * 8;
+  const bool ok = k0 < K;
+  const int kc = ok ? k0 : 0;
+  const float* hp = (const float*)a.x + hrow * a.ldx + kc;
+  const uint4 h0 = *(const uint4*)hp, h1 = *(const uint4*)(hp + 4);
+  const uint4 g = *(const uint4*)((const uint16_t*)a.gnorm + kc);
+  if (tid < 16) {
+    unsigned long long t = tid < ssq_nslots(a) ? a.ssq_in[(long)tid * a.ssq_stride + hrow] : 0ull;
+    t += __shfl_xor(t, 1, 64);
+    t += __shfl_xor(t, 2, 64);
+    t += __shfl_xor(t, 4, 64);
+    t += __shfl_xor(t, 8, 64);
+    if (tid == 0) rs_sh = 1.0f / sqrtf((float)((double)t / SSQ_SCALE) / (float)K + a.eps);
+  }
+  __syncthreads();
+  if (!ok) return;
+  const float rs = rs_sh;
+  uint4 o;
+  o.x = f2bf(__uint_as_float(h0.x) * rs * bf_lo(g.x)) | (f2bf(__uint_as_float(h0.y) * rs * bf_hi(g.x)) << 16);
+  o.y = f2bf(__uint_as_float(h0.z) * rs * bf_lo(g.y)) | (f2bf(__uint_as_float(h0.w) * rs * bf_hi(g.y)) << 16);
+  o.z = f2bf(__uint_as_float(h1.x) * rs * bf_lo(g.z)) | (f2bf(__uint_as_float(h1.y) * rs * bf_hi(g.z)) << 16);
+  o.w = f2bf(__uint_as_float(h1.z) * rs * bf_lo(g.w)) | (f2bf(__uint_as_float(h1.w) * rs * bf_hi(g.w)) << 16);
+  *(uint4*)(xn + (long)m * K + k0) = o;
+}
+
 int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info) {
   if (a.M <= 0 || a.W.N <= 0) return 0;
   if (a.ssq_slots > kMaxSsqSlots || (a.ssq_slots > 1 && a.ssq_stride < a.M)) return -1;
@@ -1783,8 +1818,8 @@ int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStrea
   if (a.xnorm && p != P_STREAM) {
     // these kernels read bf16 x: form x' = RMSNorm(h) * g once, in the workspace
     if (ws.xn && (size_t)a.M * a.W.K <= ws.xn_elems) {
-      int r = launch_rmsnorm((const float*)a.x, a.M, a.W.K, a.gnorm, true, a.eps, ws.xn, a.xrow, st);
-      if (r) return r;
+      hipLaunchKernelGGL(k_xnorm, dim3(a.M, (a.W.K + 2047) / 2048), dim3(256), 0, st, a, ws.xn);
+      if (hipGetLastError() != hipSuccess) return -3;
       LinArgs b = a;
       b.x = ws.xn;
       b.ldx = a.W.K;
