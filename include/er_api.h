@@ -271,6 +271,13 @@ typedef struct er_kernel_stat {
   double bytes;     /* summed algorithmic bytes */
   double flops;     /* summed algorithmic flops */
 } er_kernel_stat;
+/* on: ER_KPROF_OFF, ER_KPROF_ALL (every linear-layer and attention launch) or
+ * ER_KPROF_ATTENTION (the attention launches only: two event records per
+ * layer instead of per launch, for timing that kernel inside a timed run);
+ * other values give ER_EINVAL. */
+#define ER_KPROF_OFF 0
+#define ER_KPROF_ALL 1
+#define ER_KPROF_ATTENTION 2
 int er_set_kernel_profile(er_ctx *ctx, int on);
 /* Copies min(max, count) entries; *n_out = count. */
 int er_get_kernel_profile(er_ctx *ctx, er_kernel_stat *out, int max, int *n_out);

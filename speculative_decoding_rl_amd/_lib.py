@@ -16,6 +16,7 @@ ER_OK, ER_EINVAL, ER_ENOMEM, ER_EDEVICE, ER_ESTATE = 0, -1, -2, -3, -4
 ER_F32, ER_BF16 = 0, 1
 ER_W8_PERCH_SYM, ER_W4_G128_ASYM = 0, 1
 ER_POLICY_AUTO, ER_POLICY_FORCE_SD, ER_POLICY_FORCE_AR = 0, 1, 2
+ER_KPROF_OFF, ER_KPROF_ALL, ER_KPROF_ATTENTION = 0, 1, 2
 ER_MODE_AR, ER_MODE_SD = 0, 1
 ER_FMT_F32, ER_FMT_BF16, ER_FMT_W8, ER_FMT_W4 = 0, 1, 2, 3
 PURPOSE_DRAFT, PURPOSE_ACCEPT, PURPOSE_RESIDUAL, PURPOSE_AR = 0, 1, 2, 3

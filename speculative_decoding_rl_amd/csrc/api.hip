@@ -155,6 +155,11 @@ struct er_ctx {
   size_t block_bytes = 0;
   Meta meta;
 
+  // Uploads of `meta.h` (pinned) are DMA reads done when the stream reaches
+  // them: the host must not rewrite the region before the last one has run.
+  hipEvent_t meta_ev = nullptr;
+  bool meta_pending = false;
+
   int max_rows = 0;       // rows of the activation buffers
   int logit_rows = 0;     // rows of logits_p
   int lin_path = 0;
@@ -182,7 +187,7 @@ struct er_ctx {
   std::vector<int32_t> last_prefill_row;
 
   // per-kernel timing (events around each linear / attention launch)
-  bool kprof = false;
+  int kprof = 0;  // launches bracketed: KPROF_LINEAR | KPROF_ATTENTION bits
   std::vector<hipEvent_t> kev;
   size_t kev_used = 0;
   struct KRec { std::string name; double bytes, flops; int e0, e1; };
@@ -229,8 +234,29 @@ int fail(er_ctx* c, int code, const char* fmt, ...) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int kp_begin(er_ctx* c) {
-  if (!c->kprof || c->kev_used + 2 > c->kev.size()) return -1;
+// Start filling the metadata region: waits until the last queued upload of
+// it has been read (a multi-chunk prefill queues one per chunk without
+// waiting for the GPU otherwise).
+int meta_begin(er_ctx* c) {
+  if (c->meta_pending) {
+    HIPC(c, hipEventSynchronize(c->meta_ev));
+    c->meta_pending = false;
+  }
+  c->meta.reset();
+  return ER_OK;
+}
+
+// Queue the upload of the filled part of the metadata region on the stream.
+int meta_upload(er_ctx* c) {
+  HIPC(c, hipMemcpyAsync(c->meta.d, c->meta.h, c->meta.used, hipMemcpyHostToDevice, c->st));
+  HIPC(c, hipEventRecord(c->meta_ev, c->st));
+  c->meta_pending = true;
+  return ER_OK;
+}
+
+constexpr int KPROF_LINEAR = 1, KPROF_ATTENTION = 2;
+int kp_begin(er_ctx* c, int kind) {
+  if (!(c->kprof & kind) || c->kev_used + 2 > c->kev.size()) return -1;
   const int i = (int)c->kev_used;
   c->kev_used += 2;
   if (hipEventRecord(c->kev[(size_t)i], c->st) != hipSuccess) return -1;
@@ -390,7 +416,7 @@ struct Fwd {
 int lin(er_ctx* c, const void* x, int M, const LinearW& W, void* y, int ldy, int epi) {
   const int ldx = W.K;
   LinearInfo li{};
-  const int e = kp_begin(c);
+  const int e = kp_begin(c, KPROF_LINEAR);
   KC(c, launch_linear(x, c->bf16, ldx, M, W, y, ldy, epi, c->lws, c->lin_path, c->st, &li));
   if (e >= 0) {
     // algorithmic bytes: weights (with scales/zeros) + activations in + result out (read+write for +=)
@@ -445,7 +471,7 @@ int flin(er_ctx* c, const Fwd& f, const FLin& fl, int M, const LinearW& W, void*
   a.n_layers = m.n_layers;
   a.F = m.ffn;
   LinearInfo li{};
-  const int e = kp_begin(c);
+  const int e = kp_begin(c, KPROF_LINEAR);
   KC(c, launch_linear_fused(a, c->lws, c->lin_path, c->st, &li));
   if (e >= 0) {
     // algorithmic bytes: weights (with scales/zeros) + x' in (fp32 h when normalized on load) + outputs
@@ -517,7 +543,7 @@ int forward(er_ctx* c, const Fwd& f) {
     a.layer = l;
     {
       // scoring kernel and (when keys were split) the combine, timed apart
-      int e = kp_begin(c);
+      int e = kp_begin(c, KPROF_ATTENTION);
       int combined = 0;
       KC(c, launch_attention(a, c->st, 1, &combined));
       if (e >= 0) {
@@ -527,7 +553,7 @@ int forward(er_ctx* c, const Fwd& f) {
         kp_end(c, e, nm, by, 4.0 * f.kv_keys * f.max_q * (double)hq * hd);
       }
       if (combined) {
-        e = kp_begin(c);
+        e = kp_begin(c, KPROF_ATTENTION);
         KC(c, launch_attention(a, c->st, 2));
         if (e >= 0) {
           const double units = a.unit_start ? (double)a.n_units : (double)f.n_items;
@@ -725,7 +751,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     for (int j = 0; j < n; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)c->seqs[ids[j]].n);
   };
   Meta& M = c->meta;
-  M.reset();
+  if (int r_ = meta_begin(c)) { rollback(); return r_; }
   size_t o_ids, o_tok, o_pos, o_spos, o_slot, o_bt, o_ib, o_ir, o_ip, o_ic;
   int32_t* h_ids = M.push<int32_t>(n, &o_ids);
   int32_t* h_tok = M.push<int32_t>(n, &o_tok);
@@ -761,7 +787,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
   const size_t o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split, &max_units);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
-    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    if (int r_ = meta_upload(c)) return r_;
     if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
     Fwd f;
     f.draft = false;
@@ -860,7 +886,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     for (int j = 0; j < n; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)c->seqs[ids[j]].n);
   };
   Meta& M = c->meta;
-  M.reset();
+  if (int r_ = meta_begin(c)) { rollback(); return r_; }
   size_t o_ids, o_pos0, o_tok, o_bt;
   int32_t* h_ids = M.push<int32_t>(n, &o_ids);
   int32_t* h_pos0 = M.push<int32_t>(n, &o_pos0);
@@ -922,7 +948,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   const size_t o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, &n_vus, &s_vus, &m_vus);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
-    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    if (int r_ = meta_upload(c)) return r_;
     if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
     int32_t* d_tok = M.dev<int32_t>(o_tok);
     for (int j = 0; j < g; ++j) {
@@ -1146,7 +1172,7 @@ int calibrate(er_ctx* c) {
     BlockTable bt;
     if (!bt.reserve(c->pool, 1)) return ER_OK;
     Meta& M = c->meta;
-    M.reset();
+    if (int r_ = meta_begin(c)) { bt.release(c->pool); return r_; }
     size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ic;
     int32_t* t = M.push<int32_t>(1, &o_tok);
     int32_t* p = M.push<int32_t>(1, &o_pos);
@@ -1156,7 +1182,7 @@ int calibrate(er_ctx* c) {
     int32_t* ir = M.push<int32_t>(1, &o_ir);
     int32_t* ic = M.push<int32_t>(1, &o_ic);
     *t = 0; *p = 0; *s = (int64_t)bt.blocks[0] * KV_BLOCK; *btp = bt.blocks[0]; *ib = 0; *ir = 0; *ic = 1;
-    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    if (int r_ = meta_upload(c)) return r_;
     Fwd f;
     f.M = 1;
     f.tokens = M.dev<int32_t>(o_tok);
@@ -1213,7 +1239,7 @@ int calibrate(er_ctx* c) {
       const int nb = (int)bt.blocks.size();
       const int n_items = (Mc + qmax - 1) / qmax;
       Meta& M = c->meta;
-      M.reset();
+      if (int r_ = meta_begin(c)) { bt.release(c->pool); return r_; }
       size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ip, o_ic;
       int32_t* t = M.push<int32_t>(Mc, &o_tok);
       int32_t* p = M.push<int32_t>(Mc, &o_pos);
@@ -1239,7 +1265,7 @@ int calibrate(er_ctx* c) {
         int n_units = 0, n_split = 0, max_units = 0;
         const size_t o_us = push_units(M, n_items, (int)m.n_kv_heads, ip, ic, &n_units, &n_split, &max_units);
         if (M.ok) {
-          HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+          if (int r_ = meta_upload(c)) return r_;
           Fwd f;
           f.M = Mc;
           f.tokens = M.dev<int32_t>(o_tok);
@@ -1397,6 +1423,10 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     if (hipHostMalloc((void**)&c->out_h, L.out) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "hipHostMalloc"); }
     for (auto& e : c->ev) {
       if (hipEventCreate(&e) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "hipEventCreate"); }
+    }
+    if (hipEventCreateWithFlags(&c->meta_ev, hipEventDisableTiming) != hipSuccess) {
+      *out = c;
+      return fail(c, ER_EDEVICE, "hipEventCreate");
     }
     c->have_ev = true;
     // counters start at zero
@@ -1560,7 +1590,7 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
         if (done_in_seq == s.prompt_len) { ++ci; done_in_seq = 0; }
       }
       Meta& M = c->meta;
-      M.reset();
+      if (int r_ = meta_begin(c)) return r_;
       std::vector<int32_t> cids;
       for (auto& sg : segs) cids.push_back(ids[sg.call_i]);
       size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ip, o_ic, o_lr;
@@ -1608,7 +1638,7 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       int max_units = 0;
       const size_t o_us = push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split, &max_units);
       if (!M.ok) return fail(c, ER_ENOMEM, "metadata region too small for a prefill chunk");
-      HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+      if (int r_ = meta_upload(c)) return r_;
       Fwd f;
       f.M = rows;
       f.tokens = M.dev<int32_t>(o_tok);
@@ -1657,7 +1687,7 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
     }
     // first tokens: AR draws at position prompt_len
     Meta& M = c->meta;
-    M.reset();
+    if (int r_ = meta_begin(c)) return r_;
     size_t o_ids, o_pos, o_map;
     int32_t* h_ids = M.push<int32_t>(n, &o_ids);
     int32_t* h_pos = M.push<int32_t>(n, &o_pos);
@@ -1667,7 +1697,7 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       h_pos[i] = c->seqs[ids[i]].prompt_len;
       h_map[i] = row_of_call[i];
     }
-    HIPC(c, hipMemcpyAsync(M.d, M.h, M.used, hipMemcpyHostToDevice, c->st));
+    if (int r_ = meta_upload(c)) return r_;
     KC(c, launch_row_stats(c->logits_p, next_row, V, V, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
     KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, V, V, c->rd.temperature, c->rd.top_p, c->rd.seed,
                              M.dev<int32_t>(o_ids), M.dev<int32_t>(o_pos), 0, PURPOSE_AR, c->out_d, 1,
@@ -1906,7 +1936,8 @@ int er_set_kernel_profile(er_ctx* c, int on) {
     for (auto& e : c->kev)
       if (hipEventCreate(&e) != hipSuccess) return fail(c, ER_EDEVICE, "hipEventCreate");
   }
-  c->kprof = on != 0;
+  if (on < 0 || on > ER_KPROF_ATTENTION) return fail(c, ER_EINVAL, "kernel profile mode %d", on);
+  c->kprof = on == ER_KPROF_ALL ? (KPROF_LINEAR | KPROF_ATTENTION) : (on == ER_KPROF_ATTENTION ? KPROF_ATTENTION : 0);
   c->krec.clear();
   c->kev_used = 0;
   return ER_OK;
@@ -1967,6 +1998,7 @@ void er_destroy(er_ctx* c) {
   if (c->have_ev)
     for (auto& e : c->ev) (void)hipEventDestroy(e);
   for (auto& e : c->kev) (void)hipEventDestroy(e);
+  if (c->meta_ev) (void)hipEventDestroy(c->meta_ev);
   delete c;
 }
 

@@ -196,8 +196,10 @@ class Engine:
         check(self.lib.er_kv_free_blocks(self.ctx, C.byref(f), C.byref(t)), self.ctx, "er_kv_free_blocks")
         return f.value, t.value
 
-    def set_kernel_profile(self, on: bool):
-        check(self.lib.er_set_kernel_profile(self.ctx, 1 if on else 0), self.ctx, "er_set_kernel_profile")
+    def set_kernel_profile(self, on):
+        """on: False/True, or _lib.ER_KPROF_ATTENTION (attention launches only)."""
+        mode = on if isinstance(on, int) and not isinstance(on, bool) else (_lib.ER_KPROF_ALL if on else _lib.ER_KPROF_OFF)
+        check(self.lib.er_set_kernel_profile(self.ctx, mode), self.ctx, "er_set_kernel_profile")
 
     def reset_kernel_profile(self):
         check(self.lib.er_reset_kernel_profile(self.ctx), self.ctx, "er_reset_kernel_profile")

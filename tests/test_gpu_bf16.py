@@ -148,3 +148,30 @@ def test_qwen7b_width_lockstep(qwen7_2l):
     print(f"steps={tally.steps} flagged={tally.flagged} abs_q={tally.max_abs_q:.2e} abs_p={tally.max_abs_p:.2e}")
     assert tally.max_abs_q < ABS_TOL_FULL_WIDTH and tally.max_abs_p < ABS_TOL_FULL_WIDTH
     assert tally.unflagged_mismatch == 0
+
+
+def test_many_chunk_prefill_matches_one_chunk(qwen7_2l):
+    """A prefill cut into nine chunks gives the same logits as one chunk, at
+    the prompt's end and one decode step later (which reads every chunk's KV).
+    Each chunk's metadata goes up from one pinned host region by a queued
+    copy; the chunks must not overwrite a copy's source before it has run."""
+    from speculative_decoding_rl_amd import _lib
+    shape, wts, cfg, W, D = qwen7_2l
+    prompts = [list(p) for p in synth.prompts(3, 700, shape.vocab, seed=12)]
+    got = []
+    for chunk in (256, 4096):
+        eng = _engine(shape, wts, shape.quant, seed=12, max_seqs=4, max_batch=4, max_ctx=1024,
+                      prefill_chunk=chunk, kv_blocks=256, policy=_lib.ER_POLICY_FORCE_AR)
+        ids = eng.kv_alloc([700] * 3, [8] * 3)
+        first = eng.prefill(ids, prompts)
+        at_prompt = [eng.debug_logits(1, s)[0].copy() for s in range(3)]
+        eng.ar_step([int(i) for i in ids])
+        after = [eng.debug_logits(1, s)[0].copy() for s in range(3)]
+        eng.close()
+        got.append((first, at_prompt, after))
+    for s in range(3):
+        # the decode step's input is the token drawn at the prompt's end: a
+        # near-tie may draw differently under the two chunkings
+        for k in ((1, 2) if got[0][0][s] == got[1][0][s] else (1,)):
+            d = float(np.abs(got[0][k][s] - got[1][k][s]).max())
+            assert d < ABS_TOL_FULL_WIDTH, (s, k, d)
