@@ -78,9 +78,12 @@ constexpr int kSsqSlots = 16;
 // goes below 8 blocks; an item's units split its blocks evenly, and an item
 // that fits in one unit is not split (no combine for it).  Then the list of
 // the items that were split ([n] entries, n_split used), and the most units
-// of one item.
-size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, int* n_units, int* n_split,
-                  int* max_units) {
+// of one item.  *o_rec gets the offset of one record per unit, eight int32
+// each: item, split index | units of the item << 16, first block, blocks per
+// unit, query count, first query position, first query row, block-table row
+// (row0 and btrow per item), so that a work-group finds all of it in one load.
+size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, const int32_t* row0,
+                  const int32_t* btrow, int* n_units, int* n_split, int* max_units, size_t* o_rec) {
   size_t off = 0;
   int32_t* us = M.push<int32_t>((size_t)3 * n + 1, &off);
   if (!us) return 0;
@@ -102,6 +105,22 @@ size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* c
   *n_units = acc;
   *n_split = ns;
   *max_units = mu;
+  int32_t* rec = M.push<int32_t>((size_t)8 * std::max(acc, 1), o_rec);
+  if (!rec) return 0;
+  for (int i = 0; i < n; ++i) {
+    const int nu = us[i + 1] - us[i], bpu = us[n + 1 + i];
+    for (int k = 0; k < nu; ++k) {
+      int32_t* r = rec + (size_t)8 * (us[i] + k);
+      r[0] = i;
+      r[1] = k | (nu << 16);
+      r[2] = k * bpu;
+      r[3] = bpu;
+      r[4] = cnt[i];
+      r[5] = pos0[i];
+      r[6] = row0[i];
+      r[7] = btrow[i];
+    }
+  }
   return off;
 }
 
@@ -405,6 +424,7 @@ struct Fwd {
   const int32_t *it_bt = nullptr, *it_row0 = nullptr, *it_pos0 = nullptr, *it_cnt = nullptr;
   int n_items = 0, max_q = 0, max_ctx = 0;
   const int32_t* unit_start = nullptr;   // attention work units (see push_units); null = uniform splits
+  const int32_t* unit_rec = nullptr;     // per-unit records (see push_units), with unit_start
   int n_units = 0, n_split = 0, max_units = 0;
   double kv_keys = 0;                    // sum over items of keys read (for per-kernel byte counts)
   const int32_t* logit_rows = nullptr;  // rows whose logits are computed (with n_logit > 0)
@@ -508,13 +528,14 @@ int forward(er_ctx* c, const Fwd& f) {
   a.max_q_count = f.max_q;
   a.max_ctx = f.max_ctx;
   a.unit_start = f.unit_start;
+  a.unit_rec = f.unit_start ? f.unit_rec : nullptr;
   a.n_units = f.n_units;
   a.split_items = f.unit_start ? f.unit_start + 2 * f.n_items + 1 : nullptr;
   a.n_split = f.n_split;
   a.max_units = f.max_units;
   if (a.unit_start &&
       (size_t)a.n_units * hkv * (size_t)(hq / hkv) * f.max_q * (size_t)(hd + 2) > c->attn_ws_floats)
-    a.unit_start = nullptr;  // more units than the partials area holds: uniform splits instead
+    a.unit_start = a.unit_rec = nullptr;  // more units than the partials area holds: uniform splits instead
   a.hq = hq;
   a.hkv = hkv;
   a.hd = hd;
@@ -784,7 +805,9 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
   int n_units = 0;
   int n_split = 0;
   int max_units = 0;
-  const size_t o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split, &max_units);
+  size_t o_rec = 0;
+  const size_t o_us =
+      push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, h_ir, h_ib, &n_units, &n_split, &max_units, &o_rec);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     if (int r_ = meta_upload(c)) return r_;
@@ -805,6 +828,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.max_q = 1;
     f.max_ctx = max_ctx;
     f.unit_start = M.dev<int32_t>(o_us);
+    f.unit_rec = M.dev<int32_t>(o_rec);
     f.n_units = n_units;
     f.n_split = n_split;
     f.max_units = max_units;
@@ -940,12 +964,16 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   std::vector<int> n_dus(g);
   std::vector<int> s_dus(g);
   std::vector<int> m_dus(g);
+  std::vector<size_t> o_drec(g);
   for (int j = 0; j < g; ++j)
-    o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, &n_dus[j], &s_dus[j], &m_dus[j]);
+    o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, h_ir, h_ib, &n_dus[j], &s_dus[j], &m_dus[j],
+                          &o_drec[j]);
   int n_vus = 0;
   int s_vus = 0;
   int m_vus = 0;
-  const size_t o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, &n_vus, &s_vus, &m_vus);
+  size_t o_vrec = 0;
+  const size_t o_vus =
+      push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, h_vir, h_ib, &n_vus, &s_vus, &m_vus, &o_vrec);
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   auto run = [&]() -> int {
     if (int r_ = meta_upload(c)) return r_;
@@ -969,6 +997,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.max_q = 1;
       f.max_ctx = max_ctx;
       f.unit_start = M.dev<int32_t>(o_dus[j]);
+      f.unit_rec = M.dev<int32_t>(o_drec[j]);
       f.n_units = n_dus[j];
       f.n_split = s_dus[j];
       f.max_units = m_dus[j];
@@ -1001,6 +1030,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.max_q = G1;
     f.max_ctx = max_ctx;
     f.unit_start = M.dev<int32_t>(o_vus);
+    f.unit_rec = M.dev<int32_t>(o_vrec);
     f.n_units = n_vus;
     f.n_split = s_vus;
     f.max_units = m_vus;
@@ -1263,7 +1293,9 @@ int calibrate(er_ctx* c) {
           ic[k] = std::min(qmax, Mc - k * qmax);
         }
         int n_units = 0, n_split = 0, max_units = 0;
-        const size_t o_us = push_units(M, n_items, (int)m.n_kv_heads, ip, ic, &n_units, &n_split, &max_units);
+        size_t o_rec = 0;
+        const size_t o_us =
+            push_units(M, n_items, (int)m.n_kv_heads, ip, ic, ir, ib, &n_units, &n_split, &max_units, &o_rec);
         if (M.ok) {
           if (int r_ = meta_upload(c)) return r_;
           Fwd f;
@@ -1281,6 +1313,7 @@ int calibrate(er_ctx* c) {
           f.max_q = qmax;
           f.max_ctx = Mc;
           f.unit_start = M.dev<int32_t>(o_us);
+          f.unit_rec = M.dev<int32_t>(o_rec);
           f.n_units = n_units;
           f.n_split = n_split;
           f.max_units = max_units;
@@ -1636,7 +1669,9 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       int n_units = 0;
       int n_split = 0;
       int max_units = 0;
-      const size_t o_us = push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, &n_units, &n_split, &max_units);
+      size_t o_rec = 0;
+      const size_t o_us =
+          push_units(M, n_items, (int)c->md.n_kv_heads, h_ip, h_ic, h_ir, h_ib, &n_units, &n_split, &max_units, &o_rec);
       if (!M.ok) return fail(c, ER_ENOMEM, "metadata region too small for a prefill chunk");
       if (int r_ = meta_upload(c)) return r_;
       Fwd f;
@@ -1654,6 +1689,7 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       f.max_q = qmax;
       f.max_ctx = max_ctx;
       f.unit_start = M.dev<int32_t>(o_us);
+      f.unit_rec = M.dev<int32_t>(o_rec);
       f.n_units = n_units;
       f.n_split = n_split;
       f.max_units = max_units;

@@ -80,16 +80,35 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   constexpr int NQ = HD / 32;   // 32-wide k slices of the score MFMA
   const int u = blockIdx.x, g = blockIdx.y;
   if (a.unit_start && u >= a.n_units) return;
-  const Unit w = unit_of(a, u, nsplit, bps);
-  const int item = w.item;
+  // The unit's item, split and query/block-table fields: one uniform 32-byte
+  // load of its record when the host wrote records, else a search of the
+  // unit table and loads from the item arrays (a chain of dependent loads).
+  Unit w;
+  int qc, pos0, qrow0, btrow;
+  if (a.unit_rec) {
+    const int4* rp = reinterpret_cast<const int4*>(a.unit_rec) + 2 * (long)u;
+    const int4 r0 = rp[0], r1 = rp[1];
+    w.item = r0.x;
+    w.sp = r0.y & 0xFFFF;
+    w.nu = r0.y >> 16;
+    w.b0 = r0.z;
+    w.bps = r0.w;
+    qc = r1.x;
+    pos0 = r1.y;
+    qrow0 = r1.z;
+    btrow = r1.w;
+  } else {
+    w = unit_of(a, u, nsplit, bps);
+    qc = a.item_q_count[w.item];
+    pos0 = a.item_q_pos0[w.item];
+    qrow0 = a.item_q_row0[w.item];
+    btrow = a.item_bt_row[w.item];
+  }
   // the wave index through readfirstlane, so that everything derived from it
   // (this wave's block list, its block-id loads) is known to be wave-uniform
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, kb = lane >> 4;
   const int grp = a.hq / a.hkv;
-  const int qc = a.item_q_count[item];
-  const int pos0 = a.item_q_pos0[item];
-  const int qrow0 = a.item_q_row0[item];
   const int R = grp * qc;
   const int rgroups = (R + 15) >> 4;
   const int rgn = rgroups == 1 ? 1 : (rgroups == 2 ? 2 : 4);
@@ -128,7 +147,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   float m_run = -INFINITY, l_run = 0.f;
 
   const uint16_t* pool = (const uint16_t*)a.kv_pool;
-  const int32_t* bt = a.block_table + (long)a.item_bt_row[item] * a.bt_stride;
+  const int32_t* bt = a.block_table + (long)btrow * a.bt_stride;
 
   if (rgi < rgroups) {
     // This wave's blocks are first + s_in * t, t < nb.  Their K and V

@@ -889,10 +889,14 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
   for (int d = 0; d < DEPTH - 1; ++d) issue(min(d, last_it), d);
 
   {
-    // x' fill: four 16-byte pieces per thread in flight at once.  With the
-    // norm on load, the rows' 1/rms come from one slot load per (row, slot)
-    // lane summed over 16 lanes into LDS, issued together with the first
-    // pieces' loads; the pieces are normalized after the barrier.
+    // x' fill: XF 16-byte pieces per thread in flight at once (with the norm
+    // on load each piece is three loads; two pieces keep the kernel at 65
+    // VGPRs, three 512-thread work-groups per CU, where four pieces took 91
+    // and two work-groups).  With the norm on load, the rows' 1/rms come
+    // from one slot load per (row, slot) lane summed over 16 lanes into LDS,
+    // issued together with the first pieces' loads; the pieces are
+    // normalized after the barrier.
+    constexpr int XF = 2;
     __shared__ float rs_sh[16];
     if (a.xnorm && tid < 16 * M) {
       const int m = tid >> 4, sl = tid & 15;
@@ -905,10 +909,10 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
       if (sl == 0) rs_sh[m] = 1.0f / sqrtf((float)((double)t / SSQ_SCALE) / (float)K + a.eps);
     }
     const int K8 = K >> 3, tot = M * K8;
-    for (int e0 = 0; e0 < tot; e0 += 4 * 512) {
-      uint4 v[4], h1[4], g[4];
+    for (int e0 = 0; e0 < tot; e0 += XF * 512) {
+      uint4 v[XF], h1[XF], g[XF];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < XF; ++j) {
         const int e = min(e0 + tid + 512 * j, tot - 1);
         const int m = e / K8, k8 = e - m * K8;
         const long hrow = a.xrow ? a.xrow[m] : m;
@@ -923,7 +927,7 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
       }
       if (a.xnorm && e0 == 0) __syncthreads();  // rs_sh
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < XF; ++j) {
         const int e = e0 + tid + 512 * j;
         if (e < tot) {
           const int m = e / K8, k8 = e - m * K8;
@@ -1064,6 +1068,7 @@ static int run_skinny_variant(int code, const LinArgs& a, hipStream_t st, Linear
   if (nr == NR_ && ks == KS_ && dp == D_) return run_skinny<FMT, NR_, KS_, D_>(a, st, info);
 #define ER_SK(NR_, D_) ER_S(NR_, 2, D_) ER_S(NR_, 4, D_) ER_S(NR_, 8, D_)
   ER_SK(1, 2) ER_SK(1, 3) ER_SK(1, 4) ER_SK(2, 2) ER_SK(2, 3) ER_SK(2, 4)
+  ER_S(1, 1, 2) ER_S(1, 1, 3) ER_S(1, 1, 4) ER_S(1, 1, 6) ER_S(1, 1, 8) ER_S(2, 1, 2) ER_S(2, 1, 3) ER_S(2, 1, 4)
   if constexpr (FMT != FMT_BF16) { ER_SK(4, 2) ER_SK(4, 3) ER_SK(4, 4) ER_SK(1, 6) ER_SK(2, 6) ER_SK(1, 8) }
 #undef ER_SK
 #undef ER_S
@@ -1580,6 +1585,10 @@ static int run_gemm2_variant(int code, const LinArgs& a, const LinearWs& ws, hip
   if (ix == IX_ && dp == D_) return run_gemm2<BM_, WM_, D_, 32>(a, ws, want, st, info);
   ER_G32(128, 2, 5, 6) ER_G32(128, 2, 5, 8)
 #undef ER_G32
+#define ER_G128(BM_, WM_, IX_, D_) \
+  if (ix == IX_ && dp == D_) return run_gemm2<BM_, WM_, D_, 128>(a, ws, want, st, info);
+  ER_G128(64, 1, 6, 2) ER_G128(64, 1, 6, 3) ER_G128(64, 1, 6, 4) ER_G128(128, 2, 7, 2) ER_G128(128, 2, 7, 3)
+#undef ER_G128
   return -1;
 }
 
@@ -1639,7 +1648,8 @@ template <int FMT>
 static int dispatch_skinny(const LinArgs& a, hipStream_t st, LinearInfo* info) {
   const int N = a.W.N, K = a.W.K;
   if constexpr (FMT == FMT_BF16) {
-    if (N >= 16384) return a.M <= 2 ? run_skinny<FMT, 1, 4, 2>(a, st, info) : run_skinny<FMT, 1, 2, 2>(a, st, info);
+    if (N >= 65536) return a.M <= 2 ? run_skinny<FMT, 1, 2, 2>(a, st, info) : run_skinny<FMT, 2, 2, 2>(a, st, info);
+    if (N >= 16384) return run_skinny<FMT, 1, 2, 2>(a, st, info);
     if (N >= 4096) return run_skinny<FMT, 1, 4, 2>(a, st, info);
     return run_skinny<FMT, 1, 8, 2>(a, st, info);
   } else {

@@ -135,6 +135,11 @@ struct AttnArgs {
   // unit_start[n_items + 1 + i] blocks (the last one shorter).  Null: every
   // item gets the same split count.
   const int32_t* unit_start;
+  // One record of eight int32 per unit (with unit_start; null: looked up from
+  // unit_start and the item arrays): item, split index | units of the item
+  // << 16, first block, blocks per unit, query count, first query position,
+  // first query row, block-table row.
+  const int32_t* unit_rec;
   int n_units;
   int max_units;             // most units of one item (0: unknown, bounded from max_ctx)
   // Items that have more than one unit (they alone need the combine); with a
