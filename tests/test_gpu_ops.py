@@ -144,10 +144,10 @@ def test_linear_bf16_paths(ops, fmt, M, path):
 
 @pytest.mark.parametrize("fmt", ["bf16", "w8", "w4"])
 @pytest.mark.parametrize("M", [1, 5, 16])
-@pytest.mark.parametrize("code", [2182, 2142, 2223, 2124, 2186, 2244])
+@pytest.mark.parametrize("code", [2182, 2142, 2223, 2124, 2186, 2244, 2122, 2222, 2112, 2118, 2214])
 def test_linear_streaming_variants(ops, fmt, M, code):
-    # x' staged in LDS, weights through a register ring: K split 2/4/8 ways,
-    # 1/2/4 subtiles per wave, ring depth 2..6; N ragged, K = 11 chunks
+    # x' staged in LDS, weights through a register ring: K whole or split
+    # 2/4/8 ways, 1/2/4 subtiles per wave, ring depth 2..8; N ragged, K = 11 chunks
     if code in (2244, 2186) and fmt == "bf16":
         pytest.skip("4 subtiles per wave and rings deeper than 4 are built for the quantized formats only")
     r = _linear_case(ops, fmt, M, 200, 1408, code, seed=M + code)
@@ -171,6 +171,7 @@ def test_linear_wide_and_deep(ops):
     (31420, 17), (31230, 32), (31131, 50), (31221, 64), (31122, 100), (31123, 256), (31133, 130),   # weight-streaming
     (40141, 33), (40161, 64), (40231, 100), (40262, 128), (40332, 200), (40342, 256), (40241, 250),  # deep-pipelined
     (40561, 150), (40581, 256), (40562, 97),  # deep-pipelined, 32-wide k steps
+    (46621, 40), (46642, 64), (46732, 200), (46721, 129),  # deep-pipelined, 128-wide k steps
 ])
 def test_linear_gemm_variants(ops, code, M):
     # N ragged against the 128-row tiles; K = 26 chunks (split-K over groups where the grid is short)
