@@ -553,7 +553,8 @@ def main():
     st = main_run["stats"]
     out["acceptance"] = {"alpha_ema_end": round(st["alpha_ema"], 4),
                          "accepted_per_draft": round(st["accepted"] / st["drafted"], 4) if st["drafted"] else None,
-                         "mean_emitted_per_sd_seq_step": round(st["emitted"] / max(1, st["predict_times"]), 4)
+                         # each speculative sequence-step emits its accepted drafts plus one token
+                         "mean_emitted_per_sd_seq_step": round(1.0 + st["accepted"] / st["predict_times"], 4)
                          if st["predict_times"] else None,
                          "sd_steps": st["sd_steps"], "ar_steps": st["ar_steps"],
                          "effective_length": round(st["effective_length"], 4),
