@@ -140,3 +140,108 @@ def alpha_step(accepted, gammas) -> float:
         num += a
         den += (a + 1) if a < g else g
     return num / den if den > 0 else 0.0
+
+
+# ---------------------------------------------------------------------------
+# Measured-timing guard (the timing_guard policy of the History Tree Dynamic
+# RL page: section 2.2 gives the parameters, section 3.3 the logic).  Plain
+# reading used here, with autoregressive decoding as the default branch (the
+# page's history branch) and speculation as the alternative (its EAGLE3
+# branch); the history-cache warm-up rules have no counterpart:
+#
+# * large batches (above max_sd_batch) always take the default branch;
+# * per batch bucket (ceil(log2(batch))) a tokens/ms EMA is kept for each
+#   branch, weight ema_alpha on the new sample, the first sample setting it;
+# * the alternative is compared only after compare_after default steps in the
+#   bucket, and taken only while its score beats the default's by `margin`;
+# * without a score for it, the alternative is probed for probe_steps steps
+#   when the batch is at most probe_max_batch;
+# * a speculative step whose tokens/ms falls below bad_ratio x the default
+#   score is bad: back to the default branch, the speculative score is
+#   dropped, and the bucket cools down for `cooldown` steps, a length that
+#   grows by cooldown_growth up to cooldown_max with each consecutive bad
+#   probe and returns to `cooldown` once a probe completes.
+# ---------------------------------------------------------------------------
+@dataclass
+class GuardParams:
+    max_sd_batch: int = 8
+    probe_max_batch: int = 2
+    compare_after: int = 64
+    probe_steps: int = 8
+    ema_alpha: float = 0.3
+    margin: float = 1.02
+    cooldown: int = 8192
+    cooldown_max: int = 65536
+    cooldown_growth: float = 4.0
+    bad_ratio: float = 0.98
+
+
+def guard_bucket(batch: int) -> int:
+    """Smallest b with 2**b >= batch."""
+    b = 0
+    while (1 << b) < batch:
+        b += 1
+    return b
+
+
+class TimingGuard:
+    AR, SD = 0, 1
+
+    def __init__(self, p: GuardParams | None = None):
+        self.p = p or GuardParams()
+        self.step = 0
+        self.ema = {}          # (bucket, branch) -> tokens/ms
+        self.n_ar = {}         # bucket -> default-branch steps observed
+        self.probe_left = {}   # bucket -> speculative probe steps still to run
+        self.cool_until = {}   # bucket -> first step after the cooldown
+        self.cool_len = {}     # bucket -> length of the next cooldown
+
+    def choose(self, batch: int) -> int:
+        p = self.p
+        now = self.step
+        self.step += 1
+        if batch > p.max_sd_batch:
+            return self.AR
+        b = guard_bucket(batch)
+        if self.probe_left.get(b, 0) > 0:
+            return self.SD
+        if self.n_ar.get(b, 0) < p.compare_after:
+            return self.AR
+        if now < self.cool_until.get(b, 0):
+            return self.AR
+        sd = self.ema.get((b, self.SD))
+        if sd is not None:
+            ar = self.ema.get((b, self.AR))
+            return self.SD if sd > p.margin * ar else self.AR
+        if batch <= p.probe_max_batch:
+            self.probe_left[b] = p.probe_steps
+            return self.SD
+        return self.AR
+
+    def _bad_probe(self, b: int) -> None:
+        p = self.p
+        n = self.cool_len.get(b, p.cooldown)
+        self.cool_until[b] = self.step + n
+        self.cool_len[b] = min(int(n * p.cooldown_growth), p.cooldown_max)
+        self.probe_left[b] = 0
+        self.ema.pop((b, self.SD), None)
+
+    def observe(self, batch: int, branch: int, tokens: float, ms: float) -> None:
+        p = self.p
+        if batch > p.max_sd_batch:
+            return
+        b = guard_bucket(batch)
+        rate = tokens / ms
+        if branch == self.AR:
+            self.n_ar[b] = self.n_ar.get(b, 0) + 1
+        else:
+            ar = self.ema.get((b, self.AR))
+            if ar is not None and rate < p.bad_ratio * ar:
+                self._bad_probe(b)
+                return
+            if self.probe_left.get(b, 0) > 0:
+                self.probe_left[b] -= 1
+                if self.probe_left[b] == 0:
+                    self.cool_len[b] = p.cooldown
+        old = self.ema.get((b, branch))
+        self.ema[(b, branch)] = rate if old is None else (1.0 - p.ema_alpha) * old + p.ema_alpha * rate
