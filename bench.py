@@ -53,7 +53,9 @@ def parse():
     ap.add_argument("--temperature", type=float, default=1.0)
     ap.add_argument("--top-p", type=float, default=1.0)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--mode", choices=["both", "sd", "ar", "force-sd"], default="both")
+    ap.add_argument("--mode", choices=["both", "sd", "ar", "force-sd", "timing", "both+timing"], default="both",
+                    help="rollouts to run: SD-auto (roofline toggle) and AR by default; 'timing' runs the "
+                         "measured-timing guard policy")
     ap.add_argument("--gamma", type=int, default=0, help="pin gamma (0 = adaptive)")
     ap.add_argument("--layers", type=int, default=0, help="override layer count (testing only)")
     ap.add_argument("--kv-blocks", type=int, default=0)
@@ -514,13 +516,14 @@ def main():
         torch.cuda.synchronize()
 
     res = {}
-    modes = {"both": ["sd", "ar"], "sd": ["sd"], "ar": ["ar"], "force-sd": ["force-sd"]}[args.mode]
+    modes = {"both": ["sd", "ar"], "sd": ["sd"], "ar": ["ar"], "force-sd": ["force-sd"], "timing": ["timing"],
+             "both+timing": ["sd", "ar", "timing"]}[args.mode]
     for m in modes:
         eng.set_policy({"sd": _lib.ER_POLICY_AUTO, "ar": _lib.ER_POLICY_FORCE_AR,
-                        "force-sd": _lib.ER_POLICY_FORCE_SD}[m])
+                        "force-sd": _lib.ER_POLICY_FORCE_SD, "timing": _lib.ER_POLICY_TIMING}[m])
         res[m] = run_rollout(eng, args, prompts, stops, m)
 
-    main_run = res.get("sd") or res.get("force-sd") or res["ar"]
+    main_run = res.get("sd") or res.get("force-sd") or res.get("timing") or res["ar"]
     value = main_run["tokens"] / main_run["t"]
     rf, rf_detail = roofline_from(main_run["kprof"])
     out = {
@@ -550,6 +553,10 @@ def main():
         ar_v = res["ar"]["tokens"] / res["ar"]["t"]
         out["ar_value"] = round(ar_v, 2)
         out["sd_over_ar"] = round(value / ar_v, 4)
+    if "timing" in res and main_run is not res["timing"]:
+        tr = res["timing"]
+        out["timing_guard"] = {"value": round(tr["tokens"] / tr["t"], 2), "sd_steps": tr["stats"]["sd_steps"],
+                               "ar_steps": tr["stats"]["ar_steps"]}
     st = main_run["stats"]
     out["acceptance"] = {"alpha_ema_end": round(st["alpha_ema"], 4),
                          "accepted_per_draft": round(st["accepted"] / st["drafted"], 4) if st["drafted"] else None,

@@ -69,6 +69,9 @@ extern "C" {
                                    32 steps, the gap doubling to at most 1024) */
 #define ER_POLICY_FORCE_SD  1   /* always speculate (gamma adaptive unless pinned) */
 #define ER_POLICY_FORCE_AR  2   /* never speculate */
+#define ER_POLICY_TIMING    3   /* measured-timing guard (er_guard_* below) chooses
+                                   between AR and speculation per batch bucket;
+                                   gamma as under ER_POLICY_AUTO when it speculates */
 
 #define ER_MODE_AR 0
 #define ER_MODE_SD 1
@@ -240,7 +243,8 @@ int er_seq_info(er_ctx *ctx, int32_t seq_id, int32_t *generated, int32_t *contex
 
 int er_get_stats(er_ctx *ctx, er_stats *out);
 /* Clear the counters and restart the controller: acceptance EMA back to
- * alpha_init, no current choice. */
+ * alpha_init, no current choice, the timing guard's state cleared (its
+ * parameters kept). */
 int er_reset_stats(er_ctx *ctx);
 
 /* Record device time per phase for every `period`-th step and the first
@@ -308,6 +312,59 @@ double er_expected_tokens(double alpha, int gamma);
 /* The cost model a context's controller uses (roofline constants as given or
  * as calibrated at init). */
 int er_get_cost_model(const er_ctx *ctx, er_cost_model *out);
+
+/* Measured-timing guard of the SD toggle (the timing_guard policy of the
+ * History Tree Dynamic RL page, section 2.2 parameters and section 3.3 logic,
+ * with autoregressive decoding as the default branch and speculation as the
+ * alternative).  Per batch bucket (bucket = ceil(log2(batch)): 1, 2, 3-4, 5-8,
+ * ...) it keeps an EMA of measured tokens/ms for each branch.
+ *   choose: batch > max_sd_batch -> AR.  A probe in progress -> SD.  Fewer
+ *   than compare_after AR steps observed in the bucket, or the bucket cooling
+ *   down -> AR.  With a speculative score: SD iff it exceeds margin x the AR
+ *   score.  Without one: start a probe of probe_steps SD steps if batch <=
+ *   probe_max_batch, else AR.  Every call advances the step counter.
+ *   observe: a step's tokens / ms updates its branch's EMA (weight ema_alpha
+ *   on the new sample; the first sample sets it).  A speculative step below
+ *   bad_ratio x the AR score is bad: it ends the probe, clears the speculative
+ *   score and cools the bucket down for cooldown steps, a length that grows by
+ *   cooldown_growth (up to cooldown_max) with each consecutive bad probe and
+ *   is reset by a probe that completes.
+ * The state is caller-allocated plain data; a context with ER_POLICY_TIMING
+ * holds its own, fed with the wall time of each step (plan to synchronized
+ * end). */
+#define ER_GUARD_BUCKETS 16
+typedef struct er_guard_params {
+  int32_t max_sd_batch;      /* 8 */
+  int32_t probe_max_batch;   /* 2 */
+  int32_t compare_after;     /* 64 */
+  int32_t probe_steps;       /* 8 */
+  double ema_alpha;          /* 0.3 */
+  double margin;             /* 1.02 */
+  int64_t cooldown;          /* 8192 */
+  int64_t cooldown_max;      /* 65536 */
+  double cooldown_growth;    /* 4.0 */
+  double bad_ratio;          /* 0.98 */
+} er_guard_params;
+typedef struct er_guard_state {
+  er_guard_params p;
+  int64_t step;                                   /* choose calls so far */
+  double ema_ar[ER_GUARD_BUCKETS], ema_sd[ER_GUARD_BUCKETS];   /* tokens/ms, < 0: none */
+  int64_t n_ar[ER_GUARD_BUCKETS];                 /* AR steps observed */
+  int32_t probe_left[ER_GUARD_BUCKETS];
+  int64_t cool_until[ER_GUARD_BUCKETS];           /* AR while step < cool_until */
+  int64_t cool_len[ER_GUARD_BUCKETS];             /* next cooldown length */
+} er_guard_state;
+/* Defaults above. */
+void er_guard_default_params(er_guard_params *p);
+/* ER_EINVAL on bad parameters (max_sd_batch outside [1, 2^15], negative
+ * counts, ema_alpha outside (0, 1], margin or ratios <= 0). */
+int er_guard_init(er_guard_state *g, const er_guard_params *p);
+/* 1: speculate, 0: autoregressive; -1 on a null state or batch < 1. */
+int er_guard_choose(er_guard_state *g, int batch);
+/* branch: 1 speculative, 0 autoregressive; ER_EINVAL on ms <= 0, tokens < 0. */
+int er_guard_observe(er_guard_state *g, int batch, int branch, double tokens, double ms);
+/* The guard state of a context (ER_ESTATE unless its policy is ER_POLICY_TIMING). */
+int er_get_guard(const er_ctx *ctx, er_guard_state *out);
 
 const char *er_last_error(const er_ctx *ctx);
 void er_destroy(er_ctx *ctx);

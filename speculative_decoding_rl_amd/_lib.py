@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libsdrl.so")
 ER_OK, ER_EINVAL, ER_ENOMEM, ER_EDEVICE, ER_ESTATE = 0, -1, -2, -3, -4
 ER_F32, ER_BF16 = 0, 1
 ER_W8_PERCH_SYM, ER_W4_G128_ASYM = 0, 1
-ER_POLICY_AUTO, ER_POLICY_FORCE_SD, ER_POLICY_FORCE_AR = 0, 1, 2
+ER_POLICY_AUTO, ER_POLICY_FORCE_SD, ER_POLICY_FORCE_AR, ER_POLICY_TIMING = 0, 1, 2, 3
 ER_KPROF_OFF, ER_KPROF_ALL, ER_KPROF_ATTENTION = 0, 1, 2
 ER_MODE_AR, ER_MODE_SD = 0, 1
 ER_FMT_F32, ER_FMT_BF16, ER_FMT_W8, ER_FMT_W4 = 0, 1, 2, 3
@@ -82,6 +82,23 @@ class CostModel(C.Structure):
                 ("hbm_bytes_per_s", C.c_double), ("flops_per_s", C.c_double), ("t_fwd_s", C.c_double)]
 
 
+ER_GUARD_BUCKETS = 16
+
+
+class GuardParams(C.Structure):
+    _fields_ = [("max_sd_batch", C.c_int32), ("probe_max_batch", C.c_int32), ("compare_after", C.c_int32),
+                ("probe_steps", C.c_int32), ("ema_alpha", C.c_double), ("margin", C.c_double),
+                ("cooldown", C.c_int64), ("cooldown_max", C.c_int64), ("cooldown_growth", C.c_double),
+                ("bad_ratio", C.c_double)]
+
+
+class GuardState(C.Structure):
+    _fields_ = [("p", GuardParams), ("step", C.c_int64),
+                ("ema_ar", C.c_double * ER_GUARD_BUCKETS), ("ema_sd", C.c_double * ER_GUARD_BUCKETS),
+                ("n_ar", C.c_int64 * ER_GUARD_BUCKETS), ("probe_left", C.c_int32 * ER_GUARD_BUCKETS),
+                ("cool_until", C.c_int64 * ER_GUARD_BUCKETS), ("cool_len", C.c_int64 * ER_GUARD_BUCKETS)]
+
+
 P = C.c_void_p
 I32P = C.POINTER(C.c_int32)
 I64P = C.POINTER(C.c_int64)
@@ -126,6 +143,11 @@ SIGNATURES = {
                                        C.c_int, C.c_double, C.POINTER(C.c_int)]),
     "er_expected_tokens": (C.c_double, [C.c_double, C.c_int]),
     "er_get_cost_model": (C.c_int, [P, C.POINTER(CostModel)]),
+    "er_guard_default_params": (None, [C.POINTER(GuardParams)]),
+    "er_guard_init": (C.c_int, [C.POINTER(GuardState), C.POINTER(GuardParams)]),
+    "er_guard_choose": (C.c_int, [C.POINTER(GuardState), C.c_int]),
+    "er_guard_observe": (C.c_int, [C.POINTER(GuardState), C.c_int, C.c_int, C.c_double, C.c_double]),
+    "er_get_guard": (C.c_int, [P, C.POINTER(GuardState)]),
     "er_last_error": (C.c_char_p, [P]),
     "er_destroy": (None, [P]),
     # er_ops.h

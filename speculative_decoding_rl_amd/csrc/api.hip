@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -196,6 +197,7 @@ struct er_ctx {
   int ar_streak = 0;      // consecutive autoregressive steps chosen by the controller
   int probe_every = 0;    // autoregressive steps between acceptance probes (0: kAlphaProbe)
   int policy = ER_POLICY_AUTO;
+  er_guard_state guard{};  // measured-timing guard (ER_POLICY_TIMING)
 
   er_stats stats{};
   std::string err;
@@ -405,7 +407,7 @@ int validate(const er_model_desc* m, const er_draft_desc* dd, const er_rollout_d
   if (r->max_ctx <= 0 || r->prefill_chunk <= 0) return bad("bad max_ctx / prefill_chunk");
   if (!(r->temperature >= 0.f)) return bad("temperature must be >= 0");
   if (!(r->top_p > 0.f)) return bad("top_p must be > 0");
-  if (r->policy < ER_POLICY_AUTO || r->policy > ER_POLICY_FORCE_AR) return bad("unknown policy");
+  if (r->policy < ER_POLICY_AUTO || r->policy > ER_POLICY_TIMING) return bad("unknown policy");
   const int grp = m->n_q_heads / m->n_kv_heads;
   if (grp * (r->gamma_max + 1) > 64) return bad("(n_q_heads/n_kv_heads) * (gamma_max+1) must be <= 64");
   return ER_OK;
@@ -1130,6 +1132,12 @@ int plan(er_ctx* c, int n, const int32_t* ids) {
   C /= n;
   const int lo = c->gamma_pinned ? c->gamma_pinned : c->rd.gamma_min;
   const int hi = c->gamma_pinned ? c->gamma_pinned : c->rd.gamma_max;
+  if (c->policy == ER_POLICY_TIMING) {
+    // the guard picks the branch from measured tokens/ms; the draft length
+    // when it speculates is the acceptance-aware argmax over gamma >= 1
+    if (er_guard_choose(&c->guard, n) != 1) return c->choice = 0;
+    return c->choice = choose(c->cost, n, C, c->alpha_ema, lo, hi, false, -1, 1.0);
+  }
   const bool allow_ar = c->policy == ER_POLICY_AUTO;
   const int cur = c->choice;
   const int g = choose(c->cost, n, C, c->alpha_ema, lo, hi, allow_ar, cur, c->rd.switch_margin);
@@ -1391,6 +1399,11 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->arena = (char*)dev_arena;
     c->arena_bytes = arena_bytes;
     c->policy = rollout->policy;
+    {
+      er_guard_params gp;
+      er_guard_default_params(&gp);
+      er_guard_init(&c->guard, &gp);
+    }
     c->alpha_ema = rollout->alpha_init > 0 ? rollout->alpha_init : 0.8;
     c->alpha_init = c->alpha_ema;
     Layout L;
@@ -1790,10 +1803,19 @@ int er_step(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int32_t* 
     int r = check_batch(c, n, ids, true);
     if (r) return r;
     if (!tokens_out || !n_emitted_out) return fail(c, ER_EINVAL, "null output");
+    const auto t0 = std::chrono::steady_clock::now();
     const int g = plan(c, n, ids);
     const int stride = c->rd.gamma_max + 1;
-    if (g == 0) return do_ar(c, n, ids, tokens_out, stride, n_emitted_out, info);
-    return do_spec(c, n, ids, g, tokens_out, stride, n_emitted_out, info);
+    r = g == 0 ? do_ar(c, n, ids, tokens_out, stride, n_emitted_out, info)
+               : do_spec(c, n, ids, g, tokens_out, stride, n_emitted_out, info);
+    if (r == ER_OK && c->policy == ER_POLICY_TIMING) {
+      // wall time of the step, plan to the synchronized end, as the guard's sample
+      const double ms = std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+      double tok = 0;
+      for (int i = 0; i < n; ++i) tok += n_emitted_out[i];
+      if (ms > 0) er_guard_observe(&c->guard, n, g > 0 ? 1 : 0, tok, ms);
+    }
+    return r;
   } catch (...) {
     return fail(c, ER_EINVAL, "internal error");
   }
@@ -1851,7 +1873,14 @@ int er_set_gamma(er_ctx* c, int gamma) {
 
 int er_set_policy(er_ctx* c, int policy) {
   if (!c) return ER_EINVAL;
-  if (policy < ER_POLICY_AUTO || policy > ER_POLICY_FORCE_AR) return fail(c, ER_EINVAL, "unknown policy %d", policy);
+  if (policy < ER_POLICY_AUTO || policy > ER_POLICY_TIMING) return fail(c, ER_EINVAL, "unknown policy %d", policy);
+  if (policy == ER_POLICY_TIMING && c->policy != ER_POLICY_TIMING) {
+    er_guard_params gp = c->guard.p;
+    if (er_guard_init(&c->guard, &gp) != ER_OK) {
+      er_guard_default_params(&gp);
+      er_guard_init(&c->guard, &gp);
+    }
+  }
   c->policy = policy;
   c->choice = -1;
   return ER_OK;
@@ -1902,6 +1931,10 @@ int er_reset_stats(er_ctx* c) {
   c->choice = -1;
   c->ar_streak = 0;
   c->probe_every = kAlphaProbe;
+  {
+    er_guard_params gp = c->guard.p;
+    er_guard_init(&c->guard, &gp);
+  }
   return ER_OK;
 }
 
@@ -2001,6 +2034,90 @@ int er_get_kernel_profile(er_ctx* c, er_kernel_stat* out, int max, int* n_out) {
 int er_reset_kernel_profile(er_ctx* c) {
   if (!c) return ER_EINVAL;
   c->kstat.clear();
+  return ER_OK;
+}
+
+void er_guard_default_params(er_guard_params* p) {
+  if (!p) return;
+  p->max_sd_batch = 8;
+  p->probe_max_batch = 2;
+  p->compare_after = 64;
+  p->probe_steps = 8;
+  p->ema_alpha = 0.3;
+  p->margin = 1.02;
+  p->cooldown = 8192;
+  p->cooldown_max = 65536;
+  p->cooldown_growth = 4.0;
+  p->bad_ratio = 0.98;
+}
+
+int er_guard_init(er_guard_state* g, const er_guard_params* p) {
+  if (!g || !p) return ER_EINVAL;
+  if (p->max_sd_batch < 1 || p->max_sd_batch > (1 << 15) || p->probe_max_batch < 0 || p->compare_after < 1 ||
+      p->probe_steps < 0 || !(p->ema_alpha > 0 && p->ema_alpha <= 1) || !(p->margin > 0) || p->cooldown < 0 ||
+      p->cooldown_max < 0 || !(p->cooldown_growth > 0) || !(p->bad_ratio > 0))
+    return ER_EINVAL;
+  std::memset(g, 0, sizeof *g);
+  g->p = *p;
+  for (int b = 0; b < ER_GUARD_BUCKETS; ++b) {
+    g->ema_ar[b] = -1.0;
+    g->ema_sd[b] = -1.0;
+    g->cool_len[b] = p->cooldown;
+  }
+  return ER_OK;
+}
+
+namespace {
+int guard_bucket(int batch) {  // smallest b with 2^b >= batch
+  int b = 0;
+  while ((1 << b) < batch) ++b;
+  return b;
+}
+}  // namespace
+
+int er_guard_choose(er_guard_state* g, int batch) {
+  if (!g || batch < 1) return -1;
+  const int64_t now = g->step++;
+  if (batch > g->p.max_sd_batch) return 0;
+  const int b = guard_bucket(batch);
+  if (g->probe_left[b] > 0) return 1;
+  if (g->n_ar[b] < g->p.compare_after || now < g->cool_until[b]) return 0;
+  if (g->ema_sd[b] >= 0) return g->ema_sd[b] > g->p.margin * g->ema_ar[b] ? 1 : 0;
+  if (batch <= g->p.probe_max_batch) {
+    g->probe_left[b] = g->p.probe_steps;
+    return 1;
+  }
+  return 0;
+}
+
+int er_guard_observe(er_guard_state* g, int batch, int branch, double tokens, double ms) {
+  if (!g || batch < 1 || (branch != 0 && branch != 1) || !(ms > 0) || !(tokens >= 0)) return ER_EINVAL;
+  if (batch > g->p.max_sd_batch) return ER_OK;
+  const int b = guard_bucket(batch);
+  const double rate = tokens / ms;
+  if (branch == 0) {
+    ++g->n_ar[b];
+  } else {
+    if (g->ema_ar[b] >= 0 && rate < g->p.bad_ratio * g->ema_ar[b]) {
+      // bad speculative step: back to autoregressive, drop the score, cool down
+      const int64_t len = g->cool_len[b];
+      g->cool_until[b] = g->step + len;
+      g->cool_len[b] = std::min((int64_t)((double)len * g->p.cooldown_growth), (int64_t)g->p.cooldown_max);
+      g->probe_left[b] = 0;
+      g->ema_sd[b] = -1.0;
+      return ER_OK;
+    }
+    if (g->probe_left[b] > 0 && --g->probe_left[b] == 0) g->cool_len[b] = g->p.cooldown;
+  }
+  double& e = branch ? g->ema_sd[b] : g->ema_ar[b];
+  e = e < 0 ? rate : (1.0 - g->p.ema_alpha) * e + g->p.ema_alpha * rate;
+  return ER_OK;
+}
+
+int er_get_guard(const er_ctx* c, er_guard_state* out) {
+  if (!c || !out) return ER_EINVAL;
+  if (c->policy != ER_POLICY_TIMING) return ER_ESTATE;
+  *out = c->guard;
   return ER_OK;
 }
 

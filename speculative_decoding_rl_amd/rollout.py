@@ -185,6 +185,13 @@ class Engine:
         check(self.lib.er_get_cost_model(self.ctx, C.byref(m)), self.ctx, "er_get_cost_model")
         return {f: getattr(m, f) for f, _ in m._fields_}
 
+    def guard(self) -> dict:
+        """State of the measured-timing guard (policy ER_POLICY_TIMING)."""
+        g = _lib.GuardState()
+        check(self.lib.er_get_guard(self.ctx, C.byref(g)), self.ctx, "er_get_guard")
+        return dict(step=g.step, ema_ar=list(g.ema_ar), ema_sd=list(g.ema_sd), n_ar=list(g.n_ar),
+                    probe_left=list(g.probe_left), cool_until=list(g.cool_until), cool_len=list(g.cool_len))
+
     def set_fused(self, on: bool):
         check(self.lib.er_set_fused(self.ctx, int(bool(on))), self.ctx, "er_set_fused")
 

@@ -94,6 +94,29 @@ def test_greedy_spec_equals_greedy_ar(tiny):
     assert outs["ar"] == ref
 
 
+def test_timing_guard_rollout_greedy_equals_ar(tiny):
+    """Under the measured-timing guard the rollout takes autoregressive steps
+    until the batch-2 bucket has 64 of them, then probes speculation; at T = 0
+    both branches emit the target's argmax, so the tokens equal greedy AR's."""
+    shape, wts, cfg, W, D = tiny
+    from speculative_decoding_rl_amd import _lib
+    prompts = synth.prompts(2, 16, shape.vocab, seed=5)
+    outs = {}
+    for mode, pol in (("timing", _lib.ER_POLICY_TIMING), ("ar", _lib.ER_POLICY_FORCE_AR)):
+        eng = _engine(shape, wts, "w8", seed=5, temperature=0.0, policy=pol, max_ctx=256)
+        ids = eng.kv_alloc([16] * 2, [150] * 2)
+        first = eng.prefill(ids, list(prompts))
+        out, lens, st = eng.rollout(ids, 160)
+        outs[mode] = [[int(first[i])] + list(out[i, :lens[i]]) for i in range(2)]
+        if mode == "timing":
+            g = eng.guard()
+            assert g["n_ar"][1] >= 64          # batch 2 -> bucket 1
+            assert st["sd_steps"] >= 1         # the probe ran
+            assert g["ema_ar"][1] > 0
+        eng.close()
+    assert outs["timing"] == outs["ar"]
+
+
 def test_ar_step_logits_and_tokens(tiny):
     shape, wts, cfg, W, D = tiny
     from speculative_decoding_rl_amd import _lib
