@@ -151,3 +151,32 @@ def test_stop_truncation_and_kv_rollback(tiny):
         assert fin and g == [5, 9][i]
     assert eng.free_blocks()[0] == free0  # finished sequences released every block
     eng.kv_free(ids)
+
+
+def test_kernel_profile_modes(tiny):
+    """ER_KPROF_ATTENTION brackets the attention launches only; ER_KPROF_ALL the
+    linears too; other modes are rejected."""
+    shape, wts, cfg, W, D = tiny
+    from speculative_decoding_rl_amd import _lib
+    prompts = synth.prompts(2, 24, shape.vocab, seed=6)
+    eng = _engine(shape, wts, "w8", seed=6, policy=_lib.ER_POLICY_FORCE_AR)
+    ids = eng.kv_alloc([24] * 2, [8] * 2)
+    eng.prefill(ids, list(prompts))
+    act = [int(i) for i in ids]
+    eng.reset_kernel_profile()
+    eng.set_kernel_profile(_lib.ER_KPROF_ATTENTION)
+    eng.step(act)
+    eng.step(act)
+    names = {k["name"] for k in eng.kernel_profile()}
+    assert names and all(n.startswith("er::k_attn") for n in names), names
+    att = {k["name"]: k["launches"] for k in eng.kernel_profile()}
+    assert max(att.values()) == 2 * shape.n_layers
+    eng.reset_kernel_profile()
+    eng.set_kernel_profile(_lib.ER_KPROF_ALL)
+    eng.step(act)
+    names = {k["name"] for k in eng.kernel_profile()}
+    assert any(n.startswith("er::k_attn") for n in names) and any(not n.startswith("er::k_attn") for n in names)
+    eng.set_kernel_profile(_lib.ER_KPROF_OFF)
+    with pytest.raises(_lib.ErError):
+        eng.set_kernel_profile(7)
+    eng.close()
