@@ -114,3 +114,16 @@ def test_kvpool_invariants_under_sanitizers(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and "kvpool ok" in r.stdout, r.stdout + r.stderr
+
+
+def test_work_unit_split_under_sanitizers(tmp_path):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("no g++")
+    exe = tmp_path / "work_units_test"
+    src = os.path.join(ROOT, "tests", "host", "work_units_test.cpp")
+    r = subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover",
+                        src, "-o", str(exe)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "work_units ok" in r.stdout, r.stdout + r.stderr
