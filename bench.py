@@ -391,7 +391,8 @@ def crossover(args, shape, wts):
     Bmax = batches[0]
     kv_blocks = sum((C + growth(i) + 32) // 16 + 2 for i in range(Bmax))
     eng = Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
-                 gamma_init=4, gamma_min=1, gamma_max=max(gammas), policy=_lib.ER_POLICY_FORCE_AR, max_seqs=Bmax,
+                 gamma_init=min(4, max(gammas)), gamma_min=1, gamma_max=max(gammas), policy=_lib.ER_POLICY_FORCE_AR,
+                 max_seqs=Bmax,
                  max_batch=Bmax, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
     prompts = synth.prompts(Bmax, C, shape.vocab, seed=args.seed)
     ids = [int(i) for i in eng.kv_alloc([C] * Bmax, [max_ctx - C - 16] * Bmax)]
