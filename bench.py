@@ -13,7 +13,7 @@ completion and `steps` reports how many steps that took; --steps K times the
 first K steps.  The same workload is then run with speculation forced off (the
 AR baseline).  Prefill is timed separately and excluded from `value`.
 
-Prints one JSON line (rank 0, N = 1 only: this build runs on one GPU).
+Prints one JSON line (N = 1 only: the library runs on one GPU).
 """
 from __future__ import annotations
 
@@ -462,8 +462,8 @@ def main():
     args = parse()
     args.kprof_every = max(1, args.kprof_every)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 (multi-GPU sharding is "
-                                   "described in DESIGN.md but not built)"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 (sharding sequences "
+                                   "across GPUs is not built)"}))
         sys.exit(2)
     import torch
 

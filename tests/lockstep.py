@@ -7,10 +7,11 @@ GPU's tokens exactly), runs the sampler on its own logits (must agree unless
 the step is flagged), and then commits the GPU's tokens so that one boundary
 case does not cascade.
 
-Flags (the benchmark spec tolerance clause): an acceptance test whose ratio p/q lies
-within 1e-3 of the uniform draw, a greedy decision whose top-2 logit margin is
-under 1e-2, and -- for categorical draws, which that clause does not cover -- a
-draw whose outcome flips when the oracle's logits replace the GPU's.
+Flags (decisions that rounding may legitimately flip): an acceptance test
+whose ratio p/q lies within 1e-3 of the uniform draw, a greedy decision whose
+top-2 logit margin is under 1e-2, and -- for categorical draws, which those two
+rules do not cover -- a draw whose outcome flips when the oracle's logits
+replace the GPU's.
 """
 from __future__ import annotations
 
