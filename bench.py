@@ -19,6 +19,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -240,17 +241,19 @@ def measured_traffic(kernel):
     return None
 
 
-def kernel_pass(eng, args, prompts):
+def kernel_pass(eng, args, prompts, n, steps=32):
     """Every linear and attention launch timed with HIP events, outside the timed rollouts:
-    prefill of the first 64 prompts, then 32 steps of the SD-auto policy at that batch."""
+    prefill of the first n prompts, then `steps` speculative steps (forced, gamma adaptive) at that
+    batch, so that the drafter's and the verify pass's kernels both appear."""
     from speculative_decoding_rl_amd import _lib
-    n = min(64, len(prompts))
-    ids = eng.kv_alloc([args.prompt_len] * n, [40] * n)
+    n = min(n, len(prompts))
+    eng.set_policy(_lib.ER_POLICY_FORCE_SD)
+    ids = eng.kv_alloc([args.prompt_len] * n, [steps * (args.gamma_max + 1) + 8] * n)
     eng.prefill(ids, list(prompts[:n]))
     eng.reset_kernel_profile()
     eng.set_kernel_profile(_lib.ER_KPROF_ALL)
     act = [int(i) for i in ids]
-    for _ in range(32):
+    for _ in range(steps):
         act = [a for a in act if not eng.seq_info(a)[2]]
         if not act:
             break
@@ -296,11 +299,20 @@ def roofline_from(kprof):
     return rf, detail
 
 
+def kernel_role(name):
+    """draft: the quantized drafter's linears (W8 / W4 formats); verify: the bf16 target's linears;
+    attention serves both (the drafter reads the target's KV)."""
+    if name.startswith("er::k_attn"):
+        return "attention"
+    m = re.match(r"er::k_(skinny|linear_mfma)<(\d+)", name)
+    return "draft" if m and int(m.group(2)) in (2, 3) else "verify"
+
+
 def kernel_table(kprof):
     rows = []
     for k in sorted(kprof, key=lambda k: -k["ms"]):
         gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9 if k["ms"] > 0 else 0.0
-        rows.append(dict(name=k["name"], launches=k["launches"], ms=round(k["ms"], 2),
+        rows.append(dict(name=k["name"], role=kernel_role(k["name"]), launches=k["launches"], ms=round(k["ms"], 2),
                          avg_us=round(k["ms"] * 1e3 / max(1, k["launches"]), 2), gbs=round(gbs, 1),
                          frac_hbm=round(gbs / HBM_PEAK_GBS, 3)))
     return rows
@@ -580,10 +592,13 @@ def main():
         rf_detail["sampled_every_steps"] = args.kprof_every
         out["roofline_kernel"] = rf_detail
     if not args.no_kernel_profile:
-        eng.set_policy(_lib.ER_POLICY_AUTO)
-        kp = kernel_pass(eng, args, prompts)
-        out["kernels_top"] = {"pass": "untimed: prefill 64 prompts, 32 SD-auto steps, every launch timed",
+        kp = kernel_pass(eng, args, prompts, 64)
+        out["kernels_top"] = {"pass": "untimed: prefill 64 prompts, 32 forced SD steps, every launch timed",
                               "kernels": kernel_table(kp)}
+        kt = kernel_pass(eng, args, prompts, 4)
+        out["kernels_tail"] = {"pass": "untimed: prefill 4 prompts, 32 forced SD steps, every launch timed",
+                               "kernels": kernel_table(kt)}
+        eng.set_policy(_lib.ER_POLICY_AUTO)
         lin = [k for k in kp if any(n in k["name"] for n in LINEAR_KERNELS)]
         if lin and rf_detail:
             tl = max(lin, key=lambda k: k["ms"])
