@@ -85,12 +85,20 @@ __global__ __launch_bounds__(SB) void k_chunk_stats(const float* __restrict__ lo
   if (c >= nch) return;
   const float* z = logits + (long)r * ld;
   const int base = c * SCH;
+  // The chunk's 32 values per lane are loaded once, unpredicated (indices
+  // clamped into the row; lanes past V are masked by value below), and both
+  // passes run on the registers: a load under the `i < V` predicate made the
+  // compiler wait for each one in turn.
+  float zv[SCH / 64];
+#pragma unroll
+  for (int t = 0; t < SCH / 64; ++t) zv[t] = z[min(base + t * 64 + lane, V - 1)];
   float m = -INFINITY;
   int arg = 0x7FFFFFFF;
+#pragma unroll
   for (int t = 0; t < SCH / 64; ++t) {
     const int i = base + t * 64 + lane;
     if (i < V) {
-      const float v = z[i];
+      const float v = zv[t];
       if (v > m) { m = v; arg = i; }
     }
   }
@@ -104,9 +112,10 @@ __global__ __launch_bounds__(SB) void k_chunk_stats(const float* __restrict__ lo
   if (T != 0.0f) {
     RowStats thr{0u, 0x7FFFFFFF};
     if (KEPT) thr = row_thr(stats, r, nch);
+#pragma unroll
     for (int t = 0; t < SCH / 64; ++t) {
       const int i = base + t * 64 + lane;
-      const double w = (i < V) ? w_rel(z[i], i, (double)m, T, thr, KEPT) : 0.0;
+      const double w = (i < V) ? w_rel(zv[t], i, (double)m, T, thr, KEPT) : 0.0;
       s += wave_sum_d(w);
     }
   }
