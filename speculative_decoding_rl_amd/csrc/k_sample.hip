@@ -57,7 +57,7 @@ struct RowView {
   int arg;
   double S;
 };
-ER_DEV RowView row_view(const ChunkStat* ch, int nch, float T) {
+ER_DEV RowView row_view_mem(const ChunkStat* ch, int nch, float T) {
   RowView v{-INFINITY, 0, 0.0};
   for (int c = 0; c < nch; ++c)
     if (ch[c].m > v.M) { v.M = ch[c].m; v.arg = ch[c].arg; }
@@ -65,6 +65,87 @@ ER_DEV RowView row_view(const ChunkStat* ch, int nch, float T) {
   for (int c = 0; c < nch; ++c)
     if (ch[c].s > 0.0) v.S += ch[c].s * exp(((double)ch[c].m - (double)v.M) / (double)T);
   return v;
+}
+
+// A row's chunk statistics held by one wavefront (every lane active): lane l
+// keeps chunks l, l + 64, l + 128 and l + 192, loaded once, unpredicated;
+// chunk c is read back by any lane through a shuffle from lane c % 64.  The
+// chunk-order loops then cost register shuffles instead of one dependent
+// memory round trip per chunk.
+constexpr int kRegChunks = 4 * 64;
+struct ChunkRegs {
+  // four named slots per field; chunk c lives in slot c / 64 of lane c % 64
+  float m0, m1, m2, m3;
+  int a0, a1, a2, a3;
+  double s0, s1, s2, s3;
+  double f0, f1, f2, f3;  // exp((m - M) / T) once the row max M is known (row_view_regs)
+  ER_DEV void load(const ChunkStat* ch, int nch) {
+    const int lane = threadIdx.x & 63;
+    const ChunkStat& c0 = ch[min(lane, nch - 1)];
+    const ChunkStat& c1 = ch[min(lane + 64, nch - 1)];
+    const ChunkStat& c2 = ch[min(lane + 128, nch - 1)];
+    const ChunkStat& c3 = ch[min(lane + 192, nch - 1)];
+    m0 = c0.m; m1 = c1.m; m2 = c2.m; m3 = c3.m;
+    a0 = c0.arg; a1 = c1.arg; a2 = c2.arg; a3 = c3.arg;
+    s0 = c0.s; s1 = c1.s; s2 = c2.s; s3 = c3.s;
+  }
+  // One chunk's fields by a run-time index: every slot is shuffled and the
+  // value selected (selecting a slot first made the compiler address the
+  // struct in scratch memory).  For single reads, not for loops.
+  ER_DEV float mget(int c) const {
+    const int k = c >> 6, l = c & 63;
+    const float v0 = __shfl(m0, l, 64), v1 = __shfl(m1, l, 64), v2 = __shfl(m2, l, 64), v3 = __shfl(m3, l, 64);
+    return k == 0 ? v0 : k == 1 ? v1 : k == 2 ? v2 : v3;
+  }
+};
+
+// The same loops as row_view_mem over the registers (same operations, same
+// order): the four slots in turn, lanes 0..63 within each.  Each lane forms
+// its own chunks' factors exp((m - M) / T) once M is known (kept in r for
+// the draw), so the in-order sum reads them instead of evaluating them in turn.
+ER_DEV RowView row_view_regs(ChunkRegs& r, int nch, float T) {
+  RowView v{-INFINITY, 0, 0.0};
+  auto scan_m = [&](float mv, int av, int k) {
+    const int n = min(64, nch - 64 * k);
+    for (int j = 0; j < n; ++j) {
+      const float mc = __shfl(mv, j, 64);
+      const int ac = __shfl(av, j, 64);
+      if (mc > v.M) { v.M = mc; v.arg = ac; }
+    }
+  };
+  scan_m(r.m0, r.a0, 0);
+  scan_m(r.m1, r.a1, 1);
+  scan_m(r.m2, r.a2, 2);
+  scan_m(r.m3, r.a3, 3);
+  if (T == 0.0f) { v.S = 1.0; return v; }
+  const double M = (double)v.M, dT = (double)T;
+  r.f0 = exp(((double)r.m0 - M) / dT);
+  r.f1 = exp(((double)r.m1 - M) / dT);
+  r.f2 = exp(((double)r.m2 - M) / dT);
+  r.f3 = exp(((double)r.m3 - M) / dT);
+  auto scan_s = [&](double sv, double fv, int k) {
+    const int n = min(64, nch - 64 * k);
+    for (int j = 0; j < n; ++j) {
+      const double sc = __shfl(sv, j, 64);
+      const double fc = __shfl(fv, j, 64);
+      if (sc > 0.0) v.S += sc * fc;
+    }
+  };
+  scan_s(r.s0, r.f0, 0);
+  scan_s(r.s1, r.f1, 1);
+  scan_s(r.s2, r.f2, 2);
+  scan_s(r.s3, r.f3, 3);
+  return v;
+}
+
+// Row combination: global max (first chunk attaining it gives the lowest-index
+// argmax) and the mass relative to it, summed in chunk order.  Called by whole
+// wavefronts.
+ER_DEV RowView row_view(const ChunkStat* ch, int nch, float T) {
+  if (nch > kRegChunks) return row_view_mem(ch, nch, T);
+  ChunkRegs r;
+  r.load(ch, nch);
+  return row_view_regs(r, nch, T);
 }
 
 // Weight of token i relative to reference m: exp((z - m)/T) if kept, else 0.
@@ -243,27 +324,32 @@ template <class WF, class CS>
 ER_DEV int wave_draw(const WF& wf, const CS& cs, int nch, int V, double u, double total) {
   const int lane = threadIdx.x & 63;
   const double target = u * total;
-  double pre = 0.0, pre_last = 0.0;
-  int cc = -1, last_c = -1;
-  for (int c = 0; c < nch; ++c) {
-    const double sc = cs.sum(c);
-    if (sc > 0.0) {
-      if (pre + sc * cs.f(c) >= target) { cc = c; break; }
-      last_c = c;
-      pre_last = pre;
-    }
-    pre += sc * cs.f(c);
-  }
-  if (cc < 0) { cc = last_c; pre = pre_last; }
+  double pre = 0.0;
+  const int cc = cs.find(nch, target, &pre);
   if (cc < 0) return 0;
   const double f = cs.f(cc);
   const double ref = cs.ref(cc);
   const int base = cc * SCH;
+  // With WF::kPreload the chunk's inputs are loaded once, unpredicated
+  // (indices clamped into the row, lanes past V masked below), before the
+  // in-order rescan; otherwise each tile loads its own (the two-row residual
+  // did not stay in registers that way).
+  typename WF::Val vals[WF::kPreload ? SCH / 64 : 1];
+  if constexpr (WF::kPreload) {
+#pragma unroll
+    for (int t = 0; t < SCH / 64; ++t) vals[t] = wf.load(min(base + t * 64 + lane, V - 1));
+  }
   double r = 0.0;
   int found = -1, last_nz = -1;
+#pragma unroll
   for (int t = 0; t < SCH / 64 && found == -1; ++t) {
     const int i = base + t * 64 + lane;
-    const double w = (i < V) ? wf(i, ref) : 0.0;
+    double w = 0.0;
+    if constexpr (WF::kPreload) {
+      w = (i < V) ? wf.weight(vals[t], i, ref) : 0.0;
+    } else {
+      w = (i < V) ? wf.weight(wf.load(i), i, ref) : 0.0;
+    }
     const double ts = wave_sum_d(w);
     if (w > 0.0) last_nz = i;
     if (pre + (r + ts) * f >= target) {
@@ -284,6 +370,27 @@ ER_DEV int wave_draw(const WF& wf, const CS& cs, int nch, int V, double u, doubl
   return found >= 0 ? found : (last_nz >= 0 ? last_nz : base);
 }
 
+// First chunk whose running mass (chunk sums times their factors, in chunk
+// order) reaches target, with the mass before it in *pre; when rounding
+// leaves none, the last chunk with mass.  -1 when no chunk has mass.
+template <class CS>
+ER_DEV int find_chunk_mem(const CS& cs, int nch, double target, double* pre_out) {
+  double pre = 0.0, pre_last = 0.0;
+  int cc = -1, last_c = -1;
+  for (int c = 0; c < nch; ++c) {
+    const double sc = cs.sum(c);
+    if (sc > 0.0) {
+      if (pre + sc * cs.f(c) >= target) { cc = c; break; }
+      last_c = c;
+      pre_last = pre;
+    }
+    pre += sc * cs.f(c);
+  }
+  if (cc < 0) { cc = last_c; pre = pre_last; }
+  *pre_out = pre;
+  return cc;
+}
+
 struct ChunkView {
   const ChunkStat* ch;
   float M;
@@ -291,6 +398,46 @@ struct ChunkView {
   ER_DEV double sum(int c) const { return ch[c].s; }
   ER_DEV double f(int c) const { return exp(((double)ch[c].m - (double)M) / (double)T); }
   ER_DEV double ref(int c) const { return (double)ch[c].m; }
+  ER_DEV int find(int nch, double target, double* pre) const { return find_chunk_mem(*this, nch, target, pre); }
+};
+// The same view over a wavefront's registers (rows of at most kRegChunks
+// chunks): the scan walks the slots in turn with the same operations.
+struct ChunkViewRegs {
+  ChunkRegs r;
+  float M;
+  float T;
+  // the factors were formed by row_view_regs with this M
+  ER_DEV double f(int c) const {
+    const int k = c >> 6, l = c & 63;
+    const double v0 = __shfl(r.f0, l, 64), v1 = __shfl(r.f1, l, 64), v2 = __shfl(r.f2, l, 64),
+                 v3 = __shfl(r.f3, l, 64);
+    return k == 0 ? v0 : k == 1 ? v1 : k == 2 ? v2 : v3;
+  }
+  ER_DEV double ref(int c) const { return (double)r.mget(c); }
+  ER_DEV int find(int nch, double target, double* pre_out) const {
+    double pre = 0.0, pre_last = 0.0;
+    int cc = -1, last_c = -1;
+    auto scan = [&](double sv, double fv, int k) {
+      const int n = min(64, nch - 64 * k);
+      for (int j = 0; j < n && cc < 0; ++j) {
+        const double sc = __shfl(sv, j, 64);
+        const double fc = __shfl(fv, j, 64);
+        if (sc > 0.0) {
+          if (pre + sc * fc >= target) { cc = 64 * k + j; break; }
+          last_c = 64 * k + j;
+          pre_last = pre;
+        }
+        pre += sc * fc;
+      }
+    };
+    scan(r.s0, r.f0, 0);
+    if (cc < 0) scan(r.s1, r.f1, 1);
+    if (cc < 0) scan(r.s2, r.f2, 2);
+    if (cc < 0) scan(r.s3, r.f3, 3);
+    if (cc < 0) { cc = last_c; pre = pre_last; }
+    *pre_out = pre;
+    return cc;
+  }
 };
 
 struct RowW {
@@ -298,7 +445,10 @@ struct RowW {
   RowStats thr;
   float T;
   bool topp;
-  ER_DEV double operator()(int i, double ref) const { return w_rel(z[i], i, ref, T, thr, topp); }
+  typedef float Val;
+  static constexpr bool kPreload = true;
+  ER_DEV Val load(int i) const { return z[i]; }
+  ER_DEV double weight(Val v, int i, double ref) const { return w_rel(v, i, ref, T, thr, topp); }
 };
 
 __global__ __launch_bounds__(64) void k_sample_rows(const float* __restrict__ logits, const void* __restrict__ stats,
@@ -309,14 +459,27 @@ __global__ __launch_bounds__(64) void k_sample_rows(const float* __restrict__ lo
   const int r = blockIdx.x;
   const long lr = row_map ? row_map[r] : r;
   const ChunkStat* ch = row_chunks(stats, lr, nch);
-  const RowView rv = row_view(ch, nch, T);
   int t;
-  if (T == 0.0f) {
-    t = rv.arg;
+  if (nch <= kRegChunks) {
+    ChunkRegs cr;
+    cr.load(ch, nch);
+    const RowView rv = row_view_regs(cr, nch, T);
+    if (T == 0.0f) {
+      t = rv.arg;
+    } else {
+      const double u = philox_uniform(seed, (uint32_t)seq_id[r], (uint32_t)pos[r], (uint32_t)didx, (uint32_t)purpose);
+      RowW wf{logits + lr * ld, row_thr(stats, lr, nch), T, top_p < 1.0f};
+      t = wave_draw(wf, ChunkViewRegs{cr, rv.M, T}, nch, V, u, rv.S);
+    }
   } else {
-    const double u = philox_uniform(seed, (uint32_t)seq_id[r], (uint32_t)pos[r], (uint32_t)didx, (uint32_t)purpose);
-    RowW wf{logits + lr * ld, row_thr(stats, lr, nch), T, top_p < 1.0f};
-    t = wave_draw(wf, ChunkView{ch, rv.M, T}, nch, V, u, rv.S);
+    const RowView rv = row_view_mem(ch, nch, T);
+    if (T == 0.0f) {
+      t = rv.arg;
+    } else {
+      const double u = philox_uniform(seed, (uint32_t)seq_id[r], (uint32_t)pos[r], (uint32_t)didx, (uint32_t)purpose);
+      RowW wf{logits + lr * ld, row_thr(stats, lr, nch), T, top_p < 1.0f};
+      t = wave_draw(wf, ChunkView{ch, rv.M, T}, nch, V, u, rv.S);
+    }
   }
   if (threadIdx.x == 0) out[(long)r * out_stride] = t;
 }
@@ -381,17 +544,24 @@ struct ResidW {
   RowView pv, qv;
   float T;
   bool topp;
-  ER_DEV double operator()(int i, double) const {
+  // token i's residual weight from its two logits (a from p, b from q)
+  ER_DEV double from(float a, float b, int i) const {
     double p, q;
     if (T == 0.0f) {
       p = i == pv.arg ? 1.0 : 0.0;
       q = i == qv.arg ? 1.0 : 0.0;
     } else {
-      p = w_rel(zp[i], i, (double)pv.M, T, tp, topp) / pv.S;
-      q = w_rel(zq[i], i, (double)qv.M, T, tq, topp) / qv.S;
+      p = w_rel(a, i, (double)pv.M, T, tp, topp) / pv.S;
+      q = w_rel(b, i, (double)qv.M, T, tq, topp) / qv.S;
     }
     return p > q ? p - q : 0.0;
   }
+  struct Val {
+    float p, q;
+  };
+  static constexpr bool kPreload = false;
+  ER_DEV Val load(int i) const { return Val{zp[i], zq[i]}; }
+  ER_DEV double weight(Val v, int i, double) const { return from(v.p, v.q, i); }
 };
 
 __global__ __launch_bounds__(SB) void k_resid_chunks(const float* __restrict__ p_logits, const void* __restrict__ p_stats,
@@ -413,9 +583,19 @@ __global__ __launch_bounds__(SB) void k_resid_chunks(const float* __restrict__ p
             topp != 0};
   double s = 0.0;
   const int base = c * SCH;
+  // both rows' chunk values loaded once, unpredicated (indices clamped into
+  // the row, lanes past V masked by value), then the same sums as the draw
+  float ap[SCH / 64], aq[SCH / 64];
+#pragma unroll
+  for (int t = 0; t < SCH / 64; ++t) {
+    const int ic = min(base + t * 64 + lane, V - 1);
+    ap[t] = rw.zp[ic];
+    aq[t] = rw.zq[ic];
+  }
+#pragma unroll
   for (int t = 0; t < SCH / 64; ++t) {
     const int i = base + t * 64 + lane;
-    s += wave_sum_d(i < V ? rw(i, 0.0) : 0.0);
+    s += wave_sum_d(i < V ? rw.from(ap[t], aq[t], i) : 0.0);
   }
   if (lane == 0) resid[(long)b * nch + c] = s;
 }
@@ -425,6 +605,7 @@ struct ResidChunks {
   ER_DEV double sum(int c) const { return s[c]; }
   ER_DEV double f(int) const { return 1.0; }
   ER_DEV double ref(int) const { return 0.0; }
+  ER_DEV int find(int nch, double target, double* pre) const { return find_chunk_mem(*this, nch, target, pre); }
 };
 
 __global__ __launch_bounds__(64) void k_decide_draw(const float* __restrict__ p_logits, const void* __restrict__ p_stats,
