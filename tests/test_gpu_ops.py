@@ -260,11 +260,15 @@ def _stats(ops, logits_t, T, top_p):
     return st
 
 
-@pytest.mark.parametrize("T,top_p", [(1.0, 1.0), (0.7, 0.9), (1.0, 0.95), (0.0, 1.0)])
-def test_sample_rows_match_oracle(ops, T, top_p):
+# vocabularies of 5 chunks (one register slot), 147 chunks (three slots) and
+# 293 chunks (past the four register slots: the chunk records read from memory)
+@pytest.mark.parametrize("T,top_p,V", [(1.0, 1.0, 9000), (0.7, 0.9, 9000), (1.0, 0.95, 9000), (0.0, 1.0, 9000),
+                                       (1.0, 1.0, 300000), (0.7, 0.9, 300000), (1.0, 1.0, 600000),
+                                       (0.7, 0.9, 600000)])
+def test_sample_rows_match_oracle(ops, T, top_p, V):
     from speculative_decoding_rl_amd import _lib
     rng = np.random.Generator(np.random.PCG64(11))
-    R, V = 64, 9000
+    R = 64 if V <= 9000 else 12
     z = (rng.standard_normal((R, V)) * 1.5).astype(np.float32)
     z[0, 10] = z[0, 20] = z[0].max() + 1.0       # tie at the argmax
     z[1, ::2] = 0.25                              # many equal logits
@@ -289,10 +293,11 @@ def test_sample_rows_match_oracle(ops, T, top_p):
     assert flagged <= 1
 
 
-@pytest.mark.parametrize("T,top_p,gamma", [(1.0, 1.0, 4), (0.8, 0.9, 3), (0.0, 1.0, 4), (1.0, 1.0, 1)])
-def test_spec_decide_matches_oracle(ops, T, top_p, gamma):
+@pytest.mark.parametrize("T,top_p,gamma,V", [(1.0, 1.0, 4, 3000), (0.8, 0.9, 3, 3000), (0.0, 1.0, 4, 3000),
+                                             (1.0, 1.0, 1, 3000), (1.0, 1.0, 3, 300000), (0.8, 0.9, 2, 600000)])
+def test_spec_decide_matches_oracle(ops, T, top_p, gamma, V):
     rng = np.random.Generator(np.random.PCG64(5 + gamma))
-    B, V = 48, 3000
+    B = 48 if V <= 3000 else 8
     G1 = gamma + 1
     base = rng.standard_normal((B, G1, V)) * 1.2
     p = base.astype(np.float32)
