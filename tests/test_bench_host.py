@@ -63,3 +63,24 @@ def test_traffic_needs_every_source_unchanged(tmp_path, monkeypatch):
     assert b.measured_traffic("er::k<1>") is None
     (tmp_path / "b.hip").write_text("host\n")
     assert b.measured_traffic("er::k<1>") == 99.0
+
+
+def test_kernel_roles():
+    b = _bench()
+    assert b.kernel_role("er::k_skinny<3, 1, 2, 3>") == "draft"          # W4 drafter
+    assert b.kernel_role("er::k_linear_mfma<2, 16, 1, 8>") == "draft"    # W8 drafter
+    assert b.kernel_role("er::k_skinny<1, 1, 2, 2>") == "verify"         # bf16 target
+    assert b.kernel_role("er::k_gemm2<64, 1, 4, 64>") == "verify"
+    assert b.kernel_role("er::k_attn_mfma<128>") == "attention"
+    assert b.kernel_role("er::k_attn_combine<true>") == "attention"
+
+
+def test_more_than_one_gpu_is_refused():
+    import json
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
