@@ -296,16 +296,13 @@ __global__ __launch_bounds__(SB) void k_topp(const float* __restrict__ logits, i
   if (tid == 0) row_thr_w(stats, r, nch) = RowStats{prefix, s_any};
 }
 
-__global__ void k_stats_init(void* __restrict__ stats, int rows, int nch) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r < rows) row_thr_w(stats, r, nch) = RowStats{0u, 0x7FFFFFFF};
-}
-
 int launch_row_stats(const float* logits, int rows, int V, long ld, float T, float top_p, void* stats,
                      hipStream_t st) {
   if (rows <= 0) return 0;
   const int nch = sampler_chunks(V);
-  hipLaunchKernelGGL(k_stats_init, dim3((rows + 255) / 256), dim3(256), 0, st, stats, rows, nch);
+  // The row headers (top-p thresholds) are written by k_topp, the only case
+  // that reads them (top_p < 1 and T > 0); other readers check that flag
+  // first, so no initializing launch is needed.
   hipLaunchKernelGGL(k_chunk_stats<false>, dim3(rows, (nch + 3) / 4), dim3(SB), 0, st, logits, V, ld, T, stats, nch);
   if (T != 0.0f && top_p < 1.0f) {
     hipLaunchKernelGGL(k_topp, dim3(rows), dim3(SB), 0, st, logits, V, ld, T, top_p, stats, nch);
