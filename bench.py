@@ -241,13 +241,13 @@ def measured_traffic(kernel):
     return None
 
 
-def kernel_pass(eng, args, prompts, n, steps=32):
+def kernel_pass(eng, args, prompts, n, policy, steps=32):
     """Every linear and attention launch timed with HIP events, outside the timed rollouts:
-    prefill of the first n prompts, then `steps` speculative steps (forced, gamma adaptive) at that
-    batch, so that the drafter's and the verify pass's kernels both appear."""
+    prefill of the first n prompts, then `steps` steps under `policy` at that batch (forced
+    speculation makes the drafter's and the verify pass's kernels appear)."""
     from speculative_decoding_rl_amd import _lib
     n = min(n, len(prompts))
-    eng.set_policy(_lib.ER_POLICY_FORCE_SD)
+    eng.set_policy(policy)
     ids = eng.kv_alloc([args.prompt_len] * n, [steps * (args.gamma_max + 1) + 8] * n)
     eng.prefill(ids, list(prompts[:n]))
     eng.reset_kernel_profile()
@@ -592,12 +592,14 @@ def main():
         rf_detail["sampled_every_steps"] = args.kprof_every
         out["roofline_kernel"] = rf_detail
     if not args.no_kernel_profile:
-        kp = kernel_pass(eng, args, prompts, 64)
-        out["kernels_top"] = {"pass": "untimed: prefill 64 prompts, 32 forced SD steps, every launch timed",
+        kp = kernel_pass(eng, args, prompts, 64, _lib.ER_POLICY_AUTO)
+        out["kernels_top"] = {"pass": "untimed: prefill 64 prompts, 32 SD-auto steps, every launch timed",
                               "kernels": kernel_table(kp)}
-        kt = kernel_pass(eng, args, prompts, 4)
-        out["kernels_tail"] = {"pass": "untimed: prefill 4 prompts, 32 forced SD steps, every launch timed",
-                               "kernels": kernel_table(kt)}
+        out["kernels_sd"] = {}
+        for n in (64, 4):
+            ks = kernel_pass(eng, args, prompts, n, _lib.ER_POLICY_FORCE_SD)
+            out["kernels_sd"][f"b{n}"] = {"pass": f"untimed: prefill {n} prompts, 32 forced SD steps, every "
+                                                  "launch timed", "kernels": kernel_table(ks)}
         eng.set_policy(_lib.ER_POLICY_AUTO)
         lin = [k for k in kp if any(n in k["name"] for n in LINEAR_KERNELS)]
         if lin and rf_detail:
