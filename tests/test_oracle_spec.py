@@ -210,3 +210,30 @@ def test_gamma_zero_is_a_target_sample():
         counts[em[0]] += 1
     chi2 = float(np.sum((counts - N * p) ** 2 / (N * p)))
     assert chi2 < 7 + 5 * np.sqrt(14)
+
+
+@pytest.mark.parametrize("quant", ["w8", "w4"])
+def test_kv_after_rejection_equals_target_prefill(quant):
+    """KV rollback (speculative sampling over a shared paged KV): after every step, rows
+    0..n-1 must be the target's own K/V for the committed tokens, as a fresh target
+    prefill of prompt + emitted tokens writes them, whatever the drafter or the rejected
+    drafts wrote into those rows; the pending position n = P + len(generated) - 1 until
+    the stop length cuts the last emitted run (then only the kept tokens are compared)."""
+    cfg, W, D = _setup(V=64, quant=quant, L=2, std=0.6)
+    prompt = [5, 17, 42, 3, 9]
+    sp = SamplingParams(seed=11, temperature=1.0, top_p=1.0)
+    gamma, stop = 4, 24
+    st = spec.prefill(cfg, W, 0, prompt, stop, len(prompt) + stop + gamma + 2, sp)
+    rejected = 0
+    while not st.done:
+        rec = spec.spec_step(cfg, W, D, st, gamma, sp)
+        rejected += rec.n_accepted < gamma
+        toks = list(prompt) + st.generated[:-1]
+        m = len(toks)
+        if not st.done:
+            assert st.n == m and st.pending == st.generated[-1]
+        ref = KVStore(cfg, st.kv.capacity)
+        forward(cfg, W, toks, list(range(m)), ref)
+        np.testing.assert_allclose(st.kv.k[:, :m], ref.k[:, :m], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(st.kv.v[:, :m], ref.v[:, :m], rtol=0, atol=1e-12)
+    assert rejected > 0
