@@ -1727,7 +1727,13 @@ static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st
     case P_GEMM2:
       // split K until about one wave of work-groups (256): more splits cost
       // more in the reduction than they gain in parallelism
-      if (M <= 64) return run_gemm2<64, 1, 4>(a, ws, 256, st, info);
+      // 257..384 column tiles (7B gate/up: 296) overfill one wave of the chip
+      // by a fraction: a two-way split evens the tail (8 % at M = 33).  Below
+      // 256 tiles (14B gate/up: 216) the split costs 14 % instead.
+      if (M <= 64) {
+        const long nt = (N + 127) / 128;
+        return run_gemm2<64, 1, 4>(a, ws, nt > 256 && nt <= 384 ? 768 : 256, st, info);
+      }
       if (M <= 128) {
         if (K < 8192 && (N < 4096 || (N >= 16384 && N < 65536))) return run_gemm2<64, 1, 6>(a, ws, 256, st, info);
         return run_gemm2<128, 2, 3>(a, ws, 256, st, info);

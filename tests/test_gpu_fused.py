@@ -158,6 +158,30 @@ def test_fused_norm_swiglu(ops, fmt, M, path):
     assert np.all(np.abs(got - ref) <= tol), np.max(np.abs(got - ref) / tol)
 
 
+def test_fused_norm_swiglu_split_k(ops):
+    """SwiGLU applied by the split-K reduction: 2F = 32896 outputs are 257 column
+    tiles (more than one wave of the chip), K = 1024 is 16 k steps, so the
+    automatic choice at M = 40 splits K in two and the gate/up pairs meet in
+    the reduction."""
+    from speculative_decoding_rl_amd import _lib
+    g = torch.Generator().manual_seed(341)
+    M, F, K = 40, 16448, 1024
+    h, gain, xrow, ssq, xs = _norm_input(M, K, g)
+    (f, w, sc, zr), wd = _weights("bf16", 2 * F, K, g, ops)
+    y = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ops.linear_fused(_lib.EPI_SWIGLU, dev(h), M, f, w, 2 * F, K, y, sc, zr, xnorm=True,
+                     ssq_in=dev(ssq.view(np.int64)), gnorm=gain.cuda(), path=0)
+    torch.cuda.synchronize()
+    got = y.float().cpu().numpy().astype(np.float64)
+    gu = xs @ wd.T
+    bound = _bound(xs, wd) * BF
+    ga, up = gu[:, :F], gu[:, F:]
+    ref = silu(ga) * up
+    tol = BF * np.abs(ref) + 1.1 * np.abs(up) * bound[:, :F] + np.abs(silu(ga)) * bound[:, F:] + 1e-6
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= tol), np.max(np.abs(got - ref) / tol)
+
+
 @pytest.mark.parametrize("fmt,M,path", CASES)
 def test_fused_norm_qkv_rope_kv_append(ops, fmt, M, path):
     """W = [q; k; v]: RoPE on q, k at pos[m]; q -> q_out, k and v -> the paged pool at slot[m]."""

@@ -179,7 +179,8 @@ def test_linear_gemm_variants(ops, code, M):
     assert r < 4e-6, r
 
 
-@pytest.mark.parametrize("M,N,K", [(40, 96, 18944), (300, 200, 1152), (1000, 300, 512), (129, 4608, 384)])
+@pytest.mark.parametrize("M,N,K", [(40, 96, 18944), (300, 200, 1152), (1000, 300, 512), (129, 4608, 384),
+                                   (40, 33000, 1152), (64, 32900, 1024)])
 def test_linear_tiled_gemm(ops, M, N, K):
     # M > 32 takes the LDS-tiled GEMM (split-K with a fixed-order reduction when tiles are few)
     assert _linear_case(ops, "bf16", M, N, K, 0, seed=M) < 4e-6
