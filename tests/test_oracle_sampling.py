@@ -52,3 +52,27 @@ def test_residual():
     r = sampling.residual(p, q)
     assert np.allclose(r, [0.0, 0.5, 0.5])
     assert np.allclose(sampling.residual(p, p), p)  # zero mass falls back to p
+
+
+def test_top_p_nucleus_is_the_smallest_set_reaching_p():
+    """Nucleus sampling keeps the smallest set of tokens whose probability mass
+    reaches top_p (renormalized).  With distinct probabilities that set is unique:
+    found here by enumerating every subset of a 6-token vocabulary."""
+    import itertools
+    rng = np.random.Generator(np.random.PCG64(21))
+    for trial in range(60):
+        V = 6
+        z = rng.normal(0.0, 2.0, V)
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        top_p = float(rng.uniform(0.05, 0.995))
+        w = np.exp((z - z.max()) / T)
+        p = w / w.sum()
+        best = None
+        for k in range(1, V + 1):
+            sets = [s for s in itertools.combinations(range(V), k) if p[list(s)].sum() >= top_p]
+            if sets:
+                best = max(sets, key=lambda s: p[list(s)].sum())
+                break
+        want = np.zeros(V)
+        want[list(best)] = p[list(best)] / p[list(best)].sum()
+        np.testing.assert_allclose(sampling.pi(z, T, top_p), want, rtol=1e-12, atol=0)
