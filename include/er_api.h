@@ -66,7 +66,8 @@ extern "C" {
 #define ER_POLICY_AUTO      0   /* roofline toggle + adaptive gamma; while it stays
                                    autoregressive where alpha_init would make speculation
                                    pay, a speculative probe step refreshes the EMA (after
-                                   32 steps, the gap doubling to at most 1024) */
+                                   32 steps, the gap doubling to at most 1024; see
+                                   er_controller_plan) */
 #define ER_POLICY_FORCE_SD  1   /* always speculate (gamma adaptive unless pinned) */
 #define ER_POLICY_FORCE_AR  2   /* never speculate */
 #define ER_POLICY_TIMING    3   /* measured-timing guard (er_guard_* below) chooses
@@ -312,6 +313,47 @@ double er_expected_tokens(double alpha, int gamma);
 /* The cost model a context's controller uses (roofline constants as given or
  * as calibrated at init). */
 int er_get_cost_model(const er_ctx *ctx, er_cost_model *out);
+
+/* Modelled step times of the controller (EfficientRollout "关键模块" item 2:
+ * decode latency from a roofline, per-GPU constants): *t_ar = T(AR step),
+ * *t_sd = gamma T(draft forward) + T(verify forward), each forward
+ * T = t_fwd + max(bytes / hbm_bytes_per_s, flops / flops_per_s) with
+ *   AR:     bytes = wb P + B C kvb + B kvb + 4 B V,   flops = 2 P B + 4 B C hq hd L
+ *   draft:  bytes = bq P + B C kvb + B kvb + 4 B V,   flops = 2 P B + 4 B C hq hd L
+ *   verify: bytes = wb P + B C kvb + B (g+1) kvb + 4 B (g+1) V,
+ *           flops = 2 P B (g+1) + 4 B (g+1) C hq hd L
+ * (P = streamed linear parameters incl. lm_head, wb / bq = target / drafter
+ * bytes per parameter, kvb = KV bytes per token over all layers, C = mean
+ * committed context).  Either output may be NULL.  ER_EINVAL on batch < 1,
+ * gamma < 1 or non-positive rates. */
+int er_controller_times(const er_cost_model *m, int batch, double mean_ctx, int gamma, double *t_ar,
+                        double *t_sd);
+
+/* State of the roofline policy between steps: the last recorded choice
+ * (0 = AR, -1 = none yet), consecutive AR choices since the last probe or
+ * speculative choice, and the current probe gap (0 = not started). */
+typedef struct er_plan_state {
+  int32_t choice, ar_streak, probe_every;
+} er_plan_state;
+/* One step of the policy a context runs under ER_POLICY_AUTO / FORCE_SD /
+ * FORCE_AR, as a pure host function over caller-held state (EfficientRollout
+ * "关键模块" items 2-3; History Tree Dynamic RL section 2.2 margin).
+ * FORCE_AR: 0.  FORCE_SD: the argmax over [gamma_lo, gamma_hi] with the
+ * current choice kept unless beaten by `margin`.  AUTO: the same over
+ * {0 (AR)} U [gamma_lo, gamma_hi]; while the choice stays AR where alpha_init
+ * would make speculation pay, every probe_every-th consecutive AR choice
+ * returns the speculative argmax at alpha_ema instead (a probe that refreshes
+ * the acceptance estimate; the recorded choice stays AR), the gap starting at
+ * 32 and doubling up to 1024 after each probe, reset by a speculative choice.
+ * The pages leave the refresh of the estimate while speculation is off
+ * unstated; this schedule is the library's reading.  ER_EINVAL on a null
+ * pointer, batch < 1, a bad range or another policy. */
+int er_controller_plan(const er_cost_model *m, er_plan_state *st, int policy, int batch, double mean_ctx,
+                       double alpha_ema, double alpha_init, int gamma_lo, int gamma_hi, double margin,
+                       int *gamma_out);
+/* The policy state of a context (as er_controller_plan would receive it for
+ * the next step). */
+int er_get_plan_state(const er_ctx *ctx, er_plan_state *out);
 
 /* Measured-timing guard of the SD toggle (the timing_guard policy of the
  * History Tree Dynamic RL page, section 2.2 parameters and section 3.3 logic,

@@ -115,8 +115,9 @@ def score(m: ModelCost, r: Roofline, B: int, C: float, alpha: float, g: int) -> 
 
 
 def choose(m: ModelCost, r: Roofline, B: int, C: float, alpha: float, g_min: int, g_max: int,
-           current: int = -1, margin: float = 1.02) -> int:
-    cands = [0] + list(range(g_min, g_max + 1))
+           current: int = -1, margin: float = 1.02, allow_ar: bool = True) -> int:
+    """allow_ar=False restricts the argmax to speculation (the forced-SD policy and probes)."""
+    cands = ([0] if allow_ar else []) + list(range(g_min, g_max + 1))
     best, best_s = 0, -1.0
     for g in cands:
         s = score(m, r, B, C, alpha, g)
@@ -126,6 +127,51 @@ def choose(m: ModelCost, r: Roofline, B: int, C: float, alpha: float, g_min: int
         if best_s <= margin * score(m, r, B, C, alpha, current):
             return current
     return best
+
+
+# ---------------------------------------------------------------------------
+# The step-by-step policy around choose().  The acceptance estimate moves only
+# on speculative steps, and the pages do not say how it is refreshed while the
+# toggle holds AR.  Reading used here: while the choice stays AR in a regime
+# where the initial estimate alpha_init would make speculation pay, every
+# probe_every-th consecutive AR choice runs one speculative step instead (the
+# recorded choice stays AR); the gap starts at 32 and doubles after each probe
+# up to 1024, and a speculative choice resets it to 32.
+# ---------------------------------------------------------------------------
+POLICY_AUTO, POLICY_FORCE_SD, POLICY_FORCE_AR = 0, 1, 2
+PROBE_FIRST, PROBE_MAX = 32, 1024
+
+
+@dataclass
+class PlanState:
+    choice: int = -1       # last recorded choice, 0 = AR, -1 = none yet
+    ar_streak: int = 0     # consecutive AR choices since the last probe / speculative choice
+    probe_every: int = 0   # current probe gap, 0 = not started
+
+
+def plan(m: ModelCost, r: Roofline, st: PlanState, policy: int, B: int, C: float, alpha_ema: float,
+         alpha_init: float, g_lo: int, g_hi: int, margin: float = 1.02) -> int:
+    """Draft length to run this step (0 = AR); updates st."""
+    if policy == POLICY_FORCE_AR:
+        return 0
+    allow_ar = policy == POLICY_AUTO
+    g = choose(m, r, B, C, alpha_ema, g_lo, g_hi, current=st.choice, margin=margin, allow_ar=allow_ar)
+    st.choice = g
+    if g > 0 or not allow_ar:
+        st.ar_streak = 0
+        if g > 0:
+            st.probe_every = PROBE_FIRST
+        return g
+    if st.probe_every <= 0:
+        st.probe_every = PROBE_FIRST
+    st.ar_streak += 1
+    if st.ar_streak < st.probe_every:
+        return 0
+    st.ar_streak = 0
+    if choose(m, r, B, C, alpha_init, g_lo, g_hi, current=-1, margin=1.0) == 0:
+        return 0          # speculation would not pay even at the prior: no probe
+    st.probe_every = min(2 * st.probe_every, PROBE_MAX)
+    return choose(m, r, B, C, alpha_ema, g_lo, g_hi, current=-1, margin=1.0, allow_ar=False)
 
 
 def ema(alpha_ema: float, alpha_step: float, beta: float = 0.3) -> float:

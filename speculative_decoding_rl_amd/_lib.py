@@ -82,6 +82,10 @@ class CostModel(C.Structure):
                 ("hbm_bytes_per_s", C.c_double), ("flops_per_s", C.c_double), ("t_fwd_s", C.c_double)]
 
 
+class PlanState(C.Structure):
+    _fields_ = [("choice", C.c_int32), ("ar_streak", C.c_int32), ("probe_every", C.c_int32)]
+
+
 ER_GUARD_BUCKETS = 16
 
 
@@ -143,6 +147,11 @@ SIGNATURES = {
                                        C.c_int, C.c_double, C.POINTER(C.c_int)]),
     "er_expected_tokens": (C.c_double, [C.c_double, C.c_int]),
     "er_get_cost_model": (C.c_int, [P, C.POINTER(CostModel)]),
+    "er_controller_times": (C.c_int, [C.POINTER(CostModel), C.c_int, C.c_double, C.c_int,
+                                      C.POINTER(C.c_double), C.POINTER(C.c_double)]),
+    "er_controller_plan": (C.c_int, [C.POINTER(CostModel), C.POINTER(PlanState), C.c_int, C.c_int, C.c_double,
+                                     C.c_double, C.c_double, C.c_int, C.c_int, C.c_double, C.POINTER(C.c_int)]),
+    "er_get_plan_state": (C.c_int, [P, C.POINTER(PlanState)]),
     "er_guard_default_params": (None, [C.POINTER(GuardParams)]),
     "er_guard_init": (C.c_int, [C.POINTER(GuardState), C.POINTER(GuardParams)]),
     "er_guard_choose": (C.c_int, [C.POINTER(GuardState), C.c_int]),

@@ -120,9 +120,7 @@ struct er_ctx {
   double alpha_ema = 0.8;
   double alpha_init = 0.8;
   int gamma_pinned = 0;
-  int choice = -1;        // last controller choice (0 = AR), -1 none yet
-  int ar_streak = 0;      // consecutive autoregressive steps chosen by the controller
-  int probe_every = 0;    // autoregressive steps between acceptance probes (0: kAlphaProbe)
+  PlanState plan;         // roofline policy state: last choice (0 = AR, -1 none), probe schedule
   int policy = ER_POLICY_AUTO;
   er_guard_state guard{};  // measured-timing guard (ER_POLICY_TIMING)
 
@@ -1048,9 +1046,6 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   return ER_OK;
 }
 
-constexpr int kAlphaProbe = 32;
-constexpr int kAlphaProbeMax = 1024;
-
 // Controller choice for this batch (0 = AR).
 int plan(er_ctx* c, int n, const int32_t* ids) {
   if (c->policy == ER_POLICY_FORCE_AR) return 0;
@@ -1062,35 +1057,16 @@ int plan(er_ctx* c, int n, const int32_t* ids) {
   if (c->policy == ER_POLICY_TIMING) {
     // the guard picks the branch from measured tokens/ms; the draft length
     // when it speculates is the acceptance-aware argmax over gamma >= 1
-    if (er_guard_choose(&c->guard, n) != 1) return c->choice = 0;
-    return c->choice = choose(c->cost, n, C, c->alpha_ema, lo, hi, false, -1, 1.0);
+    if (er_guard_choose(&c->guard, n) != 1) return c->plan.choice = 0;
+    return c->plan.choice = choose(c->cost, n, C, c->alpha_ema, lo, hi, false, -1, 1.0);
   }
-  const bool allow_ar = c->policy == ER_POLICY_AUTO;
-  const int cur = c->choice;
-  const int g = choose(c->cost, n, C, c->alpha_ema, lo, hi, allow_ar, cur, c->rd.switch_margin);
-  c->choice = g;
-  if (g > 0 || !allow_ar) {
-    c->ar_streak = 0;
-    if (g > 0) c->probe_every = kAlphaProbe;
-    return g;
-  }
-  // The acceptance estimate only moves on speculative steps.  While the
-  // controller stays autoregressive in a regime where the initial estimate
-  // would make speculation pay, a speculative probe step refreshes it (the
-  // choice itself stays AR).  Probes start kAlphaProbe steps apart and the
-  // gap doubles (up to kAlphaProbeMax) each time the controller stays
-  // autoregressive after one, so a steady low acceptance costs few probes.
-  if (c->probe_every <= 0) c->probe_every = kAlphaProbe;
-  if (++c->ar_streak < c->probe_every) return 0;
-  c->ar_streak = 0;
-  if (choose(c->cost, n, C, c->alpha_init, lo, hi, true, -1, 1.0) == 0) return 0;
-  c->probe_every = std::min(2 * c->probe_every, kAlphaProbeMax);
-  return choose(c->cost, n, C, c->alpha_ema, lo, hi, false, -1, 1.0);
+  return plan_step(c->cost, c->plan, c->policy == ER_POLICY_AUTO, n, C, c->alpha_ema, c->alpha_init, lo, hi,
+                   c->rd.switch_margin);
 }
 
 int current_gamma(er_ctx* c) {
   if (c->gamma_pinned) return c->gamma_pinned;
-  if (c->choice > 0) return c->choice;
+  if (c->plan.choice > 0) return c->plan.choice;
   return c->rd.gamma_init;
 }
 
@@ -1794,7 +1770,7 @@ int er_set_gamma(er_ctx* c, int gamma) {
   if (!c) return ER_EINVAL;
   if (gamma < 0 || gamma > c->rd.gamma_max) return fail(c, ER_EINVAL, "gamma %d outside 0..%d", gamma, c->rd.gamma_max);
   c->gamma_pinned = gamma;
-  if (gamma > 0 && c->choice > 0) c->choice = gamma;
+  if (gamma > 0 && c->plan.choice > 0) c->plan.choice = gamma;
   return ER_OK;
 }
 
@@ -1809,7 +1785,7 @@ int er_set_policy(er_ctx* c, int policy) {
     }
   }
   c->policy = policy;
-  c->choice = -1;
+  c->plan.choice = -1;
   return ER_OK;
 }
 
@@ -1845,8 +1821,8 @@ int er_get_stats(er_ctx* c, er_stats* out) {
   s.effective_length = s.effective_times ? (double)s.total_right_length / (double)s.effective_times : 0.0;
   s.effective_percent = s.predict_times ? (double)s.effective_times / (double)s.predict_times : 0.0;
   s.alpha_ema = c->alpha_ema;
-  s.gamma = c->choice < 0 ? current_gamma(c) : c->choice;
-  s.mode = c->choice == 0 ? ER_MODE_AR : ER_MODE_SD;
+  s.gamma = c->plan.choice < 0 ? current_gamma(c) : c->plan.choice;
+  s.mode = c->plan.choice == 0 ? ER_MODE_AR : ER_MODE_SD;
   *out = s;
   return ER_OK;
 }
@@ -1855,9 +1831,7 @@ int er_reset_stats(er_ctx* c) {
   if (!c) return ER_EINVAL;
   c->stats = er_stats{};
   c->alpha_ema = c->alpha_init;
-  c->choice = -1;
-  c->ar_streak = 0;
-  c->probe_every = kAlphaProbe;
+  c->plan = PlanState{};
   {
     er_guard_params gp = c->guard.p;
     er_guard_init(&c->guard, &gp);
@@ -2048,16 +2022,53 @@ int er_get_guard(const er_ctx* c, er_guard_state* out) {
   return ER_OK;
 }
 
+static CostModel cost_of(const er_cost_model* m) {
+  return CostModel{m->n_layers, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, m->ffn, m->vocab,
+                   m->w_bytes, m->q_bytes, m->kv_bytes_el, m->hbm_bytes_per_s, m->flops_per_s, m->t_fwd_s};
+}
+
 int er_controller_choose(const er_cost_model* m, int batch, double mean_ctx, double alpha, int gamma_min,
                          int gamma_max, int current, double margin, int* gamma_out) {
   if (!m || !gamma_out || batch <= 0 || gamma_min < 1 || gamma_max < gamma_min) return ER_EINVAL;
-  CostModel cm{m->n_layers, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, m->ffn, m->vocab,
-               m->w_bytes, m->q_bytes, m->kv_bytes_el, m->hbm_bytes_per_s, m->flops_per_s, m->t_fwd_s};
-  *gamma_out = choose(cm, batch, mean_ctx, alpha, gamma_min, gamma_max, true, current, margin);
+  *gamma_out = choose(cost_of(m), batch, mean_ctx, alpha, gamma_min, gamma_max, true, current, margin);
   return ER_OK;
 }
 
 double er_expected_tokens(double alpha, int gamma) { return expected_tokens(alpha, gamma); }
+
+int er_controller_times(const er_cost_model* m, int batch, double mean_ctx, int gamma, double* t_ar, double* t_sd) {
+  if (!m || batch <= 0 || gamma < 1 || !(m->hbm_bytes_per_s > 0) || !(m->flops_per_s > 0)) return ER_EINVAL;
+  const CostModel cm = cost_of(m);
+  if (t_ar) *t_ar = ar_time(cm, batch, mean_ctx);
+  if (t_sd) *t_sd = sd_time(cm, batch, mean_ctx, gamma);
+  return ER_OK;
+}
+
+int er_controller_plan(const er_cost_model* m, er_plan_state* st, int policy, int batch, double mean_ctx,
+                       double alpha_ema, double alpha_init, int gamma_lo, int gamma_hi, double margin,
+                       int* gamma_out) {
+  if (!m || !st || !gamma_out || batch <= 0 || gamma_lo < 1 || gamma_hi < gamma_lo) return ER_EINVAL;
+  if (policy != ER_POLICY_AUTO && policy != ER_POLICY_FORCE_SD && policy != ER_POLICY_FORCE_AR) return ER_EINVAL;
+  if (policy == ER_POLICY_FORCE_AR) { *gamma_out = 0; return ER_OK; }
+  PlanState ps;
+  ps.choice = st->choice;
+  ps.ar_streak = st->ar_streak;
+  ps.probe_every = st->probe_every;
+  *gamma_out = plan_step(cost_of(m), ps, policy == ER_POLICY_AUTO, batch, mean_ctx, alpha_ema, alpha_init, gamma_lo,
+                         gamma_hi, margin);
+  st->choice = ps.choice;
+  st->ar_streak = ps.ar_streak;
+  st->probe_every = ps.probe_every;
+  return ER_OK;
+}
+
+int er_get_plan_state(const er_ctx* c, er_plan_state* out) {
+  if (!c || !out) return ER_EINVAL;
+  out->choice = c->plan.choice;
+  out->ar_streak = c->plan.ar_streak;
+  out->probe_every = c->plan.probe_every;
+  return ER_OK;
+}
 
 int er_get_cost_model(const er_ctx* c, er_cost_model* out) {
   if (!c || !out) return ER_EINVAL;

@@ -101,4 +101,39 @@ struct AlphaAcc {
 
 inline double ema(double prev, double sample, double beta) { return (1.0 - beta) * prev + beta * sample; }
 
+// Acceptance probes of the roofline policy.  The acceptance estimate only
+// moves on speculative steps; while the policy keeps choosing AR in a regime
+// where the initial estimate would make speculation pay, every probe_every-th
+// consecutive AR choice becomes one speculative step (the recorded choice stays
+// AR).  The gap starts at kProbeFirst and doubles, up to kProbeMax, after each
+// probe; a speculative choice resets it.  The pages do not say how the
+// estimate is refreshed while speculation is off; this is the reading used.
+constexpr int kProbeFirst = 32;
+constexpr int kProbeMax = 1024;
+
+struct PlanState {
+  int choice = -1;       // last recorded choice (0 = AR), -1 none yet
+  int ar_streak = 0;     // consecutive AR choices since the last probe or speculative choice
+  int probe_every = 0;   // current gap (0: kProbeFirst)
+};
+
+// One step of the roofline policy (allow_ar: the roofline toggle may choose
+// AR; false forces speculation).  Returns the gamma to run (0 = AR).
+inline int plan_step(const CostModel& m, PlanState& s, bool allow_ar, int B, double C, double alpha_ema,
+                     double alpha_init, int g_lo, int g_hi, double margin) {
+  const int g = choose(m, B, C, alpha_ema, g_lo, g_hi, allow_ar, s.choice, margin);
+  s.choice = g;
+  if (g > 0 || !allow_ar) {
+    s.ar_streak = 0;
+    if (g > 0) s.probe_every = kProbeFirst;
+    return g;
+  }
+  if (s.probe_every <= 0) s.probe_every = kProbeFirst;
+  if (++s.ar_streak < s.probe_every) return 0;
+  s.ar_streak = 0;
+  if (choose(m, B, C, alpha_init, g_lo, g_hi, true, -1, 1.0) == 0) return 0;
+  s.probe_every = std::min(2 * s.probe_every, kProbeMax);
+  return choose(m, B, C, alpha_ema, g_lo, g_hi, false, -1, 1.0);
+}
+
 }  // namespace er

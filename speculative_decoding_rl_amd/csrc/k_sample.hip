@@ -23,7 +23,13 @@
 //
 // Top-p (< 1): the nucleus threshold is found per row by a radix select over
 // the order-preserving key of the logit (ties in index order), then the chunk
-// masses are recomputed over the kept tokens only.
+// masses are recomputed over the kept tokens only.  The radix histograms add
+// each token's weight as a 64-bit fixed-point integer (units of 2^-44; a
+// weight is at most 1, so a row of up to 2^20 tokens cannot overflow), so the
+// bins are exact sums whatever order the threads add in and the threshold is
+// the same on every run; a bin sum differs from the exact real sum by at most
+// half a unit per token (V * 2^-45, 4.3e-9 at V = 152064, against a row mass
+// of at least 1).
 
 #include "common.h"
 #include "kernels.h"
@@ -216,32 +222,35 @@ __global__ __launch_bounds__(SB) void k_topp(const float* __restrict__ logits, i
   const int r = blockIdx.x;
   const float* z = logits + (long)r * ld;
   const int tid = threadIdx.x;
-  __shared__ double hist[256];
+  __shared__ unsigned long long hist[256];
   __shared__ uint32_t s_prefix;
-  __shared__ double s_above;
+  __shared__ unsigned long long s_above;
   __shared__ int s_cnt[SB];
   __shared__ int s_any;
+  constexpr double FX = 17592186044416.0;  // 2^44: fixed-point units per unit of weight
   const RowView rv = row_view(row_chunks(stats, r, nch), nch, T);
   const double M = rv.M;
   const double target = (double)top_p * rv.S;
+  const double target_fx = target * FX;
   uint32_t prefix = 0, mask = 0;
-  double above = 0.0;
+  unsigned long long above = 0;
   for (int d = 3; d >= 0; --d) {
-    for (int b = tid; b < 256; b += SB) hist[b] = 0.0;
+    for (int b = tid; b < 256; b += SB) hist[b] = 0ull;
     __syncthreads();
     for (int i = tid; i < V; i += SB) {
       const uint32_t k = float_key(z[i]);
-      if ((k & mask) == prefix) atomicAdd(&hist[(k >> (8 * d)) & 255u], exp(((double)z[i] - M) / (double)T));
+      if ((k & mask) == prefix)
+        atomicAdd(&hist[(k >> (8 * d)) & 255u], (unsigned long long)rint(exp(((double)z[i] - M) / (double)T) * FX));
     }
     __syncthreads();
     if (tid == 0) {
       // highest bin whose cumulative mass reaches the target; if rounding
       // leaves none, the lowest non-empty bin (so the bin always holds tokens)
-      double cum = above, cum_last = above;
+      unsigned long long cum = above, cum_last = above;
       int chosen = -1, last_nz = -1;
       for (int b = 255; b >= 0; --b) {
-        if (hist[b] > 0.0) {
-          if (cum + hist[b] >= target) { chosen = b; break; }
+        if (hist[b] > 0ull) {
+          if ((double)(cum + hist[b]) >= target_fx) { chosen = b; break; }
           last_nz = b;
           cum_last = cum;
         }
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(SB) void k_topp(const float* __restrict__ logits, i
     return;
   }
   const double wt = exp(((double)z[s_any] - M) / (double)T);
-  int c = (int)ceil((target - above) / wt);
+  int c = (int)ceil((target - (double)above / FX) / wt);
   if (c < 1) c = 1;
   const int chunk = (V + SB - 1) / SB;
   const int lo = tid * chunk, hi = min(V, lo + chunk);
@@ -305,6 +314,7 @@ int launch_row_stats(const float* logits, int rows, int V, long ld, float T, flo
   // first, so no initializing launch is needed.
   hipLaunchKernelGGL(k_chunk_stats<false>, dim3(rows, (nch + 3) / 4), dim3(SB), 0, st, logits, V, ld, T, stats, nch);
   if (T != 0.0f && top_p < 1.0f) {
+    if (V > (1 << 20)) return -1;  // the fixed-point radix histogram holds rows of up to 2^20 tokens
     hipLaunchKernelGGL(k_topp, dim3(rows), dim3(SB), 0, st, logits, V, ld, T, top_p, stats, nch);
     hipLaunchKernelGGL(k_chunk_stats<true>, dim3(rows, (nch + 3) / 4), dim3(SB), 0, st, logits, V, ld, T, stats, nch);
   }

@@ -40,9 +40,10 @@ struct Meta {
 // unit length aims at ~256 work-groups over all KV heads (one per compute
 // unit: fewer, longer units keep each wave's block ring full, and a long
 // sequence no longer sets the kernel time alone; from a sweep of 128 / 256 /
-// 512 / 1024 / 2048 on MI355X at batch 1..128 and 4k/8k context) but never
-// goes below 8 blocks; an item's units split its blocks evenly, and an item
-// that fits in one unit is not split (no combine for it).  Then the list of
+// 512 / 1024 / 2048 on MI355X at batch 1..128 and 4k/8k context); the target
+// is at least 8 blocks, an item of nblk blocks is cut into ceil(nblk/target)
+// even units (so at most ceil(nblk/8) units, each over half the target), and
+// an item that fits in one unit is not split (no combine for it).  Then the list of
 // the items that were split ([n] entries, n_split used), and the most units
 // of one item.  *o_rec gets the offset of one record per unit, eight int32
 // each: item, split index | units of the item << 16, first block, blocks per

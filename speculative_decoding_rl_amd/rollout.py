@@ -185,6 +185,12 @@ class Engine:
         check(self.lib.er_get_cost_model(self.ctx, C.byref(m)), self.ctx, "er_get_cost_model")
         return {f: getattr(m, f) for f, _ in m._fields_}
 
+    def plan_state(self) -> dict:
+        """State of the roofline policy (last choice, AR streak, probe gap)."""
+        st = _lib.PlanState()
+        check(self.lib.er_get_plan_state(self.ctx, C.byref(st)), self.ctx, "er_get_plan_state")
+        return dict(choice=st.choice, ar_streak=st.ar_streak, probe_every=st.probe_every)
+
     def guard(self) -> dict:
         """State of the measured-timing guard (policy ER_POLICY_TIMING)."""
         g = _lib.GuardState()
@@ -240,4 +246,27 @@ def controller_choose(cost: dict, batch: int, mean_ctx: float, alpha: float, gam
     g = C.c_int()
     check(lib.er_controller_choose(C.byref(m), batch, mean_ctx, alpha, gamma_min, gamma_max, current, margin,
                                    C.byref(g)), None, "er_controller_choose")
+    return g.value
+
+
+def controller_times(cost: dict, batch: int, mean_ctx: float, gamma: int):
+    """(AR step time, SD step time at gamma) of the library's cost model."""
+    lib = _lib.load()
+    m = _lib.CostModel(**cost)
+    ta, ts = C.c_double(), C.c_double()
+    check(lib.er_controller_times(C.byref(m), batch, mean_ctx, gamma, C.byref(ta), C.byref(ts)), None,
+          "er_controller_times")
+    return ta.value, ts.value
+
+
+def controller_plan(cost: dict, state: dict, policy: int, batch: int, mean_ctx: float, alpha_ema: float,
+                    alpha_init: float, gamma_lo: int, gamma_hi: int, margin: float = 1.02) -> int:
+    """One step of the library's roofline policy; `state` (choice, ar_streak, probe_every) is updated in place."""
+    lib = _lib.load()
+    m = _lib.CostModel(**cost)
+    st = _lib.PlanState(state["choice"], state["ar_streak"], state["probe_every"])
+    g = C.c_int()
+    check(lib.er_controller_plan(C.byref(m), C.byref(st), policy, batch, mean_ctx, alpha_ema, alpha_init, gamma_lo,
+                                 gamma_hi, margin, C.byref(g)), None, "er_controller_plan")
+    state.update(choice=st.choice, ar_streak=st.ar_streak, probe_every=st.probe_every)
     return g.value

@@ -2,7 +2,11 @@
 // with g++ and the address/undefined-behaviour sanitizers by
 // tests/test_host_abi.py: on random batches the units cover every item's key
 // blocks exactly once, the per-unit records agree with the unit table, and a
-// metadata region that is too small fails cleanly.
+// metadata region that is too small fails cleanly.  Prefill-shaped batches
+// too: one sequence's chunk of up to 4096 prompt tokens cut into items of
+// qmax = 64 / (n_q_heads / n_kv_heads) queries at consecutive positions, for
+// prompts of up to 15000 tokens filled chunk after chunk into one region (as
+// er_prefill does, each fill starting from a reset region).
 #include <algorithm>
 #include <cassert>
 #include <cstdio>
@@ -12,6 +16,54 @@
 #include "../../speculative_decoding_rl_amd/csrc/work_units.h"
 
 using namespace er;
+
+// Split n items into the region and check every invariant; returns the number of units.
+static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0, const std::vector<int32_t>& cnt,
+                       const std::vector<int32_t>& row0, const std::vector<int32_t>& btrow) {
+  int nu_tot = -1, ns = -1, mu = -1;
+  size_t o_rec = 0;
+  const size_t off = push_units(M, n, hkv, pos0.data(), cnt.data(), row0.data(), btrow.data(), &nu_tot, &ns, &mu,
+                                &o_rec);
+  assert(M.ok);
+  assert(M.used <= M.cap);
+  const int32_t* us = (const int32_t*)(M.h + off);
+  const int32_t* rec = (const int32_t*)(M.h + o_rec);
+  assert(us[0] == 0 && us[n] == nu_tot);
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
+  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 255) / 256));
+  int split_seen = 0, most = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
+    const int nu = us[i + 1] - us[i];
+    const int bpu = us[n + 1 + i];
+    assert(nu >= 1 && bpu >= 1);
+    // the units cover the blocks: the last one is non-empty and none runs past the end
+    assert((int64_t)bpu * nu >= nblk && (int64_t)bpu * (nu - 1) < nblk);
+    // an item that fits one unit is not split; a split item has at most ceil(nblk / 8) units (the
+    // bound the partials area and the combine are sized by) of more than half the target each
+    assert((nblk <= target) == (nu == 1));
+    assert(nu <= (nblk + 7) / 8 || nu == 1);
+    if (nu > 1) assert(2 * (int64_t)bpu > target);
+    if (nu > 1) {
+      assert(us[2 * n + 1 + split_seen] == i);
+      ++split_seen;
+    }
+    most = std::max(most, nu);
+    for (int k = 0; k < nu; ++k) {
+      const int32_t* r = rec + (size_t)8 * (us[i] + k);
+      assert(r[0] == i && (r[1] & 0xFFFF) == k && (r[1] >> 16) == nu);
+      assert(r[2] == k * bpu && r[3] == bpu);
+      // every unit starts inside its item's blocks
+      assert((int64_t)r[2] < nblk);
+      assert(r[4] == cnt[i] && r[5] == pos0[i] && r[6] == row0[i] && r[7] == btrow[i]);
+    }
+  }
+  assert(split_seen == ns && most == mu);
+  // about 256 (unit, KV head) pairs once the target is neither floored nor capped
+  if (target > 8 && target < 1024) assert((int64_t)nu_tot * hkv <= 256 + (int64_t)n * hkv);
+  return nu_tot;
+}
 
 int main() {
   std::mt19937 rng(11);
@@ -33,43 +85,7 @@ int main() {
     M.d = buf.data();
     M.cap = buf.size();
     M.reset();
-    int nu_tot = -1, ns = -1, mu = -1;
-    size_t o_rec = 0;
-    const size_t off = push_units(M, n, hkv, pos0.data(), cnt.data(), row0.data(), btrow.data(), &nu_tot, &ns, &mu,
-                                  &o_rec);
-    assert(M.ok);
-    const int32_t* us = (const int32_t*)(M.h + off);
-    const int32_t* rec = (const int32_t*)(M.h + o_rec);
-    assert(us[0] == 0 && us[n] == nu_tot);
-    int64_t total = 0;
-    for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-    const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 255) / 256));
-    int split_seen = 0, most = 0;
-    for (int i = 0; i < n; ++i) {
-      const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-      const int nu = us[i + 1] - us[i];
-      const int bpu = us[n + 1 + i];
-      assert(nu >= 1 && bpu >= 1);
-      // the units cover the blocks: the last one is non-empty and none runs past the end
-      assert((int64_t)bpu * nu >= nblk && (int64_t)bpu * (nu - 1) < nblk);
-      // an item that fits one unit is not split; units hold at least min(nblk, 8) blocks
-      assert((nblk <= target) == (nu == 1));
-      assert(bpu >= std::min<int64_t>(nblk, 8));
-      if (nu > 1) {
-        assert(us[2 * n + 1 + split_seen] == i);
-        ++split_seen;
-      }
-      most = std::max(most, nu);
-      for (int k = 0; k < nu; ++k) {
-        const int32_t* r = rec + (size_t)8 * (us[i] + k);
-        assert(r[0] == i && (r[1] & 0xFFFF) == k && (r[1] >> 16) == nu);
-        assert(r[2] == k * bpu && r[3] == bpu);
-        assert(r[4] == cnt[i] && r[5] == pos0[i] && r[6] == row0[i] && r[7] == btrow[i]);
-      }
-    }
-    assert(split_seen == ns && most == mu);
-    // about 256 (unit, KV head) pairs once the target is neither floored nor capped
-    if (target > 8 && target < 1024) assert((int64_t)nu_tot * hkv <= 256 + (int64_t)n * hkv);
+    check_split(M, n, hkv, pos0, cnt, row0, btrow);
     // a region too small for the records: not ok, nothing written past it
     Meta S;
     std::vector<char> small(4 * (3 * (size_t)n + 1));  // the unit table fits, the records do not
@@ -82,6 +98,38 @@ int main() {
     push_units(S, n, hkv, pos0.data(), cnt.data(), row0.data(), btrow.data(), &a, &b, &c, &o2);
     assert(!S.ok);
   }
+  // prefill-shaped batches: chunks of one long prompt, filled one after another into one region of
+  // the library's size (64 MiB), items of qmax queries at consecutive positions
+  std::vector<char> region((size_t)64 << 20);
+  const int prompts[] = {700, 2560, 4096, 9000, 15000, 15001};
+  const int qmaxes[] = {9, 64};    // 64 / group size for the 7B shape (group 7) and for MHA
+  const int chunks[] = {256, 4096};
+  for (int plen : prompts)
+    for (int qmax : qmaxes)
+      for (int chunk : chunks)
+        for (int hkv : {4, 8}) {
+          int fills = 0;
+          for (int c0 = 0; c0 < plen; c0 += chunk) {
+            const int cn = std::min(chunk, plen - c0);
+            const int n = (cn + qmax - 1) / qmax;
+            std::vector<int32_t> pos0(n), cnt(n), row0(n), btrow(n, 3);
+            for (int k = 0; k < n; ++k) {
+              pos0[k] = c0 + k * qmax;
+              cnt[k] = std::min(qmax, cn - k * qmax);
+              row0[k] = k * qmax;
+            }
+            Meta M;
+            M.h = region.data();
+            M.d = region.data();
+            M.cap = region.size();
+            M.reset();
+            // the rows of one chunk: positions c0 .. c0 + cn - 1, each item's queries inside the chunk
+            assert(row0[n - 1] + cnt[n - 1] == cn);
+            check_split(M, n, hkv, pos0, cnt, row0, btrow);
+            ++fills;
+          }
+          assert(fills == (plen + chunk - 1) / chunk);
+        }
   std::printf("work_units ok\n");
   return 0;
 }

@@ -7,13 +7,29 @@ GPU's tokens exactly), runs the sampler on its own logits (must agree unless
 the step is flagged), and then commits the GPU's tokens so that one boundary
 case does not cascade.
 
-Flags (decisions that rounding may legitimately flip): an acceptance test
-whose ratio p/q lies within 1e-3 of the uniform draw, a greedy decision whose
-top-2 logit margin is under 1e-2, and -- for categorical draws, which those two
-rules do not cover -- a draw whose outcome flips when the oracle's logits
-replace the GPU's.
+Flags (decisions that rounding may legitimately flip).  A step whose
+decision differs between the GPU's and the oracle's logits is flagged only if
+the difference is explained by the logit error measured on that step; any
+other difference is an unflagged mismatch.
+
+* Greedy (T = 0): the top-2 logit margin at a tested position is under
+  max(1e-2, 2 eps), eps the larger max |logit difference| of the two rows.
+* Acceptance tests: |p/q - u| < 1e-3 (the rule of the parity contract), or
+  within the ratio's own error bound: p/q moves by at most a factor
+  exp(2 (eps_p + eps_q) / T) when every logit moves by at most eps (softmax
+  ratios move by exp(eps/T) per logit and by the same bound through the
+  normalizer).
+* Categorical draws (residual or bonus), same accept count: u lies within
+  delta of an edge of the drawn token's CDF interval, with delta bounding how
+  far the normalized CDF can move: kappa = exp(2 eps / T) - 1 per
+  distribution; delta = kappa_p for the bonus draw from p;
+  delta = 2 (kappa_p + kappa_q) / S for the residual max(0, p - q) of mass S.
+* Nucleus (top_p < 1): the kept sets of the two rows differ and the mass
+  before or after the last kept token lies within kappa of top_p.
 """
 from __future__ import annotations
+
+from contextlib import contextmanager
 
 import numpy as np
 
@@ -30,6 +46,25 @@ def rel_err(got, ref):
 
 def abs_err(got, ref):
     return float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
+
+
+@contextmanager
+def perturbed_stores(rel, rng):
+    """Run the oracle with every stored (rounded) value perturbed before its rounding by a relative
+    N(0, rel) amount: the spread this gives is how far a different fp32 accumulation order (which
+    moves pre-rounding values by a few ulps) can move the oracle's own logits."""
+    import oracle.model as OM
+    base = OM.store
+
+    def store(x, dt):
+        x = np.asarray(x, np.float64)
+        return base(x * (1.0 + rel * rng.standard_normal(x.shape)), dt)
+
+    OM.store = store
+    try:
+        yield
+    finally:
+        OM.store = base
 
 
 def teacher_forced(cfg, W, D, st: OSP.SeqState, drafts):
@@ -50,23 +85,75 @@ def greedy_margin(z):
     return float(s[-1] - s[-2])
 
 
-def decision_flags(p_rows, q_rows, drafts, seq_id, n, sp: OSP.SamplingParams, n_acc):
-    """Is any acceptance test of this step within 1e-3 of its draw (or greedy margin < 1e-2)?"""
+def _kappa(eps, T):
+    return float(np.expm1(2.0 * eps / T))
+
+
+def _nucleus_flips(zg, zo, T, top_p, eps):
+    """Do the nucleus sets of the two rows differ (and is that explained by eps)?  -> (differ, explained)"""
+    if top_p >= 1.0 or T == 0.0:
+        return False, True
+    pg = OS.pi(zg, T, top_p) > 0
+    po = OS.pi(zo, T, top_p) > 0
+    if np.array_equal(pg, po):
+        return False, True
+    p = OS.softmax64(zg, T)
+    order = np.lexsort((np.arange(p.shape[0]), -p))
+    cum = np.cumsum(p[order])
+    k = int(np.count_nonzero(pg))
+    before = cum[k - 2] if k >= 2 else 0.0
+    k_eps = _kappa(eps, T)
+    return True, abs(before - top_p) <= k_eps + 1e-12 or abs(cum[k - 1] - top_p) <= k_eps + 1e-12
+
+
+def mismatch_explained(gp, gq, op, oq, drafts, seq_id, n, sp: OSP.SamplingParams):
+    """The GPU's and the oracle's decisions on this step differ: is the difference within what the
+    measured logit error can flip (see the module docstring)?"""
     g = len(drafts)
-    flagged = False
-    for j in range(1, min(n_acc + 1, g) + 1):
-        if sp.temperature == 0.0:
-            flagged |= greedy_margin(p_rows[j - 1]) < 1e-2 or greedy_margin(q_rows[j - 1]) < 1e-2
-            continue
-        p = OS.pi(p_rows[j - 1], sp.temperature, sp.top_p)
-        q = OS.pi(q_rows[j - 1], sp.temperature, sp.top_p)
+    T = sp.temperature
+    gp = np.asarray(gp, np.float64)
+    gq = np.asarray(gq, np.float64)
+    eps_p = [abs_err(gp[j], op[j]) for j in range(g + 1)]
+    eps_q = [abs_err(gq[j], oq[j]) for j in range(g)]
+    if T == 0.0:
+        rows = [(gp[j], max(eps_p[j], eps_q[j] if j < g else 0.0)) for j in range(g + 1)]
+        rows += [(gq[j], max(eps_p[j], eps_q[j])) for j in range(g)]
+        return any(greedy_margin(z) < max(1e-2, 2.0 * e) for z, e in rows)
+    for j in range(1, g + 1):
+        for z_g, z_o, e in ((gp[j - 1], op[j - 1], eps_p[j - 1]), (gq[j - 1], oq[j - 1], eps_q[j - 1])):
+            differ, ok = _nucleus_flips(z_g, z_o, T, sp.top_p, e)
+            if differ:
+                return ok
+        pg_, qg_ = OS.pi(gp[j - 1], T, sp.top_p), OS.pi(gq[j - 1], T, sp.top_p)
+        po_, qo_ = OS.pi(op[j - 1], T, sp.top_p), OS.pi(oq[j - 1], T, sp.top_p)
         d = int(drafts[j - 1])
         u = OP.u1(sp.seed, seq_id, n + j, j, OP.PURPOSE_ACCEPT)
-        if q[d] > 0:
-            flagged |= abs(p[d] / q[d] - u) < 1e-3
-    if sp.temperature == 0.0 and n_acc == g:
-        flagged |= greedy_margin(p_rows[g]) < 1e-2
-    return flagged
+        acc_g, acc_o = OS.accept(pg_, qg_, d, u), OS.accept(po_, qo_, d, u)
+        if acc_g != acc_o:
+            bound = np.expm1(2.0 * (eps_p[j - 1] + eps_q[j - 1]) / T)
+            for p_, q_ in ((pg_, qg_), (po_, qo_)):
+                if q_[d] > 0:
+                    ratio = p_[d] / q_[d]
+                    if abs(ratio - u) < max(1e-3, ratio * bound + 1e-12):
+                        return True
+            return False
+        if not acc_g:
+            # same rejection at j: the residual draws differ
+            r = np.maximum(0.0, pg_ - qg_)
+            S = float(np.sum(r))
+            if S <= 0.0:
+                r, S = pg_, 1.0
+            k = OS.sample(r, OP.u1(sp.seed, seq_id, n + j, j, OP.PURPOSE_RESIDUAL))
+            delta = 2.0 * (_kappa(eps_p[j - 1], T) + _kappa(eps_q[j - 1], T)) / S
+            return OS.cdf_margin(r, OP.u1(sp.seed, seq_id, n + j, j, OP.PURPOSE_RESIDUAL), k) <= delta + 1e-12
+    # every draft accepted on both sides: the bonus draws differ
+    differ, ok = _nucleus_flips(gp[g], op[g], T, sp.top_p, eps_p[g])
+    if differ:
+        return ok
+    pb = OS.pi(gp[g], T, sp.top_p)
+    u = OP.u1(sp.seed, seq_id, n + g + 1, g + 1, OP.PURPOSE_RESIDUAL)
+    k = OS.sample(pb, u)
+    return OS.cdf_margin(pb, u, k) <= _kappa(eps_p[g], T) + 1e-12
 
 
 class Tally:
@@ -79,6 +166,8 @@ class Tally:
         self.max_abs_q = 0.0
         self.max_abs_p = 0.0
         self.first_flag_step = None
+        self.first_flag_len = {}   # sequence -> tokens generated before its first flagged step
+        self.envelope = 0.0        # max |perturbed oracle - oracle| over the compared rows
 
     def logits(self, gq, oq, gp, op):
         if gq is not None and len(gq):
@@ -88,26 +177,47 @@ class Tally:
         self.max_abs_p = max(self.max_abs_p, abs_err(gp, op))
 
 
-def run_lockstep(eng, cfg, W, D, prompts, new, gamma, sp: OSP.SamplingParams, max_steps=None):
+def run_lockstep(eng, cfg, W, D, prompts, new, gamma, sp: OSP.SamplingParams, max_steps=None,
+                 envelope_rel=0.0, envelope_seeds=0, share_group=None):
     """Prefill `prompts` on the engine and run spec steps at fixed gamma until
     every sequence has `new` tokens (or `max_steps`), checking each step
-    against the oracle.  Returns (generated tokens per sequence, Tally)."""
+    against the oracle.  Returns (generated tokens per sequence, Tally).
+
+    envelope_seeds > 0 also runs that many shadow oracles with perturbed
+    stores (perturbed_stores) on the same committed tokens and records in
+    tally.envelope how far their logits move from the oracle's.  share_group is
+    passed to er_kv_alloc (sequences of one group share their prompt's KV
+    blocks; their prompts must be equal)."""
     n_seq = len(prompts)
     eng.set_gamma(gamma)
-    ids = eng.kv_alloc([len(p) for p in prompts], [new] * n_seq)
+    ids = eng.kv_alloc([len(p) for p in prompts], [new] * n_seq, share_group=share_group)
     first = eng.prefill(ids, [list(p) for p in prompts])
     tally = Tally()
     states = []
+    z_pref = []
     for i in range(n_seq):
         kv = KVStore(cfg, len(prompts[i]) + new + gamma + 4)
         z = forward(cfg, W, list(prompts[i]), list(range(len(prompts[i]))), kv)
         gz = eng.debug_logits(1, i)
+        z_pref.append(z[-1])
         tally.logits(None, None, gz[0], z[-1])
         # sampler on the GPU's logits reproduces the GPU's token exactly
         assert OSP.ar_sample(gz[0].astype(np.float64), int(ids[i]), len(prompts[i]), sp) == first[i]
         st = OSP.SeqState(seq_id=int(ids[i]), pending=int(first[i]), n=len(prompts[i]), kv=kv, stop_len=new,
                           generated=[int(first[i])])
         states.append(st)
+    shadows = []
+    for e in range(envelope_seeds):
+        rng = np.random.Generator(np.random.PCG64(1000 + e))
+        row = []
+        for i in range(n_seq):
+            kv = KVStore(cfg, len(prompts[i]) + new + gamma + 4)
+            with perturbed_stores(envelope_rel, rng):
+                zp = forward(cfg, W, list(prompts[i]), list(range(len(prompts[i]))), kv)
+            tally.envelope = max(tally.envelope, abs_err(zp[-1], z_pref[i]))
+            row.append((OSP.SeqState(seq_id=int(ids[i]), pending=int(first[i]), n=len(prompts[i]), kv=kv,
+                                     stop_len=new, generated=[int(first[i])]), rng))
+        shadows.append(row)
     gen = [[int(first[i])] for i in range(n_seq)]
     active = list(range(n_seq))
     while active and (max_steps is None or tally.steps < max_steps):
@@ -132,14 +242,19 @@ def run_lockstep(eng, cfg, W, D, prompts, new, gamma, sp: OSP.SamplingParams, ma
             # decision on the oracle's logits: equal unless flagged
             a_o, em_o = OSP.spec_decide(op, oq, drafts[slot], st.seq_id, st.n, sp)
             if (a_o, em_o) != (a_g, em_g):
-                if decision_flags(op, oq, drafts[slot], st.seq_id, st.n, sp, min(a_o, a_g)) or \
-                        decision_flags(gp.astype(np.float64), gq.astype(np.float64), drafts[slot], st.seq_id, st.n,
-                                       sp, min(a_o, a_g)) or a_o == a_g:
+                if mismatch_explained(gp, gq, op, oq, drafts[slot], st.seq_id, st.n, sp):
                     tally.flagged += 1
                     if tally.first_flag_step is None:
                         tally.first_flag_step = tally.steps
+                    tally.first_flag_len.setdefault(i, len(gen[i]))
                 else:
                     tally.unflagged_mismatch += 1
+            for row in shadows:
+                sh, rng = row[i]
+                with perturbed_stores(envelope_rel, rng):
+                    sq, spp = teacher_forced(cfg, W, D, sh, drafts[slot])
+                tally.envelope = max(tally.envelope, abs_err(sq, oq), abs_err(spp, op))
+                OSP.commit(sh, em_g, a_g)
             OSP.commit(st, em_g, a_g)
             gen[i].extend(int(t) for t in tok[slot, :kept])
             if len(st.generated) < new:

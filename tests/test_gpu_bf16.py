@@ -27,13 +27,16 @@ from oracle.model import KVStore, config_from, forward, weights_from  # noqa: E4
 from lockstep import run_lockstep  # noqa: E402
 
 ABS_TOL = 3e-2
-# At Qwen2.5-7B width the logits are ~2.7x larger (std 1.2 vs 0.45 on the
-# 2-layer mini model) and the oracle itself moves by 2.5e-2 when its
-# pre-rounding values are perturbed by 1e-7 relative (a bf16 store may round
-# the other way, and random-init layers amplify each flip), so no fp32
-# accumulation order can promise 3e-2 there; the full-width check uses twice
-# the bf16 bound.
-ABS_TOL_FULL_WIDTH = 6e-2
+# Two GPU runs that each agree with the oracle within the bf16 bound agree with
+# each other within twice it (triangle inequality).
+ABS_TOL_GPU_VS_GPU = 2 * ABS_TOL
+# Relative perturbation of every pre-rounding value for the oracle's own
+# envelope at full width: 2^-20, i.e. 16 fp32 ulps.  An fp32 sum of K terms
+# taken in another order typically moves by about sqrt(K) * 2^-24 relative
+# (3.6e-6 at K = 3584, 8.2e-6 at K = 18944), so this understates what a
+# different accumulation order does; a bf16 store can then round the other way
+# and random-init layers amplify each flip.
+ENVELOPE_REL = 2.0 ** -20
 
 
 def _engine(shape, wts, quant, **kw):
@@ -137,16 +140,23 @@ def qwen7_2l():
 
 def test_qwen7b_width_lockstep(qwen7_2l):
     """Real 7B projection shapes (2 layers, vocab 152064): prefill through the
-    tiled GEMM, drafter through the W4 skinny kernel, verify at M = 15."""
+    tiled GEMM, drafter through the W4 streaming path, verify at M = 15.
+    Logits must agree within the bf16 bound, or within the oracle's own spread
+    when its stores are perturbed by a few fp32 ulps (two shadow oracles on
+    the same committed tokens) where that spread is larger."""
     shape, wts, cfg, W, D = qwen7_2l
     prompts = [list(p) for p in synth.prompts(3, 24, shape.vocab, seed=8)]
     eng = _engine(shape, wts, shape.quant, seed=8, max_seqs=4, max_batch=4, max_ctx=128, prefill_chunk=128,
                   kv_blocks=64)
     sp = OSP.SamplingParams(seed=8)
-    gen, tally = run_lockstep(eng, cfg, W, D, prompts, 12, 4, sp, max_steps=3)
+    gen, tally = run_lockstep(eng, cfg, W, D, prompts, 40, 4, sp, max_steps=6, envelope_rel=ENVELOPE_REL,
+                              envelope_seeds=2)
     eng.close()
-    print(f"steps={tally.steps} flagged={tally.flagged} abs_q={tally.max_abs_q:.2e} abs_p={tally.max_abs_p:.2e}")
-    assert tally.max_abs_q < ABS_TOL_FULL_WIDTH and tally.max_abs_p < ABS_TOL_FULL_WIDTH
+    bound = max(ABS_TOL, tally.envelope)
+    print(f"steps={tally.steps} flagged={tally.flagged} abs_q={tally.max_abs_q:.2e} abs_p={tally.max_abs_p:.2e} "
+          f"oracle envelope={tally.envelope:.2e} bound={bound:.2e}")
+    assert tally.steps == 6
+    assert tally.max_abs_q < bound and tally.max_abs_p < bound
     assert tally.unflagged_mismatch == 0
 
 
@@ -174,4 +184,4 @@ def test_many_chunk_prefill_matches_one_chunk(qwen7_2l):
         # near-tie may draw differently under the two chunkings
         for k in ((1, 2) if got[0][0][s] == got[1][0][s] else (1,)):
             d = float(np.abs(got[0][k][s] - got[1][k][s]).max())
-            assert d < ABS_TOL_FULL_WIDTH, (s, k, d)
+            assert d < ABS_TOL_GPU_VS_GPU, (s, k, d)

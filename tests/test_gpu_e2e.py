@@ -65,13 +65,16 @@ def test_tiny_fp32_lockstep(tiny, T, top_p):
 
 
 def test_tiny_fp32_full_rollout_equals_oracle(tiny):
-    """Independent rollouts (GPU vs oracle) are identical up to the first flagged step."""
+    """Independent rollouts (GPU vs oracle) are identical up to each sequence's first flagged step."""
     shape, wts, cfg, W, D = tiny
     gen, tally, prompts = _lockstep_rollout(tiny, 1.0, 1.0, gamma=4)
-    if tally.flagged == 0:
-        sp = OSP.SamplingParams(seed=0, temperature=1.0, top_p=1.0)
-        ref = OSP.rollout_spec(cfg, W, D, [list(p) for p in prompts], [64] * 4, 4, sp)
-        assert gen == ref
+    sp = OSP.SamplingParams(seed=0, temperature=1.0, top_p=1.0)
+    ref = OSP.rollout_spec(cfg, W, D, [list(p) for p in prompts], [64] * 4, 4, sp)
+    lens = [tally.first_flag_len.get(i, len(gen[i])) for i in range(4)]
+    print(f"compared prefix lengths {lens} (flagged steps: {tally.flagged})")
+    assert sum(lens) >= 64
+    for i in range(4):
+        assert gen[i][:lens[i]] == ref[i][:lens[i]], i
 
 
 def test_greedy_spec_equals_greedy_ar(tiny):

@@ -127,3 +127,70 @@ def test_work_unit_split_under_sanitizers(tmp_path):
     assert r.returncode == 0, r.stderr
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "work_units ok" in r.stdout, r.stdout + r.stderr
+
+
+def _toy_cost(bw, flops, t_fwd, q_bytes=1.0):
+    return dict(n_layers=1, d_model=2, n_q_heads=1, n_kv_heads=1, head_dim=2, ffn=1, vocab=3, w_bytes=2.0,
+                q_bytes=q_bytes, kv_bytes_el=2.0, hbm_bytes_per_s=bw, flops_per_s=flops, t_fwd_s=t_fwd)
+
+
+def test_controller_times_at_hand_computed_points(lib):
+    # the worked toy points of tests/test_oracle_controller.py (TOY_TIMES), evaluated by the library
+    from speculative_decoding_rl_amd.rollout import controller_times
+    from tests.test_oracle_controller import TOY_TIMES
+    for (bw, fl, tf), (t_ar, t_sd) in TOY_TIMES:
+        a, s = controller_times(_toy_cost(bw, fl, tf), 2, 5.0, 2)
+        assert a == pytest.approx(t_ar, rel=1e-12) and s == pytest.approx(t_sd, rel=1e-12)
+    # gamma 1 with the cheap drafter: 122.8 + 216
+    assert controller_times(_toy_cost(1.0, 1e30, 0.0, 0.1), 2, 5.0, 1)[1] == pytest.approx(338.8, rel=1e-12)
+
+
+def test_controller_times_reject_bad_arguments(lib):
+    from speculative_decoding_rl_amd.rollout import controller_times
+    with pytest.raises(_lib.ErError):
+        controller_times(_toy_cost(1.0, 1.0, 0.0), 0, 5.0, 2)
+    with pytest.raises(_lib.ErError):
+        controller_times(_toy_cost(1.0, 1.0, 0.0), 2, 5.0, 0)
+    with pytest.raises(_lib.ErError):
+        controller_times(_toy_cost(0.0, 1.0, 0.0), 2, 5.0, 2)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_controller_plan_matches_oracle_over_scripted_streams(lib, seed):
+    """The library's policy state machine against oracle.controller.plan over long streams of
+    batches, contexts and acceptance estimates (with stretches that make it probe)."""
+    import numpy as np
+    from speculative_decoding_rl_amd.rollout import controller_plan
+    c = _cost()
+    m = OC.ModelCost(c["n_layers"], c["d_model"], c["n_q_heads"], c["n_kv_heads"], c["head_dim"], c["ffn"],
+                     c["vocab"], c["w_bytes"], c["q_bytes"], c["kv_bytes_el"])
+    r = OC.Roofline(c["hbm_bytes_per_s"], c["flops_per_s"], c["t_fwd_s"])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    ost = OC.PlanState()
+    lst = dict(choice=-1, ar_streak=0, probe_every=0)
+    n_sd = n_probe = 0
+    policy = OC.POLICY_AUTO
+    # segments of steady (B, C) with a low estimate (AR chosen, probes due), mixed with noisy stretches
+    step = 0
+    for seg in range(40):
+        if seg % 10 == 9:
+            policy = int(rng.integers(0, 3))
+        elif seg % 10 == 0:
+            policy = OC.POLICY_AUTO
+        noisy = seg % 4 == 3
+        B0 = int(rng.choice([1, 2, 4]))
+        C0 = float(rng.integers(256, 4096))
+        for _ in range(int(rng.integers(100, 400))):
+            B = int(rng.choice([1, 2, 3, 4, 8, 16, 64, 256])) if noisy else B0
+            Cx = float(rng.integers(64, 16000)) if noisy else C0
+            a = float(rng.choice([0.05, 0.2, 0.5, 0.8, 0.95])) if noisy else 0.05
+            lo, hi = (1, 8) if step % 7 else (2, 4)
+            want = OC.plan(m, r, ost, policy, B, Cx, a, 0.9, lo, hi, 1.02)
+            got = controller_plan(c, lst, policy, B, Cx, a, 0.9, lo, hi, 1.02)
+            assert got == want, step
+            assert (lst["choice"], lst["ar_streak"], lst["probe_every"]) == (ost.choice, ost.ar_streak,
+                                                                              ost.probe_every), step
+            n_sd += got > 0
+            n_probe += got > 0 and ost.choice == 0
+            step += 1
+    assert n_sd > 100 and n_probe > 3
