@@ -92,14 +92,17 @@ def test_auto_policy_live_loop_matches_oracle(mini):
     eng.prefill(ids, [list(p) for p in synth.prompts(B, plen, shape.vocab, seed=3)])
     cm = eng.cost_model()
     assert cm["t_fwd_s"] == t_fwd and cm["hbm_bytes_per_s"] == bw and cm["flops_per_s"] == fl
+    # the descriptor holds alpha_init, beta and the margin as fp32: the library computes with those values
+    f32 = lambda x: float(np.float32(x))
+    a_init, beta, margin = f32(0.9), f32(0.3), f32(1.02)
     st = OC.PlanState()
-    alpha = 0.9
+    alpha = a_init
     n_sd = n_ar = n_probe = 0
     for step in range(200):
         ctx = [eng.seq_info(i)[1] for i in ids]
         if max(ctx) > 440:
             break
-        want = OC.plan(m, r, st, OC.POLICY_AUTO, B, float(np.mean(ctx)), alpha, 0.9, 1, 8, 1.02)
+        want = OC.plan(m, r, st, OC.POLICY_AUTO, B, float(np.mean(ctx)), alpha, a_init, 1, 8, margin)
         tok, ne, info = eng.step(ids)
         got = int(info.gamma) if info.mode == _lib.ER_MODE_SD else 0
         assert got == want, step
@@ -110,7 +113,7 @@ def test_auto_policy_live_loop_matches_oracle(mini):
             assert info.accepted == sum(acc) and info.emitted == sum(acc) + B
             a_step = OC.alpha_step(acc, [got] * B)
             assert abs(info.alpha_step - a_step) < 1e-6, step
-            alpha = OC.ema(alpha, a_step, 0.3)
+            alpha = OC.ema(alpha, a_step, beta)
             n_sd += 1
             n_probe += st.choice == 0
         else:
