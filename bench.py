@@ -62,6 +62,8 @@ def parse():
     ap.add_argument("--kv-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
+    ap.add_argument("--no-persistent", action="store_true",
+                    help="run every forward as the kernel sequence (no persistent decode forward)")
     ap.add_argument("--kprof-every", type=int, default=4,
                     help="bracket the attention launches of every this many steps of the timed rollout with HIP "
                          "events (events on every launch slow each step by ~0.3 ms)")
@@ -89,9 +91,12 @@ def make_engine(args, shape, wts, policy):
         # for the expected peak with margin (the lognormal tail is long, the batch is not)
         exp_len = args.prompt_len + args.median * math.exp(0.75 ** 2 / 2)
         kv_blocks = int(args.batch * (exp_len / 16 + 2) * 1.6) + 2 * (max_ctx // 16)
-    return Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
-                  gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=policy, max_seqs=args.batch + 64,
-                  max_batch=args.batch, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
+    eng = Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
+                 gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=policy, max_seqs=args.batch + 64,
+                 max_batch=args.batch, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
+    if args.no_persistent:
+        eng.set_persistent(False)
+    return eng
 
 
 def run_rollout(eng, args, prompts, stops, label):
@@ -407,6 +412,8 @@ def crossover(args, shape, wts):
                  gamma_init=min(4, max(gammas)), gamma_min=1, gamma_max=max(gammas), policy=_lib.ER_POLICY_FORCE_AR,
                  max_seqs=Bmax,
                  max_batch=Bmax, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
+    if args.no_persistent:
+        eng.set_persistent(False)
     prompts = synth.prompts(Bmax, C, shape.vocab, seed=args.seed)
     ids = [int(i) for i in eng.kv_alloc([C] * Bmax, [max_ctx - C - 16] * Bmax)]
     t0 = time.perf_counter()

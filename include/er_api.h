@@ -260,6 +260,37 @@ int er_set_timing(er_ctx *ctx, int period, int first_n);
  * always run unfused.  Takes effect at the next forward. */
 int er_set_fused(er_ctx *ctx, int on);
 
+/* Persistent decode forward (bf16 models): a forward of at most 16 rows
+ * (decode and drafting at batch <= 16, verify at batch * (gamma + 1) <= 16)
+ * runs the embedding and every decoder layer as one cooperative launch with
+ * grid barriers between the projection and attention phases, instead of ~6
+ * launches per layer; the final norm, lm_head and sampler are unchanged.  Same
+ * arithmetic per element (fp32 accumulation, bf16 stores at the same points);
+ * K-split sums are added in a fixed order.  Off by default (on MI355X the
+ * kernel sequence is faster at every measured batch); available where the
+ * device can keep one work-group per compute unit resident.  ER_ESTATE when
+ * asked to switch it on where it cannot run.  A grid-barrier wait that times out fails
+ * the step with ER_EDEVICE and switches the path off. */
+int er_set_persistent(er_ctx *ctx, int on);
+int er_get_persistent(const er_ctx *ctx, int *on);
+/* Polls a grid-barrier wait of the persistent decode forward makes before it
+ * gives up (default 2^21, a few seconds).  A tiny value forces the time-out
+ * path (every work-group still leaves the kernel), for testing the recovery:
+ * the step fails with ER_EDEVICE, no sequence state changes, and later steps
+ * run the kernel sequence.  ER_EINVAL for polls < 1. */
+int er_set_decode_spin_limit(er_ctx *ctx, int64_t polls);
+/* Phase timing of the persistent decode forward, for profiling: while on,
+ * each launch records the 100 MHz clock at every grid barrier (one device
+ * buffer, allocated here, freed by on = 0 or er_destroy).
+ * er_get_decode_trace reports the last traced forward: for phase k (the
+ * embedding, then per layer QKV, attention, [merge], output, gate/up, down)
+ * work_us[k] = time from the first release of the previous barrier to the
+ * last arrival at this one, release_us[k] = time from that arrival to the last
+ * release; n_out = phases (min(max, phases) written).  ER_ESTATE if nothing
+ * was traced. */
+int er_set_decode_trace(er_ctx *ctx, int on);
+int er_get_decode_trace(er_ctx *ctx, double *work_us, double *release_us, int max, int *n_out);
+
 /* Free KV blocks in the pool. */
 int er_kv_free_blocks(er_ctx *ctx, int64_t *free_blocks, int64_t *total_blocks);
 

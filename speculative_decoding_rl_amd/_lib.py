@@ -137,6 +137,12 @@ SIGNATURES = {
     "er_reset_stats": (C.c_int, [P]),
     "er_set_timing": (C.c_int, [P, C.c_int, C.c_int]),
     "er_set_fused": (C.c_int, [P, C.c_int]),
+    "er_set_persistent": (C.c_int, [P, C.c_int]),
+    "er_get_persistent": (C.c_int, [P, C.POINTER(C.c_int)]),
+    "er_set_decode_spin_limit": (C.c_int, [P, C.c_int64]),
+    "er_set_decode_trace": (C.c_int, [P, C.c_int]),
+    "er_get_decode_trace": (C.c_int, [P, C.POINTER(C.c_double), C.POINTER(C.c_double), C.c_int,
+                                      C.POINTER(C.c_int)]),
     "er_kv_free_blocks": (C.c_int, [P, I64P, I64P]),
     "er_set_kernel_profile": (C.c_int, [P, C.c_int]),
     "er_get_kernel_profile": (C.c_int, [P, C.POINTER(KernelStat), C.c_int, C.POINTER(C.c_int)]),

@@ -141,6 +141,23 @@ struct er_ctx {
   struct KStat { long n = 0; double ms = 0, bytes = 0, flops = 0; };
   std::map<std::string, KStat> kstat;
 
+  // persistent decode forward (k_decode): bf16 forwards of at most
+  // kDecodeMaxRows rows run as one cooperative launch
+  bool dec_on = false;               // enabled (er_set_persistent) and available on this device
+  int dec_nwg[4] = {0, 0, 0, 0};     // its grid per weight format (0: cannot run)
+  int dec_ks[2][4] = {{8, 8, 8, 8}, {8, 8, 8, 8}};  // waves splitting K per projection: target, drafter
+  bool dec_avail = false;            // the kernel can run on this device for both weight formats
+  DecLayerW* dec_layers[2] = {nullptr, nullptr};  // device descriptors: target, drafter
+  char* dec_ws = nullptr;            // write-once activation buffers (decode_ws_bytes)
+  unsigned* dec_bar = nullptr;
+  unsigned* dec_err = nullptr;
+  int dec_err_slot = 0;              // out_h index the error word is copied to
+  bool dec_ran = false;              // the current step launched it
+  long dec_spin_limit = 1L << 21;    // polls before a grid-barrier wait gives up
+  unsigned long long* dec_trace = nullptr;  // phase trace buffer (er_set_decode_trace), device
+  int dec_trace_max = 0;
+  int dec_trace_nwg = 0;             // grid of the last traced launch
+
   // timing
   int timing_period = 0, timing_first = 0;
   long step_count = 0;
@@ -242,11 +259,12 @@ double weight_bytes(const LinearW& W) {
 struct Layout {
   size_t drafter = 0, cs = 0, h = 0, xbuf = 0, qkv = 0, qb = 0, gu = 0, lp = 0, lq = 0, sp = 0, sq = 0;
   size_t out = 0, partial = 0, counters = 0, attn = 0, w4tmp = 0, sink = 0, meta = 0, resid = 0, ssq = 0, xn = 0;
+  size_t dec = 0;  // persistent decode forward: layer descriptors, sums of squares, counters, barrier
   size_t block_bytes = 0;
   int max_rows = 0, logit_rows = 0;
   size_t total_fixed() const {
     return drafter + cs + h + xbuf + qkv + qb + gu + lp + lq + sp + sq + out + partial + counters + attn + w4tmp +
-           sink + meta + resid + ssq + xn;
+           sink + meta + resid + ssq + xn + dec;
   }
 };
 
@@ -285,7 +303,7 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
   L->resid = align256((size_t)r.max_batch * sampler_chunks((int)V) * 8);
   L->ssq = 2 * align256((size_t)kSsqSlots * R * 8);
   L->xn = align256((size_t)R * d * 2);
-  L->out = align256((size_t)(L->max_rows + r.max_batch) * 4);
+  L->out = align256((size_t)(L->max_rows + r.max_batch + 64) * 4);  // + the decode kernel's error word
   L->partial = align256((size_t)16 << 20) * 4;  // 16M floats
   L->counters = align256((size_t)65536 * 4);
   {
@@ -302,6 +320,11 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
   }
   L->w4tmp = align256(w4);
   L->sink = 256;
+  if (m.dtype == ER_BF16) {
+    L->dec = align256((size_t)2 * m.n_layers * sizeof(DecLayerW)) +
+             align256(decode_ws_bytes(m.n_layers, (int)d, (int)hq, (int)hd, (int)F, kSsqSlots)) +
+             align256((size_t)kDecodeBarWords * 4) + 256;
+  }
   L->meta = align256((size_t)64 << 20);
   L->block_bytes = (size_t)m.n_layers * 2 * hkv * KV_BLOCK * hd * ab;
   (void)why;
@@ -358,6 +381,7 @@ struct Fwd {
   int n_logit = -1;                      // -1: every row; 0: none (prefill chunk with no last token)
   float* logits = nullptr;
   long ldl = 0;
+  bool dec_ok = false;                   // a decode / draft / verify forward (the persistent kernel may run it)
 };
 
 int lin(er_ctx* c, const void* x, int M, const LinearW& W, void* y, int ldy, int epi) {
@@ -433,9 +457,127 @@ int flin(er_ctx* c, const Fwd& f, const FLin& fl, int M, const LinearW& W, void*
   return ER_OK;
 }
 
+// Final norm + lm_head over the rows that need logits.
+int logits_tail(er_ctx* c, const Fwd& f) {
+  const er_model_desc& m = c->md;
+  const int d = m.d_model;
+  const int nl = f.n_logit < 0 ? f.M : f.n_logit;
+  if (nl == 0) return ER_OK;
+  const LinearW& lm = f.draft ? c->lm_d : c->lm_t;
+  if (c->fuse) {
+    FLin h;
+    h.x = c->h;
+    h.ldx = d;
+    h.gnorm = c->final_norm;
+    h.xrow = f.logit_rows;
+    h.ssq_in = c->ssq[0];
+    return flin(c, f, h, nl, lm, f.logits, (int)f.ldl, EPI_F32, 0);
+  }
+  KC(c, launch_rmsnorm(c->h, nl, d, c->final_norm, c->bf16, m.rms_eps, c->xbuf, f.logit_rows, c->st));
+  return lin(c, c->xbuf, nl, lm, f.logits, (int)f.ldl, EPI_F32);
+}
+
+double layers_weight_bytes(const er_ctx* c, bool draft) {
+  const std::vector<Lin4>& W = draft ? c->drf : c->tgt;
+  double b = 0;
+  for (const Lin4& l : W) b += weight_bytes(l.qkv) + weight_bytes(l.o) + weight_bytes(l.gu) + weight_bytes(l.down);
+  return b;
+}
+
+// The embedding and every decoder layer as one persistent launch (k_decode).
+// Returns ER_OK when it ran, 1 when this forward does not fit it (the caller
+// runs the kernel sequence), or an error.
+int forward_decode(er_ctx* c, const Fwd& f) {
+  const er_model_desc& m = c->md;
+  const int hq = m.n_q_heads, hkv = m.n_kv_heads, hd = m.head_dim;
+  const int fmt = f.draft ? c->drf[0].qkv.fmt : FMT_BF16;
+  if (!c->dec_on || !f.dec_ok || !c->fuse || f.M > kDecodeMaxRows || !f.unit_start || !f.unit_rec) return 1;
+  if (c->dec_nwg[fmt] <= 0 || !c->dec_layers[f.draft ? 1 : 0]) return 1;
+  if ((size_t)f.n_units * hkv * (size_t)(hq / hkv) * f.max_q * (size_t)(hd + 2) > c->attn_ws_floats) return 1;
+  if ((hq / hkv) * f.max_q > 64 ||
+      decode_lds_bytes(hd, f.M, m.d_model, std::max({(hq + 2 * hkv) * hd, m.d_model, 2 * m.ffn}), c->dec_nwg[fmt]) >
+          (size_t)150 * 1024)
+    return 1;
+  DecodeArgs a{};
+  a.M = f.M;
+  a.L = m.n_layers;
+  a.d = m.d_model;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.hd = hd;
+  a.F = m.ffn;
+  a.eps = m.rms_eps;
+  a.layers = c->dec_layers[f.draft ? 1 : 0];
+  a.embed = c->embed;
+  a.tokens = f.tokens;
+  a.tok_stride = f.tok_stride;
+  a.pos = f.pos;
+  a.slot = f.slot;
+  a.cs = c->cs;
+  a.kv_pool = c->kv_pool;
+  a.block_table = f.bt;
+  a.bt_stride = f.bt_stride;
+  a.unit_rec = f.unit_rec;
+  a.unit_start = f.unit_start;
+  a.split_items = f.unit_start + 2 * f.n_items + 1;
+  a.item_q_row0 = f.it_row0;
+  a.item_q_count = f.it_cnt;
+  a.n_items = f.n_items;
+  a.n_units = f.n_units;
+  a.n_split = f.n_split;
+  a.max_q = f.max_q;
+  {
+    // write-once buffers: h per layer boundary, q / attention output / SwiGLU output per layer, sums of squares
+    const long L = m.n_layers, d = m.d_model, qn = (long)hq * hd, F = m.ffn;
+    char* p = c->dec_ws;
+    a.hbuf = (float*)p;
+    p += align256((size_t)2 * L * 16 * d * 4);
+    a.qbuf = (uint16_t*)p;
+    p += align256((size_t)L * 16 * qn * 2);
+    a.abuf = (uint16_t*)p;
+    p += align256((size_t)L * 16 * qn * 2);
+    a.act = (uint16_t*)p;
+    p += align256((size_t)L * 16 * F * 2);
+    a.ssq = (unsigned long long*)p;
+  }
+  a.h_final = c->h;
+  a.apart = c->attn_ws;
+  a.ssq_out = c->ssq[0];
+  a.ssq_slots = kSsqSlots;
+  a.ssq_stride = c->max_rows;
+  a.bar = c->dec_bar;
+  a.err = c->dec_err;
+  for (int i = 0; i < 4; ++i) a.ks[i] = c->dec_ks[f.draft ? 1 : 0][i];
+  a.n_wg = c->dec_nwg[fmt];
+  a.spin_limit = c->dec_spin_limit;
+  a.trace = c->dec_trace;
+  a.trace_max = c->dec_trace_max;
+  if (c->dec_trace) c->dec_trace_nwg = a.n_wg;
+  const int e = kp_begin(c, KPROF_LINEAR | KPROF_ATTENTION);
+  KC(c, launch_decode(a, fmt, c->st));
+  c->dec_ran = true;
+  if (e >= 0) {
+    // algorithmic bytes: every layer's weights (with scales / zeros), the K/V
+    // read and written, the embedding rows; flops of the projections and attention
+    const double kvb = 2.0 * hkv * hd * c->act_bytes;
+    const double by = layers_weight_bytes(c, f.draft) + (f.kv_keys + f.M) * kvb * m.n_layers +
+                      (double)f.M * m.d_model * c->act_bytes;
+    const double P = c->cost.p_lin() - (double)m.vocab * m.d_model;
+    char nm[64];
+    snprintf(nm, sizeof nm, "er::k_decode<%d, %d>", fmt, hd);
+    kp_end(c, e, nm, by, 2.0 * P * f.M + 4.0 * f.kv_keys * f.max_q * (double)hq * hd * m.n_layers);
+  }
+  return ER_OK;
+}
+
 int forward(er_ctx* c, const Fwd& f) {
   const er_model_desc& m = c->md;
   const int d = m.d_model, hq = m.n_q_heads, hkv = m.n_kv_heads, hd = m.head_dim, F = m.ffn;
+  {
+    const int r = forward_decode(c, f);
+    if (r == ER_OK) return logits_tail(c, f);
+    if (r < 0) return r;
+  }
   const std::vector<Lin4>& W = f.draft ? c->drf : c->tgt;
   unsigned long long* S0 = c->ssq[0];
   unsigned long long* S1 = c->ssq[1];
@@ -543,20 +685,7 @@ int forward(er_ctx* c, const Fwd& f) {
     r = lin(c, c->xbuf, f.M, W[l].down, c->h, d, EPI_RESID);
     if (r) return r;
   }
-  const int nl = f.n_logit < 0 ? f.M : f.n_logit;
-  if (nl == 0) return ER_OK;
-  const LinearW& lm = f.draft ? c->lm_d : c->lm_t;
-  if (c->fuse) {
-    FLin h;
-    h.x = c->h;
-    h.ldx = d;
-    h.gnorm = c->final_norm;
-    h.xrow = f.logit_rows;
-    h.ssq_in = S0;
-    return flin(c, f, h, nl, lm, f.logits, (int)f.ldl, EPI_F32, 0);
-  }
-  KC(c, launch_rmsnorm(c->h, nl, d, c->final_norm, c->bf16, m.rms_eps, c->xbuf, f.logit_rows, c->st));
-  return lin(c, c->xbuf, nl, lm, f.logits, (int)f.ldl, EPI_F32);
+  return logits_tail(c, f);
 }
 
 // ---- drafter build (A0) -----------------------------------------------------
@@ -627,6 +756,18 @@ int set_weights(er_ctx* c, const er_weights* w) {
   } else {
     c->lm_d = c->lm_t;
   }
+  if (c->dec_layers[0]) {
+    // layer descriptors of the persistent decode forward (target, drafter)
+    for (int which = 0; which < 2; ++which) {
+      std::vector<DecLayerW> v((size_t)m.n_layers);
+      const std::vector<Lin4>& W = which ? c->drf : c->tgt;
+      for (int l = 0; l < m.n_layers; ++l)
+        v[(size_t)l] = DecLayerW{W[l].qkv, W[l].o, W[l].gu, W[l].down, c->attn_norm[l], c->mlp_norm[l]};
+      HIPC(c, hipMemcpyAsync(c->dec_layers[which], v.data(), v.size() * sizeof(DecLayerW), hipMemcpyHostToDevice,
+                             c->st));
+      HIPC(c, hipStreamSynchronize(c->st));
+    }
+  }
   HIPC(c, hipStreamSynchronize(c->st));
   return ER_OK;
 }
@@ -681,6 +822,27 @@ int64_t slot_of(const Seq& s, int32_t pos) {
 void finish_seq(er_ctx* c, Seq& s) {
   s.finished = true;
   s.bt.release(c->pool);
+}
+
+// Queue the copy of the persistent decode kernel's error word (if it ran).
+int dec_queue_err(er_ctx* c) {
+  if (c->dec_ran) HIPC(c, hipMemcpyAsync(c->out_h + c->dec_err_slot, c->dec_err, 4, hipMemcpyDeviceToHost, c->st));
+  return ER_OK;
+}
+
+// After the stream is synchronized: did a grid-barrier wait of the persistent
+// decode kernel time out?  Then that path is switched off for the context and
+// its barrier words are cleared.
+int dec_check(er_ctx* c) {
+  if (!c->dec_ran) return ER_OK;
+  c->dec_ran = false;
+  if (c->out_h[c->dec_err_slot] == 0) return ER_OK;
+  c->out_h[c->dec_err_slot] = 0;
+  c->dec_on = false;
+  HIPC(c, hipMemsetAsync(c->dec_bar, 0, (size_t)kDecodeBarWords * 4, c->st));
+  HIPC(c, hipMemsetAsync(c->dec_err, 0, 4, c->st));
+  HIPC(c, hipStreamSynchronize(c->st));
+  return fail(c, ER_EDEVICE, "persistent decode forward: a grid-barrier wait timed out (path switched off)");
 }
 
 int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_stride, int32_t* n_emitted,
@@ -741,6 +903,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
     Fwd f;
     f.draft = false;
+    f.dec_ok = true;
     f.M = n;
     f.tokens = M.dev<int32_t>(o_tok);
     f.pos = M.dev<int32_t>(o_pos);
@@ -771,9 +934,11 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
                              nullptr, c->st));
     if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
     HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)n * 4, hipMemcpyDeviceToHost, c->st));
+    if (int r_ = dec_queue_err(c)) return r_;
     HIPC(c, hipStreamSynchronize(c->st));
-    return ER_OK;
+    return dec_check(c);
   };
+  c->dec_ran = false;
   const int r = run();
   kp_flush(c);
   if (r) { rollback(); return r; }
@@ -909,6 +1074,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     for (int j = 0; j < g; ++j) {
       Fwd f;
       f.draft = true;
+      f.dec_ok = true;
       f.M = n;
       f.tokens = d_tok + j;
       f.tok_stride = G1;
@@ -942,6 +1108,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
     Fwd f;
     f.draft = false;
+    f.dec_ok = true;
     f.M = n * G1;
     f.tokens = d_tok;
     f.tok_stride = 1;
@@ -973,9 +1140,11 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
                              c->out_d + n * G1, c->resid, c->st));
     if (timed) HIPC(c, hipEventRecord(c->ev[3], c->st));
     HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)(n * G1 + n) * 4, hipMemcpyDeviceToHost, c->st));
+    if (int r_ = dec_queue_err(c)) return r_;
     HIPC(c, hipStreamSynchronize(c->st));
-    return ER_OK;
+    return dec_check(c);
   };
+  c->dec_ran = false;
   const int r = run();
   kp_flush(c);
   if (r) { rollback(); return r; }
@@ -1123,6 +1292,10 @@ int calibrate(er_ctx* c) {
     int32_t* ir = M.push<int32_t>(1, &o_ir);
     int32_t* ic = M.push<int32_t>(1, &o_ic);
     *t = 0; *p = 0; *s = (int64_t)bt.blocks[0] * KV_BLOCK; *btp = bt.blocks[0]; *ib = 0; *ir = 0; *ic = 1;
+    int nu1 = 0, ns1 = 0, mu1 = 0;
+    size_t o_rec1 = 0;
+    const size_t o_us1 = push_units(M, 1, (int)m.n_kv_heads, p, ic, ir, ib, &nu1, &ns1, &mu1, &o_rec1);
+    if (!M.ok) { bt.release(c->pool); return fail(c, ER_ENOMEM, "metadata region too small"); }
     if (int r_ = meta_upload(c)) return r_;
     Fwd f;
     f.M = 1;
@@ -1138,6 +1311,13 @@ int calibrate(er_ctx* c) {
     f.n_items = 1;
     f.max_q = 1;
     f.max_ctx = 1;
+    f.unit_start = M.dev<int32_t>(o_us1);
+    f.unit_rec = M.dev<int32_t>(o_rec1);
+    f.n_units = nu1;
+    f.n_split = ns1;
+    f.max_units = mu1;
+    f.kv_keys = 1;
+    f.dec_ok = true;  // time the forward the decode steps run
     f.logits = c->logits_p;
     f.ldl = m.vocab;
     float times[2] = {0, 0};
@@ -1162,6 +1342,10 @@ int calibrate(er_ctx* c) {
     (void)hipEventDestroy(a);
     (void)hipEventDestroy(b);
     bt.release(c->pool);
+    if (c->dec_ran) {
+      HIPC(c, hipMemcpy(c->out_h + c->dec_err_slot, c->dec_err, 4, hipMemcpyDeviceToHost));
+      if (int r_ = dec_check(c)) return r_;
+    }
     const double P = c->cost.p_lin();
     const double tt = times[0] - c->cost.w_bytes * P / c->cost.bw;
     const double td = times[1] - c->cost.q_bytes * P / c->cost.bw;
@@ -1348,6 +1532,22 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->sink = (uint32_t*)take(L.sink);
     c->meta.d = take(L.meta);
     c->meta.cap = L.meta;
+    if (L.dec) {
+      char* d0 = take(L.dec);
+      char* dc = d0;
+      const size_t nl = (size_t)model->n_layers;
+      c->dec_layers[0] = (DecLayerW*)dc;
+      c->dec_layers[1] = c->dec_layers[0] + nl;
+      dc += align256(2 * nl * sizeof(DecLayerW));
+      c->dec_ws = dc;
+      dc += align256(decode_ws_bytes(model->n_layers, model->d_model, model->n_q_heads, model->head_dim,
+                                     model->ffn, kSsqSlots));
+      c->dec_bar = (unsigned*)dc;
+      dc += align256((size_t)kDecodeBarWords * 4);
+      c->dec_err = (unsigned*)dc;
+      if (hipMemsetAsync(d0, 0, L.dec, c->st) != hipSuccess) { *out = c; return fail(c, ER_EDEVICE, "memset"); }
+      c->dec_err_slot = L.max_rows + rollout->max_batch;
+    }
     c->max_rows = L.max_rows;
     c->logit_rows = L.logit_rows;
     c->block_bytes = L.block_bytes;
@@ -1398,6 +1598,26 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     }
     r = set_weights(c, w);
     if (r) { *out = c; return r; }
+    if (c->dec_layers[0]) {
+      // the persistent decode forward: grid per weight format, K slices per projection
+      const int fmts[2] = {FMT_BF16, c->drf[0].qkv.fmt};
+      for (int f : fmts) c->dec_nwg[f] = decode_grid(f, model->head_dim);
+      const int G = std::max(c->dec_nwg[FMT_BF16], c->dec_nwg[fmts[1]]);
+      if (c->dec_nwg[FMT_BF16] > 0 && c->dec_nwg[fmts[1]] > 0 && c->dec_nwg[FMT_BF16] == c->dec_nwg[fmts[1]] &&
+          model->head_dim == 128) {
+        const int d = model->d_model, F = model->ffn, qn = model->n_q_heads * model->head_dim;
+        const int qkvN = (model->n_q_heads + 2 * model->n_kv_heads) * model->head_dim;
+        const int NK[4][2] = {{qkvN, d}, {d, qn}, {2 * F, d}, {d, F}};
+        bool ok = true;
+        for (int which = 0; which < 2; ++which)
+          for (int i = 0; i < 4; ++i) {
+            c->dec_ks[which][i] = decode_ksplit(NK[i][0], NK[i][1], G, fmts[which]);
+            ok = ok && c->dec_ks[which][i] > 0;
+          }
+        c->dec_avail = ok;
+        c->dec_on = false;  // off until er_set_persistent: the kernel sequence is faster on MI355X today
+      }
+    }
     r = calibrate(c);
     if (r) { *out = c; return r; }
     c->stats.alpha_ema = c->alpha_ema;
@@ -1847,6 +2067,76 @@ int er_set_timing(er_ctx* c, int period, int first_n) {
   return ER_OK;
 }
 
+int er_set_persistent(er_ctx* c, int on) {
+  if (!c) return ER_EINVAL;
+  if (on && !c->dec_avail) return fail(c, ER_ESTATE, "the persistent decode forward cannot run here");
+  c->dec_on = on != 0 && c->dec_avail;
+  return ER_OK;
+}
+
+int er_set_decode_spin_limit(er_ctx* c, int64_t polls) {
+  if (!c || polls < 1) return ER_EINVAL;
+  c->dec_spin_limit = (long)polls;
+  return ER_OK;
+}
+
+int er_set_decode_trace(er_ctx* c, int on) {
+  if (!c) return ER_EINVAL;
+  if (!on) {
+    if (c->dec_trace) (void)hipFree(c->dec_trace);
+    c->dec_trace = nullptr;
+    c->dec_trace_max = 0;
+    return ER_OK;
+  }
+  if (c->dec_trace) return ER_OK;
+  const int nb = 8 * c->md.n_layers + 8;  // barriers of one forward, with room
+  const int G = std::max(c->dec_nwg[FMT_BF16], 1024);
+  HIPC(c, hipMalloc((void**)&c->dec_trace, ((size_t)nb * G * 2 + G) * 8));
+  c->dec_trace_max = nb;
+  return ER_OK;
+}
+
+int er_get_decode_trace(er_ctx* c, double* work_us, double* release_us, int max, int* n_out) {
+  if (!c || !n_out) return ER_EINVAL;
+  *n_out = 0;
+  if (!c->dec_trace || c->dec_trace_nwg <= 0) return fail(c, ER_ESTATE, "no traced persistent forward");
+  const int G = c->dec_trace_nwg, nb = c->dec_trace_max;
+  std::vector<unsigned long long> t((size_t)nb * G * 2 + G);
+  HIPC(c, hipStreamSynchronize(c->st));
+  HIPC(c, hipMemcpy(t.data(), c->dec_trace, t.size() * 8, hipMemcpyDeviceToHost));
+  // phase k runs from the first release of barrier k-1 (kernel start for k = 0) to the last
+  // arrival at barrier k; the release is the time from that arrival to the last group's release
+  int n = 0;
+  unsigned long long prev_start = ~0ull;
+  for (int b = 0; b < G; ++b) prev_start = std::min(prev_start, t[(size_t)nb * G * 2 + b]);
+  for (int k = 0; k < nb; ++k) {
+    unsigned long long arr = 0, rel = 0, first_rel = ~0ull;
+    bool any = false;
+    for (int b = 0; b < G; ++b) {
+      const unsigned long long a0 = t[((size_t)k * G + b) * 2], a1 = t[((size_t)k * G + b) * 2 + 1];
+      if (a0 == 0 || a1 == 0) continue;
+      any = true;
+      arr = std::max(arr, a0);
+      rel = std::max(rel, a1);
+      first_rel = std::min(first_rel, a1);
+    }
+    if (!any || arr < prev_start) break;
+    if (n < max && work_us) work_us[n] = (double)(arr - prev_start) * 0.01;
+    if (n < max && release_us) release_us[n] = (double)(rel - arr) * 0.01;
+    ++n;
+    prev_start = first_rel;
+  }
+  *n_out = n;
+  HIPC(c, hipMemset(c->dec_trace, 0, t.size() * 8));
+  return ER_OK;
+}
+
+int er_get_persistent(const er_ctx* c, int* on) {
+  if (!c || !on) return ER_EINVAL;
+  *on = c->dec_on ? 1 : 0;
+  return ER_OK;
+}
+
 int er_set_fused(er_ctx* c, int on) {
   if (!c) return ER_EINVAL;
   c->fuse = c->bf16 && on != 0;
@@ -2086,6 +2376,7 @@ void er_destroy(er_ctx* c) {
   else (void)hipDeviceSynchronize();
   if (c->meta.h) (void)hipHostFree(c->meta.h);
   if (c->out_h) (void)hipHostFree(c->out_h);
+  if (c->dec_trace) (void)hipFree(c->dec_trace);
   if (c->have_ev)
     for (auto& e : c->ev) (void)hipEventDestroy(e);
   for (auto& e : c->kev) (void)hipEventDestroy(e);

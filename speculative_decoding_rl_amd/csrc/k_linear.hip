@@ -23,6 +23,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "linear_dev.h"
 
 namespace er {
 
@@ -91,48 +92,6 @@ __global__ __launch_bounds__(256) void k_linear_valu(const void* __restrict__ xv
 // MFMA linears (bf16 activations) with fused prologue / epilogue.
 // ----------------------------------------------------------------------------
 template <int FMT> struct WRegs { static constexpr int n = (FMT == FMT_BF16) ? 4 : (FMT == FMT_W8 ? 2 : 1); };
-
-// LDS/register column (in bf16 elements within the 128-wide chunk) of the 8
-// k-slots that lane group kb feeds to MFMA number i; the same mapping decides
-// which weight bytes a lane loads, so A and B agree on every k.
-template <int FMT>
-ER_DEV int kcol(int i, int kb) {
-  if constexpr (FMT == FMT_BF16) return 32 * i + 8 * kb;
-  else if constexpr (FMT == FMT_W8) return 64 * (i >> 1) + 16 * kb + 8 * (i & 1);
-  else return 32 * kb + 8 * i;
-}
-
-// 8 int8 codes (two words) -> bf16 of (q + 128), exact.
-ER_DEV bf16x8_t w8_to_bf16(uint32_t a, uint32_t b) {
-  a ^= 0x80808080u;
-  b ^= 0x80808080u;
-  uint32_t r[4];
-  const uint32_t src[2] = {a, b};
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float f0 = (float)(src[h] & 0xFFu), f1 = (float)((src[h] >> 8) & 0xFFu);
-    const float f2 = (float)((src[h] >> 16) & 0xFFu), f3 = (float)(src[h] >> 24);
-    r[2 * h] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-    r[2 * h + 1] = (__float_as_uint(f2) >> 16) | (__float_as_uint(f3) & 0xFFFF0000u);
-  }
-  return __builtin_bit_cast(bf16x8_t, *(const uint4*)r);
-}
-
-// One kernel-order W4 word (8 codes) -> bf16 of (q + 128), exact: the code
-// lands in the mantissa of 128.0.
-ER_DEV bf16x8_t w4_to_bf16(uint32_t w) {
-  // (w >> 4j) & 0x000F000F | 0x43004300.  The two constants come from
-  // opaque moves (mask in an SGPR, magic in a VGPR) so that the compiler
-  // selects one v_and_or_b32 per word instead of an and + an or with literal
-  // operands; the arithmetic itself stays plain code.
-  uint32_t mask, magic;
-  asm("s_mov_b32 %0, 0x000F000F" : "=s"(mask));
-  asm("v_mov_b32 %0, 0x43004300" : "=v"(magic));
-  uint32_t r[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) r[j] = ((w >> (4 * j)) & mask) | magic;
-  return __builtin_bit_cast(bf16x8_t, *(const uint4*)r);
-}
 
 // Physical weight row of logical row 16*s + l16.  Paired epilogues need the
 // two operands of each pair in lanes l16 and l16 ^ 8 of one 16-row subtile:

@@ -151,6 +151,75 @@ struct AttnArgs {
 // (same arguments).  *combined (nullable) tells whether a combine is needed.
 int launch_attention(const AttnArgs& a, hipStream_t st, int phase = 0, int* combined = nullptr);
 
+// Persistent decode forward (bf16 models, 1..16 rows): embedding, every
+// decoder layer and the final residual stream in one cooperative launch (see
+// k_decode.hip).  The weights of one forward share one format (the bf16
+// target, or the W4/W8 drafter).
+struct DecLayerW {
+  LinearW qkv, o, gu, down;
+  const void* attn_norm;
+  const void* mlp_norm;
+};
+struct DecodeArgs {
+  int M, L, d, hq, hkv, hd, F;
+  float eps;
+  const DecLayerW* layers;        // device array [L]
+  const void* embed;
+  const int32_t* tokens;
+  int tok_stride;
+  const int32_t* pos;             // [M]
+  const int64_t* slot;            // [M] KV slot (block * 16 + offset)
+  const float2* cs;               // RoPE cos/sin [max_pos][hd/2]
+  void* kv_pool;
+  // attention work units (push_units layout)
+  const int32_t* block_table;
+  int bt_stride;
+  const int32_t* unit_rec;        // 8 int32 per unit
+  const int32_t* unit_start;      // [n_items + 1] exclusive prefix sums of units
+  const int32_t* split_items;     // items with more than one unit
+  const int32_t* item_q_row0;
+  const int32_t* item_q_count;
+  int n_items, n_units, n_split, max_q;
+  // workspaces (device).  Every activation a phase writes lives in its own
+  // buffer, written once per forward (so other work-groups can read it through
+  // their L2 without a stale copy); rows are allocated for 16.
+  float* hbuf;                    // [2L][16][d] residual stream entering each layer / after its attention block
+  float* h_final;                 // [M, d] the residual stream after the last layer (the result)
+  uint16_t* qbuf;                 // [L][16][hq * hd] rotated queries
+  uint16_t* abuf;                 // [L][16][hq * hd] attention output
+  uint16_t* act;                  // [L][16][F] SwiGLU output
+  float* apart;                   // attention partials [units][hkv][grp * max_q][hd + 2] (reused per layer)
+  unsigned long long* ssq;        // [2L][slots][16] fixed-point sums of squares of each h buffer
+  unsigned long long* ssq_out;    // the final sums of squares, slot layout of LinArgs::ssq_in
+  int ssq_slots;
+  long ssq_stride;                // of ssq_out
+  unsigned* bar;                  // barrier words (zeroed once before the first launch)
+  unsigned* err;                  // nonzero after a barrier time-out
+  int ks[4];                      // waves splitting K in the qkv and gate/up phases ([0], [2]: 8, 4 or 2)
+  int n_wg;                       // grid size (decode_grid)
+  long spin_limit;                // polls before a barrier wait gives up
+  // optional phase trace (nullable): per grid barrier k and work-group b, the
+  // 100 MHz clock when b arrived ([k][b][0]) and when it was released ([k][b][1])
+  unsigned long long* trace;
+  int trace_max;                  // barriers the trace holds
+};
+// Work-groups of the grid (one per compute unit), 0 if the kernel cannot run.
+int decode_grid(int fmt, int hd);
+// K slices of an [N, K] projection in weight format fmt for a grid of nwg work-groups.
+int decode_ksplit(int N, int K, int nwg, int fmt);
+// Dynamic LDS of a launch (n_max: the widest projection's output rows).
+size_t decode_lds_bytes(int hd, int M, int d, int n_max, int nwg);
+// Device bytes of the write-once activation buffers for a model (16 rows).
+inline size_t decode_ws_bytes(int L, int d, int hq, int hd, int F, int slots) {
+  return (size_t)2 * L * 16 * d * 4 + (size_t)2 * L * 16 * hq * hd * 2 + (size_t)L * 16 * F * 2 +
+         (size_t)2 * L * slots * 16 * 8 + 4 * 256;
+}
+// 0, -1 for arguments it does not take, -3 on a launch error.
+int launch_decode(const DecodeArgs& a, int fmt, hipStream_t st);
+constexpr int kDecodeMaxRows = 16;
+
+constexpr int kDecodeBarWords = 10 * 32;
+
 // Quantizers (drafter build) and layout conversion.
 int launch_quantize_w8(const void* W, bool bf16, int N, int K, int8_t* q, float* scale, hipStream_t st);
 int launch_quantize_w4(const void* W, int N, int K, uint8_t* packed_canon, uint16_t* scale,

@@ -198,6 +198,29 @@ class Engine:
         return dict(step=g.step, ema_ar=list(g.ema_ar), ema_sd=list(g.ema_sd), n_ar=list(g.n_ar),
                     probe_left=list(g.probe_left), cool_until=list(g.cool_until), cool_len=list(g.cool_len))
 
+    def set_persistent(self, on: bool):
+        """Run forwards of <= 16 rows as one persistent launch (bf16 models; on by default)."""
+        check(self.lib.er_set_persistent(self.ctx, int(bool(on))), self.ctx, "er_set_persistent")
+
+    def set_decode_spin_limit(self, polls: int):
+        check(self.lib.er_set_decode_spin_limit(self.ctx, int(polls)), self.ctx, "er_set_decode_spin_limit")
+
+    def set_decode_trace(self, on: bool):
+        check(self.lib.er_set_decode_trace(self.ctx, int(bool(on))), self.ctx, "er_set_decode_trace")
+
+    def decode_trace(self):
+        """(work_us, release_us) per phase of the last traced persistent forward."""
+        w = (C.c_double * 1024)()
+        r = (C.c_double * 1024)()
+        n = C.c_int()
+        check(self.lib.er_get_decode_trace(self.ctx, w, r, 1024, C.byref(n)), self.ctx, "er_get_decode_trace")
+        return np.array(w[:n.value]), np.array(r[:n.value])
+
+    def persistent(self) -> bool:
+        v = C.c_int()
+        check(self.lib.er_get_persistent(self.ctx, C.byref(v)), self.ctx, "er_get_persistent")
+        return bool(v.value)
+
     def set_fused(self, on: bool):
         check(self.lib.er_set_fused(self.ctx, int(bool(on))), self.ctx, "er_set_fused")
 
