@@ -113,6 +113,23 @@ int er_op_attention(int act_dtype, const void *d_q, void *d_out, const void *d_k
                     const int32_t *d_q_row0, const int32_t *d_q_pos0, const int32_t *d_q_count, int n_items,
                     int max_q_count, int max_ctx, void *stream);
 
+/* er_op_attention for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * same arguments, layout and result, bit for bit; it allocates nothing.  The
+ * partial results of a key range split over work-groups go to a 16 MiB
+ * device array of the library (one copy per GPU, held until the process
+ * ends) instead of the lazily allocated workspace of er_op_attention.
+ * Returns ER_ENOMEM, launching nothing, when the call's partials would need
+ * more than those 16 MiB (floats: work units x hkv x (hq/hkv) x max_q_count x
+ * (hd + 2), the units set by max_ctx and n_items); use er_op_attention then.
+ * ER_EDEVICE if the array's address cannot be obtained.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams,
+ * other threads) race. */
+int er_op_attention_noalloc(int act_dtype, const void *d_q, void *d_out, const void *d_kv_pool, int n_layers,
+                            int layer, int hq, int hkv, int hd, const int32_t *d_block_table, int bt_stride,
+                            const int32_t *d_bt_row, const int32_t *d_q_row0, const int32_t *d_q_pos0,
+                            const int32_t *d_q_count, int n_items, int max_q_count, int max_ctx, void *stream);
+
 /* Per-row sampling statistics of fp32 logits rows [rows, ld]: per vocabulary
  * chunk of 2048 tokens the max, its first index and the softmax mass relative
  * to it (fp64), plus the top-p threshold.  d_stats: er_op_stats_bytes(V) per row. */

@@ -174,6 +174,8 @@ SIGNATURES = {
                                      C.c_int, C.c_int, P, C.c_int, P, P, C.POINTER(QkvArgs), C.c_int, P]),
     "er_op_attention": (C.c_int, [C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int, P, P,
                                   P, P, C.c_int, C.c_int, C.c_int, P]),
+    "er_op_attention_noalloc": (C.c_int, [C.c_int, P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, C.c_int,
+                                          P, P, P, P, C.c_int, C.c_int, C.c_int, P]),
     "er_op_stats_bytes": (C.c_size_t, [C.c_int]),
     "er_op_row_stats": (C.c_int, [P, C.c_int, C.c_int, C.c_long, C.c_float, C.c_float, P, P]),
     "er_op_sample_rows": (C.c_int, [P, P, C.c_int, C.c_int, C.c_long, C.c_float, C.c_float, C.c_uint64, P, P, C.c_int,

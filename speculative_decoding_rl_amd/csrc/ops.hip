@@ -48,6 +48,38 @@ int code(int r) { return r == 0 ? ER_OK : (r == -1 ? ER_EINVAL : (r == -2 ? ER_E
 
 }  // namespace
 
+// Scratch of er_op_attention_noalloc: the split partials of one call, in a
+// fixed device array (each GPU holds its own copy for the life of the
+// process).  Host code never passes the array's name to a kernel: its device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+constexpr size_t kNoAllocScratchFloats = (size_t)4 << 20;   // 16 MiB
+static __device__ __align__(256) float scratch[kNoAllocScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+float* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The calling thread's device's copy of the scratch array, or null on failure.
+float* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
 extern "C" {
 
 int er_op_quantize(int quant, int w_dtype, const void* d_w, int N, int K, void* d_codes, void* d_scale, void* d_zero,
@@ -168,6 +200,44 @@ int er_op_attention(int act_dtype, const void* d_q, void* d_out, const void* d_k
   a.bf16 = act_dtype == ER_BF16;
   a.ws = g_ws.attn;
   a.ws_floats = kAttnFloats;
+  return code(launch_attention(a, (hipStream_t)stream));
+}
+
+int er_op_attention_noalloc(int act_dtype, const void* d_q, void* d_out, const void* d_kv_pool, int n_layers,
+                            int layer, int hq, int hkv, int hd, const int32_t* d_block_table, int bt_stride,
+                            const int32_t* d_bt_row, const int32_t* d_q_row0, const int32_t* d_q_pos0,
+                            const int32_t* d_q_count, int n_items, int max_q_count, int max_ctx, void* stream) {
+  if (!d_q || !d_out || !d_kv_pool || !d_block_table || !d_bt_row || !d_q_row0 || !d_q_pos0 || !d_q_count)
+    return ER_EINVAL;
+  if (act_dtype != ER_F32 && act_dtype != ER_BF16) return ER_EINVAL;
+  if (n_layers <= 0 || layer < 0 || layer >= n_layers || hq <= 0 || hkv <= 0 || n_items < 0 || max_q_count <= 0)
+    return ER_EINVAL;
+  float* ws = scratch_ptr();
+  if (!ws) return ER_EDEVICE;
+  AttnArgs a{};
+  a.q = d_q;
+  a.out = d_out;
+  a.kv_pool = d_kv_pool;
+  a.block_table = d_block_table;
+  a.bt_stride = bt_stride;
+  a.item_bt_row = d_bt_row;
+  a.item_q_row0 = d_q_row0;
+  a.item_q_pos0 = d_q_pos0;
+  a.item_q_count = d_q_count;
+  a.n_items = n_items;
+  a.max_q_count = max_q_count;
+  a.max_ctx = max_ctx;
+  a.hq = hq;
+  a.hkv = hkv;
+  a.hd = hd;
+  a.n_layers = n_layers;
+  a.layer = layer;
+  a.bf16 = act_dtype == ER_BF16;
+  // the launcher checks the partials' size against ws_floats before launching
+  // anything (-2 -> ER_ENOMEM); nothing in the scratch needs clearing, every
+  // partial row the merge reads is written by its unit in the same call
+  a.ws = ws;
+  a.ws_floats = kNoAllocScratchFloats;
   return code(launch_attention(a, (hipStream_t)stream));
 }
 

@@ -67,6 +67,14 @@ def attention(q, out, kv_pool, n_layers, layer, hq, hkv, hd, block_table, bt_row
                                       _stream()), None, "er_op_attention")
 
 
+def attention_noalloc(q, out, kv_pool, n_layers, layer, hq, hkv, hd, block_table, bt_row, q_row0, q_pos0, q_count,
+                      max_q_count, max_ctx):
+    check(_lib.load().er_op_attention_noalloc(_act(q), _ptr(q), _ptr(out), _ptr(kv_pool), n_layers, layer, hq, hkv,
+                                              hd, _ptr(block_table), block_table.shape[1], _ptr(bt_row),
+                                              _ptr(q_row0), _ptr(q_pos0), _ptr(q_count), bt_row.shape[0],
+                                              max_q_count, max_ctx, _stream()), None, "er_op_attention_noalloc")
+
+
 def stats_bytes(V: int) -> int:
     return int(_lib.load().er_op_stats_bytes(V))
 

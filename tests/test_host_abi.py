@@ -194,3 +194,30 @@ def test_controller_plan_matches_oracle_over_scripted_streams(lib, seed):
             n_probe += got > 0 and ost.choice == 0
             step += 1
     assert n_sd > 100 and n_probe > 3
+
+
+def test_noalloc_scratch_symbol_is_global_in_the_device_code():
+    """er_op_attention_noalloc finds its device scratch with hipGetSymbolAddress, which looks the
+    symbol up by name in the loaded code object: the array must be a GLOBAL symbol there (a
+    `used` attribute on the static array leaves it LOCAL, and the lookup then aborts the process)."""
+    import shutil
+    import subprocess
+    import tempfile
+    hipcc, bundler, readelf = "/opt/rocm/bin/hipcc", "/opt/rocm/llvm/bin/clang-offload-bundler", \
+        "/opt/rocm/llvm/bin/llvm-readelf"
+    if not all(os.path.exists(p) for p in (hipcc, bundler, readelf)):
+        pytest.skip("ROCm toolchain not found")
+    src = os.path.join(ROOT, "speculative_decoding_rl_amd", "csrc", "ops.hip")
+    d = tempfile.mkdtemp()
+    try:
+        obj, co = os.path.join(d, "ops.o"), os.path.join(d, "ops.co")
+        subprocess.run([hipcc, "--offload-arch=gfx950", "-O1", "-std=c++17", "--cuda-device-only", "-c", src, "-o", obj],
+                       check=True, capture_output=True)
+        subprocess.run([bundler, "--unbundle", "--type=o", f"--input={obj}",
+                        "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], check=True, capture_output=True)
+        syms = subprocess.run([readelf, "-s", co], check=True, capture_output=True, text=True).stdout
+    finally:
+        shutil.rmtree(d)
+    rows = [l.split() for l in syms.splitlines() if l.strip().endswith("scratch")]
+    assert rows, syms
+    assert all(r[4] == "GLOBAL" for r in rows), rows
