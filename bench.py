@@ -8,10 +8,22 @@ adaptive in 1..8 (roofline toggle + EMA of the acceptance rate).
 
 A step is one pass of the whole hot path over the live batch: the controller
 picks AR or SD (and gamma), then draft -> verify -> rejection sample -> KV
-commit/rollback -> batch shrink.  With --steps 0 (default) the rollout runs to
-completion and `steps` reports how many steps that took; --steps K times the
-first K steps.  The same workload is then run with speculation forced off (the
-AR baseline).  Prefill is timed separately and excluded from `value`.
+commit/rollback.
+
+Default (--steps K, --warmup W): the shrinking-batch sweep.  The stop-length
+draw fixes, for every batch bin of the rollout (129-256, 65-128, ..., 2, 1),
+how many steps it takes, how many tokens it emits, its mean live batch and
+its mean context (one token per sequence per step: at step k the live batch
+is #{stop - 1 > k} and every live sequence holds 512 + k keys).  Each bin is
+prefilled at its mean batch and context, then runs W untimed and K timed
+steps in each of SD-auto (the roofline toggle), forced SD and AR; an
+untimed pass of K steps per mode then brackets every kernel launch with HIP
+events (the roofline object and the per-bin draft / verify HBM fractions).
+`value` is SD-auto tokens / seconds over its timed steps of all bins; the
+rollout figures compose the bins' rates with their token counts.
+
+--rollout (or --steps 0) runs the whole 256 -> 1 rollout to completion in
+SD-auto and AR instead; --crossover runs the fixed-batch sweep.
 
 Prints one JSON line (N = 1 only: the library runs on one GPU).
 """
@@ -43,8 +55,10 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=0, help="0 = run the rollout to completion")
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20,
+                    help="timed steps per batch bin and mode (0 = run the rollout to completion)")
+    ap.add_argument("--warmup", type=int, default=5, help="untimed steps per batch bin and mode")
+    ap.add_argument("--rollout", action="store_true", help="the whole 256 -> 1 rollout instead of the bin sweep")
     ap.add_argument("--config", default="", help="model shape (default qwen2.5-7b; qwen2.5-14b with --crossover)")
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--prompt-len", type=int, default=512)
@@ -62,8 +76,8 @@ def parse():
     ap.add_argument("--kv-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-profile", action="store_true")
-    ap.add_argument("--no-persistent", action="store_true",
-                    help="run every forward as the kernel sequence (no persistent decode forward)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="run forwards of <= 16 rows as the persistent decode kernel (default: kernel sequence)")
     ap.add_argument("--kprof-every", type=int, default=4,
                     help="bracket the attention launches of every this many steps of the timed rollout with HIP "
                          "events (events on every launch slow each step by ~0.3 ms)")
@@ -94,8 +108,8 @@ def make_engine(args, shape, wts, policy):
     eng = Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
                  gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=policy, max_seqs=args.batch + 64,
                  max_batch=args.batch, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
-    if args.no_persistent:
-        eng.set_persistent(False)
+    if args.persistent:
+        eng.set_persistent(True)
     return eng
 
 
@@ -305,12 +319,12 @@ def roofline_from(kprof):
 
 
 def kernel_role(name):
-    """draft: the quantized drafter's linears (W8 / W4 formats); verify: the bf16 target's linears;
-    attention serves both (the drafter reads the target's KV)."""
+    """draft: the quantized drafter's linears (W8 / W4 formats); target: the bf16 target's linears
+    (the verify pass and the AR step); attention serves both (the drafter reads the target's KV)."""
     if name.startswith("er::k_attn"):
         return "attention"
     m = re.match(r"er::k_(skinny|linear_mfma)<(\d+)", name)
-    return "draft" if m and int(m.group(2)) in (2, 3) else "verify"
+    return "draft" if m and int(m.group(2)) in (2, 3) else "target"
 
 
 def kernel_table(kprof):
@@ -324,25 +338,51 @@ def kernel_table(kprof):
 
 
 def cpu_baseline(shape_name, args):
-    """The oracle (fp64 NumPy) on the host: SD and AR decode steps of the same model shape.
+    """The oracle (fp64 NumPy, per sequence) timed on the host, on all its BLAS threads and on one:
 
-    Sample: a 2-layer, full-width slice of the model (vocab, widths, heads as
-    the workload) at batch 1 from a 512-token context; gamma = 4.  Per-step
-    time is scaled to the full depth by the ratio of streamed linear
-    parameters (the oracle is bound by reading its fp64 weights).
+    - the tiny fp32 decoder (4 prompts x 32 uniform tokens, 64 new, gamma 4, W8 drafter): the full
+      SD and AR rollouts;
+    - the workload's model shape at batch 1 and 8 from a 512-token context, gamma 4: SD and AR steps,
+      each bounded by a time budget, on a 2-layer full-width slice (vocab, widths and heads as the
+      workload), per-step time scaled to the full depth by the ratio of streamed linear parameters
+      (the oracle is bound by reading its fp64 weights), so those figures are extrapolated.  The
+      batch-8 states are copies of one prefilled state under eight sequence ids (the oracle's cost
+      does not depend on the KV contents).
+
+    value: SD tokens/s of the workload shape at batch 1 on all threads (the unit of the GPU line).
     """
-    import torch
+    import copy
 
     import synth
     from oracle import spec as OSP
     from oracle.controller import ModelCost
-    from oracle.model import KVStore, config_from, forward, weights_from
+    from oracle.model import config_from, weights_from
+    from threadpoolctl import threadpool_info, threadpool_limits
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count() or 1
+    threads_all = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    sp = OSP.SamplingParams(seed=args.seed, temperature=args.temperature, top_p=args.top_p)
+    runs = []
+
+    # the tiny decoder, whole rollouts
+    ts = synth.shape("tiny")
+    tw = synth.weights(ts, seed=args.seed)
+    tcfg = config_from(ts)
+    TW = weights_from(tcfg, {k: v.float().numpy() for k, v in tw.items()})
+    TD = OSP.build_drafter(TW, "w8")
+    tpr = [list(p) for p in synth.prompts(4, 32, ts.vocab, seed=args.seed)]
+    for nthr in (threads_all, 1):
+        with threadpool_limits(limits=nthr):
+            t0 = time.perf_counter()
+            out = OSP.rollout_spec(tcfg, TW, TD, tpr, [64] * 4, 4, sp)
+            t_sd = time.perf_counter() - t0
+            t0 = time.perf_counter()
+            out_ar = OSP.rollout_ar(tcfg, TW, tpr, [64] * 4, sp)
+            t_ar = time.perf_counter() - t0
+        n_tok = sum(len(o) for o in out)
+        runs.append(dict(model="tiny", threads=nthr, batch=4, kind="full rollout", sd_tok_s=round(n_tok / t_sd, 2),
+                         ar_tok_s=round(sum(len(o) for o in out_ar) / t_ar, 2), seconds=round(t_sd + t_ar, 2)))
+
+    # the workload's shape, a 2-layer slice, bounded step samples
     full = synth.shape(shape_name)
     sl = synth.shape(shape_name, n_layers=2)
     t0 = time.perf_counter()
@@ -351,36 +391,204 @@ def cpu_baseline(shape_name, args):
     W = weights_from(cfg, {k: v.float().numpy() for k, v in wts.items()})
     del wts
     D = OSP.build_drafter(W, sl.quant)
+    ctx, gamma = 512, 4
+    budget_sd, budget_ar, max_steps = 3.0, 1.5, 64
+    cap = ctx + (gamma + 1) * max_steps * 2 + 8
+    base = OSP.prefill(cfg, W, 0, list(synth.prompts(1, ctx, sl.vocab, seed=args.seed)[0]), 10**6, cap, sp)
     setup = time.perf_counter() - t0
-    sp = OSP.SamplingParams(seed=args.seed, temperature=args.temperature, top_p=args.top_p)
-    ctx = 512
-    prompt = list(synth.prompts(1, ctx, sl.vocab, seed=args.seed)[0])
-    gamma, max_sd, max_ar = 4, 96, 192
-    # every SD step writes at most gamma + 1 positions, every AR step one
-    st = OSP.prefill(cfg, W, 0, prompt, 10**6, ctx + (gamma + 1) * max_sd + max_ar + 8, sp)
-    t1 = time.perf_counter()
-    n_sd, tok_sd = 0, 0
-    while time.perf_counter() - t1 < 10.0 and n_sd < max_sd:
-        rec = OSP.spec_step(cfg, W, D, st, gamma, sp)
-        tok_sd += len(rec.emitted)
-        n_sd += 1
-    t_sd = (time.perf_counter() - t1) / n_sd
-    t2 = time.perf_counter()
-    n_ar = 0
-    while time.perf_counter() - t2 < 5.0 and n_ar < max_ar:
-        OSP.ar_step(cfg, W, st, sp)
-        n_ar += 1
-    t_ar = (time.perf_counter() - t2) / n_ar
     mc = lambda s: ModelCost(s.n_layers, s.d_model, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ffn, s.vocab, 2, 0.52, 2)
     scale = mc(full).p_lin / mc(sl).p_lin
-    sd_tps = (tok_sd / n_sd) / (t_sd * scale)
-    ar_tps = 1.0 / (t_ar * scale)
-    return {"value": round(sd_tps, 4), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"oracle (fp64 numpy) on {threads} BLAS threads: {n_sd} SD steps (gamma {gamma}, "
-                       f"{tok_sd / n_sd:.2f} tokens/step) and {n_ar} AR steps at batch 1, context {ctx} growing to {st.n}, on a "
-                       f"2-layer full-width slice of {shape_name}; per-step time scaled to {full.n_layers} layers "
-                       f"by streamed parameters (x{scale:.2f}, extrapolated); setup {setup:.0f} s untimed"),
-            "ar_value": round(ar_tps, 4), "measured_s": round(t_sd * n_sd + t_ar * n_ar, 2)}
+    for nthr in (threads_all, 1):
+        for B in (1, 8):
+            states = []
+            for b in range(B):
+                st = copy.copy(base)
+                st.kv = base.kv.copy()
+                st.generated = list(base.generated)
+                st.seq_id = b
+                states.append(st)
+            with threadpool_limits(limits=nthr):
+                t0 = time.perf_counter()
+                n_sd = tok_sd = 0
+                while n_sd < 1 or (time.perf_counter() - t0 < budget_sd and n_sd < max_steps):
+                    for st in states:
+                        tok_sd += len(OSP.spec_step(cfg, W, D, st, gamma, sp).emitted)
+                    n_sd += 1
+                t_sd = (time.perf_counter() - t0) / n_sd
+                t0 = time.perf_counter()
+                n_ar = 0
+                while n_ar < 1 or (time.perf_counter() - t0 < budget_ar and n_ar < max_steps):
+                    for st in states:
+                        OSP.ar_step(cfg, W, st, sp)
+                    n_ar += 1
+                t_ar = (time.perf_counter() - t0) / n_ar
+            runs.append(dict(model=f"{shape_name} (2 of {full.n_layers} layers, extrapolated x{scale:.2f})",
+                             threads=nthr, batch=B, context=ctx, gamma=gamma, sd_steps=n_sd, ar_steps=n_ar,
+                             tokens_per_seq_sd_step=round(tok_sd / (n_sd * B), 3),
+                             sd_tok_s=round((tok_sd / n_sd) / (t_sd * scale), 4),
+                             ar_tok_s=round(B / (t_ar * scale), 4), seconds=round(t_sd * n_sd + t_ar * n_ar, 2)))
+    head = next(r for r in runs if r["model"] != "tiny" and r["threads"] == threads_all and r["batch"] == 1)
+    return {"value": head["sd_tok_s"], "unit": "tokens/s", "cores": int(threads_all), "kind": "oracle",
+            "sample": (f"oracle (fp64 numpy, one sequence at a time): {shape_name} at batch 1, context {ctx}, "
+                       f"gamma {gamma}, SD steps for {budget_sd:.0f} s on a 2-layer full-width slice, per-step time "
+                       f"scaled to {full.n_layers} layers by streamed parameters (x{scale:.2f}, extrapolated); "
+                       f"also batch 8, one thread, and the tiny decoder's full rollouts (runs); setup "
+                       f"{setup:.0f} s untimed"),
+            "host_cpu_count": os.cpu_count(), "ar_value": head["ar_tok_s"],
+            "measured_s": round(sum(r["seconds"] for r in runs), 2), "runs": runs}
+
+
+BIN_EDGES = (256, 128, 64, 32, 16, 8, 4, 2, 1)
+
+
+def bin_plan(stops, prompt_len, batch):
+    """The batch bins of the shrinking-batch rollout, paced one token per sequence per step: at step k
+    the live batch is #{i : stop_i - 1 > k} (the prefill token counts toward the stop length) and every
+    live sequence holds prompt_len + k committed keys.  Per bin (lo, hi]: its steps, its tokens, the
+    step-mean live batch and the step-mean context."""
+    act = np.asarray(stops, dtype=np.int64) - 1
+    ks = np.arange(int(act.max()))
+    B = np.searchsorted(np.sort(act), ks, side="right")
+    B = len(act) - B                                   # #{act > k}
+    edges = [e for e in BIN_EDGES if e < batch]
+    out = []
+    for hi, lo in zip([batch] + edges, edges + [0]):
+        sel = (B > lo) & (B <= hi)
+        n = int(sel.sum())
+        if n == 0:
+            continue
+        tok = int(B[sel].sum())
+        out.append(dict(bin=f"{lo + 1}-{hi}" if hi > lo + 1 else f"{hi}", lo=lo, hi=hi, plan_steps=n,
+                        plan_tokens=tok, batch=max(1, int(round(tok / n))),
+                        context=int(round(prompt_len + ks[sel].mean()))))
+    return out
+
+
+def merge_kprof(lists):
+    """Sum kernel-profile records (one list per pass) by kernel name."""
+    acc = {}
+    for lst in lists:
+        for k in lst:
+            a = acc.setdefault(k["name"], dict(name=k["name"], launches=0, ms=0.0, bytes=0.0, flops=0.0))
+            a["launches"] += k["launches"]
+            a["ms"] += k["ms"]
+            a["bytes"] += k["bytes"]
+            a["flops"] += k["flops"]
+    return list(acc.values())
+
+
+def role_tops(kprof):
+    """The largest-time kernel of each role with its achieved HBM rate."""
+    out = {}
+    for role in ("draft", "target", "attention"):
+        ks = [k for k in kprof if kernel_role(k["name"]) == role and k["ms"] > 0]
+        if not ks:
+            continue
+        k = max(ks, key=lambda k: k["ms"])
+        gbs = k["bytes"] / (k["ms"] * 1e-3) / 1e9
+        out[role] = dict(kernel=k["name"], avg_us=round(k["ms"] * 1e3 / k["launches"], 2), gbs=round(gbs, 1),
+                         frac_hbm=round(gbs / HBM_PEAK_GBS, 4), share=round(k["ms"] / sum(x["ms"] for x in kprof), 4))
+    return out
+
+
+SWEEP_MODES = (("sd", "SD-auto"), ("force-sd", "forced SD"), ("ar", "AR"))
+
+
+def sweep(args, shape, wts, stops):
+    """The timed measurement: every batch bin of the rollout at its mean batch and context, W
+    untimed and K timed steps per mode, then an untimed all-launch profile pass (see the module notes)."""
+    import torch
+
+    import synth
+    from speculative_decoding_rl_amd import Engine, _lib
+
+    plan = bin_plan(stops, args.prompt_len, args.batch)
+    K, Wm = args.steps, args.warmup
+    per_step = args.gamma_max + 1
+    room = (len(SWEEP_MODES) * (Wm + 2 * K)) * per_step + 16      # keys a sequence may gain in its bin
+    max_ctx = (max(b["context"] for b in plan) + room + 32 + 15) // 16 * 16
+    kv_blocks = max(b["batch"] * ((b["context"] + room + 15) // 16 + 2) for b in plan) + 64
+    eng = Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
+                 gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=_lib.ER_POLICY_AUTO,
+                 max_seqs=max(b["batch"] for b in plan) + 8, max_batch=max(b["batch"] for b in plan),
+                 max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
+    if args.persistent:
+        eng.set_persistent(True)
+    if args.gamma:
+        eng.set_gamma(args.gamma)
+    pol = {"sd": _lib.ER_POLICY_AUTO, "force-sd": _lib.ER_POLICY_FORCE_SD, "ar": _lib.ER_POLICY_FORCE_AR}
+    roof = Roofline(shape)
+    rows, all_kprof, timed_recs = [], [], {m: [] for m, _ in SWEEP_MODES}
+    t_prefill = 0.0
+    for bi, b in enumerate(plan):
+        B, C = b["batch"], b["context"]
+        prompts = synth.prompts(B, C, shape.vocab, seed=args.seed + 101 * (bi + 1))
+        ids = eng.kv_alloc([C] * B, [room] * B)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eng.prefill(ids, list(prompts))
+        torch.cuda.synchronize()
+        t_prefill += time.perf_counter() - t0
+        act = [int(i) for i in ids]
+        row = dict(bin=b["bin"], batch=B, context=C, plan_steps=b["plan_steps"], plan_tokens=b["plan_tokens"])
+        for m, _ in SWEEP_MODES:
+            eng.set_policy(pol[m])
+            for _ in range(Wm):
+                eng.step(act)
+            recs = []
+            cbar = sum(eng.seq_info(a)[1] for a in act) / B     # committed keys, tracked from the emitted counts
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(K):
+                ts = time.perf_counter()
+                tok, ne, info = eng.step(act)
+                te = time.perf_counter()
+                n_em = int(ne.sum())
+                recs.append((B, int(info.mode), int(info.gamma), n_em, te - ts, int(info.accepted), cbar))
+                cbar += n_em / B
+            torch.cuda.synchronize()
+            dt = time.perf_counter() - t0
+            tokens = sum(r[3] for r in recs)
+            timed_recs[m].extend(recs)
+            row[m] = dict(tok_s=round(tokens / dt, 1), ms_per_step=round(dt * 1e3 / K, 3), tokens=tokens,
+                          seconds=round(dt, 4), sd_steps=sum(1 for r in recs if r[1] == 1),
+                          mean_gamma=round(float(np.mean([r[2] for r in recs if r[1] == 1])), 2)
+                          if any(r[1] == 1 for r in recs) else None,
+                          roofline_frac=round(sum(roof.step(r[1], r[2], r[0], r[6]) for r in recs) / dt, 4))
+        row["sd_over_ar"] = round(row["sd"]["tok_s"] / row["ar"]["tok_s"], 4)
+        row["force_sd_over_ar"] = round(row["force-sd"]["tok_s"] / row["ar"]["tok_s"], 4)
+        # untimed: the same steps again with every launch bracketed by HIP events
+        kp_bin = []
+        if not args.no_kernel_profile:
+            for m, _ in SWEEP_MODES:
+                eng.set_policy(pol[m])
+                eng.reset_kernel_profile()
+                eng.set_kernel_profile(_lib.ER_KPROF_ALL)
+                for _ in range(K):
+                    eng.step(act)
+                kp_bin.append(eng.kernel_profile())
+                eng.set_kernel_profile(_lib.ER_KPROF_OFF)
+            all_kprof.extend(kp_bin)
+            row["kernels"] = role_tops(merge_kprof(kp_bin))
+        eng.kv_free(ids)
+        st = eng.stats()
+        row["alpha_ema"] = round(st["alpha_ema"], 4)
+        log(f"[sweep] bin {b['bin']:>7s} B={B:3d} C={C:5d}: SD-auto {row['sd']['tok_s']:9.1f} tok/s "
+            f"({row['sd']['sd_steps']}/{K} SD), forced SD {row['force-sd']['tok_s']:9.1f}, AR {row['ar']['tok_s']:9.1f}"
+            f" -> SD-auto/AR {row['sd_over_ar']:.3f}")
+        rows.append(row)
+    eng.set_policy(_lib.ER_POLICY_AUTO)
+    st = eng.stats()
+    cm = eng.cost_model()
+    eng.close()
+
+    def composed(m):   # rollout seconds: each bin's planned tokens at its measured rate
+        t = sum(r["plan_tokens"] / r[m]["tok_s"] for r in rows)
+        return sum(r["plan_tokens"] for r in rows) / t
+
+    comp = {m: round(composed(m), 1) for m, _ in SWEEP_MODES}
+    return dict(rows=rows, recs=timed_recs, kprof=merge_kprof(all_kprof), composed=comp, stats=st, cost=cm,
+                prefill_s=t_prefill)
 
 
 def crossover(args, shape, wts):
@@ -412,8 +620,8 @@ def crossover(args, shape, wts):
                  gamma_init=min(4, max(gammas)), gamma_min=1, gamma_max=max(gammas), policy=_lib.ER_POLICY_FORCE_AR,
                  max_seqs=Bmax,
                  max_batch=Bmax, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
-    if args.no_persistent:
-        eng.set_persistent(False)
+    if args.persistent:
+        eng.set_persistent(True)
     prompts = synth.prompts(Bmax, C, shape.vocab, seed=args.seed)
     ids = [int(i) for i in eng.kv_alloc([C] * Bmax, [max_ctx - C - 16] * Bmax)]
     t0 = time.perf_counter()
@@ -478,6 +686,86 @@ def crossover(args, shape, wts):
             "rows": rows}
 
 
+def sweep_line(args, shape, wts, stops):
+    """The JSON line of the bin sweep."""
+    t0 = time.perf_counter()
+    sw = sweep(args, shape, wts, stops)
+    log(f"[sweep] done in {time.perf_counter() - t0:.1f} s (prefill {sw['prefill_s']:.1f} s untimed)")
+    rows, recs = sw["rows"], sw["recs"]
+    t_sd = sum(r["sd"]["seconds"] for r in rows)
+    tok_sd = sum(r["sd"]["tokens"] for r in rows)
+    t_ar = sum(r["ar"]["seconds"] for r in rows)
+    tok_ar = sum(r["ar"]["tokens"] for r in rows)
+    n_steps = len(rows) * args.steps
+    rf, rf_detail = roofline_from(sw["kprof"])
+    roof = Roofline(shape)
+    st = sw["stats"]
+    bins_desc = ", ".join(f"{r['bin']}: B={r['batch']} C={r['context']}" for r in rows)
+    out = {
+        "metric": METRIC,
+        "value": round(tok_sd / t_sd, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_sd * 1e3 / n_steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (random-init weights N(0,0.02), uniform prompts, lognormal stop lengths)",
+        "config": {"workload": (f"{args.config}-shaped decoder{'' if not args.layers else f' ({args.layers} layers)'}, "
+                                f"{shape.quant.upper()} self-drafter, {args.batch} prompts x {args.prompt_len} tokens, "
+                                f"stop lengths lognormal(median {int(args.median)}, sigma 0.75) cap {args.cap}, "
+                                f"T={args.temperature}, top-p={args.top_p}, gamma "
+                                f"{'adaptive 1..%d' % args.gamma_max if not args.gamma else args.gamma}; "
+                                f"the {len(rows)} batch bins of its 256->1 rollout, each prefilled at the bin's mean "
+                                f"batch B and mean context C ({bins_desc}), {args.warmup} untimed + {args.steps} "
+                                f"timed steps per bin in SD-auto, forced SD and AR; value = SD-auto tokens / "
+                                f"seconds over its {n_steps} timed steps, ms_per_step their mean"),
+                   "mode": "SD-auto (roofline toggle)", "global_batch": args.batch, "seq_len": args.prompt_len,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": rf,
+        "ar_value": round(tok_ar / t_ar, 2),
+        "sd_over_ar": round((tok_sd / t_sd) / (tok_ar / t_ar), 4),
+        "force_sd_value": round(sum(r["force-sd"]["tokens"] for r in rows) /
+                                sum(r["force-sd"]["seconds"] for r in rows), 2),
+        "rollout_composed": {"note": "each bin's planned tokens at its measured rate: tokens / sum(bin tokens / "
+                                     "bin tok/s) over the bins of the stop-length draw",
+                             "tokens": sum(r["plan_tokens"] for r in rows),
+                             "sd_auto_tok_s": sw["composed"]["sd"], "forced_sd_tok_s": sw["composed"]["force-sd"],
+                             "ar_tok_s": sw["composed"]["ar"],
+                             "sd_auto_over_ar": round(sw["composed"]["sd"] / sw["composed"]["ar"], 4),
+                             "forced_sd_over_ar": round(sw["composed"]["force-sd"] / sw["composed"]["ar"], 4)},
+        "by_bin": rows,
+    }
+    out["acceptance"] = {"alpha_ema_end": round(st["alpha_ema"], 4),
+                         "accepted_per_draft": round(st["accepted"] / st["drafted"], 4) if st["drafted"] else None,
+                         "mean_emitted_per_sd_seq_step": round(1.0 + st["accepted"] / st["predict_times"], 4)
+                         if st["predict_times"] else None,
+                         "sd_steps": sum(r["sd"]["sd_steps"] for r in rows),
+                         "sd_steps_all_modes": st["sd_steps"], "ar_steps_all_modes": st["ar_steps"],
+                         "effective_length": round(st["effective_length"], 4),
+                         "effective_percent": round(st["effective_percent"], 4)}
+    cm = sw["cost"]
+    out["controller"] = {"hbm_gbs": round(cm["hbm_bytes_per_s"] / 1e9, 1), "tflops": round(cm["flops_per_s"] / 1e12, 1),
+                         "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3)}
+    out["roofline_frac_timed"] = {m: round(sum(roof.step(x[1], x[2], x[0], x[6]) for x in recs[m]) /
+                                           sum(x[4] for x in recs[m]), 4) for m, _ in SWEEP_MODES}
+    out["prefill_s"] = round(sw["prefill_s"], 3)
+    if rf_detail:
+        rf_detail["from"] = ("untimed pass: the same bins and modes, every launch bracketed with HIP events on "
+                             "the library's stream")
+        out["roofline_kernel"] = rf_detail
+        out["kernels_top"] = kernel_table(sw["kprof"])[:12]
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(args.config, args)
+        except Exception as e:  # reported, not fatal
+            out["cpu_baseline"] = {"error": repr(e)}
+    return out
+
+
 def main():
     args = parse()
     args.kprof_every = max(1, args.kprof_every)
@@ -513,6 +801,10 @@ def main():
     prompts = synth.prompts(args.batch, args.prompt_len, shape.vocab, seed=args.seed)
     stops = synth.stop_lengths(args.batch, args.median, args.cap, seed=args.seed)
     log(f"stop lengths: sum {int(stops.sum())}, max {int(stops.max())}, median {int(np.median(stops))}")
+    if args.steps > 0 and not args.rollout:
+        print(json.dumps(sweep_line(args, shape, wts, stops)), flush=True)
+        return
+    args.steps = 0
 
     t0 = time.perf_counter()
     eng = make_engine(args, shape, wts, _lib.ER_POLICY_AUTO)
