@@ -639,7 +639,8 @@ int forward(er_ctx* c, const Fwd& f) {
       if (e >= 0) {
         const double kvb = 2.0 * hkv * hd * c->act_bytes;  // K and V of one position, one layer
         const double by = f.kv_keys * kvb + 2.0 * f.M * hq * hd * c->act_bytes;
-        const char* nm = !c->bf16 ? "er::k_attn_valu" : (hd == 128 ? "er::k_attn_mfma<128>" : "er::k_attn_mfma<64>");
+        const char* nm = !c->bf16 ? "er::k_attn_valu" : (hd == 128 ? "er::k_attn_mfma<128, 4>" : "er::k_attn_mfma<64, 4>");
+        static_assert(kAttnWaves == 4, "kernel-profile names carry the wave count");
         kp_end(c, e, nm, by, 4.0 * f.kv_keys * f.max_q * (double)hq * hd);
       }
       if (combined) {

@@ -33,6 +33,10 @@
 namespace er {
 
 typedef short __attribute__((ext_vector_type(4))) bf16x4s_t;
+typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2_t;
+
+// Most KV blocks one work unit covers (its block ids are staged in LDS).
+constexpr int kAttnMaxUnitBlocks = 1024;
 
 ER_DEV long kv_block_base(long phys, int layer, int L, int kv, int hkv, int head, int hd) {
   return ((((phys * L + layer) * 2 + kv) * hkv + head) * 16) * (long)hd;
@@ -74,8 +78,8 @@ ER_DEV Unit unit_of(const AttnArgs& a, int u, int nsplit, int bps) {
   return w;
 }
 
-template <int HD>
-__global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int bps) {
+template <int HD, int NW>
+__global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a, int nsplit, int bps) {
   constexpr int NC = HD / 16;   // 16-column output tiles
   constexpr int NQ = HD / 32;   // 32-wide k slices of the score MFMA
   const int u = blockIdx.x, g = blockIdx.y;
@@ -112,16 +116,19 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   const int R = grp * qc;
   const int rgroups = (R + 15) >> 4;
   const int rgn = rgroups == 1 ? 1 : (rgroups == 2 ? 2 : 4);
-  const int s_in = 4 / rgn;                  // waves sharing one row group
+  const int s_in = NW / rgn;                 // waves sharing one row group
   const int rgi = wave / s_in, sin = wave % s_in;
   const int nblk = (pos0 + qc + 15) >> 4;
   const int b0 = w.b0;
-  const int b1 = min(nblk, b0 + w.bps);
-  const float scale = 1.0f / sqrtf((float)HD);
+  const int b1 = min(min(nblk, b0 + w.bps), b0 + kAttnMaxUnitBlocks);
+  // scores in the log2 domain: s * log2(e) / sqrt(hd), so that every
+  // exponential is one v_exp_f32 (exp2); the running maxima, the partial
+  // records and the merges all use that domain
+  const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
   constexpr int OS = HD + 4;   // padded row stride of the merge area (rows 4 apart hit other banks)
-  __shared__ float o_sh[4][16 * OS];
-  __shared__ float ml_sh[4][2][16];
+  __shared__ float o_sh[NW][16 * OS];
+  __shared__ float ml_sh[NW][2][16];
 
   // this lane's query row (as the MFMA column n = l16)
   const int r_q = rgi * 16 + l16;
@@ -149,20 +156,32 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
   const uint16_t* pool = (const uint16_t*)a.kv_pool;
   const int32_t* bt = a.block_table + (long)btrow * a.bt_stride;
 
+  // the unit's block ids, staged once (the launcher keeps a unit at most
+  // kAttnMaxUnitBlocks blocks long)
+  __shared__ int ids_sh[kAttnMaxUnitBlocks];
+  for (int j = tid; j < b1 - b0; j += NW * 64) ids_sh[j] = bt[b0 + j];
+  __syncthreads();
+
   if (rgi < rgroups) {
     // This wave's blocks are first + s_in * t, t < nb.  Their K and V
     // fragments go through a ring of D register stages (loads of blocks t+1
-    // and t+2 are in flight while block t is scored); the block ids come from
-    // scalar loads one iteration ahead.  Every load is unconditional (indices
-    // clamped to the last block): conditional loads would make the compiler
-    // drain the whole load counter at each use.
+    // and t+2 are in flight while block t is scored).  The block ids come
+    // from LDS one iteration ahead: LDS reads are counted apart from the
+    // vector-memory loads, so reading an id never waits on K/V loads in
+    // flight (an id from a global or scalar load issued in the loop either
+    // stalls on that load's latency or makes the compiler drain the ring).
+    // Every load is unconditional (indices clamped to the last block):
+    // conditional loads would make the compiler drain the whole load counter
+    // at each use.
     constexpr int D = 3;
     const int first = b0 + sin;
     const int nb = first < b1 ? (b1 - first + s_in - 1) / s_in : 0;
     const int tl = nb > 0 ? nb - 1 : 0;
     uint4 kq[D][NQ];
     uint2 vq[D][NC];
-    auto bid = [&](int t) -> long { return (long)bt[first + s_in * min(t, tl)]; };
+    auto bid = [&](int t) -> long {
+      return (long)__builtin_amdgcn_readfirstlane(ids_sh[sin + s_in * min(t, tl)]);
+    };
     auto fetch = [&](int slot, long phys) {
       const uint16_t* kp = pool + kv_block_base(phys, a.layer, a.n_layers, 0, a.hkv, g, HD);
       const uint16_t* vp = pool + kv_block_base(phys, a.layer, a.n_layers, 1, a.hkv, g, HD);
@@ -203,35 +222,46 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
         corr = 1.f;
         pk[0] = pk[1] = pl[0] = pl[1] = 0u;
       } else {
-        corr = expf(m_run - m_new);
-        float p[4];
-        uint32_t hb[4], lb[4];
+        corr = __builtin_amdgcn_exp2f(m_run - m_new);
+        float p[4], lo[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          p[r] = (s[r] == -INFINITY) ? 0.f : expf(s[r] - m_new);
+          p[r] = __builtin_amdgcn_exp2f(s[r] - m_new);   // exp2(-inf) = 0 for masked keys
           psum += p[r];
-          hb[r] = f2bf(p[r]);
-          lb[r] = f2bf(p[r] - bf2f((uint16_t)hb[r]));
         }
-        pk[0] = hb[0] | (hb[1] << 16);
-        pk[1] = hb[2] | (hb[3] << 16);
-        pl[0] = lb[0] | (lb[1] << 16);
-        pl[1] = lb[2] | (lb[3] << 16);
+        // bf16 pairs by the hardware conversion (round to nearest even)
+        const bf16x2_t h01 = {(__bf16)p[0], (__bf16)p[1]}, h23 = {(__bf16)p[2], (__bf16)p[3]};
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          lo[r] = p[r] - (float)h01[r];
+          lo[2 + r] = p[2 + r] - (float)h23[r];
+        }
+        const bf16x2_t l01 = {(__bf16)lo[0], (__bf16)lo[1]}, l23 = {(__bf16)lo[2], (__bf16)lo[3]};
+        pk[0] = __builtin_bit_cast(uint32_t, h01);
+        pk[1] = __builtin_bit_cast(uint32_t, h23);
+        pl[0] = __builtin_bit_cast(uint32_t, l01);
+        pl[1] = __builtin_bit_cast(uint32_t, l23);
       }
       psum += __shfl_xor(psum, 16, 64);
       psum += __shfl_xor(psum, 32, 64);
       l_run = l_run * corr + psum;
       m_run = m_new;
-      // rescale O rows (rows 4*kb + r live in lanes l16 == 4*kb + r of the score layout)
-      float cr[4];
+      // rescale O rows (rows 4*kb + r live in lanes l16 == 4*kb + r of the
+      // score layout) -- skipped when no row's maximum moved, where every
+      // factor is exactly 1
+      if (__builtin_amdgcn_ballot_w64(corr != 1.0f) != 0) {
+        float cr[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * kb + r, 64);
+        for (int r = 0; r < 4; ++r) cr[r] = __shfl(corr, 4 * kb + r, 64);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[c][r] *= cr[r];
+      }
       const bf16x4s_t pa = __builtin_bit_cast(bf16x4s_t, *(const uint2*)pk);
       const bf16x4s_t pb = __builtin_bit_cast(bf16x4s_t, *(const uint2*)pl);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[c][r] *= cr[r];
         // B = V^T: n = column 16c + l16, k = tokens 4*kb .. +4
         const bf16x4s_t vf = __builtin_bit_cast(bf16x4s_t, vc[c]);
         o[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vf, o[c], 0, 0, 0);
@@ -266,20 +296,20 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
     if (kb == 0) { ml_sh[wave][0][l16] = m_run; ml_sh[wave][1][l16] = l_run; }
     __syncthreads();
     const int w0 = rgi * s_in;
-    float f[4][4];
+    float f[4][NW];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * kb + r;
-      float mr[4], M = -INFINITY;
+      float mr[NW], M = -INFINITY;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         mr[w] = w < s_in ? ml_sh[w0 + w][0][row] : -INFINITY;
         M = fmaxf(M, mr[w]);
       }
       float L = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        f[r][w] = (mr[w] == -INFINITY) ? 0.f : expf(mr[w] - M);
+      for (int w = 0; w < NW; ++w) {
+        f[r][w] = (mr[w] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mr[w] - M);
         if (w < s_in) L = fmaf(f[r][w], ml_sh[w0 + w][1][row], L);
       }
       rm[r] = M;
@@ -292,7 +322,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(AttnArgs a, int nsplit, int b
       for (int r = 0; r < 4; ++r) {
         float v = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w)
+        for (int w = 0; w < NW; ++w)
           if (w < s_in) v = fmaf(f[r][w], o_sh[w0 + w][(4 * kb + r) * OS + 16 * c + l16], v);
         o[c][r] = v;
       }
@@ -411,7 +441,8 @@ __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
   float dl = 0.f;
   for (int s = tid; s < nu; s += nt) {
     const float ms = base[s * stride_sp + hd];
-    const float wt = (ms == -INFINITY) ? 0.f : expf(ms - M);
+    // the bf16 kernel's partial maxima are in the log2 domain, the fp32 one's natural
+    const float wt = (ms == -INFINITY) ? 0.f : (BF ? __builtin_amdgcn_exp2f(ms - M) : expf(ms - M));
     w_sh[s] = wt;
     dl = fmaf(wt, base[s * stride_sp + hd + 1], dl);
   }
@@ -453,7 +484,7 @@ int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined
   // rows): 4 when the rows fit one 16-row group, 2 for two, else 1.
   const int rows = grp * a.max_q_count;
   const int rgroups = (rows + 15) / 16;
-  const int s_in = rgroups == 1 ? 4 : (rgroups == 2 ? 2 : 1);
+  const int s_in = (rgroups == 1 ? 4 : (rgroups == 2 ? 2 : 1)) * (kAttnWaves / 4);
   // Split the keys over work-groups until each wave walks at most 4 blocks
   // (each block is a dependent load of scattered pages), but no further than
   // ~512 groups in flight.
@@ -461,6 +492,7 @@ int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined
   int nsplit = 1;
   if (maxblk > per_wg)
     nsplit = (int)std::max(1L, std::min((long)(maxblk + per_wg - 1) / per_wg, (512 + base - 1) / base));
+  if ((maxblk + nsplit - 1) / nsplit > kAttnMaxUnitBlocks) nsplit = (maxblk + kAttnMaxUnitBlocks - 1) / kAttnMaxUnitBlocks;
   const int bps = (maxblk + nsplit - 1) / nsplit;
   nsplit = (maxblk + bps - 1) / bps;
   const long units = a.unit_start ? (long)a.n_units : (long)a.n_items * nsplit;
@@ -475,8 +507,8 @@ int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined
   dim3 grid((unsigned)units, a.hkv, 1);
   if (phase != 2) {
   if (a.bf16) {
-    if (a.hd == 128) hipLaunchKernelGGL(k_attn_mfma<128>, grid, dim3(256), 0, st, a, nsplit, bps);
-    else hipLaunchKernelGGL(k_attn_mfma<64>, grid, dim3(256), 0, st, a, nsplit, bps);
+    if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
+    else hipLaunchKernelGGL((k_attn_mfma<64, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
   } else {
     hipLaunchKernelGGL(k_attn_valu, grid, dim3(256), 0, st, a, nsplit, bps);
   }

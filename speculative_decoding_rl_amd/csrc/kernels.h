@@ -149,6 +149,8 @@ struct AttnArgs {
 };
 // phase 0: scores + combine; 1: the scoring kernel only; 2: the combine only
 // (same arguments).  *combined (nullable) tells whether a combine is needed.
+// Waves per work-group of the bf16 attention kernel (k_attn_mfma<hd, waves>).
+constexpr int kAttnWaves = 4;
 int launch_attention(const AttnArgs& a, hipStream_t st, int phase = 0, int* combined = nullptr);
 
 // Persistent decode forward (bf16 models, 1..16 rows): embedding, every

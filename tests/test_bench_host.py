@@ -69,9 +69,9 @@ def test_kernel_roles():
     b = _bench()
     assert b.kernel_role("er::k_skinny<3, 1, 2, 3>") == "draft"          # W4 drafter
     assert b.kernel_role("er::k_linear_mfma<2, 16, 1, 8>") == "draft"    # W8 drafter
-    assert b.kernel_role("er::k_skinny<1, 1, 2, 2>") == "verify"         # bf16 target
-    assert b.kernel_role("er::k_gemm2<64, 1, 4, 64>") == "verify"
-    assert b.kernel_role("er::k_attn_mfma<128>") == "attention"
+    assert b.kernel_role("er::k_skinny<1, 1, 2, 2>") == "target"         # bf16 target (verify and AR)
+    assert b.kernel_role("er::k_gemm2<64, 1, 4, 64>") == "target"
+    assert b.kernel_role("er::k_attn_mfma<128, 4>") == "attention"
     assert b.kernel_role("er::k_attn_combine<true>") == "attention"
 
 
@@ -84,3 +84,22 @@ def test_more_than_one_gpu_is_refused():
     assert r.returncode == 2
     msg = json.loads(r.stdout.strip().splitlines()[-1])
     assert "one GPU" in msg["error"]
+
+
+def test_bin_plan_counts_every_step_and_token_once():
+    """The batch bins of the stop-length draw: at step k the live batch is #{stop - 1 > k}; every step
+    falls in exactly one bin, the bins' tokens add up to the rollout's (the prefill token aside), and
+    each bin's mean batch lies inside the bin."""
+    import numpy as np
+    b = _bench()
+    stops = np.array([1, 2, 2, 5, 9, 9, 40, 300, 1000], dtype=np.int32)
+    plan = b.bin_plan(stops, 512, len(stops))
+    assert sum(p["plan_steps"] for p in plan) == int(stops.max()) - 1
+    assert sum(p["plan_tokens"] for p in plan) == int((stops - 1).sum())
+    for p in plan:
+        assert p["lo"] < p["batch"] <= p["hi"]
+        assert p["context"] >= 512
+    # a hand count: steps 0..998 for the longest; batch 1 from step 299 to 998 (700 steps, context 512 + 648.5)
+    last = plan[-1]
+    assert (last["hi"], last["plan_steps"], last["plan_tokens"]) == (1, 700, 700)
+    assert last["context"] == round(512 + (299 + 998) / 2)
