@@ -59,6 +59,8 @@ def parse():
                     help="timed steps per batch bin and mode (0 = run the rollout to completion)")
     ap.add_argument("--warmup", type=int, default=5, help="untimed steps per batch bin and mode")
     ap.add_argument("--rollout", action="store_true", help="the whole 256 -> 1 rollout instead of the bin sweep")
+    ap.add_argument("--group", type=int, default=0,
+                    help="GRPO-style groups: every G sequences of a bin share their prefilled context's KV blocks")
     ap.add_argument("--config", default="", help="model shape (default qwen2.5-7b; qwen2.5-14b with --crossover)")
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--prompt-len", type=int, default=512)
@@ -522,8 +524,13 @@ def sweep(args, shape, wts, stops):
     t_prefill = 0.0
     for bi, b in enumerate(plan):
         B, C = b["batch"], b["context"]
-        prompts = synth.prompts(B, C, shape.vocab, seed=args.seed + 101 * (bi + 1))
-        ids = eng.kv_alloc([C] * B, [room] * B)
+        if args.group > 1:   # one prompt per group, its members share the prompt's blocks
+            gp = synth.prompts((B + args.group - 1) // args.group, C, shape.vocab, seed=args.seed + 101 * (bi + 1))
+            prompts = [gp[i // args.group] for i in range(B)]
+            ids = eng.kv_alloc([C] * B, [room] * B, share_group=[i // args.group for i in range(B)])
+        else:
+            prompts = synth.prompts(B, C, shape.vocab, seed=args.seed + 101 * (bi + 1))
+            ids = eng.kv_alloc([C] * B, [room] * B)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         eng.prefill(ids, list(prompts))
@@ -722,7 +729,9 @@ def sweep_line(args, shape, wts, stops):
                                 f"the {len(rows)} batch bins of its 256->1 rollout, each prefilled at the bin's mean "
                                 f"batch B and mean context C ({bins_desc}), {args.warmup} untimed + {args.steps} "
                                 f"timed steps per bin in SD-auto, forced SD and AR; value = SD-auto tokens / "
-                                f"seconds over its {n_steps} timed steps, ms_per_step their mean"),
+                                f"seconds over its {n_steps} timed steps, ms_per_step their mean"
+                                + (f"; groups of {args.group} sequences share their bin's prefilled context"
+                                   if args.group > 1 else "")),
                    "mode": "SD-auto (roofline toggle)", "global_batch": args.batch, "seq_len": args.prompt_len,
                    "parallelism": "none (1 GPU)"},
         "roofline": rf,

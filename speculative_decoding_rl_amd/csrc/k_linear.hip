@@ -1613,7 +1613,8 @@ static int dispatch_skinny(const LinArgs& a, hipStream_t st, LinearInfo* info) {
     return run_skinny<FMT, 1, 8, 2>(a, st, info);
   } else {
     if (K >= 8192) return run_skinny<FMT, 1, 8, 4>(a, st, info);
-    if (N >= 8192) return run_skinny<FMT, 1, 2, 3>(a, st, info);
+    // 64 rows per work-group: their scale/zero pairs must fit beside x' (the caller checked 16 rows)
+    if (N >= 8192 && skinny_lds(FMT, a.M, K, 1, 2).total <= kSkinnyLdsMax) return run_skinny<FMT, 1, 2, 3>(a, st, info);
     return run_skinny<FMT, 1, 8, 2>(a, st, info);
   }
 }
@@ -1662,10 +1663,15 @@ static int run_stream_auto(const LinArgs& a, hipStream_t st, LinearInfo* info) {
     return dispatch_skinny<FMT>(a, st, info);
   } else {
     if (M > 8) {
-      if (N >= 65536) return run_skinny<FMT, 2, 2, 3>(a, st, info);
-      return run_skinny<FMT, 4, 2, 3>(a, st, info);
+      // the work-group's scale/zero pairs grow with its rows (16 * NR * 8 / KS): take the widest
+      // variant whose LDS still fits (the caller checked the 16-row one)
+      auto fits = [&](int nr, int ks) { return skinny_lds(FMT, M, K, nr, ks).total <= kSkinnyLdsMax; };
+      if (N >= 65536 && fits(2, 2)) return run_skinny<FMT, 2, 2, 3>(a, st, info);
+      if (fits(4, 2)) return run_skinny<FMT, 4, 2, 3>(a, st, info);
+      if (fits(2, 2)) return run_skinny<FMT, 2, 2, 3>(a, st, info);
+      if (fits(1, 2)) return run_skinny<FMT, 1, 2, 3>(a, st, info);
+      return run_skinny<FMT, 1, 8, 2>(a, st, info);
     }
-    (void)N; (void)K;
     return dispatch_skinny<FMT>(a, st, info);
   }
 }

@@ -38,6 +38,8 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
     const int nu = us[i + 1] - us[i];
     const int bpu = us[n + 1 + i];
     assert(nu >= 1 && bpu >= 1);
+    // the attention kernel stages one unit's block ids in LDS, at most 1024 of them
+    assert(bpu <= 1024);
     // the units cover the blocks: the last one is non-empty and none runs past the end
     assert((int64_t)bpu * nu >= nblk && (int64_t)bpu * (nu - 1) < nblk);
     // an item that fits one unit is not split; a split item has at most ceil(nblk / 8) units (the

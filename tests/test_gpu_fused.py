@@ -239,3 +239,24 @@ def test_fused_norm_qkv_rope_kv_append(ops, fmt, M, path):
         tv[:, :, o] = True
         touched[b, layer, 1] = tv.reshape(hkv, 16, hd)
     assert np.all(P[~touched] == sentinel)
+
+
+@pytest.mark.parametrize("M", [9, 12])
+def test_w4_streaming_at_the_32b_width(ops, M):
+    """K = 5120 (the 32B / 14B models' width) at 9..16 rows: the widest W4 streaming variant's
+    scale/zero pairs no longer fit beside x' in LDS, and the dispatch takes a narrower one
+    instead of refusing the launch."""
+    from speculative_decoding_rl_amd import _lib
+    g = torch.Generator().manual_seed(500 + M)
+    N, K = 1000, 5120
+    h, gain, xrow, ssq, xs = _norm_input(M, K, g, rows=M + 3)
+    (f, w, sc, zr), wd = _weights("w4", N, K, g, ops)
+    y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+    ops.linear_fused(_lib.EPI_F32, dev(h), M, f, w, N, K, y, sc, zr, xnorm=True, xrow=dev(xrow),
+                     ssq_in=dev(ssq.view(np.int64)), gnorm=gain.cuda())
+    torch.cuda.synchronize()
+    got = y.cpu().numpy().astype(np.float64)
+    ref = xs @ wd.T
+    bound = _bound(xs, wd)
+    assert np.all(np.isfinite(got))
+    assert np.all(np.abs(got - ref) <= BF * bound + 1e-6), np.max(np.abs(got - ref) / bound)
