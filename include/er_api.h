@@ -299,7 +299,9 @@ int er_kv_free_blocks(er_ctx *ctx, int64_t *free_blocks, int64_t *total_blocks);
  * with HIP events on the context's stream; totals are kept per kernel name
  * (the name the profiler shows, e.g. "er::k_linear_mfma<3, 16, 2>") with the
  * algorithmic bytes (weights incl. scales/zeros + activations in + results
- * out; attention: K/V of every key read + q + out) and flops of each launch. */
+ * out; attention: K/V of every key read + q + out, a shared prompt block that
+ * several members of a group read in one launch counted once) and flops of
+ * each launch (every member's keys). */
 typedef struct er_kernel_stat {
   char name[64];
   int64_t launches;

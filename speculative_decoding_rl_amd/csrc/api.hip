@@ -376,7 +376,9 @@ struct Fwd {
   const int32_t* unit_start = nullptr;   // attention work units (see push_units); null = uniform splits
   const int32_t* unit_rec = nullptr;     // per-unit records (see push_units), with unit_start
   int n_units = 0, n_split = 0, max_units = 0;
-  double kv_keys = 0;                    // sum over items of keys read (for per-kernel byte counts)
+  double kv_keys = 0;                    // sum over items of keys read (for per-kernel flop counts)
+  double kv_shared = 0;                  // of those, keys of shared prompt blocks read again by other
+                                         // members of a group in the same forward (bytes count them once)
   const int32_t* logit_rows = nullptr;  // rows whose logits are computed (with n_logit > 0)
   int n_logit = -1;                      // -1: every row; 0: none (prefill chunk with no last token)
   float* logits = nullptr;
@@ -560,7 +562,7 @@ int forward_decode(er_ctx* c, const Fwd& f) {
     // algorithmic bytes: every layer's weights (with scales / zeros), the K/V
     // read and written, the embedding rows; flops of the projections and attention
     const double kvb = 2.0 * hkv * hd * c->act_bytes;
-    const double by = layers_weight_bytes(c, f.draft) + (f.kv_keys + f.M) * kvb * m.n_layers +
+    const double by = layers_weight_bytes(c, f.draft) + (f.kv_keys - f.kv_shared + f.M) * kvb * m.n_layers +
                       (double)f.M * m.d_model * c->act_bytes;
     const double P = c->cost.p_lin() - (double)m.vocab * m.d_model;
     char nm[64];
@@ -638,7 +640,7 @@ int forward(er_ctx* c, const Fwd& f) {
       KC(c, launch_attention(a, c->st, 1, &combined));
       if (e >= 0) {
         const double kvb = 2.0 * hkv * hd * c->act_bytes;  // K and V of one position, one layer
-        const double by = f.kv_keys * kvb + 2.0 * f.M * hq * hd * c->act_bytes;
+        const double by = (f.kv_keys - f.kv_shared) * kvb + 2.0 * f.M * hq * hd * c->act_bytes;
         const char* nm = !c->bf16 ? "er::k_attn_valu" : (hd == 128 ? "er::k_attn_mfma<128, 4>" : "er::k_attn_mfma<64, 4>");
         static_assert(kAttnWaves == 4, "kernel-profile names carry the wave count");
         kp_end(c, e, nm, by, 4.0 * f.kv_keys * f.max_q * (double)hq * hd);
@@ -846,6 +848,23 @@ int dec_check(er_ctx* c) {
   return fail(c, ER_EDEVICE, "persistent decode forward: a grid-barrier wait timed out (path switched off)");
 }
 
+// Keys of shared prompt blocks that more than one of the n sequences read: a
+// group shares its prompt's full blocks, so every member after the first one
+// in the batch reads floor(prompt_len / 16) * 16 keys another member reads too.
+double shared_keys(const er_ctx* c, int n, const int32_t* ids) {
+  double dup = 0;
+  std::vector<int32_t> seen;
+  for (int i = 0; i < n; ++i) {
+    const Seq& s = c->seqs[ids[i]];
+    if (s.group < 0) continue;
+    if (std::find(seen.begin(), seen.end(), s.group) != seen.end())
+      dup += (double)(s.prompt_len / KV_BLOCK) * KV_BLOCK;
+    else
+      seen.push_back(s.group);
+  }
+  return dup;
+}
+
 int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_stride, int32_t* n_emitted,
           er_step_info* info) {
   const bool timed = timed_step(c);
@@ -924,6 +943,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.n_split = n_split;
     f.max_units = max_units;
     f.kv_keys = kv_keys;
+    f.kv_shared = shared_keys(c, n, ids);
     f.logits = c->logits_p;
     f.ldl = c->md.vocab;
     int r = forward(c, f);
@@ -1096,6 +1116,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.n_split = s_dus[j];
       f.max_units = m_dus[j];
       f.kv_keys = kv_sum + (double)n * (j + 1);
+      f.kv_shared = shared_keys(c, n, ids);
       f.logits = c->logits_q + (size_t)j * n * V;
       f.ldl = V;
       int r = forward(c, f);
@@ -1130,6 +1151,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.n_split = s_vus;
     f.max_units = m_vus;
     f.kv_keys = kv_sum + (double)n * G1;
+    f.kv_shared = shared_keys(c, n, ids);
     f.logits = c->logits_p;
     f.ldl = V;
     int r = forward(c, f);
