@@ -197,6 +197,20 @@ int er_update_weights(er_ctx *ctx, const er_weights *w);
 int er_kv_alloc(er_ctx *ctx, int n, const int32_t *prompt_lens, const int32_t *max_new,
                 const int32_t *share_group, int32_t *seq_ids_out);
 
+/* Fork a running sequence into n children that continue from its state (the
+ * SRT review, section "三、技术架构": rollouts of one prompt form a tree whose
+ * nodes share the KV of their common prefix, with copy-on-write at the fork
+ * point).  Each child shares the parent's full committed KV blocks
+ * (reference-counted; committed positions are never rewritten) and gets a
+ * private copy of the parent's partial last block; it inherits the pending
+ * token, the position and the generated count, and gets a new sequence id,
+ * which is also its Philox sequence word, so its draws are its own.
+ * max_new[i] is child i's total generated-token cap (it must exceed the
+ * parent's generated count).  The parent must be prefilled and not finished.
+ * ER_ENOMEM if max_seqs would be exceeded or no block is free for a copy; on
+ * any error nothing changes.  Writes child_ids_out[n]. */
+int er_kv_fork(er_ctx *ctx, int32_t parent, int n, const int32_t *max_new, int32_t *child_ids_out);
+
 /* Run the target over each sequence's prompt (tokens of sequence i are
  * tokens[offsets[i] .. offsets[i+1])) and draw its first generated token as
  * an autoregressive sample at position prompt_len.  first_tok_out[n]. */

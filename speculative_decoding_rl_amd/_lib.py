@@ -131,6 +131,7 @@ SIGNATURES = {
     "er_rollout": (C.c_int, [P, C.c_int, I32P, C.c_int32, I32P, I32P, C.POINTER(Stats)]),
     "er_set_gamma": (C.c_int, [P, C.c_int]),
     "er_set_policy": (C.c_int, [P, C.c_int]),
+    "er_kv_fork": (C.c_int, [P, C.c_int32, C.c_int, P, P]),
     "er_kv_free": (C.c_int, [P, C.c_int, I32P]),
     "er_seq_info": (C.c_int, [P, C.c_int32, I32P, I32P, I32P]),
     "er_get_stats": (C.c_int, [P, C.POINTER(Stats)]),

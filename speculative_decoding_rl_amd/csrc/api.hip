@@ -45,6 +45,11 @@ struct Seq {
   int32_t group = -1;
   bool leader = true;   // computes the shared prompt for its group
   int32_t leader_id = -1;
+  // sequences whose leading KV blocks are the same physical blocks (a share
+  // group, or a sequence and its forks): family id (-1 = none) and how many
+  // leading positions this sequence shares with the family
+  int32_t family = -1;
+  int32_t shared_len = 0;
   BlockTable bt;
 };
 
@@ -848,19 +853,20 @@ int dec_check(er_ctx* c) {
   return fail(c, ER_EDEVICE, "persistent decode forward: a grid-barrier wait timed out (path switched off)");
 }
 
-// Keys of shared prompt blocks that more than one of the n sequences read: a
-// group shares its prompt's full blocks, so every member after the first one
-// in the batch reads floor(prompt_len / 16) * 16 keys another member reads too.
+// Keys of shared blocks that more than one of the n sequences read: a family
+// (share group, or a sequence and its forks) shares its leading full blocks,
+// so every member after the first one in the batch reads
+// floor(shared_len / 16) * 16 keys another member reads too.
 double shared_keys(const er_ctx* c, int n, const int32_t* ids) {
   double dup = 0;
   std::vector<int32_t> seen;
   for (int i = 0; i < n; ++i) {
     const Seq& s = c->seqs[ids[i]];
-    if (s.group < 0) continue;
-    if (std::find(seen.begin(), seen.end(), s.group) != seen.end())
-      dup += (double)(s.prompt_len / KV_BLOCK) * KV_BLOCK;
+    if (s.family == -1) continue;
+    if (std::find(seen.begin(), seen.end(), s.family) != seen.end())
+      dup += (double)(s.shared_len / KV_BLOCK) * KV_BLOCK;
     else
-      seen.push_back(s.group);
+      seen.push_back(s.family);
   }
   return dup;
 }
@@ -1684,6 +1690,8 @@ int er_kv_alloc(er_ctx* c, int n, const int32_t* prompt_lens, const int32_t* max
       s.prompt_len = prompt_lens[i];
       s.max_new = max_new[i];
       s.group = share_group ? share_group[i] : -1;
+      s.family = s.group >= 0 ? s.group : -1;
+      s.shared_len = s.group >= 0 ? s.prompt_len : 0;
       s.leader = true;
       s.leader_id = (int32_t)(base + i);
       if (s.group >= 0) {
@@ -1722,6 +1730,70 @@ int er_kv_alloc(er_ctx* c, int n, const int32_t* prompt_lens, const int32_t* max
     for (int i = 0; i < n; ++i) {
       c->seqs.push_back(std::move(add[(size_t)i]));
       seq_ids_out[i] = (int32_t)(base + i);
+    }
+    c->alive += n;
+    return ER_OK;
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_kv_fork(er_ctx* c, int32_t parent, int n, const int32_t* max_new, int32_t* child_ids_out) {
+  if (!c) return ER_EINVAL;
+  try {
+    if (n <= 0 || !max_new || !child_ids_out) return fail(c, ER_EINVAL, "bad arguments");
+    if (parent < 0 || parent >= (int32_t)c->seqs.size() || !c->seqs[parent].alive)
+      return fail(c, ER_EINVAL, "unknown sequence %d", parent);
+    if (!c->seqs[parent].prefilled || c->seqs[parent].finished)
+      return fail(c, ER_ESTATE, "sequence %d must be prefilled and not finished to fork", parent);
+    if (c->alive + n > c->rd.max_seqs) return fail(c, ER_ENOMEM, "max_seqs %d exceeded", c->rd.max_seqs);
+    const Seq P = c->seqs[parent];
+    for (int i = 0; i < n; ++i) {
+      if (max_new[i] <= P.generated) return fail(c, ER_EINVAL, "max_new must exceed the %d tokens already generated", P.generated);
+      if ((int64_t)P.prompt_len + max_new[i] + c->rd.gamma_max + 1 > c->rd.max_ctx)
+        return fail(c, ER_EINVAL, "fork of %d + %d tokens exceeds max_ctx %d", P.prompt_len, max_new[i], c->rd.max_ctx);
+    }
+    // the parent's committed positions [0, n): full blocks shared, the partial one copied
+    const int full = P.n / KV_BLOCK;
+    const bool partial = P.n % KV_BLOCK != 0;
+    if (partial && c->pool.free_count() < n) return fail(c, ER_ENOMEM, "KV pool exhausted while forking");
+    const int32_t fam = P.family != -1 ? P.family : -2 - parent;
+    // the children's copies of the partial block first, so that a failed copy changes nothing
+    std::vector<int32_t> tail;
+    if (partial) {
+      for (int i = 0; i < n; ++i) tail.push_back(c->pool.alloc());  // available: checked above
+      for (int i = 0; i < n; ++i) {
+        const hipError_t e = hipMemcpyAsync((char*)c->kv_pool + (size_t)tail[(size_t)i] * c->block_bytes,
+                                            (char*)c->kv_pool + (size_t)P.bt.blocks[(size_t)full] * c->block_bytes,
+                                            c->block_bytes, hipMemcpyDeviceToDevice, c->st);
+        if (e != hipSuccess) {
+          for (int32_t b : tail) c->pool.decref(b);
+          return fail(c, ER_EDEVICE, "copy of the partial block: %s", hipGetErrorString(e));
+        }
+      }
+    }
+    const size_t base = c->seqs.size();
+    for (int i = 0; i < n; ++i) {
+      Seq s = P;
+      s.bt.blocks.clear();
+      for (int b = 0; b < full; ++b) {
+        s.bt.blocks.push_back(P.bt.blocks[(size_t)b]);
+        c->pool.incref(P.bt.blocks[(size_t)b]);
+      }
+      if (partial) s.bt.blocks.push_back(tail[(size_t)i]);
+      s.max_new = max_new[i];
+      s.group = -1;
+      s.leader = true;
+      s.leader_id = (int32_t)(base + i);
+      s.family = fam;
+      s.shared_len = full * KV_BLOCK;
+      c->seqs.push_back(std::move(s));
+      child_ids_out[i] = (int32_t)(base + i);
+    }
+    Seq& Pm = c->seqs[parent];
+    if (Pm.family == -1) {
+      Pm.family = fam;
+      Pm.shared_len = full * KV_BLOCK;
     }
     c->alive += n;
     return ER_OK;

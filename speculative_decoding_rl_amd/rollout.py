@@ -110,6 +110,13 @@ class Engine:
         check(self.lib.er_kv_alloc(self.ctx, n, _p32(pl), _p32(mn), sg, _p32(ids)), self.ctx, "er_kv_alloc")
         return ids
 
+    def kv_fork(self, parent: int, max_new) -> np.ndarray:
+        """Children of a running sequence sharing its committed KV (copy-on-write at the last block)."""
+        mn = _i32(max_new)
+        out = np.zeros(len(mn), dtype=np.int32)
+        check(self.lib.er_kv_fork(self.ctx, int(parent), len(mn), _p32(mn), _p32(out)), self.ctx, "er_kv_fork")
+        return out
+
     def prefill(self, ids, prompts) -> np.ndarray:
         ids = _i32(ids)
         toks = _i32(np.concatenate([np.asarray(p, dtype=np.int32).ravel() for p in prompts]))
