@@ -73,9 +73,14 @@ extern "C" {
 #define ER_POLICY_TIMING    3   /* measured-timing guard (er_guard_* below) chooses
                                    between AR and speculation per batch bucket;
                                    gamma as under ER_POLICY_AUTO when it speculates */
+#define ER_POLICY_HISTORY   4   /* drafts copied from earlier rollouts (er_set_history):
+                                   a history step while the attached cache holds a
+                                   record and the batch is at most its max_batch,
+                                   else AR */
 
 #define ER_MODE_AR 0
 #define ER_MODE_SD 1
+#define ER_MODE_HISTORY 3  /* a step with drafts copied from earlier rollouts */
 
 typedef struct er_ctx er_ctx;
 
@@ -164,6 +169,8 @@ typedef struct er_stats {
   int32_t gamma;              /* current choice: 0 = AR */
   int32_t mode;
   double ms_draft, ms_verify, ms_sample, ms_ar, ms_prefill;   /* accumulated, timed steps only */
+  int64_t history_steps;      /* steps with drafts copied from earlier rollouts */
+  int64_t history_drafted, history_accepted;
 } er_stats;
 
 /* Create a context.  Carves dev_arena (device memory the caller owns, e.g. a
@@ -304,6 +311,49 @@ int er_set_decode_spin_limit(er_ctx *ctx, int64_t polls);
  * was traced. */
 int er_set_decode_trace(er_ctx *ctx, int on);
 int er_get_decode_trace(er_ctx *ctx, double *work_us, double *release_us, int max, int *n_out);
+
+/* ---- model-free history drafter --------------------------------------------
+ * History Tree Dynamic RL page, section 1 (drafts taken from the responses of
+ * earlier rollouts, high-reward pieces first, for later rollouts of the same
+ * prompt) and section 3.3 (a fixed-prefix history cache per prompt plus a
+ * global fallback; candidates at a fixed prefix length; reward-first
+ * updates); section 2.2 (4 draft tokens, at most 64 requests by default).
+ * The cache is a host object independent of any context.  A record is one
+ * earlier rollout (prompt, response, reward); position i of its response is
+ * keyed by the prefix_len tokens before it in prompt + response and offers the
+ * record's tokens from i on.  Each prompt has its own map and one global map
+ * holds every prompt's keys; a key keeps the candidate of the highest reward,
+ * among equal rewards the one recorded last.  A sequence's draft: the key of
+ * its last prefix_len tokens (prompt + generated) in its prompt's map, else in
+ * the global map, and the first gamma tokens of that candidate. */
+typedef struct er_history er_history;
+/* prefix_len >= 1, else ER_EINVAL. */
+int er_history_create(int prefix_len, er_history **out);
+int er_history_destroy(er_history *h);
+/* Record one rollout (tokens copied).  ER_EINVAL for negative lengths, null
+ * arrays with positive lengths, or a NaN reward. */
+int er_history_add(er_history *h, int prompt_len, const int32_t *prompt, int resp_len, const int32_t *resp,
+                   float reward);
+/* The draft for a sequence with this prompt and these tokens so far (ctx =
+ * prompt + generated): up to gamma tokens into out, their count into *n_out
+ * (0 when the cache has no candidate).  Pure host computation. */
+int er_history_propose(const er_history *h, int prompt_len, const int32_t *prompt, int ctx_len,
+                       const int32_t *ctx, int gamma, int32_t *out, int32_t *n_out);
+int er_history_records(const er_history *h, int64_t *n);
+/* Attach a cache to a context (borrowed: it must outlive its use; NULL
+ * detaches): history steps draft gamma (1..gamma_max) tokens per sequence,
+ * and ER_POLICY_HISTORY takes them for batches of at most max_batch. */
+int er_set_history(er_ctx *ctx, er_history *h, int gamma, int max_batch);
+/* One step with drafts from the attached cache: each sequence's gamma drafts
+ * (where the cache offers fewer, the rest are the sequence's pending token;
+ * any fixed token is a valid proposal), one target forward over the gamma + 1
+ * positions, and the lossless decision with the point mass on each draft as
+ * the proposal: draft i is accepted with probability p_i(draft), a rejection
+ * is redrawn from p_i without the draft, and full acceptance adds a bonus
+ * token.  Outputs as er_spec_step; info->mode = ER_MODE_HISTORY.  ER_ESTATE
+ * without an attached cache. */
+int er_history_step(er_ctx *ctx, int n, const int32_t *seq_ids, int32_t *tokens_out, int32_t *n_emitted_out,
+                    er_step_info *info);
 
 /* Free KV blocks in the pool. */
 int er_kv_free_blocks(er_ctx *ctx, int64_t *free_blocks, int64_t *total_blocks);

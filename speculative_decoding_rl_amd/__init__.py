@@ -8,4 +8,4 @@ a roofline controller toggles speculation and adapts gamma.  This package is
 its Python binding (argument marshalling only).
 """
 from ._lib import load, lib_path, ErError  # noqa: F401
-from .rollout import Engine, controller_choose  # noqa: F401
+from .rollout import Engine, History, controller_choose  # noqa: F401

@@ -15,9 +15,9 @@ LIB_PATH = os.path.join(HERE, "libsdrl.so")
 ER_OK, ER_EINVAL, ER_ENOMEM, ER_EDEVICE, ER_ESTATE = 0, -1, -2, -3, -4
 ER_F32, ER_BF16 = 0, 1
 ER_W8_PERCH_SYM, ER_W4_G128_ASYM = 0, 1
-ER_POLICY_AUTO, ER_POLICY_FORCE_SD, ER_POLICY_FORCE_AR, ER_POLICY_TIMING = 0, 1, 2, 3
+ER_POLICY_AUTO, ER_POLICY_FORCE_SD, ER_POLICY_FORCE_AR, ER_POLICY_TIMING, ER_POLICY_HISTORY = 0, 1, 2, 3, 4
 ER_KPROF_OFF, ER_KPROF_ALL, ER_KPROF_ATTENTION = 0, 1, 2
-ER_MODE_AR, ER_MODE_SD = 0, 1
+ER_MODE_AR, ER_MODE_SD, ER_MODE_HISTORY = 0, 1, 3
 ER_FMT_F32, ER_FMT_BF16, ER_FMT_W8, ER_FMT_W4 = 0, 1, 2, 3
 PURPOSE_DRAFT, PURPOSE_ACCEPT, PURPOSE_RESIDUAL, PURPOSE_AR = 0, 1, 2, 3
 
@@ -64,7 +64,8 @@ class Stats(C.Structure):
                 ("emitted", C.c_int64), ("bonus", C.c_int64), ("tokens_kept", C.c_int64),
                 ("alpha_ema", C.c_double), ("gamma", C.c_int32), ("mode", C.c_int32),
                 ("ms_draft", C.c_double), ("ms_verify", C.c_double), ("ms_sample", C.c_double),
-                ("ms_ar", C.c_double), ("ms_prefill", C.c_double)]
+                ("ms_ar", C.c_double), ("ms_prefill", C.c_double),
+                ("history_steps", C.c_int64), ("history_drafted", C.c_int64), ("history_accepted", C.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -131,7 +132,14 @@ SIGNATURES = {
     "er_rollout": (C.c_int, [P, C.c_int, I32P, C.c_int32, I32P, I32P, C.POINTER(Stats)]),
     "er_set_gamma": (C.c_int, [P, C.c_int]),
     "er_set_policy": (C.c_int, [P, C.c_int]),
-    "er_kv_fork": (C.c_int, [P, C.c_int32, C.c_int, P, P]),
+    "er_history_create": (C.c_int, [C.c_int, C.POINTER(P)]),
+    "er_history_destroy": (C.c_int, [P]),
+    "er_history_add": (C.c_int, [P, C.c_int, I32P, C.c_int, I32P, C.c_float]),
+    "er_history_propose": (C.c_int, [P, C.c_int, I32P, C.c_int, I32P, C.c_int, I32P, I32P]),
+    "er_history_records": (C.c_int, [P, C.POINTER(C.c_int64)]),
+    "er_set_history": (C.c_int, [P, P, C.c_int, C.c_int]),
+    "er_history_step": (C.c_int, [P, C.c_int, I32P, I32P, I32P, C.POINTER(StepInfo)]),
+    "er_kv_fork": (C.c_int, [P, C.c_int32, C.c_int, I32P, I32P]),
     "er_kv_free": (C.c_int, [P, C.c_int, I32P]),
     "er_seq_info": (C.c_int, [P, C.c_int32, I32P, I32P, I32P]),
     "er_get_stats": (C.c_int, [P, C.POINTER(Stats)]),

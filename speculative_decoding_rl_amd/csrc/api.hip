@@ -26,6 +26,7 @@
 #include "../../include/er_api.h"
 #include "controller.h"
 #include "kernels.h"
+#include "history.h"
 #include "kvpool.h"
 #include "work_units.h"
 
@@ -50,6 +51,7 @@ struct Seq {
   // leading positions this sequence shares with the family
   int32_t family = -1;
   int32_t shared_len = 0;
+  std::vector<int32_t> toks;  // prompt + generated tokens (the last one is the pending token)
   BlockTable bt;
 };
 
@@ -58,6 +60,11 @@ struct Seq {
 constexpr int kSsqSlots = 16;
 
 }  // namespace
+
+struct er_history {
+  er::HistoryCache cache;
+  explicit er_history(int prefix_len) : cache(prefix_len) {}
+};
 
 struct er_ctx {
   er_model_desc md{};
@@ -139,6 +146,8 @@ struct er_ctx {
 
   // per-kernel timing (events around each linear / attention launch)
   int kprof = 0;  // launches bracketed: KPROF_LINEAR | KPROF_ATTENTION bits
+  er_history* hist = nullptr;  // borrowed: drafts copied from earlier rollouts (er_set_history)
+  int hist_gamma = 4, hist_max_batch = 64;
   std::vector<hipEvent_t> kev;
   size_t kev_used = 0;
   struct KRec { std::string name; double bytes, flops; int e0, e1; };
@@ -360,7 +369,7 @@ int validate(const er_model_desc* m, const er_draft_desc* dd, const er_rollout_d
   if (r->max_ctx <= 0 || r->prefill_chunk <= 0) return bad("bad max_ctx / prefill_chunk");
   if (!(r->temperature >= 0.f)) return bad("temperature must be >= 0");
   if (!(r->top_p > 0.f)) return bad("top_p must be > 0");
-  if (r->policy < ER_POLICY_AUTO || r->policy > ER_POLICY_TIMING) return bad("unknown policy");
+  if (r->policy < ER_POLICY_AUTO || r->policy > ER_POLICY_HISTORY) return bad("unknown policy");
   const int grp = m->n_q_heads / m->n_kv_heads;
   if (grp * (r->gamma_max + 1) > 64) return bad("(n_q_heads/n_kv_heads) * (gamma_max+1) must be <= 64");
   return ER_OK;
@@ -977,6 +986,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     s.n += 1;
     s.pending = t;
     s.generated += 1;
+    s.toks.push_back(t);
     tokens_out[(size_t)i * out_stride] = t;
     if (n_emitted) n_emitted[i] = 1;
     ++kept_tot;
@@ -1011,8 +1021,11 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
   return ER_OK;
 }
 
+// One speculative step.  hdraft (host, [n][g]) null: the self-drafter proposes g
+// tokens per sequence; else those tokens are the drafts (copied from earlier
+// rollouts, not sampled) and their proposal is the point mass on each.
 int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, int out_stride, int32_t* n_emitted,
-            er_step_info* info) {
+            er_step_info* info, const int32_t* hdraft = nullptr) {
   const bool timed = timed_step(c);
   const int G1 = g + 1;
   const int V = c->md.vocab;
@@ -1062,7 +1075,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     h_ids[b] = ids[b];
     h_pos0[b] = s.n;
     h_tok[(size_t)b * G1] = s.pending;
-    for (int i = 1; i < G1; ++i) h_tok[(size_t)b * G1 + i] = 0;
+    for (int i = 1; i < G1; ++i) h_tok[(size_t)b * G1 + i] = hdraft ? hdraft[(size_t)b * g + i - 1] : 0;
     for (int j = 0; j < g; ++j) {
       h_dp[j][b] = s.n + j;
       h_ds[j][b] = slot_of(s, s.n + j);
@@ -1098,7 +1111,13 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     if (int r_ = meta_upload(c)) return r_;
     if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
     int32_t* d_tok = M.dev<int32_t>(o_tok);
-    for (int j = 0; j < g; ++j) {
+    if (hdraft) {
+      KC(c, launch_point_mass(c->logits_q, g, n, V, d_tok, G1, c->st));
+      for (int j = 0; j < g; ++j)
+        KC(c, launch_row_stats(c->logits_q + (size_t)j * n * V, n, V, V, c->rd.temperature, c->rd.top_p,
+                               (char*)c->stats_q + (size_t)j * n * stats_row_bytes(c->nch), c->st));
+    }
+    for (int j = 0; j < (hdraft ? 0 : g); ++j) {
       Fwd f;
       f.draft = true;
       f.dec_ok = true;
@@ -1190,6 +1209,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     const int room = s.max_new - s.generated;
     const int kept = std::min(em, room);
     for (int i = 0; i < kept; ++i) tokens_out[(size_t)b * out_stride + i] = out_tok[(size_t)b * G1 + i];
+    s.toks.insert(s.toks.end(), out_tok + (size_t)b * G1, out_tok + (size_t)b * G1 + em);
     if (n_emitted) n_emitted[b] = kept;
     s.generated += kept;
     s.n += a + 1;
@@ -1206,10 +1226,17 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     if (s.generated >= s.max_new) { finish_seq(c, s); ++fin; }
   }
   const double a_step = acc.value();
-  c->alpha_ema = ema(c->alpha_ema, a_step, c->rd.ema_beta);
-  c->stats.sd_steps += 1;
-  c->stats.drafted += (int64_t)n * g;
-  c->stats.accepted += acc_tot;
+  if (hdraft) {
+    // the self-drafter's acceptance EMA tracks the self-drafter only
+    c->stats.history_steps += 1;
+    c->stats.history_drafted += (int64_t)n * g;
+    c->stats.history_accepted += acc_tot;
+  } else {
+    c->alpha_ema = ema(c->alpha_ema, a_step, c->rd.ema_beta);
+    c->stats.sd_steps += 1;
+    c->stats.drafted += (int64_t)n * g;
+    c->stats.accepted += acc_tot;
+  }
   c->stats.emitted += emit_tot;
   c->stats.tokens_kept += kept_tot;
   float md = 0.f, mv = 0.f, ms = 0.f;
@@ -1226,7 +1253,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   c->last_B = n;
   if (info) {
     *info = er_step_info{};
-    info->mode = ER_MODE_SD;
+    info->mode = hdraft ? ER_MODE_HISTORY : ER_MODE_SD;
     info->gamma = g;
     info->batch = n;
     info->accepted = acc_tot;
@@ -1242,6 +1269,26 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   }
   ++c->step_count;
   return ER_OK;
+}
+
+// One step with drafts copied from earlier rollouts: each sequence's g drafts
+// from the history cache (padded with its pending token where the cache has
+// fewer or none: any fixed token is a valid proposal), then the target's
+// verify pass and the lossless decision with point-mass proposals.
+int do_history(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_stride, int32_t* n_emitted,
+               er_step_info* info) {
+  const int g = c->hist_gamma;
+  const int V = c->md.vocab;
+  std::vector<int32_t> d((size_t)n * g);
+  for (int b = 0; b < n; ++b) {
+    const Seq& s = c->seqs[ids[b]];
+    int32_t* db = d.data() + (size_t)b * g;
+    int k = c->hist->cache.propose(s.toks.data(), s.prompt_len, s.toks.data(), (int)s.toks.size(), g, db);
+    for (int i = 0; i < k; ++i)
+      if (db[i] < 0 || db[i] >= V) { k = i; break; }
+    for (int i = k; i < g; ++i) db[i] = s.pending;
+  }
+  return do_spec(c, n, ids, g, tokens_out, out_stride, n_emitted, info, d.data());
 }
 
 // Controller choice for this batch (0 = AR).
@@ -1980,6 +2027,8 @@ int er_prefill(er_ctx* c, int n, const int32_t* ids, const int32_t* tokens, cons
       s.n = s.prompt_len;
       s.pending = c->out_h[i];
       s.generated = 1;
+      s.toks.assign(tokens + offsets[i], tokens + offsets[i + 1]);
+      s.toks.push_back(s.pending);
       first_tok_out[i] = c->out_h[i];
       c->stats.tokens_kept += 1;
       if (s.generated >= s.max_new) finish_seq(c, s);
@@ -2022,8 +2071,14 @@ int er_step(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int32_t* 
     if (r) return r;
     if (!tokens_out || !n_emitted_out) return fail(c, ER_EINVAL, "null output");
     const auto t0 = std::chrono::steady_clock::now();
-    const int g = plan(c, n, ids);
     const int stride = c->rd.gamma_max + 1;
+    if (c->policy == ER_POLICY_HISTORY) {
+      // history drafts once the cache holds a record and the batch is small enough, else AR
+      const bool hist = c->hist && c->hist->cache.records() >= 1 && n <= c->hist_max_batch;
+      return hist ? do_history(c, n, ids, tokens_out, stride, n_emitted_out, info)
+                  : do_ar(c, n, ids, tokens_out, stride, n_emitted_out, info);
+    }
+    const int g = plan(c, n, ids);
     r = g == 0 ? do_ar(c, n, ids, tokens_out, stride, n_emitted_out, info)
                : do_spec(c, n, ids, g, tokens_out, stride, n_emitted_out, info);
     if (r == ER_OK && c->policy == ER_POLICY_TIMING) {
@@ -2091,7 +2146,7 @@ int er_set_gamma(er_ctx* c, int gamma) {
 
 int er_set_policy(er_ctx* c, int policy) {
   if (!c) return ER_EINVAL;
-  if (policy < ER_POLICY_AUTO || policy > ER_POLICY_TIMING) return fail(c, ER_EINVAL, "unknown policy %d", policy);
+  if (policy < ER_POLICY_AUTO || policy > ER_POLICY_HISTORY) return fail(c, ER_EINVAL, "unknown policy %d", policy);
   if (policy == ER_POLICY_TIMING && c->policy != ER_POLICY_TIMING) {
     er_guard_params gp = c->guard.p;
     if (er_guard_init(&c->guard, &gp) != ER_OK) {
@@ -2236,6 +2291,73 @@ int er_set_fused(er_ctx* c, int on) {
   if (!c) return ER_EINVAL;
   c->fuse = c->bf16 && on != 0;
   return ER_OK;
+}
+
+int er_history_create(int prefix_len, er_history** out) {
+  if (!out || prefix_len < 1) return ER_EINVAL;
+  try {
+    *out = new er_history(prefix_len);
+    return ER_OK;
+  } catch (...) {
+    return ER_ENOMEM;
+  }
+}
+
+int er_history_destroy(er_history* h) {
+  delete h;
+  return ER_OK;
+}
+
+int er_history_add(er_history* h, int prompt_len, const int32_t* prompt, int resp_len, const int32_t* resp,
+                   float reward) {
+  if (!h || prompt_len < 0 || resp_len < 0 || (prompt_len > 0 && !prompt) || (resp_len > 0 && !resp) ||
+      !(reward == reward))
+    return ER_EINVAL;
+  try {
+    h->cache.add(prompt, prompt_len, resp, resp_len, reward);
+    return ER_OK;
+  } catch (...) {
+    return ER_ENOMEM;
+  }
+}
+
+int er_history_propose(const er_history* h, int prompt_len, const int32_t* prompt, int ctx_len, const int32_t* ctx,
+                       int gamma, int32_t* out, int32_t* n_out) {
+  if (!h || !n_out || prompt_len < 0 || ctx_len < 0 || gamma < 0 || (prompt_len > 0 && !prompt) ||
+      (ctx_len > 0 && !ctx) || (gamma > 0 && !out))
+    return ER_EINVAL;
+  *n_out = h->cache.propose(prompt, prompt_len, ctx, ctx_len, gamma, out);
+  return ER_OK;
+}
+
+int er_history_records(const er_history* h, int64_t* n) {
+  if (!h || !n) return ER_EINVAL;
+  *n = h->cache.records();
+  return ER_OK;
+}
+
+int er_set_history(er_ctx* c, er_history* h, int gamma, int max_batch) {
+  if (!c) return ER_EINVAL;
+  if (gamma < 1 || gamma > c->rd.gamma_max || max_batch < 1)
+    return fail(c, ER_EINVAL, "history gamma must be in 1..%d and max_batch >= 1", c->rd.gamma_max);
+  c->hist = h;
+  c->hist_gamma = gamma;
+  c->hist_max_batch = max_batch;
+  return ER_OK;
+}
+
+int er_history_step(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int32_t* n_emitted_out,
+                    er_step_info* info) {
+  if (!c) return ER_EINVAL;
+  try {
+    int r = check_batch(c, n, ids, true);
+    if (r) return r;
+    if (!tokens_out || !n_emitted_out) return fail(c, ER_EINVAL, "null output");
+    if (!c->hist) return fail(c, ER_ESTATE, "no history cache attached (er_set_history)");
+    return do_history(c, n, ids, tokens_out, c->rd.gamma_max + 1, n_emitted_out, info);
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
 }
 
 int er_kv_free_blocks(er_ctx* c, int64_t* free_blocks, int64_t* total_blocks) {

@@ -305,6 +305,28 @@ __global__ __launch_bounds__(SB) void k_topp(const float* __restrict__ logits, i
   if (tid == 0) row_thr_w(stats, r, nch) = RowStats{prefix, s_any};
 }
 
+// Logit rows whose distribution is the point mass on one token (a draft that
+// is not sampled, e.g. copied from an earlier rollout): row j * n + b of a
+// [g][n][V] block gets 0 at tok[b * G1 + j + 1] and -1e30 elsewhere.  exp of
+// -1e30 / T underflows to exactly 0, so the row's softmax, its top-p nucleus
+// and its argmax are the point mass, and the lossless rule accepts the draft
+// with probability p(draft).
+__global__ __launch_bounds__(256) void k_point_mass(float* __restrict__ q, int n, int V, const int32_t* __restrict__ tok,
+                                                    int G1) {
+  const int row = blockIdx.y;
+  const int j = row / n, b = row - j * n;
+  const int d = tok[(long)b * G1 + j + 1];
+  float* r = q + (long)row * V;
+  for (int k = blockIdx.x * blockDim.x + threadIdx.x; k < V; k += gridDim.x * blockDim.x) r[k] = (k == d) ? 0.0f : -1e30f;
+}
+
+int launch_point_mass(float* q, int g, int n, int V, const int32_t* tok, int G1, hipStream_t st) {
+  if (g <= 0 || n <= 0) return 0;
+  if ((long)g * n > 65535) return -1;
+  hipLaunchKernelGGL(k_point_mass, dim3(64, g * n), dim3(256), 0, st, q, n, V, tok, G1);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
+
 int launch_row_stats(const float* logits, int rows, int V, long ld, float T, float top_p, void* stats,
                      hipStream_t st) {
   if (rows <= 0) return 0;

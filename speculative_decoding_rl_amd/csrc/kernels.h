@@ -247,6 +247,8 @@ struct ChunkStat {           // per vocabulary chunk: max logit, its first index
 __host__ __device__ inline int sampler_chunks(int V) { return (V + 2047) / 2048; }
 __host__ __device__ inline long stats_row_bytes(int nch) { return (long)sizeof(RowStats) + (long)nch * sizeof(ChunkStat); }
 
+// Point-mass logit rows for drafts that are not sampled (k_sample.hip).
+int launch_point_mass(float* q, int g, int n, int V, const int32_t* tok, int G1, hipStream_t st);
 int launch_row_stats(const float* logits, int rows, int V, long ld, float T, float top_p, void* stats,
                      hipStream_t st);
 // Draw one token per row r from pi(logits row row_map[r] (or r)) with

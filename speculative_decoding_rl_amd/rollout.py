@@ -127,6 +127,22 @@ class Engine:
               self.ctx, "er_prefill")
         return out
 
+    def set_history(self, hist, gamma: int = 4, max_batch: int = 64):
+        """Attach a History (drafts copied from earlier rollouts); None detaches."""
+        check(self.lib.er_set_history(self.ctx, hist.h if hist is not None else None, gamma, max_batch), self.ctx,
+              "er_set_history")
+        self._hist = hist   # keep the cache alive while attached
+
+    def history_step(self, ids):
+        ids = _i32(ids)
+        n = len(ids)
+        tok = np.zeros((n, self.gamma_max + 1), dtype=np.int32)
+        ne = np.zeros(n, dtype=np.int32)
+        info = _lib.StepInfo()
+        check(self.lib.er_history_step(self.ctx, n, _p32(ids), _p32(tok), _p32(ne), C.byref(info)), self.ctx,
+              "er_history_step")
+        return tok, ne, info
+
     def spec_step(self, ids):
         ids = _i32(ids)
         n = len(ids)
@@ -300,3 +316,42 @@ def controller_plan(cost: dict, state: dict, policy: int, batch: int, mean_ctx: 
                                  gamma_hi, margin, C.byref(g)), None, "er_controller_plan")
     state.update(choice=st.choice, ar_streak=st.ar_streak, probe_every=st.probe_every)
     return g.value
+
+
+class History:
+    """The model-free history drafter's cache (er_history_*): records of earlier rollouts."""
+
+    def __init__(self, prefix_len: int = 2):
+        self.lib = _lib.load()
+        h = C.c_void_p()
+        check(self.lib.er_history_create(prefix_len, C.byref(h)), None, "er_history_create")
+        self.h = h
+
+    def add(self, prompt, response, reward: float = 0.0):
+        p, r = _i32(prompt), _i32(response)
+        check(self.lib.er_history_add(self.h, len(p), _p32(p), len(r), _p32(r), float(reward)), None,
+              "er_history_add")
+
+    def propose(self, prompt, context, gamma: int) -> list:
+        p, c = _i32(prompt), _i32(context)
+        out = np.zeros(max(1, gamma), dtype=np.int32)
+        n = np.zeros(1, dtype=np.int32)
+        check(self.lib.er_history_propose(self.h, len(p), _p32(p), len(c), _p32(c), gamma, _p32(out), _p32(n)), None,
+              "er_history_propose")
+        return [int(t) for t in out[:int(n[0])]]
+
+    def records(self) -> int:
+        n = C.c_int64()
+        check(self.lib.er_history_records(self.h, C.byref(n)), None, "er_history_records")
+        return int(n.value)
+
+    def close(self):
+        if self.h:
+            self.lib.er_history_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
