@@ -59,6 +59,12 @@ def parse():
                     help="timed steps per batch bin and mode (0 = run the rollout to completion)")
     ap.add_argument("--warmup", type=int, default=5, help="untimed steps per batch bin and mode")
     ap.add_argument("--rollout", action="store_true", help="the whole 256 -> 1 rollout instead of the bin sweep")
+    ap.add_argument("--history", action="store_true",
+                    help="the history drafter: an untimed earlier rollout of the prompts fills its cache, then "
+                         "the same prompts are timed under ER_POLICY_HISTORY and AR")
+    ap.add_argument("--history-new", type=int, default=256, help="tokens per sequence in --history")
+    ap.add_argument("--history-gamma", type=int, default=4)
+    ap.add_argument("--history-prefix", type=int, default=4)
     ap.add_argument("--group", type=int, default=0,
                     help="GRPO-style groups: every G sequences of a bin share their prefilled context's KV blocks")
     ap.add_argument("--config", default="", help="model shape (default qwen2.5-7b; qwen2.5-14b with --crossover)")
@@ -693,6 +699,71 @@ def crossover(args, shape, wts):
             "rows": rows}
 
 
+def history_line(args, shape, wts):
+    """Drafts copied from an earlier rollout of the same prompts (the history drafter): the batch's
+    prompts are rolled out once under AR (untimed) and recorded with reward 1; the same prompts are then
+    rolled out again, timed, under ER_POLICY_HISTORY and under AR, each sequence to --history-new
+    tokens.  Under sampling the second rollout differs from the first, and a copied draft is accepted
+    with probability p(draft); at temperature 0 it repeats the first."""
+    import torch
+
+    import synth
+    from speculative_decoding_rl_amd import Engine, History, _lib
+
+    B, P, N, g = args.batch, args.prompt_len, args.history_new, args.history_gamma
+    max_ctx = (P + N + args.gamma_max + 32 + 15) // 16 * 16
+    eng = Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
+                 gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=_lib.ER_POLICY_FORCE_AR,
+                 max_seqs=B + 4, max_batch=B, max_ctx=max_ctx, prefill_chunk=8192,
+                 kv_blocks=B * (max_ctx // 16 + 2) + 64)
+    hist = History(args.history_prefix)
+    eng.set_history(hist, gamma=g, max_batch=max(B, 1))
+    prompts = [list(p) for p in synth.prompts(B, P, shape.vocab, seed=args.seed)]
+
+    def rollout(policy, timed):
+        eng.set_policy(policy)
+        eng.reset_stats()
+        ids = [int(i) for i in eng.kv_alloc([P] * B, [N] * B)]
+        first = eng.prefill(ids, prompts)
+        out = {i: [int(first[k])] for k, i in enumerate(ids)}
+        act = list(ids)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        steps = 0
+        while act:
+            tok, ne, _ = eng.step(act)
+            for k, i in enumerate(act):
+                out[i] += [int(t) for t in tok[k, :ne[k]]]
+            act = [i for i in act if not eng.seq_info(i)[2]]
+            steps += 1
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        st = eng.stats()
+        eng.kv_free(ids)
+        return [out[i] for i in ids], dt, steps, st
+
+    first, _, _, _ = rollout(_lib.ER_POLICY_FORCE_AR, False)
+    for p_, r_ in zip(prompts, first):
+        hist.add(p_, r_, 1.0)
+    toks_h, t_h, steps_h, st_h = rollout(_lib.ER_POLICY_HISTORY, True)
+    toks_a, t_a, steps_a, _ = rollout(_lib.ER_POLICY_FORCE_AR, True)
+    n_tok = sum(len(t) - 1 for t in toks_h)
+    eng.close()
+    hist.close()
+    return {"metric": "history drafter: tokens/s of a second rollout of the same prompts vs AR", "unit": "tokens/s",
+            "value": round(n_tok / t_h, 2), "ar_value": round(sum(len(t) - 1 for t in toks_a) / t_a, 2),
+            "history_over_ar": round((n_tok / t_h) / (sum(len(t) - 1 for t in toks_a) / t_a), 4),
+            "steps": {"history": steps_h, "ar": steps_a},
+            "acceptance": {"history_drafted": st_h["history_drafted"], "history_accepted": st_h["history_accepted"],
+                           "per_draft": round(st_h["history_accepted"] / max(1, st_h["history_drafted"]), 4),
+                           "tokens_per_sequence_step": round(n_tok / max(1, steps_h) / B, 3)},
+            "second_rollout_repeats_first": toks_h == first,
+            "config": {"workload": f"{args.config}-shaped decoder, batch {B}, prompts {P} tokens, {N} tokens per "
+                                   f"sequence, T={args.temperature}, top-p={args.top_p}, history gamma {g}, "
+                                   f"prefix {args.history_prefix}"},
+            "data": "synthetic (random-init weights N(0,0.02), uniform prompts)"}
+
+
 def sweep_line(args, shape, wts, stops):
     """The JSON line of the bin sweep."""
     t0 = time.perf_counter()
@@ -806,6 +877,9 @@ def main():
     log(f"weights {sum(v.numel() for v in wts.values()) / 1e9:.2f} B params on device in {time.perf_counter() - t0:.1f} s")
     if args.crossover:
         print(json.dumps(crossover(args, shape, wts)), flush=True)
+        return
+    if args.history:
+        print(json.dumps(history_line(args, shape, wts)), flush=True)
         return
     prompts = synth.prompts(args.batch, args.prompt_len, shape.vocab, seed=args.seed)
     stops = synth.stop_lengths(args.batch, args.median, args.cap, seed=args.seed)
