@@ -38,8 +38,12 @@ extern "C" {
 int er_op_quantize(int quant, int w_dtype, const void *d_w, int N, int K, void *d_codes, void *d_scale,
                    void *d_zero, void *stream);
 
-/* Canonical W4 nibble order -> the order er_op_linear's ER_FMT_W4 reads
- * (within each 32-bit word covering k..k+7: k+2i at bits 4i, k+2i+1 at bits 16+4i). */
+/* Canonical W4 (row-major [N][K/2] bytes, code k at bits 4k of its word) ->
+ * the layout er_op_linear's ER_FMT_W4 reads: within each 32-bit word covering
+ * k..k+7, k+2i at bits 4i and k+2i+1 at bits 16+4i; the rows in groups of 8,
+ * each group's 64-byte pieces (128 codes of one row) stored chunk after chunk
+ * with the group's rows adjacent within a chunk (the last group may have fewer
+ * rows).  Same size, N * K / 2 bytes; K % 128 == 0 (else ER_EINVAL). */
 int er_op_w4_kernel_order(const void *d_canon, int N, int K, void *d_out, void *stream);
 
 /* y[m, n] = sum_k x[m, k] W[n, k] for m < M, n < N; y fp32 [M, ldy].

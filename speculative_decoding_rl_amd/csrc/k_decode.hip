@@ -352,7 +352,7 @@ __device__ __noinline__ void lin_phase(const DecodeArgs& a, const LinearW& W_, i
 #pragma unroll
       for (int h = 0; h < 2; ++h) wreg[slot][h] = ldg128((const void*)(p + 64 * h));
     } else {
-      wreg[slot][0] = ldg128((const void*)(gptr<uint8_t>(W.w) + (nrow * K + c * 128) / 2 + 16 * kb));
+      wreg[slot][0] = ldg128((const void*)(gptr<uint8_t>(W.w) + w4_piece(nrow, c, W.N, K) + 16 * kb));
       // raw codes: converting here would make the issue wait for its own loads
       scr[slot] = gptr<uint16_t>(W.scale)[nrow * G + c];
       zcr[slot] = gptr<uint8_t>(W.zero)[nrow * G + c];

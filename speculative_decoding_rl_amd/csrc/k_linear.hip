@@ -32,7 +32,7 @@ namespace er {
 // ----------------------------------------------------------------------------
 template <int FMT>
 ER_DEV float w_elem(const void* __restrict__ w, const void* __restrict__ s, const void* __restrict__ z,
-                    long n, long k, long K) {
+                    long n, long k, long K, long N) {
   if constexpr (FMT == FMT_F32) {
     return ((const float*)w)[n * K + k];
   } else if constexpr (FMT == FMT_BF16) {
@@ -40,7 +40,7 @@ ER_DEV float w_elem(const void* __restrict__ w, const void* __restrict__ s, cons
   } else if constexpr (FMT == FMT_W8) {
     return (float)((const int8_t*)w)[n * K + k] * ((const float*)s)[n];
   } else {
-    const uint32_t word = ((const uint32_t*)w)[(n * K + k) >> 3];
+    const uint32_t word = ((const uint32_t*)w)[(w4_piece(n, k >> 7, N, K) + ((k & 127) >> 1)) >> 2];
     const int j = (int)(k & 7);
     const int bit = (j & 1) ? 16 + 4 * (j >> 1) : 4 * (j >> 1);
     const int q = (int)((word >> bit) & 15u);
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256) void k_linear_valu(const void* __restrict__ xv
   for (int k = lane * 4; k < K; k += 256) {
     float wv[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) wv[t] = w_elem<FMT>(w, s, z, n, k + t, K);
+    for (int t = 0; t < 4; ++t) wv[t] = w_elem<FMT>(w, s, z, n, k + t, K, N);
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
       if (m0 + mm < M) {
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(512) void k_linear_mfma(LinArgs a, int mtiles) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) wreg[buf][ni][h] = *(const uint4*)(p + 64 * h + 16 * kb);
       } else {
-        const uint8_t* p = (const uint8_t*)wv + (nrow[ni] * K + (long)c * 128) / 2;
+        const uint8_t* p = (const uint8_t*)wv + w4_piece(nrow[ni], c, N, K);
         wreg[buf][ni][0] = *(const uint4*)(p + 16 * kb);
         wsc[buf][ni] = bf2f(((const uint16_t*)sv)[nrow[ni] * G + c]);
         wz[buf][ni] = 128.0f + (float)((const uint8_t*)zv)[nrow[ni] * G + c];
@@ -773,7 +773,7 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) wreg[slot][ni][h] = *(const uint4*)(p + 64 * h);
       } else {
-        const uint8_t* p = (const uint8_t*)wv + (nrow[ni] * K + c * 128) / 2 + 16 * kb;
+        const uint8_t* p = (const uint8_t*)wv + w4_piece(nrow[ni], c, N, K) + 16 * kb;
         wreg[slot][ni][0] = *(const uint4*)p;
       }
     }

@@ -17,6 +17,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "linear_dev.h"
 
 namespace er {
 
@@ -266,9 +267,11 @@ int launch_quantize_w4(const void* W, int N, int K, uint8_t* packed_canon, uint1
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// Canonical nibble order (k at bits 4k of the word) -> kernel order
-// (k = 2i at bits 4i, k = 2i+1 at bits 16 + 4i).
-__global__ __launch_bounds__(256) void k_w4_order(const uint32_t* __restrict__ in, long nwords,
+// Canonical W4 (row-major bytes, k at bits 4k of each word) -> kernel order:
+// within a word, k = 2i at bits 4i and k = 2i+1 at bits 16 + 4i; the words
+// placed in the kernel layout (w4_piece: rows in groups of 8, a group's
+// 64-byte pieces chunk after chunk).
+__global__ __launch_bounds__(256) void k_w4_order(const uint32_t* __restrict__ in, long nwords, int N, int K,
                                                   uint32_t* __restrict__ out) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= nwords) return;
@@ -279,14 +282,17 @@ __global__ __launch_bounds__(256) void k_w4_order(const uint32_t* __restrict__ i
     r |= ((c >> (8 * j)) & 0xFu) << (4 * j);
     r |= ((c >> (8 * j + 4)) & 0xFu) << (16 + 4 * j);
   }
-  out[i] = r;
+  const long wpr = (long)K >> 3;             // words per row
+  const long n = i / wpr, kw = i - n * wpr;  // kw: word within the row, 16 per 128-code chunk
+  out[(w4_piece(n, kw >> 4, N, K) >> 2) + (kw & 15)] = r;
 }
 
 int launch_w4_to_kernel_order(const uint8_t* canon, int N, int K, uint8_t* out, hipStream_t st) {
   const long nwords = (long)N * K / 8;
   if (nwords <= 0) return 0;
+  if (K % 128 != 0) return -1;
   hipLaunchKernelGGL(k_w4_order, dim3((unsigned)((nwords + 255) / 256)), dim3(256), 0, st, (const uint32_t*)canon,
-                     nwords, (uint32_t*)out);
+                     nwords, N, K, (uint32_t*)out);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 

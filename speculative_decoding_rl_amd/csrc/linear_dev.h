@@ -18,6 +18,19 @@ ER_DEV int kcol(int i, int kb) {
   else return 32 * kb + 8 * i;
 }
 
+// Kernel layout of a W4 matrix [N][K]: rows in groups of 8; within a group,
+// the 64-byte pieces of 128 codes are stored chunk after chunk, the group's
+// rows adjacent within a chunk.  Byte offset of the piece of row n, chunk c
+// (the last group may hold fewer than 8 rows; the matrix stays N * K / 2
+// bytes).  A 16-row tile made of two aligned 8-row groups (consecutive rows,
+// or the paired halves the fused epilogues use) reads two 512-byte runs per
+// chunk instead of 16 pieces one row stride apart.
+ER_DEV long w4_piece(long n, long c, long N, long K) {
+  const long g8 = n & ~7L;
+  const long rows = N - g8 < 8 ? N - g8 : 8;
+  return g8 * (K >> 1) + c * rows * 64 + (n & 7) * 64;
+}
+
 // 8 int8 codes (two words) -> bf16 of (q + 128), exact.
 ER_DEV bf16x8_t w8_to_bf16(uint32_t a, uint32_t b) {
   a ^= 0x80808080u;
