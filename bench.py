@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--no-kernel-profile", action="store_true")
     ap.add_argument("--persistent", action="store_true",
                     help="run forwards of <= 16 rows as the persistent decode kernel (default: kernel sequence)")
+    ap.add_argument("--graphs", type=int, default=16,
+                    help="replay recorded graphs for steps of at most this many sequences (0: every step eager)")
     ap.add_argument("--kprof-every", type=int, default=4,
                     help="bracket the attention launches of every this many steps of the timed rollout with HIP "
                          "events (events on every launch slow each step by ~0.3 ms)")
@@ -99,6 +101,14 @@ def parse():
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only copy this many bytes device-to-device 10 times and exit (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def engine_options(eng, args):
+    """The launch options every bench engine runs with."""
+    if args.persistent:
+        eng.set_persistent(True)
+    if args.graphs:
+        eng.set_graphs(args.graphs)
 
 
 def make_engine(args, shape, wts, policy):
@@ -116,8 +126,7 @@ def make_engine(args, shape, wts, policy):
     eng = Engine(shape, wts, shape.quant, seed=args.seed, temperature=args.temperature, top_p=args.top_p,
                  gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=policy, max_seqs=args.batch + 64,
                  max_batch=args.batch, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
-    if args.persistent:
-        eng.set_persistent(True)
+    engine_options(eng, args)
     return eng
 
 
@@ -520,8 +529,7 @@ def sweep(args, shape, wts, stops):
                  gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=_lib.ER_POLICY_AUTO,
                  max_seqs=max(b["batch"] for b in plan) + 8, max_batch=max(b["batch"] for b in plan),
                  max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
-    if args.persistent:
-        eng.set_persistent(True)
+    engine_options(eng, args)
     if args.gamma:
         eng.set_gamma(args.gamma)
     pol = {"sd": _lib.ER_POLICY_AUTO, "force-sd": _lib.ER_POLICY_FORCE_SD, "ar": _lib.ER_POLICY_FORCE_AR}
@@ -633,8 +641,7 @@ def crossover(args, shape, wts):
                  gamma_init=min(4, max(gammas)), gamma_min=1, gamma_max=max(gammas), policy=_lib.ER_POLICY_FORCE_AR,
                  max_seqs=Bmax,
                  max_batch=Bmax, max_ctx=max_ctx, prefill_chunk=8192, kv_blocks=kv_blocks)
-    if args.persistent:
-        eng.set_persistent(True)
+    engine_options(eng, args)
     prompts = synth.prompts(Bmax, C, shape.vocab, seed=args.seed)
     ids = [int(i) for i in eng.kv_alloc([C] * Bmax, [max_ctx - C - 16] * Bmax)]
     t0 = time.perf_counter()
@@ -716,6 +723,7 @@ def history_line(args, shape, wts):
                  gamma_init=4, gamma_min=1, gamma_max=args.gamma_max, policy=_lib.ER_POLICY_FORCE_AR,
                  max_seqs=B + 4, max_batch=B, max_ctx=max_ctx, prefill_chunk=8192,
                  kv_blocks=B * (max_ctx // 16 + 2) + 64)
+    engine_options(eng, args)
     hist = History(args.history_prefix)
     eng.set_history(hist, gamma=g, max_batch=max(B, 1))
     prompts = [list(p) for p in synth.prompts(B, P, shape.vocab, seed=args.seed)]
@@ -804,7 +812,7 @@ def sweep_line(args, shape, wts, stops):
                                 + (f"; groups of {args.group} sequences share their bin's prefilled context"
                                    if args.group > 1 else "")),
                    "mode": "SD-auto (roofline toggle)", "global_batch": args.batch, "seq_len": args.prompt_len,
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)", "graphs": args.graphs},
         "roofline": rf,
         "ar_value": round(tok_ar / t_ar, 2),
         "sd_over_ar": round((tok_sd / t_sd) / (tok_ar / t_ar), 4),
@@ -942,7 +950,8 @@ def main():
                                 f"{'adaptive 1..%d' % args.gamma_max if not args.gamma else args.gamma}, "
                                 f"{'full rollout 256->1' if args.steps == 0 else f'first {args.steps} steps'}"),
                    "mode": "SD-auto (roofline toggle)" if "sd" in res else modes[0],
-                   "global_batch": args.batch, "seq_len": args.prompt_len, "parallelism": "none (1 GPU)"},
+                   "global_batch": args.batch, "seq_len": args.prompt_len, "parallelism": "none (1 GPU)",
+                   "graphs": args.graphs},
         "roofline": rf,
     }
     if "ar" in res and main_run is not res["ar"]:

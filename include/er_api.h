@@ -312,6 +312,44 @@ int er_set_decode_spin_limit(er_ctx *ctx, int64_t polls);
 int er_set_decode_trace(er_ctx *ctx, int on);
 int er_get_decode_trace(er_ctx *ctx, double *work_us, double *release_us, int max, int *n_out);
 
+/* ---- bucketed graph capture ------------------------------------------------
+ * TLT notes, section 3, Design A, A3: a range of batch sizes shares one set
+ * of recorded graphs, and the drafter's graphs are recorded apart from the
+ * target's.  With max_batch > 0, a step over n <= max_batch sequences runs as
+ * nb sequences, nb = n for n <= 4, else the next power of two >= n, and
+ * replays up to two graphs: AR steps one (target forward and draw);
+ * speculative steps the drafter's (gamma forwards and draws) and the
+ * target's (verify forward and lossless decision); history steps only that
+ * verify graph, shared with the self-drafted steps.  Conditions: gamma + 1 <=
+ * 16, nb <= max_batch of er_rollout_init, nb * (gamma + 1) rows within the
+ * activation buffers, the attention partials within their area; other steps
+ * run eagerly, as do steps with the kernel profile or the persistent forward
+ * on.  A graph is recorded at the first step of its key (kind, nb, gamma,
+ * capacity) and replayed after; capacity = the smallest power-of-two number
+ * of 16-token blocks >= 16 that holds every sequence's context plus this
+ * step's positions, so a key is recorded again only when the longest context
+ * crosses a power of two.  The padding sequences n .. nb-1 decode token 0 at
+ * positions 0 .. gamma of one reserved KV block (taken from the pool while
+ * graphs are on) and are dropped; attention gives every sequence the same
+ * number of work units (units past a sequence's end read nothing).  Tokens,
+ * acceptances and sequence state follow the same kernels and per-row
+ * arithmetic as the eager step; the attention split may differ, which changes
+ * rounding only.  Timed steps time each graph as a whole (the split between
+ * forward and sampling is folded into ms_verify, ms_sample = 0).  At most 64
+ * graphs are kept (least recently replayed evicted); er_update_weights,
+ * er_set_fused and max_batch = 0 drop them (0 also returns the reserved
+ * block).  Default 0 (off).  ER_ENOMEM when no KV block is free for the
+ * padding rows. */
+int er_set_graphs(er_ctx *ctx, int max_batch);
+typedef struct er_graph_stats {
+  int32_t max_batch;  /* er_set_graphs value (0: off) */
+  int32_t cached;     /* graphs held */
+  int64_t captures;   /* graphs recorded */
+  int64_t replays;    /* graph launches */
+  int64_t evictions;  /* graphs dropped to stay within 64 */
+} er_graph_stats;
+int er_get_graph_stats(const er_ctx *ctx, er_graph_stats *out);
+
 /* ---- model-free history drafter --------------------------------------------
  * History Tree Dynamic RL page, section 1 (drafts taken from the responses of
  * earlier rollouts, high-reward pieces first, for later rollouts of the same

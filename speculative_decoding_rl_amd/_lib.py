@@ -71,6 +71,11 @@ class Stats(C.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class GraphStats(C.Structure):
+    _fields_ = [("max_batch", C.c_int32), ("cached", C.c_int32), ("captures", C.c_int64), ("replays", C.c_int64),
+                ("evictions", C.c_int64)]
+
+
 class KernelStat(C.Structure):
     _fields_ = [("name", C.c_char * 64), ("launches", C.c_int64), ("ms", C.c_double), ("bytes", C.c_double),
                 ("flops", C.c_double)]
@@ -148,6 +153,8 @@ SIGNATURES = {
     "er_set_fused": (C.c_int, [P, C.c_int]),
     "er_set_persistent": (C.c_int, [P, C.c_int]),
     "er_get_persistent": (C.c_int, [P, C.POINTER(C.c_int)]),
+    "er_set_graphs": (C.c_int, [P, C.c_int]),
+    "er_get_graph_stats": (C.c_int, [P, C.POINTER(GraphStats)]),
     "er_set_decode_spin_limit": (C.c_int, [P, C.c_int64]),
     "er_set_decode_trace": (C.c_int, [P, C.c_int]),
     "er_get_decode_trace": (C.c_int, [P, C.POINTER(C.c_double), C.POINTER(C.c_double), C.c_int,

@@ -21,6 +21,7 @@
 #include <cstring>
 #include <map>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/er_api.h"
@@ -141,6 +142,7 @@ struct er_ctx {
 
   // diagnostics
   int last_mode = -1, last_gamma = 0, last_B = 0;
+  int last_rows = 0;      // sequences the last step ran (last_B plus graph padding): the drafter logits' stride
   size_t last_tok_off = 0;  // verify tokens [B, gamma+1] of the last speculative step, in the metadata region
   std::vector<int32_t> last_prefill_row;
 
@@ -171,6 +173,26 @@ struct er_ctx {
   unsigned long long* dec_trace = nullptr;  // phase trace buffer (er_set_decode_trace), device
   int dec_trace_max = 0;
   int dec_trace_nwg = 0;             // grid of the last traced launch
+
+  // bucketed graph capture (er_set_graphs): steps of at most graph_max rows
+  // per phase run padded to a power-of-two batch bucket and replay graphs
+  // recorded per (kind, bucket, gamma, context capacity in blocks)
+  struct GKey {
+    int kind, nb, g, cap;
+    bool operator<(const GKey& o) const { return std::tie(kind, nb, g, cap) < std::tie(o.kind, o.nb, o.g, o.cap); }
+  };
+  struct GEnt {
+    hipGraphExec_t x = nullptr;
+    size_t meta_used = 0;   // metadata layout size the graph was recorded with
+    long used = 0;          // last replay (least recently used is evicted)
+  };
+  int graph_max = 0;                 // largest batch run through graphs (0: off)
+  int graph_keep = 64;               // graphs kept
+  hipStream_t cap_st = nullptr;      // private stream the graphs are recorded on
+  int32_t pad_block = -1;            // KV block the padding rows write and read
+  std::map<GKey, GEnt> graphs;
+  long graph_tick = 0;
+  int64_t graph_captures = 0, graph_replays = 0, graph_evictions = 0;
 
   // timing
   int timing_period = 0, timing_first = 0;
@@ -209,6 +231,13 @@ int fail(er_ctx* c, int code, const char* fmt, ...) {
     }                                                                                   \
   } while (0)
 
+// Propagate an error code already recorded by fail().
+#define HIPC_OK(x)              \
+  do {                          \
+    const int r_ = (x);         \
+    if (r_ != ER_OK) return r_; \
+  } while (0)
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Start filling the metadata region: waits until the last queued upload of
@@ -228,6 +257,111 @@ int meta_upload(er_ctx* c) {
   HIPC(c, hipMemcpyAsync(c->meta.d, c->meta.h, c->meta.used, hipMemcpyHostToDevice, c->st));
   HIPC(c, hipEventRecord(c->meta_ev, c->st));
   c->meta_pending = true;
+  return ER_OK;
+}
+
+// ---- bucketed graph capture --------------------------------------------------
+// TLT notes, section 3, Design A, A3: a batch range shares one set of
+// recorded graphs (here: 1, 2, 3, 4, then 5-8, 9-16, ... padded to the
+// range's top), and the
+// drafter's and the target's graphs are recorded apart, so that the verify
+// graph serves both self-drafted and history-drafted steps.  Everything a
+// replayed kernel reads that changes from step to step sits in the metadata
+// region at offsets fixed by the key: the block table (stride = the
+// context-capacity class), the work-unit table (a fixed number of units per
+// item), positions, slots and tokens.
+constexpr int GRAPH_AR = 0, GRAPH_DRAFT = 1, GRAPH_VERIFY = 2;
+
+int pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Batch bucket: batches of 1 .. 4 run as they are (padding one of 3 to 4
+// costs more than the replay saves on MI355X: 2-6 % at 7B widths), larger
+// ones padded to the next power of two.
+int graph_bucket(int n) { return n <= 4 ? n : pow2_at_least(n); }
+
+void graph_drop(er_ctx* c) {
+  for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second.x);
+  c->graphs.clear();
+}
+
+// How a step over n sequences of rows_per_seq query rows each runs through
+// graphs: nb padded rows (0: eagerly), capacity cap blocks per sequence, U
+// attention units per item.
+struct GraphPlan {
+  int nb = 0, cap = 0, U = 0;
+};
+GraphPlan graph_plan(const er_ctx* c, int n, const int32_t* ids, int rows_per_seq) {
+  GraphPlan p;
+  // (the padding rows' positions 0 .. rows_per_seq - 1 must stay inside the one padding block)
+  if (c->graph_max <= 0 || c->kprof || c->dec_on || n > c->graph_max || c->pad_block < 0 ||
+      rows_per_seq > KV_BLOCK)
+    return p;
+  const int nb = graph_bucket(n);
+  if (nb > c->rd.max_batch || nb * rows_per_seq > c->max_rows || nb * rows_per_seq > c->logit_rows) return p;
+  int most = 1;
+  for (int i = 0; i < n; ++i) most = std::max(most, (c->seqs[ids[i]].n + rows_per_seq + KV_BLOCK - 1) / KV_BLOCK);
+  const int cap = std::max(16, pow2_at_least(most));
+  const int hkv = c->md.n_kv_heads, grp = c->md.n_q_heads / hkv;
+  const int U = graph_units_per_item(nb, hkv, cap);
+  if ((size_t)nb * U * hkv * grp * rows_per_seq * (size_t)(c->md.head_dim + 2) > c->attn_ws_floats) return p;
+  p.nb = nb;
+  p.cap = cap;
+  p.U = U;
+  return p;
+}
+
+// Replay the graph of key (kind, nb, g, cap) on the context's stream,
+// recording it from `body` (kernel launches only) when the cache has none:
+// the launches are captured on the private capture stream (torch's default
+// stream cannot be captured).  A cached graph recorded with a different
+// metadata layout size is recorded again.
+template <class F>
+int graph_run(er_ctx* c, int kind, int nb, int g, int cap, F&& body) {
+  const er_ctx::GKey k{kind, nb, g, cap};
+  auto it = c->graphs.find(k);
+  if (it != c->graphs.end() && it->second.meta_used != c->meta.used) {
+    (void)hipGraphExecDestroy(it->second.x);
+    c->graphs.erase(it);
+    it = c->graphs.end();
+  }
+  if (it == c->graphs.end()) {
+    while (!c->graphs.empty() && (int)c->graphs.size() >= c->graph_keep) {
+      auto lru = c->graphs.begin();
+      for (auto j = c->graphs.begin(); j != c->graphs.end(); ++j)
+        if (j->second.used < lru->second.used) lru = j;
+      (void)hipGraphExecDestroy(lru->second.x);
+      c->graphs.erase(lru);
+      ++c->graph_evictions;
+    }
+    HIPC(c, hipStreamBeginCapture(c->cap_st, hipStreamCaptureModeThreadLocal));
+    hipStream_t user = c->st;
+    c->st = c->cap_st;
+    const int r = body();
+    c->st = user;
+    hipGraph_t gr = nullptr;
+    const hipError_t e = hipStreamEndCapture(c->cap_st, &gr);
+    if (r) {
+      if (gr) (void)hipGraphDestroy(gr);
+      return r;
+    }
+    if (e != hipSuccess || !gr) return fail(c, ER_EDEVICE, "graph capture: %s", hipGetErrorString(e));
+    hipGraphExec_t x = nullptr;
+    const hipError_t e2 = hipGraphInstantiate(&x, gr, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(gr);
+    if (e2 != hipSuccess) return fail(c, ER_EDEVICE, "graph instantiate: %s", hipGetErrorString(e2));
+    er_ctx::GEnt ent;
+    ent.x = x;
+    ent.meta_used = c->meta.used;
+    it = c->graphs.emplace(k, ent).first;
+    ++c->graph_captures;
+  }
+  it->second.used = ++c->graph_tick;
+  HIPC(c, hipGraphLaunch(it->second.x, c->st));
+  ++c->graph_replays;
   return ER_OK;
 }
 
@@ -739,6 +873,7 @@ int quantize_into(er_ctx* c, const void* W, long N, long K, LinearW* out, char**
 
 int set_weights(er_ctx* c, const er_weights* w) {
   const er_model_desc& m = c->md;
+  graph_drop(c);  // recorded graphs hold the old weight pointers
   if (!w || !w->embed || !w->final_norm || !w->lm_head || !w->attn_norm || !w->wqkv || !w->wo || !w->mlp_norm ||
       !w->wgate_up || !w->wdown)
     return fail(c, ER_EINVAL, "null weight pointer");
@@ -832,6 +967,24 @@ int32_t* put_block_table(er_ctx* c, int n, const int32_t* ids, int* stride, size
   return bt;
 }
 
+// The block table of a graph step: nb rows of stride cap; rows n .. nb-1
+// (padding) name only the padding block.
+int32_t* put_block_table_padded(er_ctx* c, int n, int nb, const int32_t* ids, int cap, size_t* off) {
+  int32_t* bt = c->meta.push<int32_t>((size_t)nb * cap, off);
+  if (!bt) return nullptr;
+  for (int i = 0; i < nb; ++i) {
+    int32_t* row = bt + (size_t)i * cap;
+    if (i >= n) {
+      row[0] = c->pad_block;
+      for (int j = 1; j < cap; ++j) row[j] = 0;
+      continue;
+    }
+    const auto& b = c->seqs[ids[i]].bt.blocks;
+    for (int j = 0; j < cap; ++j) row[j] = (size_t)j < b.size() ? b[(size_t)j] : 0;
+  }
+  return bt;
+}
+
 int64_t slot_of(const Seq& s, int32_t pos) {
   return (int64_t)s.bt.blocks[(size_t)(pos / KV_BLOCK)] * KV_BLOCK + (pos % KV_BLOCK);
 }
@@ -895,24 +1048,41 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
   auto rollback = [&]() {
     for (int j = 0; j < n; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)c->seqs[ids[j]].n);
   };
+  // graph steps run nr = nb rows; padding rows n .. nr-1 decode token 0 at
+  // position 0 of the padding block and are dropped
+  const GraphPlan gp = graph_plan(c, n, ids, 1);
+  const int nr = gp.nb ? gp.nb : n;
   Meta& M = c->meta;
   if (int r_ = meta_begin(c)) { rollback(); return r_; }
   size_t o_ids, o_tok, o_pos, o_spos, o_slot, o_bt, o_ib, o_ir, o_ip, o_ic;
-  int32_t* h_ids = M.push<int32_t>(n, &o_ids);
-  int32_t* h_tok = M.push<int32_t>(n, &o_tok);
-  int32_t* h_pos = M.push<int32_t>(n, &o_pos);
-  int32_t* h_spos = M.push<int32_t>(n, &o_spos);
-  int64_t* h_slot = M.push<int64_t>(n, &o_slot);
-  int stride = 0;
-  int32_t* h_bt = put_block_table(c, n, ids, &stride, &o_bt);
-  int32_t* h_ib = M.push<int32_t>(n, &o_ib);
-  int32_t* h_ir = M.push<int32_t>(n, &o_ir);
-  int32_t* h_ip = M.push<int32_t>(n, &o_ip);
-  int32_t* h_ic = M.push<int32_t>(n, &o_ic);
+  int32_t* h_ids = M.push<int32_t>(nr, &o_ids);
+  int32_t* h_tok = M.push<int32_t>(nr, &o_tok);
+  int32_t* h_pos = M.push<int32_t>(nr, &o_pos);
+  int32_t* h_spos = M.push<int32_t>(nr, &o_spos);
+  int64_t* h_slot = M.push<int64_t>(nr, &o_slot);
+  int stride = gp.cap;
+  int32_t* h_bt =
+      gp.nb ? put_block_table_padded(c, n, nr, ids, gp.cap, &o_bt) : put_block_table(c, n, ids, &stride, &o_bt);
+  int32_t* h_ib = M.push<int32_t>(nr, &o_ib);
+  int32_t* h_ir = M.push<int32_t>(nr, &o_ir);
+  int32_t* h_ip = M.push<int32_t>(nr, &o_ip);
+  int32_t* h_ic = M.push<int32_t>(nr, &o_ic);
   if (!M.ok || !h_bt) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   int max_ctx = 1;
   double kv_keys = 0;
-  for (int i = 0; i < n; ++i) {
+  for (int i = 0; i < nr; ++i) {
+    h_ib[i] = i;
+    h_ir[i] = i;
+    h_ic[i] = 1;
+    if (i >= n) {
+      h_ids[i] = -1;
+      h_tok[i] = 0;
+      h_pos[i] = 0;
+      h_spos[i] = 1;
+      h_slot[i] = (int64_t)c->pad_block * KV_BLOCK;
+      h_ip[i] = 0;
+      continue;
+    }
     const Seq& s = c->seqs[ids[i]];
     kv_keys += s.n + 1;
     h_ids[i] = ids[i];
@@ -920,26 +1090,31 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     h_pos[i] = s.n;
     h_spos[i] = s.n + 1;
     h_slot[i] = slot_of(s, s.n);
-    h_ib[i] = i;
-    h_ir[i] = i;
     h_ip[i] = s.n;
-    h_ic[i] = 1;
     max_ctx = std::max(max_ctx, s.n + 1);
   }
   int n_units = 0;
   int n_split = 0;
   int max_units = 0;
   size_t o_rec = 0;
-  const size_t o_us =
-      push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, h_ir, h_ib, &n_units, &n_split, &max_units, &o_rec);
+  size_t o_us;
+  if (gp.nb) {
+    o_us = push_units_fixed(M, nr, gp.U, h_ip, h_ic, h_ir, h_ib, &o_rec);
+    n_units = nr * gp.U;
+    n_split = gp.U > 1 ? nr : 0;
+    max_units = gp.U;
+    max_ctx = gp.cap * KV_BLOCK;
+  } else {
+    o_us = push_units(M, n, (int)c->md.n_kv_heads, h_ip, h_ic, h_ir, h_ib, &n_units, &n_split, &max_units, &o_rec);
+  }
   if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
-  auto run = [&]() -> int {
-    if (int r_ = meta_upload(c)) return r_;
-    if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
+  // the step's kernels: target forward over nr rows, then the AR draw (mid:
+  // record the event between the two, on eager timed steps)
+  auto ar_body = [&](bool mid) -> int {
     Fwd f;
     f.draft = false;
     f.dec_ok = true;
-    f.M = n;
+    f.M = nr;
     f.tokens = M.dev<int32_t>(o_tok);
     f.pos = M.dev<int32_t>(o_pos);
     f.slot = M.dev<int64_t>(o_slot);
@@ -949,7 +1124,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.it_row0 = M.dev<int32_t>(o_ir);
     f.it_pos0 = M.dev<int32_t>(o_ip);
     f.it_cnt = M.dev<int32_t>(o_ic);
-    f.n_items = n;
+    f.n_items = nr;
     f.max_q = 1;
     f.max_ctx = max_ctx;
     f.unit_start = M.dev<int32_t>(o_us);
@@ -963,11 +1138,24 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
     f.ldl = c->md.vocab;
     int r = forward(c, f);
     if (r) return r;
-    if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
-    KC(c, launch_row_stats(c->logits_p, n, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
-    KC(c, launch_sample_rows(c->logits_p, c->stats_p, n, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.top_p,
+    if (mid) HIPC(c, hipEventRecord(c->ev[1], c->st));
+    KC(c, launch_row_stats(c->logits_p, nr, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.top_p, c->stats_p,
+                           c->st));
+    KC(c, launch_sample_rows(c->logits_p, c->stats_p, nr, c->md.vocab, c->md.vocab, c->rd.temperature, c->rd.top_p,
                              c->rd.seed, M.dev<int32_t>(o_ids), M.dev<int32_t>(o_spos), 0, PURPOSE_AR, c->out_d, 1,
                              nullptr, c->st));
+    return ER_OK;
+  };
+  auto run = [&]() -> int {
+    if (int r_ = meta_upload(c)) return r_;
+    if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
+    if (gp.nb) {
+      // one graph: forward and draw (the split between them is not timed)
+      HIPC_OK(graph_run(c, GRAPH_AR, nr, 0, gp.cap, [&]() { return ar_body(false); }));
+      if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
+    } else {
+      HIPC_OK(ar_body(timed));
+    }
     if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
     HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)n * 4, hipMemcpyDeviceToHost, c->st));
     if (int r_ = dec_queue_err(c)) return r_;
@@ -1004,6 +1192,7 @@ int do_ar(er_ctx* c, int n, const int32_t* ids, int32_t* tokens_out, int out_str
   c->last_mode = ER_MODE_AR;
   c->last_gamma = 0;
   c->last_B = n;
+  c->last_rows = nr;
   if (info) {
     *info = er_step_info{};
     info->mode = ER_MODE_AR;
@@ -1041,87 +1230,103 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   auto rollback = [&]() {
     for (int j = 0; j < n; ++j) c->seqs[ids[j]].bt.truncate(c->pool, (int64_t)c->seqs[ids[j]].n);
   };
+  // graph steps run nr = nb padded sequences; padding sequences draft and
+  // verify from token 0 at position 0 of the padding block and are dropped
+  const GraphPlan gp = graph_plan(c, n, ids, G1);
+  const int nr = gp.nb ? gp.nb : n;
   Meta& M = c->meta;
   if (int r_ = meta_begin(c)) { rollback(); return r_; }
   size_t o_ids, o_pos0, o_tok, o_bt;
-  int32_t* h_ids = M.push<int32_t>(n, &o_ids);
-  int32_t* h_pos0 = M.push<int32_t>(n, &o_pos0);
-  int32_t* h_tok = M.push<int32_t>((size_t)n * G1, &o_tok);
-  int stride = 0;
-  int32_t* h_bt = put_block_table(c, n, ids, &stride, &o_bt);
+  int32_t* h_ids = M.push<int32_t>(nr, &o_ids);
+  int32_t* h_pos0 = M.push<int32_t>(nr, &o_pos0);
+  int32_t* h_tok = M.push<int32_t>((size_t)nr * G1, &o_tok);
+  int stride = gp.cap;
+  int32_t* h_bt =
+      gp.nb ? put_block_table_padded(c, n, nr, ids, gp.cap, &o_bt) : put_block_table(c, n, ids, &stride, &o_bt);
   // per draft step j (1..g): positions, slots, items (bt row, q row0, pos0, count), sample positions
   std::vector<size_t> o_dp(g), o_ds(g), o_dsp(g);
   size_t o_ib, o_ir, o_ic, o_vp, o_vs, o_vir, o_vic;
   std::vector<int32_t*> h_dp(g), h_dsp(g);
   std::vector<int64_t*> h_ds(g);
   for (int j = 0; j < g; ++j) {
-    h_dp[j] = M.push<int32_t>(n, &o_dp[j]);
-    h_ds[j] = M.push<int64_t>(n, &o_ds[j]);
-    h_dsp[j] = M.push<int32_t>(n, &o_dsp[j]);
+    h_dp[j] = M.push<int32_t>(nr, &o_dp[j]);
+    h_ds[j] = M.push<int64_t>(nr, &o_ds[j]);
+    h_dsp[j] = M.push<int32_t>(nr, &o_dsp[j]);
   }
-  int32_t* h_ib = M.push<int32_t>(n, &o_ib);   // item b -> block-table row b (draft and verify)
-  int32_t* h_ir = M.push<int32_t>(n, &o_ir);   // draft: q row b
-  int32_t* h_ic = M.push<int32_t>(n, &o_ic);   // draft: 1 query
-  int32_t* h_vp = M.push<int32_t>((size_t)n * G1, &o_vp);
-  int64_t* h_vs = M.push<int64_t>((size_t)n * G1, &o_vs);
-  int32_t* h_vir = M.push<int32_t>(n, &o_vir);  // verify: q row b*G1
-  int32_t* h_vic = M.push<int32_t>(n, &o_vic);  // verify: G1 queries
+  int32_t* h_ib = M.push<int32_t>(nr, &o_ib);   // item b -> block-table row b (draft and verify)
+  int32_t* h_ir = M.push<int32_t>(nr, &o_ir);   // draft: q row b
+  int32_t* h_ic = M.push<int32_t>(nr, &o_ic);   // draft: 1 query
+  int32_t* h_vp = M.push<int32_t>((size_t)nr * G1, &o_vp);
+  int64_t* h_vs = M.push<int64_t>((size_t)nr * G1, &o_vs);
+  int32_t* h_vir = M.push<int32_t>(nr, &o_vir);  // verify: q row b*G1
+  int32_t* h_vic = M.push<int32_t>(nr, &o_vic);  // verify: G1 queries
   if (!M.ok || !h_bt) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
   int max_ctx = 1;
   double kv_sum = 0;
-  for (int b = 0; b < n; ++b) {
-    const Seq& s = c->seqs[ids[b]];
-    kv_sum += s.n;
-    h_ids[b] = ids[b];
-    h_pos0[b] = s.n;
-    h_tok[(size_t)b * G1] = s.pending;
-    for (int i = 1; i < G1; ++i) h_tok[(size_t)b * G1 + i] = hdraft ? hdraft[(size_t)b * g + i - 1] : 0;
+  for (int b = 0; b < nr; ++b) {
+    const bool pad = b >= n;
+    const Seq* s = pad ? nullptr : &c->seqs[ids[b]];
+    const int32_t n0 = pad ? 0 : s->n;
+    const int64_t pslot = (int64_t)c->pad_block * KV_BLOCK;
+    if (!pad) kv_sum += n0;
+    h_ids[b] = pad ? -1 : ids[b];
+    h_pos0[b] = n0;
+    h_tok[(size_t)b * G1] = pad ? 0 : s->pending;
+    for (int i = 1; i < G1; ++i) h_tok[(size_t)b * G1 + i] = (hdraft && !pad) ? hdraft[(size_t)b * g + i - 1] : 0;
     for (int j = 0; j < g; ++j) {
-      h_dp[j][b] = s.n + j;
-      h_ds[j][b] = slot_of(s, s.n + j);
-      h_dsp[j][b] = s.n + j + 1;
+      h_dp[j][b] = n0 + j;
+      h_ds[j][b] = pad ? pslot + j : slot_of(*s, n0 + j);
+      h_dsp[j][b] = n0 + j + 1;
     }
     h_ib[b] = b;
     h_ir[b] = b;
     h_ic[b] = 1;
     for (int i = 0; i < G1; ++i) {
-      h_vp[(size_t)b * G1 + i] = s.n + i;
-      h_vs[(size_t)b * G1 + i] = slot_of(s, s.n + i);
+      h_vp[(size_t)b * G1 + i] = n0 + i;
+      h_vs[(size_t)b * G1 + i] = pad ? pslot + i : slot_of(*s, n0 + i);
     }
     h_vir[b] = b * G1;
     h_vic[b] = G1;
-    max_ctx = std::max(max_ctx, s.n + G1);
+    if (!pad) max_ctx = std::max(max_ctx, n0 + G1);
   }
   std::vector<size_t> o_dus(g);
   std::vector<int> n_dus(g);
   std::vector<int> s_dus(g);
   std::vector<int> m_dus(g);
   std::vector<size_t> o_drec(g);
-  for (int j = 0; j < g; ++j)
-    o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, h_ir, h_ib, &n_dus[j], &s_dus[j], &m_dus[j],
-                          &o_drec[j]);
   int n_vus = 0;
   int s_vus = 0;
   int m_vus = 0;
   size_t o_vrec = 0;
-  const size_t o_vus =
-      push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, h_vir, h_ib, &n_vus, &s_vus, &m_vus, &o_vrec);
-  if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
-  auto run = [&]() -> int {
-    if (int r_ = meta_upload(c)) return r_;
-    if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
-    int32_t* d_tok = M.dev<int32_t>(o_tok);
-    if (hdraft) {
-      KC(c, launch_point_mass(c->logits_q, g, n, V, d_tok, G1, c->st));
-      for (int j = 0; j < g; ++j)
-        KC(c, launch_row_stats(c->logits_q + (size_t)j * n * V, n, V, V, c->rd.temperature, c->rd.top_p,
-                               (char*)c->stats_q + (size_t)j * n * stats_row_bytes(c->nch), c->st));
+  size_t o_vus;
+  if (gp.nb) {
+    for (int j = 0; j < g; ++j) {
+      o_dus[j] = push_units_fixed(M, nr, gp.U, h_dp[j], h_ic, h_ir, h_ib, &o_drec[j]);
+      n_dus[j] = nr * gp.U;
+      s_dus[j] = gp.U > 1 ? nr : 0;
+      m_dus[j] = gp.U;
     }
-    for (int j = 0; j < (hdraft ? 0 : g); ++j) {
+    o_vus = push_units_fixed(M, nr, gp.U, h_pos0, h_vic, h_vir, h_ib, &o_vrec);
+    n_vus = nr * gp.U;
+    s_vus = gp.U > 1 ? nr : 0;
+    m_vus = gp.U;
+    max_ctx = gp.cap * KV_BLOCK;
+  } else {
+    for (int j = 0; j < g; ++j)
+      o_dus[j] = push_units(M, n, (int)c->md.n_kv_heads, h_dp[j], h_ic, h_ir, h_ib, &n_dus[j], &s_dus[j], &m_dus[j],
+                            &o_drec[j]);
+    o_vus = push_units(M, n, (int)c->md.n_kv_heads, h_pos0, h_vic, h_vir, h_ib, &n_vus, &s_vus, &m_vus, &o_vrec);
+  }
+  if (!M.ok) { rollback(); return fail(c, ER_ENOMEM, "metadata region too small"); }
+  const double kv_dup = shared_keys(c, n, ids);
+  int32_t* d_tok = M.dev<int32_t>(o_tok);
+  // the drafter's g forwards over nr rows, each followed by its draw
+  auto draft_body = [&]() -> int {
+    for (int j = 0; j < g; ++j) {
       Fwd f;
       f.draft = true;
       f.dec_ok = true;
-      f.M = n;
+      f.M = nr;
       f.tokens = d_tok + j;
       f.tok_stride = G1;
       f.pos = M.dev<int32_t>(o_dp[j]);
@@ -1132,7 +1337,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.it_row0 = M.dev<int32_t>(o_ir);
       f.it_pos0 = M.dev<int32_t>(o_dp[j]);
       f.it_cnt = M.dev<int32_t>(o_ic);
-      f.n_items = n;
+      f.n_items = nr;
       f.max_q = 1;
       f.max_ctx = max_ctx;
       f.unit_start = M.dev<int32_t>(o_dus[j]);
@@ -1141,22 +1346,26 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
       f.n_split = s_dus[j];
       f.max_units = m_dus[j];
       f.kv_keys = kv_sum + (double)n * (j + 1);
-      f.kv_shared = shared_keys(c, n, ids);
-      f.logits = c->logits_q + (size_t)j * n * V;
+      f.kv_shared = kv_dup;
+      f.logits = c->logits_q + (size_t)j * nr * V;
       f.ldl = V;
       int r = forward(c, f);
       if (r) return r;
-      void* sq = (char*)c->stats_q + (size_t)j * n * stats_row_bytes(c->nch);
-      KC(c, launch_row_stats(f.logits, n, V, V, c->rd.temperature, c->rd.top_p, sq, c->st));
-      KC(c, launch_sample_rows(f.logits, sq, n, V, V, c->rd.temperature, c->rd.top_p, c->rd.seed,
+      void* sq = (char*)c->stats_q + (size_t)j * nr * stats_row_bytes(c->nch);
+      KC(c, launch_row_stats(f.logits, nr, V, V, c->rd.temperature, c->rd.top_p, sq, c->st));
+      KC(c, launch_sample_rows(f.logits, sq, nr, V, V, c->rd.temperature, c->rd.top_p, c->rd.seed,
                                M.dev<int32_t>(o_ids), M.dev<int32_t>(o_dsp[j]), j + 1, PURPOSE_DRAFT, d_tok + j + 1,
                                G1, nullptr, c->st));
     }
-    if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
+    return ER_OK;
+  };
+  // the target's verify forward over nr * (g + 1) rows, then the lossless
+  // decision (mid: record the event between the two, on eager timed steps)
+  auto verify_body = [&](bool mid) -> int {
     Fwd f;
     f.draft = false;
     f.dec_ok = true;
-    f.M = n * G1;
+    f.M = nr * G1;
     f.tokens = d_tok;
     f.tok_stride = 1;
     f.pos = M.dev<int32_t>(o_vp);
@@ -1167,7 +1376,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.it_row0 = M.dev<int32_t>(o_vir);
     f.it_pos0 = M.dev<int32_t>(o_pos0);
     f.it_cnt = M.dev<int32_t>(o_vic);
-    f.n_items = n;
+    f.n_items = nr;
     f.max_q = G1;
     f.max_ctx = max_ctx;
     f.unit_start = M.dev<int32_t>(o_vus);
@@ -1176,18 +1385,42 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
     f.n_split = s_vus;
     f.max_units = m_vus;
     f.kv_keys = kv_sum + (double)n * G1;
-    f.kv_shared = shared_keys(c, n, ids);
+    f.kv_shared = kv_dup;
     f.logits = c->logits_p;
     f.ldl = V;
     int r = forward(c, f);
     if (r) return r;
-    if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
-    KC(c, launch_row_stats(c->logits_p, n * G1, V, V, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
-    KC(c, launch_spec_decide(c->logits_p, c->stats_p, c->logits_q, c->stats_q, d_tok, n, g, V, c->rd.temperature,
+    if (mid) HIPC(c, hipEventRecord(c->ev[2], c->st));
+    KC(c, launch_row_stats(c->logits_p, nr * G1, V, V, c->rd.temperature, c->rd.top_p, c->stats_p, c->st));
+    KC(c, launch_spec_decide(c->logits_p, c->stats_p, c->logits_q, c->stats_q, d_tok, nr, g, V, c->rd.temperature,
                              c->rd.top_p, c->rd.seed, M.dev<int32_t>(o_ids), M.dev<int32_t>(o_pos0), c->out_d,
-                             c->out_d + n * G1, c->resid, c->st));
+                             c->out_d + nr * G1, c->resid, c->st));
+    return ER_OK;
+  };
+  auto run = [&]() -> int {
+    if (int r_ = meta_upload(c)) return r_;
+    if (timed) HIPC(c, hipEventRecord(c->ev[0], c->st));
+    if (hdraft) {
+      // point-mass proposals of the copied drafts (not recorded: a few small launches)
+      KC(c, launch_point_mass(c->logits_q, g, nr, V, d_tok, G1, c->st));
+      for (int j = 0; j < g; ++j)
+        KC(c, launch_row_stats(c->logits_q + (size_t)j * nr * V, nr, V, V, c->rd.temperature, c->rd.top_p,
+                               (char*)c->stats_q + (size_t)j * nr * stats_row_bytes(c->nch), c->st));
+    } else if (gp.nb) {
+      HIPC_OK(graph_run(c, GRAPH_DRAFT, nr, g, gp.cap, draft_body));
+    } else {
+      HIPC_OK(draft_body());
+    }
+    if (timed) HIPC(c, hipEventRecord(c->ev[1], c->st));
+    if (gp.nb) {
+      // one graph: verify forward and decision (the split between them is not timed)
+      HIPC_OK(graph_run(c, GRAPH_VERIFY, nr, g, gp.cap, [&]() { return verify_body(false); }));
+      if (timed) HIPC(c, hipEventRecord(c->ev[2], c->st));
+    } else {
+      HIPC_OK(verify_body(timed));
+    }
     if (timed) HIPC(c, hipEventRecord(c->ev[3], c->st));
-    HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)(n * G1 + n) * 4, hipMemcpyDeviceToHost, c->st));
+    HIPC(c, hipMemcpyAsync(c->out_h, c->out_d, (size_t)(nr * G1 + nr) * 4, hipMemcpyDeviceToHost, c->st));
     if (int r_ = dec_queue_err(c)) return r_;
     HIPC(c, hipStreamSynchronize(c->st));
     return dec_check(c);
@@ -1201,7 +1434,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   AlphaAcc acc;
   int acc_tot = 0, emit_tot = 0, kept_tot = 0, fin = 0;
   const int32_t* out_tok = c->out_h;
-  const int32_t* nacc = c->out_h + n * G1;
+  const int32_t* nacc = c->out_h + nr * G1;
   for (int b = 0; b < n; ++b) {
     Seq& s = c->seqs[ids[b]];
     const int a = nacc[b];
@@ -1251,6 +1484,7 @@ int do_spec(er_ctx* c, int n, const int32_t* ids, int g, int32_t* tokens_out, in
   c->last_mode = ER_MODE_SD;
   c->last_gamma = g;
   c->last_B = n;
+  c->last_rows = nr;
   if (info) {
     *info = er_step_info{};
     info->mode = hdraft ? ER_MODE_HISTORY : ER_MODE_SD;
@@ -2224,6 +2458,44 @@ int er_set_persistent(er_ctx* c, int on) {
   return ER_OK;
 }
 
+int er_set_graphs(er_ctx* c, int max_batch) {
+  if (!c) return ER_EINVAL;
+  if (max_batch < 0) return fail(c, ER_EINVAL, "max_batch must be >= 0");
+  try {
+    HIPC(c, hipStreamSynchronize(c->st));
+    graph_drop(c);
+    if (max_batch == 0) {
+      c->graph_max = 0;
+      if (c->pad_block >= 0) c->pool.decref(c->pad_block);
+      c->pad_block = -1;
+      if (c->cap_st) (void)hipStreamDestroy(c->cap_st);
+      c->cap_st = nullptr;
+      return ER_OK;
+    }
+    if (!c->cap_st) HIPC(c, hipStreamCreateWithFlags(&c->cap_st, hipStreamNonBlocking));
+    if (c->pad_block < 0) {
+      c->pad_block = c->pool.alloc();
+      if (c->pad_block < 0) return fail(c, ER_ENOMEM, "no free KV block for the padding rows");
+      HIPC(c, hipMemsetAsync((char*)c->kv_pool + (size_t)c->pad_block * c->block_bytes, 0, c->block_bytes, c->st));
+      HIPC(c, hipStreamSynchronize(c->st));
+    }
+    c->graph_max = max_batch;
+    return ER_OK;
+  } catch (...) {
+    return fail(c, ER_EINVAL, "internal error");
+  }
+}
+
+int er_get_graph_stats(const er_ctx* c, er_graph_stats* out) {
+  if (!c || !out) return ER_EINVAL;
+  out->max_batch = c->graph_max;
+  out->cached = (int32_t)c->graphs.size();
+  out->captures = c->graph_captures;
+  out->replays = c->graph_replays;
+  out->evictions = c->graph_evictions;
+  return ER_OK;
+}
+
 int er_set_decode_spin_limit(er_ctx* c, int64_t polls) {
   if (!c || polls < 1) return ER_EINVAL;
   c->dec_spin_limit = (long)polls;
@@ -2289,6 +2561,7 @@ int er_get_persistent(const er_ctx* c, int* on) {
 
 int er_set_fused(er_ctx* c, int on) {
   if (!c) return ER_EINVAL;
+  graph_drop(c);
   c->fuse = c->bf16 && on != 0;
   return ER_OK;
 }
@@ -2374,7 +2647,7 @@ int er_debug_logits(er_ctx* c, int which, int slot, float* host_out, int32_t* ro
   std::vector<const float*> rows;
   if (which == 0) {
     if (c->last_mode != ER_MODE_SD) return fail(c, ER_ESTATE, "last step was not speculative");
-    for (int j = 0; j < c->last_gamma; ++j) rows.push_back(c->logits_q + ((size_t)j * c->last_B + slot) * V);
+    for (int j = 0; j < c->last_gamma; ++j) rows.push_back(c->logits_q + ((size_t)j * c->last_rows + slot) * V);
   } else if (which == 1) {
     if (c->last_mode == ER_MODE_SD) {
       for (int i = 0; i <= c->last_gamma; ++i) rows.push_back(c->logits_p + ((size_t)slot * (c->last_gamma + 1) + i) * V);
@@ -2591,6 +2864,8 @@ void er_destroy(er_ctx* c) {
   if (!c) return;
   if (c->st) (void)hipStreamSynchronize(c->st);
   else (void)hipDeviceSynchronize();
+  graph_drop(c);
+  if (c->cap_st) (void)hipStreamDestroy(c->cap_st);
   if (c->meta.h) (void)hipHostFree(c->meta.h);
   if (c->out_h) (void)hipHostFree(c->out_h);
   if (c->dec_trace) (void)hipFree(c->dec_trace);

@@ -91,4 +91,44 @@ inline size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int
   return off;
 }
 
+// A fixed-shape split for replayed graphs: every item gets exactly U units
+// (so the unit count n * U, the split list and the combine grid depend on n
+// and U alone, not on the contexts).  Item i's units are ceil(nblk_i / U)
+// blocks long; units that start past the item's last block read nothing and
+// leave an empty partial (running max -inf, sum 0), which the combine weighs
+// by zero.  With U = 1 no item is split.  The layout (unit table [3n + 1],
+// then n * U records) is the one push_units writes.
+inline int graph_units_per_item(int n, int hkv, int cap_blocks) {
+  const int64_t total = (int64_t)n * cap_blocks;
+  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 255) / 256));
+  return (int)std::max<int64_t>(1, (cap_blocks + target - 1) / target);
+}
+inline size_t push_units_fixed(Meta& M, int n, int U, const int32_t* pos0, const int32_t* cnt, const int32_t* row0,
+                               const int32_t* btrow, size_t* o_rec) {
+  size_t off = 0;
+  int32_t* us = M.push<int32_t>((size_t)3 * n + 1, &off);
+  if (!us) return 0;
+  int32_t* rec = M.push<int32_t>((size_t)8 * n * U, o_rec);
+  if (!rec) return 0;
+  for (int i = 0; i <= n; ++i) us[i] = i * U;
+  for (int i = 0; i < n; ++i) {
+    const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
+    const int32_t bpu = (int32_t)std::max<int64_t>(1, (nblk + U - 1) / U);
+    us[n + 1 + i] = bpu;
+    us[2 * n + 1 + i] = i;
+    for (int k = 0; k < U; ++k) {
+      int32_t* r = rec + (size_t)8 * ((size_t)i * U + k);
+      r[0] = i;
+      r[1] = k | (U << 16);
+      r[2] = k * bpu;
+      r[3] = bpu;
+      r[4] = cnt[i];
+      r[5] = pos0[i];
+      r[6] = row0[i];
+      r[7] = btrow[i];
+    }
+  }
+  return off;
+}
+
 }  // namespace er

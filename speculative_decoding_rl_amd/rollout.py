@@ -222,8 +222,17 @@ class Engine:
                     probe_left=list(g.probe_left), cool_until=list(g.cool_until), cool_len=list(g.cool_len))
 
     def set_persistent(self, on: bool):
-        """Run forwards of <= 16 rows as one persistent launch (bf16 models; on by default)."""
+        """Run forwards of <= 16 rows as one persistent launch (bf16 models; off by default)."""
         check(self.lib.er_set_persistent(self.ctx, int(bool(on))), self.ctx, "er_set_persistent")
+
+    def set_graphs(self, max_batch: int):
+        """Replay recorded graphs for steps of at most max_batch sequences (0: off, the default)."""
+        check(self.lib.er_set_graphs(self.ctx, int(max_batch)), self.ctx, "er_set_graphs")
+
+    def graph_stats(self) -> dict:
+        g = _lib.GraphStats()
+        check(self.lib.er_get_graph_stats(self.ctx, C.byref(g)), self.ctx, "er_get_graph_stats")
+        return {f: getattr(g, f) for f, _ in g._fields_}
 
     def set_decode_spin_limit(self, polls: int):
         check(self.lib.er_set_decode_spin_limit(self.ctx, int(polls)), self.ctx, "er_set_decode_spin_limit")

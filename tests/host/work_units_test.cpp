@@ -6,7 +6,9 @@
 // too: one sequence's chunk of up to 4096 prompt tokens cut into items of
 // qmax = 64 / (n_q_heads / n_kv_heads) queries at consecutive positions, for
 // prompts of up to 15000 tokens filled chunk after chunk into one region (as
-// er_prefill does, each fill starting from a reset region).
+// er_prefill does, each fill starting from a reset region).  And the
+// fixed-shape split of replayed graphs (push_units_fixed): every item's blocks
+// covered exactly once by its U units, no unit over 1024 blocks.
 #include <algorithm>
 #include <cassert>
 #include <cstdio>
@@ -65,6 +67,39 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
   // about 256 (unit, KV head) pairs once the target is neither floored nor capped
   if (target > 8 && target < 1024) assert((int64_t)nu_tot * hkv <= 256 + (int64_t)n * hkv);
   return nu_tot;
+}
+
+// The fixed-shape split of replayed graphs: U units per item, the item's
+// blocks covered exactly once in unit order, units past the end empty, no
+// unit longer than the 1024 block ids a work-group stages, and the layout of
+// push_units (unit table, blocks per unit, split list, records).
+static void check_fixed(Meta& M, int n, int hkv, int cap, const std::vector<int32_t>& pos0,
+                        const std::vector<int32_t>& cnt, const std::vector<int32_t>& row0,
+                        const std::vector<int32_t>& btrow) {
+  const int U = graph_units_per_item(n, hkv, cap);
+  assert(U >= 1 && U <= (cap + 7) / 8 + 1);
+  size_t o_rec = 0;
+  const size_t off = push_units_fixed(M, n, U, pos0.data(), cnt.data(), row0.data(), btrow.data(), &o_rec);
+  assert(M.ok && M.used <= M.cap);
+  const int32_t* us = (const int32_t*)(M.h + off);
+  const int32_t* rec = (const int32_t*)(M.h + o_rec);
+  for (int i = 0; i <= n; ++i) assert(us[i] == i * U);
+  for (int i = 0; i < n; ++i) {
+    const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
+    assert(nblk <= cap);
+    const int bpu = us[n + 1 + i];
+    assert(bpu >= 1 && bpu <= 1024);
+    assert(us[2 * n + 1 + i] == i);
+    std::vector<int> seen((size_t)nblk, 0);
+    for (int k = 0; k < U; ++k) {
+      const int32_t* r = rec + (size_t)8 * ((size_t)i * U + k);
+      assert(r[0] == i && (r[1] & 0xFFFF) == k && (r[1] >> 16) == U);
+      assert(r[2] == k * bpu && r[3] == bpu);
+      assert(r[4] == cnt[i] && r[5] == pos0[i] && r[6] == row0[i] && r[7] == btrow[i]);
+      for (int64_t b = r[2]; b < std::min<int64_t>(nblk, (int64_t)r[2] + bpu); ++b) ++seen[(size_t)b];
+    }
+    for (int64_t b = 0; b < nblk; ++b) assert(seen[(size_t)b] == 1);
+  }
 }
 
 int main() {
@@ -132,6 +167,25 @@ int main() {
           }
           assert(fills == (plen + chunk - 1) / chunk);
         }
+  // fixed-shape splits: power-of-two batches and capacity classes, contexts up to the capacity
+  for (int it = 0; it < 300; ++it) {
+    const int n = 1 << (rng() % 5);
+    const int hkv = 1 << (rng() % 4);
+    const int cap = 16 << (rng() % 8);
+    const int q = 1 + (int)(rng() % 9);
+    std::vector<int32_t> pos0(n), cnt(n, q), row0(n), btrow(n);
+    for (int i = 0; i < n; ++i) {
+      pos0[i] = (int32_t)(rng() % (cap * KV_BLOCK - q + 1));
+      row0[i] = i * q;
+      btrow[i] = i;
+    }
+    Meta M;
+    M.h = buf.data();
+    M.d = buf.data();
+    M.cap = buf.size();
+    M.reset();
+    check_fixed(M, n, hkv, cap, pos0, cnt, row0, btrow);
+  }
   std::printf("work_units ok\n");
   return 0;
 }
