@@ -687,16 +687,19 @@ static int run_gemm(const LinArgs& a, const LinearWs& ws, hipStream_t st, Linear
 // in flight, and a normalizing prologue does not serialize the weight stream.
 // A stage is 128 k of one 16-row subtile per lane group: bf16 4 x 16 B per
 // lane, W8 2 x 16 B, W4 1 x 16 B (one quantization group).  For the quantized
-// formats the per-group row sums of x' (zero-point terms) are computed once in
-// the prologue.  Waves split K (KS) within the work-group and reduce in LDS in
-// a fixed order; the first DEPTH-1 weight stages are issued before the x'
-// fill so that the two overlap.
+// formats the per-group row sums of x' (zero-point terms) are formed in the
+// prologue from the x' pieces themselves.  Waves split K (KS) within the
+// work-group and reduce in LDS in a fixed order; the first DEPTH-1 weight
+// stages, the W4 scale / zero staging loads and the x' loads all go out
+// before the prologue's first wait, so that they overlap (the prologue once
+// took ~4 us of a 17-21 us W4 launch at M = 1 with three dependent trips).
 // ----------------------------------------------------------------------------
 template <int FMT> struct StageW { static constexpr int NW = (FMT == FMT_BF16) ? 4 : (FMT == FMT_W8 ? 2 : 1); };
 
 // LDS of k_skinny: x' [M][K+8] bf16; quantized formats add per-chunk row sums
-// of x' [K/128][16] and the work-group's scale/zero pairs [R][K/128] (float2);
-// then the KS reduction area.
+// of x' [K/128][16] (rows < M written; the others feed only output rows that
+// are never stored) and the work-group's scale/zero pairs [R][K/128]
+// (float2); then the KS reduction area.
 struct SkinnyLds {
   size_t xsum, sz, red, total;
 };
@@ -848,15 +851,42 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
   for (int d = 0; d < DEPTH - 1; ++d) issue(min(d, last_it), d);
 
   {
-    // x' fill: XF 16-byte pieces per thread in flight at once (with the norm
-    // on load each piece is three loads; two pieces keep the kernel at 65
-    // VGPRs, three 512-thread work-groups per CU, where four pieces took 91
-    // and two work-groups).  With the norm on load, the rows' 1/rms come
-    // from one slot load per (row, slot) lane summed over 16 lanes into LDS,
-    // issued together with the first pieces' loads; the pieces are
-    // normalized after the barrier.
+    // Prologue, one memory round trip before the first barrier: the first
+    // pass of the W4 scale / zero staging, the rows' 1/rms (from one slot
+    // load per (row, slot) lane summed over 16 lanes) and the first x' pieces
+    // are all issued before anything waits.  x' fill: XF 16-byte pieces per
+    // thread in flight at once (with the norm on load each piece is three
+    // loads; two pieces keep the kernel at 65 VGPRs, three 512-thread
+    // work-groups per CU, where four pieces took 91 and two work-groups).
+    // The per-chunk row sums of x' (zero-point terms of the quantized
+    // formats) come from the pieces themselves: the 16 pieces of one
+    // (row, chunk) are 16 consecutive threads (K is a multiple of 128), summed
+    // by shuffles.
     constexpr int XF = 2;
+    constexpr int SZJ = 2;  // scale / zero entries per thread per staging pass (4 measured no better)
     __shared__ float rs_sh[16];
+    const int sz_total = (FMT == FMT_W4) ? R * nchunks : 0;
+    uint32_t sc[SZJ], zc[SZJ];
+    auto sz_load = [&](int e0) {
+#pragma unroll
+      for (int j = 0; j < SZJ; ++j) {
+        const int e = min(e0 + tid + 512 * j, sz_total - 1);
+        const int rr = e / nchunks, c = e - rr * nchunks;
+        const int s2 = nt * RG * NR + (rr >> 4);
+        const int l = rr & 15;
+        const long n = (16 * s2 + l < N) ? phys_row(a, s2, l) : N - 1;
+        sc[j] = ((const uint16_t*)sv)[n * G + c];
+        zc[j] = ((const uint8_t*)zv)[n * G + c];
+      }
+    };
+    auto sz_store = [&](int e0) {
+#pragma unroll
+      for (int j = 0; j < SZJ; ++j) {
+        const int e = e0 + tid + 512 * j;
+        if (e < sz_total) szl[e] = make_float2(bf2f((uint16_t)sc[j]), 128.0f + (float)zc[j]);
+      }
+    };
+    if constexpr (FMT == FMT_W4) sz_load(0);
     if (a.xnorm && tid < 16 * M) {
       const int m = tid >> 4, sl = tid & 15;
       const long hrow = a.xrow ? a.xrow[m] : m;
@@ -888,60 +918,35 @@ __global__ __launch_bounds__(512) void k_skinny(LinArgs a, SkinnyLds L) {
 #pragma unroll
       for (int j = 0; j < XF; ++j) {
         const int e = e0 + tid + 512 * j;
-        if (e < tot) {
-          const int m = e / K8, k8 = e - m * K8;
-          uint4 o = v[j];
-          if (a.xnorm) {
-            const float rs = rs_sh[m];
-            const uint4 h0 = v[j], hh = h1[j], gg = g[j];
-            o.x = f2bf(__uint_as_float(h0.x) * rs * bf_lo(gg.x)) | (f2bf(__uint_as_float(h0.y) * rs * bf_hi(gg.x)) << 16);
-            o.y = f2bf(__uint_as_float(h0.z) * rs * bf_lo(gg.y)) | (f2bf(__uint_as_float(h0.w) * rs * bf_hi(gg.y)) << 16);
-            o.z = f2bf(__uint_as_float(hh.x) * rs * bf_lo(gg.z)) | (f2bf(__uint_as_float(hh.y) * rs * bf_hi(gg.z)) << 16);
-            o.w = f2bf(__uint_as_float(hh.z) * rs * bf_lo(gg.w)) | (f2bf(__uint_as_float(hh.w) * rs * bf_hi(gg.w)) << 16);
-          }
-          *(uint4*)(xs + m * ldsx + k8 * 8) = o;
+        const bool in = e < tot;   // the same for the 16 lanes of one (row, chunk)
+        const int m = e / K8, k8 = e - m * K8;
+        uint4 o = v[j];
+        if (a.xnorm) {
+          const float rs = rs_sh[in ? m : 0];
+          const uint4 h0 = v[j], hh = h1[j], gg = g[j];
+          o.x = f2bf(__uint_as_float(h0.x) * rs * bf_lo(gg.x)) | (f2bf(__uint_as_float(h0.y) * rs * bf_hi(gg.x)) << 16);
+          o.y = f2bf(__uint_as_float(h0.z) * rs * bf_lo(gg.y)) | (f2bf(__uint_as_float(h0.w) * rs * bf_hi(gg.y)) << 16);
+          o.z = f2bf(__uint_as_float(hh.x) * rs * bf_lo(gg.z)) | (f2bf(__uint_as_float(hh.y) * rs * bf_hi(gg.z)) << 16);
+          o.w = f2bf(__uint_as_float(hh.z) * rs * bf_lo(gg.w)) | (f2bf(__uint_as_float(hh.w) * rs * bf_hi(gg.w)) << 16);
+        }
+        if (in) *(uint4*)(xs + m * ldsx + k8 * 8) = o;
+        if constexpr (FMT != FMT_BF16) {
+          float sm = bf_lo(o.x) + bf_hi(o.x) + bf_lo(o.y) + bf_hi(o.y) + bf_lo(o.z) + bf_hi(o.z) + bf_lo(o.w) + bf_hi(o.w);
+          sm += __shfl_xor(sm, 1, 64);
+          sm += __shfl_xor(sm, 2, 64);
+          sm += __shfl_xor(sm, 4, 64);
+          sm += __shfl_xor(sm, 8, 64);
+          if (in && (tid & 15) == 0) xsum[(k8 >> 4) * 16 + m] = sm;
         }
       }
     }
     if constexpr (FMT == FMT_W4) {
-      // this work-group's rows: logical subtile (nt*RG + rg')*NR + ni, lane row
-      // l16; eight entries per thread in flight at once (a plain loop would
-      // wait out one load latency per entry)
-      const int rows = 16 * NR * RG;
-      const int total = rows * nchunks;
-      for (int e0 = 0; e0 < total; e0 += 8 * 512) {
-        uint32_t sc[8], zc[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int e = min(e0 + tid + 512 * j, total - 1);
-          const int rr = e / nchunks, c = e - rr * nchunks;
-          const int s2 = nt * RG * NR + (rr >> 4);
-          const int l = rr & 15;
-          const long n = (16 * s2 + l < N) ? phys_row(a, s2, l) : N - 1;
-          sc[j] = ((const uint16_t*)sv)[n * G + c];
-          zc[j] = ((const uint8_t*)zv)[n * G + c];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int e = e0 + tid + 512 * j;
-          if (e < total) szl[e] = make_float2(bf2f((uint16_t)sc[j]), 128.0f + (float)zc[j]);
-        }
-      }
-    }
-    if constexpr (FMT != FMT_BF16) {
-      __syncthreads();
-      for (int e = tid; e < 16 * nchunks; e += 512) {
-        const int c = e >> 4, m = e & 15;
-        float sm = 0.f;
-        if (m < M) {
-          const uint4* p = (const uint4*)(xs + m * ldsx + c * 128);
-#pragma unroll 4
-          for (int j = 0; j < 16; ++j) {
-            const uint4 v = p[j];
-            sm += bf_lo(v.x) + bf_hi(v.x) + bf_lo(v.y) + bf_hi(v.y) + bf_lo(v.z) + bf_hi(v.z) + bf_lo(v.w) + bf_hi(v.w);
-          }
-        }
-        xsum[e] = sm;
+      // this work-group's rows: logical subtile (nt*RG + rg')*NR + ni, lane
+      // row l16; SZJ entries per thread in flight at once
+      sz_store(0);
+      for (int e0 = SZJ * 512; e0 < sz_total; e0 += SZJ * 512) {
+        sz_load(e0);
+        sz_store(e0);
       }
     }
     __syncthreads();
