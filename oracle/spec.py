@@ -73,9 +73,17 @@ def build_drafter(W: Weights, quant: str, group: int = 128, quant_lm_head: bool 
 
 @dataclass
 class SamplingParams:
+    """Sampler settings.  The library receives the temperature and top_p as 32-bit floats (its
+    rollout descriptor), so they are held here as those float32 values: where a decision sits within
+    float32 rounding of the threshold (a nucleus whose cumulative mass lies between float32(0.95) and
+    0.95), both sides then decide on the same number."""
     seed: int = 0
     temperature: float = 1.0
     top_p: float = 1.0
+
+    def __post_init__(self):
+        self.temperature = float(np.float32(self.temperature))
+        self.top_p = float(np.float32(self.top_p))
 
 
 @dataclass
