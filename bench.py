@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--no-kernel-profile", action="store_true")
     ap.add_argument("--persistent", action="store_true",
                     help="run forwards of <= 16 rows as the persistent decode kernel (default: kernel sequence)")
+    ap.add_argument("--library-gemm", type=int, default=128,
+                    help="run the target's projections of at least this many rows as library GEMMs (0: never)")
     ap.add_argument("--graphs", type=int, default=16,
                     help="replay recorded graphs for steps of at most this many sequences (0: every step eager)")
     ap.add_argument("--kprof-every", type=int, default=4,
@@ -103,12 +105,18 @@ def parse():
     return ap.parse_args()
 
 
+def shape_is_bf16(eng):
+    return getattr(eng.shape, "dtype", "bf16") == "bf16"
+
+
 def engine_options(eng, args):
     """The launch options every bench engine runs with."""
     if args.persistent:
         eng.set_persistent(True)
     if args.graphs:
         eng.set_graphs(args.graphs)
+    if args.library_gemm != 128 and shape_is_bf16(eng):
+        eng.set_library_gemm(args.library_gemm)
 
 
 def make_engine(args, shape, wts, policy):
@@ -812,7 +820,8 @@ def sweep_line(args, shape, wts, stops):
                                 + (f"; groups of {args.group} sequences share their bin's prefilled context"
                                    if args.group > 1 else "")),
                    "mode": "SD-auto (roofline toggle)", "global_batch": args.batch, "seq_len": args.prompt_len,
-                   "parallelism": "none (1 GPU)", "graphs": args.graphs},
+                   "parallelism": "none (1 GPU)", "graphs": args.graphs,
+                   "library_gemm_rows": args.library_gemm},
         "roofline": rf,
         "ar_value": round(tok_ar / t_ar, 2),
         "sd_over_ar": round((tok_sd / t_sd) / (tok_ar / t_ar), 4),
@@ -837,7 +846,9 @@ def sweep_line(args, shape, wts, stops):
                          "effective_percent": round(st["effective_percent"], 4)}
     cm = sw["cost"]
     out["controller"] = {"hbm_gbs": round(cm["hbm_bytes_per_s"] / 1e9, 1), "tflops": round(cm["flops_per_s"] / 1e12, 1),
-                         "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3)}
+                         "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3),
+                         "t_row_draft_us": round(cm["t_row_draft_s"] * 1e6, 2),
+                         "t_row_target_us": round(cm["t_row_target_s"] * 1e6, 2)}
     out["roofline_frac_timed"] = {m: round(sum(roof.step(x[1], x[2], x[0], x[6]) for x in recs[m]) /
                                            sum(x[4] for x in recs[m]), 4) for m, _ in SWEEP_MODES}
     out["prefill_s"] = round(sw["prefill_s"], 3)
@@ -951,7 +962,7 @@ def main():
                                 f"{'full rollout 256->1' if args.steps == 0 else f'first {args.steps} steps'}"),
                    "mode": "SD-auto (roofline toggle)" if "sd" in res else modes[0],
                    "global_batch": args.batch, "seq_len": args.prompt_len, "parallelism": "none (1 GPU)",
-                   "graphs": args.graphs},
+                   "graphs": args.graphs, "library_gemm_rows": args.library_gemm},
         "roofline": rf,
     }
     if "ar" in res and main_run is not res["ar"]:
@@ -973,7 +984,9 @@ def main():
                          "effective_percent": round(st["effective_percent"], 4)}
     cm = eng.cost_model()
     out["controller"] = {"hbm_gbs": round(cm["hbm_bytes_per_s"] / 1e9, 1), "tflops": round(cm["flops_per_s"] / 1e12, 1),
-                         "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3)}
+                         "t_fwd_ms": round(cm["t_fwd_s"] * 1e3, 3),
+                         "t_row_draft_us": round(cm["t_row_draft_s"] * 1e6, 2),
+                         "t_row_target_us": round(cm["t_row_target_s"] * 1e6, 2)}
     out["prefill_s"] = round(main_run["prefill_s"], 3)
     roof = Roofline(shape)
     out["by_batch"] = {m: bins(r["recs"], roof) for m, r in res.items()}

@@ -312,6 +312,19 @@ int er_set_decode_spin_limit(er_ctx *ctx, int64_t polls);
 int er_set_decode_trace(er_ctx *ctx, int on);
 int er_get_decode_trace(er_ctx *ctx, double *work_us, double *release_us, int max, int *n_out);
 
+/* Library GEMMs (bf16 models): the target's projections of at least
+ * min_rows rows run as hipBLASLt bf16 GEMMs with fp32 accumulation, their
+ * fused work around them as small kernels of this library (x' = RMSNorm(h) g
+ * formed once, RoPE and the KV append, SwiGLU, the residual added by the GEMM
+ * itself and the next norm's sums of squares).  The 18944-wide down
+ * projection of the 7B shape (K >= 8192) stays on this library's GEMM below
+ * 1024 rows, and steps recorded into graphs use this library's kernels only.
+ * Same arithmetic per element up to the order of the fp32 sums.  Default 128
+ * (from 128 rows the library's GEMM is 1.3-2.3x faster on MI355X); 0 = never.
+ * ER_ESTATE for min_rows > 0 where no library GEMM is available (fp32
+ * models). */
+int er_set_library_gemm(er_ctx *ctx, int min_rows);
+
 /* ---- bucketed graph capture ------------------------------------------------
  * TLT notes, section 3, Design A, A3: a range of batch sizes shares one set
  * of recorded graphs, and the drafter's graphs are recorded apart from the
@@ -441,6 +454,9 @@ typedef struct er_cost_model {
   int32_t n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   double w_bytes, q_bytes, kv_bytes_el;
   double hbm_bytes_per_s, flops_per_s, t_fwd_s;
+  /* time per row beyond the first that drafter / target forwards take beyond
+   * the roofline (0 unless measured at init, see er_controller_times) */
+  double t_row_draft_s, t_row_target_s;
 } er_cost_model;
 int er_controller_choose(const er_cost_model *m, int batch, double mean_ctx, double alpha,
                          int gamma_min, int gamma_max, int current, double margin, int *gamma_out);
@@ -452,7 +468,9 @@ int er_get_cost_model(const er_ctx *ctx, er_cost_model *out);
 /* Modelled step times of the controller (EfficientRollout "关键模块" item 2:
  * decode latency from a roofline, per-GPU constants): *t_ar = T(AR step),
  * *t_sd = gamma T(draft forward) + T(verify forward), each forward
- * T = t_fwd + max(bytes / hbm_bytes_per_s, flops / flops_per_s) with
+ * T = t_fwd + (rows - 1) t_row + max(bytes / hbm_bytes_per_s, flops / flops_per_s)
+ * (rows = B for AR and a draft forward, B (g+1) for the verify; t_row =
+ * t_row_draft_s for drafter forwards, t_row_target_s for the target's) with
  *   AR:     bytes = wb P + B C kvb + B kvb + 4 B V,   flops = 2 P B + 4 B C hq hd L
  *   draft:  bytes = bq P + B C kvb + B kvb + 4 B V,   flops = 2 P B + 4 B C hq hd L
  *   verify: bytes = wb P + B C kvb + B (g+1) kvb + 4 B (g+1) V,

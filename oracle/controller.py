@@ -23,7 +23,12 @@ Plain reading used here (the pages print no formula):
   E[n](alpha, gamma) = (1 - alpha^(gamma+1)) / (1 - alpha)  (tokens per SD step;
   gamma + 1 when alpha = 1).
 
-  Forward time T(bytes, flops) = t_fwd + max(bytes / BW, flops / FLOPS).
+  Forward time T(bytes, flops) = t_fwd + (rows - 1) * t_row + max(bytes / BW, flops / FLOPS),
+  rows = the forward's rows (B for AR and a draft forward, B*(g+1) for the
+  verify), t_row = t_row_draft for drafter forwards and t_row_target for the
+  target's.  t_fwd and the per-row terms are what the GPU's forwards take
+  beyond the roofline at 1 row and per further row (p1 "局限": calibrated per
+  GPU; measured at init from forwards of 1 and 16 rows); zero unless measured.
   AR step:    bytes = wb*P + B*C*kvb + B*kvb + B*V*4,  flops = 2*P*B + 4*B*C*hq*hd*L
   draft fwd:  bytes = bq*P + B*C*kvb + B*kvb + B*V*4,  flops = 2*P*B + 4*B*C*hq*hd*L
   verify fwd: bytes = wb*P + B*C*kvb + B*(g+1)*kvb + B*(g+1)*V*4,
@@ -77,6 +82,8 @@ class Roofline:
     bw: float = 8.0e12        # bytes/s
     flops: float = 2.5e15     # flop/s
     t_fwd: float = 0.0        # fixed seconds per forward (launch overhead)
+    t_row_draft: float = 0.0  # seconds per drafter-forward row beyond the first, beyond the roofline
+    t_row_target: float = 0.0 # seconds per target-forward row beyond the first, beyond the roofline
 
 
 def expected_tokens(alpha: float, gamma: int) -> float:
@@ -87,15 +94,15 @@ def expected_tokens(alpha: float, gamma: int) -> float:
     return (1.0 - alpha ** (gamma + 1)) / (1.0 - alpha)
 
 
-def fwd_time(r: Roofline, nbytes: float, nflops: float) -> float:
-    return r.t_fwd + max(nbytes / r.bw, nflops / r.flops)
+def fwd_time(r: Roofline, nbytes: float, nflops: float, extra: float = 0.0) -> float:
+    return r.t_fwd + extra + max(nbytes / r.bw, nflops / r.flops)
 
 
 def ar_time(m: ModelCost, r: Roofline, B: int, C: float) -> float:
     P, kvb = m.p_lin, m.kvb
     by = m.w_bytes * P + B * C * kvb + B * kvb + B * m.vocab * 4.0
     fl = 2.0 * P * B + 4.0 * B * C * m.n_q_heads * m.head_dim * m.n_layers
-    return fwd_time(r, by, fl)
+    return fwd_time(r, by, fl, r.t_row_target * (B - 1))
 
 
 def sd_time(m: ModelCost, r: Roofline, B: int, C: float, g: int) -> float:
@@ -105,7 +112,8 @@ def sd_time(m: ModelCost, r: Roofline, B: int, C: float, g: int) -> float:
     d_fl = 2.0 * P * B + B * att
     v_by = m.w_bytes * P + B * C * kvb + B * (g + 1) * kvb + B * (g + 1) * m.vocab * 4.0
     v_fl = 2.0 * P * B * (g + 1) + B * (g + 1) * att
-    return g * fwd_time(r, d_by, d_fl) + fwd_time(r, v_by, v_fl)
+    return (g * fwd_time(r, d_by, d_fl, r.t_row_draft * (B - 1)) +
+            fwd_time(r, v_by, v_fl, r.t_row_target * (B * (g + 1) - 1)))
 
 
 def score(m: ModelCost, r: Roofline, B: int, C: float, alpha: float, g: int) -> float:

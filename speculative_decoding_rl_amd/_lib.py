@@ -85,7 +85,8 @@ class CostModel(C.Structure):
     _fields_ = [("n_layers", C.c_int32), ("d_model", C.c_int32), ("n_q_heads", C.c_int32),
                 ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32), ("vocab", C.c_int32),
                 ("w_bytes", C.c_double), ("q_bytes", C.c_double), ("kv_bytes_el", C.c_double),
-                ("hbm_bytes_per_s", C.c_double), ("flops_per_s", C.c_double), ("t_fwd_s", C.c_double)]
+                ("hbm_bytes_per_s", C.c_double), ("flops_per_s", C.c_double), ("t_fwd_s", C.c_double),
+                ("t_row_draft_s", C.c_double), ("t_row_target_s", C.c_double)]
 
 
 class PlanState(C.Structure):
@@ -154,6 +155,7 @@ SIGNATURES = {
     "er_set_persistent": (C.c_int, [P, C.c_int]),
     "er_get_persistent": (C.c_int, [P, C.POINTER(C.c_int)]),
     "er_set_graphs": (C.c_int, [P, C.c_int]),
+    "er_set_library_gemm": (C.c_int, [P, C.c_int]),
     "er_get_graph_stats": (C.c_int, [P, C.POINTER(GraphStats)]),
     "er_set_decode_spin_limit": (C.c_int, [P, C.c_int64]),
     "er_set_decode_trace": (C.c_int, [P, C.c_int]),

@@ -408,11 +408,12 @@ struct Layout {
   size_t drafter = 0, cs = 0, h = 0, xbuf = 0, qkv = 0, qb = 0, gu = 0, lp = 0, lq = 0, sp = 0, sq = 0;
   size_t out = 0, partial = 0, counters = 0, attn = 0, w4tmp = 0, sink = 0, meta = 0, resid = 0, ssq = 0, xn = 0;
   size_t dec = 0;  // persistent decode forward: layer descriptors, sums of squares, counters, barrier
+  size_t blas = 0; // library GEMM workspace (bf16 models)
   size_t block_bytes = 0;
   int max_rows = 0, logit_rows = 0;
   size_t total_fixed() const {
     return drafter + cs + h + xbuf + qkv + qb + gu + lp + lq + sp + sq + out + partial + counters + attn + w4tmp +
-           sink + meta + resid + ssq + xn + dec;
+           sink + meta + resid + ssq + xn + dec + blas;
   }
 };
 
@@ -474,6 +475,7 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
              align256((size_t)kDecodeBarWords * 4) + 256;
   }
   L->meta = align256((size_t)64 << 20);
+  if (m.dtype == ER_BF16) L->blas = (size_t)32 << 20;
   L->block_bytes = (size_t)m.n_layers * 2 * hkv * KV_BLOCK * hd * ab;
   (void)why;
   return 0;
@@ -1588,78 +1590,103 @@ int calibrate(er_ctx* c) {
     }
   }
   if (c->rd.t_fwd_s < 0 && c->pool.free_count() >= 1) {
-    // one scratch block: run both forwards at position 0 of a throwaway sequence
+    // One scratch block: forwards of `rows` rows, every row at position 0 of
+    // the block (each writes and reads that one key), timed after a warm one.
+    // The target's and the drafter's forwards at 1 row give the fixed time
+    // per forward beyond the roofline, at Mr rows the time per further row
+    // (the kernels read the same bytes more slowly as rows are added:
+    // dequantizing linears past 8 rows, more attention items).
     BlockTable bt;
     if (!bt.reserve(c->pool, 1)) return ER_OK;
-    Meta& M = c->meta;
-    if (int r_ = meta_begin(c)) { bt.release(c->pool); return r_; }
-    size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ic;
-    int32_t* t = M.push<int32_t>(1, &o_tok);
-    int32_t* p = M.push<int32_t>(1, &o_pos);
-    int64_t* s = M.push<int64_t>(1, &o_slot);
-    int32_t* btp = M.push<int32_t>(1, &o_bt);
-    int32_t* ib = M.push<int32_t>(1, &o_ib);
-    int32_t* ir = M.push<int32_t>(1, &o_ir);
-    int32_t* ic = M.push<int32_t>(1, &o_ic);
-    *t = 0; *p = 0; *s = (int64_t)bt.blocks[0] * KV_BLOCK; *btp = bt.blocks[0]; *ib = 0; *ir = 0; *ic = 1;
-    int nu1 = 0, ns1 = 0, mu1 = 0;
-    size_t o_rec1 = 0;
-    const size_t o_us1 = push_units(M, 1, (int)m.n_kv_heads, p, ic, ir, ib, &nu1, &ns1, &mu1, &o_rec1);
-    if (!M.ok) { bt.release(c->pool); return fail(c, ER_ENOMEM, "metadata region too small"); }
-    if (int r_ = meta_upload(c)) return r_;
-    Fwd f;
-    f.M = 1;
-    f.tokens = M.dev<int32_t>(o_tok);
-    f.pos = M.dev<int32_t>(o_pos);
-    f.slot = M.dev<int64_t>(o_slot);
-    f.bt = M.dev<int32_t>(o_bt);
-    f.bt_stride = 1;
-    f.it_bt = M.dev<int32_t>(o_ib);
-    f.it_row0 = M.dev<int32_t>(o_ir);
-    f.it_pos0 = M.dev<int32_t>(o_pos);
-    f.it_cnt = M.dev<int32_t>(o_ic);
-    f.n_items = 1;
-    f.max_q = 1;
-    f.max_ctx = 1;
-    f.unit_start = M.dev<int32_t>(o_us1);
-    f.unit_rec = M.dev<int32_t>(o_rec1);
-    f.n_units = nu1;
-    f.n_split = ns1;
-    f.max_units = mu1;
-    f.kv_keys = 1;
-    f.dec_ok = true;  // time the forward the decode steps run
-    f.logits = c->logits_p;
-    f.ldl = m.vocab;
-    float times[2] = {0, 0};
-    hipEvent_t a, b;
-    HIPC(c, hipEventCreate(&a));
-    HIPC(c, hipEventCreate(&b));
-    for (int which = 0; which < 2; ++which) {
-      f.draft = which == 1;
-      int r = forward(c, f);  // warm
-      if (r) { bt.release(c->pool); return r; }
-      HIPC(c, hipEventRecord(a, c->st));
-      for (int i = 0; i < 3; ++i) {
-        r = forward(c, f);
-        if (r) { bt.release(c->pool); return r; }
+    auto time_fwd = [&](int rows, bool draft, double* sec) -> int {
+      Meta& M = c->meta;
+      if (int r_ = meta_begin(c)) return r_;
+      size_t o_tok, o_pos, o_slot, o_bt, o_ib, o_ir, o_ic;
+      int32_t* t = M.push<int32_t>(rows, &o_tok);
+      int32_t* p = M.push<int32_t>(rows, &o_pos);
+      int64_t* s = M.push<int64_t>(rows, &o_slot);
+      int32_t* btp = M.push<int32_t>(1, &o_bt);
+      int32_t* ib = M.push<int32_t>(rows, &o_ib);
+      int32_t* ir = M.push<int32_t>(rows, &o_ir);
+      int32_t* ic = M.push<int32_t>(rows, &o_ic);
+      if (!M.ok) return fail(c, ER_ENOMEM, "metadata region too small");
+      for (int i = 0; i < rows; ++i) {
+        t[i] = 0;
+        p[i] = 0;
+        s[i] = (int64_t)bt.blocks[0] * KV_BLOCK;
+        ib[i] = 0;
+        ir[i] = i;
+        ic[i] = 1;
       }
-      HIPC(c, hipEventRecord(b, c->st));
-      HIPC(c, hipEventSynchronize(b));
+      *btp = bt.blocks[0];
+      int nu = 0, ns = 0, mu = 0;
+      size_t o_rec = 0;
+      const size_t o_us = push_units(M, rows, (int)m.n_kv_heads, p, ic, ir, ib, &nu, &ns, &mu, &o_rec);
+      if (!M.ok) return fail(c, ER_ENOMEM, "metadata region too small");
+      if (int r_ = meta_upload(c)) return r_;
+      Fwd f;
+      f.draft = draft;
+      f.M = rows;
+      f.tokens = M.dev<int32_t>(o_tok);
+      f.pos = M.dev<int32_t>(o_pos);
+      f.slot = M.dev<int64_t>(o_slot);
+      f.bt = M.dev<int32_t>(o_bt);
+      f.bt_stride = 1;
+      f.it_bt = M.dev<int32_t>(o_ib);
+      f.it_row0 = M.dev<int32_t>(o_ir);
+      f.it_pos0 = M.dev<int32_t>(o_pos);
+      f.it_cnt = M.dev<int32_t>(o_ic);
+      f.n_items = rows;
+      f.max_q = 1;
+      f.max_ctx = 1;
+      f.unit_start = M.dev<int32_t>(o_us);
+      f.unit_rec = M.dev<int32_t>(o_rec);
+      f.n_units = nu;
+      f.n_split = ns;
+      f.max_units = mu;
+      f.kv_keys = rows;
+      f.dec_ok = true;  // time the forward the decode steps run
+      f.logits = c->logits_p;
+      f.ldl = m.vocab;
+      int r = forward(c, f);  // warm
+      if (r) return r;
+      hipEvent_t a, b;
+      HIPC(c, hipEventCreate(&a));
+      HIPC(c, hipEventCreate(&b));
+      HIPC(c, hipEventRecord(a, c->st));
+      for (int i = 0; i < 3 && r == ER_OK; ++i) r = forward(c, f);
+      if (r == ER_OK) {
+        HIPC(c, hipEventRecord(b, c->st));
+        HIPC(c, hipEventSynchronize(b));
+      }
       float ms = 0.f;
-      HIPC(c, hipEventElapsedTime(&ms, a, b));
-      times[which] = ms / 3.0f * 1e-3f;
-    }
-    (void)hipEventDestroy(a);
-    (void)hipEventDestroy(b);
+      if (r == ER_OK) HIPC(c, hipEventElapsedTime(&ms, a, b));
+      (void)hipEventDestroy(a);
+      (void)hipEventDestroy(b);
+      *sec = ms / 3.0 * 1e-3;
+      return r;
+    };
+    const int Mr = std::min({16, c->rd.max_batch, c->max_rows, c->logit_rows});
+    double t1[2] = {0, 0}, tr[2] = {0, 0};
+    int r = ER_OK;
+    for (int which = 0; which < 2 && r == ER_OK; ++which) r = time_fwd(1, which == 1, &t1[which]);
+    for (int which = 0; which < 2 && r == ER_OK && Mr >= 2; ++which) r = time_fwd(Mr, which == 1, &tr[which]);
     bt.release(c->pool);
+    if (r) return r;
     if (c->dec_ran) {
       HIPC(c, hipMemcpy(c->out_h + c->dec_err_slot, c->dec_err, 4, hipMemcpyDeviceToHost));
       if (int r_ = dec_check(c)) return r_;
     }
-    const double P = c->cost.p_lin();
-    const double tt = times[0] - c->cost.w_bytes * P / c->cost.bw;
-    const double td = times[1] - c->cost.q_bytes * P / c->cost.bw;
-    c->cost.t_fwd = std::max(0.0, 0.5 * (tt + td));
+    const double P = c->cost.p_lin(), kvb = c->cost.kvb(), V = m.vocab;
+    auto roof = [&](double wb, int rows) {
+      return std::max((wb * P + rows * kvb + 4.0 * rows * V) / c->cost.bw, 2.0 * P * rows / c->cost.flops);
+    };
+    const double rt = t1[0] - roof(c->cost.w_bytes, 1), rd = t1[1] - roof(c->cost.q_bytes, 1);
+    c->cost.t_fwd = std::max(0.0, 0.5 * (rt + rd));
+    if (Mr >= 2) {
+      c->cost.t_row_target = std::max(0.0, (tr[0] - roof(c->cost.w_bytes, Mr) - rt) / (Mr - 1));
+      c->cost.t_row_draft = std::max(0.0, (tr[1] - roof(c->cost.q_bytes, Mr) - rd) / (Mr - 1));
+    }
   }
   if (c->rd.flops_per_s <= 0) {
     // Dense-contraction rate the kernels reach: a target forward over Mc
@@ -1842,6 +1869,14 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->sink = (uint32_t*)take(L.sink);
     c->meta.d = take(L.meta);
     c->meta.cap = L.meta;
+    if (L.blas) {
+      // library GEMMs for the target's projections from 128 rows (er_set_library_gemm)
+      char* bw = take(L.blas);
+      c->lws.blas = blas_create(bw, L.blas);
+      c->lws.blas_min_m = 128;
+      c->lws.blas_out = c->gu;
+      c->lws.blas_out_floats = L.gu / 4;
+    }
     if (L.dec) {
       char* d0 = take(L.dec);
       char* dc = d0;
@@ -2486,6 +2521,13 @@ int er_set_graphs(er_ctx* c, int max_batch) {
   }
 }
 
+int er_set_library_gemm(er_ctx* c, int min_rows) {
+  if (!c || min_rows < 0) return ER_EINVAL;
+  if (min_rows > 0 && !c->lws.blas) return fail(c, ER_ESTATE, "no library GEMM here (fp32 model or hipBLASLt unavailable)");
+  c->lws.blas_min_m = min_rows > 0 ? min_rows : INT32_MAX;
+  return ER_OK;
+}
+
 int er_get_graph_stats(const er_ctx* c, er_graph_stats* out) {
   if (!c || !out) return ER_EINVAL;
   out->max_batch = c->graph_max;
@@ -2804,7 +2846,8 @@ int er_get_guard(const er_ctx* c, er_guard_state* out) {
 
 static CostModel cost_of(const er_cost_model* m) {
   return CostModel{m->n_layers, m->d_model, m->n_q_heads, m->n_kv_heads, m->head_dim, m->ffn, m->vocab,
-                   m->w_bytes, m->q_bytes, m->kv_bytes_el, m->hbm_bytes_per_s, m->flops_per_s, m->t_fwd_s};
+                   m->w_bytes, m->q_bytes, m->kv_bytes_el, m->hbm_bytes_per_s, m->flops_per_s, m->t_fwd_s,
+                   m->t_row_draft_s, m->t_row_target_s};
 }
 
 int er_controller_choose(const er_cost_model* m, int batch, double mean_ctx, double alpha, int gamma_min,
@@ -2854,7 +2897,7 @@ int er_get_cost_model(const er_ctx* c, er_cost_model* out) {
   if (!c || !out) return ER_EINVAL;
   const CostModel& m = c->cost;
   *out = er_cost_model{m.n_layers, m.d_model, m.n_q_heads, m.n_kv_heads, m.head_dim, m.ffn, m.vocab,
-                       m.w_bytes, m.q_bytes, m.kv_bytes_el, m.bw, m.flops, m.t_fwd};
+                       m.w_bytes, m.q_bytes, m.kv_bytes_el, m.bw, m.flops, m.t_fwd, m.t_row_draft, m.t_row_target};
   return ER_OK;
 }
 
@@ -2866,6 +2909,7 @@ void er_destroy(er_ctx* c) {
   else (void)hipDeviceSynchronize();
   graph_drop(c);
   if (c->cap_st) (void)hipStreamDestroy(c->cap_st);
+  blas_destroy(c->lws.blas);
   if (c->meta.h) (void)hipHostFree(c->meta.h);
   if (c->out_h) (void)hipHostFree(c->out_h);
   if (c->dec_trace) (void)hipFree(c->dec_trace);

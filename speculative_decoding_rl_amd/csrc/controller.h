@@ -12,7 +12,9 @@
 // Model (gamma = 0 is autoregressive decoding, so one argmax covers the toggle
 // and the draft length):
 //   E[n](a, g)   = (1 - a^(g+1)) / (1 - a)
-//   T(bytes, fl) = t_fwd + max(bytes / BW, fl / FLOPS)
+//   T(bytes, fl) = t_fwd + (rows - 1) t_row + max(bytes / BW, fl / FLOPS),
+//   rows = B (AR, draft) or B (g+1) (verify), t_row = t_row_draft / t_row_target:
+//   what the GPU's forwards take beyond the roofline per further row
 //   AR:     bytes = wb P + B C kvb + B kvb + 4 B V,   fl = 2 P B + 4 B C hq hd L
 //   draft:  bytes = bq P + B C kvb + B kvb + 4 B V,   fl = 2 P B + 4 B C hq hd L
 //   verify: bytes = wb P + B C kvb + B (g+1) kvb + 4 B (g+1) V,
@@ -31,6 +33,7 @@ struct CostModel {
   int n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
   double w_bytes, q_bytes, kv_bytes_el;
   double bw, flops, t_fwd;
+  double t_row_draft = 0.0, t_row_target = 0.0;
 
   double p_lin() const {
     const double d = d_model, hq = n_q_heads, hkv = n_kv_heads, hd = head_dim, F = ffn;
@@ -46,15 +49,15 @@ inline double expected_tokens(double alpha, int gamma) {
   return (1.0 - std::pow(alpha, gamma + 1)) / (1.0 - alpha);
 }
 
-inline double fwd_time(const CostModel& m, double bytes, double fl) {
-  return m.t_fwd + std::max(bytes / m.bw, fl / m.flops);
+inline double fwd_time(const CostModel& m, double bytes, double fl, double extra) {
+  return m.t_fwd + extra + std::max(bytes / m.bw, fl / m.flops);
 }
 
 inline double ar_time(const CostModel& m, int B, double C) {
   const double P = m.p_lin(), kvb = m.kvb();
   const double by = m.w_bytes * P + B * C * kvb + B * kvb + (double)B * m.vocab * 4.0;
   const double fl = 2.0 * P * B + 4.0 * B * C * m.n_q_heads * m.head_dim * m.n_layers;
-  return fwd_time(m, by, fl);
+  return fwd_time(m, by, fl, m.t_row_target * (B - 1));
 }
 
 inline double sd_time(const CostModel& m, int B, double C, int g) {
@@ -64,7 +67,8 @@ inline double sd_time(const CostModel& m, int B, double C, int g) {
   const double d_fl = 2.0 * P * B + B * att;
   const double v_by = m.w_bytes * P + B * C * kvb + (double)B * (g + 1) * kvb + (double)B * (g + 1) * m.vocab * 4.0;
   const double v_fl = 2.0 * P * B * (g + 1) + (double)B * (g + 1) * att;
-  return g * fwd_time(m, d_by, d_fl) + fwd_time(m, v_by, v_fl);
+  return g * fwd_time(m, d_by, d_fl, m.t_row_draft * (B - 1)) +
+         fwd_time(m, v_by, v_fl, m.t_row_target * ((double)B * (g + 1) - 1));
 }
 
 inline double score(const CostModel& m, int B, double C, double alpha, int g) {

@@ -1760,6 +1760,104 @@ __global__ __launch_bounds__(256) void k_xnorm(LinArgs a, uint16_t* __restrict__
   *(uint4*)(xn + (long)m * K + k0) = o;
 }
 
+// After a library GEMM that added x W^T into h: each row's sum of squares
+// into slot 0 of ssq_acc (partial sums of 256 threads, each converted to
+// fixed point, added as integers, so the total does not depend on the order)
+// and the consumed buffer ssq_zero cleared for the rows, as the fused
+// residual epilogues do.
+__global__ __launch_bounds__(256) void k_resid_ssq(LinArgs a) {
+  const int m = blockIdx.x, tid = threadIdx.x;
+  if (a.ssq_zero && tid < ssq_nslots(a)) a.ssq_zero[(long)tid * a.ssq_stride + m] = 0ull;
+  if (!a.ssq_acc) return;
+  const float* h = (const float*)a.y + (long)m * a.ldy;
+  float sq = 0.f;
+  for (int k = tid * 4; k < a.W.N; k += 256 * 4) {
+    const float4 v = *(const float4*)(h + k);
+    sq = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, sq))));
+  }
+  unsigned long long t = (unsigned long long)rint((double)sq * SSQ_SCALE);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o, 64);
+  __shared__ unsigned long long part[4];
+  if ((tid & 63) == 0) part[tid >> 6] = t;
+  __syncthreads();
+  if (tid == 0) atomicAdd(a.ssq_acc + m, part[0] + part[1] + part[2] + part[3]);
+}
+
+// Large-M bf16 projections through the library GEMM (blas.hip), with the
+// epilogue as its own kernel: x' formed once (k_xnorm) when normalizing on
+// load; QKV and gate/up land in fp32 in ws.blas_out for RoPE + the KV append
+// and SwiGLU; the residual projections add into h (beta = 1) and then sum its
+// squares; logits are written directly.  Returns 1 when the case does not
+// apply (the hand-written kernels run): below blas_min_m rows, the long-K
+// down projection below 1024 rows (where the hand-written GEMM is faster),
+// gathered rows without the norm, or while the stream is being captured
+// (recorded graphs hold the hand-written kernels only).
+static int run_blas(const LinArgs& a, const LinearWs& ws, hipStream_t st, LinearInfo* info) {
+  const int M = a.M, N = a.W.N, K = a.W.K;
+  if (!ws.blas || a.W.fmt != FMT_BF16 || !a.act_bf16 || M < ws.blas_min_m) return 1;
+  if (K >= 8192 && M < 1024) return 1;
+  if (!a.xnorm && a.xrow) return 1;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return 1;
+  float* out = nullptr;
+  int ldo = 0;
+  float beta = 0.f;
+  const char* what = nullptr;
+  switch (a.epi) {
+    case EPI_F32:
+      if (a.ssq_zero || a.ssq_acc) return 1;
+      out = (float*)a.y;
+      ldo = a.ldy;
+      what = "logits";
+      break;
+    case EPI_RESID:
+      out = (float*)a.y;
+      ldo = a.ldy;
+      beta = 1.f;
+      what = "residual";
+      if (a.ldy % 4 != 0 || N % 4 != 0) return 1;
+      break;
+    case EPI_QKV:
+    case EPI_SWIGLU:
+      if (a.ssq_zero || a.ssq_acc || !ws.blas_out || (size_t)M * N > ws.blas_out_floats) return 1;
+      if (a.epi == EPI_SWIGLU && a.ldy != a.F) return 1;
+      out = ws.blas_out;
+      ldo = N;
+      what = a.epi == EPI_QKV ? "rope_kv" : "swiglu";
+      break;
+    default:
+      return 1;
+  }
+  const void* x = a.x;
+  int ldx = a.ldx;
+  if (a.xnorm) {
+    if (!ws.xn || (size_t)M * K > ws.xn_elems) return 1;
+    hipLaunchKernelGGL(k_xnorm, dim3(M, (K + 2047) / 2048), dim3(256), 0, st, a, ws.xn);
+    if (hipGetLastError() != hipSuccess) return -3;
+    x = ws.xn;
+    ldx = K;
+  }
+  const int r = blas_gemm(ws.blas, x, ldx, M, a.W.w, N, K, out, ldo, true, beta, st);
+  if (r != 0) return r;  // 1: no algorithm for the shape, the hand-written kernels run
+  int e = 0;
+  if (a.epi == EPI_QKV)
+    e = launch_rope_kv(ws.blas_out, M, a.hq, a.hkv, a.hd, a.pos, a.slot, a.cs, a.qout, a.kv_pool, a.layer,
+                       a.n_layers, true, st);
+  else if (a.epi == EPI_SWIGLU)
+    e = launch_swiglu(ws.blas_out, M, a.F, a.y, true, st);
+  else if (a.epi == EPI_RESID && (a.ssq_acc || a.ssq_zero)) {
+    hipLaunchKernelGGL(k_resid_ssq, dim3(M), dim3(256), 0, st, a);
+    e = hipGetLastError() == hipSuccess ? 0 : -3;
+  }
+  if (e) return e;
+  if (info) {
+    snprintf(info->name, sizeof info->name, "hipblaslt::gemm_bf16+%s", what);
+    info->nsplit = 1;
+  }
+  return 0;
+}
+
 int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStream_t st, LinearInfo* info) {
   if (a.M <= 0 || a.W.N <= 0) return 0;
   if (a.ssq_slots > kMaxSsqSlots || (a.ssq_slots > 1 && a.ssq_stride < a.M)) return -1;
@@ -1769,6 +1867,10 @@ int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStrea
     return -1;
   if (a.epi == EPI_SWIGLU && a.F % 8 != 0) return -1;
   const bool gemm_ok = a.W.fmt == FMT_BF16 && a.W.K % GB_K == 0 && ws.partial != nullptr;
+  if (path == 0) {
+    const int r = run_blas(a, ws, st, info);
+    if (r != 1) return r;
+  }
   if (path == 3) {
     if (!gemm_ok) return -1;
     return run_gemm(a, ws, st, info);

@@ -70,6 +70,16 @@ struct LinArgs {
   int F;
 };
 
+// Plain bf16 GEMMs through hipBLASLt (blas.hip): y = beta * y + x W^T, x
+// [M][ldx] bf16, W [N][K] bf16, y [M][ldy] fp32 (out32) or bf16.  Returns 0,
+// 1 when the library has no algorithm for the shape (nothing launched), or a
+// negative error.
+struct Blas;
+Blas* blas_create(void* workspace, size_t ws_bytes);
+void blas_destroy(Blas* b);
+int blas_gemm(Blas* b, const void* x, int ldx, int M, const void* W, int N, int K, void* y, int ldy, bool out32,
+              float beta, hipStream_t st);
+
 struct LinearWs {
   float* partial;     // split-K partial tiles
   size_t partial_floats;
@@ -77,6 +87,13 @@ struct LinearWs {
   int n_counters;
   uint16_t* xn;       // bf16 x' for kernels that do not normalize on load (nullable)
   size_t xn_elems;
+  // Library GEMMs for bf16 weights from blas_min_m rows (nullable = never):
+  // the fp32 result of the QKV and gate/up projections goes to blas_out
+  // before its epilogue kernel.
+  Blas* blas;
+  int blas_min_m;
+  float* blas_out;
+  size_t blas_out_floats;
 };
 
 // What a launch_linear call ran (for per-kernel timing): kernel name as the

@@ -229,6 +229,10 @@ class Engine:
         """Replay recorded graphs for steps of at most max_batch sequences (0: off, the default)."""
         check(self.lib.er_set_graphs(self.ctx, int(max_batch)), self.ctx, "er_set_graphs")
 
+    def set_library_gemm(self, min_rows: int):
+        """Run the target's projections of >= min_rows rows as hipBLASLt GEMMs (default 128; 0: never)."""
+        check(self.lib.er_set_library_gemm(self.ctx, int(min_rows)), self.ctx, "er_set_library_gemm")
+
     def graph_stats(self) -> dict:
         g = _lib.GraphStats()
         check(self.lib.er_get_graph_stats(self.ctx, C.byref(g)), self.ctx, "er_get_graph_stats")

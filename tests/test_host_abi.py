@@ -46,7 +46,7 @@ def _cost(shape_q=0.5 + 3 / 128):
     # Qwen2.5-7B-shaped constants
     return dict(n_layers=28, d_model=3584, n_q_heads=28, n_kv_heads=4, head_dim=128, ffn=18944, vocab=152064,
                 w_bytes=2.0, q_bytes=shape_q, kv_bytes_el=2.0, hbm_bytes_per_s=6.4e12, flops_per_s=2.5e15,
-                t_fwd_s=4.0e-4)
+                t_fwd_s=4.0e-4, t_row_draft_s=3.0e-5, t_row_target_s=1.0e-5)
 
 
 @pytest.mark.parametrize("B,C,alpha,cur", [(1, 600, 0.55, -1), (1, 600, 0.9, -1), (4, 2000, 0.8, 0),
@@ -57,7 +57,7 @@ def test_controller_choice_matches_oracle(lib, B, C, alpha, cur):
     c = _cost()
     m = OC.ModelCost(c["n_layers"], c["d_model"], c["n_q_heads"], c["n_kv_heads"], c["head_dim"], c["ffn"],
                      c["vocab"], c["w_bytes"], c["q_bytes"], c["kv_bytes_el"])
-    r = OC.Roofline(c["hbm_bytes_per_s"], c["flops_per_s"], c["t_fwd_s"])
+    r = OC.Roofline(c["hbm_bytes_per_s"], c["flops_per_s"], c["t_fwd_s"], c["t_row_draft_s"], c["t_row_target_s"])
     want = OC.choose(m, r, B, C, alpha, 1, 8, current=cur, margin=1.02)
     assert controller_choose(c, B, C, alpha, 1, 8, current=cur, margin=1.02) == want
 
@@ -129,20 +129,21 @@ def test_work_unit_split_under_sanitizers(tmp_path):
     assert r.returncode == 0 and "work_units ok" in r.stdout, r.stdout + r.stderr
 
 
-def _toy_cost(bw, flops, t_fwd, q_bytes=1.0):
+def _toy_cost(bw, flops, t_fwd, t_row_draft=0.0, t_row_target=0.0, q_bytes=1.0):
     return dict(n_layers=1, d_model=2, n_q_heads=1, n_kv_heads=1, head_dim=2, ffn=1, vocab=3, w_bytes=2.0,
-                q_bytes=q_bytes, kv_bytes_el=2.0, hbm_bytes_per_s=bw, flops_per_s=flops, t_fwd_s=t_fwd)
+                q_bytes=q_bytes, kv_bytes_el=2.0, hbm_bytes_per_s=bw, flops_per_s=flops, t_fwd_s=t_fwd,
+                t_row_draft_s=t_row_draft, t_row_target_s=t_row_target)
 
 
 def test_controller_times_at_hand_computed_points(lib):
     # the worked toy points of tests/test_oracle_controller.py (TOY_TIMES), evaluated by the library
     from speculative_decoding_rl_amd.rollout import controller_times
     from tests.test_oracle_controller import TOY_TIMES
-    for (bw, fl, tf), (t_ar, t_sd) in TOY_TIMES:
-        a, s = controller_times(_toy_cost(bw, fl, tf), 2, 5.0, 2)
+    for (bw, fl, tf, trd, trt), (t_ar, t_sd) in TOY_TIMES:
+        a, s = controller_times(_toy_cost(bw, fl, tf, trd, trt), 2, 5.0, 2)
         assert a == pytest.approx(t_ar, rel=1e-12) and s == pytest.approx(t_sd, rel=1e-12)
     # gamma 1 with the cheap drafter: 122.8 + 216
-    assert controller_times(_toy_cost(1.0, 1e30, 0.0, 0.1), 2, 5.0, 1)[1] == pytest.approx(338.8, rel=1e-12)
+    assert controller_times(_toy_cost(1.0, 1e30, 0.0, q_bytes=0.1), 2, 5.0, 1)[1] == pytest.approx(338.8, rel=1e-12)
 
 
 def test_controller_times_reject_bad_arguments(lib):
@@ -164,7 +165,7 @@ def test_controller_plan_matches_oracle_over_scripted_streams(lib, seed):
     c = _cost()
     m = OC.ModelCost(c["n_layers"], c["d_model"], c["n_q_heads"], c["n_kv_heads"], c["head_dim"], c["ffn"],
                      c["vocab"], c["w_bytes"], c["q_bytes"], c["kv_bytes_el"])
-    r = OC.Roofline(c["hbm_bytes_per_s"], c["flops_per_s"], c["t_fwd_s"])
+    r = OC.Roofline(c["hbm_bytes_per_s"], c["flops_per_s"], c["t_fwd_s"], c["t_row_draft_s"], c["t_row_target_s"])
     rng = np.random.Generator(np.random.PCG64(seed))
     ost = OC.PlanState()
     lst = dict(choice=-1, ar_streak=0, probe_every=0)

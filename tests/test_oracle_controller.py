@@ -101,12 +101,15 @@ def toy_cost():
                        w_bytes=2.0, q_bytes=1.0, kv_bytes_el=2.0)
 
 
-# (bw, flops, t_fwd) -> (AR step, SD step at gamma 2), worked by hand from the table above
+# (bw, flops, t_fwd, t_row_draft, t_row_target) -> (AR step, SD step at gamma 2), worked by hand from the
+# table above (B = 2: the AR and draft forwards have 2 rows, 1 beyond the first; the verify has 6, 5 beyond)
 TOY_TIMES = [
-    ((1.0, 1e30, 0.0), (176.0, 2 * 148.0 + 256.0)),               # bytes-bound: 176, 552
-    ((1e30, 1.0, 0.0), (192.0, 2 * 192.0 + 576.0)),               # flop-bound: 192, 960
-    ((1.0, 1e30, 0.5), (176.5, 2 * 148.5 + 256.5)),               # fixed time per forward: 176.5, 553.5
-    ((1.0, 1.5, 0.0), (176.0, 2 * max(148.0, 128.0) + 384.0)),    # the max is per forward: 176, 680
+    ((1.0, 1e30, 0.0, 0.0, 0.0), (176.0, 2 * 148.0 + 256.0)),               # bytes-bound: 176, 552
+    ((1e30, 1.0, 0.0, 0.0, 0.0), (192.0, 2 * 192.0 + 576.0)),               # flop-bound: 192, 960
+    ((1.0, 1e30, 0.5, 0.0, 0.0), (176.5, 2 * 148.5 + 256.5)),               # fixed time per forward: 176.5, 553.5
+    ((1.0, 1.5, 0.0, 0.0, 0.0), (176.0, 2 * max(148.0, 128.0) + 384.0)),    # the max is per forward: 176, 680
+    # per-row terms: AR 176 + 1 * 0.125; SD 2 * (148 + 1 * 0.25) + 256 + 5 * 0.125 = 553.125
+    ((1.0, 1e30, 0.0, 0.25, 0.125), (176.125, 553.125)),
 ]
 
 
