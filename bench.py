@@ -86,8 +86,9 @@ def parse():
     ap.add_argument("--no-kernel-profile", action="store_true")
     ap.add_argument("--persistent", action="store_true",
                     help="run forwards of <= 16 rows as the persistent decode kernel (default: kernel sequence)")
-    ap.add_argument("--library-gemm", type=int, default=128,
-                    help="run the target's projections of at least this many rows as library GEMMs (0: never)")
+    ap.add_argument("--library-gemm", type=int, default=-1,
+                    help="library GEMMs for the target's projections: -1 from each shape's measured row threshold, "
+                         "N > 0 from N rows for every shape, 0 never")
     ap.add_argument("--graphs", type=int, default=16,
                     help="replay recorded graphs for steps of at most this many sequences (0: every step eager)")
     ap.add_argument("--kprof-every", type=int, default=4,
@@ -115,7 +116,7 @@ def engine_options(eng, args):
         eng.set_persistent(True)
     if args.graphs:
         eng.set_graphs(args.graphs)
-    if args.library_gemm != 128 and shape_is_bf16(eng):
+    if args.library_gemm != -1 and shape_is_bf16(eng):
         eng.set_library_gemm(args.library_gemm)
 
 

@@ -312,17 +312,18 @@ int er_set_decode_spin_limit(er_ctx *ctx, int64_t polls);
 int er_set_decode_trace(er_ctx *ctx, int on);
 int er_get_decode_trace(er_ctx *ctx, double *work_us, double *release_us, int max, int *n_out);
 
-/* Library GEMMs (bf16 models): the target's projections of at least
- * min_rows rows run as hipBLASLt bf16 GEMMs with fp32 accumulation, their
- * fused work around them as small kernels of this library (x' = RMSNorm(h) g
- * formed once, RoPE and the KV append, SwiGLU, the residual added by the GEMM
- * itself and the next norm's sums of squares).  The 18944-wide down
- * projection of the 7B shape (K >= 8192) stays on this library's GEMM below
- * 1024 rows, and steps recorded into graphs use this library's kernels only.
- * Same arithmetic per element up to the order of the fp32 sums.  Default 128
- * (from 128 rows the library's GEMM is 1.3-2.3x faster on MI355X); 0 = never.
- * ER_ESTATE for min_rows > 0 where no library GEMM is available (fp32
- * models). */
+/* Library GEMMs (bf16 models): the target's projections run as hipBLASLt
+ * bf16 GEMMs with fp32 accumulation, their fused work around them as small
+ * kernels of this library (x' = RMSNorm(h) g formed once, RoPE and the KV
+ * append, SwiGLU, the residual added by the GEMM itself and the next norm's
+ * sums of squares), from a row count that depends on the shape.  min_rows =
+ * -1 (the default): each shape from the rows where the library's GEMM was
+ * measured faster on MI355X (output width >= 16384: 16 rows; >= 65536: 48;
+ * >= 4096: 80; narrower: 160; K >= 8192: 1024); > 0: every shape from that
+ * many rows (K >= 8192 still from 1024); 0: never.  Steps recorded into
+ * graphs use this library's kernels only.  Same arithmetic per element up to
+ * the order of the fp32 sums.  ER_EINVAL for min_rows < -1; ER_ESTATE for
+ * min_rows != 0 where no library GEMM is available (fp32 models). */
 int er_set_library_gemm(er_ctx *ctx, int min_rows);
 
 /* ---- bucketed graph capture ------------------------------------------------

@@ -1870,10 +1870,10 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     c->meta.d = take(L.meta);
     c->meta.cap = L.meta;
     if (L.blas) {
-      // library GEMMs for the target's projections from 128 rows (er_set_library_gemm)
+      // library GEMMs for the target's projections from each shape's row threshold (er_set_library_gemm)
       char* bw = take(L.blas);
       c->lws.blas = blas_create(bw, L.blas);
-      c->lws.blas_min_m = 128;
+      c->lws.blas_min_m = -1;
       c->lws.blas_out = c->gu;
       c->lws.blas_out_floats = L.gu / 4;
     }
@@ -2522,9 +2522,9 @@ int er_set_graphs(er_ctx* c, int max_batch) {
 }
 
 int er_set_library_gemm(er_ctx* c, int min_rows) {
-  if (!c || min_rows < 0) return ER_EINVAL;
-  if (min_rows > 0 && !c->lws.blas) return fail(c, ER_ESTATE, "no library GEMM here (fp32 model or hipBLASLt unavailable)");
-  c->lws.blas_min_m = min_rows > 0 ? min_rows : INT32_MAX;
+  if (!c || min_rows < -1) return ER_EINVAL;
+  if (min_rows != 0 && !c->lws.blas) return fail(c, ER_ESTATE, "no library GEMM here (fp32 model or hipBLASLt unavailable)");
+  c->lws.blas_min_m = min_rows;
   return ER_OK;
 }
 

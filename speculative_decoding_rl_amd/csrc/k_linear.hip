@@ -1789,14 +1789,29 @@ __global__ __launch_bounds__(256) void k_resid_ssq(LinArgs a) {
 // load; QKV and gate/up land in fp32 in ws.blas_out for RoPE + the KV append
 // and SwiGLU; the residual projections add into h (beta = 1) and then sum its
 // squares; logits are written directly.  Returns 1 when the case does not
-// apply (the hand-written kernels run): below blas_min_m rows, the long-K
-// down projection below 1024 rows (where the hand-written GEMM is faster),
-// gathered rows without the norm, or while the stream is being captured
-// (recorded graphs hold the hand-written kernels only).
+// apply (the hand-written kernels run): below the shape's row threshold
+// (blas_wins, or a fixed blas_min_m; the long-K down projection always below
+// 1024 rows), gathered rows without the norm, or while the stream is being
+// captured (recorded graphs hold the hand-written kernels only).
+// Rows from which the library's GEMM beats the hand-written kernels, by
+// shape (same-box sweeps of the Qwen2.5-7B projections on MI355X, library
+// time / hand-written time): output widths from 16384 (gate/up: 0.89 at 16
+// rows, 0.61 at 96) from 16 rows; the vocabulary projection from 48 (0.93 at
+// 46); widths from 4096 (QKV: 0.90 at 80) from 80; narrower ones (the square
+// O projection: 1.04-1.08 up to 112, 0.73 at 204) from 160; K from 8192
+// (down: 1.5-2.6 below 1024 rows) from 1024.
+static bool blas_wins(int M, int N, int K) {
+  if (K >= 8192) return M >= 1024;
+  if (N >= 65536) return M >= 48;
+  if (N >= 16384) return M >= 16;
+  if (N >= 4096) return M >= 80;
+  return M >= 160;
+}
+
 static int run_blas(const LinArgs& a, const LinearWs& ws, hipStream_t st, LinearInfo* info) {
   const int M = a.M, N = a.W.N, K = a.W.K;
-  if (!ws.blas || a.W.fmt != FMT_BF16 || !a.act_bf16 || M < ws.blas_min_m) return 1;
-  if (K >= 8192 && M < 1024) return 1;
+  if (!ws.blas || ws.blas_min_m == 0 || a.W.fmt != FMT_BF16 || !a.act_bf16) return 1;
+  if (ws.blas_min_m < 0 ? !blas_wins(M, N, K) : (M < ws.blas_min_m || (K >= 8192 && M < 1024))) return 1;
   if (!a.xnorm && a.xrow) return 1;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return 1;

@@ -87,9 +87,10 @@ struct LinearWs {
   int n_counters;
   uint16_t* xn;       // bf16 x' for kernels that do not normalize on load (nullable)
   size_t xn_elems;
-  // Library GEMMs for bf16 weights from blas_min_m rows (nullable = never):
-  // the fp32 result of the QKV and gate/up projections goes to blas_out
-  // before its epilogue kernel.
+  // Library GEMMs for bf16 weights (nullable = never): blas_min_m < 0 from
+  // each shape's measured row threshold, > 0 from that many rows for every
+  // shape, 0 never.  The fp32 result of the QKV and gate/up projections goes
+  // to blas_out before its epilogue kernel.
   Blas* blas;
   int blas_min_m;
   float* blas_out;

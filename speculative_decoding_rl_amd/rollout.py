@@ -230,7 +230,8 @@ class Engine:
         check(self.lib.er_set_graphs(self.ctx, int(max_batch)), self.ctx, "er_set_graphs")
 
     def set_library_gemm(self, min_rows: int):
-        """Run the target's projections of >= min_rows rows as hipBLASLt GEMMs (default 128; 0: never)."""
+        """Run the target's projections as hipBLASLt GEMMs: -1 from each shape's measured row threshold
+        (the default), > 0 from min_rows rows for every shape, 0 never."""
         check(self.lib.er_set_library_gemm(self.ctx, int(min_rows)), self.ctx, "er_set_library_gemm")
 
     def graph_stats(self) -> dict:
