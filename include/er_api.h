@@ -330,7 +330,7 @@ int er_set_library_gemm(er_ctx *ctx, int min_rows);
  * TLT notes, section 3, Design A, A3: a range of batch sizes shares one set
  * of recorded graphs, and the drafter's graphs are recorded apart from the
  * target's.  With max_batch > 0, a step over n <= max_batch sequences runs as
- * nb sequences, nb = n for n <= 4, else the next power of two >= n, and
+ * nb sequences, nb = n for n <= 16, else the next power of two >= n, and
  * replays up to two graphs: AR steps one (target forward and draw);
  * speculative steps the drafter's (gamma forwards and draws) and the
  * target's (verify forward and lossless decision); history steps only that

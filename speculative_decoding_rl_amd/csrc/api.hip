@@ -262,8 +262,8 @@ int meta_upload(er_ctx* c) {
 
 // ---- bucketed graph capture --------------------------------------------------
 // TLT notes, section 3, Design A, A3: a batch range shares one set of
-// recorded graphs (here: 1, 2, 3, 4, then 5-8, 9-16, ... padded to the
-// range's top), and the
+// recorded graphs (here: every batch up to 16 alone, then 17-32, 33-64, ...
+// padded to the range's top), and the
 // drafter's and the target's graphs are recorded apart, so that the verify
 // graph serves both self-drafted and history-drafted steps.  Everything a
 // replayed kernel reads that changes from step to step sits in the metadata
@@ -278,10 +278,12 @@ int pow2_at_least(int x) {
   return p;
 }
 
-// Batch bucket: batches of 1 .. 4 run as they are (padding one of 3 to 4
-// costs more than the replay saves on MI355X: 2-6 % at 7B widths), larger
-// ones padded to the next power of two.
-int graph_bucket(int n) { return n <= 4 ? n : pow2_at_least(n); }
+// Batch bucket: batches of 1 .. 16 run as they are, larger ones padded to
+// the next power of two.  On MI355X at the 7B shape padding costs more than
+// a replay saves (3 to 4: 2-6 %; 6 to 8: 2-4 %; 11 to 16: 3-8 % slower than
+// the eager step, where exact buckets gain 1-4 %), while a recorded graph
+// holds only kernel nodes, so graphs per exact batch cost little memory.
+int graph_bucket(int n) { return n <= 16 ? n : pow2_at_least(n); }
 
 void graph_drop(er_ctx* c) {
   for (auto& kv : c->graphs) (void)hipGraphExecDestroy(kv.second.x);

@@ -37,18 +37,25 @@ struct Meta {
 // Attention work units of the n items whose queries start at pos0[i] and
 // number cnt[i], pushed into the metadata region as [n + 1] exclusive prefix
 // sums of units per item followed by [n] blocks per unit of each item.  The
-// unit length aims at ~256 work-groups over all KV heads (one per compute
-// unit: fewer, longer units keep each wave's block ring full, and a long
-// sequence no longer sets the kernel time alone; from a sweep of 128 / 256 /
-// 512 / 1024 / 2048 on MI355X at batch 1..128 and 4k/8k context); the target
-// is at least 8 blocks, an item of nblk blocks is cut into ceil(nblk/target)
-// even units (so at most ceil(nblk/8) units, each over half the target), and
-// an item that fits in one unit is not split (no combine for it).  Then the list of
+// unit length (unit_target) aims at ~1024 work-groups over all KV heads but
+// is at least 16 blocks (4 per wave of a work-group): from sweeps on MI355X
+// at the rollout's batch and context pairs, against the earlier aim of ~256
+// work-groups with 8 blocks at least, attention ran 12-15 % faster at batch
+// 11-22, 13 % at batch 3 and the same at batch 1, where shorter units only
+// add partials to combine.  An item of nblk blocks is cut into
+// ceil(nblk/target) even units (so at most ceil(nblk/16) units, each over
+// half the target), and an item that fits in one unit is not split (no
+// combine for it).  Then the list of
 // the items that were split ([n] entries, n_split used), and the most units
 // of one item.  *o_rec gets the offset of one record per unit, eight int32
 // each: item, split index | units of the item << 16, first block, blocks per
 // unit, query count, first query position, first query row, block-table row
 // (row0 and btrow per item), so that a work-group finds all of it in one load.
+// Blocks per attention work unit for `total` key blocks over all items.
+inline int64_t unit_target(int64_t total, int hkv) {
+  return std::min<int64_t>(1024, std::max<int64_t>(16, (total * hkv + 1023) / 1024));
+}
+
 inline size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, const int32_t* row0,
                          const int32_t* btrow, int* n_units, int* n_split, int* max_units, size_t* o_rec) {
   size_t off = 0;
@@ -56,7 +63,7 @@ inline size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int
   if (!us) return 0;
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 255) / 256));
+  const int64_t target = unit_target(total, hkv);
   int32_t acc = 0;
   int ns = 0, mu = 0;
   for (int i = 0; i < n; ++i) {
@@ -98,10 +105,16 @@ inline size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int
 // leave an empty partial (running max -inf, sum 0), which the combine weighs
 // by zero.  With U = 1 no item is split.  The layout (unit table [3n + 1],
 // then n * U records) is the one push_units writes.
+// Units per item of a graph's fixed split, for n items of at most cap_blocks
+// blocks: sized at half the capacity, the low end of a capacity class, so
+// that units stay at the eager split's length where contexts sit (a class
+// spans cap/2 .. cap), and never longer than the 1024 block ids one
+// work-group of the attention kernel stages.
 inline int graph_units_per_item(int n, int hkv, int cap_blocks) {
-  const int64_t total = (int64_t)n * cap_blocks;
-  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 255) / 256));
-  return (int)std::max<int64_t>(1, (cap_blocks + target - 1) / target);
+  const int64_t half = std::max<int64_t>(1, cap_blocks / 2);
+  const int64_t target = unit_target((int64_t)n * half, hkv);
+  const int64_t u = std::max<int64_t>((half + target - 1) / target, ((int64_t)cap_blocks + 1023) / 1024);
+  return (int)std::max<int64_t>(1, u);
 }
 inline size_t push_units_fixed(Meta& M, int n, int U, const int32_t* pos0, const int32_t* cnt, const int32_t* row0,
                                const int32_t* btrow, size_t* o_rec) {

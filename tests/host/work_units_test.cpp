@@ -33,7 +33,7 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
   assert(us[0] == 0 && us[n] == nu_tot);
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(8, (total * hkv + 255) / 256));
+  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(16, (total * hkv + 1023) / 1024));
   int split_seen = 0, most = 0;
   for (int i = 0; i < n; ++i) {
     const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
@@ -44,10 +44,10 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
     assert(bpu <= 1024);
     // the units cover the blocks: the last one is non-empty and none runs past the end
     assert((int64_t)bpu * nu >= nblk && (int64_t)bpu * (nu - 1) < nblk);
-    // an item that fits one unit is not split; a split item has at most ceil(nblk / 8) units (the
-    // bound the partials area and the combine are sized by) of more than half the target each
+    // an item that fits one unit is not split; a split item has at most ceil(nblk / 16) units (within
+    // the ceil(nblk / 8) the partials area and the combine are sized by) of more than half the target
     assert((nblk <= target) == (nu == 1));
-    assert(nu <= (nblk + 7) / 8 || nu == 1);
+    assert(nu <= (nblk + 15) / 16 || nu == 1);
     if (nu > 1) assert(2 * (int64_t)bpu > target);
     if (nu > 1) {
       assert(us[2 * n + 1 + split_seen] == i);
@@ -64,8 +64,8 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
     }
   }
   assert(split_seen == ns && most == mu);
-  // about 256 (unit, KV head) pairs once the target is neither floored nor capped
-  if (target > 8 && target < 1024) assert((int64_t)nu_tot * hkv <= 256 + (int64_t)n * hkv);
+  // about 1024 (unit, KV head) pairs once the target is neither floored nor capped
+  if (target > 16 && target < 1024) assert((int64_t)nu_tot * hkv <= 1024 + (int64_t)n * hkv);
   return nu_tot;
 }
 
@@ -77,7 +77,7 @@ static void check_fixed(Meta& M, int n, int hkv, int cap, const std::vector<int3
                         const std::vector<int32_t>& cnt, const std::vector<int32_t>& row0,
                         const std::vector<int32_t>& btrow) {
   const int U = graph_units_per_item(n, hkv, cap);
-  assert(U >= 1 && U <= (cap + 7) / 8 + 1);
+  assert(U >= 1 && U <= (cap + 15) / 16 + 1 && (int64_t)U * 1024 >= cap);
   size_t o_rec = 0;
   const size_t off = push_units_fixed(M, n, U, pos0.data(), cnt.data(), row0.data(), btrow.data(), &o_rec);
   assert(M.ok && M.used <= M.cap);
@@ -171,7 +171,7 @@ int main() {
   for (int it = 0; it < 300; ++it) {
     const int n = 1 << (rng() % 5);
     const int hkv = 1 << (rng() % 4);
-    const int cap = 16 << (rng() % 8);
+    const int cap = 16 << (rng() % 12);   // up to 32768 blocks (512k keys)
     const int q = 1 + (int)(rng() % 9);
     std::vector<int32_t> pos0(n), cnt(n, q), row0(n), btrow(n);
     for (int i = 0; i < n; ++i) {

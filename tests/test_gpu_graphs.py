@@ -1,12 +1,12 @@
 """Bucketed graph capture (er_set_graphs) against the oracle.
 
-With graphs on, steps run as their batch bucket (1 .. 4 as they are, larger
+With graphs on, steps run as their batch bucket (1 .. 16 as they are, larger
 batches padded to a power of two) and replay graphs recorded per (kind,
 bucket, gamma, context capacity).  Every replay is
 checked: the speculative lockstep (tests/lockstep.py) compares each step's
 drafter and target logits with the oracle's (tiny fp32 decoder within 1e-4
 relative; the bf16 decoder within 3e-2 absolute) and the tokens exactly on the
-GPU's own logits, while the batch shrinks through the buckets 8, 4, 3, 2, 1 and
+GPU's own logits, while the batch shrinks through the buckets 32, 16, ..., 1 and
 the host's own work and synchronizations run between replays.  AR steps with
 a padded bucket are checked the same way, a history step reuses the verify
 graph recorded by a self-drafted step of the same key, and the settings that
@@ -64,14 +64,16 @@ def mini():
     return _setup("mini-bf16", shape.quant)
 
 
-@pytest.mark.parametrize("T,top_p", [(1.0, 1.0), (0.8, 0.9)])
-def test_tiny_fp32_graph_lockstep(tiny, T, top_p):
-    """5 sequences (bucket 8, three padding rows) with ragged prompts, shrinking to one."""
+@pytest.mark.parametrize("n,T,top_p", [(5, 1.0, 1.0), (5, 0.8, 0.9), (18, 1.0, 1.0)])
+def test_tiny_fp32_graph_lockstep(tiny, n, T, top_p):
+    """5 sequences (buckets of their own) and 18 (bucket 32, fourteen padding rows, then their own
+    buckets from 16 down) with ragged prompts, shrinking to one."""
     shape, wts, cfg, W, D = tiny
-    prompts = [list(p) for p in synth.prompts(5, 40, shape.vocab, seed=7)]
-    prompts = [p[:20 + 4 * i] for i, p in enumerate(prompts)]
-    eng = _engine(shape, wts, "w8", seed=7, temperature=T, top_p=top_p, gamma_max=8)
-    eng.set_graphs(8)
+    prompts = [list(p) for p in synth.prompts(n, 40, shape.vocab, seed=7)]
+    prompts = [p[:20 + (4 * i) % 20] for i, p in enumerate(prompts)]
+    eng = _engine(shape, wts, "w8", seed=7, temperature=T, top_p=top_p, gamma_max=8, max_seqs=40, max_batch=32,
+                  kv_blocks=512)
+    eng.set_graphs(32)
     sp = OSP.SamplingParams(seed=7, temperature=T, top_p=top_p)
     gen, tally = run_lockstep(eng, cfg, W, D, prompts, 60, 4, sp)
     gs = eng.graph_stats()
@@ -104,15 +106,16 @@ def test_mini_bf16_graph_lockstep(mini, n_seq, gamma):
     assert gs["replays"] == 2 * tally.steps and gs["captures"] < gs["replays"]
 
 
-@pytest.mark.parametrize("n", [3, 5])
+@pytest.mark.parametrize("n", [3, 17])
 def test_graph_ar_steps_match_the_oracle(tiny, n):
-    """AR steps of 3 sequences (bucket 3) and of 5 (bucket 8, three padding rows); logits and tokens of
-    every step against the oracle."""
+    """AR steps of 3 sequences (bucket 3) and of 17 (bucket 32, fifteen padding rows); logits and tokens
+    of every step against the oracle."""
     shape, wts, cfg, W, D = tiny
     from speculative_decoding_rl_amd import _lib
     prompts = synth.prompts(n, 20, shape.vocab, seed=2)
-    eng = _engine(shape, wts, "w8", seed=2, policy=_lib.ER_POLICY_FORCE_AR)
-    eng.set_graphs(8)
+    eng = _engine(shape, wts, "w8", seed=2, policy=_lib.ER_POLICY_FORCE_AR, max_seqs=40, max_batch=32,
+                  kv_blocks=512)
+    eng.set_graphs(32)
     ids = eng.kv_alloc([20] * n, [12] * n)
     first = eng.prefill(ids, list(prompts))
     sp = OSP.SamplingParams(seed=2)
