@@ -477,7 +477,7 @@ int make_layout(const er_model_desc& m, const er_draft_desc& dd, const er_rollou
              align256((size_t)kDecodeBarWords * 4) + 256;
   }
   L->meta = align256((size_t)64 << 20);
-  if (m.dtype == ER_BF16) L->blas = (size_t)32 << 20;
+  if (m.dtype == ER_BF16) L->blas = (size_t)64 << 20;  // the library's largest 7B-shaped prefill GEMMs want 64 MiB
   L->block_bytes = (size_t)m.n_layers * 2 * hkv * KV_BLOCK * hd * ab;
   (void)why;
   return 0;

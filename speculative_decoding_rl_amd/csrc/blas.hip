@@ -14,7 +14,7 @@
 // matrix B; row-major W [N][K] the column-major K x N matrix A, used
 // transposed; the row-major result y [M][N] (leading dimension ldy) is the
 // column-major N x M matrix D = A^T B.  One plan (descriptors and the
-// heuristic's first algorithm) is kept per shape.
+// heuristic's best-ranked algorithm that fits the workspace) is kept per shape.
 
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
@@ -55,7 +55,7 @@ void free_plan(Blas::Plan& p) {
   p = Blas::Plan{};
 }
 
-// Descriptors and the heuristic's first algorithm for one shape; ok = false
+// Descriptors and the heuristic's best-ranked fitting algorithm for one shape; ok = false
 // when the library offers none (the caller then runs the hand-written kernel).
 Blas::Plan make_plan(Blas* b, const Blas::Key& k) {
   Blas::Plan p;
@@ -79,12 +79,17 @@ Blas::Plan make_plan(Blas* b, const Blas::Key& k) {
                                                  sizeof wsb) == HIPBLAS_STATUS_SUCCESS;
   }
   if (good) {
-    hipblasLtMatmulHeuristicResult_t res[4];
+    // The heuristic can rank first an algorithm that needs more workspace than the preference allows (seen
+    // at the 7B widths: 41-67 MB asked with 32 MB set); take the best-ranked one that fits.
+    hipblasLtMatmulHeuristicResult_t res[16];
     int n = 0;
-    good = hipblasLtMatmulAlgoGetHeuristic(b->h, p.op, p.A, p.B, p.D, p.D, pref, 4, res, &n) ==
-               HIPBLAS_STATUS_SUCCESS &&
-           n > 0 && res[0].state == HIPBLAS_STATUS_SUCCESS && res[0].workspaceSize <= b->ws_bytes;
-    if (good) p.algo = res[0].algo;
+    good = hipblasLtMatmulAlgoGetHeuristic(b->h, p.op, p.A, p.B, p.D, p.D, pref, 16, res, &n) ==
+           HIPBLAS_STATUS_SUCCESS;
+    int pick = -1;
+    for (int i = 0; good && i < n && pick < 0; ++i)
+      if (res[i].state == HIPBLAS_STATUS_SUCCESS && res[i].workspaceSize <= b->ws_bytes) pick = i;
+    good = good && pick >= 0;
+    if (good) p.algo = res[pick].algo;
   }
   if (pref) hipblasLtMatmulPreferenceDestroy(pref);
   if (!good) {
