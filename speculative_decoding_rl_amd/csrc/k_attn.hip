@@ -269,15 +269,15 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a, int nsplit, i
       }
     };
     if (nb > 0) {
-      fetch(0, bid(0));
-      fetch(1, bid(1));
-      long idn = bid(2);
+#pragma unroll
+      for (int d = 0; d < D - 1; ++d) fetch(d, bid(d));
+      long idn = bid(D - 1);
       for (int t0 = 0; t0 < nb; t0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
           const int t = t0 + d;
-          fetch((d + 2) % D, idn);  // block t + 2 (re-loads of the last block past the end)
-          idn = bid(t + 3);
+          fetch((d + D - 1) % D, idn);  // block t + D - 1 (re-loads of the last block past the end)
+          idn = bid(t + D);
           if (t < nb) process(d, first + s_in * t);
         }
       }

@@ -42,7 +42,11 @@ struct Meta {
 // at the rollout's batch and context pairs, against the earlier aim of ~256
 // work-groups with 8 blocks at least, attention ran 12-15 % faster at batch
 // 11-22, 13 % at batch 3 and the same at batch 1, where shorter units only
-// add partials to combine.  An item of nblk blocks is cut into
+// add partials to combine.  Once the items alone give 512 work-groups or more
+// (two per CU), no item is split below 1024 blocks: at batch 204 and 1.6k keys
+// the 816 unsplit work-groups ran the attention op 8 % faster (150.4 us
+// against 145.8 us for the 1632 split ones plus 18.0 us of combine), and
+// batches 46 and 96 (184 and 384 items) are unaffected.  An item of nblk blocks is cut into
 // ceil(nblk/target) even units (so at most ceil(nblk/16) units, each over
 // half the target), and an item that fits in one unit is not split (no
 // combine for it).  Then the list of
@@ -63,7 +67,7 @@ inline size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int
   if (!us) return 0;
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  const int64_t target = unit_target(total, hkv);
+  const int64_t target = (int64_t)n * hkv >= 512 ? 1024 : unit_target(total, hkv);
   int32_t acc = 0;
   int ns = 0, mu = 0;
   for (int i = 0; i < n; ++i) {

@@ -33,7 +33,10 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
   assert(us[0] == 0 && us[n] == nu_tot);
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  const int64_t target = std::min<int64_t>(1024, std::max<int64_t>(16, (total * hkv + 1023) / 1024));
+  // ~1024 (unit, KV head) pairs of at least 16 blocks; no split below 1024 blocks once the items alone
+  // give 512 pairs
+  const bool many = (int64_t)n * hkv >= 512;
+  const int64_t target = many ? 1024 : std::min<int64_t>(1024, std::max<int64_t>(16, (total * hkv + 1023) / 1024));
   int split_seen = 0, most = 0;
   for (int i = 0; i < n; ++i) {
     const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
@@ -65,7 +68,8 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
   }
   assert(split_seen == ns && most == mu);
   // about 1024 (unit, KV head) pairs once the target is neither floored nor capped
-  if (target > 16 && target < 1024) assert((int64_t)nu_tot * hkv <= 1024 + (int64_t)n * hkv);
+  if (!many && target > 16 && target < 1024) assert((int64_t)nu_tot * hkv <= 1024 + (int64_t)n * hkv);
+  if (many) assert(ns == 0 || mu >= 2);
   return nu_tot;
 }
 
