@@ -1874,7 +1874,7 @@ int er_rollout_init(const er_model_desc* model, const er_weights* w, const er_dr
     if (L.blas) {
       // library GEMMs for the target's projections from each shape's row threshold (er_set_library_gemm)
       char* bw = take(L.blas);
-      c->lws.blas = blas_create(bw, L.blas);
+      c->lws.blas = blas_create(bw, L.blas, c->gu, L.gu / 4);
       c->lws.blas_min_m = -1;
       c->lws.blas_out = c->gu;
       c->lws.blas_out_floats = L.gu / 4;

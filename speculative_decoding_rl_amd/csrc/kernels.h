@@ -73,9 +73,12 @@ struct LinArgs {
 // Plain bf16 GEMMs through hipBLASLt (blas.hip): y = beta * y + x W^T, x
 // [M][ldx] bf16, W [N][K] bf16, y [M][ldy] fp32 (out32) or bf16.  Returns 0,
 // 1 when the library has no algorithm for the shape (nothing launched), or a
-// negative error.
+// negative error.  The first call of a shape with up to 512 rows times
+// candidate algorithms and waits for the stream (never under stream capture);
+// scratch (scratch_floats fp32) receives the timing runs of accumulating
+// calls (beta = 1).
 struct Blas;
-Blas* blas_create(void* workspace, size_t ws_bytes);
+Blas* blas_create(void* workspace, size_t ws_bytes, float* scratch, size_t scratch_floats);
 void blas_destroy(Blas* b);
 int blas_gemm(Blas* b, const void* x, int ldx, int M, const void* W, int N, int K, void* y, int ldy, bool out32,
               float beta, hipStream_t st);
