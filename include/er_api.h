@@ -321,7 +321,10 @@ int er_get_decode_trace(er_ctx *ctx, double *work_us, double *release_us, int ma
  * measured faster on MI355X (output width >= 16384: 16 rows; >= 65536: 48;
  * >= 4096: 80; narrower: 160; K >= 8192: 1024); > 0: every shape from that
  * many rows (K >= 8192 still from 1024); 0: never.  Steps recorded into
- * graphs use this library's kernels only.  Same arithmetic per element up to
+ * graphs use this library's kernels only.  The first step with a new shape
+ * of up to 512 rows times a few of the library's algorithms for it and keeps
+ * the fastest (that step waits for the stream once per shape and projection),
+ * so runs may pick different algorithms.  Same arithmetic per element up to
  * the order of the fp32 sums.  ER_EINVAL for min_rows < -1; ER_ESTATE for
  * min_rows != 0 where no library GEMM is available (fp32 models). */
 int er_set_library_gemm(er_ctx *ctx, int min_rows);
