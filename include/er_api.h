@@ -319,7 +319,7 @@ int er_get_decode_trace(er_ctx *ctx, double *work_us, double *release_us, int ma
  * sums of squares), from a row count that depends on the shape.  min_rows =
  * -1 (the default): each shape from the rows where the library's GEMM was
  * measured faster on MI355X (output width >= 16384: 16 rows; >= 65536: 48;
- * >= 4096: 80; narrower: 160; K >= 8192: 1024); > 0: every shape from that
+ * >= 4096: 80; narrower: 17; K >= 8192: 1024); > 0: every shape from that
  * many rows (K >= 8192 still from 1024); 0: never.  Steps recorded into
  * graphs use this library's kernels only.  The first step with a new shape
  * of up to 512 rows times a few of the library's algorithms for it and keeps

@@ -1798,14 +1798,17 @@ __global__ __launch_bounds__(256) void k_resid_ssq(LinArgs a) {
 // time / hand-written time): output widths from 16384 (gate/up: 0.89 at 16
 // rows, 0.61 at 96) from 16 rows; the vocabulary projection from 48 (0.93 at
 // 46); widths from 4096 (QKV: 0.90 at 80) from 80; narrower ones (the square
-// O projection: 1.04-1.08 up to 112, 0.73 at 204) from 160; K from 8192
-// (down: 1.5-2.6 below 1024 rows) from 1024.
+// O projection) from 17: with the library's algorithm chosen by timing, the
+// whole AR step ran 1.4-3.2 % faster at 17-32 rows and 1.1 % at 48-64 with
+// the O projection on the library, and the same from 96 to 192; K from 8192
+// (down: 1.5-2.6 below 1024 rows; the AR step 8-16 % slower with it on the
+// library at 17-192 rows) from 1024.
 static bool blas_wins(int M, int N, int K) {
   if (K >= 8192) return M >= 1024;
   if (N >= 65536) return M >= 48;
   if (N >= 16384) return M >= 16;
   if (N >= 4096) return M >= 80;
-  return M >= 160;
+  return M >= 17;
 }
 
 static int run_blas(const LinArgs& a, const LinearWs& ws, hipStream_t st, LinearInfo* info) {
