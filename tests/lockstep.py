@@ -85,6 +85,32 @@ def greedy_margin(z):
     return float(s[-1] - s[-2])
 
 
+def greedy_paths_agree(cfg, W, prompts, ref, other, bound):
+    """Two greedy rollouts of the same prompts by two GPU paths that may sum in
+    different orders (a 1-row and a (gamma+1)-row target forward).  With the
+    oracle teacher-forced on `ref`: wherever the greedy top-2 margin is at least
+    `bound` (twice the per-path logit bound), `ref` holds the oracle's argmax;
+    the two rollouts agree token for token up to their first difference, which
+    must sit at a position whose margin is under `bound` (either argmax is then
+    the target's) and ends the comparison of that sequence.  Returns the tokens
+    compared."""
+    checked = 0
+    for i, pr in enumerate(prompts):
+        a, b = list(ref[i]), list(other[i])
+        assert len(a) == len(b), i
+        toks = list(pr) + a[:-1]
+        z = forward(cfg, W, toks, list(range(len(toks))), KVStore(cfg, len(toks)))[len(pr) - 1:]
+        for k in range(len(a)):
+            near_tie = greedy_margin(z[k]) < bound
+            if not near_tie:
+                assert a[k] == int(np.argmax(z[k])), (i, k)
+            if a[k] != b[k]:
+                assert near_tie, (i, k, greedy_margin(z[k]))
+                break
+            checked += 1
+    return checked
+
+
 def _kappa(eps, T):
     return float(np.expm1(2.0 * eps / T))
 

