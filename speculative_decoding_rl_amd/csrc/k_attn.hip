@@ -78,8 +78,13 @@ ER_DEV Unit unit_of(const AttnArgs& a, int u, int nsplit, int bps) {
   return w;
 }
 
-template <int HD, int NW>
-__global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a, int nsplit, int bps) {
+// D: stages of the K/V register ring (block t + D - 1 is loaded while block
+// t is scored).  D = 2 fits 168 registers, three waves per SIMD (three
+// work-groups per CU); D = 1 fits 128, four (LDS allows four work-groups per
+// CU).  The three-stage ring needed ~221, two work-groups per CU.
+template <int HD, int NW, int D>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(D == 2 ? 3 : 4)))
+void k_attn_mfma(AttnArgs a, int nsplit, int bps) {
   constexpr int NC = HD / 16;   // 16-column output tiles
   constexpr int NQ = HD / 32;   // 32-wide k slices of the score MFMA
   const int u = blockIdx.x, g = blockIdx.y;
@@ -173,7 +178,6 @@ __global__ __launch_bounds__(NW * 64) void k_attn_mfma(AttnArgs a, int nsplit, i
     // Every load is unconditional (indices clamped to the last block):
     // conditional loads would make the compiler drain the whole load counter
     // at each use.
-    constexpr int D = 3;
     const int first = b0 + sin;
     const int nb = first < b1 ? (b1 - first + s_in - 1) / s_in : 0;
     const int tl = nb > 0 ? nb - 1 : 0;
@@ -410,9 +414,13 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int nsplit, int b
 }
 
 // Combine of an item's units for one (KV head, row): the units' maxima and
-// weights exp(m_s - M) first (weights kept in LDS), then blockDim / hd thread
+// weights exp(m_s - M) (weights kept in LDS), then blockDim / hd thread
 // groups each sum a strided subset of the units for one output element per
-// thread, and the groups add in a fixed order.
+// thread, and the groups add in a fixed order.  Every load of the first
+// nt units' (max, sum) and of each group's first eight strided partials is
+// issued before anything waits, so an item of up to 8 * ng units costs one
+// memory round trip (the maxima, the weights and the partial sums were three
+// dependent trips).  The sums run in the same order either way.
 constexpr int kCombineMaxUnits = 4096;
 template <bool BF>
 __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
@@ -430,19 +438,33 @@ __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
   const long stride_sp = (long)a.hkv * (grp * a.max_q_count) * (hd + 2);
   const float* base = partial_row(a, u0, g, r);
   const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+  const int ng = nt / hd, gi = tid / hd, e = tid - gi * hd;
 
-  float mx = -INFINITY;
-  for (int s = tid; s < nu; s += nt) mx = fmaxf(mx, base[s * stride_sp + hd]);
+  // the round trip: (max, sum) of unit tid and this group's first eight partials
+  const int s_own = min(tid, nu - 1);
+  const float m_own = base[s_own * stride_sp + hd];
+  const float l_own = base[s_own * stride_sp + hd + 1];
+  float p0[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) p0[j] = base[min(gi + j * ng, nu - 1) * stride_sp + e];
+
+  float mx = tid < nu ? m_own : -INFINITY;
+  for (int s = tid + nt; s < nu; s += nt) mx = fmaxf(mx, base[s * stride_sp + hd]);
   mx = wave_max(mx);
   if (lane == 0) red[0][wave] = mx;
   __syncthreads();
   float M = -INFINITY;
   for (int w = 0; w < nw; ++w) M = fmaxf(M, red[0][w]);
+  // the bf16 kernel's partial maxima are in the log2 domain, the fp32 one's natural
+  auto weight = [&](float ms) { return (ms == -INFINITY) ? 0.f : (BF ? __builtin_amdgcn_exp2f(ms - M) : expf(ms - M)); };
   float dl = 0.f;
-  for (int s = tid; s < nu; s += nt) {
-    const float ms = base[s * stride_sp + hd];
-    // the bf16 kernel's partial maxima are in the log2 domain, the fp32 one's natural
-    const float wt = (ms == -INFINITY) ? 0.f : (BF ? __builtin_amdgcn_exp2f(ms - M) : expf(ms - M));
+  if (tid < nu) {
+    const float wt = weight(m_own);
+    w_sh[tid] = wt;
+    dl = wt * l_own;   // fmaf(wt, l, 0)
+  }
+  for (int s = tid + nt; s < nu; s += nt) {
+    const float wt = weight(base[s * stride_sp + hd]);
     w_sh[s] = wt;
     dl = fmaf(wt, base[s * stride_sp + hd + 1], dl);
   }
@@ -452,9 +474,11 @@ __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
   float den = 0.f;
   for (int w = 0; w < nw; ++w) den += red[1][w];
 
-  const int ng = nt / hd, gi = tid / hd, e = tid - gi * hd;
   float num = 0.f;
-  int s = gi;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (gi + j * ng < nu) num = fmaf(w_sh[gi + j * ng], p0[j], num);
+  int s = gi + 8 * ng;
   for (; s + 7 * ng < nu; s += 8 * ng) {
     float p[8];
 #pragma unroll
@@ -473,11 +497,14 @@ __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
   Act<BF>::st((T*)a.out, o, den > 0.f ? num / den : 0.f);
 }
 
-int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined) {
-  if (a.n_items <= 0) return 0;
+// The split without a unit table: every item gets nsplit units of bps
+// blocks.  Keys are split over work-groups until each wave walks at most 4
+// blocks, but no further than ~512 groups in flight.
+struct UniformSplit {
+  int nsplit, bps;
+};
+static UniformSplit uniform_split(const AttnArgs& a) {
   const int grp = a.hq / a.hkv;
-  if ((a.hd != 64 && a.hd != 128) || a.hq % a.hkv != 0) return -1;
-  if (grp * a.max_q_count > 64) return -1;
   const int maxblk = (a.max_ctx + 15) / 16;
   const long base = (long)a.n_items * a.hkv;
   // Waves of a work-group that share its KV range (the rest hold other query
@@ -485,16 +512,44 @@ int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined
   const int rows = grp * a.max_q_count;
   const int rgroups = (rows + 15) / 16;
   const int s_in = (rgroups == 1 ? 4 : (rgroups == 2 ? 2 : 1)) * (kAttnWaves / 4);
-  // Split the keys over work-groups until each wave walks at most 4 blocks
-  // (each block is a dependent load of scattered pages), but no further than
-  // ~512 groups in flight.
   const int per_wg = 4 * s_in;
   int nsplit = 1;
   if (maxblk > per_wg)
     nsplit = (int)std::max(1L, std::min((long)(maxblk + per_wg - 1) / per_wg, (512 + base - 1) / base));
   if ((maxblk + nsplit - 1) / nsplit > kAttnMaxUnitBlocks) nsplit = (maxblk + kAttnMaxUnitBlocks - 1) / kAttnMaxUnitBlocks;
-  const int bps = (maxblk + nsplit - 1) / nsplit;
-  nsplit = (maxblk + bps - 1) / bps;
+  const int bps = std::max(1, (maxblk + nsplit - 1) / nsplit);
+  return UniformSplit{std::max(1, (maxblk + bps - 1) / bps), bps};
+}
+
+// Ring depth of the scoring kernel for a launch: units of at most
+// kAttnShortUnit blocks (about 12 per wave) take the one-stage ring at four
+// work-groups per CU, longer ones the two-stage ring at three.  Measured on
+// the rollout's batch bins (against the three-stage ring at two work-groups
+// per CU): batch 1-11 16-19 % faster with one stage (21.6 -> 17.1 us at
+// batch 1, 44.8 -> 35.1 at batch 6) where two stages gave 11-17 %, batch
+// 46-204 1-2 % faster with two stages where one stage gave 0-6 % slower.
+constexpr long kAttnShortUnit = 48;
+int attn_ring(const AttnArgs& a) {
+  const int maxblk = (a.max_ctx + 15) / 16;
+  long units, bpu;
+  if (a.unit_start) {
+    units = std::max(1, a.n_units);
+    bpu = ((long)maxblk * a.n_items + units - 1) / units;
+  } else {
+    bpu = uniform_split(a).bps;
+  }
+  return bpu <= kAttnShortUnit ? 1 : 2;
+}
+
+int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined) {
+  if (a.n_items <= 0) return 0;
+  const int grp = a.hq / a.hkv;
+  if ((a.hd != 64 && a.hd != 128) || a.hq % a.hkv != 0) return -1;
+  if (grp * a.max_q_count > 64) return -1;
+  const int maxblk = (a.max_ctx + 15) / 16;
+  const UniformSplit us = uniform_split(a);
+  int nsplit = us.nsplit;
+  const int bps = us.bps;
   const long units = a.unit_start ? (long)a.n_units : (long)a.n_items * nsplit;
   const bool combine = a.unit_start ? a.n_split > 0 : nsplit > 1;
   if (combine && (a.unit_start ? (maxblk + 7) / 8 : nsplit) > kCombineMaxUnits) return -1;
@@ -507,8 +562,13 @@ int launch_attention(const AttnArgs& a, hipStream_t st, int phase, int* combined
   dim3 grid((unsigned)units, a.hkv, 1);
   if (phase != 2) {
   if (a.bf16) {
-    if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
-    else hipLaunchKernelGGL((k_attn_mfma<64, kAttnWaves>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
+    if (attn_ring(a) == 1) {
+      if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, kAttnWaves, 1>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
+      else hipLaunchKernelGGL((k_attn_mfma<64, kAttnWaves, 1>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
+    } else {
+      if (a.hd == 128) hipLaunchKernelGGL((k_attn_mfma<128, kAttnWaves, 2>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
+      else hipLaunchKernelGGL((k_attn_mfma<64, kAttnWaves, 2>), grid, dim3(kAttnWaves * 64), 0, st, a, nsplit, bps);
+    }
   } else {
     hipLaunchKernelGGL(k_attn_valu, grid, dim3(256), 0, st, a, nsplit, bps);
   }

@@ -173,6 +173,8 @@ struct AttnArgs {
 // Waves per work-group of the bf16 attention kernel (k_attn_mfma<hd, waves>).
 constexpr int kAttnWaves = 4;
 int launch_attention(const AttnArgs& a, hipStream_t st, int phase = 0, int* combined = nullptr);
+// Ring depth (1 or 2) launch_attention picks for the bf16 scoring kernel.
+int attn_ring(const AttnArgs& a);
 
 // Persistent decode forward (bf16 models, 1..16 rows): embedding, every
 // decoder layer and the final residual stream in one cooperative launch (see

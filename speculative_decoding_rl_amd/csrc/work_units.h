@@ -37,16 +37,19 @@ struct Meta {
 // Attention work units of the n items whose queries start at pos0[i] and
 // number cnt[i], pushed into the metadata region as [n + 1] exclusive prefix
 // sums of units per item followed by [n] blocks per unit of each item.  The
-// unit length (unit_target) aims at ~1024 work-groups over all KV heads but
-// is at least 16 blocks (4 per wave of a work-group): from sweeps on MI355X
-// at the rollout's batch and context pairs, against the earlier aim of ~256
-// work-groups with 8 blocks at least, attention ran 12-15 % faster at batch
-// 11-22, 13 % at batch 3 and the same at batch 1, where shorter units only
-// add partials to combine.  Once the items alone give 512 work-groups or more
-// (two per CU), no item is split below 1024 blocks: at batch 204 and 1.6k keys
-// the 816 unsplit work-groups ran the attention op 8 % faster (150.4 us
-// against 145.8 us for the 1632 split ones plus 18.0 us of combine), and
-// batches 46 and 96 (184 and 384 items) are unaffected.  An item of nblk blocks is cut into
+// unit length (unit_target) aims at ~768 work-groups over all KV heads -- one
+// resident round of the attention kernel at three work-groups per CU -- but
+// is at least 16 blocks (4 per wave of a work-group), and once the items
+// alone give 768 work-groups no item is split below 1024 blocks.  From sweeps
+// on MI355X at the rollout's batch and context pairs, against an aim of ~1024
+// work-groups with no split from 512 items: attention 4 % faster at batch 96
+// (2 units of 103 blocks each instead of 3: 128.0 vs 133.4 us), 2-6 % at
+// batch 6-46, 1-2 % slower at batch 1 and 22, and the same at batch 204 (816
+// items, not split either way; splitting them in two made the kernel 3 %
+// faster but the combine cost more).  An aim of ~1536 with units from 8
+// blocks was 6 % faster at batch 1 and 7 % slower at batch 11.  Earlier, with
+// two resident work-groups per CU, ~1024 with 16 blocks at least had beaten
+// ~256 with 8 by 12-15 % at batch 11-22.  An item of nblk blocks is cut into
 // ceil(nblk/target) even units (so at most ceil(nblk/16) units, each over
 // half the target), and an item that fits in one unit is not split (no
 // combine for it).  Then the list of
@@ -56,8 +59,12 @@ struct Meta {
 // unit, query count, first query position, first query row, block-table row
 // (row0 and btrow per item), so that a work-group finds all of it in one load.
 // Blocks per attention work unit for `total` key blocks over all items.
+// The split's aim and floor: kAttnAimPairs (unit, KV head) pairs, units of
+// at least kAttnMinUnitBlocks blocks, no split once the items alone give
+// kAttnNoSplitPairs pairs.
+constexpr int64_t kAttnAimPairs = 768, kAttnMinUnitBlocks = 16, kAttnNoSplitPairs = 768;
 inline int64_t unit_target(int64_t total, int hkv) {
-  return std::min<int64_t>(1024, std::max<int64_t>(16, (total * hkv + 1023) / 1024));
+  return std::min<int64_t>(1024, std::max<int64_t>(kAttnMinUnitBlocks, (total * hkv + kAttnAimPairs - 1) / kAttnAimPairs));
 }
 
 inline size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int32_t* cnt, const int32_t* row0,
@@ -67,7 +74,7 @@ inline size_t push_units(Meta& M, int n, int hkv, const int32_t* pos0, const int
   if (!us) return 0;
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  const int64_t target = (int64_t)n * hkv >= 512 ? 1024 : unit_target(total, hkv);
+  const int64_t target = (int64_t)n * hkv >= kAttnNoSplitPairs ? 1024 : unit_target(total, hkv);
   int32_t acc = 0;
   int ns = 0, mu = 0;
   for (int i = 0; i < n; ++i) {

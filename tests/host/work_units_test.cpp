@@ -33,10 +33,10 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
   assert(us[0] == 0 && us[n] == nu_tot);
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
-  // ~1024 (unit, KV head) pairs of at least 16 blocks; no split below 1024 blocks once the items alone
-  // give 512 pairs
-  const bool many = (int64_t)n * hkv >= 512;
-  const int64_t target = many ? 1024 : std::min<int64_t>(1024, std::max<int64_t>(16, (total * hkv + 1023) / 1024));
+  // ~768 (unit, KV head) pairs of at least 16 blocks; no split below 1024 blocks once the items alone
+  // give 768 pairs
+  const bool many = (int64_t)n * hkv >= 768;
+  const int64_t target = many ? 1024 : std::min<int64_t>(1024, std::max<int64_t>(16, (total * hkv + 767) / 768));
   int split_seen = 0, most = 0;
   for (int i = 0; i < n; ++i) {
     const int64_t nblk = (pos0[i] + cnt[i] + KV_BLOCK - 1) / KV_BLOCK;
@@ -67,8 +67,8 @@ static int check_split(Meta& M, int n, int hkv, const std::vector<int32_t>& pos0
     }
   }
   assert(split_seen == ns && most == mu);
-  // about 1024 (unit, KV head) pairs once the target is neither floored nor capped
-  if (!many && target > 16 && target < 1024) assert((int64_t)nu_tot * hkv <= 1024 + (int64_t)n * hkv);
+  // about 768 (unit, KV head) pairs once the target is neither floored nor capped
+  if (!many && target > 16 && target < 1024) assert((int64_t)nu_tot * hkv <= 768 + (int64_t)n * hkv);
   if (many) assert(ns == 0 || mu >= 2);
   return nu_tot;
 }
