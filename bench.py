@@ -350,7 +350,13 @@ def kernel_role(name):
     if name.startswith("er::k_attn"):
         return "attention"
     m = re.match(r"er::k_(skinny|linear_mfma)<(\d+)", name)
-    return "draft" if m and int(m.group(2)) in (2, 3) else "target"
+    if m:
+        return "draft" if int(m.group(2)) in (2, 3) else "target"
+    # the weight-streaming GEMM names its format first only for the quantized weights (five arguments)
+    m = re.match(r"er::k_wgemm<([^>]*)>", name)
+    if m and len(m.group(1).split(",")) == 5:
+        return "draft" if int(m.group(1).split(",")[0]) in (2, 3) else "target"
+    return "target"
 
 
 def kernel_table(kprof):

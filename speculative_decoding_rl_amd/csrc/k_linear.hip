@@ -1040,30 +1040,42 @@ static int run_skinny_variant(int code, const LinArgs& a, hipStream_t st, Linear
 }
 
 // ----------------------------------------------------------------------------
-// Weight-streaming GEMM for 16 < M <= 256 (bf16 weights): large-batch decode
-// and verify, where the layer is still bound by reading W once.  Each wave
-// streams its own 16*NR weight rows through a register ring (DEPTH stages of
-// 128 k); the M x (KS*128) window of x for the current step is staged in LDS
-// and shared by every wave (double-buffered, one barrier per step).  The next
+// Weight-streaming GEMM for 16 < M <= 256: large-batch decode and verify
+// (bf16 weights) and drafting (W8 / W4 weights), where the layer is still
+// bound by reading W once.  Each wave streams its own 16*NR weight rows
+// through a register ring (DEPTH stages of 128 k); the M x (KS*128) window of
+// x for the current step is staged in LDS and shared by every wave
+// (double-buffered, one barrier per step).  Quantized weights are converted
+// in registers once per stage and feed every m-subtile of the window (so each
+// weight byte is read once whatever M is), as bf16 of (q + 128); the
+// zero-point term uses the window's per-chunk row sums of x, formed once per
+// work-group while the window is written to LDS (16 lanes per row and chunk,
+// summed by shuffles): W4 adds s * (acc_chunk - (128 + z) * sum) per chunk,
+// W8 acc_chunk - 128 * sum, scaled per row at the end.  The next
 // window's loads are issued ahead of the weights so that writing it to LDS
 // never waits on weight loads still in flight.  KS waves split each step's K
 // range and reduce in LDS; nsplit > 1 splits K over work-groups, with the
 // partial tiles summed in a fixed order by k_splitk_reduce.
 // ----------------------------------------------------------------------------
-template <int MI, int NR, int KS, int DEPTH>
-__global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ part, int nsplit, int cps) {
+template <int FMT, int MI, int NR, int KS, int DEPTH>
+__global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ part, int nsplit, int cps, int mtiles) {
   constexpr int RG = 8 / KS;
   constexpr int MT = 16 * MI;
   constexpr int WK = KS * 128;           // k per step
   constexpr int LDX = WK + 8;            // LDS row stride (bf16)
   constexpr int XV = MT * WK / 8 / 512;  // uint4 of the x window per thread
   static_assert(MT * WK % (8 * 512) == 0, "x window must split evenly over the threads");
+  constexpr int NW = StageW<FMT>::NW;   // uint4 of one stage of one subtile per lane
+  constexpr bool Q = FMT != FMT_BF16;
   __shared__ __attribute__((aligned(16))) uint16_t xw[2][MT * LDX];
+  __shared__ __attribute__((aligned(16))) float xsum_sh[Q ? 2 : 1][Q ? KS * MT : 1];  // [buf][chunk of window][row]
 
   const int b = blockIdx.x, nwg = gridDim.x;
   const int xcd = b & 7, loc = b >> 3, per = nwg >> 3, rem = nwg & 7;
   const int L = (xcd < rem) ? xcd * (per + 1) + loc : rem * (per + 1) + (xcd - rem) * per + loc;
-  const int sp = L % nsplit, nt = L / nsplit;
+  // the m-tiles of one weight tile are adjacent block indices (one XCD, one L2)
+  const int mt = L % mtiles, sp = (L / mtiles) % nsplit, nt = L / mtiles / nsplit;
+  const int m0 = mt * MT;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
   const int rg = wave / KS, ks = wave % KS;
   const int kb = lane >> 4, l16 = lane & 15;
@@ -1071,8 +1083,9 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
   const int nchunks = K >> 7;
   const int c0 = sp * cps, c1 = min(nchunks, c0 + cps);
   const int T = (c1 - c0 + KS - 1) / KS;  // steps
-  const uint16_t* __restrict__ W = (const uint16_t*)a.W.w;
+  const void* __restrict__ Wv = a.W.w;
   const uint16_t* __restrict__ X = (const uint16_t*)a.x;
+  const long G = K >> 7;
 
   if (b == 0 && a.ssq_zero && nsplit == 1)
     ssq_clear(a, tid, 512);
@@ -1087,16 +1100,28 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
     nrow[ni] = in ? n_lane[ni] : N - 1;
   }
 
-  uint4 wreg[DEPTH][NR][4];
+  uint4 wreg[DEPTH][NR][NW];
+  float wsc[DEPTH][NR], wzp[DEPTH][NR];   // W4: scale and 128 + zero of (row, chunk)
   uint4 xr[XV];
   auto issue_w = [&](int t, int slot) {
     const long c = c0 + (long)t * KS + ks;
     if (c >= c1) return;
 #pragma unroll
     for (int ni = 0; ni < NR; ++ni) {
-      const uint16_t* p = W + nrow[ni] * K + c * 128 + 8 * kb;
+      if constexpr (FMT == FMT_BF16) {
+        const uint16_t* p = (const uint16_t*)Wv + nrow[ni] * K + c * 128 + 8 * kb;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wreg[slot][ni][i] = *(const uint4*)(p + 32 * i);
+        for (int i = 0; i < 4; ++i) wreg[slot][ni][i] = *(const uint4*)(p + 32 * i);
+      } else if constexpr (FMT == FMT_W8) {
+        const int8_t* p = (const int8_t*)Wv + nrow[ni] * K + c * 128 + 16 * kb;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) wreg[slot][ni][h] = *(const uint4*)(p + 64 * h);
+      } else {
+        const uint8_t* p = (const uint8_t*)Wv + w4_piece(nrow[ni], c, N, K) + 16 * kb;
+        wreg[slot][ni][0] = *(const uint4*)p;
+        wsc[slot][ni] = bf2f(((const uint16_t*)a.W.scale)[nrow[ni] * G + c]);
+        wzp[slot][ni] = 128.0f + (float)((const uint8_t*)a.W.zero)[nrow[ni] * G + c];
+      }
     }
   };
   auto load_x = [&](int t) {
@@ -1106,7 +1131,7 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
       const int e = tid + 512 * v;
       const int m = e / (WK / 8), k8 = e - m * (WK / 8);
       uint4 val = uint4{0u, 0u, 0u, 0u};
-      if (m < M && k0 + k8 * 8 < (long)c1 * 128) val = *(const uint4*)(X + (long)m * a.ldx + k0 + k8 * 8);
+      if (m0 + m < M && k0 + k8 * 8 < (long)c1 * 128) val = *(const uint4*)(X + (long)(m0 + m) * a.ldx + k0 + k8 * 8);
       xr[v] = val;
     }
   };
@@ -1116,6 +1141,16 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
       const int e = tid + 512 * v;
       const int m = e / (WK / 8), k8 = e - m * (WK / 8);
       *(uint4*)(&xw[buf][m * LDX + k8 * 8]) = xr[v];
+      if constexpr (Q) {
+        // the 16 pieces of one (row, chunk) are 16 aligned consecutive threads
+        const uint4 o = xr[v];
+        float sm = bf_lo(o.x) + bf_hi(o.x) + bf_lo(o.y) + bf_hi(o.y) + bf_lo(o.z) + bf_hi(o.z) + bf_lo(o.w) + bf_hi(o.w);
+        sm += __shfl_xor(sm, 1, 64);
+        sm += __shfl_xor(sm, 2, 64);
+        sm += __shfl_xor(sm, 4, 64);
+        sm += __shfl_xor(sm, 8, 64);
+        if ((k8 & 15) == 0) xsum_sh[buf][(k8 >> 4) * MT + m] = sm;
+      }
     }
   };
 
@@ -1128,16 +1163,59 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
   auto compute = [&](int t, int slot, int buf) {
     const int c = c0 + t * KS + ks;
     if (c >= c1) return;
-    const uint16_t* xb = &xw[buf][ks * 128 + 8 * kb];
+    if constexpr (FMT == FMT_BF16) {
+      const uint16_t* xb = &xw[buf][ks * 128 + 8 * kb];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+          const bf16x8_t xa = *(const bf16x8_t*)(xb + (mi * 16 + l16) * LDX + 32 * i);
+#pragma unroll
+          for (int ni = 0; ni < NR; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8_t, wreg[slot][ni][i]),
+                                                                  acc[mi][ni], 0, 0, 0);
+        }
+      }
+    } else {
+      // the stage's weights as bf16 of (q + 128), converted once for every m-subtile
+      bf16x8_t bw[NR][4];
+#pragma unroll
+      for (int ni = 0; ni < NR; ++ni)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (FMT == FMT_W8) {
+            const uint4 v = wreg[slot][ni][i >> 1];
+            bw[ni][i] = (i & 1) ? w8_to_bf16(v.z, v.w) : w8_to_bf16(v.x, v.y);
+          } else {
+            const uint4 v = wreg[slot][ni][0];
+            bw[ni][i] = w4_to_bf16((i == 0) ? v.x : (i == 1) ? v.y : (i == 2) ? v.z : v.w);
+          }
+        }
+      const uint16_t* xb = &xw[buf][ks * 128];
 #pragma unroll
       for (int mi = 0; mi < MI; ++mi) {
-        const bf16x8_t xa = *(const bf16x8_t*)(xb + (mi * 16 + l16) * LDX + 32 * i);
+        f32x4_t accg[NR];
+#pragma unroll
+        for (int ni = 0; ni < NR; ++ni) accg[ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8_t xa = *(const bf16x8_t*)(xb + (mi * 16 + l16) * LDX + kcol<FMT>(i, kb));
+#pragma unroll
+          for (int ni = 0; ni < NR; ++ni)
+            accg[ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bw[ni][i], accg[ni], 0, 0, 0);
+        }
+        // rows mi*16 + 4kb + r of this chunk's row sums
+        const float4 xs4 = *reinterpret_cast<const float4*>(&xsum_sh[buf][ks * MT + mi * 16 + 4 * kb]);
+        const float xsm[4] = {xs4.x, xs4.y, xs4.z, xs4.w};
 #pragma unroll
         for (int ni = 0; ni < NR; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, __builtin_bit_cast(bf16x8_t, wreg[slot][ni][i]),
-                                                                acc[mi][ni], 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if constexpr (FMT == FMT_W8)
+              acc[mi][ni][r] += accg[ni][r] - 128.0f * xsm[r];
+            else
+              acc[mi][ni][r] = fmaf(wsc[slot][ni], fmaf(-wzp[slot][ni], xsm[r], accg[ni][r]), acc[mi][ni][r]);
+          }
       }
     }
   };
@@ -1161,6 +1239,17 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
         if (t + 1 < T) store_x((d + 1) & 1);
         lds_barrier();
       }
+    }
+  }
+
+  if constexpr (FMT == FMT_W8) {
+#pragma unroll
+    for (int ni = 0; ni < NR; ++ni) {
+      const float sc = ((const float*)a.W.scale)[nrow[ni]];
+#pragma unroll
+      for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[mi][ni][r] *= sc;
     }
   }
 
@@ -1205,7 +1294,7 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
     __syncthreads();
     for (int e = tid; e < MT * R; e += 512) {
       const int row = e >> 7, col = e & 127;  // a wave covers 64 columns of one row
-      const int m = row;
+      const int m = m0 + row;
       const int sidx = (nt * RG) * NR + (col >> 4);
       const bool mok = m < M, nok = 16 * sidx + (col & 15) < N;
       const int n = nok ? phys_row(a, sidx, col & 15) : N;
@@ -1232,7 +1321,7 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
   for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = mi * 16 + 4 * kb + r;
+      const int m = m0 + mi * 16 + 4 * kb + r;
       const bool mok = m < M;
       float sq = 0.f;
 #pragma unroll
@@ -1254,26 +1343,31 @@ __global__ __launch_bounds__(512) void k_wgemm(LinArgs a, float* __restrict__ pa
     }
 }
 
-template <int MI, int NR, int KS, int DEPTH>
-static int run_wgemm(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStream_t st, LinearInfo* info) {
+template <int FMT, int MI, int NR, int KS, int DEPTH>
+static int run_wgemm_fmt(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStream_t st, LinearInfo* info) {
   constexpr int R = 16 * NR * (8 / KS);
-  if (a.M > 16 * MI || a.W.fmt != FMT_BF16 || a.xnorm) return -1;
+  constexpr int MT = 16 * MI;
+  // bf16 weights: one m-tile (the plan sends larger M to the tiled GEMMs); quantized weights are
+  // re-read once per m-tile of up to MT rows
+  if ((FMT == FMT_BF16 && a.M > MT) || a.W.fmt != FMT || a.xnorm) return -1;
+  const int mtiles = (a.M + MT - 1) / MT;
   const int nchunks = a.W.K / 128;
   const long ntiles = (a.W.N + R - 1) / R;
   int nsplit = 1;
   // split K over work-groups while the grid is short of want_wgs and every
   // split keeps at least 4 steps
-  while (ntiles * nsplit * 2 <= want_wgs && nchunks / (nsplit * 2 * KS) >= 4 &&
+  while (ntiles * mtiles * nsplit * 2 <= want_wgs && nchunks / (nsplit * 2 * KS) >= 4 &&
          (size_t)(nsplit * 2) * a.M * a.W.N <= ws.partial_floats && ws.partial)
     nsplit *= 2;
   const int cps = (nchunks + nsplit - 1) / nsplit;
   nsplit = (nchunks + cps - 1) / cps;
   if (info) {
-    snprintf(info->name, sizeof info->name, "er::k_wgemm<%d, %d, %d, %d>", MI, NR, KS, DEPTH);
+    if (FMT == FMT_BF16) snprintf(info->name, sizeof info->name, "er::k_wgemm<%d, %d, %d, %d>", MI, NR, KS, DEPTH);
+    else snprintf(info->name, sizeof info->name, "er::k_wgemm<%d, %d, %d, %d, %d>", FMT, MI, NR, KS, DEPTH);
     info->nsplit = nsplit;
   }
-  hipLaunchKernelGGL((k_wgemm<MI, NR, KS, DEPTH>), dim3((unsigned)(ntiles * nsplit)), dim3(512), 0, st, a, ws.partial,
-                     nsplit, cps);
+  hipLaunchKernelGGL((k_wgemm<FMT, MI, NR, KS, DEPTH>), dim3((unsigned)(ntiles * nsplit * mtiles)), dim3(512), 0, st, a,
+                     ws.partial, nsplit, cps, mtiles);
   if (hipGetLastError() != hipSuccess) return -3;
   if (nsplit > 1) {
     const long waves = (long)a.M * ((a.W.N + 63) / 64);
@@ -1281,6 +1375,17 @@ static int run_wgemm(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStre
     if (hipGetLastError() != hipSuccess) return -3;
   }
   return 0;
+}
+
+// The weight-streaming GEMM for the weights' format.
+template <int MI, int NR, int KS, int DEPTH>
+static int run_wgemm(const LinArgs& a, const LinearWs& ws, int want_wgs, hipStream_t st, LinearInfo* info) {
+  switch (a.W.fmt) {
+    case FMT_BF16: return run_wgemm_fmt<FMT_BF16, MI, NR, KS, DEPTH>(a, ws, want_wgs, st, info);
+    case FMT_W8: return run_wgemm_fmt<FMT_W8, MI, NR, KS, DEPTH>(a, ws, want_wgs, st, info);
+    case FMT_W4: return run_wgemm_fmt<FMT_W4, MI, NR, KS, DEPTH>(a, ws, want_wgs, st, info);
+  }
+  return -1;
 }
 
 // Explicit weight-streaming variant: code = 3000 + 100*MI(1 digit: 2,4,8; 0 = 16) + 10*KS + 10000*NR... kept
@@ -1639,8 +1744,11 @@ static Plan plan_of(const LinArgs& a) {
   const size_t lds = skinny_lds(a.W.fmt, M, K, 1, 8).total;
   const bool stream_fits = M <= 16 && lds <= kSkinnyLdsMax;
   if (a.W.fmt != FMT_BF16) {
-    if (!stream_fits) return P_SKINNY_OLD;
-    if (M <= 8 || N >= 65536 || (N >= 16384 && M <= 12)) return P_STREAM;
+    if (stream_fits && (M <= 8 || N >= 65536 || (N >= 16384 && M <= 12))) return P_STREAM;
+    // above 16 rows the weight-streaming GEMM (each quantized weight read once per 32- or 64-row
+    // m-tile, converted once for the tile's rows), except the narrow square layers at <= 32 rows,
+    // where the register-fed kernel was faster (W4 O projection at M = 22: 10.6 vs 14.4 us)
+    if (M > 16 && M <= 256 && !(M <= 32 && N <= 4096 && K <= 4096)) return P_WGEMM;
     return P_SKINNY_OLD;
   }
   if (M <= 8 && stream_fits) return P_STREAM;
@@ -1692,6 +1800,14 @@ static int run_auto(const LinArgs& a, const LinearWs& ws, Plan p, hipStream_t st
       }
       return -1;
     case P_WGEMM:
+      if (a.W.fmt != FMT_BF16) {
+        // W4 at the 7B shape (us; register-fed kernel / 32-row tiles, 64 rows per group / 64-row tiles,
+        // 128 rows per group): QKV at M = 46 29.7 / 19.7 / 20.0, at 204 74.6 / 28.6 / 38.4; gate/up at
+        // 22 60.3 / 49.1 / 57.8, at 46 110.0 / 72.7 / 60.5, at 204 354.1 / 211.9 / 167.6; down at 46
+        // 82.6 / 40.1 / 33.1, at 204 268.2 / 119.4 / 86.5.  128-row tiles were slower still.
+        if (M <= 32 || (N <= 8192 && K <= 4096)) return run_wgemm<2, 1, 2, 3>(a, ws, 512, st, info);
+        return run_wgemm<4, 1, 1, 3>(a, ws, 512, st, info);
+      }
       if (M <= 32) return run_wgemm<2, 1, 4, 3>(a, ws, 512, st, info);
       return run_wgemm<4, 1, 1, 3>(a, ws, 512, st, info);
     case P_GEMM2:
@@ -1920,7 +2036,8 @@ int launch_linear_fused(const LinArgs& a, const LinearWs& ws, int path, hipStrea
     return -1;
   }
   Plan p = plan_of(a);
-  if ((p == P_GEMM || p == P_GEMM2 || p == P_WGEMM) && !gemm_ok) p = P_SKINNY_OLD;
+  if ((p == P_GEMM || p == P_GEMM2 || (p == P_WGEMM && a.W.fmt == FMT_BF16)) && !gemm_ok) p = P_SKINNY_OLD;
+  if (p == P_WGEMM && !ws.partial) p = P_SKINNY_OLD;
   if (a.xnorm && p != P_STREAM) {
     // these kernels read bf16 x: form x' = RMSNorm(h) * g once, in the workspace
     if (ws.xn && (size_t)a.M * a.W.K <= ws.xn_elems) {

@@ -71,6 +71,9 @@ def test_kernel_roles():
     assert b.kernel_role("er::k_linear_mfma<2, 16, 1, 8>") == "draft"    # W8 drafter
     assert b.kernel_role("er::k_skinny<1, 1, 2, 2>") == "target"         # bf16 target (verify and AR)
     assert b.kernel_role("er::k_gemm2<64, 1, 4, 64>") == "target"
+    assert b.kernel_role("er::k_wgemm<3, 8, 1, 1, 3>") == "draft"        # W4 weight-streaming GEMM
+    assert b.kernel_role("er::k_wgemm<2, 4, 1, 1, 3>") == "draft"        # W8
+    assert b.kernel_role("er::k_wgemm<2, 1, 4, 3>") == "target"          # bf16 (four arguments, MI first)
     assert b.kernel_role("er::k_attn_mfma<128, 4>") == "attention"
     assert b.kernel_role("er::k_attn_combine<true>") == "attention"
 

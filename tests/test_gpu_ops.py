@@ -179,6 +179,27 @@ def test_linear_gemm_variants(ops, code, M):
     assert r < 4e-6, r
 
 
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("code,M", [
+    (31420, 17), (31430, 32), (32420, 30), (31230, 70), (31221, 64), (32221, 49), (31131, 50), (31122, 100),
+    (31132, 128), (31132, 129), (31132, 256), (31123, 200),
+])
+def test_linear_quantized_weight_streaming(ops, fmt, code, M):
+    # W8 / W4 weights converted in registers once per stage for every m-subtile of the x window; M past
+    # the window's rows runs further m-tiles (70 rows in 32-row windows, 129 and 256 in 128-row ones);
+    # N ragged, K = 26 chunks (split-K over groups where the grid is short)
+    r = _linear_case(ops, fmt, M, 456, 3328, code, seed=code % 89 + M)
+    assert r < 4e-6, r
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("M", [17, 40, 130])
+def test_linear_quantized_long_k(ops, fmt, M):
+    # the 18944-deep down projection's K through the automatic plan (many split-K groups)
+    r = _linear_case(ops, fmt, M, 200, 18944, 1, seed=M)
+    assert r < 4e-6, r
+
+
 @pytest.mark.parametrize("M,N,K", [(40, 96, 18944), (300, 200, 1152), (1000, 300, 512), (129, 4608, 384),
                                    (40, 33000, 1152), (64, 32900, 1024)])
 def test_linear_tiled_gemm(ops, M, N, K):
