@@ -58,7 +58,8 @@ int er_op_w4_kernel_order(const void *d_canon, int N, int K, void *d_out, void *
  *          wave, K split over KS of the 8 waves, m-tile MT in {16, 32})
  *   2000 + 100*NR + 10*KS + D       streaming kernel, M <= 16: x staged in LDS,
  *          weights through a D-deep register ring
- *   30000 + 1000*NR + 100*KS + 10*D + i   weight-streaming GEMM, M <= 16 * {2,4,8,16}[i]
+ *   30000 + 1000*NR + 100*KS + 10*D + i   weight-streaming GEMM over m-tiles of 16 * {2,4,8,16}[i]
+ *          rows (bf16 weights: M at most one m-tile; W8/W4: any M, one m-tile per work-group)
  *   40000 + 100*i + 10*D + w        deep-pipelined GEMM, BM = {_,64,128,256}[i] with 64-wide
  *          k steps (i = 1..3) or BM = 128 with 32-wide k steps (i = 5), register
  *          ring depth D, split-K until 256*w work-groups */
