@@ -417,12 +417,11 @@ __global__ __launch_bounds__(256) void k_attn_valu(AttnArgs a, int nsplit, int b
 // weights exp(m_s - M) (weights kept in LDS), then blockDim / hd thread
 // groups each sum a strided subset of the units for one output element per
 // thread, and the groups add in a fixed order.  Every load of the first
-// nt units' (max, sum) and of each group's first sixteen strided partials is
-// issued before anything waits, so an item of up to 16 * ng units costs one
+// nt units' (max, sum) and of each group's first eight strided partials is
+// issued before anything waits, so an item of up to 8 * ng units costs one
 // memory round trip (the maxima, the weights and the partial sums were three
 // dependent trips).  The sums run in the same order either way.
 constexpr int kCombineMaxUnits = 4096;
-constexpr int kCombineFirst = 16;  // partials per thread in the first round trip
 template <bool BF>
 __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
   __shared__ float w_sh[kCombineMaxUnits];
@@ -445,9 +444,9 @@ __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
   const int s_own = min(tid, nu - 1);
   const float m_own = base[s_own * stride_sp + hd];
   const float l_own = base[s_own * stride_sp + hd + 1];
-  float p0[kCombineFirst];
+  float p0[8];
 #pragma unroll
-  for (int j = 0; j < kCombineFirst; ++j) p0[j] = base[min(gi + j * ng, nu - 1) * stride_sp + e];
+  for (int j = 0; j < 8; ++j) p0[j] = base[min(gi + j * ng, nu - 1) * stride_sp + e];
 
   float mx = tid < nu ? m_own : -INFINITY;
   for (int s = tid + nt; s < nu; s += nt) mx = fmaxf(mx, base[s * stride_sp + hd]);
@@ -477,9 +476,9 @@ __global__ __launch_bounds__(1024) void k_attn_combine(AttnArgs a, int nsplit) {
 
   float num = 0.f;
 #pragma unroll
-  for (int j = 0; j < kCombineFirst; ++j)
+  for (int j = 0; j < 8; ++j)
     if (gi + j * ng < nu) num = fmaf(w_sh[gi + j * ng], p0[j], num);
-  int s = gi + kCombineFirst * ng;
+  int s = gi + 8 * ng;
   for (; s + 7 * ng < nu; s += 8 * ng) {
     float p[8];
 #pragma unroll
