@@ -21,11 +21,17 @@
 // 204 rows: 25.6 against 19.1 us; gate/up at 96 rows: 59.5 against 46.8 us)
 // and 4x slower for QKV at 512 rows; above 512 rows it was within a few
 // percent of the best, and timing there would cost milliseconds per shape.
+// The choice (the candidate's rank) is kept per process and device, so every
+// context of a process runs a shape with the same algorithm and the same
+// summation order: results do not depend on which context computed them
+// (two contexts that timed apart could pick different algorithms and round
+// differently).  Across processes the choice follows the timing.
 
 #include <hip/hip_runtime.h>
 #include <hipblaslt/hipblaslt.h>
 
 #include <map>
+#include <mutex>
 #include <tuple>
 
 #include "kernels.h"
@@ -118,11 +124,17 @@ Blas::Plan make_plan(Blas* b, const Blas::Key& k) {
 // call whose output accumulates (beta = 1) is timed with beta = 0 into the
 // scratch area, so the real output is written once, by the caller's run; when
 // the scratch is too small the first-ranked algorithm stays.
-void tune_plan(Blas* b, Blas::Plan& p, const void* x, const void* W, void* y, int M, int ldy, float beta,
-               hipStream_t st) {
+// Rank of the candidate timed fastest per (device, workspace size, shape), for every context of the
+// process (the heuristic ranks the same candidates for the same descriptors and workspace).
+std::mutex g_pick_mu;
+std::map<std::tuple<int, size_t, Blas::Key>, int> g_pick;
+
+// Returns the rank of the fastest candidate, or -1 when nothing was timed.
+int tune_plan(Blas* b, Blas::Plan& p, const void* x, const void* W, void* y, int M, int ldy, float beta,
+              hipStream_t st) {
   void* out = y;
   if (beta != 0.f) {
-    if (!b->scratch || (size_t)M * ldy > b->scratch_floats) return;
+    if (!b->scratch || (size_t)M * ldy > b->scratch_floats) return -1;
     out = b->scratch;
   }
   const float alpha = 1.0f, beta0 = 0.f;
@@ -134,9 +146,9 @@ void tune_plan(Blas* b, Blas::Plan& p, const void* x, const void* W, void* y, in
                              b->ws_bytes, st) == HIPBLAS_STATUS_SUCCESS;
     };
     if (!run()) continue;
-    if (hipEventRecord(b->ev[0], st) != hipSuccess) return;
+    if (hipEventRecord(b->ev[0], st) != hipSuccess) return -1;
     const bool ok = run() && run();
-    if (hipEventRecord(b->ev[1], st) != hipSuccess || hipEventSynchronize(b->ev[1]) != hipSuccess) return;
+    if (hipEventRecord(b->ev[1], st) != hipSuccess || hipEventSynchronize(b->ev[1]) != hipSuccess) return -1;
     float ms = 0.f;
     if (!ok || hipEventElapsedTime(&ms, b->ev[0], b->ev[1]) != hipSuccess) continue;
     if (best < 0.f || ms < best) {
@@ -144,7 +156,9 @@ void tune_plan(Blas* b, Blas::Plan& p, const void* x, const void* W, void* y, in
       pick = i;
     }
   }
+  if (best < 0.f) return -1;
   p.algo = p.cand[pick];
+  return pick;
 }
 
 }  // namespace
@@ -182,7 +196,20 @@ int blas_gemm(Blas* b, const void* x, int ldx, int M, const void* W, int N, int 
   auto it = b->plans.find(k);
   if (it == b->plans.end()) {
     it = b->plans.emplace(k, make_plan(b, k)).first;
-    if (it->second.ok && it->second.ncand > 1 && M <= kBlasTuneMaxM) tune_plan(b, it->second, x, W, y, M, ldy, beta, st);
+    Blas::Plan& p = it->second;
+    if (p.ok && p.ncand > 1 && M <= kBlasTuneMaxM) {
+      int dev = 0;
+      (void)hipGetDevice(&dev);
+      const auto key = std::make_tuple(dev, b->ws_bytes, k);
+      std::lock_guard<std::mutex> lk(g_pick_mu);
+      const auto got = g_pick.find(key);
+      if (got != g_pick.end()) {
+        if (got->second < p.ncand) p.algo = p.cand[got->second];
+      } else {
+        const int pick = tune_plan(b, p, x, W, y, M, ldy, beta, st);
+        if (pick >= 0) g_pick.emplace(key, pick);
+      }
+    }
   }
   const Blas::Plan& p = it->second;
   if (!p.ok) return 1;

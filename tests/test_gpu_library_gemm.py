@@ -115,3 +115,25 @@ def test_library_gemm_at_7b_widths_matches_the_kernel_path(qwen7_2l):
     print(f"max |library - kernels| = {d:.2e}")
     assert got[0][0] == got[1][0]
     assert d < 2 * ABS_TOL
+
+
+def test_contexts_of_one_process_compute_alike(mini):
+    """Two contexts prefilling the same prompts through library GEMMs (66 and 130 rows: algorithms chosen
+    by timing on a shape's first use) produce bit-identical logits and first tokens: the timed choice is
+    kept per process and device, so the second context runs the first one's algorithms."""
+    from speculative_decoding_rl_amd import _lib
+    shape, wts, cfg, W, D = mini
+    outs = []
+    for _ in range(2):
+        eng = _engine(shape, wts, shape.quant, seed=5, policy=_lib.ER_POLICY_FORCE_AR)
+        for n, plen in ((2, 33), (2, 65)):
+            prompts = [list(p) for p in synth.prompts(n, plen, shape.vocab, seed=plen)]
+            ids = eng.kv_alloc([plen] * n, [4] * n)
+            first = eng.prefill(ids, prompts)
+            outs.append((list(first), [eng.debug_logits(1, i).copy() for i in range(n)]))
+        eng.close()
+    half = len(outs) // 2
+    for (fa, za), (fb, zb) in zip(outs[:half], outs[half:]):
+        assert fa == fb
+        for a, b in zip(za, zb):
+            assert np.array_equal(a, b)
