@@ -1746,9 +1746,9 @@ static Plan plan_of(const LinArgs& a) {
   if (a.W.fmt != FMT_BF16) {
     if (stream_fits && (M <= 8 || N >= 65536 || (N >= 16384 && M <= 12))) return P_STREAM;
     // above 16 rows the weight-streaming GEMM (each quantized weight read once per 32- or 64-row
-    // m-tile, converted once for the tile's rows), except the narrow square layers at <= 32 rows,
+    // m-tile, converted once for the tile's rows; any M, in m-tiles), except the narrow square layers at <= 32 rows,
     // where the register-fed kernel was faster (W4 O projection at M = 22: 10.6 vs 14.4 us)
-    if (M > 16 && M <= 256 && !(M <= 32 && N <= 4096 && K <= 4096)) return P_WGEMM;
+    if (M > 16 && !(M <= 32 && N <= 4096 && K <= 4096)) return P_WGEMM;
     return P_SKINNY_OLD;
   }
   if (M <= 8 && stream_fits) return P_STREAM;

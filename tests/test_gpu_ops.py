@@ -193,6 +193,14 @@ def test_linear_quantized_weight_streaming(ops, fmt, code, M):
 
 
 @pytest.mark.parametrize("fmt", ["w8", "w4"])
+@pytest.mark.parametrize("M,N,K", [(300, 456, 3328), (520, 200, 1152)])
+def test_linear_quantized_many_rows(ops, fmt, M, N, K):
+    # the automatic plan past 256 rows (GRPO-sized drafter batches): the weight-streaming GEMM in m-tiles
+    r = _linear_case(ops, fmt, M, N, K, 0, seed=M + N)
+    assert r < 4e-6, r
+
+
+@pytest.mark.parametrize("fmt", ["w8", "w4"])
 @pytest.mark.parametrize("M", [17, 40, 130])
 def test_linear_quantized_long_k(ops, fmt, M):
     # the 18944-deep down projection's K through the automatic plan (many split-K groups)
