@@ -30,6 +30,8 @@ Prints one JSON line (N = 1 only: the library runs on one GPU).
 from __future__ import annotations
 
 import argparse
+import contextlib
+import gc
 import json
 import re
 import math
@@ -50,6 +52,21 @@ MFMA_PEAK_TFS = 2500.0  # dense bf16
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+@contextlib.contextmanager
+def no_gc():
+    """Timed loops run without the cyclic garbage collector (collected just before): a full
+    collection over the interpreter's objects takes tens of milliseconds, which would otherwise
+    land inside whichever timed step triggers it.  Reference counting still frees as usual."""
+    gc.collect()
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
 
 
 def parse():
@@ -160,6 +177,9 @@ def run_rollout(eng, args, prompts, stops, label):
     prof = not args.no_kernel_profile
     if prof:
         eng.reset_kernel_profile()
+    gc.collect()
+    gc_was = gc.isenabled()
+    gc.disable()   # as no_gc(): no collection pause inside a timed step
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     t_last = t_start
@@ -184,6 +204,8 @@ def run_rollout(eng, args, prompts, stops, label):
             t_last = te
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
+    if gc_was:
+        gc.enable()
     kprof = eng.kernel_profile() if prof else []
     if prof:
         eng.set_kernel_profile(False)
@@ -573,17 +595,18 @@ def sweep(args, shape, wts, stops):
                 eng.step(act)
             recs = []
             cbar = sum(eng.seq_info(a)[1] for a in act) / B     # committed keys, tracked from the emitted counts
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(K):
-                ts = time.perf_counter()
-                tok, ne, info = eng.step(act)
-                te = time.perf_counter()
-                n_em = int(ne.sum())
-                recs.append((B, int(info.mode), int(info.gamma), n_em, te - ts, int(info.accepted), cbar))
-                cbar += n_em / B
-            torch.cuda.synchronize()
-            dt = time.perf_counter() - t0
+            with no_gc():
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(K):
+                    ts = time.perf_counter()
+                    tok, ne, info = eng.step(act)
+                    te = time.perf_counter()
+                    n_em = int(ne.sum())
+                    recs.append((B, int(info.mode), int(info.gamma), n_em, te - ts, int(info.accepted), cbar))
+                    cbar += n_em / B
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
             tokens = sum(r[3] for r in recs)
             timed_recs[m].extend(recs)
             row[m] = dict(tok_s=round(tokens / dt, 1), ms_per_step=round(dt * 1e3 / K, 3), tokens=tokens,
@@ -678,13 +701,14 @@ def crossover(args, shape, wts):
                 eng.step(act)
             torch.cuda.synchronize()
             timed = timed_steps(B)
-            ts = time.perf_counter()
-            tok = 0
-            for _ in range(timed):
-                _, ne, _ = eng.step(act)
-                tok += int(ne.sum())
-            torch.cuda.synchronize()
-            dt = (time.perf_counter() - ts) / timed
+            with no_gc():
+                ts = time.perf_counter()
+                tok = 0
+                for _ in range(timed):
+                    _, ne, _ = eng.step(act)
+                    tok += int(ne.sum())
+                torch.cuda.synchronize()
+                dt = (time.perf_counter() - ts) / timed
             cbar = C + sum(eng.seq_info(a)[1] - C for a in act) / B
             en = tok / timed / B
             t_roof = roof.step(0 if g == 0 else 1, g, B, cbar)
